@@ -1,0 +1,181 @@
+"""Seeded synthetic inputs for the selective-scan forward.
+
+This module only draws random numbers and encodes them; it holds none of the
+scan's arithmetic.  Both the HIP path (through the binding) and the CPU oracle
+consume the arrays it returns, so both sides see the same bf16 bit patterns.
+
+Workloads are the five Mamba-shaped layers of the scan's benchmark set:
+
+  0  tiny fp32 layer: batch 1, 16 channels, L 64, N 4
+  1  Mamba-130M-like: batch 8, 1536 channels, L 2048, N 16, bf16 inputs
+  2  Mamba-2.8B-like: batch 4, 5120 channels, L 4096, N 16, bf16 inputs
+  3  long-sequence layer: batch 1, 1024 channels, L 1,048,576, N 16, bf16 inputs
+  4  scalar-decay multi-head layer: batch 2, 80 heads x 64 channels, L 8192, N 128
+
+Recipe (per workload k): ``numpy.random.default_rng(1000 + k)`` (PCG64).
+Tensors are drawn in the fixed order u, delta_raw, z, B, C, dt, D, A as float32
+(dt as float64) and rounded to bf16 with round-to-nearest-even where the
+workload is bf16.  Large tensors are drawn in fixed-size blocks, so the stream
+is defined block by block.  A is the S4D-real diagonal A[d, n] = -(n + 1) for
+workloads 0-3 (no draw) and -U(1, 16) per head for workload 4.  The step bias
+is delta_bias = log(expm1(dt)) (the inverse of softplus) computed in float64
+and stored as float32, with dt log-uniform, one per channel (per head in
+workload 4).
+
+Every size can be overridden to make smaller cases with the same value
+distributions and flags.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+_BLOCK = 1 << 24  # elements drawn per block for large tensors
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return the uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32)
+    rounded = b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclass
+class Problem:
+    """One scan problem.  Arrays are contiguous; bf16 tensors are uint16 bit patterns.
+
+    Layouts (L innermost):
+      u, z      [batch, channels, L]
+      delta     [batch, heads, L]            heads == channels unless scalar_decay
+      A         [channels, N] or [heads]     (scalar decay per head)
+      B, C      [batch, groups, N, L]
+      D         [channels] or [heads]
+      delta_bias[heads]
+    """
+
+    name: str
+    batch: int
+    channels: int
+    length: int
+    nstate: int
+    groups: int
+    heads: int
+    in_dtype: str  # "f32" or "bf16"
+    u: np.ndarray
+    delta: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    C: np.ndarray
+    D: Optional[np.ndarray]
+    z: Optional[np.ndarray]
+    delta_bias: Optional[np.ndarray]
+    softplus: bool = True
+    scalar_decay: bool = False
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def elements(self) -> int:
+        return self.batch * self.channels * self.length
+
+    @property
+    def gate(self) -> bool:
+        return self.z is not None
+
+
+DEFAULTS = {
+    0: dict(batch=1, channels=16, length=64, nstate=4, heads=None, in_dtype="f32", gate=False,
+            bc_scale=1.0, dt=(1e-3, 1e-1)),
+    1: dict(batch=8, channels=1536, length=2048, nstate=16, heads=None, in_dtype="bf16", gate=True,
+            bc_scale=1.0, dt=(1e-3, 1e-1)),
+    2: dict(batch=4, channels=5120, length=4096, nstate=16, heads=None, in_dtype="bf16", gate=True,
+            bc_scale=1.0, dt=(1e-3, 1e-1)),
+    3: dict(batch=1, channels=1024, length=1 << 20, nstate=16, heads=None, in_dtype="bf16", gate=True,
+            bc_scale=0.25, dt=(1e-4, 1e-2)),
+    4: dict(batch=2, channels=80 * 64, length=8192, nstate=128, heads=80, in_dtype="bf16", gate=False,
+            bc_scale=None, dt=(1e-3, 1e-1)),
+}
+
+NAMES = {
+    0: "tiny-fp32 (1x16x64, N=4)",
+    1: "mamba-130m-layer (8x1536x2048, N=16)",
+    2: "mamba-2.8b-layer (4x5120x4096, N=16)",
+    3: "long-seq-layer (1x1024x1048576, N=16)",
+    4: "scalar-decay-multihead (2x(80x64)x8192, N=128)",
+}
+
+
+def _normal(rng: np.random.Generator, shape, scale: float, dtype: str) -> np.ndarray:
+    """Standard normal draws (float32), times ``scale`` in float32, encoded as ``dtype``."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    s = np.float32(scale)
+    for lo in range(0, n, _BLOCK):
+        hi = min(n, lo + _BLOCK)
+        x = rng.standard_normal(hi - lo, dtype=np.float32)
+        if scale != 1.0:
+            x = x * s
+        out[lo:hi] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    return out.reshape(shape)
+
+
+def make(cfg: int, *, batch: Optional[int] = None, channels: Optional[int] = None,
+         length: Optional[int] = None, nstate: Optional[int] = None, heads: Optional[int] = None,
+         headdim: Optional[int] = None, seed: Optional[int] = None, in_dtype: Optional[str] = None,
+         gate: Optional[bool] = None, with_D: bool = True, with_bias: bool = True) -> Problem:
+    """Build workload ``cfg`` (0-4), optionally resized.  Deterministic for a given seed.
+
+    For the scalar-decay workload (4) the channel count is ``heads * headdim``
+    (defaults 80 and 64); ``channels`` is ignored there.
+    """
+    d = dict(DEFAULTS[cfg])
+    Bt = batch if batch is not None else d["batch"]
+    N = nstate if nstate is not None else d["nstate"]
+    L = length if length is not None else d["length"]
+    dt_lo, dt_hi = d["dt"]
+    dtype = in_dtype if in_dtype is not None else d["in_dtype"]
+    use_gate = d["gate"] if gate is None else gate
+    scalar = cfg == 4
+    if scalar:
+        H = heads if heads is not None else d["heads"]
+        P = headdim if headdim is not None else 64
+        Dc = H * P
+    else:
+        Dc = channels if channels is not None else d["channels"]
+        H = Dc
+    G = 1
+    bc_scale = d["bc_scale"] if d["bc_scale"] is not None else 1.0 / np.sqrt(N)
+    rng = np.random.default_rng(1000 + cfg if seed is None else seed)
+
+    u = _normal(rng, (Bt, Dc, L), 1.0, dtype)
+    delta = _normal(rng, (Bt, H, L), 1.0, dtype)
+    z = _normal(rng, (Bt, Dc, L), 1.0, dtype) if use_gate else None
+    B = _normal(rng, (Bt, G, N, L), bc_scale, dtype)
+    C = _normal(rng, (Bt, G, N, L), bc_scale, dtype)
+    dt = np.exp(rng.uniform(np.log(dt_lo), np.log(dt_hi), size=H))
+    delta_bias = np.log(np.expm1(dt)).astype(np.float32) if with_bias else None
+    Dvec = rng.standard_normal(H if scalar else Dc, dtype=np.float32)
+    if scalar:
+        A = (-rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    else:
+        A = np.broadcast_to(-(np.arange(N, dtype=np.float32) + 1.0), (Dc, N)).copy()
+    return Problem(
+        name=NAMES[cfg], batch=Bt, channels=Dc, length=L, nstate=N, groups=G, heads=H,
+        in_dtype=dtype, u=u, delta=delta, A=A, B=B, C=C,
+        D=Dvec if with_D else None, z=z, delta_bias=delta_bias, softplus=True,
+        scalar_decay=scalar, meta=dict(cfg=cfg, seed=1000 + cfg if seed is None else seed),
+    )
+
+
+def to_f32(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
+    """Decode an input array (bf16 bits or float32) to float32."""
+    if a is None:
+        return None
+    return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)

@@ -1,0 +1,337 @@
+"""Pins for the CPU oracle: each test checks it against something other than itself.
+
+The pages print no worked numeric example for the scan, so the oracle is pinned by
+closed forms, library routines for special cases, brute-force formulations that share
+no loop structure with the recurrence, and invariants of the recurrence:
+
+  P1  A = 0: the state is a Delta*B*u-weighted prefix sum (numpy.cumsum); softplus via
+      numpy.logaddexp; the gate via scipy.special.expit.
+  P2  constant Delta, B, C (time-invariant): each state is a first-order IIR filter
+      (scipy.signal.lfilter); the impulse response is C . exp(Delta A)^t Delta B.
+  P3  tiny sizes: the materialised state and output from the pairwise decay form
+      h_t = sum_{s<=t} exp(A (S_t - S_s)) Delta_s B_s u_s with S the running sum of Delta.
+  P4  L = 1 closed form.
+  P5  decay underflow (Delta*A << 0): memoryless output.
+  P6  linearity in u; P7 causality; P8 channel-permutation equivariance;
+  P9  segment composition through the carried state.
+  P10 scalar decay per head: equals the per-channel oracle with A and Delta broadcast, and
+      the masked quadratic form Y = (M o C B^T)(Delta X) with M_ts = prod a.
+  P11 the study notes' one-step example (A = -1, N = 1) on a hand-derived case.
+  P12 the gate: z = 0 gives 0, large z gives y*z.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+import scipy.special
+
+import oracle
+from conftest import normwise
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_problem(rng, Bt=2, Dc=5, L=40, N=3, G=1, H=None, softplus=True, scalar=False,
+                 with_D=True, with_bias=True, with_z=False):
+    """A small float64 problem with general (random, not S4D) A."""
+    H = Dc if H is None else H
+    u = rng.standard_normal((Bt, Dc, L))
+    delta = rng.standard_normal((Bt, H, L)) * 0.7 - 1.0
+    if not softplus:
+        delta = rng.uniform(0.01, 0.5, (Bt, H, L))
+    B = rng.standard_normal((Bt, G, N, L))
+    C = rng.standard_normal((Bt, G, N, L))
+    A = -rng.uniform(0.1, 3.0, H) if scalar else -rng.uniform(0.1, 3.0, (Dc, N))
+    D = rng.standard_normal(H if scalar else Dc) if with_D else None
+    bias = rng.standard_normal(H) * 0.5 if with_bias else None
+    z = rng.standard_normal((Bt, Dc, L)) if with_z else None
+    return dict(u=u, delta=delta, A=A, B=B, C=C, D=D, z=z, delta_bias=bias, softplus=softplus)
+
+
+def run(p, **kw):
+    return oracle.scan_fwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"],
+                           p["delta_bias"], softplus=p["softplus"], **kw)
+
+
+def step_sizes(p):
+    """Delta per (b, head, t), with softplus taken from numpy.logaddexp (a library routine)."""
+    x = p["delta"] + (0.0 if p["delta_bias"] is None else p["delta_bias"][None, :, None])
+    return np.logaddexp(0.0, x) if p["softplus"] else x
+
+
+# ---------------------------------------------------------------- P1
+@pytest.mark.parametrize("gate", [False, True])
+def test_p1_zero_A_is_weighted_prefix_sum(gate):
+    rng = np.random.default_rng(1)
+    p = rand_problem(rng, Bt=2, Dc=4, L=50, N=3, G=1, with_z=gate)
+    p["A"] = np.zeros_like(p["A"])
+    y = run(p)
+    dt = step_sizes(p)  # [Bt, Dc, L]
+    # state_n(t) = cumsum_s dt_s * B_{s,n} * u_s
+    w = dt[:, :, None, :] * p["B"][:, :, :, :] * p["u"][:, :, None, :]  # [Bt, Dc, N, L] (G = 1)
+    h = np.cumsum(w, axis=-1)
+    ref = np.einsum("bdnl,bnl->bdl", h, p["C"][:, 0]) + p["D"][None, :, None] * p["u"]
+    if gate:
+        ref = ref * p["z"] * scipy.special.expit(p["z"])
+    assert normwise(y, ref) < 1e-12
+
+
+def test_p1_softplus_matches_logaddexp_over_wide_range():
+    # N = 1, A = 0, B = C = u = 1: y_t is the running sum of softplus(delta_t + bias).
+    x = np.concatenate([np.linspace(-40, 40, 161), [-700.0, -30.5, 0.0, 1e-8, 35.0, 700.0]])
+    L = x.size
+    delta = x.reshape(1, 1, L)
+    ones = np.ones((1, 1, 1, L))
+    y = oracle.scan_fwd(np.ones((1, 1, L)), delta, np.zeros((1, 1)), ones, ones, softplus=True)
+    sp = np.diff(np.concatenate([[0.0], y[0, 0]]))
+    ref = np.logaddexp(0.0, x)
+    # compare term by term (relative), the running sum only adds rounding
+    rel = np.abs(sp - ref) / np.maximum(np.abs(ref), 1e-300)
+    big = ref > 1e-12
+    assert np.all(rel[big] < 1e-9)
+
+
+# ---------------------------------------------------------------- P2
+def test_p2_time_invariant_is_iir_filter():
+    rng = np.random.default_rng(2)
+    Bt, Dc, L, N = 1, 3, 200, 4
+    dtc = rng.uniform(0.05, 0.3, Dc)
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    A = -rng.uniform(0.1, 2.0, (Dc, N))
+    u = rng.standard_normal((Bt, Dc, L))
+    D = rng.standard_normal(Dc)
+    delta = np.broadcast_to(dtc[None, :, None], (Bt, Dc, L)).copy()
+    B = np.broadcast_to(Bc[None, None, :, None], (Bt, 1, N, L)).copy()
+    C = np.broadcast_to(Cc[None, None, :, None], (Bt, 1, N, L)).copy()
+    y = oracle.scan_fwd(u, delta, A, B, C, D, softplus=False)
+    for d in range(Dc):
+        ref = D[d] * u[0, d]
+        for n in range(N):
+            hn = scipy.signal.lfilter([dtc[d] * Bc[n]], [1.0, -np.exp(dtc[d] * A[d, n])], u[0, d])
+            ref = ref + Cc[n] * hn
+        assert normwise(y[0, d], ref) < 1e-12
+
+
+def test_p2_impulse_response_closed_form():
+    rng = np.random.default_rng(3)
+    L, N = 120, 5
+    dtc = 0.17
+    A = -rng.uniform(0.1, 2.0, (1, N))
+    Bc = rng.standard_normal(N)
+    Cc = rng.standard_normal(N)
+    u = np.zeros((1, 1, L))
+    u[0, 0, 0] = 1.0
+    delta = np.full((1, 1, L), dtc)
+    B = np.broadcast_to(Bc[None, None, :, None], (1, 1, N, L)).copy()
+    C = np.broadcast_to(Cc[None, None, :, None], (1, 1, N, L)).copy()
+    y = oracle.scan_fwd(u, delta, A, B, C, softplus=False)[0, 0]
+    t = np.arange(L)[:, None]
+    ref = (Cc[None, :] * np.exp(t * dtc * A[0][None, :]) * dtc * Bc[None, :]).sum(axis=1)
+    assert normwise(y, ref) < 1e-13
+
+
+# ---------------------------------------------------------------- P3
+def pairwise_reference(p):
+    """Materialise h[b,d,n,t] from the pairwise decay form (O(L^2 N) per channel)."""
+    u, A, B, C = p["u"], p["A"], p["B"], p["C"]
+    Bt, Dc, L = u.shape
+    H = p["delta"].shape[1]
+    G, N = B.shape[1], B.shape[2]
+    dt = step_sizes(p)
+    scalar = A.ndim == 1
+    h = np.zeros((Bt, Dc, N, L))
+    y = np.zeros((Bt, Dc, L))
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(Bt):
+        for d in range(Dc):
+            hd = d // (Dc // H)
+            g = d // (Dc // G)
+            S = np.cumsum(dt[b, hd])
+            gap = S[:, None] - S[None, :]  # S_t - S_s
+            for n in range(N):
+                an = A[hd] if scalar else A[d, n]
+                M = np.where(causal, np.exp(np.where(causal, an * gap, 0.0)), 0.0)
+                h[b, d, n] = M @ (dt[b, hd] * B[b, g, n] * u[b, d])
+            y[b, d] = np.einsum("nl,nl->l", C[b, g], h[b, d])
+            if p["D"] is not None:
+                Dv = p["D"][hd] if p["D"].shape[0] == H and scalar else p["D"][d]
+                y[b, d] += Dv * u[b, d]
+    if p["z"] is not None:
+        y = y * p["z"] * scipy.special.expit(p["z"])
+    return y, h
+
+
+@pytest.mark.parametrize("G", [1, 2])
+@pytest.mark.parametrize("softplus", [True, False])
+def test_p3_matches_materialised_pairwise_form(G, softplus):
+    rng = np.random.default_rng(4 + G)
+    p = rand_problem(rng, Bt=2, Dc=4, L=33, N=3, G=G, softplus=softplus, with_z=True)
+    y, hf = run(p, return_state=True)
+    yref, h = pairwise_reference(p)
+    assert normwise(y, yref) < 1e-12
+    assert normwise(hf.reshape(2, 4, 3), h[..., -1]) < 1e-12
+
+
+def test_p3_row_selection_and_initial_state_zero():
+    rng = np.random.default_rng(6)
+    p = rand_problem(rng, Bt=2, Dc=4, L=20, N=2)
+    y = run(p)
+    rows = [7, 0, 5]
+    ys = run(p, rows=rows, h0=np.zeros((3, 2)))
+    for i, r in enumerate(rows):
+        assert np.array_equal(ys[i], y.reshape(8, 20)[r])
+
+
+# ---------------------------------------------------------------- P4
+def test_p4_single_step_closed_form():
+    rng = np.random.default_rng(7)
+    p = rand_problem(rng, Bt=1, Dc=3, L=1, N=4, with_z=True)
+    y = run(p)[0, :, 0]
+    dt = step_sizes(p)[0, :, 0]
+    Bv, Cv = p["B"][0, 0, :, 0], p["C"][0, 0, :, 0]
+    z = p["z"][0, :, 0]
+    ref = ((Cv * Bv).sum() * dt + p["D"]) * p["u"][0, :, 0] * z * scipy.special.expit(z)
+    assert normwise(y, ref) < 1e-14
+
+
+# ---------------------------------------------------------------- P5
+def test_p5_decay_underflow_is_memoryless():
+    rng = np.random.default_rng(8)
+    p = rand_problem(rng, Bt=1, Dc=3, L=30, N=4, softplus=False, with_bias=False)
+    p["delta"] = rng.uniform(0.1, 1.0, p["delta"].shape)
+    p["A"] = np.full_like(p["A"], -1e4)  # exp(dt*A) <= exp(-1000) == 0 in float64
+    y = run(p)
+    dt = p["delta"]
+    cb = (p["C"][:, 0] * p["B"][:, 0]).sum(axis=1)  # [Bt, L]
+    ref = (cb[:, None, :] * dt + p["D"][None, :, None]) * p["u"]
+    assert normwise(y, ref) < 1e-14
+
+
+# ---------------------------------------------------------------- P6-P9
+def test_p6_linear_in_u():
+    rng = np.random.default_rng(9)
+    p = rand_problem(rng, Bt=2, Dc=3, L=60, N=4)
+    v = rng.standard_normal(p["u"].shape)
+    alpha, beta = 1.7, -0.3
+    ya = run(p)
+    q = dict(p, u=v)
+    yb = run(q)
+    r = dict(p, u=alpha * p["u"] + beta * v)
+    assert normwise(run(r), alpha * ya + beta * yb) < 1e-12
+
+
+def test_p7_causal():
+    rng = np.random.default_rng(10)
+    p = rand_problem(rng, Bt=1, Dc=3, L=80, N=4, with_z=True)
+    y = run(p)
+    for t0 in (0, 1, 37, 79):
+        q = dict(p, u=p["u"].copy(), delta=p["delta"].copy(), z=p["z"].copy())
+        q["u"][..., t0] += 1.0
+        q["delta"][..., t0] -= 0.5
+        yq = run(q)
+        assert np.array_equal(yq[..., :t0], y[..., :t0])
+        assert not np.array_equal(yq[..., t0], y[..., t0])
+
+
+def test_p8_channel_permutation():
+    rng = np.random.default_rng(11)
+    p = rand_problem(rng, Bt=2, Dc=6, L=40, N=3, with_z=True)
+    perm = rng.permutation(6)
+    q = dict(p, u=p["u"][:, perm], delta=p["delta"][:, perm], z=p["z"][:, perm], A=p["A"][perm],
+             D=p["D"][perm], delta_bias=p["delta_bias"][perm])
+    assert np.array_equal(run(q), run(p)[:, perm])
+
+
+def test_p9_segment_composition():
+    rng = np.random.default_rng(12)
+    p = rand_problem(rng, Bt=2, Dc=3, L=90, N=5, with_z=True)
+    y, hf = run(p, return_state=True)
+    for T in (1, 31, 64, 89):
+        first = {k: (v[..., :T] if k in ("u", "delta", "z", "B", "C") else v) for k, v in p.items()}
+        second = {k: (v[..., T:] if k in ("u", "delta", "z", "B", "C") else v) for k, v in p.items()}
+        y1, h1 = run(first, return_state=True)
+        y2, h2 = run(second, h0=h1, return_state=True)
+        assert normwise(np.concatenate([y1, y2], axis=-1), y) < 1e-14
+        assert normwise(h2, hf) < 1e-14
+
+
+# ---------------------------------------------------------------- P10
+def test_p10_scalar_decay_equals_broadcast_per_channel():
+    rng = np.random.default_rng(13)
+    Hh, P, N = 3, 4, 6
+    p = rand_problem(rng, Bt=2, Dc=Hh * P, H=Hh, L=45, N=N, scalar=True)
+    y = run(p)
+    head = np.arange(Hh * P) // P
+    q = dict(p, delta=p["delta"][:, head], A=np.repeat(p["A"][head][:, None], N, axis=1),
+             D=p["D"][head], delta_bias=p["delta_bias"][head])
+    assert normwise(y, run(q)) < 1e-15
+
+
+def test_p10_scalar_decay_masked_quadratic_form():
+    """Y = (M o C B^T)(Delta X): M_ts = prod_{r=s+1..t} a_r = exp(A_h (S_t - S_s))."""
+    rng = np.random.default_rng(14)
+    Hh, P, N, L = 2, 3, 5, 30
+    p = rand_problem(rng, Bt=1, Dc=Hh * P, H=Hh, L=L, N=N, scalar=True)
+    y = run(p)
+    dt = step_sizes(p)[0]  # [H, L]
+    Bm, Cm = p["B"][0, 0].T, p["C"][0, 0].T  # [L, N]
+    CB = Cm @ Bm.T  # [t, s]
+    for h in range(Hh):
+        S = np.cumsum(dt[h])
+        M = np.tril(np.exp(np.tril(p["A"][h] * (S[:, None] - S[None, :]))))
+        X = p["u"][0, h * P:(h + 1) * P].T  # [L, P]
+        Y = (M * CB) @ (dt[h][:, None] * X) + p["D"][h] * X
+        assert normwise(y[0, h * P:(h + 1) * P].T, Y) < 1e-12
+
+
+# ---------------------------------------------------------------- P11 / golden
+def test_p11_golden_halving_decay():
+    with open(os.path.join(GOLDEN, "halving_decay.json")) as f:
+        g = json.load(f)
+    L = len(g["u"])
+    u = np.array(g["u"], dtype=np.float64).reshape(1, 1, L)
+    delta = np.full((1, 1, L), g["delta"])
+    B = np.full((1, 1, 1, L), g["B"])
+    C = np.full((1, 1, 1, L), g["C"])
+    y = oracle.scan_fwd(u, delta, np.array([[g["A"]]]), B, C, softplus=False)[0, 0]
+    assert normwise(y, np.array(g["y"])) < 1e-15
+
+
+def test_golden_single_step():
+    with open(os.path.join(GOLDEN, "single_step.json")) as f:
+        g = json.load(f)
+    N = len(g["B"])
+    y = oracle.scan_fwd(np.array(g["u"]).reshape(1, 1, 1), np.array(g["delta"]).reshape(1, 1, 1),
+                        np.array(g["A"]).reshape(1, N), np.array(g["B"]).reshape(1, 1, N, 1),
+                        np.array(g["C"]).reshape(1, 1, N, 1), np.array([g["D"]]),
+                        np.array(g["z"]).reshape(1, 1, 1), softplus=False)
+    assert abs(y[0, 0, 0] - g["y"]) <= 1e-15 * abs(g["y"])
+
+
+# ---------------------------------------------------------------- P12
+def test_p12_gate():
+    rng = np.random.default_rng(15)
+    p = rand_problem(rng, Bt=1, Dc=3, L=25, N=3)
+    y0 = run(p)
+    zero = run(dict(p, z=np.zeros_like(p["u"])))
+    assert np.all(zero == 0.0)
+    big = run(dict(p, z=np.full_like(p["u"], 40.0)))
+    assert normwise(big, 40.0 * y0) < 1e-15
+    z = rng.standard_normal(p["u"].shape) * 3
+    assert normwise(run(dict(p, z=z)), y0 * z * scipy.special.expit(z)) < 1e-14
+
+
+# ---------------------------------------------------------------- dtypes
+def test_bf16_bits_decode_like_torch():
+    torch = pytest.importorskip("torch")
+    from selective_state_space_88_amd import inputs
+
+    p = inputs.make(1, batch=1, channels=8, length=64)
+    dec = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).float().numpy()
+    y_bits = oracle.scan_problem(p)
+    y_f32 = oracle.scan_fwd(dec(p.u), dec(p.delta), p.A, dec(p.B), dec(p.C), p.D, dec(p.z),
+                            p.delta_bias)
+    assert np.array_equal(y_bits, y_f32)
