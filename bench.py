@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Selective-scan forward benchmark on one MI355X.
+
+One step = one ss_scan_fwd call over the whole Mamba-130M-like layer (batch 8, 1536 channels,
+L 2048, N 16; bf16 u/delta/z/B/C, f32 A/D/delta_bias, softplus and silu gate on, y in f32),
+inputs resident in HBM.  Prints one JSON line:
+
+  value         elements (batch*channels*L) per second over the K timed steps
+  roofline      the scan kernel against the VALU (ALU) ceiling, and its HBM rate
+  cpu_baseline  the CPU oracle (float64, all host cores) on the same workload
+
+Usage: python bench.py [--steps K] [--warmup W] [--workload 0-4] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 GPU"
+
+# MI355X published peaks
+HBM_PEAK_GBPS = 8000.0
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 128 FP32 FMA lanes/clk x 2 FLOP x 2.4 GHz
+
+# Work model (per element = one (b, d, t)); see DESIGN.md "Roofline model".
+# A transcendental (v_exp/v_log/v_rcp) issues at a quarter of the FMA rate on gfx950, so it
+# is counted as 8 FLOP-equivalents (4 FMA issue slots).
+TRANS = 8.0
+
+
+def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
+    if scalar_decay:
+        # per (t, p, n): dt*u*B multiply 1, state FMA 2, readout FMA 2; the decay exp is per head
+        per = 5.0 * N + (TRANS + 1.0) / P
+    else:
+        # per (t, n): exp 8, dt*A 1, (dt*u)*B 1, state FMA 2, readout FMA 2
+        per = 14.0 * N
+    per += 1.0 + 2.0  # dt*u, D*u FMA
+    if softplus:
+        per += 2 * TRANS + 4.0  # exp, log1p, bias add, max, adds
+    if gate:
+        per += 2 * TRANS + 3.0  # exp, reciprocal, add, two multiplies
+    return per
+
+
+def algorithmic_bytes(p, y_bytes):
+    ib = 2 if p.in_dtype == "bf16" else 4
+    E = p.batch * p.channels * p.length
+    n = E * ib + E * y_bytes                      # u, y
+    n += p.batch * p.heads * p.length * ib        # delta
+    if p.gate:
+        n += E * ib                               # z
+    n += 2 * p.batch * p.groups * p.nstate * p.length * ib  # B, C
+    n += p.A.size * 4 + (p.D.size * 4 if p.D is not None else 0)
+    n += p.delta_bias.size * 4 if p.delta_bias is not None else 0
+    return n
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan's rows are independent, so more GPUs would "
+              "each run the same kernel on their own share; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_88_amd import inputs
+    from selective_state_space_88_amd.scan import scan_fwd
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    p = inputs.make(args.workload)
+
+    def to_dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    y = torch.empty(p.u.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
+                 softplus=p.softplus, y=y, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K back-to-back steps, bracketed by device synchronisation
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_launch_s = float(np.mean(launch_ms)) * 1e-3
+
+    E = p.batch * p.channels * p.length
+    value = E * K / wall
+    nbytes = algorithmic_bytes(p, 4)
+    flops = E * flop_equiv_per_element(p.nstate, p.softplus, p.gate, p.scalar_decay,
+                                       P=p.channels // p.heads)
+    alu_tflops = flops / avg_launch_s / 1e12
+    hbm_gbps = nbytes / avg_launch_s / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "elems/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": p.name + ": bf16 u/delta/z/B/C, f32 A/D/delta_bias, softplus + silu gate, "
+                        "y f32" if args.workload != 0 else p.name,
+            "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
+            "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
+            "kernel": "scalar_fwd_kernel" if p.scalar_decay else "diag_fwd_kernel",
+        },
+        "roofline": {
+            "bound": "alu",
+            "achieved": alu_tflops,
+            "peak": FP32_VECTOR_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "traffic": None,
+            "launch_ms": avg_launch_s * 1e3,
+            "flop_equiv_per_launch": flops,
+            "hbm_algorithmic_bytes_per_launch": nbytes,
+            "hbm_achieved_GBps": hbm_gbps,
+            "hbm_frac": hbm_gbps / HBM_PEAK_GBPS,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = oracle.default_threads()
+        # bounded sample: the whole workload when it is small, else a prefix of its rows
+        total_rows = p.batch * p.channels
+        budget = 2.0e9  # state-steps (t, n) per repeat: a few seconds on a few dozen cores
+        nrows = int(min(total_rows, max(1, budget // (p.length * p.nstate))))
+        rows = np.arange(nrows, dtype=np.int64) if nrows < total_rows else None
+        best = None
+        for _ in range(max(1, args.cpu_repeats)):
+            c0 = time.perf_counter()
+            oracle.scan_problem(p, rows=rows, threads=cores)
+            dt = time.perf_counter() - c0
+            best = dt if best is None else min(best, dt)
+        out["cpu_baseline"] = {
+            "value": nrows * p.length / best,
+            "unit": "elems/s",
+            "cores": cores,
+            "kind": "oracle",
+            "sample": "%s rows of %d (each L=%d, N=%d) of the same workload, best of %d runs, "
+                      "float64 sequential recurrence, %d threads"
+                      % ("all" if rows is None else str(nrows), total_rows, p.length, p.nstate,
+                         max(1, args.cpu_repeats), cores),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

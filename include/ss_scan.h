@@ -1,0 +1,118 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan forward library (libssscan.so).
+ *
+ * The operation is the S6 selective-scan forward.  For batch b, channel d and time t:
+ *
+ *   dt_t  = softplus(delta[b, hd, t] + delta_bias[hd])   if SS_DELTA_SOFTPLUS, else delta + bias
+ *   h_t   = exp(dt_t * A) (.) h_{t-1} + dt_t * B[b, g, :, t] * u[b, d, t]        h_{-1} = 0
+ *   y_t   = C[b, g, :, t] . h_t + D * u[b, d, t]
+ *   y_t  *= silu(z[b, d, t]) = z / (1 + exp(-z))          if SS_Z_GATE_SILU
+ *
+ * hd = d / (channels / heads) is the head of channel d (hd = d when delta is per channel) and
+ * g = d / (channels / groups) the B/C group.  The state h has N entries per channel; with a
+ * per-channel A [channels, N] the decay is diagonal (Mamba-1), with A [heads] it is one scalar
+ * per head shared by all N states (Mamba-2 style scalar decay).
+ *
+ * Where this is defined (pages of the method's description):
+ *  - the recurrence h_t = Abar_t h_{t-1} + Bbar_t x_t, y_t = C_t h_t, and the input-dependent
+ *    B_t, C_t and Delta_t = softplus(Linear(x_t)): omica.com.cn Mamba explainer (news 823493),
+ *    sections 3 and 5; the bqwf.cn state-space survey (news 437117), sections 2.1 and 2.2;
+ *  - Abar = exp(Delta A), Bbar = Delta B (exponential-Euler; explainer section 6.3) and the one-step
+ *    pseudocode h_t = exp(-Delta) h_{t-1} + Delta B x_t in the "Mamba -- selective state space
+ *    model" study notes (estelledc.github.io), case 1;
+ *  - the D feed-through: explainer section 3 (output equation);
+ *  - scalar decay A_t = alpha_t I with heads: survey section 3.2; explainer section 6.2;
+ *  - the gate after the selective SSM: juejin.cn post on Mamba's history, section 2 (the pages
+ *    give no formula; silu(z) = z * sigmoid(z) is the reading taken);
+ *  - one SISO system per channel (channels independent): explainer section 6.3.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor data pointers are DEVICE pointers owned by the caller.  The library only
+ *    borrows them until the enqueued work completes; it never frees or retains them.
+ *  - Strides are in elements.  The innermost (time / last) stride of every time-major tensor
+ *    must be 1; outer strides are free (non-negative).
+ *  - Every argument is validated on the host before anything is enqueued.  On any error the
+ *    call returns a negative SS_ERR_* code, enqueues nothing and leaves y untouched.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
+ *    stream).  Kernel execution errors surface at stream synchronisation or via ss_check().
+ *  - Calls on different streams may run concurrently; the library keeps no per-call global state.
+ *  - Results are deterministic: the same inputs give bitwise the same y on every run.
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SS_VERSION 100 /* 1.0.0 */
+
+typedef enum { SS_F32 = 0, SS_BF16 = 1 } ss_dtype;
+
+/* A strided view of caller-owned device memory. */
+typedef struct {
+  void* data;        /* device pointer (may be NULL only for an optional, absent tensor) */
+  int32_t dtype;     /* ss_dtype */
+  int32_t ndim;      /* 1..4 */
+  int64_t shape[4];  /* sizes, outermost first */
+  int64_t stride[4]; /* in elements */
+} ss_tensor;
+
+/* flags */
+#define SS_DELTA_SOFTPLUS (1u << 0) /* dt = softplus(delta + delta_bias) */
+#define SS_Z_GATE_SILU (1u << 1)    /* y *= silu(z); requires z */
+
+/* return codes */
+#define SS_OK 0
+#define SS_ERR_NULL (-1)        /* a required tensor or data pointer is NULL */
+#define SS_ERR_DTYPE (-2)       /* unsupported dtype or dtype mix */
+#define SS_ERR_SHAPE (-3)       /* inconsistent shapes */
+#define SS_ERR_STRIDE (-4)      /* innermost stride != 1, or a negative stride */
+#define SS_ERR_FLAGS (-5)       /* unknown flag bits, or SS_Z_GATE_SILU without z */
+#define SS_ERR_UNSUPPORTED (-6) /* valid but unsupported size (N > 128, or > 2^31 steps per row) */
+#define SS_ERR_ALIAS (-7)       /* y overlaps an input */
+#define SS_ERR_HIP (-8)         /* a HIP runtime call failed (launch, workspace allocation) */
+
+/*
+ * ss_scan_fwd -- selective-scan forward, y = S6(u, delta, A, B, C, D, z, delta_bias).
+ *
+ *   u          [batch, channels, L]          f32 | bf16
+ *   delta      [batch, heads, L]             same dtype as u; heads divides channels
+ *   A          [channels, N] f32  (diagonal decay per channel), or
+ *              [heads] f32        (one scalar decay per head, shared by its N states)
+ *   B, C       [batch, groups, N, L]         same dtype as u; groups divides channels
+ *   D          [channels] or [heads] f32     optional (NULL or data == NULL): no feed-through
+ *   z          [batch, channels, L]          same dtype as u; optional, required by SS_Z_GATE_SILU
+ *   delta_bias [heads] f32                   optional: no bias
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU
+ *   y          [batch, channels, L]          f32 | bf16, written; must not overlap any input
+ *   stream     hipStream_t (as void*), NULL for the default stream
+ *
+ * N must be 1..128.  L = 0 or batch * channels = 0 is a successful no-op.  The state starts at
+ * zero for every (b, d).  Internally the computation is in f32 (bf16 inputs are widened exactly);
+ * y in bf16 is rounded to nearest even once.  Scalar-decay calls use a stream-ordered device
+ * workspace of batch * groups * L * 16 * ceil(N / 16) floats, allocated and freed on `stream`
+ * (SS_ERR_HIP if that allocation fails).
+ *
+ * Returns SS_OK or a negative SS_ERR_* code.
+ */
+int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream);
+
+/* Synchronises `stream` and returns SS_OK, or SS_ERR_HIP if any enqueued work failed. */
+int ss_check(void* stream);
+
+/* Static, NUL-terminated description of a return code (never NULL). */
+const char* ss_strerror(int code);
+
+/* SS_VERSION of the built library. */
+int ss_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

@@ -1,0 +1,46 @@
+"""Build libssscan.so (the gfx950 HIP kernels and their C ABI) in-tree with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libssscan.so")
+SOURCES = ["ss_api.hip", "ss_diag.hip", "ss_scalar.hip"]
+ARCH = "gfx950"
+
+FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    # packed FP32 (v_pk_*_f32) stays off: plain f32 VALU code only
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + os.path.join(ROOT, "include"),
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the HIP library cannot be built")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 into selective_state_space_88_amd/libssscan.so."""
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc()] + FLAGS + ["-o", tmp] + srcs
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    if verbose:
+        print(" ".join(cmd))
+        print(res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

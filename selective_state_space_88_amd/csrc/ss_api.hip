@@ -1,0 +1,188 @@
+// ss_api.hip -- C ABI of libssscan.so: validation, dispatch, workspace.  See include/ss_scan.h.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/ss_scan.h"
+#include "ss_launch.h"
+
+namespace {
+
+bool present(const ss_tensor* t) { return t != nullptr && t->data != nullptr; }
+
+int64_t esize(int32_t dt) { return dt == SS_BF16 ? 2 : 4; }
+
+// Byte extent [lo, hi) touched by a strided tensor (strides non-negative, checked first).
+void extent(const ss_tensor* t, uintptr_t* lo, uintptr_t* hi) {
+  int64_t last = 0;
+  for (int i = 0; i < t->ndim; ++i) last += (t->shape[i] - 1) * t->stride[i];
+  *lo = reinterpret_cast<uintptr_t>(t->data);
+  *hi = *lo + (uintptr_t)((last + 1) * esize(t->dtype));
+}
+
+int64_t numel(const ss_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+int check_basic(const ss_tensor* t, int ndim) {
+  if (t->ndim != ndim) return SS_ERR_SHAPE;
+  if (t->dtype != SS_F32 && t->dtype != SS_BF16) return SS_ERR_DTYPE;
+  for (int i = 0; i < ndim; ++i) {
+    if (t->shape[i] < 0) return SS_ERR_SHAPE;
+    if (t->stride[i] < 0) return SS_ERR_STRIDE;
+  }
+  if (t->stride[ndim - 1] != 1 && t->shape[ndim - 1] > 1) return SS_ERR_STRIDE;
+  return SS_OK;
+}
+
+bool aligned16(const ss_tensor* t) {
+  if (reinterpret_cast<uintptr_t>(t->data) % 16) return false;
+  const int64_t es = esize(t->dtype);
+  for (int i = 0; i + 1 < t->ndim; ++i)
+    if (t->shape[i] > 1 && (t->stride[i] * es) % 16) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_version(void) { return SS_VERSION; }
+
+const char* ss_strerror(int code) {
+  switch (code) {
+    case SS_OK: return "ok";
+    case SS_ERR_NULL: return "a required tensor or data pointer is NULL";
+    case SS_ERR_DTYPE: return "unsupported dtype or dtype mix";
+    case SS_ERR_SHAPE: return "inconsistent tensor shapes";
+    case SS_ERR_STRIDE: return "innermost stride must be 1 and strides non-negative";
+    case SS_ERR_FLAGS: return "unknown flag bits, or SS_Z_GATE_SILU without z";
+    case SS_ERR_UNSUPPORTED: return "unsupported size (N must be 1..128; at most 2^31 steps per row)";
+    case SS_ERR_ALIAS: return "y overlaps an input";
+    case SS_ERR_HIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+int ss_check(void* stream) {
+  if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SS_ERR_HIP;
+  if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
+  return SS_OK;
+}
+
+int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream) {
+  if (!u || !delta || !A || !B || !C || !y) return SS_ERR_NULL;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU)) return SS_ERR_FLAGS;
+  const bool gate = (flags & SS_Z_GATE_SILU) != 0;
+  if (gate && !present(z)) return SS_ERR_FLAGS;
+  if (!gate && present(z)) return SS_ERR_FLAGS;
+  int rc;
+  if ((rc = check_basic(u, 3)) || (rc = check_basic(delta, 3)) || (rc = check_basic(B, 4)) ||
+      (rc = check_basic(C, 4)) || (rc = check_basic(y, 3)))
+    return rc;
+  if (A->ndim != 1 && A->ndim != 2) return SS_ERR_SHAPE;
+  if ((rc = check_basic(A, A->ndim))) return rc;
+  if (gate && (rc = check_basic(z, 3))) return rc;
+  if (present(D) && (rc = check_basic(D, 1))) return rc;
+  if (present(delta_bias) && (rc = check_basic(delta_bias, 1))) return rc;
+
+  // dtypes: u, delta, B, C, z agree; A, D, bias are f32; y is f32 or bf16
+  const int32_t idt = u->dtype;
+  if (delta->dtype != idt || B->dtype != idt || C->dtype != idt || (gate && z->dtype != idt))
+    return SS_ERR_DTYPE;
+  if (A->dtype != SS_F32 || (present(D) && D->dtype != SS_F32) ||
+      (present(delta_bias) && delta_bias->dtype != SS_F32))
+    return SS_ERR_DTYPE;
+
+  const int64_t Bt = u->shape[0], Dc = u->shape[1], L = u->shape[2];
+  const int64_t H = delta->shape[1], G = B->shape[1], N = B->shape[2];
+  if (delta->shape[0] != Bt || delta->shape[2] != L) return SS_ERR_SHAPE;
+  if (B->shape[0] != Bt || B->shape[3] != L) return SS_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i)
+    if (C->shape[i] != B->shape[i]) return SS_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (y->shape[i] != u->shape[i] || (gate && z->shape[i] != u->shape[i])) return SS_ERR_SHAPE;
+  if (H <= 0 || G <= 0 || (Dc > 0 && (Dc % H || Dc % G))) return SS_ERR_SHAPE;
+  const bool scalar = A->ndim == 1;
+  if (scalar ? A->shape[0] != H : (A->shape[0] != Dc || A->shape[1] != N)) return SS_ERR_SHAPE;
+  if (present(D) && D->shape[0] != Dc && D->shape[0] != H) return SS_ERR_SHAPE;
+  if (present(delta_bias) && delta_bias->shape[0] != H) return SS_ERR_SHAPE;
+  if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
+  if (L > ((int64_t)1 << 31)) return SS_ERR_UNSUPPORTED;
+  if (L == 0 || Bt * Dc == 0) return SS_OK;  // nothing to compute
+  if (!u->data || !delta->data || !A->data || !B->data || !C->data || !y->data) return SS_ERR_NULL;
+  if (scalar && G > 1 && (Dc / G) % 64) return SS_ERR_UNSUPPORTED;
+
+  // y must not overlap any input
+  uintptr_t ylo, yhi;
+  extent(y, &ylo, &yhi);
+  const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias};
+  for (const ss_tensor* t : ins) {
+    if (!present(t) || numel(t) == 0) continue;
+    uintptr_t lo, hi;
+    extent(t, &lo, &hi);
+    if (lo < yhi && ylo < hi) return SS_ERR_ALIAS;
+  }
+
+  ss::ScanArgs a{};
+  a.u = u->data;
+  a.delta = delta->data;
+  a.B = B->data;
+  a.C = C->data;
+  a.z = gate ? z->data : nullptr;
+  a.A = static_cast<const float*>(A->data);
+  a.D = present(D) ? static_cast<const float*>(D->data) : nullptr;
+  a.bias = present(delta_bias) ? static_cast<const float*>(delta_bias->data) : nullptr;
+  a.y = y->data;
+  a.batch = Bt;
+  a.channels = Dc;
+  a.L = L;
+  a.N = (int32_t)N;
+  a.heads = (int32_t)H;
+  a.groups = (int32_t)G;
+  a.chan_per_head = (int32_t)(Dc / H);
+  a.chan_per_group = (int32_t)(Dc / G);
+  a.d_per_head = present(D) && D->shape[0] != Dc ? 1 : 0;
+  a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
+  a.in_bf16 = idt == SS_BF16;
+  a.out_bf16 = y->dtype == SS_BF16;
+  a.vec = aligned16(u) && aligned16(delta) && aligned16(B) && aligned16(C) && aligned16(y) &&
+          (!gate || aligned16(z));
+  a.u_sb = u->stride[0];
+  a.u_sd = u->stride[1];
+  a.dl_sb = delta->stride[0];
+  a.dl_sh = delta->stride[1];
+  a.z_sb = gate ? z->stride[0] : 0;
+  a.z_sd = gate ? z->stride[1] : 0;
+  a.B_sb = B->stride[0];
+  a.B_sg = B->stride[1];
+  a.B_sn = B->stride[2];
+  a.C_sb = C->stride[0];
+  a.C_sg = C->stride[1];
+  a.C_sn = C->stride[2];
+  a.y_sb = y->stride[0];
+  a.y_sd = y->stride[1];
+  a.A_sd = scalar ? 0 : A->stride[0];
+  if (present(D) && D->stride[0] != 1 && D->shape[0] > 1) return SS_ERR_STRIDE;
+  if (present(delta_bias) && delta_bias->stride[0] != 1 && delta_bias->shape[0] > 1) return SS_ERR_STRIDE;
+  if (scalar && A->stride[0] != 1 && A->shape[0] > 1) return SS_ERR_STRIDE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!scalar) return ss::launch_diag(a, s) == hipSuccess ? SS_OK : SS_ERR_HIP;
+
+  float* ws = nullptr;
+  const size_t bytes = (size_t)ss::scalar_workspace_floats(a) * sizeof(float);
+  if (hipMallocAsync(reinterpret_cast<void**>(&ws), bytes, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return SS_ERR_HIP;
+  }
+  const hipError_t e = ss::launch_scalar(a, ws, s);
+  const hipError_t f = hipFreeAsync(ws, s);
+  return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// ss_device.h -- device helpers shared by the gfx950 selective-scan kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Read-only memory seen through the constant address space: wave-uniform loads from it are
+// selected as scalar (SMEM) loads.  Only for data no kernel writes while the reader runs.
+typedef const __attribute__((address_space(4))) float cfloat;
+__device__ __forceinline__ cfloat* to_constant(const float* p) { return (cfloat*)(p); }
+
+// bf16 is carried as its raw 16 bits; widening to f32 is exact (the bits are the high half).
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+
+// f32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Load K consecutive elements p[t0 .. t0+K) as f32; elements at t >= L read as 0.
+// `vec` promises that p is 16-byte aligned at every multiple-of-8 (bf16) / 4 (f32) offset,
+// and t0 is a multiple of K.
+template <int K>
+__device__ __forceinline__ void load_seg(const bf16_t* __restrict__ p, int64_t t0, int64_t L,
+                                         bool vec, float (&out)[K]) {
+  static_assert(K % 8 == 0, "K must be a multiple of 8");
+  if (vec && t0 + K <= L) {
+    const u32x4* q = reinterpret_cast<const u32x4*>(p + t0);
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      const u32x4 v = __builtin_nontemporal_load(q + i);
+      out[8 * i + 0] = bf16_lo(v.x);
+      out[8 * i + 1] = bf16_hi(v.x);
+      out[8 * i + 2] = bf16_lo(v.y);
+      out[8 * i + 3] = bf16_hi(v.y);
+      out[8 * i + 4] = bf16_lo(v.z);
+      out[8 * i + 5] = bf16_hi(v.z);
+      out[8 * i + 6] = bf16_lo(v.w);
+      out[8 * i + 7] = bf16_hi(v.w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) out[j] = (t0 + j < L) ? to_f32(p[t0 + j]) : 0.f;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void load_seg(const float* __restrict__ p, int64_t t0, int64_t L,
+                                         bool vec, float (&out)[K]) {
+  static_assert(K % 4 == 0, "K must be a multiple of 4");
+  if (vec && t0 + K <= L) {
+    const f32x4* q = reinterpret_cast<const f32x4*>(p + t0);
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      const f32x4 v = __builtin_nontemporal_load(q + i);
+      out[4 * i + 0] = v.x;
+      out[4 * i + 1] = v.y;
+      out[4 * i + 2] = v.z;
+      out[4 * i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j) out[j] = (t0 + j < L) ? p[t0 + j] : 0.f;
+  }
+}
+
+// Store K consecutive values to p[t0 .. t0+K), skipping t >= L.
+template <int K>
+__device__ __forceinline__ void store_seg(float* __restrict__ p, int64_t t0, int64_t L, bool vec,
+                                          const float (&v)[K]) {
+  if (vec && t0 + K <= L) {
+    f32x4* q = reinterpret_cast<f32x4*>(p + t0);
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      f32x4 w = {v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]};
+      __builtin_nontemporal_store(w, q + i);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (t0 + j < L) p[t0 + j] = v[j];
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void store_seg(bf16_t* __restrict__ p, int64_t t0, int64_t L, bool vec,
+                                          const float (&v)[K]) {
+  if (vec && t0 + K <= L) {
+    u32x4* q = reinterpret_cast<u32x4*>(p + t0);
+#pragma unroll
+    for (int i = 0; i < K / 8; ++i) {
+      u32x4 w;
+      w.x = f32_to_bf16_bits(v[8 * i + 0]) | (f32_to_bf16_bits(v[8 * i + 1]) << 16);
+      w.y = f32_to_bf16_bits(v[8 * i + 2]) | (f32_to_bf16_bits(v[8 * i + 3]) << 16);
+      w.z = f32_to_bf16_bits(v[8 * i + 4]) | (f32_to_bf16_bits(v[8 * i + 5]) << 16);
+      w.w = f32_to_bf16_bits(v[8 * i + 6]) | (f32_to_bf16_bits(v[8 * i + 7]) << 16);
+      __builtin_nontemporal_store(w, q + i);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      if (t0 + j < L) p[t0 + j].bits = (uint16_t)f32_to_bf16_bits(v[j]);
+  }
+}
+
+__device__ __forceinline__ void store_one(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_one(bf16_t* p, float v) { p->bits = (uint16_t)f32_to_bf16_bits(v); }
+
+// softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(e^-|x|) so that it neither
+// overflows for large x nor loses the small result for very negative x.
+__device__ __forceinline__ float softplus_f32(float x) {
+  return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x)));
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z)
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.f + __expf(-z)); }
+
+__device__ __forceinline__ float readlane_f(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// DPP move within a row of 16 lanes; lanes whose source is outside the row are fixed up
+// by the caller (their value here is unspecified).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+}  // namespace ss

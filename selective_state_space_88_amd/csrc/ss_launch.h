@@ -1,0 +1,40 @@
+// ss_launch.h -- internal interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+// Arguments of one scan, already validated.  Strides are in elements; the time stride is 1.
+struct ScanArgs {
+  const void* u;
+  const void* delta;
+  const void* B;
+  const void* C;
+  const void* z;          // nullptr: no gate
+  const float* A;         // [channels, N] (diagonal) or [heads] (scalar decay)
+  const float* D;         // nullable
+  const float* bias;      // nullable, [heads]
+  void* y;
+  int64_t batch, channels, L;
+  int32_t N, heads, groups;
+  int32_t chan_per_head, chan_per_group;
+  int32_t d_per_head;     // D indexed by head
+  int32_t softplus;
+  int32_t in_bf16, out_bf16;
+  int32_t vec;            // every time row is 16-byte aligned (vector loads / stores allowed)
+  int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd;
+  int64_t B_sb, B_sg, B_sn, C_sb, C_sg, C_sn;
+  int64_t y_sb, y_sd, A_sd;
+};
+
+// Diagonal decay A [channels, N]: one wave per (b, d) row, lanes along time.
+hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
+
+// Scalar decay A [heads]: lanes along channels, 16 states per wave.  `ws` must hold
+// scalar_workspace_floats(a) floats of device memory, ordered on `stream`.
+int64_t scalar_workspace_floats(const ScanArgs& a);
+hipError_t launch_scalar(const ScanArgs& a, float* ws, hipStream_t stream);
+
+}  // namespace ss

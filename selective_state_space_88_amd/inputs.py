@@ -179,3 +179,39 @@ def to_f32(a: Optional[np.ndarray]) -> Optional[np.ndarray]:
     if a is None:
         return None
     return bf16_bits_to_f32(a) if a.dtype == np.uint16 else np.asarray(a, dtype=np.float32)
+
+
+def random_problem(seed: int, batch: int, channels: int, length: int, nstate: int, *,
+                   heads: Optional[int] = None, groups: int = 1, scalar_decay: bool = False,
+                   in_dtype: str = "bf16", gate: bool = True, with_D: bool = True,
+                   with_bias: bool = True, softplus: bool = True,
+                   dt: tuple = (1e-3, 1e-1), bc_scale: float = 1.0) -> Problem:
+    """A general problem for edge cases: per-channel random A (not S4D), any heads/groups.
+
+    u, delta_raw, z, B, C ~ N(0,1) (B, C times bc_scale); A[d, n] ~ -U(0.5, 4) (or A[h] per
+    head when scalar_decay); D ~ N(0,1); delta_bias = inv_softplus(dt), dt log-uniform in ``dt``.
+    With softplus off the raw steps are U(0.001, 0.3) and no bias is drawn.
+    """
+    H = channels if heads is None else heads
+    rng = np.random.default_rng(seed)
+    Bt, Dc, L, N, G = batch, channels, length, nstate, groups
+    u = _normal(rng, (Bt, Dc, L), 1.0, in_dtype)
+    if softplus:
+        delta = _normal(rng, (Bt, H, L), 1.0, in_dtype)
+    else:
+        raw = rng.uniform(0.001, 0.3, size=(Bt, H, L)).astype(np.float32)
+        delta = f32_to_bf16_bits(raw).reshape(raw.shape) if in_dtype == "bf16" else raw
+    z = _normal(rng, (Bt, Dc, L), 1.0, in_dtype) if gate else None
+    B = _normal(rng, (Bt, G, N, L), bc_scale, in_dtype)
+    C = _normal(rng, (Bt, G, N, L), bc_scale, in_dtype)
+    dts = np.exp(rng.uniform(np.log(dt[0]), np.log(dt[1]), size=H))
+    bias = np.log(np.expm1(dts)).astype(np.float32) if (with_bias and softplus) else None
+    Dv = rng.standard_normal(H if scalar_decay else Dc, dtype=np.float32) if with_D else None
+    if scalar_decay:
+        A = (-rng.uniform(0.5, 4.0, size=H)).astype(np.float32)
+    else:
+        A = (-rng.uniform(0.5, 4.0, size=(Dc, N))).astype(np.float32)
+    return Problem(name="random", batch=Bt, channels=Dc, length=L, nstate=N, groups=G, heads=H,
+                   in_dtype=in_dtype, u=u, delta=delta, A=A, B=B, C=C, D=Dv, z=z,
+                   delta_bias=bias, softplus=softplus, scalar_decay=scalar_decay,
+                   meta=dict(seed=seed))

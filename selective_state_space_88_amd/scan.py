@@ -1,0 +1,122 @@
+"""Python binding of libssscan.so (argument marshalling only; every step runs in the HIP kernels).
+
+PyTorch supplies device memory and the stream.  Tensors are passed to the C ABI as
+(pointer, dtype, shape, strides) descriptors; nothing is computed on the host and there is
+no fallback: if the library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libssscan.so")
+
+SS_F32, SS_BF16 = 0, 1
+SS_DELTA_SOFTPLUS = 1 << 0
+SS_Z_GATE_SILU = 1 << 1
+EXPORTS = ("ss_scan_fwd", "ss_check", "ss_strerror", "ss_version")
+
+
+class SSTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class ScanError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("ss_scan_fwd failed (%d): %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libssscan.so (built in-tree by build.py); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libssscan.so is not built (run selective_state_space_88_amd/build.py)")
+        l = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER(SSTensor)
+        l.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, ctypes.c_void_p]
+        l.ss_scan_fwd.restype = ctypes.c_int
+        l.ss_check.argtypes = [ctypes.c_void_p]
+        l.ss_check.restype = ctypes.c_int
+        l.ss_strerror.argtypes = [ctypes.c_int]
+        l.ss_strerror.restype = ctypes.c_char_p
+        l.ss_version.argtypes = []
+        l.ss_version.restype = ctypes.c_int
+        _lib = l
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().ss_strerror(code).decode()
+
+
+def version() -> int:
+    return lib().ss_version()
+
+
+def describe(t: Optional[torch.Tensor]) -> Optional[SSTensor]:
+    """ss_tensor descriptor of a torch tensor (no copy).  None stays None."""
+    if t is None:
+        return None
+    if t.dtype == torch.float32:
+        code = SS_F32
+    elif t.dtype == torch.bfloat16:
+        code = SS_BF16
+    else:
+        raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+    if t.dim() < 1 or t.dim() > 4:
+        raise ValueError("tensors must have 1 to 4 dimensions")
+    d = SSTensor()
+    d.data = t.data_ptr() if t.numel() else 0
+    d.dtype = code
+    d.ndim = t.dim()
+    for i, (n, s) in enumerate(zip(t.shape, t.stride())):
+        d.shape[i] = n
+        d.stride[i] = s
+    return d
+
+
+def _ref(d: Optional[SSTensor]):
+    return ctypes.byref(d) if d is not None else None
+
+
+def call(u, delta, A, B, C, D, z, delta_bias, flags: int, y, stream) -> int:
+    """Raw call with descriptors (or None); returns the library's code."""
+    return lib().ss_scan_fwd(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+                             _ref(delta_bias), ctypes.c_uint32(flags), _ref(y),
+                             ctypes.c_void_p(stream or 0))
+
+
+def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+             C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, *, softplus: bool = True,
+             y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+             stream: Optional[int] = None) -> torch.Tensor:
+    """Selective-scan forward on the GPU through ss_scan_fwd (see include/ss_scan.h).
+
+    u, z: [batch, channels, L]; delta: [batch, heads, L]; A: [channels, N] (diagonal) or
+    [heads] (scalar decay); B, C: [batch, groups, N, L]; D: [channels] or [heads];
+    delta_bias: [heads].  Returns y [batch, channels, L] (float32 unless out_dtype/y say so).
+    """
+    for t in (u, delta, A, B, C, D, z, delta_bias):
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be GPU tensors")
+    if y is None:
+        y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    rc = call(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
+              describe(z), describe(delta_bias), flags, describe(y), stream)
+    if rc != 0:
+        raise ScanError(rc, strerror(rc))
+    return y
