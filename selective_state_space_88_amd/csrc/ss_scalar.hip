@@ -97,7 +97,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
 #pragma unroll
       for (int j = 0; j < kT; ++j) {
         const float x = dv[j] + bias;
-        float s = p.softplus ? softplus_f32(x) : x;
+        float s = p.softplus ? softplus_fast(x) : x;
         if (tb + j >= L) s = 0.f;
         av[j] = __builtin_amdgcn_exp2f(s * An);
         wv_[j] = s * uv[j];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
         const int64_t hdc = d / p.chan_per_head;
         const float uu = to_f32(static_cast<const TIn*>(p.u)[b * p.u_sb + d * p.u_sd + t]);
         if (p.D) s = fmaf(p.D[p.d_per_head ? hdc : d], uu, s);
-        if constexpr (GATE) s *= silu_f32(to_f32(static_cast<const TIn*>(p.z)[b * p.z_sb + d * p.z_sd + t]));
+        if constexpr (GATE) s *= silu_fast(to_f32(static_cast<const TIn*>(p.z)[b * p.z_sb + d * p.z_sd + t]));
         store_one(static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd + t, s);
       }
     }
