@@ -29,9 +29,11 @@ METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 
 HBM_PEAK_GBPS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 128 FP32 FMA lanes/clk x 2 FLOP x 2.4 GHz
 
-# Work model (per element = one (b, d, t)); see DESIGN.md "Roofline model".
-# A transcendental (v_exp/v_log/v_rcp) issues at a quarter of the FMA rate on gfx950, so it
-# is counted as 8 FLOP-equivalents (4 FMA issue slots).
+# ALU work model, per element (one (b, d, t)), in FP32 FLOP-equivalents: an FMA is 2, a
+# multiply or add 1, and a transcendental (v_exp/v_log/v_rcp, which issues at a quarter of the
+# FMA rate on gfx950) 8, i.e. the four FMA issue slots it occupies.  The counts are the
+# method's own operations (the minimum any implementation performs), not the kernel's
+# instruction count: per (t, n) one exp, dt*A, (dt*u)*B, the state FMA and the readout FMA.
 TRANS = 8.0
 
 
@@ -48,6 +50,40 @@ def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
     if gate:
         per += 2 * TRANS + 3.0  # exp, reciprocal, add, two multiplies
     return per
+
+
+def kernel_source_digest(scalar_decay):
+    """sha256 of the HIP source of the kernel the workload runs (to match stored counters)."""
+    import hashlib
+
+    name = "ss_scalar.hip" if scalar_decay else "ss_diag.hip"
+    path = os.path.join(ROOT, "selective_state_space_88_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def stored_traffic(kernel, workload, digest):
+    """HBM bytes per launch from the committed counter summary, if it was taken on this source.
+
+    The summary (profiles/traffic_<kernel>_w<workload>.txt) holds `key: value` lines written
+    from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by the same counter's
+    reading for a plain copy of known size in the same process.
+    """
+    path = os.path.join(ROOT, "profiles", "traffic_%s_w%d.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(p, y_bytes):
@@ -71,6 +107,9 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="also run a plain device copy of MB megabytes (10^6 B) per step, so that "
+                         "HBM byte counters can be scaled against a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -108,6 +147,17 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    if args.copy_calibration:
+        # a plain streaming kernel of known size: the elementwise multiply reads and writes
+        # copy_calibration * 10^6 bytes per launch (its own kernel name in the profile)
+        n = args.copy_calibration * 1000000 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # timed region: K back-to-back steps, bracketed by device synchronisation
     K = args.steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -130,6 +180,8 @@ def main():
                                        P=p.channels // p.heads)
     alu_tflops = flops / avg_launch_s / 1e12
     hbm_gbps = nbytes / avg_launch_s / 1e9
+    kernel = "scalar_fwd_kernel" if p.scalar_decay else "diag_fwd_kernel"
+    traffic = stored_traffic(kernel, args.workload, kernel_source_digest(p.scalar_decay))
 
     out = {
         "metric": METRIC,
@@ -149,7 +201,7 @@ def main():
                         "y f32" if args.workload != 0 else p.name,
             "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
             "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
-            "kernel": "scalar_fwd_kernel" if p.scalar_decay else "diag_fwd_kernel",
+            "kernel": kernel,
         },
         "roofline": {
             "bound": "alu",
@@ -157,7 +209,7 @@ def main():
             "peak": FP32_VECTOR_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": traffic,
             "launch_ms": avg_launch_s * 1e3,
             "flop_equiv_per_launch": flops,
             "hbm_algorithmic_bytes_per_launch": nbytes,
