@@ -24,6 +24,9 @@ constexpr int kMaxWaves = 8;
 
 int npad_of(int N) { return (N + kNT - 1) / kNT * kNT; }
 
+// The head-uniform path: every head's channels fill whole 64-lane waves.
+bool head_path(const ScanArgs& a) { return a.chan_per_head % 64 == 0 && a.channels % 64 == 0; }
+
 // B, C [batch, groups, N, L] (strided, bf16/f32)  ->  ws [batch, groups, L, Npad] f32,
 // zero for n >= N.  One block transposes 64 steps x Npad states through LDS.
 template <typename TIn>
@@ -50,6 +53,44 @@ __global__ __launch_bounds__(256) void transpose_bc_kernel(const TIn* __restrict
   for (int idx = threadIdx.x; idx < 64 * Npad; idx += blockDim.x) {
     const int tt = idx / Npad, n = idx % Npad;
     if (t0 + tt < L) o[(int64_t)tt * Npad + n] = tile[tt][n];
+  }
+}
+
+// B and C [batch, groups, N, L] -> ws [batch, groups, L, Npad/8, 16] f32: for each step and
+// each group of 8 states, the 8 B values then the 8 C values (zero for n >= N), so that a
+// wave owning 8 states reads one step with a single 64-byte scalar load.
+template <typename TIn>
+__global__ __launch_bounds__(256) void interleave_bc_kernel(const TIn* __restrict__ Bsrc,
+                                                            const TIn* __restrict__ Csrc,
+                                                            int64_t b_sb, int64_t b_sg, int64_t b_sn,
+                                                            int64_t c_sb, int64_t c_sg, int64_t c_sn,
+                                                            int groups, int N, int Npad, int64_t L,
+                                                            float* __restrict__ dst) {
+  __shared__ float tile[2][64][129];
+  const int64_t tiles_per_row = (L + 63) / 64;
+  const int64_t bg = blockIdx.x / tiles_per_row;
+  const int64_t t0 = (blockIdx.x % tiles_per_row) * 64;
+  const int64_t b = bg / groups, g = bg % groups;
+  const TIn* sb = Bsrc + b * b_sb + g * b_sg;
+  const TIn* sc = Csrc + b * c_sb + g * c_sg;
+  for (int idx = threadIdx.x; idx < 64 * Npad; idx += blockDim.x) {
+    const int n = idx / 64, tt = idx % 64;
+    const int64_t t = t0 + tt;
+    float vb = 0.f, vc = 0.f;
+    if (n < N && t < L) {
+      vb = to_f32(sb[n * b_sn + t]);
+      vc = to_f32(sc[n * c_sn + t]);
+    }
+    tile[0][tt][n] = vb;
+    tile[1][tt][n] = vc;
+  }
+  __syncthreads();
+  float* o = dst + (bg * L + t0) * (2 * Npad);
+  for (int idx = threadIdx.x; idx < 64 * 2 * Npad; idx += blockDim.x) {
+    const int tt = idx / (2 * Npad), r = idx % (2 * Npad);
+    const int grp = r / 16, k = r % 16;
+    const int n = grp * 8 + (k % 8);
+    if (t0 + tt < L) o[(int64_t)tt * (2 * Npad) + r] = tile[k / 8][tt][n];
   }
 }
 
@@ -137,6 +178,161 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
   }
 }
 
+// Fast path when every head covers whole waves (channels per head a multiple of 64): the
+// head's step size and decay are computed once per step for the whole block, and the states
+// are spread over NW (a power of two, at most 8) waves of kHS states each.  Per block of kHT
+// steps:
+//  (1) wave 0 computes dt and a = exp(dt A_h), one step per lane; the block copies the B/C
+//      tile of these steps (f32, interleaved per 8 states, see interleave_bc_kernel) into LDS
+//      and stores w = dt u transposed ([step][channel]);
+//  (2) each wave advances its kHS states per step, reading B/C with wave-uniform (broadcast)
+//      LDS reads, and keeps its partial readouts of the kHT steps in registers;
+//  (3) the partial readouts are summed over the waves by a tree through LDS and the first
+//      wave writes y = sum + D u (gated) for its 64 channels.
+constexpr int kHS = 16;        // states per wave
+constexpr int kHT = 32;        // steps per time block
+constexpr int kHMaxWaves = 8;
+
+int head_waves(int N) {
+  int w = 1;
+  while (w * kHS < N) w *= 2;
+  return w;
+}
+
+template <typename TIn, typename TOut, bool GATE>
+__global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p,
+                                                                      const float* __restrict__ wsBC,
+                                                                      int Nh) {
+  // bc[j][k]: step j of the tile; k = 16 * group + (0..7: B, 8..15: C) for 8-state groups
+  __shared__ float bc[kHT][2 * kHS * kHMaxWaves];
+  __shared__ float wbuf[kHT][65];
+  __shared__ float red[kHMaxWaves / 2][kHT][64];
+  __shared__ float abuf[kHT];
+  __shared__ float dbuf[kHT];
+  constexpr int E = 16 / (int)sizeof(TIn);  // elements per 16-byte chunk of a row
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nthreads = blockDim.x;
+  const int nw = nthreads >> 6;
+  const int64_t cblocks = p.channels / 64;
+  const int64_t b = blockIdx.x / cblocks;
+  const int64_t d0 = (blockIdx.x % cblocks) * 64;
+  const int64_t L = p.L;
+  const int64_t hd = d0 / p.chan_per_head;  // the block's 64 channels share one head
+  const int64_t g = d0 / p.chan_per_group;
+  const float An = p.A[hd] * kLog2e;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  const TIn* __restrict__ dlr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
+  const float* __restrict__ bcg = wsBC + (b * p.groups + g) * L * 2 * Nh;  // [t][2 * Nh]
+  const bool vec = p.vec != 0;
+  const int64_t d = d0 + lane;  // this lane's channel (wave 0 writes it)
+  const TIn* __restrict__ ur = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
+  const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
+
+  float h[kHS];
+#pragma unroll
+  for (int i = 0; i < kHS; ++i) h[i] = 0.f;
+
+  for (int64_t tb = 0; tb < L; tb += kHT) {
+    if (wv == 0 && lane < kHT) {
+      const int64_t t = tb + lane;
+      float dtv = 0.f, av = 1.f;  // steps past the end are the identity
+      if (t < L) {
+        const float x = to_f32(dlr[t]) + bias;
+        dtv = p.softplus ? softplus_fast(x) : x;
+        av = __builtin_amdgcn_exp2f(dtv * An);
+      }
+      dbuf[lane] = dtv;
+      abuf[lane] = av;
+    }
+    // the B/C tile: kHT rows of 2 * Nh floats, contiguous in the workspace
+    {
+      const int rowq = 2 * Nh / 4;  // 16-byte quads per step
+      const f32x4* src = reinterpret_cast<const f32x4*>(bcg + tb * 2 * Nh);
+      for (int q = threadIdx.x; q < kHT * rowq; q += nthreads) {
+        const int j = q / rowq, k = q % rowq;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (tb + j < L) v = src[q];
+        *reinterpret_cast<f32x4*>(&bc[j][4 * k]) = v;
+      }
+    }
+    __syncthreads();
+    for (int q = threadIdx.x; q < 64 * (kHT / E); q += nthreads) {
+      const int c = q / (kHT / E), k = q % (kHT / E);
+      const int64_t t0 = tb + k * E;
+      const TIn* __restrict__ uc = static_cast<const TIn*>(p.u) + b * p.u_sb + (d0 + c) * p.u_sd;
+      float uv[E];
+      if (vec && t0 + E <= L) {
+        load_seg<E>(uc, t0, L, true, uv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) uv[e] = (t0 + e < L) ? to_f32(uc[t0 + e]) : 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) wbuf[k * E + e][c] = dbuf[k * E + e] * uv[e];
+    }
+    __syncthreads();
+
+    // the recurrence: this wave's kHS states, partial readouts of the tile kept in registers
+    float acc[kHT];
+#pragma unroll
+    for (int j = 0; j < kHT; ++j) {
+      const float a = abuf[j];
+      const float w = wbuf[j][lane];
+      const f32x4* q = reinterpret_cast<const f32x4*>(&bc[j][2 * kHS * wv]);
+      float Bj[kHS], Cj[kHS];
+#pragma unroll
+      for (int grp = 0; grp < kHS / 8; ++grp) {
+        const f32x4 b0 = q[4 * grp], b1 = q[4 * grp + 1], c0 = q[4 * grp + 2], c1 = q[4 * grp + 3];
+        Bj[8 * grp + 0] = b0.x; Bj[8 * grp + 1] = b0.y; Bj[8 * grp + 2] = b0.z; Bj[8 * grp + 3] = b0.w;
+        Bj[8 * grp + 4] = b1.x; Bj[8 * grp + 5] = b1.y; Bj[8 * grp + 6] = b1.z; Bj[8 * grp + 7] = b1.w;
+        Cj[8 * grp + 0] = c0.x; Cj[8 * grp + 1] = c0.y; Cj[8 * grp + 2] = c0.z; Cj[8 * grp + 3] = c0.w;
+        Cj[8 * grp + 4] = c1.x; Cj[8 * grp + 5] = c1.y; Cj[8 * grp + 6] = c1.z; Cj[8 * grp + 7] = c1.w;
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kHS; ++i) {
+        h[i] = fmaf(a, h[i], w * Bj[i]);
+        sum = fmaf(Cj[i], h[i], sum);
+      }
+      acc[j] = sum;
+    }
+
+    // tree reduction over the waves
+    for (int half = nw / 2; half >= 1; half /= 2) {
+      if (wv >= half && wv < 2 * half) {
+#pragma unroll
+        for (int j = 0; j < kHT; ++j) red[wv - half][j][lane] = acc[j];
+      }
+      __syncthreads();
+      if (wv < half) {
+#pragma unroll
+        for (int j = 0; j < kHT; ++j) acc[j] += red[wv][j][lane];
+      }
+      __syncthreads();
+    }
+
+    if (wv == 0) {
+      const int64_t t0 = tb;
+      float uv[kHT], out[kHT];
+      load_seg<kHT>(ur, t0, L, vec, uv);
+      float zv[kHT];
+      if constexpr (GATE) {
+        const TIn* __restrict__ zr = static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd;
+        load_seg<kHT>(zr, t0, L, vec, zv);
+      }
+#pragma unroll
+      for (int j = 0; j < kHT; ++j) {
+        float s = p.D ? fmaf(Dd, uv[j], acc[j]) : acc[j];
+        if constexpr (GATE) s *= silu_fast(zv[j]);
+        out[j] = s;
+      }
+      TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
+      store_seg<kHT>(yr, t0, L, vec, out);
+    }
+  }
+}
+
 template <typename TIn>
 hipError_t transpose(const ScanArgs& a, const void* src, int64_t sb, int64_t sg, int64_t sn,
                      float* dst, hipStream_t s) {
@@ -151,6 +347,23 @@ template <typename TIn, typename TOut>
 hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
   const int Npad = npad_of(a.N);
   const int64_t plane = a.batch * a.groups * a.L * Npad;
+  if (head_path(a)) {
+    const int nw = head_waves(a.N);
+    const int Nh = nw * kHS;
+    const int64_t tblocks = a.batch * a.groups * ((a.L + 63) / 64);
+    hipLaunchKernelGGL((interleave_bc_kernel<TIn>), dim3((unsigned)tblocks), dim3(256), 0, s,
+                       static_cast<const TIn*>(a.B), static_cast<const TIn*>(a.C), a.B_sb, a.B_sg,
+                       a.B_sn, a.C_sb, a.C_sg, a.C_sn, a.groups, a.N, Nh, a.L, ws);
+    hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+    const int64_t blocks = a.batch * (a.channels / 64);
+    const dim3 block(64 * nw);
+    if (a.z)
+      hipLaunchKernelGGL((scalar_head_kernel<TIn, TOut, true>), dim3((unsigned)blocks), block, 0, s, a, ws, Nh);
+    else
+      hipLaunchKernelGGL((scalar_head_kernel<TIn, TOut, false>), dim3((unsigned)blocks), block, 0, s, a, ws, Nh);
+    return hipGetLastError();
+  }
   hipError_t e = transpose<TIn>(a, a.B, a.B_sb, a.B_sg, a.B_sn, ws, s);
   if (e != hipSuccess) return e;
   e = transpose<TIn>(a, a.C, a.C_sb, a.C_sg, a.C_sn, ws + plane, s);
@@ -169,7 +382,8 @@ hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
 }  // namespace
 
 int64_t scalar_workspace_floats(const ScanArgs& a) {
-  return 2 * a.batch * a.groups * a.L * (int64_t)npad_of(a.N);
+  const int64_t n = head_path(a) ? (int64_t)head_waves(a.N) * kHS : (int64_t)npad_of(a.N);
+  return 2 * a.batch * a.groups * a.L * n;
 }
 
 hipError_t launch_scalar(const ScanArgs& a, float* ws, hipStream_t s) {
