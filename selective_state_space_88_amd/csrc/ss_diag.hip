@@ -11,18 +11,25 @@
 //  - a block is 4 waves over 4 channels of one (batch, B/C group); each wave owns one channel
 //    and its 64 lanes lie along time, lane j owning K consecutive steps, so one window of the
 //    row covers 64*K steps.  Windows are walked in order; the state at the end of each window
-//    is carried to the next in registers, so each exp is evaluated exactly once;
-//  - the N states are processed two at a time (n outer).  For a state each lane runs its K steps
-//    from zero (keeping the K decays a_t and inputs b_t in registers), the wave combines the 64
-//    lane aggregates with a DPP scan (row_shr within rows of 16, row_bcast across rows, wave_shr
-//    for the exclusive prefix), and each lane re-runs its K steps from the true incoming state
-//    to form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair are independent
+//    is carried to the next through LDS, so each exp is evaluated exactly once;
+//  - the N states are processed two at a time.  For a state each lane runs its K steps from
+//    zero (keeping the K decays a_t and inputs b_t in registers), the wave combines the 64 lane
+//    aggregates with a DPP scan (row_shr within rows of 16, row_bcast across rows, wave_shr for
+//    the exclusive prefix), and each lane re-runs its K steps from the true incoming state to
+//    form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair are independent
 //    chains, which the wave interleaves (and whose two scans fill each other's DPP wait states);
-//  - the B and C rows of state n are shared by every channel of the block: they are read once
-//    per block with coalesced 16-byte loads, widened to f32 and staged in LDS (double-buffered
-//    over n, laid out [quad][lane] so each wave-wide 16-byte LDS read is one contiguous 1 KB);
+//  - B and C are shared by every channel of a (batch, group).  A small pre-pass widens them to
+//    f32 and lays them out per window and state pair exactly as the scan reads them from LDS;
+//    the scan then copies each pair's 16 KB into a three-slot LDS ring with direct-to-LDS
+//    loads (global_load_lds_dwordx4), two pairs ahead of use, so the copy never passes through
+//    registers and overlaps two pairs of arithmetic;
+//  - u, delta and z of the next window are copied the same way into per-wave LDS slots while
+//    the current window runs (u and delta right after they are read, z after the gate), so no
+//    global load latency sits on the path.  The waits are explicit: before each ring barrier a
+//    wave waits only for the pair the next iteration reads (s_waitcnt vmcnt counts loads in
+//    issue order), never for the copies issued after it;
 //  - softplus, D*u and the silu gate are fused; u, delta, z and y stream through HBM once.
-#include <type_traits>
+#include <algorithm>
 
 #include "ss_device.h"
 #include "ss_launch.h"
@@ -30,7 +37,13 @@
 namespace ss {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                   // channels per block, one wave each
+constexpr int kK = 16;                      // steps per lane
+constexpr int kW = 64 * kK;                 // steps per window
+constexpr int kQ = kK / 4;                  // 16-byte quads per lane of one row
+constexpr int kSlotFloats = 4 * kW;         // one pair: B, C of state 2p, then of state 2p + 1
+constexpr int kRing = 3;                    // pair slots in LDS
+constexpr int kMaxPairs = 64;               // N <= 128
 
 // Two independent exclusive scans over the 64 lanes (lane 0 earliest) of (a, b) pairs under
 // (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2).  Each step is one fused DPP multiply and one
@@ -74,347 +87,368 @@ __device__ __forceinline__ void wave_exclusive_scan2(float& a0, float& b0, float
   b1 = eb1;
 }
 
-// Elements of TIn per 16-byte chunk.
-template <typename TIn>
-constexpr int chunk_elems() { return 16 / (int)sizeof(TIn); }
+// One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes from `src` land at
+// lds_base + 16 i (lds_base is wave-uniform).
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
 
-// A 16-byte chunk of a B/C row, held in registers between its global load and its LDS store.
-template <typename TIn>
-struct Chunk {
-  u32x4 raw;
-};
-
-template <bool FULL, typename TIn>
-__device__ __forceinline__ void load_chunk(const TIn* __restrict__ p, int64_t t, int64_t L, Chunk<TIn>& c) {
-  constexpr int E = chunk_elems<TIn>();
-  if constexpr (FULL) {
-    // a plain (cached) load: B and C rows are shared by every channel and should stay in L2
-    c.raw = *reinterpret_cast<const u32x4*>(p + t);
-  } else {
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      uint32_t bits = 0u;
-      if (t + e < L) {
-        if constexpr (sizeof(TIn) == 2) bits = reinterpret_cast<const uint16_t*>(p)[t + e];
-        else bits = __float_as_uint(reinterpret_cast<const float*>(p)[t + e]);
-      }
-      if constexpr (sizeof(TIn) == 2) w[e / 2] |= bits << (16 * (e % 2));
-      else w[e] = bits;
-    }
-    c.raw = u32x4{w[0], w[1], w[2], w[3]};
+// s_waitcnt vmcnt(n) lgkmcnt(0) then s_barrier: this wave's loads older than its last n have
+// landed and its LDS reads are done.  vmcnt is an immediate, so n is dispatched over the
+// values the kernel uses; anything larger waits for everything (always safe).
+__device__ __forceinline__ void wait_vm_barrier(int n) {
+  switch (n) {
+#define SS_W(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ") lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
+    SS_W(1) SS_W(2) SS_W(3) SS_W(4) SS_W(5) SS_W(6) SS_W(7) SS_W(8) SS_W(9) SS_W(10)
+    SS_W(11) SS_W(12) SS_W(13) SS_W(14) SS_W(15) SS_W(16) SS_W(17) SS_W(18) SS_W(19) SS_W(20)
+#undef SS_W
+    default: asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); break;
   }
 }
 
-// Widen a chunk to f32 and write it into an LDS row laid out as [quad][lane][4]: the chunk
-// starts at quad i of lane j (a bf16 chunk spans quads i and i + 1).
+// K consecutive steps of one input row for one lane, as raw 32-bit words (bf16 pairs or f32).
+// In a wave's LDS slot, 16-byte chunk c of lane j sits at word c * 256 + 4 j.
 template <typename TIn>
-__device__ __forceinline__ void store_chunk(float* row, int i, int j, const Chunk<TIn>& c) {
-  f32x4* q = reinterpret_cast<f32x4*>(row);
-  if constexpr (sizeof(TIn) == 2) {
-    q[i * 64 + j] = f32x4{bf16_lo(c.raw.x), bf16_hi(c.raw.x), bf16_lo(c.raw.y), bf16_hi(c.raw.y)};
-    q[(i + 1) * 64 + j] = f32x4{bf16_lo(c.raw.z), bf16_hi(c.raw.z), bf16_lo(c.raw.w), bf16_hi(c.raw.w)};
-  } else {
-    q[i * 64 + j] =
-        f32x4{__uint_as_float(c.raw.x), __uint_as_float(c.raw.y), __uint_as_float(c.raw.z), __uint_as_float(c.raw.w)};
-  }
-}
-
-// K consecutive elements of one time row as raw 32-bit words (bf16 pairs or f32), so that a
-// segment can be loaded one work item ahead and widened when it is used.
-template <typename TIn, int K>
 struct Seg {
-  static constexpr int kWords = K * (int)sizeof(TIn) / 4;
+  static constexpr int kChunks = kK * (int)sizeof(TIn) / 16;
+  static constexpr int kWords = 4 * kChunks;
   uint32_t w[kWords];
 };
 
-template <typename TIn, int K>
-__device__ __forceinline__ void seg_load(const TIn* __restrict__ p, int64_t t0, int64_t L, bool full,
-                                         Seg<TIn, K>& s) {
-  constexpr int NW = Seg<TIn, K>::kWords;
-  if (full) {
-    const u32x4* q = reinterpret_cast<const u32x4*>(p + t0);
+template <typename TIn>
+__device__ __forceinline__ void seg_read(const uint32_t* slot, int lane, Seg<TIn>& s) {
 #pragma unroll
-    for (int i = 0; i < NW / 4; ++i) {
-      const u32x4 v = __builtin_nontemporal_load(q + i);
-      s.w[4 * i] = v.x;
-      s.w[4 * i + 1] = v.y;
-      s.w[4 * i + 2] = v.z;
-      s.w[4 * i + 3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < NW; ++i) s.w[i] = 0u;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
-      if (t0 + j < L) {
-        if constexpr (sizeof(TIn) == 2)
-          s.w[j / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(p)[t0 + j] << (16 * (j % 2));
-        else
-          s.w[j] = __float_as_uint(reinterpret_cast<const float*>(p)[t0 + j]);
-      }
-    }
+  for (int c = 0; c < Seg<TIn>::kChunks; ++c) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(slot + c * 256)[lane];
+    s.w[4 * c] = v.x;
+    s.w[4 * c + 1] = v.y;
+    s.w[4 * c + 2] = v.z;
+    s.w[4 * c + 3] = v.w;
   }
 }
 
-template <typename TIn, int K>
-__device__ __forceinline__ float seg_get(const Seg<TIn, K>& s, int j) {
+template <typename TIn>
+__device__ __forceinline__ float seg_get(const Seg<TIn>& s, int j) {
   if constexpr (sizeof(TIn) == 2) return (j & 1) ? bf16_hi(s.w[j / 2]) : bf16_lo(s.w[j / 2]);
   else return __uint_as_float(s.w[j]);
 }
 
-// Per-wave parameters of one channel.
-struct Chan {
-  int64_t b, g, d, hd;
-  bool live;
-};
+// Copy this lane's K steps of `row` starting at t0 into the wave's slot with direct-to-LDS
+// loads.  Needs 16-byte aligned rows and L a multiple of 16 / sizeof(TIn), so that a chunk is
+// either wholly inside the row or wholly past its end; chunks past the end copy the row's
+// first chunk instead (in bounds; the scan masks those steps).
+template <typename TIn>
+__device__ __forceinline__ void seg_dma(const TIn* row, int64_t t0, int64_t L, uint32_t* slot) {
+  constexpr int E = 16 / (int)sizeof(TIn);
+#pragma unroll
+  for (int c = 0; c < Seg<TIn>::kChunks; ++c) {
+    const int64_t t = t0 + (int64_t)c * E;
+    dma16(t < L ? row + t : row, slot + c * 256);
+  }
+}
 
-template <typename TIn, typename TOut, bool GATE, int K>
-#ifndef SS_DIAG_WAVES_PER_EU
-#define SS_DIAG_WAVES_PER_EU 2
-#endif
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(SS_DIAG_WAVES_PER_EU))) void diag_fwd_kernel(
-    ScanArgs p, int64_t blocks_per_bg) {
-  constexpr int W = 64 * K;                      // steps per window
-  constexpr int Q = K / 4;                       // 16-byte quads per lane per row
-  constexpr int E = chunk_elems<TIn>();          // elements per 16-byte chunk
-  constexpr int CH = W / E;                      // chunks per row (of one tensor) per window
-  constexpr int NCH = 4 * CH;                    // chunks per pair of states (B, C for each)
-  constexpr int CPT = (NCH + 64 * kWaves - 1) / (64 * kWaves);  // chunks per thread
-  static_assert(K % 8 == 0 && W % E == 0, "bad window");
-  // stage[buf][r]: r = 0, 1 -> B, C of the pair's first state; 2, 3 -> B, C of the second.
-  // Within a row, quad i (steps 4i..4i+3) of lane j sits at float offset (i * 64 + j) * 4, so
-  // that one ds_read_b128 of the whole wave covers 1 KB of consecutive LDS (no bank conflicts).
-  __shared__ float stage[2][4][Q * 64 * 4];
+// The same with ordinary element loads (any alignment; steps >= L read as 0), completed
+// before returning.  Each wave reads only its own slot, so no barrier is needed after it.
+template <typename TIn>
+__device__ __forceinline__ void seg_fill(const TIn* row, int64_t t0, int64_t L, uint32_t* slot, int lane) {
+  Seg<TIn> s;
+#pragma unroll
+  for (int i = 0; i < Seg<TIn>::kWords; ++i) s.w[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < kK; ++j) {
+    if (t0 + j < L) {
+      if constexpr (sizeof(TIn) == 2)
+        s.w[j / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(row)[t0 + j] << (16 * (j % 2));
+      else
+        s.w[j] = __float_as_uint(reinterpret_cast<const float*>(row)[t0 + j]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < Seg<TIn>::kChunks; ++c)
+    reinterpret_cast<u32x4*>(slot + c * 256)[lane] =
+        u32x4{s.w[4 * c], s.w[4 * c + 1], s.w[4 * c + 2], s.w[4 * c + 3]};
+}
+
+// Pre-pass: B and C of every (batch, group) widened to f32, zero past L and past state N - 1,
+// in the order the scan copies them: [batch, group][window][pair][row r][quad i][lane j][4],
+// r = (B, C of state 2 pair, B, C of state 2 pair + 1), and element e of quad i of lane j is
+// window step 16 j + 4 i + e.  One thread writes one 16-byte quad.
+template <typename TIn>
+__global__ __launch_bounds__(256) void bc_pack_kernel(ScanArgs p, f32x4* __restrict__ ws, int npairs,
+                                                      int64_t nwin) {
+  const int64_t total = p.batch * p.groups * nwin * npairs * 4 * kQ * 64;
+  const int64_t L = p.L;
+  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+    const int j = (int)(o % 64);
+    int64_t rest = o / 64;
+    const int i = (int)(rest % kQ);
+    rest /= kQ;
+    const int r = (int)(rest % 4);
+    rest /= 4;
+    const int pair = (int)(rest % npairs);
+    rest /= npairs;
+    const int64_t win = rest % nwin;
+    const int64_t bg = rest / nwin;
+    const int64_t b = bg / p.groups, g = bg % p.groups;
+    const int n = 2 * pair + (r >> 1);
+    const int64_t t = win * kW + (int64_t)j * kK + 4 * i;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (n < p.N) {
+      const TIn* row = (r & 1) ? static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg + n * p.C_sn
+                               : static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg + n * p.B_sn;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (t + e < L) v[e] = to_f32(row[t + e]);
+    }
+    ws[o] = v;
+  }
+}
+
+template <typename TIn, typename TOut, bool GATE, bool VEC>
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
+    ScanArgs p, const float* __restrict__ ws, int npairs, int64_t nwin, int64_t blocks_per_bg) {
+  constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
+  constexpr int kSegWords = NCI * 256;
+  // ring[s]: one pair of B/C rows.  Row r of a slot holds quad i of lane j at float offset
+  // (i * 64 + j) * 4, so one ds_read_b128 of the whole wave is 1 KB of consecutive LDS.
+  __shared__ __attribute__((aligned(16))) float ring[kRing][kSlotFloats];
+  // per wave: u, delta, z of one window
+  __shared__ __attribute__((aligned(16))) uint32_t xin[3][kWaves][kSegWords];
+  // per wave and pair: [0] = (A_2p, A_2p+1) * log2 e, [1] = the carried state of the pair
+  __shared__ float2 par[kWaves][kMaxPairs][2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t L = p.L;
   const int N = p.N;
-  const bool vec = p.vec != 0;
-  const int64_t nwin = (L + W - 1) / W;
-  const int64_t quads = p.batch * p.groups * blocks_per_bg;
+  const int P = npairs;
 
-  // Work item k of this block: quad blockIdx.x + (k / nwin) * gridDim.x, window k % nwin.  The
-  // four waves of a block walk the same items (same batch, group and window; four channels).
-  auto chan_of = [&](int64_t quad) {
-    Chan c;
-    const int64_t bg = quad / blocks_per_bg, blk = quad % blocks_per_bg;
-    c.b = bg / p.groups;
-    c.g = bg % p.groups;
-    const int64_t local = blk * kWaves + wave;
-    c.live = local < p.chan_per_group;
-    c.d = c.g * p.chan_per_group + (c.live ? local : p.chan_per_group - 1);
-    c.hd = c.d / p.chan_per_head;
-    return c;
-  };
-  auto urow = [&](const Chan& c) { return static_cast<const TIn*>(p.u) + c.b * p.u_sb + c.d * p.u_sd; };
-  auto drow = [&](const Chan& c) { return static_cast<const TIn*>(p.delta) + c.b * p.dl_sb + c.hd * p.dl_sh; };
-  auto zrow = [&](const Chan& c) { return static_cast<const TIn*>(p.z) + c.b * p.z_sb + c.d * p.z_sd; };
+  const int64_t quad = blockIdx.x;
+  const int64_t bg = quad / blocks_per_bg, blk = quad % blocks_per_bg;
+  const int64_t b = bg / p.groups, g = bg % p.groups;
+  const int64_t local = blk * kWaves + wave;
+  const bool live = local < p.chan_per_group;
+  const int64_t d = g * p.chan_per_group + (live ? local : p.chan_per_group - 1);
+  const int64_t hd = d / p.chan_per_head;
+  const TIn* urow = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
+  const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
+  const TIn* zrow = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
+  const float* wsq = ws + bg * nwin * P * (int64_t)kSlotFloats;
+  const int Qt = (int)(nwin * P);  // pair stages of this block, in order (window-major)
 
-  const int64_t my_items = blockIdx.x < quads ? ((quads - 1 - blockIdx.x) / gridDim.x + 1) * nwin : 0;
-  if (my_items == 0) return;  // uniform over the block
-
-  int64_t quad = blockIdx.x;
-  Chan cc = chan_of(quad);
-  Seg<TIn, K> su, sd, sz;
-  float aq0 = 0.f, aq1 = 0.f;  // A row (times log2 e) across lanes: lane n holds state n (and 64 + n)
-  auto lane_get = [&](float q0, float q1, int n) {
-    return n < 64 ? readlane_f(q0, n) : readlane_f(q1, n - 64);
-  };
-  float cq0 = 0.f, cq1 = 0.f;  // carried state, lane n holds state n (and 64 + n)
-
-  for (int64_t k = 0; k < my_items; ++k) {
-    const int64_t win = k % nwin;
-    const int64_t w0 = win * W;
-    const bool full = vec && w0 + W <= L;
-    const int64_t t0 = w0 + (int64_t)lane * K;
-    if (win == 0) {
-      if (k > 0) {
-        quad += gridDim.x;
-        cc = chan_of(quad);
-      }
-      const float* Arow = p.A + cc.d * p.A_sd;
-      aq0 = lane < N ? Arow[lane] * kLog2e : 0.f;
-      aq1 = lane + 64 < N ? Arow[lane + 64] * kLog2e : 0.f;
-      cq0 = 0.f;
-      cq1 = 0.f;
+  {
+    const float* Ar = p.A + d * p.A_sd;
+    for (int pp = lane; pp < P; pp += 64) {
+      const int n = 2 * pp;
+      par[wave][pp][0] = make_float2(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f);
+      par[wave][pp][1] = make_float2(0.f, 0.f);
     }
-    seg_load<TIn, K>(urow(cc), t0, L, full, su);
-    seg_load<TIn, K>(drow(cc), t0, L, full, sd);
-    const float bias = p.bias ? p.bias[cc.hd] : 0.f;
-    const float Dd = p.D ? p.D[p.d_per_head ? cc.hd : cc.d] : 0.f;
+  }
+  uint32_t* xu = xin[0][wave];
+  uint32_t* xd = xin[1][wave];
+  uint32_t* xz = xin[2][wave];
 
-    // prologue: step sizes from the prefetched u and delta
-    float dt[K], wv[K], yv[K];
+  // this wave's quarter (4 KB) of pair stage qs into ring slot s
+  auto stage_dma = [&](int qs, int s) {
+    const float* src = wsq + (int64_t)qs * kSlotFloats + wave * 1024 + lane * 4;
+    float* dst = &ring[s][wave * 1024];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(src + i * 256, dst + i * 256);
+  };
+  auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
+    const int64_t t0 = w * kW + (int64_t)lane * kK;
+    if constexpr (VEC) seg_dma<TIn>(row, t0, L, slot);
+    else seg_fill<TIn>(row, t0, L, slot, lane);
+  };
+
+  if constexpr (VEC) {
+    x_copy(urow, 0, xu);
+    x_copy(drow, 0, xd);
+    if constexpr (GATE) x_copy(zrow, 0, xz);
+  }
+  stage_dma(0, 0);
+  if (Qt > 1) stage_dma(1, 1);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+  int q = 0;       // current pair stage
+  int slot = 0;    // its ring slot (q mod 3)
+  int carry_ops = 0;  // loads issued in the last epilogue (counted by the first wait after it)
+  for (int64_t w = 0; w < nwin; ++w) {
+    const int64_t w0 = w * kW;
+    const int64_t t0 = w0 + (int64_t)lane * kK;
+    const bool full = w0 + kW <= L;
+
+    // prologue: step sizes from this window's u and delta
+    if constexpr (!VEC) {
+      x_copy(urow, w, xu);
+      x_copy(drow, w, xd);
+    }
+    float dt[kK], wv[kK], yv[kK];
     float sdt = 0.f;
+    {
+      Seg<TIn> su, sd;
+      seg_read<TIn>(xu, lane, su);
+      seg_read<TIn>(xd, lane, sd);
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      const float x = seg_get<TIn, K>(sd, j) + bias;
-      float sp = p.softplus ? softplus_fast(x) : x;
-      if (!full && t0 + j >= L) sp = 0.f;  // steps past the end are the identity (a = 1, b = 0)
-      const float uu = seg_get<TIn, K>(su, j);
-      dt[j] = sp;
-      wv[j] = sp * uu;
-      yv[j] = Dd * uu;
-      sdt += sp;
-    }
-
-    // B/C rows of the states n0 and n0 + 1 (a state >= N reads as zeros): chunk q of the pair
-    // is row r = q / CH (B n0, C n0, B n0+1, C n0+1) at window step (q % CH) * E.  Each thread
-    // keeps a running source pointer per chunk (advanced by two states per pair) and the
-    // chunk's LDS position.
-    const TIn* __restrict__ Bg = static_cast<const TIn*>(p.B) + cc.b * p.B_sb + cc.g * p.B_sg;
-    const TIn* __restrict__ Cg = static_cast<const TIn*>(p.C) + cc.b * p.C_sb + cc.g * p.C_sg;
-    Chunk<TIn> st[CPT];
-    const TIn* src[CPT];
-    int64_t srcstep[CPT];
-    int rrow[CPT], rq[CPT], rl[CPT];
-#pragma unroll
-    for (int kk = 0; kk < CPT; ++kk) {
-      const int q = threadIdx.x + kk * 64 * kWaves;
-      const int qc = (NCH % (64 * kWaves) == 0 || q < NCH) ? q : 0;
-      const int r = qc / CH, qq = qc % CH, sw = qq * E;
-      const int64_t stride = (r & 1) ? p.C_sn : p.B_sn;
-      src[kk] = ((r & 1) ? Cg : Bg) + (r >> 1) * stride + w0 + sw;
-      srcstep[kk] = 2 * stride;
-      rrow[kk] = r;
-      rq[kk] = (sw % K) / 4;
-      rl[kk] = sw / K;
-    }
-    auto stage_load = [&](int n0) {
-#pragma unroll
-      for (int kk = 0; kk < CPT; ++kk) {
-        const int q = threadIdx.x + kk * 64 * kWaves;
-        if (NCH % (64 * kWaves) == 0 || q < NCH) {
-          if (n0 + (rrow[kk] >> 1) >= N)
-            st[kk].raw = u32x4{0u, 0u, 0u, 0u};
-          else if (full)
-            load_chunk<true>(src[kk], 0, 0, st[kk]);
-          else
-            load_chunk<false>(src[kk], 0, L - (w0 + (int64_t)(rl[kk] * K + rq[kk] * 4)), st[kk]);
-          src[kk] += srcstep[kk];
+      for (int j = 0; j < kK; ++j) {
+        const float x = seg_get<TIn>(sd, j) + bias;
+        float sp = p.softplus ? softplus_fast(x) : x;
+        float uu = seg_get<TIn>(su, j);
+        if (!full && t0 + j >= L) {  // steps past the end are the identity (a = 1, b = 0)
+          sp = 0.f;
+          uu = 0.f;
         }
+        dt[j] = sp;
+        wv[j] = sp * uu;
+        yv[j] = Dd * uu;
+        sdt += sp;
       }
-    };
-    auto stage_store = [&](int buf) {
-#pragma unroll
-      for (int kk = 0; kk < CPT; ++kk) {
-        const int q = threadIdx.x + kk * 64 * kWaves;
-        if (NCH % (64 * kWaves) == 0 || q < NCH) store_chunk<TIn>(&stage[buf][rrow[kk]][0], rq[kk], rl[kk], st[kk]);
+    }
+    // the next window's u and delta into the slots just read
+    int boundary_ops = carry_ops;
+    if constexpr (VEC) {
+      if (w + 1 < nwin) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        x_copy(urow, w + 1, xu);
+        x_copy(drow, w + 1, xd);
+        boundary_ops += 2 * NCI;
       }
-    };
+    }
 
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
-    for (int n0 = 0; n0 < N; n0 += 2) {
-      const int buf = (n0 >> 1) & 1;
-      const bool more = n0 + 2 < N;
-      if (more) stage_load(n0 + 2);
-      const bool two = n0 + 1 < N;
-      const float A0 = lane_get(aq0, aq1, n0);
-      const float A1 = two ? lane_get(aq0, aq1, n0 + 1) : 0.f;  // a missing second state is inert
+    for (int pp = 0; pp < P; ++pp) {
+      int allow = pp == 0 ? boundary_ops : 0;
+      if (q + 2 < Qt) {
+        stage_dma(q + 2, slot == 0 ? 2 : slot - 1);
+        allow += 4;
+      }
+      const float2 Ap = par[wave][pp][0];
+      const float2 hin = par[wave][pp][1];
+      const float* S = ring[slot];
       // this lane's B values of both states, all LDS reads issued before any use
-      f32x4 bq0[Q], bq1[Q];
+      f32x4 bq0[kQ], bq1[kQ];
       {
-        const f32x4* B0 = reinterpret_cast<const f32x4*>(&stage[buf][0][0]) + lane;
-        const f32x4* B1 = reinterpret_cast<const f32x4*>(&stage[buf][2][0]) + lane;
+        const f32x4* B0 = reinterpret_cast<const f32x4*>(S) + lane;
+        const f32x4* B1 = reinterpret_cast<const f32x4*>(S + 2 * kW) + lane;
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
+        for (int i = 0; i < kQ; ++i) {
           bq0[i] = B0[i * 64];
           bq1[i] = B1[i * 64];
         }
       }
-      float av0[K], bv0[K], av1[K], bv1[K];
+      float av0[kK], bv0[kK], av1[kK], bv1[kK];
       float h0 = 0.f, h1 = 0.f;
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
-        av0[j] = __builtin_amdgcn_exp2f(dt[j] * A0);
-        av1[j] = __builtin_amdgcn_exp2f(dt[j] * A1);
+      for (int j = 0; j < kK; ++j) {
+        av0[j] = __builtin_amdgcn_exp2f(dt[j] * Ap.x);
+        av1[j] = __builtin_amdgcn_exp2f(dt[j] * Ap.y);
       }
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
+      for (int j = 0; j < kK; ++j) {
         bv0[j] = wv[j] * bq0[j / 4][j % 4];
         bv1[j] = wv[j] * bq1[j / 4][j % 4];
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
       }
       // this lane's C values, read while the scan runs
-      f32x4 cq0v[Q], cq1v[Q];
+      f32x4 cq0[kQ], cq1[kQ];
       {
-        const f32x4* C0 = reinterpret_cast<const f32x4*>(&stage[buf][1][0]) + lane;
-        const f32x4* C1 = reinterpret_cast<const f32x4*>(&stage[buf][3][0]) + lane;
+        const f32x4* C0 = reinterpret_cast<const f32x4*>(S + kW) + lane;
+        const f32x4* C1 = reinterpret_cast<const f32x4*>(S + 3 * kW) + lane;
 #pragma unroll
-        for (int i = 0; i < Q; ++i) {
-          cq0v[i] = C0[i * 64];
-          cq1v[i] = C1[i * 64];
+        for (int i = 0; i < kQ; ++i) {
+          cq0[i] = C0[i * 64];
+          cq1[i] = C1[i * 64];
         }
       }
       // lane aggregates: decay over the lane's K steps and the lane's state from zero
-      float sa0 = __builtin_amdgcn_exp2f(sdt * A0), sb0 = h0;
-      float sa1 = __builtin_amdgcn_exp2f(sdt * A1), sb1 = h1;
+      float sa0 = __builtin_amdgcn_exp2f(sdt * Ap.x), sb0 = h0;
+      float sa1 = __builtin_amdgcn_exp2f(sdt * Ap.y), sb1 = h1;
       wave_exclusive_scan2(sa0, sb0, sa1, sb1);
-      h0 = fmaf(sa0, lane_get(cq0, cq1, n0), sb0);
-      h1 = fmaf(sa1, two ? lane_get(cq0, cq1, n0 + 1) : 0.f, sb1);
+      h0 = fmaf(sa0, hin.x, sb0);
+      h1 = fmaf(sa1, hin.y, sb1);
 #pragma unroll
-      for (int j = 0; j < K; ++j) {
+      for (int j = 0; j < kK; ++j) {
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
-        yv[j] = fmaf(cq0v[j / 4][j % 4], h0, yv[j]);
-        yv[j] = fmaf(cq1v[j / 4][j % 4], h1, yv[j]);
+        yv[j] = fmaf(cq0[j / 4][j % 4], h0, yv[j]);
+        yv[j] = fmaf(cq1[j / 4][j % 4], h1, yv[j]);
       }
-      // the window's end state (lane 63) starts the next window of the row
-      const float e0 = readlane_f(h0, 63), e1 = readlane_f(h1, 63);
-      if (n0 < 64) cq0 = writelane_f(e0, n0, cq0); else cq1 = writelane_f(e0, n0 - 64, cq1);
-      if (two) {
-        if (n0 + 1 < 64) cq0 = writelane_f(e1, n0 + 1, cq0); else cq1 = writelane_f(e1, n0 - 63, cq1);
-      }
-      if (more) stage_store(buf ^ 1);
-      __syncthreads();
+      // the window's end state (lane 63) starts the same pair in the next window
+      if (lane == 63) par[wave][pp][1] = make_float2(h0, h1);
+      // the next stage's copies (this wave's and, after the barrier, everyone's) have landed
+      if (q + 1 < Qt) wait_vm_barrier(allow);
+      ++q;
+      slot = slot == 2 ? 0 : slot + 1;
     }
 
+    // epilogue: gate, store, then this slot's z for the next window.  Only the stage copy
+    // issued by the last pair may still be in flight here: everything before it (this
+    // window's z and the next window's u and delta) has landed.
+    if (q + 1 < Qt) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    carry_ops = 0;
     if constexpr (GATE) {
-      seg_load<TIn, K>(zrow(cc), t0, L, full, sz);
+      if constexpr (!VEC) x_copy(zrow, w, xz);
+      Seg<TIn> sz;
+      seg_read<TIn>(xz, lane, sz);
 #pragma unroll
-      for (int j = 0; j < K; ++j) yv[j] *= silu_fast(seg_get<TIn, K>(sz, j));
+      for (int j = 0; j < kK; ++j) yv[j] *= silu_fast(seg_get<TIn>(sz, j));
     }
-    if (cc.live) {
-      TOut* __restrict__ y = static_cast<TOut*>(p.y) + cc.b * p.y_sb + cc.d * p.y_sd;
-      store_seg<K>(y, t0, L, full, yv);
+    if (live) {
+      TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
+      store_seg<kK>(y, t0, L, VEC && full, yv);
     }
-
+    if constexpr (VEC && GATE) {
+      if (w + 1 < nwin) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        x_copy(zrow, w + 1, xz);
+        carry_ops = NCI;
+      }
+    }
   }
 }
 
-template <typename TIn, typename TOut, int K>
-hipError_t launch_k(const ScanArgs& a, hipStream_t s) {
-  const int64_t blocks_per_bg = (a.chan_per_group + kWaves - 1) / kWaves;
-  const int64_t quads = a.batch * a.groups * blocks_per_bg;
-  // one block per channel quad; the block walks the quad's windows in order
-  const int64_t blocks = quads;
-  const dim3 grid((unsigned)blocks), block(64 * kWaves);
-  if (a.z)
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, true, K>), grid, block, 0, s, a, blocks_per_bg);
-  else
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, false, K>), grid, block, 0, s, a, blocks_per_bg);
-  return hipGetLastError();
-}
-
-#ifndef SS_DIAG_K
-#define SS_DIAG_K 16
-#endif
+int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
+int64_t nwin_of(const ScanArgs& a) { return (a.L + kW - 1) / kW; }
 
 template <typename TIn, typename TOut>
-hipError_t launch_t(const ScanArgs& a, hipStream_t s) {
-  return launch_k<TIn, TOut, SS_DIAG_K>(a, s);
+hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
+  const int P = npairs_of(a);
+  const int64_t nwin = nwin_of(a);
+  {
+    const int64_t quads = a.batch * a.groups * nwin * P * 4 * kQ * 64;
+    const int64_t blocks = std::min<int64_t>((quads + 255) / 256, 16384);
+    hipLaunchKernelGGL((bc_pack_kernel<TIn>), dim3((unsigned)blocks), dim3(256), 0, s, a,
+                       reinterpret_cast<f32x4*>(ws), P, nwin);
+  }
+  const int64_t blocks_per_bg = (a.chan_per_group + kWaves - 1) / kWaves;
+  const int64_t blocks = a.batch * a.groups * blocks_per_bg;  // one block per channel quad
+  const bool dma = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
+  const dim3 grid((unsigned)blocks), block(64 * kWaves);
+#define SS_LAUNCH(G, V) \
+  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V>), grid, block, 0, s, a, ws, P, nwin, blocks_per_bg)
+  if (a.z) {
+    if (dma) SS_LAUNCH(true, true); else SS_LAUNCH(true, false);
+  } else {
+    if (dma) SS_LAUNCH(false, true); else SS_LAUNCH(false, false);
+  }
+#undef SS_LAUNCH
+  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_diag(const ScanArgs& a, hipStream_t s) {
-  if (a.in_bf16) return a.out_bf16 ? launch_t<bf16_t, bf16_t>(a, s) : launch_t<bf16_t, float>(a, s);
-  return a.out_bf16 ? launch_t<float, bf16_t>(a, s) : launch_t<float, float>(a, s);
+int64_t diag_workspace_floats(const ScanArgs& a) {
+  return a.batch * a.groups * nwin_of(a) * npairs_of(a) * (int64_t)kSlotFloats;
+}
+
+hipError_t launch_diag(const ScanArgs& a, float* ws, hipStream_t s) {
+  if (a.in_bf16) return a.out_bf16 ? launch_t<bf16_t, bf16_t>(a, ws, s) : launch_t<bf16_t, float>(a, ws, s);
+  return a.out_bf16 ? launch_t<float, bf16_t>(a, ws, s) : launch_t<float, float>(a, ws, s);
 }
 
 }  // namespace ss
