@@ -26,9 +26,10 @@
 //  - u, delta and z of the next window are copied the same way into per-wave LDS slots while
 //    the current window runs (u and delta right after they are read, z after the gate), so no
 //    global load latency sits on the path.  The waits are explicit: before each ring barrier a
-//    wave waits only for the pair the next iteration reads (s_waitcnt vmcnt counts loads in
-//    issue order), never for the copies issued after it;
-//  - softplus, D*u and the silu gate are fused; u, delta, z and y stream through HBM once.
+//    wave waits only for the pair the next iteration reads (vmcnt retires this wave's vector
+//    memory operations, loads and stores alike, in issue order), never for what it issued after;
+//  - softplus, D*u and the silu gate are fused; u, delta, z and y stream through HBM once, y
+//    leaving through LDS so that every store instruction writes 1 KB of consecutive memory.
 #include <algorithm>
 
 #include "ss_device.h"
@@ -171,6 +172,42 @@ __device__ __forceinline__ void seg_fill(const TIn* row, int64_t t0, int64_t L, 
         u32x4{s.w[4 * c], s.w[4 * c + 1], s.w[4 * c + 2], s.w[4 * c + 3]};
 }
 
+// Store this wave's window of y (lane j holds steps 16 j .. 16 j + 15) with each store
+// instruction covering 1 KB of consecutive y: the lanes' 16-byte granules go to LDS, granule
+// g at g ^ ((g >> 4) & (NC - 1)) so that neither the writes nor the reads conflict on banks,
+// and instruction i then has lane j read and store granule 64 i + j.
+template <typename TOut>
+__device__ __forceinline__ void store_window_coalesced(uint32_t* stg, int lane, const float (&v)[kK],
+                                                       TOut* __restrict__ y) {
+  constexpr int NC = kK * (int)sizeof(TOut) / 16;
+  u32x4 gr[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    if constexpr (sizeof(TOut) == 4) {
+      gr[c] = u32x4{__float_as_uint(v[4 * c]), __float_as_uint(v[4 * c + 1]), __float_as_uint(v[4 * c + 2]),
+                    __float_as_uint(v[4 * c + 3])};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = f32_to_bf16_bits(v[8 * c + 2 * e]) | (f32_to_bf16_bits(v[8 * c + 2 * e + 1]) << 16);
+      gr[c] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+  }
+  u32x4* q = reinterpret_cast<u32x4*>(stg);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int g = NC * lane + c;
+    q[g ^ ((g >> 4) & (NC - 1))] = gr[c];
+  }
+  u32x4* out = reinterpret_cast<u32x4*>(y);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int g = 64 * i + lane;
+    __builtin_nontemporal_store(q[g ^ ((g >> 4) & (NC - 1))], out + g);
+  }
+}
+
 // Pre-pass: B and C of every (batch, group) widened to f32, zero past L and past state N - 1,
 // in the order the scan copies them: [batch, group][window][pair][row r][quad i][lane j][4],
 // r = (B, C of state 2 pair, B, C of state 2 pair + 1), and element e of quad i of lane j is
@@ -211,6 +248,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     ScanArgs p, const float* __restrict__ ws, int npairs, int64_t nwin, int64_t blocks_per_bg) {
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
+  constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
   // ring[s]: one pair of B/C rows.  Row r of a slot holds quad i of lane j at float offset
   // (i * 64 + j) * 4, so one ds_read_b128 of the whole wave is 1 KB of consecutive LDS.
   __shared__ __attribute__((aligned(16))) float ring[kRing][kSlotFloats];
@@ -253,11 +291,19 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   uint32_t* xz = xin[2][wave];
 
   // this wave's quarter (4 KB) of pair stage qs into ring slot s
+  // Stage copies go through a buffer resource over this (batch, group)'s stages of one window,
+  // so that the per-stage offset is a scalar and the lane offset a constant.
+  const uint32_t lane_off = (uint32_t)lane * 16u + (uint32_t)wave * 4096u;
   auto stage_dma = [&](int qs, int s) {
-    const float* src = wsq + (int64_t)qs * kSlotFloats + wave * 1024 + lane * 4;
+    const int64_t wq = qs / P;
+    const uint32_t off = (uint32_t)(qs - wq * P) * (uint32_t)(kSlotFloats * 4);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(wsq + wq * P * (int64_t)kSlotFloats), (short)0, P * kSlotFloats * 4, 0x00020000);
     float* dst = &ring[s][wave * 1024];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(src + i * 256, dst + i * 256);
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 256), 16,
+                                               lane_off + i * 1024, off, 0, 0);
   };
   auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
     const int64_t t0 = w * kW + (int64_t)lane * kK;
@@ -276,7 +322,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
   int q = 0;       // current pair stage
   int slot = 0;    // its ring slot (q mod 3)
-  int carry_ops = 0;  // loads issued in the last epilogue (counted by the first wait after it)
+  int carry_ops = 0;  // memory ops issued in the last epilogue (counted by the first wait after it)
   for (int64_t w = 0; w < nwin; ++w) {
     const int64_t w0 = w * kW;
     const int64_t t0 = w0 + (int64_t)lane * kK;
@@ -293,19 +339,30 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       Seg<TIn> su, sd;
       seg_read<TIn>(xu, lane, su);
       seg_read<TIn>(xd, lane, sd);
+      if (full) {
 #pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        const float x = seg_get<TIn>(sd, j) + bias;
-        float sp = p.softplus ? softplus_fast(x) : x;
-        float uu = seg_get<TIn>(su, j);
-        if (!full && t0 + j >= L) {  // steps past the end are the identity (a = 1, b = 0)
-          sp = 0.f;
-          uu = 0.f;
+        for (int j = 0; j < kK; ++j) {
+          const float x = seg_get<TIn>(sd, j) + bias;
+          const float sp = p.softplus ? softplus_fast(x) : x;
+          const float uu = seg_get<TIn>(su, j);
+          dt[j] = sp;
+          wv[j] = sp * uu;
+          yv[j] = Dd * uu;
+          sdt += sp;
         }
-        dt[j] = sp;
-        wv[j] = sp * uu;
-        yv[j] = Dd * uu;
-        sdt += sp;
+      } else {
+        // steps past the end are the identity (a = 1, b = 0)
+        const int rem = (int)(L - t0 < 0 ? 0 : (L - t0 > kK ? kK : L - t0));
+#pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          const float x = seg_get<TIn>(sd, j) + bias;
+          const float sp = j < rem ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+          const float uu = j < rem ? seg_get<TIn>(su, j) : 0.f;
+          dt[j] = sp;
+          wv[j] = sp * uu;
+          yv[j] = Dd * uu;
+          sdt += sp;
+        }
       }
     }
     // the next window's u and delta into the slots just read
@@ -381,6 +438,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       if (lane == 63) par[wave][pp][1] = make_float2(h0, h1);
       // the next stage's copies (this wave's and, after the barrier, everyone's) have landed
       if (q + 1 < Qt) wait_vm_barrier(allow);
+      else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slot free for y
       ++q;
       slot = slot == 2 ? 0 : slot + 1;
     }
@@ -400,13 +458,22 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     }
     if (live) {
       TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
-      store_seg<kK>(y, t0, L, VEC && full, yv);
+      if (VEC && full) {
+        // through this wave's quarter of the last pair's ring slot (free after that pair's
+        // barrier; the next copy into it is issued by this wave after these reads), so that
+        // each store instruction writes 1 KB of consecutive y
+        uint32_t* stg = reinterpret_cast<uint32_t*>(&ring[slot == 0 ? 2 : slot - 1][wave * 1024]);
+        store_window_coalesced<TOut>(stg, lane, yv, y + w0);
+        carry_ops += NCO;
+      } else {
+        store_seg<kK>(y, t0, L, false, yv);
+      }
     }
     if constexpr (VEC && GATE) {
       if (w + 1 < nwin) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         x_copy(zrow, w + 1, xz);
-        carry_ops = NCI;
+        carry_ops += NCI;
       }
     }
   }

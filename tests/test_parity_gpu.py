@@ -74,6 +74,35 @@ def test_lengths(L):
           "scalar L=%d" % L)
 
 
+@pytest.mark.parametrize("L", [8, 1032, 2056, 3000])
+def test_lengths_bf16_copy_path(L):
+    """bf16 rows 16-byte aligned with L a multiple of 8: the direct-to-LDS input path,
+    with a partial last window (and a whole one for L = 8 * 129)."""
+    torch_dev()
+    check(inputs.random_problem(300 + L, 1, 8, L, 16), "bf16 L=%d" % L)
+
+
+def test_softplus_elementwise():
+    """One step per channel with A = 0, u = B = C = 1: y = softplus(delta) exactly in the
+    method, so every element checks the kernel's softplus against float64 (relative 4e-6)."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_fwd
+
+    x = np.concatenate([np.linspace(-30.0, 30.0, 6001), np.linspace(-12.0, 2.0, 4096)]).astype(np.float32)
+    Dc = x.size
+    ones = lambda *s: torch.ones(*s, dtype=torch.float32, device="cuda")
+    delta = torch.from_numpy(x.reshape(1, Dc, 1)).cuda()
+    y = scan_fwd(ones(1, Dc, 1), delta, torch.zeros(Dc, 1, device="cuda"), ones(1, 1, 1, 1),
+                 ones(1, 1, 1, 1), None, None, None, softplus=True)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().reshape(-1).astype(np.float64)
+    ref = oracle.scan_fwd(np.ones((1, Dc, 1), np.float32), x.reshape(1, Dc, 1), np.zeros((Dc, 1), np.float32),
+                          np.ones((1, 1, 1, 1), np.float32), np.ones((1, 1, 1, 1), np.float32)).reshape(-1)
+    rel = np.max(np.abs(got - ref) / ref)
+    say("[parity] softplus elementwise: max relative error %.3e" % rel)
+    assert rel <= 4e-6
+
+
 def test_heads_and_groups_diagonal():
     torch_dev()
     # delta per head (4 channels per head) with a per-channel diagonal A; two B/C groups
