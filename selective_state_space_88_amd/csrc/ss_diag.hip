@@ -8,20 +8,23 @@
 // the study notes' history and the bqwf.cn survey section 2.2) possible.
 //
 // Mapping on gfx950 (wave64):
-//  - a block is 4 waves over 4 channels of one (batch, B/C group); each wave owns one channel
-//    and its 64 lanes lie along time, lane j owning K consecutive steps, so one window of the
-//    row covers 64*K steps.  Windows are walked in order; the state at the end of each window
-//    is carried to the next through LDS, so each exp is evaluated exactly once;
+//  - a wave holds ROWS channels (1, 2 or 4) of one (batch, B/C group), each on a row of
+//    64 / ROWS lanes laid along time: lane j of a row owns K consecutive steps, so one window
+//    of a channel covers (64 / ROWS) * K steps.  A block is 4 waves, i.e. 4 * ROWS channels
+//    sharing B and C.  Windows are walked in order; the state at the end of each window is
+//    carried to the next through LDS, so each exp is evaluated exactly once;
 //  - the N states are processed two at a time.  For a state each lane runs its K steps from
-//    zero (keeping the K decays a_t and inputs b_t in registers), the wave combines the 64 lane
-//    aggregates with a DPP scan (row_shr within rows of 16, row_bcast across rows, wave_shr for
-//    the exclusive prefix), and each lane re-runs its K steps from the true incoming state to
-//    form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair are independent
-//    chains, which the wave interleaves (and whose two scans fill each other's DPP wait states);
+//    zero (keeping the K decays a_t and inputs b_t in registers), the row combines its lane
+//    aggregates with a DPP scan (row_shr within rows of 16 lanes, row_bcast across them, then
+//    a shift for the exclusive prefix), and each lane re-runs its K steps from the true
+//    incoming state to form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair
+//    are independent chains, which the wave interleaves (and whose two scans fill each other's
+//    DPP wait states).  More channels per wave means a shorter scan and less B/C traffic per
+//    channel; fewer means more waves for short batches; the launch picks;
 //  - B and C are shared by every channel of a (batch, group).  A small pre-pass widens them to
 //    f32 and lays them out per window and state pair exactly as the scan reads them from LDS;
-//    the scan then copies each pair's 16 KB into a three-slot LDS ring with direct-to-LDS
-//    loads (global_load_lds_dwordx4), two pairs ahead of use, so the copy never passes through
+//    the scan then copies each pair into a three-slot LDS ring with direct-to-LDS loads
+//    (buffer_load ... lds), two pairs ahead of use, so the copy never passes through
 //    registers and overlaps two pairs of arithmetic;
 //  - u, delta and z of the next window are copied the same way into per-wave LDS slots while
 //    the current window runs (u and delta right after they are read, z after the gate), so no
@@ -29,7 +32,7 @@
 //    wave waits only for the pair the next iteration reads (vmcnt retires this wave's vector
 //    memory operations, loads and stores alike, in issue order), never for what it issued after;
 //  - softplus, D*u and the silu gate are fused; u, delta, z and y stream through HBM once, y
-//    leaving through LDS so that every store instruction writes 1 KB of consecutive memory.
+//    leaving through LDS so that every store instruction writes whole rows of consecutive y.
 #include <algorithm>
 
 #include "ss_device.h"
@@ -38,49 +41,109 @@
 namespace ss {
 namespace {
 
-constexpr int kWaves = 4;                   // channels per block, one wave each
+constexpr int kWaves = 4;                   // waves per block
 constexpr int kK = 16;                      // steps per lane
-constexpr int kW = 64 * kK;                 // steps per window
 constexpr int kQ = kK / 4;                  // 16-byte quads per lane of one row
-constexpr int kSlotFloats = 4 * kW;         // one pair: B, C of state 2p, then of state 2p + 1
 constexpr int kRing = 3;                    // pair slots in LDS
 constexpr int kMaxPairs = 64;               // N <= 128
 
-// Two independent exclusive scans over the 64 lanes (lane 0 earliest) of (a, b) pairs under
-// (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2).  Each step is one fused DPP multiply and one
-// fused DPP FMA per scan: v_fmac_f32_dpp b, b[src], a  (b += b[src] * a) and
-// v_mul_f32_dpp a, a[src], a.  A lane whose DPP source is outside its row (row_shr) or whose
-// row is masked off (row_bcast with row_mask) is not written, i.e. it keeps its pair, which is
-// the same as combining with the identity (1, 0).  Steps: row_shr:1,2,4,8 scan each row of 16
-// lanes; row_bcast:15 (rows 1, 3) and row_bcast:31 (rows 2, 3) add the earlier rows; wave_shr:1
-// turns the inclusive scan into the exclusive one (lane 0 gets the identity).  The two scans
-// are interleaved so that every DPP read of a VGPR comes at least four instructions after the
-// VALU write of it (the hardware needs two wait states there); the leading s_nop covers the
-// compiler's last writes.
-__device__ __forceinline__ void wave_exclusive_scan2(float& a0, float& b0, float& a1, float& b1) {
+// Steps per window of one channel, floats of one pair slot (B, C of state 2p, then of 2p + 1),
+// and direct-to-LDS copies per wave per slot.
+template <int ROWS> constexpr int win_steps() { return (64 / ROWS) * kK; }
+template <int ROWS> constexpr int slot_floats() { return 4 * win_steps<ROWS>(); }
+template <int ROWS> constexpr int slot_copies() { return slot_floats<ROWS>() / (kWaves * 256); }
+
+// Two independent exclusive scans, within each row of 64 / ROWS lanes (lane 0 of the row
+// earliest), of (a, b) pairs under (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2).  Each step is
+// one fused DPP multiply and one fused DPP FMA per scan: v_fmac_f32_dpp b, b[src], a
+// (b += b[src] * a) and v_mul_f32_dpp a, a[src], a.  A lane whose DPP source is outside its
+// 16-lane DPP row (row_shr) or whose DPP row is masked off (row_bcast with row_mask) is not
+// written, i.e. it keeps its pair, which is the same as combining with the identity (1, 0).
+// Steps: row_shr:1,2,4,8 scan each DPP row of 16 lanes; for 32-lane rows row_bcast:15 on DPP
+// rows 1 and 3 adds rows 0 and 2; for 64-lane rows row_bcast:31 on rows 2 and 3 then adds the
+// first half.  The exclusive prefix shifts by one lane inside the row (lane 0 of the row gets
+// the identity): wave_shr:1 for 64 lanes; for 16 and 32 lanes row_shr:1, with lane 16 of a
+// 32-lane row first given lane 15's value by row_bcast:15 on bank 0 of rows 1 and 3.  The two
+// scans are interleaved so that every DPP read of a VGPR comes at least two instructions after
+// the VALU write of it (the hardware needs two wait states there); the leading s_nop covers
+// the compiler's last writes.
+//
+// The same statement also loads this lane's C values of the pair (eight 16-byte LDS reads at
+// cbase + the given offsets, into c[0..7]) and waits for them at its end, so that the reads
+// overlap the scan.  The slot they read is filled by direct-to-LDS copies whose completion the
+// kernel establishes with its own vmcnt waits; read through plain C++, the compiler would
+// put a wait for every copy in flight in front of them.
+template <int ROWS, int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void row_exclusive_scan2(float& a0, float& b0, float& a1, float& b1, uint32_t cbase,
+                                                    f32x4 (&c)[8]) {
   float ea0, eb0, ea1, eb1;
 #define SS_STEP(CTRL)                                   \
   "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n"                \
   "v_fmac_f32_dpp %3, %3, %2 " CTRL "\n"                \
   "v_mul_f32_dpp %0, %0, %0 " CTRL "\n"                 \
   "v_mul_f32_dpp %2, %2, %2 " CTRL "\n"
-  asm volatile(
-      "s_nop 1\n"
-      SS_STEP("row_shr:1 row_mask:0xf bank_mask:0xf")
-      SS_STEP("row_shr:2 row_mask:0xf bank_mask:0xf")
-      SS_STEP("row_shr:4 row_mask:0xf bank_mask:0xf")
-      SS_STEP("row_shr:8 row_mask:0xf bank_mask:0xf")
-      SS_STEP("row_bcast:15 row_mask:0xa bank_mask:0xf")
-      SS_STEP("row_bcast:31 row_mask:0xc bank_mask:0xf")
-      "v_mov_b32 %4, 1.0\n"
-      "v_mov_b32 %6, 1.0\n"
-      "v_mov_b32 %5, 0\n"
-      "v_mov_b32 %7, 0\n"
-      "v_mov_b32_dpp %4, %0 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %6, %2 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %5, %1 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      "v_mov_b32_dpp %7, %3 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
-      : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "=&v"(ea0), "=&v"(eb0), "=&v"(ea1), "=&v"(eb1));
+#define SS_SCAN16                                       \
+  "s_nop 1\n"                                           \
+  SS_STEP("row_shr:1 row_mask:0xf bank_mask:0xf")       \
+  SS_STEP("row_shr:2 row_mask:0xf bank_mask:0xf")       \
+  SS_STEP("row_shr:4 row_mask:0xf bank_mask:0xf")       \
+  SS_STEP("row_shr:8 row_mask:0xf bank_mask:0xf")
+#define SS_IDENT                                        \
+  "v_mov_b32 %4, 1.0\n"                                 \
+  "v_mov_b32 %6, 1.0\n"                                 \
+  "v_mov_b32 %5, 0\n"                                   \
+  "v_mov_b32 %7, 0\n"
+#define SS_SHIFT(CTRL)                                  \
+  "v_mov_b32_dpp %4, %0 " CTRL "\n"                     \
+  "v_mov_b32_dpp %6, %2 " CTRL "\n"                     \
+  "v_mov_b32_dpp %5, %1 " CTRL "\n"                     \
+  "v_mov_b32_dpp %7, %3 " CTRL "\n"
+#define SS_LOADC                                        \
+  "ds_read_b128 %8, %16 offset:%17\n"                   \
+  "ds_read_b128 %9, %16 offset:%18\n"                   \
+  "ds_read_b128 %10, %16 offset:%19\n"                  \
+  "ds_read_b128 %11, %16 offset:%20\n"                  \
+  "ds_read_b128 %12, %16 offset:%21\n"                  \
+  "ds_read_b128 %13, %16 offset:%22\n"                  \
+  "ds_read_b128 %14, %16 offset:%23\n"                  \
+  "ds_read_b128 %15, %16 offset:%24\n"
+#define SS_OPS                                                                                  \
+  : "+v"(a0), "+v"(b0), "+v"(a1), "+v"(b1), "=&v"(ea0), "=&v"(eb0), "=&v"(ea1), "=&v"(eb1),      \
+    "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]), "=&v"(c[4]), "=&v"(c[5]), "=&v"(c[6]),   \
+    "=&v"(c[7])                                                                                 \
+  : "v"(cbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+  if constexpr (ROWS == 1) {
+    asm volatile(SS_LOADC
+                 SS_SCAN16
+                 SS_STEP("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                 SS_STEP("row_bcast:31 row_mask:0xc bank_mask:0xf")
+                 SS_IDENT
+                 SS_SHIFT("wave_shr:1 row_mask:0xf bank_mask:0xf")
+                 "s_waitcnt lgkmcnt(0)\n"
+                 SS_OPS);
+  } else if constexpr (ROWS == 2) {
+    asm volatile(SS_LOADC
+                 SS_SCAN16
+                 SS_STEP("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                 SS_IDENT
+                 SS_SHIFT("row_bcast:15 row_mask:0xa bank_mask:0x1")
+                 SS_SHIFT("row_shr:1 row_mask:0xf bank_mask:0xf")
+                 "s_waitcnt lgkmcnt(0)\n"
+                 SS_OPS);
+  } else {
+    static_assert(ROWS == 4, "1, 2 or 4 channels per wave");
+    asm volatile(SS_LOADC
+                 SS_SCAN16
+                 SS_IDENT
+                 SS_SHIFT("row_shr:1 row_mask:0xf bank_mask:0xf")
+                 "s_waitcnt lgkmcnt(0)\n"
+                 SS_OPS);
+  }
+#undef SS_OPS
+#undef SS_LOADC
+#undef SS_SHIFT
+#undef SS_IDENT
+#undef SS_SCAN16
 #undef SS_STEP
   a0 = ea0;
   b0 = eb0;
@@ -95,9 +158,9 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
-// s_waitcnt vmcnt(n) lgkmcnt(0) then s_barrier: this wave's loads older than its last n have
-// landed and its LDS reads are done.  vmcnt is an immediate, so n is dispatched over the
-// values the kernel uses; anything larger waits for everything (always safe).
+// s_waitcnt vmcnt(n) lgkmcnt(0) then s_barrier: this wave's memory operations older than its
+// last n have completed and its LDS reads are done.  vmcnt is an immediate, so n is
+// dispatched over the values the kernel uses; anything larger waits for everything (safe).
 __device__ __forceinline__ void wait_vm_barrier(int n) {
   switch (n) {
 #define SS_W(k) \
@@ -118,15 +181,55 @@ struct Seg {
   uint32_t w[kWords];
 };
 
+// Two 16-byte LDS reads, waited for in the same statement.  The slots they read are filled by
+// direct-to-LDS copies whose completion the kernel establishes with its own vmcnt waits; read
+// through plain C++ the compiler would put a wait for every copy in flight (stage copies and
+// y stores included) in front of them.
+__device__ __forceinline__ void lds_read2(const void* p0, const void* p1, u32x4& v0, u32x4& v1) {
+  const uint32_t a0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p0;
+  const uint32_t a1 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p1;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(v0), "=&v"(v1)
+               : "v"(a0), "v"(a1)
+               : "memory");
+}
+
+// Eight 16-byte LDS reads at base + the given byte offsets, waited for in the same statement
+// (for the same reason as lds_read2).
+template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_read8(uint32_t base, f32x4 (&v)[8]) {
+  asm volatile(
+      "ds_read_b128 %0, %8 offset:%9\n\tds_read_b128 %1, %8 offset:%10\n\t"
+      "ds_read_b128 %2, %8 offset:%11\n\tds_read_b128 %3, %8 offset:%12\n\t"
+      "ds_read_b128 %4, %8 offset:%13\n\tds_read_b128 %5, %8 offset:%14\n\t"
+      "ds_read_b128 %6, %8 offset:%15\n\tds_read_b128 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+      : "v"(base), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+      : "memory");
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 template <typename TIn>
 __device__ __forceinline__ void seg_read(const uint32_t* slot, int lane, Seg<TIn>& s) {
+  static_assert(Seg<TIn>::kChunks % 2 == 0, "chunks are read in pairs");
 #pragma unroll
-  for (int c = 0; c < Seg<TIn>::kChunks; ++c) {
-    const u32x4 v = reinterpret_cast<const u32x4*>(slot + c * 256)[lane];
-    s.w[4 * c] = v.x;
-    s.w[4 * c + 1] = v.y;
-    s.w[4 * c + 2] = v.z;
-    s.w[4 * c + 3] = v.w;
+  for (int c = 0; c < Seg<TIn>::kChunks; c += 2) {
+    u32x4 v0, v1;
+    lds_read2(reinterpret_cast<const u32x4*>(slot + c * 256) + lane,
+              reinterpret_cast<const u32x4*>(slot + (c + 1) * 256) + lane, v0, v1);
+    s.w[4 * c] = v0.x;
+    s.w[4 * c + 1] = v0.y;
+    s.w[4 * c + 2] = v0.z;
+    s.w[4 * c + 3] = v0.w;
+    s.w[4 * c + 4] = v1.x;
+    s.w[4 * c + 5] = v1.y;
+    s.w[4 * c + 6] = v1.z;
+    s.w[4 * c + 7] = v1.w;
   }
 }
 
@@ -172,54 +275,20 @@ __device__ __forceinline__ void seg_fill(const TIn* row, int64_t t0, int64_t L, 
         u32x4{s.w[4 * c], s.w[4 * c + 1], s.w[4 * c + 2], s.w[4 * c + 3]};
 }
 
-// Store this wave's window of y (lane j holds steps 16 j .. 16 j + 15) with each store
-// instruction covering 1 KB of consecutive y: the lanes' 16-byte granules go to LDS, granule
-// g at g ^ ((g >> 4) & (NC - 1)) so that neither the writes nor the reads conflict on banks,
-// and instruction i then has lane j read and store granule 64 i + j.
-template <typename TOut>
-__device__ __forceinline__ void store_window_coalesced(uint32_t* stg, int lane, const float (&v)[kK],
-                                                       TOut* __restrict__ y) {
-  constexpr int NC = kK * (int)sizeof(TOut) / 16;
-  u32x4 gr[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if constexpr (sizeof(TOut) == 4) {
-      gr[c] = u32x4{__float_as_uint(v[4 * c]), __float_as_uint(v[4 * c + 1]), __float_as_uint(v[4 * c + 2]),
-                    __float_as_uint(v[4 * c + 3])};
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        w[e] = f32_to_bf16_bits(v[8 * c + 2 * e]) | (f32_to_bf16_bits(v[8 * c + 2 * e + 1]) << 16);
-      gr[c] = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  }
-  u32x4* q = reinterpret_cast<u32x4*>(stg);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int g = NC * lane + c;
-    q[g ^ ((g >> 4) & (NC - 1))] = gr[c];
-  }
-  u32x4* out = reinterpret_cast<u32x4*>(y);
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int g = 64 * i + lane;
-    __builtin_nontemporal_store(q[g ^ ((g >> 4) & (NC - 1))], out + g);
-  }
-}
-
 // Pre-pass: B and C of every (batch, group) widened to f32, zero past L and past state N - 1,
 // in the order the scan copies them: [batch, group][window][pair][row r][quad i][lane j][4],
-// r = (B, C of state 2 pair, B, C of state 2 pair + 1), and element e of quad i of lane j is
-// window step 16 j + 4 i + e.  One thread writes one 16-byte quad.
-template <typename TIn>
+// r = (B, C of state 2 pair, B, C of state 2 pair + 1), j over the 64 / ROWS lanes of a
+// channel row, and element e of quad i of lane j is window step K j + 4 i + e.  One thread
+// writes one 16-byte quad.
+template <typename TIn, int ROWS>
 __global__ __launch_bounds__(256) void bc_pack_kernel(ScanArgs p, f32x4* __restrict__ ws, int npairs,
                                                       int64_t nwin) {
-  const int64_t total = p.batch * p.groups * nwin * npairs * 4 * kQ * 64;
+  constexpr int LPC = 64 / ROWS;
+  const int64_t total = p.batch * p.groups * nwin * npairs * 4 * kQ * LPC;
   const int64_t L = p.L;
   for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
-    const int j = (int)(o % 64);
-    int64_t rest = o / 64;
+    const int j = (int)(o % LPC);
+    int64_t rest = o / LPC;
     const int i = (int)(rest % kQ);
     rest /= kQ;
     const int r = (int)(rest % 4);
@@ -230,7 +299,7 @@ __global__ __launch_bounds__(256) void bc_pack_kernel(ScanArgs p, f32x4* __restr
     const int64_t bg = rest / nwin;
     const int64_t b = bg / p.groups, g = bg % p.groups;
     const int n = 2 * pair + (r >> 1);
-    const int64_t t = win * kW + (int64_t)j * kK + 4 * i;
+    const int64_t t = win * win_steps<ROWS>() + (int64_t)j * kK + 4 * i;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (n < p.N) {
       const TIn* row = (r & 1) ? static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg + n * p.C_sn
@@ -243,70 +312,85 @@ __global__ __launch_bounds__(256) void bc_pack_kernel(ScanArgs p, f32x4* __restr
   }
 }
 
-template <typename TIn, typename TOut, bool GATE, bool VEC>
+template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
     ScanArgs p, const float* __restrict__ ws, int npairs, int64_t nwin, int64_t blocks_per_bg) {
+  constexpr int LPC = 64 / ROWS;                     // lanes per channel row
+  constexpr int W = win_steps<ROWS>();               // steps per window of a channel
+  constexpr int SLOT = slot_floats<ROWS>();
+  constexpr int NDMA = slot_copies<ROWS>();          // this wave's copies per pair slot
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
   constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
+  constexpr int GPR = LPC * NCO;                     // 16-byte granules of y per channel row
+  // y is staged in this wave's share of the last pair's ring slot when it fits there
+  constexpr bool kYInRing = SLOT / kWaves >= NCO * 256;
   // ring[s]: one pair of B/C rows.  Row r of a slot holds quad i of lane j at float offset
-  // (i * 64 + j) * 4, so one ds_read_b128 of the whole wave is 1 KB of consecutive LDS.
-  __shared__ __attribute__((aligned(16))) float ring[kRing][kSlotFloats];
-  // per wave: u, delta, z of one window
-  __shared__ __attribute__((aligned(16))) uint32_t xin[3][kWaves][kSegWords];
-  // per wave and pair: [0] = (A_2p, A_2p+1) * log2 e, [1] = the carried state of the pair
-  __shared__ float2 par[kWaves][kMaxPairs][2];
+  // (i * LPC + j) * 4, so every ds_read_b128 reads consecutive LDS (the rows of a wave read
+  // the same addresses).
+  __shared__ __attribute__((aligned(16))) float ring[kRing][SLOT];
+  // per wave: u, delta, z of one window, and y on its way out
+  __shared__ __attribute__((aligned(16))) uint32_t xin[kWaves][3][kSegWords];
+  __shared__ __attribute__((aligned(16))) uint32_t ystg[kWaves][kYInRing ? 4 : NCO * 256];
+  // per (wave, row, pair): (A_2p, A_2p+1) * log2 e and the carried state of the pair.  A
+  // static array: the compiler then knows the ring copies in flight cannot write it, and
+  // reads of it need not wait for them.
+  __shared__ float4 par[kWaves * ROWS * kMaxPairs];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane / LPC;        // channel row of this lane
+  const int jl = lane % LPC;       // lane within the row
   const int64_t L = p.L;
   const int N = p.N;
   const int P = npairs;
 
-  const int64_t quad = blockIdx.x;
-  const int64_t bg = quad / blocks_per_bg, blk = quad % blocks_per_bg;
+  const int64_t bg = blockIdx.x / blocks_per_bg, blk = blockIdx.x % blocks_per_bg;
   const int64_t b = bg / p.groups, g = bg % p.groups;
-  const int64_t local = blk * kWaves + wave;
-  const bool live = local < p.chan_per_group;
-  const int64_t d = g * p.chan_per_group + (live ? local : p.chan_per_group - 1);
+  const int64_t local0 = (blk * kWaves + wave) * ROWS;  // first channel (in the group) of the wave
+  const int64_t cpg = p.chan_per_group;
+  const int64_t local = local0 + r;
+  const bool live = local < cpg;
+  const bool wave_live = local0 + ROWS <= cpg;         // every row of the wave is a channel
+  const int64_t d = g * cpg + (live ? local : cpg - 1);
   const int64_t hd = d / p.chan_per_head;
   const TIn* urow = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
   const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
   const TIn* zrow = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
   const float bias = p.bias ? p.bias[hd] : 0.f;
   const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
-  const float* wsq = ws + bg * nwin * P * (int64_t)kSlotFloats;
+  const float* wsq = ws + bg * nwin * P * (int64_t)SLOT;
   const int Qt = (int)(nwin * P);  // pair stages of this block, in order (window-major)
 
+  float4* mypar = par + (wave * ROWS + r) * kMaxPairs;
   {
     const float* Ar = p.A + d * p.A_sd;
-    for (int pp = lane; pp < P; pp += 64) {
+    for (int pp = jl; pp < P; pp += LPC) {
       const int n = 2 * pp;
-      par[wave][pp][0] = make_float2(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f);
-      par[wave][pp][1] = make_float2(0.f, 0.f);
+      mypar[pp] = make_float4(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f, 0.f, 0.f);
     }
   }
-  uint32_t* xu = xin[0][wave];
-  uint32_t* xd = xin[1][wave];
-  uint32_t* xz = xin[2][wave];
+  uint32_t* xu = xin[wave][0];
+  uint32_t* xd = xin[wave][1];
+  uint32_t* xz = xin[wave][2];
 
-  // this wave's quarter (4 KB) of pair stage qs into ring slot s
-  // Stage copies go through a buffer resource over this (batch, group)'s stages of one window,
-  // so that the per-stage offset is a scalar and the lane offset a constant.
-  const uint32_t lane_off = (uint32_t)lane * 16u + (uint32_t)wave * 4096u;
+  // This wave's share of pair stage qs into ring slot s.  The copies go through a buffer
+  // resource over this (batch, group)'s stages of one window, so that the per-stage offset is
+  // a scalar and the lane offset a constant.
+  const uint32_t lane_off = (uint32_t)lane * 16u + (uint32_t)wave * (NDMA * 1024u);
   auto stage_dma = [&](int qs, int s) {
     const int64_t wq = qs / P;
-    const uint32_t off = (uint32_t)(qs - wq * P) * (uint32_t)(kSlotFloats * 4);
+    const uint32_t off = (uint32_t)(qs - wq * P) * (uint32_t)(SLOT * 4);
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(wsq + wq * P * (int64_t)kSlotFloats), (short)0, P * kSlotFloats * 4, 0x00020000);
-    float* dst = &ring[s][wave * 1024];
+        const_cast<float*>(wsq + wq * P * (int64_t)SLOT), (short)0, P * SLOT * 4, 0x00020000);
+    float* dst = &ring[s][wave * NDMA * 256];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NDMA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 256), 16,
                                                lane_off + i * 1024, off, 0, 0);
   };
   auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
-    const int64_t t0 = w * kW + (int64_t)lane * kK;
+    const int64_t t0 = w * W + (int64_t)jl * kK;
     if constexpr (VEC) seg_dma<TIn>(row, t0, L, slot);
     else seg_fill<TIn>(row, t0, L, slot, lane);
   };
@@ -320,13 +404,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   if (Qt > 1) stage_dma(1, 1);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
 
-  int q = 0;       // current pair stage
-  int slot = 0;    // its ring slot (q mod 3)
+  int q = 0;          // current pair stage
+  int slot = 0;       // its ring slot (q mod 3)
   int carry_ops = 0;  // memory ops issued in the last epilogue (counted by the first wait after it)
   for (int64_t w = 0; w < nwin; ++w) {
-    const int64_t w0 = w * kW;
-    const int64_t t0 = w0 + (int64_t)lane * kK;
-    const bool full = w0 + kW <= L;
+    const int64_t w0 = w * W;
+    const int64_t t0 = w0 + (int64_t)jl * kK;
+    const bool full = w0 + W <= L;
 
     // prologue: step sizes from this window's u and delta
     if constexpr (!VEC) {
@@ -380,62 +464,47 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       int allow = pp == 0 ? boundary_ops : 0;
       if (q + 2 < Qt) {
         stage_dma(q + 2, slot == 0 ? 2 : slot - 1);
-        allow += 4;
+        allow += NDMA;
       }
-      const float2 Ap = par[wave][pp][0];
-      const float2 hin = par[wave][pp][1];
-      const float* S = ring[slot];
-      // this lane's B values of both states, all LDS reads issued before any use
-      f32x4 bq0[kQ], bq1[kQ];
-      {
-        const f32x4* B0 = reinterpret_cast<const f32x4*>(S) + lane;
-        const f32x4* B1 = reinterpret_cast<const f32x4*>(S + 2 * kW) + lane;
-#pragma unroll
-        for (int i = 0; i < kQ; ++i) {
-          bq0[i] = B0[i * 64];
-          bq1[i] = B1[i * 64];
-        }
-      }
+      const float4 pv = mypar[pp];  // (A pair, carried state pair) of this lane's channel
+      // this lane's B values of both states: quad i of row r of the slot is at byte offset
+      // 4 W r + 16 (i LPC + j) from the slot
+      const uint32_t lbase = lds_addr(ring[slot]) + 16u * (uint32_t)jl;
+      constexpr int QS = 16 * LPC;
+      f32x4 bq[8];  // B of state 2p (quads 0-3), then of state 2p + 1
+      lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq);
       float av0[kK], bv0[kK], av1[kK], bv1[kK];
       float h0 = 0.f, h1 = 0.f;
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
-        av0[j] = __builtin_amdgcn_exp2f(dt[j] * Ap.x);
-        av1[j] = __builtin_amdgcn_exp2f(dt[j] * Ap.y);
+        av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
+        av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
       }
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
-        bv0[j] = wv[j] * bq0[j / 4][j % 4];
-        bv1[j] = wv[j] * bq1[j / 4][j % 4];
+        bv0[j] = wv[j] * bq[j / 4][j % 4];
+        bv1[j] = wv[j] * bq[4 + j / 4][j % 4];
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
-      }
-      // this lane's C values, read while the scan runs
-      f32x4 cq0[kQ], cq1[kQ];
-      {
-        const f32x4* C0 = reinterpret_cast<const f32x4*>(S + kW) + lane;
-        const f32x4* C1 = reinterpret_cast<const f32x4*>(S + 3 * kW) + lane;
-#pragma unroll
-        for (int i = 0; i < kQ; ++i) {
-          cq0[i] = C0[i * 64];
-          cq1[i] = C1[i * 64];
-        }
       }
       // lane aggregates: decay over the lane's K steps and the lane's state from zero
-      float sa0 = __builtin_amdgcn_exp2f(sdt * Ap.x), sb0 = h0;
-      float sa1 = __builtin_amdgcn_exp2f(sdt * Ap.y), sb1 = h1;
-      wave_exclusive_scan2(sa0, sb0, sa1, sb1);
-      h0 = fmaf(sa0, hin.x, sb0);
-      h1 = fmaf(sa1, hin.y, sb1);
+      float sa0 = __builtin_amdgcn_exp2f(sdt * pv.x), sb0 = h0;
+      float sa1 = __builtin_amdgcn_exp2f(sdt * pv.y), sb1 = h1;
+      // the scan, with this lane's C values of both states read while it runs
+      f32x4 cq[8];
+      row_exclusive_scan2<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS, 12 * W, 12 * W + QS,
+                          12 * W + 2 * QS, 12 * W + 3 * QS>(sa0, sb0, sa1, sb1, lbase, cq);
+      h0 = fmaf(sa0, pv.z, sb0);
+      h1 = fmaf(sa1, pv.w, sb1);
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
-        yv[j] = fmaf(cq0[j / 4][j % 4], h0, yv[j]);
-        yv[j] = fmaf(cq1[j / 4][j % 4], h1, yv[j]);
+        yv[j] = fmaf(cq[j / 4][j % 4], h0, yv[j]);
+        yv[j] = fmaf(cq[4 + j / 4][j % 4], h1, yv[j]);
       }
-      // the window's end state (lane 63) starts the same pair in the next window
-      if (lane == 63) par[wave][pp][1] = make_float2(h0, h1);
+      // the window's end state (the row's last lane) starts the same pair in the next window
+      if (jl == LPC - 1) *reinterpret_cast<float2*>(&mypar[pp].z) = make_float2(h0, h1);
       // the next stage's copies (this wave's and, after the barrier, everyone's) have landed
       if (q + 1 < Qt) wait_vm_barrier(allow);
       else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slot free for y
@@ -446,8 +515,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     // epilogue: gate, store, then this slot's z for the next window.  Only the stage copy
     // issued by the last pair may still be in flight here: everything before it (this
     // window's z and the next window's u and delta) has landed.
-    if (q + 1 < Qt) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (q + 1 < Qt) {
+      if constexpr (NDMA == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+      else if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     carry_ops = 0;
     if constexpr (GATE) {
       if constexpr (!VEC) x_copy(zrow, w, xz);
@@ -456,18 +530,66 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
       for (int j = 0; j < kK; ++j) yv[j] *= silu_fast(seg_get<TIn>(sz, j));
     }
-    if (live) {
-      TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
-      if (VEC && full) {
-        // through this wave's quarter of the last pair's ring slot (free after that pair's
-        // barrier; the next copy into it is issued by this wave after these reads), so that
-        // each store instruction writes 1 KB of consecutive y
-        uint32_t* stg = reinterpret_cast<uint32_t*>(&ring[slot == 0 ? 2 : slot - 1][wave * 1024]);
-        store_window_coalesced<TOut>(stg, lane, yv, y + w0);
-        carry_ops += NCO;
-      } else {
-        store_seg<kK>(y, t0, L, false, yv);
+    if (VEC && full) {
+      // Through LDS, so that each store instruction writes whole channel rows of consecutive
+      // y.  Lane granule c (steps 4c.. of a f32 lane, 8c.. of a bf16 lane) is granule
+      // g = NCO lane + c of the wave's window; it is kept at g ^ ((g >> 4) & (NCO - 1)) so that
+      // neither the writes nor the reads conflict on banks, and store instruction i has lane
+      // l take granule 64 i + l, i.e. granule (64 i + l) mod GPR of row (64 i + l) / GPR.
+      // (a ring slot is free once its pair's barrier has passed, and this wave's share of it
+      // is next written by this wave's own copy, issued after these reads)
+      // (written and read through asm: plain C++ here would make the compiler wait for every
+      // copy in flight)
+      const uint32_t sbase = kYInRing ? lds_addr(&ring[slot == 0 ? 2 : slot - 1][wave * (SLOT / kWaves)])
+                                      : lds_addr(ystg[wave]);
+#pragma unroll
+      for (int c = 0; c < NCO; ++c) {
+        u32x4 gr;
+        if constexpr (sizeof(TOut) == 4) {
+          gr = u32x4{__float_as_uint(yv[4 * c]), __float_as_uint(yv[4 * c + 1]), __float_as_uint(yv[4 * c + 2]),
+                     __float_as_uint(yv[4 * c + 3])};
+        } else {
+          uint32_t wd[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            wd[e] = f32_to_bf16_bits(yv[8 * c + 2 * e]) | (f32_to_bf16_bits(yv[8 * c + 2 * e + 1]) << 16);
+          gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
+        }
+        const int gi = NCO * lane + c;
+        const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
+        asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
       }
+      // granule 64 i + l sits at 64 i + (l ^ ((l >> 4) & (NCO - 1))): one base, offsets 1 KB i
+      u32x4 yo[NCO];
+      {
+        const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
+        if constexpr (NCO == 4)
+          asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+                       "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+                       "s_waitcnt lgkmcnt(0)"
+                       : "=&v"(yo[0]), "=&v"(yo[1]), "=&v"(yo[2]), "=&v"(yo[3])
+                       : "v"(a)
+                       : "memory");
+        else
+          asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                       : "=&v"(yo[0]), "=&v"(yo[1])
+                       : "v"(a)
+                       : "memory");
+      }
+#pragma unroll
+      for (int i = 0; i < NCO; ++i) {
+        const int gi = 64 * i + lane;
+        const int row = gi / GPR;
+        const u32x4 v = yo[i];
+        if (local0 + row < cpg) {
+          TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + (g * cpg + local0 + row) * p.y_sd;
+          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(yr + w0) + gi % GPR);
+        }
+      }
+      if (wave_live) carry_ops += NCO;  // exactly NCO store instructions were issued
+    } else if (live) {
+      TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
+      store_seg<kK>(y, t0, L, false, yv);
     }
     if constexpr (VEC && GATE) {
       if (w + 1 < nwin) {
@@ -480,24 +602,42 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
-int64_t nwin_of(const ScanArgs& a) { return (a.L + kW - 1) / kW; }
 
-template <typename TIn, typename TOut>
-hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
+// Channels per wave: the most that still leave several rounds of waves for the chip's 2048
+// two-per-SIMD slots, so that the last, partial round stays a small part of the run.
+int rows_of(const ScanArgs& a) {
+#ifdef SS_DIAG_ROWS
+  return SS_DIAG_ROWS;
+#else
+  const int64_t chans = a.batch * a.channels;
+  if (chans >= 4 * 2048 * 6) return 4;
+  if (chans >= 2 * 2048 * 3) return 2;
+  return 1;
+#endif
+}
+
+int64_t nwin_of(const ScanArgs& a, int rows) {
+  const int64_t W = (64 / rows) * kK;
+  return (a.L + W - 1) / W;
+}
+
+template <typename TIn, typename TOut, int ROWS>
+hipError_t launch_r(const ScanArgs& a, float* ws, hipStream_t s) {
   const int P = npairs_of(a);
-  const int64_t nwin = nwin_of(a);
+  const int64_t nwin = nwin_of(a, ROWS);
   {
-    const int64_t quads = a.batch * a.groups * nwin * P * 4 * kQ * 64;
+    const int64_t quads = a.batch * a.groups * nwin * P * 4 * kQ * (64 / ROWS);
     const int64_t blocks = std::min<int64_t>((quads + 255) / 256, 16384);
-    hipLaunchKernelGGL((bc_pack_kernel<TIn>), dim3((unsigned)blocks), dim3(256), 0, s, a,
+    hipLaunchKernelGGL((bc_pack_kernel<TIn, ROWS>), dim3((unsigned)blocks), dim3(256), 0, s, a,
                        reinterpret_cast<f32x4*>(ws), P, nwin);
   }
-  const int64_t blocks_per_bg = (a.chan_per_group + kWaves - 1) / kWaves;
-  const int64_t blocks = a.batch * a.groups * blocks_per_bg;  // one block per channel quad
+  const int64_t chans_per_block = kWaves * ROWS;
+  const int64_t blocks_per_bg = (a.chan_per_group + chans_per_block - 1) / chans_per_block;
+  const int64_t blocks = a.batch * a.groups * blocks_per_bg;
   const bool dma = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
 #define SS_LAUNCH(G, V) \
-  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V>), grid, block, 0, s, a, ws, P, nwin, blocks_per_bg)
+  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS>), grid, block, 0, s, a, ws, P, nwin, blocks_per_bg)
   if (a.z) {
     if (dma) SS_LAUNCH(true, true); else SS_LAUNCH(true, false);
   } else {
@@ -507,10 +647,20 @@ hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TIn, typename TOut>
+hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
+  switch (rows_of(a)) {
+    case 4: return launch_r<TIn, TOut, 4>(a, ws, s);
+    case 2: return launch_r<TIn, TOut, 2>(a, ws, s);
+    default: return launch_r<TIn, TOut, 1>(a, ws, s);
+  }
+}
+
 }  // namespace
 
 int64_t diag_workspace_floats(const ScanArgs& a) {
-  return a.batch * a.groups * nwin_of(a) * npairs_of(a) * (int64_t)kSlotFloats;
+  const int rows = rows_of(a);
+  return a.batch * a.groups * nwin_of(a, rows) * npairs_of(a) * (int64_t)(4 * (64 / rows) * kK);
 }
 
 hipError_t launch_diag(const ScanArgs& a, float* ws, hipStream_t s) {

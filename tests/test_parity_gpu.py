@@ -82,6 +82,14 @@ def test_lengths_bf16_copy_path(L):
     check(inputs.random_problem(300 + L, 1, 8, L, 16), "bf16 L=%d" % L)
 
 
+@pytest.mark.parametrize("channels,L", [(12288, 1064), (12288, 301), (49152, 536), (49152, 203)])
+def test_many_channels(channels, L):
+    """Enough channels that the launch packs 2 (12288) or 4 (49152) channels into each wave;
+    L a multiple of 8 (direct-to-LDS inputs, two whole windows and a partial one) or not."""
+    torch_dev()
+    check(inputs.random_problem(400 + L, 1, channels, L, 16), "%d channels L=%d" % (channels, L))
+
+
 def test_softplus_elementwise():
     """One step per channel with A = 0, u = B = C = 1: y = softplus(delta) exactly in the
     method, so every element checks the kernel's softplus against float64 (relative 4e-6)."""
