@@ -172,14 +172,16 @@ int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (scalar && A->stride[0] != 1 && A->shape[0] > 1) return SS_ERR_STRIDE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // stream-ordered workspace: B/C re-laid out (diagonal) or transposed (scalar decay)
+  if (!scalar) return ss::launch_diag(a, s) == hipSuccess ? SS_OK : SS_ERR_HIP;
+
+  // scalar decay: stream-ordered workspace for B/C in the order the kernel reads them
   float* ws = nullptr;
-  const int64_t wsf = scalar ? ss::scalar_workspace_floats(a) : ss::diag_workspace_floats(a);
+  const int64_t wsf = ss::scalar_workspace_floats(a);
   if (hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)wsf * sizeof(float), s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
   }
-  const hipError_t e = scalar ? ss::launch_scalar(a, ws, s) : ss::launch_diag(a, ws, s);
+  const hipError_t e = ss::launch_scalar(a, ws, s);
   const hipError_t f = hipFreeAsync(ws, s);
   return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
 }

@@ -8,7 +8,7 @@
 // the study notes' history and the bqwf.cn survey section 2.2) possible.
 //
 // Mapping on gfx950 (wave64):
-//  - a wave holds ROWS channels (1, 2 or 4) of one (batch, B/C group), each on a row of
+//  - a wave holds ROWS channels (1 or 2) of one (batch, B/C group), each on a row of
 //    64 / ROWS lanes laid along time: lane j of a row owns K consecutive steps, so one window
 //    of a channel covers (64 / ROWS) * K steps.  A block is 4 waves, i.e. 4 * ROWS channels
 //    sharing B and C.  Windows are walked in order; the state at the end of each window is
@@ -19,13 +19,12 @@
 //    a shift for the exclusive prefix), and each lane re-runs its K steps from the true
 //    incoming state to form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair
 //    are independent chains, which the wave interleaves (and whose two scans fill each other's
-//    DPP wait states).  More channels per wave means a shorter scan and less B/C traffic per
-//    channel; fewer means more waves for short batches; the launch picks;
-//  - B and C are shared by every channel of a (batch, group).  A small pre-pass widens them to
-//    f32 and lays them out per window and state pair exactly as the scan reads them from LDS;
-//    the scan then copies each pair into a three-slot LDS ring with direct-to-LDS loads
-//    (buffer_load ... lds), two pairs ahead of use, so the copy never passes through
-//    registers and overlaps two pairs of arithmetic;
+//    DPP wait states).  Two channels per wave means a shorter scan and half the B/C traffic per
+//    channel; one means more waves for short batches; the launch picks;
+//  - B and C are shared by every channel of a (batch, group).  Per state pair and window they
+//    are copied into LDS with direct-to-LDS loads (buffer_load ... lds) several pairs ahead of
+//    use, so the copies never pass through registers and overlap the arithmetic, and widened
+//    to f32 in LDS by the whole block one pair ahead of use (see "B/C stages" below);
 //  - u, delta and z of the next window are copied the same way into per-wave LDS slots while
 //    the current window runs (u and delta right after they are read, z after the gate), so no
 //    global load latency sits on the path.  The waits are explicit: before each ring barrier a
@@ -44,14 +43,12 @@ namespace {
 constexpr int kWaves = 4;                   // waves per block
 constexpr int kK = 16;                      // steps per lane
 constexpr int kQ = kK / 4;                  // 16-byte quads per lane of one row
-constexpr int kRing = 3;                    // pair slots in LDS
 constexpr int kMaxPairs = 64;               // N <= 128
 
-// Steps per window of one channel, floats of one pair slot (B, C of state 2p, then of 2p + 1),
-// and direct-to-LDS copies per wave per slot.
+// Steps per window of one channel and floats of one f32 pair stage (B, C of state 2p, then of
+// state 2p + 1).
 template <int ROWS> constexpr int win_steps() { return (64 / ROWS) * kK; }
 template <int ROWS> constexpr int slot_floats() { return 4 * win_steps<ROWS>(); }
-template <int ROWS> constexpr int slot_copies() { return slot_floats<ROWS>() / (kWaves * 256); }
 
 // Two independent exclusive scans, within each row of 64 / ROWS lanes (lane 0 of the row
 // earliest), of (a, b) pairs under (a1, b1) then (a2, b2) = (a1 a2, a2 b1 + b2).  Each step is
@@ -59,11 +56,11 @@ template <int ROWS> constexpr int slot_copies() { return slot_floats<ROWS>() / (
 // (b += b[src] * a) and v_mul_f32_dpp a, a[src], a.  A lane whose DPP source is outside its
 // 16-lane DPP row (row_shr) or whose DPP row is masked off (row_bcast with row_mask) is not
 // written, i.e. it keeps its pair, which is the same as combining with the identity (1, 0).
-// Steps: row_shr:1,2,4,8 scan each DPP row of 16 lanes; for 32-lane rows row_bcast:15 on DPP
-// rows 1 and 3 adds rows 0 and 2; for 64-lane rows row_bcast:31 on rows 2 and 3 then adds the
-// first half.  The exclusive prefix shifts by one lane inside the row (lane 0 of the row gets
-// the identity): wave_shr:1 for 64 lanes; for 16 and 32 lanes row_shr:1, with lane 16 of a
-// 32-lane row first given lane 15's value by row_bcast:15 on bank 0 of rows 1 and 3.  The two
+// Steps: row_shr:1,2,4,8 scan each DPP row of 16 lanes; row_bcast:15 on DPP rows 1 and 3 adds
+// rows 0 and 2 (a 32-lane channel row is complete here); for 64-lane rows row_bcast:31 on rows
+// 2 and 3 then adds the first half.  The exclusive prefix shifts by one lane inside the row
+// (lane 0 of the row gets the identity): wave_shr:1 for 64 lanes; for 32 lanes row_shr:1,
+// with lane 16 of the row first given lane 15's value by row_bcast:15 on bank 0.  The two
 // scans are interleaved so that every DPP read of a VGPR comes at least two instructions after
 // the VALU write of it (the hardware needs two wait states there); the leading s_nop covers
 // the compiler's last writes.
@@ -131,13 +128,7 @@ __device__ __forceinline__ void row_exclusive_scan2(float& a0, float& b0, float&
                  "s_waitcnt lgkmcnt(0)\n"
                  SS_OPS);
   } else {
-    static_assert(ROWS == 4, "1, 2 or 4 channels per wave");
-    asm volatile(SS_LOADC
-                 SS_SCAN16
-                 SS_IDENT
-                 SS_SHIFT("row_shr:1 row_mask:0xf bank_mask:0xf")
-                 "s_waitcnt lgkmcnt(0)\n"
-                 SS_OPS);
+    static_assert(ROWS == 1 || ROWS == 2, "1 or 2 channels per wave");
   }
 #undef SS_OPS
 #undef SS_LOADC
@@ -181,6 +172,42 @@ struct Seg {
   uint32_t w[kWords];
 };
 
+// lds_read8 plus CPT (1 or 2) 16-byte reads at rbase + 4 KB m, in the same statement.
+template <int CPT, int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
+__device__ __forceinline__ void lds_read8_plus(uint32_t base, f32x4 (&v)[8], uint32_t rbase, u32x4 (&raw)[CPT]) {
+  if constexpr (CPT == 1) {
+    asm volatile(
+        "ds_read_b128 %8, %10\n\t"
+        "ds_read_b128 %0, %9 offset:%11\n\tds_read_b128 %1, %9 offset:%12\n\t"
+        "ds_read_b128 %2, %9 offset:%13\n\tds_read_b128 %3, %9 offset:%14\n\t"
+        "ds_read_b128 %4, %9 offset:%15\n\tds_read_b128 %5, %9 offset:%16\n\t"
+        "ds_read_b128 %6, %9 offset:%17\n\tds_read_b128 %7, %9 offset:%18\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(raw[0])
+        : "v"(base), "v"(rbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+        : "memory");
+  } else {
+    static_assert(CPT == 2, "one or two chunks");
+    asm volatile(
+        "ds_read_b128 %8, %11\n\tds_read_b128 %9, %11 offset:4096\n\t"
+        "ds_read_b128 %0, %10 offset:%12\n\tds_read_b128 %1, %10 offset:%13\n\t"
+        "ds_read_b128 %2, %10 offset:%14\n\tds_read_b128 %3, %10 offset:%15\n\t"
+        "ds_read_b128 %4, %10 offset:%16\n\tds_read_b128 %5, %10 offset:%17\n\t"
+        "ds_read_b128 %6, %10 offset:%18\n\tds_read_b128 %7, %10 offset:%19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+          "=&v"(raw[0]), "=&v"(raw[1])
+        : "v"(base), "v"(rbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+        : "memory");
+  }
+}
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Two 16-byte LDS reads, waited for in the same statement.  The slots they read are filled by
 // direct-to-LDS copies whose completion the kernel establishes with its own vmcnt waits; read
 // through plain C++ the compiler would put a wait for every copy in flight (stage copies and
@@ -192,6 +219,12 @@ __device__ __forceinline__ void lds_read2(const void* p0, const void* p1, u32x4&
                : "=&v"(v0), "=&v"(v1)
                : "v"(a0), "v"(a1)
                : "memory");
+}
+
+__device__ __forceinline__ u32x4 lds_read1(const void* p0) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(lds_addr(p0)) : "memory");
+  return v;
 }
 
 // Eight 16-byte LDS reads at base + the given byte offsets, waited for in the same statement
@@ -209,10 +242,6 @@ __device__ __forceinline__ void lds_read8(uint32_t base, f32x4 (&v)[8]) {
       : "memory");
 }
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
 
 template <typename TIn>
 __device__ __forceinline__ void seg_read(const uint32_t* slot, int lane, Seg<TIn>& s) {
@@ -275,66 +304,65 @@ __device__ __forceinline__ void seg_fill(const TIn* row, int64_t t0, int64_t L, 
         u32x4{s.w[4 * c], s.w[4 * c + 1], s.w[4 * c + 2], s.w[4 * c + 3]};
 }
 
-// Pre-pass: B and C of every (batch, group) widened to f32, zero past L and past state N - 1,
-// in the order the scan copies them: [batch, group][window][pair][row r][quad i][lane j][4],
-// r = (B, C of state 2 pair, B, C of state 2 pair + 1), j over the 64 / ROWS lanes of a
-// channel row, and element e of quad i of lane j is window step K j + 4 i + e.  One thread
-// writes one 16-byte quad.
-template <typename TIn, int ROWS>
-__global__ __launch_bounds__(256) void bc_pack_kernel(ScanArgs p, f32x4* __restrict__ ws, int npairs,
-                                                      int64_t nwin) {
-  constexpr int LPC = 64 / ROWS;
-  const int64_t total = p.batch * p.groups * nwin * npairs * 4 * kQ * LPC;
-  const int64_t L = p.L;
-  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
-    const int j = (int)(o % LPC);
-    int64_t rest = o / LPC;
-    const int i = (int)(rest % kQ);
-    rest /= kQ;
-    const int r = (int)(rest % 4);
-    rest /= 4;
-    const int pair = (int)(rest % npairs);
-    rest /= npairs;
-    const int64_t win = rest % nwin;
-    const int64_t bg = rest / nwin;
-    const int64_t b = bg / p.groups, g = bg % p.groups;
-    const int n = 2 * pair + (r >> 1);
-    const int64_t t = win * win_steps<ROWS>() + (int64_t)j * kK + 4 * i;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (n < p.N) {
-      const TIn* row = (r & 1) ? static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg + n * p.C_sn
-                               : static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg + n * p.B_sn;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (t + e < L) v[e] = to_f32(row[t + e]);
-    }
-    ws[o] = v;
-  }
+// ---------------------------------------------------------------------------------------
+// B/C stages.  Pair p of window w is one stage: rows r = 0..3 are B, C of state 2p and B, C of
+// state 2p + 1 over the window's W steps.  For odd N the last pair's second state reads as
+// zeros (B = C = 0 leaves it at zero and out of y): its copies go through a buffer resource of
+// zero size, and loads outside a buffer resource's range return zero.  In LDS the scan reads a stage
+// as f32, row r's quad i (steps 4i..4i+3 of a lane) of lane j at float r W + (i LPC + j) 4, so
+// that every ds_read_b128 of a wave reads consecutive LDS.  How a stage gets there:
+//  - bf16 inputs, 16-byte rows: the four rows are copied raw (each wave one row, 16 bytes a
+//    lane, direct-to-LDS buffer loads) into a 3-slot raw ring three stages ahead of use; one
+//    stage ahead of use the block widens them into a 2-slot f32 ring (each thread 8 steps);
+//  - f32 inputs, 16-byte rows: copied straight into the f32 layout, into a 3-slot f32 ring two
+//    stages ahead of use;
+//  - anything else: loaded element by element and widened into the 2-slot f32 ring one stage
+//    ahead of use.
+enum class StageMode { kWiden, kDirect, kElementwise };
+
+template <typename TIn, bool VEC>
+constexpr StageMode stage_mode() {
+  return !VEC ? StageMode::kElementwise : (sizeof(TIn) == 2 ? StageMode::kWiden : StageMode::kDirect);
+}
+
+// One direct-to-LDS buffer load of 16 bytes per lane from a wave-uniform resource: lane i's
+// 16 bytes at byte offset voff land at lds_base + 16 i.
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t rs, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// 16-byte LDS write through asm (the compiler would otherwise wait for every copy in flight
+// before it, not knowing which LDS the copies write).
+__device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
-    ScanArgs p, const float* __restrict__ ws, int npairs, int64_t nwin, int64_t blocks_per_bg) {
+    ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
+  constexpr StageMode MODE = stage_mode<TIn, VEC>();
   constexpr int LPC = 64 / ROWS;                     // lanes per channel row
   constexpr int W = win_steps<ROWS>();               // steps per window of a channel
-  constexpr int SLOT = slot_floats<ROWS>();
-  constexpr int NDMA = slot_copies<ROWS>();          // this wave's copies per pair slot
+  constexpr int SLOT = slot_floats<ROWS>();          // floats of one f32 stage
+  constexpr int NF = MODE == StageMode::kDirect ? 3 : 2;       // f32 ring slots
+  constexpr int AHEAD = MODE == StageMode::kWiden ? 3 : 2;     // stages copied ahead of use
+  constexpr int ROWB = W * (int)sizeof(TIn);                   // bytes of one stage row
+  constexpr int NDMA = MODE == StageMode::kWiden ? ROWB / 1024 : W / 256;  // copies per wave per stage
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
   constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
   constexpr int GPR = LPC * NCO;                     // 16-byte granules of y per channel row
-  // y is staged in this wave's share of the last pair's ring slot when it fits there
-  constexpr bool kYInRing = SLOT / kWaves >= NCO * 256;
-  // ring[s]: one pair of B/C rows.  Row r of a slot holds quad i of lane j at float offset
-  // (i * LPC + j) * 4, so every ds_read_b128 reads consecutive LDS (the rows of a wave read
-  // the same addresses).
-  __shared__ __attribute__((aligned(16))) float ring[kRing][SLOT];
+  constexpr int CPT = W / 512;                       // 8-step chunks widened per thread per stage
+  static_assert(ROWS == 1 || ROWS == 2, "1 or 2 channels per wave");
+  __shared__ __attribute__((aligned(16))) float fring[NF][SLOT];
+  __shared__ __attribute__((aligned(16))) uint32_t rring[MODE == StageMode::kWiden ? 3 : 1]
+                                                       [MODE == StageMode::kWiden ? ROWB : 4];
   // per wave: u, delta, z of one window, and y on its way out
   __shared__ __attribute__((aligned(16))) uint32_t xin[kWaves][3][kSegWords];
-  __shared__ __attribute__((aligned(16))) uint32_t ystg[kWaves][kYInRing ? 4 : NCO * 256];
+  __shared__ __attribute__((aligned(16))) uint32_t ystg[kWaves][NCO * 256];
   // per (wave, row, pair): (A_2p, A_2p+1) * log2 e and the carried state of the pair.  A
-  // static array: the compiler then knows the ring copies in flight cannot write it, and
-  // reads of it need not wait for them.
+  // static array: the compiler then knows the copies in flight cannot write it, and reads of
+  // it need not wait for them.
   __shared__ float4 par[kWaves * ROWS * kMaxPairs];
 
   const int lane = threadIdx.x & 63;
@@ -359,7 +387,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   const TIn* zrow = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
   const float bias = p.bias ? p.bias[hd] : 0.f;
   const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
-  const float* wsq = ws + bg * nwin * P * (int64_t)SLOT;
+  const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
+  const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
   const int Qt = (int)(nwin * P);  // pair stages of this block, in order (window-major)
 
   float4* mypar = par + (wave * ROWS + r) * kMaxPairs;
@@ -374,20 +403,70 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   uint32_t* xd = xin[wave][1];
   uint32_t* xz = xin[wave][2];
 
-  // This wave's share of pair stage qs into ring slot s.  The copies go through a buffer
-  // resource over this (batch, group)'s stages of one window, so that the per-stage offset is
-  // a scalar and the lane offset a constant.
-  const uint32_t lane_off = (uint32_t)lane * 16u + (uint32_t)wave * (NDMA * 1024u);
-  auto stage_dma = [&](int qs, int s) {
-    const int64_t wq = qs / P;
-    const uint32_t off = (uint32_t)(qs - wq * P) * (uint32_t)(SLOT * 4);
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(wsq + wq * P * (int64_t)SLOT), (short)0, P * SLOT * 4, 0x00020000);
-    float* dst = &ring[s][wave * NDMA * 256];
+  // row r (0..3) of stage qs: its global row (nullptr for a state >= N) and first step
+  auto stage_row = [&](int qs, int rr, int64_t& t_first) -> const TIn* {
+    const int wq = qs / P;
+    const int pp = qs - wq * P;
+    const int n = 2 * pp + (rr >> 1);
+    t_first = (int64_t)wq * W;
+    if (n >= N) return nullptr;
+    return (rr & 1) ? Cg + n * p.C_sn : Bg + n * p.B_sn;
+  };
+  // Issue the copies of stage qs (kWiden: this wave's raw row; kDirect: this wave's row,
+  // already in the f32 layout).  Chunks past L copy the row's first chunk (in bounds; the
+  // scan masks those steps).
+  auto stage_copy = [&](int qs) {
+    int64_t t_first;
+    const TIn* row = stage_row(qs, wave, t_first);
+    const __amdgpu_buffer_rsrc_t rs =  // over the window, so offsets stay small; empty for no state
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(row ? row + t_first : Bg), (short)0,
+                                          row ? 0x7fffffff : 0, 0x00020000);
+    const int64_t lim = L - t_first;  // steps of this window inside the row
+    if constexpr (MODE == StageMode::kWiden) {
+      uint32_t* dst = rring[qs % 3] + wave * (ROWB / 4);
 #pragma unroll
-    for (int i = 0; i < NDMA; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + i * 256), 16,
-                                               lane_off + i * 1024, off, 0, 0);
+      for (int c = 0; c < NDMA; ++c) {
+        const int64_t tl = (int64_t)(c * 64 + lane) * 8;  // 8 bf16 a lane
+        dma16_buf(rs, (uint32_t)(tl < lim ? tl * 2 : 0), dst + c * 256);
+      }
+    } else {
+      float* dst = &fring[qs % 3][wave * W];
+#pragma unroll
+      for (int c = 0; c < NDMA; ++c) {
+        const int qd = c * 64 + lane;                  // quad (i, j) of the row in LDS order
+        const int64_t tl = (int64_t)(qd % LPC) * kK + 4 * (qd / LPC);
+        dma16_buf(rs, (uint32_t)(tl < lim ? tl * 4 : 0), dst + c * 256);
+      }
+    }
+  };
+  // Widen (kWiden: from the raw ring; kElementwise: from global memory) stage qs into f32 slot
+  // fs: each thread does CPT chunks of 8 consecutive steps of one row.
+  // (kWiden: raw[m] holds this thread's chunks of stage qs, read from the raw ring)
+  auto stage_widen = [&](int qs, int fs, const u32x4* raw) {
+    const uint32_t fbase = lds_addr(fring[fs]);
+#pragma unroll
+    for (int m = 0; m < CPT; ++m) {
+      const int k = (int)threadIdx.x + 256 * m;
+      const int rr = k / (W / 8), cc = k % (W / 8);
+      float v[8];
+      if constexpr (MODE == StageMode::kWiden) {
+        const uint32_t wd[4] = {raw[m].x, raw[m].y, raw[m].z, raw[m].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = bf16_lo(wd[e]);
+          v[2 * e + 1] = bf16_hi(wd[e]);
+        }
+      } else {
+        int64_t t_first;
+        const TIn* row = stage_row(qs, rr, t_first);
+        const int64_t t = t_first + 8 * cc;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = row && t + e < L ? to_f32(row[t + e]) : 0.f;
+      }
+      const int j = cc / 2, i0 = 2 * (cc % 2);
+      lds_write16(fbase + 4u * (uint32_t)(rr * W + (i0 * LPC + j) * 4), f32x4{v[0], v[1], v[2], v[3]});
+      lds_write16(fbase + 4u * (uint32_t)(rr * W + ((i0 + 1) * LPC + j) * 4), f32x4{v[4], v[5], v[6], v[7]});
+    }
   };
   auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
     const int64_t t0 = w * W + (int64_t)jl * kK;
@@ -395,17 +474,31 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     else seg_fill<TIn>(row, t0, L, slot, lane);
   };
 
+  // preamble: the first window's inputs and the first stages
   if constexpr (VEC) {
     x_copy(urow, 0, xu);
     x_copy(drow, 0, xd);
     if constexpr (GATE) x_copy(zrow, 0, xz);
   }
-  stage_dma(0, 0);
-  if (Qt > 1) stage_dma(1, 1);
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  if constexpr (MODE == StageMode::kWiden) {
+    for (int qs = 0; qs < 3 && qs < Qt; ++qs) stage_copy(qs);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    {
+      u32x4 raw[CPT];
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) raw[m] = lds_read1(rring[0] + ((int)threadIdx.x + 256 * m) * 4);
+      stage_widen(0, 0, raw);
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else if constexpr (MODE == StageMode::kDirect) {
+    for (int qs = 0; qs < 2 && qs < Qt; ++qs) stage_copy(qs);
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    stage_widen(0, 0, nullptr);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
 
   int q = 0;          // current pair stage
-  int slot = 0;       // its ring slot (q mod 3)
   int carry_ops = 0;  // memory ops issued in the last epilogue (counted by the first wait after it)
   for (int64_t w = 0; w < nwin; ++w) {
     const int64_t w0 = w * W;
@@ -461,18 +554,32 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     }
 
     for (int pp = 0; pp < P; ++pp) {
+      // copies of a later stage, and (kWiden, kElementwise) the next stage into f32
       int allow = pp == 0 ? boundary_ops : 0;
-      if (q + 2 < Qt) {
-        stage_dma(q + 2, slot == 0 ? 2 : slot - 1);
-        allow += NDMA;
+      if constexpr (MODE != StageMode::kElementwise) {
+        if (q + AHEAD < Qt) {
+          stage_copy(q + AHEAD);
+          allow += NDMA;
+        }
       }
+      if constexpr (MODE == StageMode::kElementwise)
+        if (q + 1 < Qt) stage_widen(q + 1, (q + 1) & 1, nullptr);
+      const int fs = MODE == StageMode::kDirect ? q % 3 : (q & 1);
       const float4 pv = mypar[pp];  // (A pair, carried state pair) of this lane's channel
       // this lane's B values of both states: quad i of row r of the slot is at byte offset
       // 4 W r + 16 (i LPC + j) from the slot
-      const uint32_t lbase = lds_addr(ring[slot]) + 16u * (uint32_t)jl;
+      const uint32_t lbase = lds_addr(fring[fs]) + 16u * (uint32_t)jl;
       constexpr int QS = 16 * LPC;
       f32x4 bq[8];  // B of state 2p (quads 0-3), then of state 2p + 1
-      lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq);
+      if constexpr (MODE == StageMode::kWiden) {
+        // with this thread's raw chunks of the next stage, widened right after
+        u32x4 raw[CPT];
+        lds_read8_plus<CPT, 0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(
+            lbase, bq, lds_addr(rring[(q + 1) % 3]) + 16u * threadIdx.x, raw);
+        if (q + 1 < Qt) stage_widen(q + 1, (q + 1) & 1, raw);
+      } else {
+        lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq);
+      }
       float av0[kK], bv0[kK], av1[kK], bv1[kK];
       float h0 = 0.f, h1 = 0.f;
 #pragma unroll
@@ -505,17 +612,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       }
       // the window's end state (the row's last lane) starts the same pair in the next window
       if (jl == LPC - 1) *reinterpret_cast<float2*>(&mypar[pp].z) = make_float2(h0, h1);
-      // the next stage's copies (this wave's and, after the barrier, everyone's) have landed
+      // The copies the next iteration reads (kDirect: stage q + 1; kWiden: stage q + 2, which
+      // it widens) have landed, this wave's and, after the barrier, everyone's; and every
+      // wave is done with the slots the next iteration overwrites.
       if (q + 1 < Qt) wait_vm_barrier(allow);
-      else asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // slot free for y
       ++q;
-      slot = slot == 2 ? 0 : slot + 1;
     }
 
     // epilogue: gate, store, then this slot's z for the next window.  Only the stage copy
     // issued by the last pair may still be in flight here: everything before it (this
     // window's z and the next window's u and delta) has landed.
-    if (q + 1 < Qt) {
+    if (MODE != StageMode::kElementwise && q - 1 + AHEAD < Qt) {
       if constexpr (NDMA == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
       else if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -536,12 +643,9 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       // g = NCO lane + c of the wave's window; it is kept at g ^ ((g >> 4) & (NCO - 1)) so that
       // neither the writes nor the reads conflict on banks, and store instruction i has lane
       // l take granule 64 i + l, i.e. granule (64 i + l) mod GPR of row (64 i + l) / GPR.
-      // (a ring slot is free once its pair's barrier has passed, and this wave's share of it
-      // is next written by this wave's own copy, issued after these reads)
       // (written and read through asm: plain C++ here would make the compiler wait for every
       // copy in flight)
-      const uint32_t sbase = kYInRing ? lds_addr(&ring[slot == 0 ? 2 : slot - 1][wave * (SLOT / kWaves)])
-                                      : lds_addr(ystg[wave]);
+      const uint32_t sbase = lds_addr(ystg[wave]);
 #pragma unroll
       for (int c = 0; c < NCO; ++c) {
         u32x4 gr;
@@ -603,16 +707,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
 int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
 
-// Channels per wave: the most that still leave several rounds of waves for the chip's 2048
-// two-per-SIMD slots, so that the last, partial round stays a small part of the run.
+// Channels per wave: two when that still leaves several rounds of waves for the chip's
+// 2048 two-per-SIMD slots (so that the last, partial round stays a small part of the run).
 int rows_of(const ScanArgs& a) {
 #ifdef SS_DIAG_ROWS
   return SS_DIAG_ROWS;
 #else
-  const int64_t chans = a.batch * a.channels;
-  if (chans >= 4 * 2048 * 6) return 4;
-  if (chans >= 2 * 2048 * 3) return 2;
-  return 1;
+  return a.batch * a.channels >= 2 * 2048 * 3 ? 2 : 1;
 #endif
 }
 
@@ -622,50 +723,37 @@ int64_t nwin_of(const ScanArgs& a, int rows) {
 }
 
 template <typename TIn, typename TOut, int ROWS>
-hipError_t launch_r(const ScanArgs& a, float* ws, hipStream_t s) {
+hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   const int P = npairs_of(a);
   const int64_t nwin = nwin_of(a, ROWS);
-  {
-    const int64_t quads = a.batch * a.groups * nwin * P * 4 * kQ * (64 / ROWS);
-    const int64_t blocks = std::min<int64_t>((quads + 255) / 256, 16384);
-    hipLaunchKernelGGL((bc_pack_kernel<TIn, ROWS>), dim3((unsigned)blocks), dim3(256), 0, s, a,
-                       reinterpret_cast<f32x4*>(ws), P, nwin);
-  }
   const int64_t chans_per_block = kWaves * ROWS;
   const int64_t blocks_per_bg = (a.chan_per_group + chans_per_block - 1) / chans_per_block;
   const int64_t blocks = a.batch * a.groups * blocks_per_bg;
-  const bool dma = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
+  // every time row 16-byte aligned and L a whole number of 16-byte chunks: copied with
+  // direct-to-LDS loads
+  const bool vec = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
 #define SS_LAUNCH(G, V) \
-  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS>), grid, block, 0, s, a, ws, P, nwin, blocks_per_bg)
+  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS>), grid, block, 0, s, a, P, nwin, blocks_per_bg)
   if (a.z) {
-    if (dma) SS_LAUNCH(true, true); else SS_LAUNCH(true, false);
+    if (vec) SS_LAUNCH(true, true); else SS_LAUNCH(true, false);
   } else {
-    if (dma) SS_LAUNCH(false, true); else SS_LAUNCH(false, false);
+    if (vec) SS_LAUNCH(false, true); else SS_LAUNCH(false, false);
   }
 #undef SS_LAUNCH
   return hipGetLastError();
 }
 
 template <typename TIn, typename TOut>
-hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
-  switch (rows_of(a)) {
-    case 4: return launch_r<TIn, TOut, 4>(a, ws, s);
-    case 2: return launch_r<TIn, TOut, 2>(a, ws, s);
-    default: return launch_r<TIn, TOut, 1>(a, ws, s);
-  }
+hipError_t launch_t(const ScanArgs& a, hipStream_t s) {
+  return rows_of(a) == 2 ? launch_r<TIn, TOut, 2>(a, s) : launch_r<TIn, TOut, 1>(a, s);
 }
 
 }  // namespace
 
-int64_t diag_workspace_floats(const ScanArgs& a) {
-  const int rows = rows_of(a);
-  return a.batch * a.groups * nwin_of(a, rows) * npairs_of(a) * (int64_t)(4 * (64 / rows) * kK);
-}
-
-hipError_t launch_diag(const ScanArgs& a, float* ws, hipStream_t s) {
-  if (a.in_bf16) return a.out_bf16 ? launch_t<bf16_t, bf16_t>(a, ws, s) : launch_t<bf16_t, float>(a, ws, s);
-  return a.out_bf16 ? launch_t<float, bf16_t>(a, ws, s) : launch_t<float, float>(a, ws, s);
+hipError_t launch_diag(const ScanArgs& a, hipStream_t s) {
+  if (a.in_bf16) return a.out_bf16 ? launch_t<bf16_t, bf16_t>(a, s) : launch_t<bf16_t, float>(a, s);
+  return a.out_bf16 ? launch_t<float, bf16_t>(a, s) : launch_t<float, float>(a, s);
 }
 
 }  // namespace ss

@@ -29,10 +29,9 @@ struct ScanArgs {
   int64_t y_sb, y_sd, A_sd;
 };
 
-// Diagonal decay A [channels, N]: one wave per (b, d) row, lanes along time.  `ws` must hold
-// diag_workspace_floats(a) floats of device memory (16-byte aligned), ordered on `stream`.
-int64_t diag_workspace_floats(const ScanArgs& a);
-hipError_t launch_diag(const ScanArgs& a, float* ws, hipStream_t stream);
+// Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time.  One
+// kernel, no workspace.
+hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
 
 // Scalar decay A [heads]: lanes along channels, 16 states per wave.  `ws` must hold
 // scalar_workspace_floats(a) floats of device memory, ordered on `stream`.
