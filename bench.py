@@ -180,7 +180,8 @@ def main():
                                        P=p.channels // p.heads)
     alu_tflops = flops / avg_launch_s / 1e12
     hbm_gbps = nbytes / avg_launch_s / 1e9
-    kernel = "scalar_fwd_kernel" if p.scalar_decay else "diag_fwd_kernel"
+    # the kernel that dominates the step (the diagonal path is that one kernel alone)
+    kernel = "scalar_head_kernel" if p.scalar_decay else "diag_fwd_kernel"
     traffic = stored_traffic(kernel, args.workload, kernel_source_digest(p.scalar_decay))
 
     out = {
