@@ -174,14 +174,16 @@ int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!scalar) return ss::launch_diag(a, s) == hipSuccess ? SS_OK : SS_ERR_HIP;
 
-  // scalar decay: stream-ordered workspace for B/C in the order the kernel reads them
-  float* ws = nullptr;
-  const int64_t wsf = ss::scalar_workspace_floats(a);
-  if (hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)wsf * sizeof(float), s) != hipSuccess) {
+  // scalar decay: stream-ordered workspace for B/C (and, on the matrix path, C B^T per chunk)
+  // in the order the kernel reads them
+  const bool mfma = ss::ssd_path(a);
+  void* ws = nullptr;
+  const int64_t wsb = mfma ? ss::ssd_workspace_bytes(a) : ss::scalar_workspace_floats(a) * (int64_t)sizeof(float);
+  if (hipMallocAsync(&ws, (size_t)wsb, s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
   }
-  const hipError_t e = ss::launch_scalar(a, ws, s);
+  const hipError_t e = mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
   const hipError_t f = hipFreeAsync(ws, s);
   return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
 }

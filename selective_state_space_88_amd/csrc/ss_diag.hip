@@ -42,7 +42,6 @@ namespace {
 
 constexpr int kWaves = 4;                   // waves per block
 constexpr int kK = 16;                      // steps per lane
-constexpr int kQ = kK / 4;                  // 16-byte quads per lane of one row
 constexpr int kMaxPairs = 64;               // N <= 128
 
 // Steps per window of one channel and floats of one f32 pair stage (B, C of state 2p, then of

@@ -38,4 +38,11 @@ hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
 int64_t scalar_workspace_floats(const ScanArgs& a);
 hipError_t launch_scalar(const ScanArgs& a, float* ws, hipStream_t stream);
 
+// Scalar decay in the chunked matrix form on MFMA (bf16 inputs, heads and B/C groups in whole
+// 64-channel slabs).  `ws` must hold ssd_workspace_bytes(a) bytes (16-byte aligned) of device
+// memory, ordered on `stream`.
+bool ssd_path(const ScanArgs& a);
+int64_t ssd_workspace_bytes(const ScanArgs& a);
+hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t stream);
+
 }  // namespace ss

@@ -1,0 +1,356 @@
+// ss_ssd.hip -- scalar-decay selective scan in its chunked matrix form, on MFMA (gfx950).
+//
+// Method.  With one scalar decay per head, a_t = exp(dt_t A_h) (bqwf.cn state-space survey,
+// section 3.2; omica.com.cn Mamba explainer, section 6.2), the recurrence over a chunk of T
+// steps is a masked matrix product.  With S_t = sum_{r <= t} log2(a_r) inside the chunk and
+// H the state entering it ([N, P] for the head's P channels):
+//   y_t  = sum_{s <= t} 2^(S_t - S_s) (C_t . B_s) dt_s u_s  +  2^(S_t) C_t H  +  D u_t
+//   H'   = 2^(S_{T-1}) H  +  sum_s 2^(S_{T-1} - S_s) B_s (dt_s u_s)
+// (expanding h_t = a_t h_{t-1} + dt_t B_t u_t from the chunk's start: the mask matrix of the
+// explainer's section 6.2 and the survey's block decomposition).  Per chunk that is
+//   Y = (G o L) X  +  diag(2^S) C H,     H' = 2^(S_{T-1}) H + B^T Xd,
+// G = C B^T [T, T], L the decay mask, X = dt u [T, P], Xd = X scaled by 2^(S_{T-1} - S_s):
+// three dense contractions, done here with v_mfma_f32_16x16x32_bf16.
+//
+// Precision: B, C and u are bf16 inputs, exact as MFMA operands.  The f32 operands (G o L, X,
+// Xd, H) are split as x = hi + lo with hi = bf16(x), lo = bf16(x - hi), and the products take
+// hi*hi + hi*lo + lo*hi (or hi + lo against an exact operand): relative error ~2^-16 per
+// product with f32 accumulation, and bf16's exponent range (nothing overflows that would not
+// overflow in f32).
+//
+// Mapping.  A pre-pass computes, per (batch, group, chunk), G in f32 and copies of C as
+// [t][n] and B as [n][t] (bf16, n padded to a multiple of 32 with zeros) into one record.
+// The scan gives each block one (batch, head, 64-channel slab) and walks the chunks in order;
+// wave w owns channels 16w..16w+15 of the slab and keeps their state H (N x 16) in MFMA
+// accumulators across chunks.  MFMA 16x16x32 operand layout (checked on the device): lane l
+// holds A[l % 16][8 (l / 16) + k], B[8 (l / 16) + k][l % 16] (k = 0..7), and
+// D[4 (l / 16) + r][l % 16] (r = 0..3).  C H takes H straight from the accumulators: the
+// contraction index n is permuted so that lane group g's eight K slots are the n it holds
+// (4g..4g+3 of two consecutive 16-row tiles), and C is read in the same order.
+#include <algorithm>
+
+#include "ss_device.h"
+#include "ss_launch.h"
+
+namespace ss {
+namespace {
+
+constexpr int kT = 32;          // steps per chunk
+constexpr int kSlab = 64;       // channels per block
+constexpr int kWaves = 4;       // one per 16 channels
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+int npad32(int N) { return (N + 31) / 32 * 32; }
+int64_t nchunks_of(const ScanArgs& a) { return (a.L + kT - 1) / kT; }
+// bytes of one chunk record: G [T][T] f32, C [T][Np] bf16, B [Np][T] bf16
+__host__ __device__ inline int64_t rec_bytes(int Np) { return (int64_t)kT * kT * 4 + 2LL * kT * Np * 2; }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// x = hi + lo, both bf16 (round to nearest even), for eight values
+__device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  u32x4 h, l;
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h0 = f32_to_bf16_bits(x[2 * e]), h1 = f32_to_bf16_bits(x[2 * e + 1]);
+    const float r0 = x[2 * e] - __uint_as_float(h0 << 16), r1 = x[2 * e + 1] - __uint_as_float(h1 << 16);
+    hw[e] = h0 | (h1 << 16);
+    lw[e] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
+  }
+  h = u32x4{hw[0], hw[1], hw[2], hw[3]};
+  l = u32x4{lw[0], lw[1], lw[2], lw[3]};
+  hi = as_bf16x8(h);
+  lo = as_bf16x8(l);
+}
+
+__device__ __forceinline__ f32x4v mfma(bf16x8 a, bf16x8 b, f32x4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pre-pass: one block per (batch, group, chunk).
+template <typename TIn>
+__global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __restrict__ ws, int Np,
+                                                       int64_t nchunks) {
+  __shared__ float sB[128][kT + 1], sC[128][kT + 1];
+  const int64_t bgc = blockIdx.x;
+  const int64_t c = bgc % nchunks, bg = bgc / nchunks;
+  const int64_t b = bg / p.groups, g = bg % p.groups;
+  const int64_t t0 = c * kT;
+  const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
+  const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
+  for (int i = threadIdx.x; i < Np * kT; i += 256) {
+    const int n = i / kT, t = i % kT;
+    const bool in = n < p.N && t0 + t < p.L;
+    sB[n][t] = in ? to_f32(Bg[n * p.B_sn + t0 + t]) : 0.f;
+    sC[n][t] = in ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.f;
+  }
+  __syncthreads();
+  uint8_t* rec = ws + bgc * rec_bytes(Np);
+  float* G = reinterpret_cast<float*>(rec);
+  uint16_t* Ct = reinterpret_cast<uint16_t*>(rec + kT * kT * 4);
+  uint16_t* Bn = Ct + kT * Np;
+  // G[t][s] = sum_n C[t][n] B[s][n]: products of bf16 values are exact in f32
+  for (int i = threadIdx.x; i < kT * kT; i += 256) {
+    const int t = i / kT, s = i % kT;
+    float acc = 0.f;
+    for (int n = 0; n < Np; ++n) acc = fmaf(sC[n][t], sB[n][s], acc);
+    G[i] = acc;
+  }
+  for (int i = threadIdx.x; i < kT * Np; i += 256) {
+    const int t = i / Np, n = i % Np;
+    Ct[i] = (uint16_t)(__float_as_uint(sC[n][t]) >> 16);  // exact: the value is a bf16
+  }
+  for (int i = threadIdx.x; i < Np * kT; i += 256) {
+    const int n = i / kT, t = i % kT;
+    Bn[i] = (uint16_t)(__float_as_uint(sB[n][t]) >> 16);
+  }
+}
+
+template <typename TOut, bool GATE>
+__global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const uint8_t* __restrict__ ws,
+                                                               int Np, int64_t nchunks) {
+  using TIn = bf16_t;
+  constexpr int kRecMax = kT * kT * 4 + 2 * kT * 128 * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t srec[kRecMax];
+  __shared__ __attribute__((aligned(16))) uint16_t su[kSlab][kT];   // u of the slab's channels
+  __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab : 1][kT];
+  // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, 2^(S_{T-1} - S)
+  __shared__ __attribute__((aligned(16))) float sw[kWaves][4][kT];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g16 = lane >> 4, q = lane & 15;
+  const int64_t L = p.L;
+  const int64_t slabs = p.chan_per_head / kSlab;
+  const int64_t blk = blockIdx.x;
+  const int64_t slab = blk % slabs, bh = blk / slabs;
+  const int64_t b = bh / p.heads, h = bh % p.heads;
+  const int64_t c0 = h * p.chan_per_head + slab * kSlab;   // first channel of the slab
+  const int64_t grp = c0 / p.chan_per_group;
+  const float A2 = p.A[h] * kLog2e;
+  const float bias = p.bias ? p.bias[h] : 0.f;
+  const int64_t rb = rec_bytes(Np);
+  const uint8_t* recs = ws + (b * p.groups + grp) * nchunks * rb;
+  const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + h * p.dl_sh;
+  const int nk = Np / 16;   // state tiles of 16
+
+  // this wave's state H[n][16w + q]: tile k holds rows 16k + 4 g16 + r
+  f32x4v hacc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
+
+  // staging of one chunk: record (rb bytes) and the u (and z) tile, 16 bytes per thread a piece
+  const int nrec16 = (int)(rb / 16);
+  auto stage_in = [&](int64_t c) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb);
+    u32x4* dst = reinterpret_cast<u32x4*>(srec);
+    for (int i = threadIdx.x; i < nrec16; i += 256) dst[i] = src[i];
+    // u tile: thread -> channel row threadIdx / 4, 8 steps (threadIdx % 4) * 8
+    const int pr = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 8;
+    const int64_t t = c * kT + seg;
+    const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    if (p.vec && t + 8 <= L) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ur + t);
+      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t + e < L) w[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(ur)[t + e] << (16 * (e % 2));
+    }
+    *reinterpret_cast<u32x4*>(&su[pr][seg]) = u32x4{w[0], w[1], w[2], w[3]};
+    if constexpr (GATE) {
+      const TIn* zr = static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd;
+      uint32_t v2[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (t + e < L) v2[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(zr)[t + e] << (16 * (e % 2));
+      *reinterpret_cast<u32x4*>(&sz[pr][seg]) = u32x4{v2[0], v2[1], v2[2], v2[3]};
+    }
+  };
+
+  const float* G = reinterpret_cast<const float*>(srec);
+  const uint16_t* Ct = reinterpret_cast<const uint16_t*>(srec + kT * kT * 4);
+  const uint16_t* Bn = Ct + kT * Np;
+  float* wdt = sw[wave][0];
+  float* wS = sw[wave][1];
+  float* weS = sw[wave][2];
+  float* weD = sw[wave][3];
+  const int pch = 16 * wave + q;   // this lane's channel in the slab (B operand / D column)
+
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t t0 = c * kT;
+    __syncthreads();  // the previous chunk's reads of the staging buffers are done
+    stage_in(c);
+    // dt and S of the chunk, in lanes 0..31 of every wave (each wave keeps its own copy)
+    {
+      const int t = lane & (kT - 1);
+      float dt = 0.f;
+      if (lane < kT && t0 + t < L) {
+        const float x = to_f32(drow[t0 + t]) + bias;
+        dt = p.softplus ? softplus_fast(x) : x;
+      }
+      // inclusive prefix sum of dt * A * log2 e over the 32 lanes
+      float s = dt * A2;
+#pragma unroll
+      for (int d = 1; d < kT; d <<= 1) {
+        const float o = __shfl_up(s, d, 64);
+        if (t >= d) s += o;
+      }
+      const float sEnd = __shfl(s, kT - 1, 64);
+      if (lane < kT) {
+        wdt[t] = dt;
+        wS[t] = s;
+        weS[t] = __builtin_amdgcn_exp2f(s);
+        weD[t] = __builtin_amdgcn_exp2f(sEnd - s);
+      }
+    }
+    __syncthreads();  // staging visible to every wave
+    const float eT = weS[kT - 1];
+
+    // X[s][pch] and Xd[s][pch] for s = 8 g16 + k: the B operand of both contractions over s
+    bf16x8 xhi, xlo, xdhi, xdlo;
+    {
+      const u32x4 uw = *reinterpret_cast<const u32x4*>(&su[pch][8 * g16]);
+      const uint32_t uwv[4] = {uw.x, uw.y, uw.z, uw.w};
+      float x[8], xd[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float uu = (k & 1) ? bf16_hi(uwv[k / 2]) : bf16_lo(uwv[k / 2]);
+        x[k] = wdt[8 * g16 + k] * uu;
+        xd[k] = x[k] * weD[8 * g16 + k];
+      }
+      split8(x, xhi, xlo);
+      split8(xd, xdhi, xdlo);
+    }
+
+    // y tiles: t-tile i (rows 16 i + 4 g16 + r), this wave's 16 channels
+    f32x4v yacc[2], iacc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
+    // within the chunk: A operand (G o L)[t = 16 i + q][s = 8 g16 + k]
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 16 * i + q;
+      const float St = wS[t];
+      float m[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = 8 * g16 + k;
+        m[k] = s <= t ? G[t * kT + s] * __builtin_amdgcn_exp2f(St - wS[s]) : 0.f;
+      }
+      bf16x8 mhi, mlo;
+      split8(m, mhi, mlo);
+      yacc[i] = mfma(mhi, xhi, yacc[i]);
+      yacc[i] = mfma(mhi, xlo, yacc[i]);
+      yacc[i] = mfma(mlo, xhi, yacc[i]);
+    }
+    // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (2 * ks < nk) {
+        float hv[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          hv[r] = hacc[2 * ks][r];
+          hv[4 + r] = hacc[2 * ks + 1][r];
+        }
+        bf16x8 hhi, hlo;
+        split8(hv, hhi, hlo);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint16_t* cr = Ct + (16 * i + q) * Np + 32 * ks + 4 * g16;
+          const uint2 c0w = *reinterpret_cast<const uint2*>(cr);
+          const uint2 c1w = *reinterpret_cast<const uint2*>(cr + 16);
+          const bf16x8 ca = as_bf16x8(u32x4{c0w.x, c0w.y, c1w.x, c1w.y});
+          iacc[i] = mfma(ca, hhi, iacc[i]);
+          iacc[i] = mfma(ca, hlo, iacc[i]);
+        }
+      }
+    }
+    // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
+    {
+      const int64_t ch = c0 + pch;
+      const float Dd = p.D ? p.D[p.d_per_head ? h : ch] : 0.f;
+      TOut* yr = static_cast<TOut*>(p.y) + b * p.y_sb + ch * p.y_sd;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int tl = 16 * i + 4 * g16;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = tl + r;
+          const uint16_t ub = su[pch][t];
+          float yy = yacc[i][r] + weS[t] * iacc[i][r] + Dd * __uint_as_float((uint32_t)ub << 16);
+          if constexpr (GATE) yy *= silu_fast(__uint_as_float((uint32_t)sz[pch][t] << 16));
+          v[r] = yy;
+        }
+        const int64_t tg = t0 + tl;
+        if (tg + 4 <= L) {
+          if constexpr (sizeof(TOut) == 4) {
+            if (p.vec) {
+              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(yr + tg));
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) store_one(yr + tg + r, v[r]);
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_one(yr + tg + r, v[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (tg + r < L) store_one(yr + tg + r, v[r]);
+        }
+      }
+    }
+    // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (k < nk) {
+        hacc[k] = hacc[k] * eT;
+        const u32x4 bw = *reinterpret_cast<const u32x4*>(Bn + (16 * k + q) * kT + 8 * g16);
+        const bf16x8 ba = as_bf16x8(bw);
+        hacc[k] = mfma(ba, xdhi, hacc[k]);
+        hacc[k] = mfma(ba, xdlo, hacc[k]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool ssd_path(const ScanArgs& a) {
+  return a.in_bf16 && a.chan_per_head % kSlab == 0 && a.chan_per_group % kSlab == 0;
+}
+
+int64_t ssd_workspace_bytes(const ScanArgs& a) {
+  return a.batch * a.groups * nchunks_of(a) * rec_bytes(npad32(a.N));
+}
+
+hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t s) {
+  const int Np = npad32(a.N);
+  const int64_t nch = nchunks_of(a);
+  hipLaunchKernelGGL((ssd_prep_kernel<bf16_t>), dim3((unsigned)(a.batch * a.groups * nch)), dim3(256), 0, s, a,
+                     static_cast<uint8_t*>(ws), Np, nch);
+  const int64_t blocks = a.batch * a.heads * (a.chan_per_head / kSlab);
+  const dim3 grid((unsigned)blocks), block(64 * kWaves);
+  const uint8_t* w = static_cast<const uint8_t*>(ws);
+  if (a.out_bf16) {
+    if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, true>), grid, block, 0, s, a, w, Np, nch);
+    else hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, false>), grid, block, 0, s, a, w, Np, nch);
+  } else {
+    if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<float, true>), grid, block, 0, s, a, w, Np, nch);
+    else hipLaunchKernelGGL((ssd_scan_kernel<float, false>), grid, block, 0, s, a, w, Np, nch);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ss

@@ -90,6 +90,26 @@ def test_many_channels(channels, L):
     check(inputs.random_problem(400 + L, 1, channels, L, 16), "%d channels L=%d" % (channels, L))
 
 
+@pytest.mark.parametrize("N,L,headdim,gate", [
+    (1, 100, 64, False), (16, 33, 64, True), (17, 1000, 64, False), (40, 31, 64, False),
+    (64, 257, 128, True), (128, 2048, 64, False), (128, 1, 64, True)])
+def test_scalar_matrix_path(N, L, headdim, gate):
+    """bf16 inputs, heads of whole 64-channel slabs: the chunked matrix (MFMA) form; ragged
+    chunks (32 steps), state counts padded to 32, two slabs per head, the gate."""
+    torch_dev()
+    check(inputs.random_problem(500 + N + L, 2, 2 * headdim, L, N, heads=2, scalar_decay=True, gate=gate),
+          "scalar matrix N=%d L=%d P=%d gate=%s" % (N, L, headdim, gate))
+
+
+@pytest.mark.parametrize("opts", [dict(softplus=False), dict(with_D=False), dict(with_bias=False),
+                                  dict(groups=2), dict(in_dtype="f32")])
+def test_scalar_matrix_options(opts):
+    """The matrix path's options; f32 inputs take the sequential kernel (bar 1e-5)."""
+    torch_dev()
+    check(inputs.random_problem(600, 1, 256, 700, 32, heads=4, scalar_decay=True, **opts),
+          "scalar 4x64 %s" % opts)
+
+
 def test_softplus_elementwise():
     """One step per channel with A = 0, u = B = C = 1: y = softplus(delta) exactly in the
     method, so every element checks the kernel's softplus against float64 (relative 4e-6)."""
