@@ -16,6 +16,8 @@ FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
     # packed FP32 (v_pk_*_f32) stays off: plain f32 VALU code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the scan updates them with VALU work every chunk
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

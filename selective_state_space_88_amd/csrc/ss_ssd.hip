@@ -49,21 +49,19 @@ __host__ __device__ inline int64_t rec_bytes(int Np) { return (int64_t)kT * kT *
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// x = hi + lo, both bf16 (round to nearest even), for eight values
+// x = hi + lo, both bf16 (round to nearest even: v_cvt_pk_bf16_f32), for eight values
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
-  u32x4 h, l;
-  uint32_t hw[4], lw[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t h0 = f32_to_bf16_bits(x[2 * e]), h1 = f32_to_bf16_bits(x[2 * e + 1]);
-    const float r0 = x[2 * e] - __uint_as_float(h0 << 16), r1 = x[2 * e + 1] - __uint_as_float(h1 << 16);
-    hw[e] = h0 | (h1 << 16);
-    lw[e] = f32_to_bf16_bits(r0) | (f32_to_bf16_bits(r1) << 16);
-  }
-  h = u32x4{hw[0], hw[1], hw[2], hw[3]};
-  l = u32x4{lw[0], lw[1], lw[2], lw[3]};
-  hi = as_bf16x8(h);
-  lo = as_bf16x8(l);
+  for (int k = 0; k < 8; ++k) hi[k] = (__bf16)x[k];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) lo[k] = (__bf16)(x[k] - (float)hi[k]);
+}
+
+// DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source, and lanes of
+// masked rows, read 0
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_zero(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWMASK, 0xf, true));
 }
 
 __device__ __forceinline__ f32x4v mfma(bf16x8 a, bf16x8 b, f32x4v c) {
@@ -109,11 +107,12 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __re
   }
 }
 
-template <typename TOut, bool GATE>
+template <typename TOut, bool GATE, int NP>
 __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const uint8_t* __restrict__ ws,
-                                                               int Np, int64_t nchunks) {
+                                                               int64_t nchunks) {
   using TIn = bf16_t;
-  constexpr int kRecMax = kT * kT * 4 + 2 * kT * 128 * 2;
+  constexpr int Np = NP;    // states padded to a multiple of 32
+  constexpr int kRecMax = kT * kT * 4 + 2 * kT * NP * 2;
   __shared__ __attribute__((aligned(16))) uint8_t srec[kRecMax];
   __shared__ __attribute__((aligned(16))) uint16_t su[kSlab][kT];   // u of the slab's channels
   __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab : 1][kT];
@@ -135,41 +134,47 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   const int64_t rb = rec_bytes(Np);
   const uint8_t* recs = ws + (b * p.groups + grp) * nchunks * rb;
   const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + h * p.dl_sh;
-  const int nk = Np / 16;   // state tiles of 16
+  constexpr int nk = Np / 16;   // state tiles of 16
 
   // this wave's state H[n][16w + q]: tile k holds rows 16k + 4 g16 + r
   f32x4v hacc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
 
-  // staging of one chunk: record (rb bytes) and the u (and z) tile, 16 bytes per thread a piece
-  const int nrec16 = (int)(rb / 16);
-  auto stage_in = [&](int64_t c) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb);
-    u32x4* dst = reinterpret_cast<u32x4*>(srec);
-    for (int i = threadIdx.x; i < nrec16; i += 256) dst[i] = src[i];
-    // u tile: thread -> channel row threadIdx / 4, 8 steps (threadIdx % 4) * 8
-    const int pr = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 8;
-    const int64_t t = c * kT + seg;
-    const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
+  // Staging: chunk c + 1's record (rb bytes) and u (and z) tile are loaded into registers, 16
+  // bytes per thread a piece, while chunk c is computed, and written to LDS at the top of the
+  // next iteration.
+  constexpr int kRecPieces = kRecMax / 16 / 256;   // 16-byte record pieces per thread (exact)
+  static_assert(kRecMax % (16 * 256) == 0, "record pieces");
+  const int pr = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 8;  // u / z tile piece of this thread
+  const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
+  const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd : nullptr;
+  u32x4 pf_rec[kRecPieces], pf_u, pf_z;
+  uint32_t pf_d = 0u;   // raw bits of delta at step (lane % 32) of the prefetched chunk
+  auto load_piece = [&](const TIn* row, int64_t t) -> u32x4 {
+    if (p.vec && t + 8 <= L) return *reinterpret_cast<const u32x4*>(row + t);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
-    if (p.vec && t + 8 <= L) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ur + t);
-      w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t + e < L) w[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(ur)[t + e] << (16 * (e % 2));
-    }
-    *reinterpret_cast<u32x4*>(&su[pr][seg]) = u32x4{w[0], w[1], w[2], w[3]};
-    if constexpr (GATE) {
-      const TIn* zr = static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd;
-      uint32_t v2[4] = {0u, 0u, 0u, 0u};
+    for (int e = 0; e < 8; ++e)
+      if (t + e < L) w[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(row)[t + e] << (16 * (e % 2));
+    return u32x4{w[0], w[1], w[2], w[3]};
+  };
+  auto prefetch = [&](int64_t c) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb);
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (t + e < L) v2[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(zr)[t + e] << (16 * (e % 2));
-      *reinterpret_cast<u32x4*>(&sz[pr][seg]) = u32x4{v2[0], v2[1], v2[2], v2[3]};
-    }
+    for (int m = 0; m < kRecPieces; ++m) pf_rec[m] = src[threadIdx.x + 256 * m];
+    pf_u = load_piece(ur, c * kT + seg);
+    if constexpr (GATE) pf_z = load_piece(zr, c * kT + seg);
+    // (kept raw: widening it here would make the compiler wait for every load just issued)
+    const int64_t t = c * kT + (lane & (kT - 1));
+    pf_d = reinterpret_cast<const uint16_t*>(drow)[t < L ? t : 0];
+  };
+  auto commit = [&]() {
+    u32x4* dst = reinterpret_cast<u32x4*>(srec);
+#pragma unroll
+    for (int m = 0; m < kRecPieces; ++m) dst[threadIdx.x + 256 * m] = pf_rec[m];
+    *reinterpret_cast<u32x4*>(&su[pr][seg]) = pf_u;
+    if constexpr (GATE) *reinterpret_cast<u32x4*>(&sz[pr][seg]) = pf_z;
   };
 
   const float* G = reinterpret_cast<const float*>(srec);
@@ -180,27 +185,38 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   float* weS = sw[wave][2];
   float* weD = sw[wave][3];
   const int pch = 16 * wave + q;   // this lane's channel in the slab (B operand / D column)
+  // (read once here: inside the loop the compiler reloads it after every y store, and the
+  // reload's wait would also wait for the next chunk's prefetch)
+  const float Dd = p.D ? p.D[p.d_per_head ? h : c0 + pch] : 0.f;
 
+  prefetch(0);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kT;
     __syncthreads();  // the previous chunk's reads of the staging buffers are done
-    stage_in(c);
+    commit();
+    const float draw = __uint_as_float(pf_d << 16);
+    prefetch(c + 1 < nchunks ? c + 1 : c);  // (the last chunk loads itself again, unused)
+    // keep the prefetch here, at the top: the scheduler would otherwise sink the loads to the
+    // end of the iteration, where the next commit waits for them at once
+    __builtin_amdgcn_sched_barrier(0);
     // dt and S of the chunk, in lanes 0..31 of every wave (each wave keeps its own copy)
     {
       const int t = lane & (kT - 1);
       float dt = 0.f;
       if (lane < kT && t0 + t < L) {
-        const float x = to_f32(drow[t0 + t]) + bias;
+        const float x = draw + bias;
         dt = p.softplus ? softplus_fast(x) : x;
       }
-      // inclusive prefix sum of dt * A * log2 e over the 32 lanes
+      // inclusive prefix sum of dt * A * log2 e over lanes 0..31: DPP row_shr 1, 2, 4, 8
+      // within rows of 16 (a source outside the row reads 0), then row 0's total added to
+      // row 1 (row_bcast:15 on rows 1 and 3)
       float s = dt * A2;
-#pragma unroll
-      for (int d = 1; d < kT; d <<= 1) {
-        const float o = __shfl_up(s, d, 64);
-        if (t >= d) s += o;
-      }
-      const float sEnd = __shfl(s, kT - 1, 64);
+      s += dpp_zero<0x111, 0xf>(s);
+      s += dpp_zero<0x112, 0xf>(s);
+      s += dpp_zero<0x114, 0xf>(s);
+      s += dpp_zero<0x118, 0xf>(s);
+      s += dpp_zero<0x142, 0xa>(s);
+      const float sEnd = readlane_f(s, kT - 1);
       if (lane < kT) {
         wdt[t] = dt;
         wS[t] = s;
@@ -243,7 +259,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int s = 8 * g16 + k;
-        m[k] = s <= t ? G[t * kT + s] * __builtin_amdgcn_exp2f(St - wS[s]) : 0.f;
+        const float v = G[t * kT + s] * __builtin_amdgcn_exp2f(fminf(St - wS[s], 0.f));
+        m[k] = s <= t ? v : 0.f;
       }
       bf16x8 mhi, mlo;
       split8(m, mhi, mlo);
@@ -276,9 +293,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     }
     // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
     {
-      const int64_t ch = c0 + pch;
-      const float Dd = p.D ? p.D[p.d_per_head ? h : ch] : 0.f;
-      TOut* yr = static_cast<TOut*>(p.y) + b * p.y_sb + ch * p.y_sd;
+      TOut* yr = static_cast<TOut*>(p.y) + b * p.y_sb + (c0 + pch) * p.y_sd;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tl = 16 * i + 4 * g16;
@@ -343,13 +358,21 @@ hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t s) {
   const int64_t blocks = a.batch * a.heads * (a.chan_per_head / kSlab);
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
   const uint8_t* w = static_cast<const uint8_t*>(ws);
-  if (a.out_bf16) {
-    if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, true>), grid, block, 0, s, a, w, Np, nch);
-    else hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, false>), grid, block, 0, s, a, w, Np, nch);
-  } else {
-    if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<float, true>), grid, block, 0, s, a, w, Np, nch);
-    else hipLaunchKernelGGL((ssd_scan_kernel<float, false>), grid, block, 0, s, a, w, Np, nch);
+#define SS_NP(NPV)                                                                                         \
+  case NPV:                                                                                                \
+    if (a.out_bf16) {                                                                                      \
+      if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, true, NPV>), grid, block, 0, s, a, w, nch);     \
+      else hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, false, NPV>), grid, block, 0, s, a, w, nch);        \
+    } else {                                                                                               \
+      if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<float, true, NPV>), grid, block, 0, s, a, w, nch);      \
+      else hipLaunchKernelGGL((ssd_scan_kernel<float, false, NPV>), grid, block, 0, s, a, w, nch);         \
+    }                                                                                                      \
+    break;
+  switch (Np) {
+    SS_NP(32) SS_NP(64) SS_NP(96) SS_NP(128)
+    default: return hipErrorInvalidValue;
   }
+#undef SS_NP
   return hipGetLastError();
 }
 
