@@ -28,6 +28,7 @@ METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 
 # MI355X published peaks
 HBM_PEAK_GBPS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 128 FP32 FMA lanes/clk x 2 FLOP x 2.4 GHz
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 
 # ALU work model, per element (one (b, d, t)), in FP32 FLOP-equivalents: an FMA is 2, a
 # multiply or add 1, and a transcendental (v_exp/v_log/v_rcp, which issues at a quarter of the
@@ -52,11 +53,28 @@ def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
     return per
 
 
-def kernel_source_digest(scalar_decay):
-    """sha256 of the HIP source of the kernel the workload runs (to match stored counters)."""
+# source file of each scan kernel
+KERNEL_SOURCE = {"diag_fwd_kernel": "ss_diag.hip", "scalar_head_kernel": "ss_scalar.hip",
+                 "ssd_scan_kernel": "ss_ssd.hip"}
+
+
+def scan_kernel(p):
+    """Name of the kernel that dominates one call on this workload (the library's own choice:
+    scalar decay with bf16 inputs and heads of a multiple of 64 channels takes the matrix form)."""
+    if not p.scalar_decay:
+        return "diag_fwd_kernel"
+    P = p.channels // p.heads
+    cpg = p.channels // p.groups
+    if p.in_dtype == "bf16" and P % 64 == 0 and cpg % 64 == 0:
+        return "ssd_scan_kernel"
+    return "scalar_head_kernel"
+
+
+def kernel_source_digest(kernel):
+    """sha256 of the HIP source of the kernel (to match stored counters)."""
     import hashlib
 
-    name = "ss_scalar.hip" if scalar_decay else "ss_diag.hip"
+    name = KERNEL_SOURCE[kernel]
     path = os.path.join(ROOT, "selective_state_space_88_amd", "csrc", name)
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -84,6 +102,13 @@ def stored_traffic(kernel, workload, digest):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def describe(p):
+    """One line naming the workload: its name, input types and flags."""
+    ins = "u/delta" + ("/z" if p.gate else "") + "/B/C"
+    flags = ["softplus" if p.softplus else "raw delta"] + (["silu gate"] if p.gate else ["no gate"])
+    return "%s: %s %s, f32 A/D/delta_bias, %s, y f32" % (p.name, p.in_dtype, ins, " + ".join(flags))
 
 
 def algorithmic_bytes(p, y_bytes):
@@ -181,8 +206,8 @@ def main():
     alu_tflops = flops / avg_launch_s / 1e12
     hbm_gbps = nbytes / avg_launch_s / 1e9
     # the kernel that dominates the step (the diagonal path is that one kernel alone)
-    kernel = "scalar_head_kernel" if p.scalar_decay else "diag_fwd_kernel"
-    traffic = stored_traffic(kernel, args.workload, kernel_source_digest(p.scalar_decay))
+    kernel = scan_kernel(p)
+    traffic = stored_traffic(kernel, args.workload, kernel_source_digest(kernel))
 
     out = {
         "metric": METRIC,
@@ -198,8 +223,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": p.name + ": bf16 u/delta/z/B/C, f32 A/D/delta_bias, softplus + silu gate, "
-                        "y f32" if args.workload != 0 else p.name,
+            "workload": describe(p),
             "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
             "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
             "kernel": kernel,
@@ -219,6 +243,18 @@ def main():
         },
         "cpu_baseline": None,
     }
+
+    if kernel == "ssd_scan_kernel":
+        # the matrix form runs on v_mfma_f32_16x16x32_bf16 (16*16*32*2 flops each): per
+        # (batch, head, 64-channel slab, 32-step chunk) each of 4 waves issues 6 for the masked
+        # product, Np/8 for the readout from the carried state and Np/8 for the state update
+        # (Np = N padded to a multiple of 32), counting the bf16 hi/lo split passes
+        Np = (p.nstate + 31) // 32 * 32
+        nch = (p.length + 31) // 32
+        mf = p.batch * p.heads * (p.channels // p.heads // 64) * nch * 4 * (6 + Np // 4) * 16384.0
+        mf_tflops = mf / avg_launch_s / 1e12
+        out["roofline"].update({"mfma_executed_flops_per_launch": mf, "mfma_achieved_TFLOPs": mf_tflops,
+                                "mfma_frac_bf16_peak": mf_tflops / BF16_MFMA_PEAK_TFLOPS})
 
     if not args.no_cpu_baseline:
         import oracle

@@ -18,8 +18,9 @@
 // product with f32 accumulation, and bf16's exponent range (nothing overflows that would not
 // overflow in f32).
 //
-// Mapping.  A pre-pass computes, per (batch, group, chunk), G in f32 and copies of C as
-// [t][n] and B as [n][t] (bf16, n padded to a multiple of 32 with zeros) into one record.
+// Mapping.  A pre-pass computes, per (batch, group, chunk), G (causally masked) in f32 and
+// copies of C and B (bf16, n padded to a multiple of 32 with zeros) into one record, each
+// operand stored in the order the MFMA lanes consume it.
 // The scan gives each block one (batch, head, 64-channel slab) and walks the chunks in order;
 // wave w owns channels 16w..16w+15 of the slab and keeps their state H (N x 16) in MFMA
 // accumulators across chunks.  MFMA 16x16x32 operand layout (checked on the device): lane l
@@ -86,24 +87,36 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __re
     sC[n][t] = in ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.f;
   }
   __syncthreads();
+  // the record holds every operand in the order the scan's MFMA lanes read it (lane l =
+  // 16 g + q holds row q, K slots 8 g .. 8 g + 7), so that each wave reads it as contiguous
+  // 16-byte pieces with no LDS bank conflicts
   uint8_t* rec = ws + bgc * rec_bytes(Np);
-  float* G = reinterpret_cast<float*>(rec);
-  uint16_t* Ct = reinterpret_cast<uint16_t*>(rec + kT * kT * 4);
-  uint16_t* Bn = Ct + kT * Np;
-  // G[t][s] = sum_n C[t][n] B[s][n]: products of bf16 values are exact in f32
+  // G [i][half][lane][4] f32: (G o causal)[t = 16 i + q][s = 8 g + 4 half + e], where
+  // G[t][s] = sum_n C[t][n] B[s][n] (products of bf16 values are exact in f32)
+  float* Gp = reinterpret_cast<float*>(rec);
   for (int i = threadIdx.x; i < kT * kT; i += 256) {
-    const int t = i / kT, s = i % kT;
+    const int e = i & 3, l = (i >> 2) & 63, half = (i >> 8) & 1, ti = i >> 9;
+    const int t = 16 * ti + (l & 15), s = 8 * (l >> 4) + 4 * half + e;
     float acc = 0.f;
     for (int n = 0; n < Np; ++n) acc = fmaf(sC[n][t], sB[n][s], acc);
-    G[i] = acc;
+    Gp[i] = s <= t ? acc : 0.f;
   }
+  // C [i][ks][lane][8] bf16: C[t = 16 i + q][n], with K slot e of lane group g holding
+  // n = 32 ks + 4 g + (e % 4) + 16 (e / 4) (the order of the state accumulators' rows)
+  uint16_t* Cp = reinterpret_cast<uint16_t*>(rec + kT * kT * 4);
+  const int nks = Np / 32;
   for (int i = threadIdx.x; i < kT * Np; i += 256) {
-    const int t = i / Np, n = i % Np;
-    Ct[i] = (uint16_t)(__float_as_uint(sC[n][t]) >> 16);  // exact: the value is a bf16
+    const int e = i & 7, l = (i >> 3) & 63, r = i >> 9;
+    const int ks = r % nks, ti = r / nks;
+    const int t = 16 * ti + (l & 15), n = 32 * ks + 4 * (l >> 4) + (e & 3) + 16 * (e >> 2);
+    Cp[i] = (uint16_t)(__float_as_uint(sC[n][t]) >> 16);  // exact: the value is a bf16
   }
-  for (int i = threadIdx.x; i < Np * kT; i += 256) {
-    const int n = i / kT, t = i % kT;
-    Bn[i] = (uint16_t)(__float_as_uint(sB[n][t]) >> 16);
+  // B [k][lane][8] bf16: B^T[n = 16 k + q][s = 8 g + e]
+  uint16_t* Bp = Cp + kT * Np;
+  for (int i = threadIdx.x; i < kT * Np; i += 256) {
+    const int e = i & 7, l = (i >> 3) & 63, k = i >> 9;
+    const int n = 16 * k + (l & 15), s = 8 * (l >> 4) + e;
+    Bp[i] = (uint16_t)(__float_as_uint(sB[n][s]) >> 16);
   }
 }
 
@@ -114,8 +127,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   constexpr int Np = NP;    // states padded to a multiple of 32
   constexpr int kRecMax = kT * kT * 4 + 2 * kT * NP * 2;
   __shared__ __attribute__((aligned(16))) uint8_t srec[kRecMax];
-  __shared__ __attribute__((aligned(16))) uint16_t su[kSlab][kT];   // u of the slab's channels
-  __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab : 1][kT];
+  // u (and z) of the slab's channels, in lane order: channel 16 w + q, steps 8 g .. 8 g + 7 at
+  // [w][g][q][8], the B operand of wave w's lane 16 g + q
+  __shared__ __attribute__((aligned(16))) uint16_t su[kSlab * kT];
+  __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab * kT : 8];
   // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, 2^(S_{T-1} - S)
   __shared__ __attribute__((aligned(16))) float sw[kWaves][4][kT];
 
@@ -146,7 +161,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   // next iteration.
   constexpr int kRecPieces = kRecMax / 16 / 256;   // 16-byte record pieces per thread (exact)
   static_assert(kRecMax % (16 * 256) == 0, "record pieces");
-  const int pr = threadIdx.x >> 2, seg = (threadIdx.x & 3) * 8;  // u / z tile piece of this thread
+  // u / z piece of this thread: channel 16 (tid / 64) + tid % 16, steps 8 ((tid / 16) % 4) + 0..7
+  const int pr = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15), seg = 8 * ((threadIdx.x >> 4) & 3);
   const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
   const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd : nullptr;
   u32x4 pf_rec[kRecPieces], pf_u, pf_z;
@@ -173,13 +189,13 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     u32x4* dst = reinterpret_cast<u32x4*>(srec);
 #pragma unroll
     for (int m = 0; m < kRecPieces; ++m) dst[threadIdx.x + 256 * m] = pf_rec[m];
-    *reinterpret_cast<u32x4*>(&su[pr][seg]) = pf_u;
-    if constexpr (GATE) *reinterpret_cast<u32x4*>(&sz[pr][seg]) = pf_z;
+    reinterpret_cast<u32x4*>(su)[threadIdx.x] = pf_u;
+    if constexpr (GATE) reinterpret_cast<u32x4*>(sz)[threadIdx.x] = pf_z;
   };
 
-  const float* G = reinterpret_cast<const float*>(srec);
-  const uint16_t* Ct = reinterpret_cast<const uint16_t*>(srec + kT * kT * 4);
-  const uint16_t* Bn = Ct + kT * Np;
+  const f32x4v* Gp = reinterpret_cast<const f32x4v*>(srec);             // [i][half][lane]
+  const u32x4* Cp = reinterpret_cast<const u32x4*>(srec + kT * kT * 4);  // [i][ks][lane]
+  const u32x4* Bp = Cp + kT * Np / 8;                                      // [k][lane]
   float* wdt = sw[wave][0];
   float* wS = sw[wave][1];
   float* weS = sw[wave][2];
@@ -230,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     // X[s][pch] and Xd[s][pch] for s = 8 g16 + k: the B operand of both contractions over s
     bf16x8 xhi, xlo, xdhi, xdlo;
     {
-      const u32x4 uw = *reinterpret_cast<const u32x4*>(&su[pch][8 * g16]);
+      const u32x4 uw = reinterpret_cast<const u32x4*>(su)[64 * wave + lane];
       const uint32_t uwv[4] = {uw.x, uw.y, uw.z, uw.w};
       float x[8], xd[8];
 #pragma unroll
@@ -255,12 +271,15 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     for (int i = 0; i < 2; ++i) {
       const int t = 16 * i + q;
       const float St = wS[t];
+      const f32x4v g0 = Gp[(2 * i) * 64 + lane], g1 = Gp[(2 * i + 1) * 64 + lane];
       float m[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int s = 8 * g16 + k;
-        const float v = G[t * kT + s] * __builtin_amdgcn_exp2f(fminf(St - wS[s], 0.f));
-        m[k] = s <= t ? v : 0.f;
+        // (the record holds 0 above the diagonal; the exponent is masked there too, where it
+        // may be large and positive)
+        const float gv = k < 4 ? g0[k] : g1[k - 4];
+        m[k] = gv * __builtin_amdgcn_exp2f(s <= t ? St - wS[s] : -INFINITY);
       }
       bf16x8 mhi, mlo;
       split8(m, mhi, mlo);
@@ -282,10 +301,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         split8(hv, hhi, hlo);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          const uint16_t* cr = Ct + (16 * i + q) * Np + 32 * ks + 4 * g16;
-          const uint2 c0w = *reinterpret_cast<const uint2*>(cr);
-          const uint2 c1w = *reinterpret_cast<const uint2*>(cr + 16);
-          const bf16x8 ca = as_bf16x8(u32x4{c0w.x, c0w.y, c1w.x, c1w.y});
+          const bf16x8 ca = as_bf16x8(Cp[(i * (Np / 32) + ks) * 64 + lane]);
           iacc[i] = mfma(ca, hhi, iacc[i]);
           iacc[i] = mfma(ca, hlo, iacc[i]);
         }
@@ -297,13 +313,19 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int tl = 16 * i + 4 * g16;
+        // u (and z) at steps tl .. tl + 3 of channel pch: four bf16 of one lane-order piece
+        const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
+        const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
+        uint2 zq = uint2{0u, 0u};
+        if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
+        const uint32_t uw[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = tl + r;
-          const uint16_t ub = su[pch][t];
-          float yy = yacc[i][r] + weS[t] * iacc[i][r] + Dd * __uint_as_float((uint32_t)ub << 16);
-          if constexpr (GATE) yy *= silu_fast(__uint_as_float((uint32_t)sz[pch][t] << 16));
+          const float uu = (r & 1) ? bf16_hi(uw[r / 2]) : bf16_lo(uw[r / 2]);
+          float yy = yacc[i][r] + weS[t] * iacc[i][r] + Dd * uu;
+          if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
           v[r] = yy;
         }
         const int64_t tg = t0 + tl;
@@ -331,8 +353,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     for (int k = 0; k < 8; ++k) {
       if (k < nk) {
         hacc[k] = hacc[k] * eT;
-        const u32x4 bw = *reinterpret_cast<const u32x4*>(Bn + (16 * k + q) * kT + 8 * g16);
-        const bf16x8 ba = as_bf16x8(bw);
+        const bf16x8 ba = as_bf16x8(Bp[k * 64 + lane]);
         hacc[k] = mfma(ba, xdhi, hacc[k]);
         hacc[k] = mfma(ba, xdlo, hacc[k]);
       }

@@ -5,6 +5,8 @@ y written in f32.  Bars: 1e-5 for f32 inputs, 2e-3 for bf16 inputs (both sides c
 same bf16 bits, so the error is f32-vs-f64 arithmetic only).  y written in bf16 is checked
 against |y - y_ref| <= 2^-8 |y_ref| + 2e-3 max|y_ref| (one rounding to bf16 on top).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -108,6 +110,15 @@ def test_scalar_matrix_options(opts):
     torch_dev()
     check(inputs.random_problem(600, 1, 256, 700, 32, heads=4, scalar_decay=True, **opts),
           "scalar 4x64 %s" % opts)
+
+
+def test_scalar_matrix_growing_state():
+    """A > 0: the state grows, so the in-chunk factors 2^(S_t - S_s) exceed 1 (and the masked
+    entries above the diagonal have large positive exponents); the matrix form must not clip."""
+    torch_dev()
+    p = inputs.random_problem(650, 1, 128, 600, 64, heads=2, scalar_decay=True)
+    p = dataclasses.replace(p, A=(-0.05 * p.A).astype(np.float32))
+    check(p, "scalar matrix A>0")
 
 
 def test_softplus_elementwise():
