@@ -246,12 +246,12 @@ def main():
 
     if kernel == "ssd_scan_kernel":
         # the matrix form runs on v_mfma_f32_16x16x32_bf16 (16*16*32*2 flops each): per
-        # (batch, head, 64-channel slab, 32-step chunk) each of 4 waves issues 6 for the masked
+        # (batch, head, 64-channel slab, 32-step chunk) each of 4 waves issues 4 for the masked
         # product, Np/8 for the readout from the carried state and Np/8 for the state update
         # (Np = N padded to a multiple of 32), counting the bf16 hi/lo split passes
         Np = (p.nstate + 31) // 32 * 32
         nch = (p.length + 31) // 32
-        mf = p.batch * p.heads * (p.channels // p.heads // 64) * nch * 4 * (6 + Np // 4) * 16384.0
+        mf = p.batch * p.heads * (p.channels // p.heads // 64) * nch * 4 * (4 + Np // 4) * 16384.0
         mf_tflops = mf / avg_launch_s / 1e12
         out["roofline"].update({"mfma_executed_flops_per_launch": mf, "mfma_achieved_TFLOPs": mf_tflops,
                                 "mfma_frac_bf16_peak": mf_tflops / BF16_MFMA_PEAK_TFLOPS})

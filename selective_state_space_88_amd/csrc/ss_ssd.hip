@@ -50,12 +50,25 @@ __host__ __device__ inline int64_t rec_bytes(int Np) { return (int64_t)kT * kT *
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-// x = hi + lo, both bf16 (round to nearest even: v_cvt_pk_bf16_f32), for eight values
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// two f32 -> two bf16 (round to nearest even), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2));
+}
+
+// x = hi + lo, both bf16 (round to nearest even), for eight values; the conversions go in
+// pairs (converting the elements one by one takes one instruction each)
 __device__ __forceinline__ void split8(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  uint32_t h[4], l[4];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) hi[k] = (__bf16)x[k];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) lo[k] = (__bf16)(x[k] - (float)hi[k]);
+  for (int j = 0; j < 4; ++j) {
+    h[j] = pk_bf16(x[2 * j], x[2 * j + 1]);
+    l[j] = pk_bf16(x[2 * j] - __uint_as_float(h[j] << 16), x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+  }
+  hi = as_bf16x8(u32x4{h[0], h[1], h[2], h[3]});
+  lo = as_bf16x8(u32x4{l[0], l[1], l[2], l[3]});
 }
 
 // DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source, and lanes of
@@ -120,7 +133,9 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __re
   }
 }
 
-template <typename TOut, bool GATE, int NP>
+// FULL: every chunk holds kT steps and every row is 16-byte aligned, so that the loop has no
+// bounds checks (and the compiler can count the memory operations in flight exactly).
+template <typename TOut, bool GATE, int NP, bool FULL>
 __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const uint8_t* __restrict__ ws,
                                                                int64_t nchunks) {
   using TIn = bf16_t;
@@ -131,7 +146,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   // [w][g][q][8], the B operand of wave w's lane 16 g + q
   __shared__ __attribute__((aligned(16))) uint16_t su[kSlab * kT];
   __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab * kT : 8];
-  // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, 2^(S_{T-1} - S)
+  // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, dt 2^(S_{T-1} - S)
   __shared__ __attribute__((aligned(16))) float sw[kWaves][4][kT];
 
   const int lane = threadIdx.x & 63;
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   u32x4 pf_rec[kRecPieces], pf_u, pf_z;
   uint32_t pf_d = 0u;   // raw bits of delta at step (lane % 32) of the prefetched chunk
   auto load_piece = [&](const TIn* row, int64_t t) -> u32x4 {
-    if (p.vec && t + 8 <= L) return *reinterpret_cast<const u32x4*>(row + t);
+    if (FULL || (p.vec && t + 8 <= L)) return *reinterpret_cast<const u32x4*>(row + t);
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     if constexpr (GATE) pf_z = load_piece(zr, c * kT + seg);
     // (kept raw: widening it here would make the compiler wait for every load just issued)
     const int64_t t = c * kT + (lane & (kT - 1));
-    pf_d = reinterpret_cast<const uint16_t*>(drow)[t < L ? t : 0];
+    pf_d = reinterpret_cast<const uint16_t*>(drow)[(FULL || t < L) ? t : 0];
   };
   auto commit = [&]() {
     u32x4* dst = reinterpret_cast<u32x4*>(srec);
@@ -199,17 +214,46 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   float* wdt = sw[wave][0];
   float* wS = sw[wave][1];
   float* weS = sw[wave][2];
-  float* weD = sw[wave][3];
+  float* wXd = sw[wave][3];
   const int pch = 16 * wave + q;   // this lane's channel in the slab (B operand / D column)
   // (read once here: inside the loop the compiler reloads it after every y store, and the
   // reload's wait would also wait for the next chunk's prefetch)
   const float Dd = p.D ? p.D[p.d_per_head ? h : c0 + pch] : 0.f;
+  TOut* const yr = static_cast<TOut*>(p.y) + b * p.y_sb + (c0 + pch) * p.y_sd;
+
+  // y of one chunk, t = 16 i + 4 g16 + r; in the FULL variant it is stored at the top of the
+  // next iteration, just before the next prefetch, so that no wait for the prefetched data
+  // has a store of the same iteration queued in front of it
+  float ypend[2][4];
+  auto store_y = [&](int64_t tc) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t tg = tc + 16 * i + 4 * g16;
+      const float* v = ypend[i];
+      if (FULL || (p.vec && tg + 4 <= L)) {
+        if constexpr (sizeof(TOut) == 4) {
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(yr + tg));
+        } else {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(u32x2{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])},
+                                      reinterpret_cast<u32x2*>(yr + tg));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tg + r < L) store_one(yr + tg + r, v[r]);
+      }
+    }
+  };
 
   prefetch(0);
   for (int64_t c = 0; c < nchunks; ++c) {
     const int64_t t0 = c * kT;
     __syncthreads();  // the previous chunk's reads of the staging buffers are done
     commit();
+    if constexpr (FULL) {
+      if (c > 0) store_y(t0 - kT);
+    }
     const float draw = __uint_as_float(pf_d << 16);
     prefetch(c + 1 < nchunks ? c + 1 : c);  // (the last chunk loads itself again, unused)
     // keep the prefetch here, at the top: the scheduler would otherwise sink the loads to the
@@ -219,7 +263,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     {
       const int t = lane & (kT - 1);
       float dt = 0.f;
-      if (lane < kT && t0 + t < L) {
+      if (lane < kT && (FULL || t0 + t < L)) {
         const float x = draw + bias;
         dt = p.softplus ? softplus_fast(x) : x;
       }
@@ -237,25 +281,23 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         wdt[t] = dt;
         wS[t] = s;
         weS[t] = __builtin_amdgcn_exp2f(s);
-        weD[t] = __builtin_amdgcn_exp2f(sEnd - s);
+        wXd[t] = dt * __builtin_amdgcn_exp2f(sEnd - s);
       }
     }
     __syncthreads();  // staging visible to every wave
     const float eT = weS[kT - 1];
 
-    // X[s][pch] and Xd[s][pch] for s = 8 g16 + k: the B operand of both contractions over s
-    bf16x8 xhi, xlo, xdhi, xdlo;
+    // u[s = 8 g16 + k][pch]: the exact (bf16) B operand of the masked product; and
+    // Xd[s][pch] = dt_s 2^(S_{T-1} - S_s) u_s, the B operand of the state update, split
+    const u32x4 uw = reinterpret_cast<const u32x4*>(su)[64 * wave + lane];
+    const bf16x8 ub = as_bf16x8(uw);
+    bf16x8 xdhi, xdlo;
     {
-      const u32x4 uw = reinterpret_cast<const u32x4*>(su)[64 * wave + lane];
       const uint32_t uwv[4] = {uw.x, uw.y, uw.z, uw.w};
-      float x[8], xd[8];
+      float xd[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float uu = (k & 1) ? bf16_hi(uwv[k / 2]) : bf16_lo(uwv[k / 2]);
-        x[k] = wdt[8 * g16 + k] * uu;
-        xd[k] = x[k] * weD[8 * g16 + k];
-      }
-      split8(x, xhi, xlo);
+      for (int k = 0; k < 8; ++k)
+        xd[k] = wXd[8 * g16 + k] * ((k & 1) ? bf16_hi(uwv[k / 2]) : bf16_lo(uwv[k / 2]));
       split8(xd, xdhi, xdlo);
     }
 
@@ -266,7 +308,12 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
       iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
     }
-    // within the chunk: A operand (G o L)[t = 16 i + q][s = 8 g16 + k]
+    // within the chunk: A operand (G o L)[t][s] dt_s for t = 16 i + q, s = 8 g16 + k
+    // (dt and S at this lane's eight s read as vectors, unconditionally)
+    const f32x4v* wdt4 = reinterpret_cast<const f32x4v*>(wdt);
+    const f32x4v* wS4 = reinterpret_cast<const f32x4v*>(wS);
+    const f32x4v dts0 = wdt4[2 * g16], dts1 = wdt4[2 * g16 + 1];
+    const f32x4v Ss0 = wS4[2 * g16], Ss1 = wS4[2 * g16 + 1];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int t = 16 * i + q;
@@ -279,13 +326,14 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         // (the record holds 0 above the diagonal; the exponent is masked there too, where it
         // may be large and positive)
         const float gv = k < 4 ? g0[k] : g1[k - 4];
-        m[k] = gv * __builtin_amdgcn_exp2f(s <= t ? St - wS[s] : -INFINITY);
+        const float dts = k < 4 ? dts0[k] : dts1[k - 4];
+        const float ex = St - (k < 4 ? Ss0[k] : Ss1[k - 4]);
+        m[k] = gv * dts * __builtin_amdgcn_exp2f(s <= t ? ex : -INFINITY);
       }
       bf16x8 mhi, mlo;
       split8(m, mhi, mlo);
-      yacc[i] = mfma(mhi, xhi, yacc[i]);
-      yacc[i] = mfma(mhi, xlo, yacc[i]);
-      yacc[i] = mfma(mlo, xhi, yacc[i]);
+      yacc[i] = mfma(mhi, ub, yacc[i]);
+      yacc[i] = mfma(mlo, ub, yacc[i]);
     }
     // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
 #pragma unroll
@@ -308,46 +356,25 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       }
     }
     // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
-    {
-      TOut* yr = static_cast<TOut*>(p.y) + b * p.y_sb + (c0 + pch) * p.y_sd;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int tl = 16 * i + 4 * g16;
-        // u (and z) at steps tl .. tl + 3 of channel pch: four bf16 of one lane-order piece
-        const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
-        const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
-        uint2 zq = uint2{0u, 0u};
-        if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
-        const uint32_t uw[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
-        float v[4];
+    for (int i = 0; i < 2; ++i) {
+      const int tl = 16 * i + 4 * g16;
+      // u (and z) at steps tl .. tl + 3 of channel pch: four bf16 of one lane-order piece
+      const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
+      const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
+      uint2 zq = uint2{0u, 0u};
+      if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
+      const uint32_t uwq[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
+      const f32x4v eS = reinterpret_cast<const f32x4v*>(weS)[4 * i + g16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = tl + r;
-          const float uu = (r & 1) ? bf16_hi(uw[r / 2]) : bf16_lo(uw[r / 2]);
-          float yy = yacc[i][r] + weS[t] * iacc[i][r] + Dd * uu;
-          if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
-          v[r] = yy;
-        }
-        const int64_t tg = t0 + tl;
-        if (tg + 4 <= L) {
-          if constexpr (sizeof(TOut) == 4) {
-            if (p.vec) {
-              __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(yr + tg));
-            } else {
-#pragma unroll
-              for (int r = 0; r < 4; ++r) store_one(yr + tg + r, v[r]);
-            }
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) store_one(yr + tg + r, v[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (tg + r < L) store_one(yr + tg + r, v[r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float uu = (r & 1) ? bf16_hi(uwq[r / 2]) : bf16_lo(uwq[r / 2]);
+        float yy = yacc[i][r] + eS[r] * iacc[i][r] + Dd * uu;
+        if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
+        ypend[i][r] = yy;
       }
     }
+    if constexpr (!FULL) store_y(t0);
     // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -359,6 +386,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       }
     }
   }
+  if constexpr (FULL) store_y((nchunks - 1) * kT);
 }
 
 }  // namespace
@@ -379,20 +407,24 @@ hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t s) {
   const int64_t blocks = a.batch * a.heads * (a.chan_per_head / kSlab);
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
   const uint8_t* w = static_cast<const uint8_t*>(ws);
+  // whole chunks and 16-byte aligned rows: the variant without bounds checks
+  const bool full = a.vec && a.L % kT == 0;
+#define SS_LAUNCH(TO, GT, NPV)                                                                              \
+  if (full) hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, true>), grid, block, 0, s, a, w, nch);         \
+  else hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, false>), grid, block, 0, s, a, w, nch);
 #define SS_NP(NPV)                                                                                         \
   case NPV:                                                                                                \
     if (a.out_bf16) {                                                                                      \
-      if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, true, NPV>), grid, block, 0, s, a, w, nch);     \
-      else hipLaunchKernelGGL((ssd_scan_kernel<bf16_t, false, NPV>), grid, block, 0, s, a, w, nch);        \
+      if (a.z) { SS_LAUNCH(bf16_t, true, NPV) } else { SS_LAUNCH(bf16_t, false, NPV) }                     \
     } else {                                                                                               \
-      if (a.z) hipLaunchKernelGGL((ssd_scan_kernel<float, true, NPV>), grid, block, 0, s, a, w, nch);      \
-      else hipLaunchKernelGGL((ssd_scan_kernel<float, false, NPV>), grid, block, 0, s, a, w, nch);         \
+      if (a.z) { SS_LAUNCH(float, true, NPV) } else { SS_LAUNCH(float, false, NPV) }                       \
     }                                                                                                      \
     break;
   switch (Np) {
     SS_NP(32) SS_NP(64) SS_NP(96) SS_NP(128)
     default: return hipErrorInvalidValue;
   }
+#undef SS_LAUNCH
 #undef SS_NP
   return hipGetLastError();
 }
