@@ -148,6 +148,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab * kT : 8];
   // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, dt 2^(S_{T-1} - S)
   __shared__ __attribute__((aligned(16))) float sw[kWaves][4][kT];
+  // the masked matrix of the chunk (the same for every channel of the head), split into bf16
+  // hi and lo parts, as the A operand of t-tile i: [i][lane][8]; wave w computes the quarter
+  // i = w / 2, K slots 4 (w % 2) .. 4 (w % 2) + 3
+  __shared__ __attribute__((aligned(16))) u32x4 smh[2 * 64], sml[2 * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,7 +222,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   const int pch = 16 * wave + q;   // this lane's channel in the slab (B operand / D column)
   // (read once here: inside the loop the compiler reloads it after every y store, and the
   // reload's wait would also wait for the next chunk's prefetch)
-  const float Dd = p.D ? p.D[p.d_per_head ? h : c0 + pch] : 0.f;
+  // with one D per head, D u_t is folded into the diagonal of the masked matrix (u is its
+  // exact B operand); with one D per channel it is added to y
+  const bool dfold = p.D && p.d_per_head;
+  const float Dfold = dfold ? p.D[h] : 0.f;
+  const float Dd = (p.D && !dfold) ? p.D[c0 + pch] : 0.f;
   TOut* const yr = static_cast<TOut*>(p.y) + b * p.y_sb + (c0 + pch) * p.y_sd;
 
   // y of one chunk, t = 16 i + 4 g16 + r; in the FULL variant it is stored at the top of the
@@ -284,7 +292,31 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         wXd[t] = dt * __builtin_amdgcn_exp2f(sEnd - s);
       }
     }
-    __syncthreads();  // staging visible to every wave
+    // this wave's quarter of the masked matrix (G o L)[t][s] dt_s (+ D on the diagonal), for
+    // t = 16 iq + q, s = 8 g16 + 4 hq + e; its G piece is the one this thread committed
+    {
+      const int iq = wave >> 1, hq = wave & 1;
+      const int t = 16 * iq + q;
+      const float St = wS[t];
+      const f32x4v Ssq = reinterpret_cast<const f32x4v*>(wS)[2 * g16 + hq];
+      const f32x4v dtq = reinterpret_cast<const f32x4v*>(wdt)[2 * g16 + hq];
+      const f32x4v gq = Gp[wave * 64 + lane];
+      float m[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = 8 * g16 + 4 * hq + e;
+        // (the record holds 0 above the diagonal; the exponent is masked there too, where it
+        // may be large and positive)
+        m[e] = gq[e] * dtq[e] * __builtin_amdgcn_exp2f(s <= t ? St - Ssq[e] : -INFINITY) + (s == t ? Dfold : 0.f);
+      }
+      const uint32_t h0 = pk_bf16(m[0], m[1]), h1 = pk_bf16(m[2], m[3]);
+      const uint32_t l0 = pk_bf16(m[0] - __uint_as_float(h0 << 16), m[1] - __uint_as_float(h0 & 0xffff0000u));
+      const uint32_t l1 = pk_bf16(m[2] - __uint_as_float(h1 << 16), m[3] - __uint_as_float(h1 & 0xffff0000u));
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      reinterpret_cast<u32x2*>(smh)[2 * (iq * 64 + lane) + hq] = u32x2{h0, h1};
+      reinterpret_cast<u32x2*>(sml)[2 * (iq * 64 + lane) + hq] = u32x2{l0, l1};
+    }
+    __syncthreads();  // staging and the masked matrix visible to every wave
     const float eT = weS[kT - 1];
 
     // u[s = 8 g16 + k][pch]: the exact (bf16) B operand of the masked product; and
@@ -308,32 +340,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
       iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
     }
-    // within the chunk: A operand (G o L)[t][s] dt_s for t = 16 i + q, s = 8 g16 + k
-    // (dt and S at this lane's eight s read as vectors, unconditionally)
-    const f32x4v* wdt4 = reinterpret_cast<const f32x4v*>(wdt);
-    const f32x4v* wS4 = reinterpret_cast<const f32x4v*>(wS);
-    const f32x4v dts0 = wdt4[2 * g16], dts1 = wdt4[2 * g16 + 1];
-    const f32x4v Ss0 = wS4[2 * g16], Ss1 = wS4[2 * g16 + 1];
+    // within the chunk: the shared masked matrix (hi + lo) times u
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int t = 16 * i + q;
-      const float St = wS[t];
-      const f32x4v g0 = Gp[(2 * i) * 64 + lane], g1 = Gp[(2 * i + 1) * 64 + lane];
-      float m[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = 8 * g16 + k;
-        // (the record holds 0 above the diagonal; the exponent is masked there too, where it
-        // may be large and positive)
-        const float gv = k < 4 ? g0[k] : g1[k - 4];
-        const float dts = k < 4 ? dts0[k] : dts1[k - 4];
-        const float ex = St - (k < 4 ? Ss0[k] : Ss1[k - 4]);
-        m[k] = gv * dts * __builtin_amdgcn_exp2f(s <= t ? ex : -INFINITY);
-      }
-      bf16x8 mhi, mlo;
-      split8(m, mhi, mlo);
-      yacc[i] = mfma(mhi, ub, yacc[i]);
-      yacc[i] = mfma(mlo, ub, yacc[i]);
+      yacc[i] = mfma(as_bf16x8(smh[i * 64 + lane]), ub, yacc[i]);
+      yacc[i] = mfma(as_bf16x8(sml[i * 64 + lane]), ub, yacc[i]);
     }
     // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
 #pragma unroll
@@ -358,8 +369,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int tl = 16 * i + 4 * g16;
-      // u (and z) at steps tl .. tl + 3 of channel pch: four bf16 of one lane-order piece
+      // u (and z) at steps 16 i + 4 g16 + 0..3 of channel pch: four bf16 of one lane-order piece
       const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
       const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
       uint2 zq = uint2{0u, 0u};
@@ -369,7 +379,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float uu = (r & 1) ? bf16_hi(uwq[r / 2]) : bf16_lo(uwq[r / 2]);
-        float yy = yacc[i][r] + eS[r] * iacc[i][r] + Dd * uu;
+        float yy = yacc[i][r] + eS[r] * iacc[i][r];
+        if (!dfold) yy += Dd * uu;
         if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
         ypend[i][r] = yy;
       }
