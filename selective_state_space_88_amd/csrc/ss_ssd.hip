@@ -29,6 +29,7 @@
 // contraction index n is permuted so that lane group g's eight K slots are the n it holds
 // (4g..4g+3 of two consecutive 16-row tiles), and C is read in the same order.
 #include <algorithm>
+#include <atomic>
 
 #include "ss_device.h"
 #include "ss_launch.h"
@@ -133,11 +134,24 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __re
   }
 }
 
+// Sequence segments: each (batch, head, slab) row is cut into nseg segments of cps chunks,
+// one block each.  A state pass (STATE) runs the recurrence over every segment but the last
+// from a zero state, with no output, and stores the segment's final state and its total
+// log2 decay; the output pass starts segment k from the state the earlier segments hand
+// over, H_in(k) = sum_{j<k} (product of the decays of segments j+1 .. k-1) H_end(j).
+struct Segs {
+  int64_t cps;          // chunks per segment
+  int32_t nseg;         // segments per row
+  float* hloc;          // per state-pass block: its wave-ordered final state (Np * 64 floats)
+  float* dsum;          // per state-pass block: the log2 decay over its segment
+};
+
 // FULL: every chunk holds kT steps and every row is 16-byte aligned, so that the loop has no
 // bounds checks (and the compiler can count the memory operations in flight exactly).
-template <typename TOut, bool GATE, int NP, bool FULL>
+// STATE: the state pass (no y; only the B part of the record is staged).
+template <typename TOut, bool GATE, int NP, bool FULL, bool STATE>
 __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const uint8_t* __restrict__ ws,
-                                                               int64_t nchunks) {
+                                                               int64_t nchunks, Segs sg) {
   using TIn = bf16_t;
   constexpr int Np = NP;    // states padded to a multiple of 32
   constexpr int kRecMax = kT * kT * 4 + 2 * kT * NP * 2;
@@ -158,9 +172,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   const int g16 = lane >> 4, q = lane & 15;
   const int64_t L = p.L;
   const int64_t slabs = p.chan_per_head / kSlab;
+  // block = ((segment * batch + b) * heads + h) * slabs + slab: neighbouring blocks share the
+  // segment's chunk records
   const int64_t blk = blockIdx.x;
-  const int64_t slab = blk % slabs, bh = blk / slabs;
-  const int64_t b = bh / p.heads, h = bh % p.heads;
+  const int64_t slab = blk % slabs;
+  const int64_t h = (blk / slabs) % p.heads;
+  const int64_t b = (blk / (slabs * p.heads)) % p.batch;
+  const int64_t sgi = blk / (slabs * p.heads * p.batch);
+  const int64_t row = (b * p.heads + h) * slabs + slab;   // (b, h, slab) index
+  const int64_t rows = p.batch * p.heads * slabs;
+  const int64_t cb = sgi * sg.cps, ce = (cb + sg.cps < nchunks) ? cb + sg.cps : nchunks;
   const int64_t c0 = h * p.chan_per_head + slab * kSlab;   // first channel of the slab
   const int64_t grp = c0 / p.chan_per_group;
   const float A2 = p.A[h] * kLog2e;
@@ -178,8 +199,10 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   // Staging: chunk c + 1's record (rb bytes) and u (and z) tile are loaded into registers, 16
   // bytes per thread a piece, while chunk c is computed, and written to LDS at the top of the
   // next iteration.
-  constexpr int kRecPieces = kRecMax / 16 / 256;   // 16-byte record pieces per thread (exact)
-  static_assert(kRecMax % (16 * 256) == 0, "record pieces");
+  // (the state pass stages only the B part, which starts at kROff)
+  constexpr int kROff = STATE ? kT * kT * 4 + kT * NP * 2 : 0;
+  constexpr int kRecPieces = (kRecMax - kROff) / 16 / 256;   // 16-byte record pieces per thread
+  static_assert((kRecMax - kROff) % (16 * 256) == 0, "record pieces");
   // u / z piece of this thread: channel 16 (tid / 64) + tid % 16, steps 8 ((tid / 16) % 4) + 0..7
   const int pr = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15), seg = 8 * ((threadIdx.x >> 4) & 3);
   const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
@@ -195,7 +218,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     return u32x4{w[0], w[1], w[2], w[3]};
   };
   auto prefetch = [&](int64_t c) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb);
+    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb + kROff);
 #pragma unroll
     for (int m = 0; m < kRecPieces; ++m) pf_rec[m] = src[threadIdx.x + 256 * m];
     pf_u = load_piece(ur, c * kT + seg);
@@ -205,7 +228,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     pf_d = reinterpret_cast<const uint16_t*>(drow)[(FULL || t < L) ? t : 0];
   };
   auto commit = [&]() {
-    u32x4* dst = reinterpret_cast<u32x4*>(srec);
+    u32x4* dst = reinterpret_cast<u32x4*>(srec + kROff);
 #pragma unroll
     for (int m = 0; m < kRecPieces; ++m) dst[threadIdx.x + 256 * m] = pf_rec[m];
     reinterpret_cast<u32x4*>(su)[threadIdx.x] = pf_u;
@@ -254,16 +277,32 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     }
   };
 
-  prefetch(0);
-  for (int64_t c = 0; c < nchunks; ++c) {
+  if constexpr (!STATE) {
+    // the state entering this segment, from the state pass's results (j = sgi - 1 first, whose
+    // end state enters undecayed)
+    float lg = 0.f;
+    for (int64_t j = sgi - 1; j >= 0; --j) {
+      const int64_t sb = j * rows + row;   // state-pass block of segment j of this row
+      const float f = __builtin_amdgcn_exp2f(lg);
+      const f32x4v* hl = reinterpret_cast<const f32x4v*>(sg.hloc) + (sb * kWaves + wave) * nk * 64 + lane;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (k < nk) hacc[k] += f * hl[k * 64];
+      lg += sg.dsum[sb];
+    }
+  }
+  float dlog = 0.f;   // log2 decay over the chunks done so far (state pass)
+
+  prefetch(cb);
+  for (int64_t c = cb; c < ce; ++c) {
     const int64_t t0 = c * kT;
     __syncthreads();  // the previous chunk's reads of the staging buffers are done
     commit();
-    if constexpr (FULL) {
-      if (c > 0) store_y(t0 - kT);
+    if constexpr (FULL && !STATE) {
+      if (c > cb) store_y(t0 - kT);
     }
     const float draw = __uint_as_float(pf_d << 16);
-    prefetch(c + 1 < nchunks ? c + 1 : c);  // (the last chunk loads itself again, unused)
+    prefetch(c + 1 < ce ? c + 1 : c);  // (the last chunk loads itself again, unused)
     // keep the prefetch here, at the top: the scheduler would otherwise sink the loads to the
     // end of the iteration, where the next commit waits for them at once
     __builtin_amdgcn_sched_barrier(0);
@@ -285,6 +324,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       s += dpp_zero<0x118, 0xf>(s);
       s += dpp_zero<0x142, 0xa>(s);
       const float sEnd = readlane_f(s, kT - 1);
+      dlog += sEnd;
       if (lane < kT) {
         wdt[t] = dt;
         wS[t] = s;
@@ -294,7 +334,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     }
     // this wave's quarter of the masked matrix (G o L)[t][s] dt_s (+ D on the diagonal), for
     // t = 16 iq + q, s = 8 g16 + 4 hq + e; its G piece is the one this thread committed
-    {
+    if constexpr (!STATE) {
       const int iq = wave >> 1, hq = wave & 1;
       const int t = 16 * iq + q;
       const float St = wS[t];
@@ -333,59 +373,61 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       split8(xd, xdhi, xdlo);
     }
 
-    // y tiles: t-tile i (rows 16 i + 4 g16 + r), this wave's 16 channels
-    f32x4v yacc[2], iacc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-      iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    }
-    // within the chunk: the shared masked matrix (hi + lo) times u
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      yacc[i] = mfma(as_bf16x8(smh[i * 64 + lane]), ub, yacc[i]);
-      yacc[i] = mfma(as_bf16x8(sml[i * 64 + lane]), ub, yacc[i]);
-    }
-    // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (2 * ks < nk) {
-        float hv[8];
-#pragma unroll
+    if constexpr (!STATE) {
+      // y tiles: t-tile i (rows 16 i + 4 g16 + r), this wave's 16 channels
+      f32x4v yacc[2], iacc[2];
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+        iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
+      }
+      // within the chunk: the shared masked matrix (hi + lo) times u
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        yacc[i] = mfma(as_bf16x8(smh[i * 64 + lane]), ub, yacc[i]);
+        yacc[i] = mfma(as_bf16x8(sml[i * 64 + lane]), ub, yacc[i]);
+      }
+      // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
+  #pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (2 * ks < nk) {
+          float hv[8];
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hv[r] = hacc[2 * ks][r];
+            hv[4 + r] = hacc[2 * ks + 1][r];
+          }
+          bf16x8 hhi, hlo;
+          split8(hv, hhi, hlo);
+  #pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bf16x8 ca = as_bf16x8(Cp[(i * (Np / 32) + ks) * 64 + lane]);
+            iacc[i] = mfma(ca, hhi, iacc[i]);
+            iacc[i] = mfma(ca, hlo, iacc[i]);
+          }
+        }
+      }
+      // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
+  #pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // u (and z) at steps 16 i + 4 g16 + 0..3 of channel pch: four bf16 of one lane-order piece
+        const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
+        const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
+        uint2 zq = uint2{0u, 0u};
+        if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
+        const uint32_t uwq[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
+        const f32x4v eS = reinterpret_cast<const f32x4v*>(weS)[4 * i + g16];
+  #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          hv[r] = hacc[2 * ks][r];
-          hv[4 + r] = hacc[2 * ks + 1][r];
-        }
-        bf16x8 hhi, hlo;
-        split8(hv, hhi, hlo);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const bf16x8 ca = as_bf16x8(Cp[(i * (Np / 32) + ks) * 64 + lane]);
-          iacc[i] = mfma(ca, hhi, iacc[i]);
-          iacc[i] = mfma(ca, hlo, iacc[i]);
+          const float uu = (r & 1) ? bf16_hi(uwq[r / 2]) : bf16_lo(uwq[r / 2]);
+          float yy = yacc[i][r] + eS[r] * iacc[i][r];
+          if (!dfold) yy += Dd * uu;
+          if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
+          ypend[i][r] = yy;
         }
       }
+      if constexpr (!FULL) store_y(t0);
     }
-    // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // u (and z) at steps 16 i + 4 g16 + 0..3 of channel pch: four bf16 of one lane-order piece
-      const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
-      const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
-      uint2 zq = uint2{0u, 0u};
-      if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
-      const uint32_t uwq[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
-      const f32x4v eS = reinterpret_cast<const f32x4v*>(weS)[4 * i + g16];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float uu = (r & 1) ? bf16_hi(uwq[r / 2]) : bf16_lo(uwq[r / 2]);
-        float yy = yacc[i][r] + eS[r] * iacc[i][r];
-        if (!dfold) yy += Dd * uu;
-        if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
-        ypend[i][r] = yy;
-      }
-    }
-    if constexpr (!FULL) store_y(t0);
     // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -397,7 +439,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       }
     }
   }
-  if constexpr (FULL) store_y((nchunks - 1) * kT);
+  if constexpr (STATE) {
+    // this segment's end state (wave-ordered, as the output pass reads it) and decay
+    f32x4v* hl = reinterpret_cast<f32x4v*>(sg.hloc) + (blk * kWaves + wave) * nk * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (k < nk) hl[k * 64] = hacc[k];
+    if (threadIdx.x == 0) sg.dsum[blk] = dlog;
+  } else if constexpr (FULL) {
+    store_y((ce - 1) * kT);
+  }
 }
 
 }  // namespace
@@ -406,8 +457,52 @@ bool ssd_path(const ScanArgs& a) {
   return a.in_bf16 && a.chan_per_head % kSlab == 0 && a.chan_per_group % kSlab == 0;
 }
 
+namespace {
+
+constexpr int kBlocksPerCU = 3;     // resident scan blocks per CU (VGPRs: three waves per SIMD)
+constexpr int64_t kMinSegChunks = 16;
+
+// compute units of the current device (cached per device)
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+struct SegPlan {
+  int64_t cps;
+  int32_t nseg;
+  int64_t rows;
+};
+
+// enough segments to give every CU kBlocksPerCU blocks, none shorter than kMinSegChunks
+// chunks (the state pass stages the B part in whole 16-byte pieces per thread: Np of 64, 128)
+SegPlan seg_plan(const ScanArgs& a) {
+  const int64_t nch = nchunks_of(a);
+  const int64_t rows = a.batch * a.heads * (a.chan_per_head / kSlab);
+  int64_t nseg = 1;
+  if (npad32(a.N) % 64 == 0 && rows > 0)
+    nseg = std::min<int64_t>((int64_t)kBlocksPerCU * cu_count() / rows, nch / kMinSegChunks);
+  nseg = std::max<int64_t>(nseg, 1);
+  const int64_t cps = (nch + nseg - 1) / nseg;
+  nseg = (nch + cps - 1) / cps;
+  return {cps, (int32_t)nseg, rows};
+}
+
+int64_t records_bytes(const ScanArgs& a) { return a.batch * a.groups * nchunks_of(a) * rec_bytes(npad32(a.N)); }
+
+}  // namespace
+
 int64_t ssd_workspace_bytes(const ScanArgs& a) {
-  return a.batch * a.groups * nchunks_of(a) * rec_bytes(npad32(a.N));
+  const SegPlan sp = seg_plan(a);
+  const int64_t hand = (int64_t)(sp.nseg - 1) * sp.rows;   // state-pass blocks
+  return records_bytes(a) + hand * (int64_t)npad32(a.N) * 64 * 4 + hand * 4;
 }
 
 hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t s) {
@@ -415,28 +510,38 @@ hipError_t launch_ssd(const ScanArgs& a, void* ws, hipStream_t s) {
   const int64_t nch = nchunks_of(a);
   hipLaunchKernelGGL((ssd_prep_kernel<bf16_t>), dim3((unsigned)(a.batch * a.groups * nch)), dim3(256), 0, s, a,
                      static_cast<uint8_t*>(ws), Np, nch);
-  const int64_t blocks = a.batch * a.heads * (a.chan_per_head / kSlab);
-  const dim3 grid((unsigned)blocks), block(64 * kWaves);
-  const uint8_t* w = static_cast<const uint8_t*>(ws);
+  const SegPlan sp = seg_plan(a);
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  const int64_t hand = (int64_t)(sp.nseg - 1) * sp.rows;
+  Segs sg{sp.cps, sp.nseg, reinterpret_cast<float*>(w + records_bytes(a)), nullptr};
+  sg.dsum = sg.hloc + hand * (int64_t)Np * 64;
+  const dim3 block(64 * kWaves), sgrid((unsigned)hand), grid((unsigned)(sp.nseg * sp.rows));
   // whole chunks and 16-byte aligned rows: the variant without bounds checks
   const bool full = a.vec && a.L % kT == 0;
+#define SS_STATE(TO, NPV)                                                                                  \
+  if (hand > 0) {                                                                                          \
+    if (full) hipLaunchKernelGGL((ssd_scan_kernel<TO, false, NPV, true, true>), sgrid, block, 0, s, a, w, nch, sg);  \
+    else hipLaunchKernelGGL((ssd_scan_kernel<TO, false, NPV, false, true>), sgrid, block, 0, s, a, w, nch, sg);      \
+  }
 #define SS_LAUNCH(TO, GT, NPV)                                                                              \
-  if (full) hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, true>), grid, block, 0, s, a, w, nch);         \
-  else hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, false>), grid, block, 0, s, a, w, nch);
-#define SS_NP(NPV)                                                                                         \
-  case NPV:                                                                                                \
-    if (a.out_bf16) {                                                                                      \
-      if (a.z) { SS_LAUNCH(bf16_t, true, NPV) } else { SS_LAUNCH(bf16_t, false, NPV) }                     \
-    } else {                                                                                               \
-      if (a.z) { SS_LAUNCH(float, true, NPV) } else { SS_LAUNCH(float, false, NPV) }                       \
-    }                                                                                                      \
-    break;
+  if (full) hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, true, false>), grid, block, 0, s, a, w, nch, sg);     \
+  else hipLaunchKernelGGL((ssd_scan_kernel<TO, GT, NPV, false, false>), grid, block, 0, s, a, w, nch, sg);
+#define SS_OUT(NPV)                                                                                        \
+  if (a.out_bf16) {                                                                                        \
+    if (a.z) { SS_LAUNCH(bf16_t, true, NPV) } else { SS_LAUNCH(bf16_t, false, NPV) }                       \
+  } else {                                                                                                 \
+    if (a.z) { SS_LAUNCH(float, true, NPV) } else { SS_LAUNCH(float, false, NPV) }                         \
+  }
   switch (Np) {
-    SS_NP(32) SS_NP(64) SS_NP(96) SS_NP(128)
+    case 32: SS_OUT(32) break;
+    case 64: SS_STATE(float, 64) SS_OUT(64) break;
+    case 96: SS_OUT(96) break;
+    case 128: SS_STATE(float, 128) SS_OUT(128) break;
     default: return hipErrorInvalidValue;
   }
+#undef SS_STATE
 #undef SS_LAUNCH
-#undef SS_NP
+#undef SS_OUT
   return hipGetLastError();
 }
 

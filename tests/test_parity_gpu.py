@@ -112,6 +112,16 @@ def test_scalar_matrix_options(opts):
           "scalar 4x64 %s" % opts)
 
 
+@pytest.mark.parametrize("N,L,batch,heads", [(128, 4096, 1, 1), (64, 1000, 1, 2), (100, 2560, 2, 1)])
+def test_scalar_matrix_segments(N, L, batch, heads):
+    """Few (batch, head) rows and long sequences: the rows are cut into sequence segments
+    (up to 8 here), each started from the state the earlier ones hand over; whole chunks with
+    aligned rows (no bounds checks) and a ragged last chunk."""
+    torch_dev()
+    check(inputs.random_problem(660 + N, batch, 64 * heads, L, N, heads=heads, scalar_decay=True, gate=False),
+          "scalar matrix segments N=%d L=%d" % (N, L))
+
+
 def test_scalar_matrix_growing_state():
     """A > 0: the state grows, so the in-chunk factors 2^(S_t - S_s) exceed 1 (and the masked
     entries above the diagonal have large positive exponents); the matrix form must not clip."""
