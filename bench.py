@@ -245,16 +245,28 @@ def main():
     }
 
     if kernel == "ssd_scan_kernel":
-        # the matrix form runs on v_mfma_f32_16x16x32_bf16 (16*16*32*2 flops each): per
-        # (batch, head, 64-channel slab, 32-step chunk) each of 4 waves issues 4 for the masked
-        # product, Np/8 for the readout from the carried state and Np/8 for the state update
-        # (Np = N padded to a multiple of 32), counting the bf16 hi/lo split passes
+        # The matrix form is a dense contraction on v_mfma_f32_16x16x32_bf16 (16*16*32*2 flops
+        # each), so its roofline is the bf16 matrix peak.  Per (batch, head, 64-channel slab,
+        # 32-step chunk) each of 4 waves issues 4 for the masked product, Np/8 for the readout
+        # from the carried state and Np/8 for the state update (Np = N padded to a multiple of
+        # 32), counting the bf16 hi/lo split passes; the state pass that hands state between
+        # sequence segments is not counted.  The time is the whole call (pre-pass, state pass
+        # and output pass), so the rate is a lower bound for the output pass.  The ALU figures
+        # are kept beside it: the matrix form does less than the recurrence's own arithmetic.
         Np = (p.nstate + 31) // 32 * 32
         nch = (p.length + 31) // 32
         mf = p.batch * p.heads * (p.channels // p.heads // 64) * nch * 4 * (4 + Np // 4) * 16384.0
         mf_tflops = mf / avg_launch_s / 1e12
-        out["roofline"].update({"mfma_executed_flops_per_launch": mf, "mfma_achieved_TFLOPs": mf_tflops,
-                                "mfma_frac_bf16_peak": mf_tflops / BF16_MFMA_PEAK_TFLOPS})
+        rl = out["roofline"]
+        out["roofline"] = {
+            "bound": "mfma", "achieved": mf_tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": mf_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+            "launch_ms": rl["launch_ms"], "mfma_flops_per_launch": mf,
+            "alu_flop_equiv_per_launch": flops, "alu_equiv_TFLOPs": alu_tflops,
+            "alu_equiv_frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "hbm_algorithmic_bytes_per_launch": nbytes, "hbm_achieved_GBps": hbm_gbps,
+            "hbm_frac": hbm_gbps / HBM_PEAK_GBPS,
+        }
 
     if not args.no_cpu_baseline:
         import oracle

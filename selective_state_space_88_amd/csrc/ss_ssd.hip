@@ -149,26 +149,39 @@ struct Segs {
 // FULL: every chunk holds kT steps and every row is 16-byte aligned, so that the loop has no
 // bounds checks (and the compiler can count the memory operations in flight exactly).
 // STATE: the state pass (no y; only the B part of the record is staged).
+//
+// The loop is software-pipelined with one barrier per chunk.  While chunk c is computed from
+// LDS buffer c % 2, chunk c + 1 (loaded into registers during chunk c - 1) is staged into the
+// other buffer together with its step sizes and its masked matrix, and chunk c + 2 is loaded.
+// What crosses waves (the C and B parts of the record, the masked matrix) is double-buffered;
+// u, z, the G piece and the step sizes never leave the wave that loads them.
 template <typename TOut, bool GATE, int NP, bool FULL, bool STATE>
 __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const uint8_t* __restrict__ ws,
                                                                int64_t nchunks, Segs sg) {
   using TIn = bf16_t;
   constexpr int Np = NP;    // states padded to a multiple of 32
-  constexpr int kRecMax = kT * kT * 4 + 2 * kT * NP * 2;
-  __shared__ __attribute__((aligned(16))) uint8_t srec[kRecMax];
+  constexpr int nk = Np / 16;   // state tiles of 16
+  constexpr int kGBytes = kT * kT * 4, kCBytes = kT * Np * 2, kBBytes = kT * Np * 2;
+  // the record's part staged for all waves: C and B (output pass) or B (state pass)
+  constexpr int kShOff = STATE ? kGBytes + kCBytes : kGBytes;
+  constexpr int kShBytes = STATE ? kBBytes : kCBytes + kBBytes;
+  constexpr int kShPieces = kShBytes / 16 / 256;   // 16-byte pieces per thread
+  static_assert(kShBytes % (16 * 256) == 0, "record pieces");
+  __shared__ __attribute__((aligned(16))) u32x4 sh[2][kShBytes / 16];
   // u (and z) of the slab's channels, in lane order: channel 16 w + q, steps 8 g .. 8 g + 7 at
-  // [w][g][q][8], the B operand of wave w's lane 16 g + q
-  __shared__ __attribute__((aligned(16))) uint16_t su[kSlab * kT];
-  __shared__ __attribute__((aligned(16))) uint16_t sz[GATE ? kSlab * kT : 8];
+  // [w][g][q][8], the B operand of wave w's lane 16 g + q (each wave reads only its own part)
+  __shared__ __attribute__((aligned(16))) u32x4 su[64 * kWaves];
+  __shared__ __attribute__((aligned(16))) u32x4 sz[GATE ? 64 * kWaves : 1];
   // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, dt 2^(S_{T-1} - S)
-  __shared__ __attribute__((aligned(16))) float sw[kWaves][4][kT];
+  __shared__ __attribute__((aligned(16))) float sw[2][kWaves][4][kT];
   // the masked matrix of the chunk (the same for every channel of the head), split into bf16
   // hi and lo parts, as the A operand of t-tile i: [i][lane][8]; wave w computes the quarter
   // i = w / 2, K slots 4 (w % 2) .. 4 (w % 2) + 3
-  __shared__ __attribute__((aligned(16))) u32x4 smh[2 * 64], sml[2 * 64];
+  __shared__ __attribute__((aligned(16))) u32x4 smh[2][STATE ? 1 : 2 * 64], sml[2][STATE ? 1 : 2 * 64];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, q = lane & 15;
   const int64_t L = p.L;
   const int64_t slabs = p.chan_per_head / kSlab;
@@ -189,94 +202,19 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   const int64_t rb = rec_bytes(Np);
   const uint8_t* recs = ws + (b * p.groups + grp) * nchunks * rb;
   const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + h * p.dl_sh;
-  constexpr int nk = Np / 16;   // state tiles of 16
-
-  // this wave's state H[n][16w + q]: tile k holds rows 16k + 4 g16 + r
-  f32x4v hacc[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
-
-  // Staging: chunk c + 1's record (rb bytes) and u (and z) tile are loaded into registers, 16
-  // bytes per thread a piece, while chunk c is computed, and written to LDS at the top of the
-  // next iteration.
-  // (the state pass stages only the B part, which starts at kROff)
-  constexpr int kROff = STATE ? kT * kT * 4 + kT * NP * 2 : 0;
-  constexpr int kRecPieces = (kRecMax - kROff) / 16 / 256;   // 16-byte record pieces per thread
-  static_assert((kRecMax - kROff) % (16 * 256) == 0, "record pieces");
-  // u / z piece of this thread: channel 16 (tid / 64) + tid % 16, steps 8 ((tid / 16) % 4) + 0..7
-  const int pr = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15), seg = 8 * ((threadIdx.x >> 4) & 3);
-  const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
-  const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd : nullptr;
-  u32x4 pf_rec[kRecPieces], pf_u, pf_z;
-  uint32_t pf_d = 0u;   // raw bits of delta at step (lane % 32) of the prefetched chunk
-  auto load_piece = [&](const TIn* row, int64_t t) -> u32x4 {
-    if (FULL || (p.vec && t + 8 <= L)) return *reinterpret_cast<const u32x4*>(row + t);
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (t + e < L) w[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(row)[t + e] << (16 * (e % 2));
-    return u32x4{w[0], w[1], w[2], w[3]};
-  };
-  auto prefetch = [&](int64_t c) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(recs + c * rb + kROff);
-#pragma unroll
-    for (int m = 0; m < kRecPieces; ++m) pf_rec[m] = src[threadIdx.x + 256 * m];
-    pf_u = load_piece(ur, c * kT + seg);
-    if constexpr (GATE) pf_z = load_piece(zr, c * kT + seg);
-    // (kept raw: widening it here would make the compiler wait for every load just issued)
-    const int64_t t = c * kT + (lane & (kT - 1));
-    pf_d = reinterpret_cast<const uint16_t*>(drow)[(FULL || t < L) ? t : 0];
-  };
-  auto commit = [&]() {
-    u32x4* dst = reinterpret_cast<u32x4*>(srec + kROff);
-#pragma unroll
-    for (int m = 0; m < kRecPieces; ++m) dst[threadIdx.x + 256 * m] = pf_rec[m];
-    reinterpret_cast<u32x4*>(su)[threadIdx.x] = pf_u;
-    if constexpr (GATE) reinterpret_cast<u32x4*>(sz)[threadIdx.x] = pf_z;
-  };
-
-  const f32x4v* Gp = reinterpret_cast<const f32x4v*>(srec);             // [i][half][lane]
-  const u32x4* Cp = reinterpret_cast<const u32x4*>(srec + kT * kT * 4);  // [i][ks][lane]
-  const u32x4* Bp = Cp + kT * Np / 8;                                      // [k][lane]
-  float* wdt = sw[wave][0];
-  float* wS = sw[wave][1];
-  float* weS = sw[wave][2];
-  float* wXd = sw[wave][3];
   const int pch = 16 * wave + q;   // this lane's channel in the slab (B operand / D column)
-  // (read once here: inside the loop the compiler reloads it after every y store, and the
-  // reload's wait would also wait for the next chunk's prefetch)
   // with one D per head, D u_t is folded into the diagonal of the masked matrix (u is its
-  // exact B operand); with one D per channel it is added to y
+  // exact B operand); with one D per channel it is added to y.  (Read once here: inside the
+  // loop the compiler would reload them after every y store.)
   const bool dfold = p.D && p.d_per_head;
   const float Dfold = dfold ? p.D[h] : 0.f;
   const float Dd = (p.D && !dfold) ? p.D[c0 + pch] : 0.f;
   TOut* const yr = static_cast<TOut*>(p.y) + b * p.y_sb + (c0 + pch) * p.y_sd;
 
-  // y of one chunk, t = 16 i + 4 g16 + r; in the FULL variant it is stored at the top of the
-  // next iteration, just before the next prefetch, so that no wait for the prefetched data
-  // has a store of the same iteration queued in front of it
-  float ypend[2][4];
-  auto store_y = [&](int64_t tc) {
+  // this wave's state H[n][16w + q]: tile k holds rows 16k + 4 g16 + r
+  f32x4v hacc[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t tg = tc + 16 * i + 4 * g16;
-      const float* v = ypend[i];
-      if (FULL || (p.vec && tg + 4 <= L)) {
-        if constexpr (sizeof(TOut) == 4) {
-          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(yr + tg));
-        } else {
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          __builtin_nontemporal_store(u32x2{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])},
-                                      reinterpret_cast<u32x2*>(yr + tg));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (tg + r < L) store_one(yr + tg + r, v[r]);
-      }
-    }
-  };
-
+  for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
   if constexpr (!STATE) {
     // the state entering this segment, from the state pass's results (j = sgi - 1 first, whose
     // end state enters undecayed)
@@ -293,54 +231,76 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   }
   float dlog = 0.f;   // log2 decay over the chunks done so far (state pass)
 
-  prefetch(cb);
-  for (int64_t c = cb; c < ce; ++c) {
-    const int64_t t0 = c * kT;
-    __syncthreads();  // the previous chunk's reads of the staging buffers are done
-    commit();
-    if constexpr (FULL && !STATE) {
-      if (c > cb) store_y(t0 - kT);
-    }
-    const float draw = __uint_as_float(pf_d << 16);
-    prefetch(c + 1 < ce ? c + 1 : c);  // (the last chunk loads itself again, unused)
-    // keep the prefetch here, at the top: the scheduler would otherwise sink the loads to the
-    // end of the iteration, where the next commit waits for them at once
-    __builtin_amdgcn_sched_barrier(0);
+  // registers holding the next chunk to stage
+  // u / z piece of this thread: channel 16 (tid / 64) + tid % 16, steps 8 ((tid / 16) % 4) + 0..7
+  const int pr = 16 * (tid >> 6) + (tid & 15), seg = 8 * ((tid >> 4) & 3);
+  const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + (c0 + pr) * p.u_sd;
+  const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + (c0 + pr) * p.z_sd : nullptr;
+  u32x4 pf_sh[kShPieces], pf_g, pf_u, pf_z;
+  uint32_t pf_d = 0u;   // raw bits of delta at step (lane % 32) of the chunk
+  auto load_piece = [&](const TIn* rp, int64_t t) -> u32x4 {
+    if (FULL || (p.vec && t + 8 <= L)) return *reinterpret_cast<const u32x4*>(rp + t);
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (t + e < L) w[e / 2] |= (uint32_t)reinterpret_cast<const uint16_t*>(rp)[t + e] << (16 * (e % 2));
+    return u32x4{w[0], w[1], w[2], w[3]};
+  };
+  auto prefetch = [&](int64_t c) {
+    const uint8_t* rec = recs + c * rb;
+    // the G piece this thread's quarter of the masked matrix needs is piece tid
+    if constexpr (!STATE) pf_g = reinterpret_cast<const u32x4*>(rec)[tid];
+#pragma unroll
+    for (int m = 0; m < kShPieces; ++m) pf_sh[m] = reinterpret_cast<const u32x4*>(rec + kShOff)[tid + 256 * m];
+    pf_u = load_piece(ur, c * kT + seg);
+    if constexpr (GATE) pf_z = load_piece(zr, c * kT + seg);
+    const int64_t t = c * kT + (lane & (kT - 1));
+    pf_d = reinterpret_cast<const uint16_t*>(drow)[(FULL || t < L) ? t : 0];
+  };
+
+  // stage chunk c (from the registers) into buffer bf: the shared record part, this wave's
+  // u / z, its step sizes and (output pass) its quarter of the masked matrix
+  auto stage = [&](int64_t c, int bf) {
+#pragma unroll
+    for (int m = 0; m < kShPieces; ++m) sh[bf][tid + 256 * m] = pf_sh[m];
+    su[tid] = pf_u;
+    if constexpr (GATE) sz[tid] = pf_z;
+    float* wdt = sw[bf][wave][0];
+    float* wS = sw[bf][wave][1];
     // dt and S of the chunk, in lanes 0..31 of every wave (each wave keeps its own copy)
     {
       const int t = lane & (kT - 1);
       float dt = 0.f;
-      if (lane < kT && (FULL || t0 + t < L)) {
-        const float x = draw + bias;
+      if (lane < kT && (FULL || c * kT + t < L)) {
+        const float x = __uint_as_float(pf_d << 16) + bias;
         dt = p.softplus ? softplus_fast(x) : x;
       }
       // inclusive prefix sum of dt * A * log2 e over lanes 0..31: DPP row_shr 1, 2, 4, 8
       // within rows of 16 (a source outside the row reads 0), then row 0's total added to
       // row 1 (row_bcast:15 on rows 1 and 3)
-      float s = dt * A2;
-      s += dpp_zero<0x111, 0xf>(s);
-      s += dpp_zero<0x112, 0xf>(s);
-      s += dpp_zero<0x114, 0xf>(s);
-      s += dpp_zero<0x118, 0xf>(s);
-      s += dpp_zero<0x142, 0xa>(s);
-      const float sEnd = readlane_f(s, kT - 1);
-      dlog += sEnd;
+      float sc = dt * A2;
+      sc += dpp_zero<0x111, 0xf>(sc);
+      sc += dpp_zero<0x112, 0xf>(sc);
+      sc += dpp_zero<0x114, 0xf>(sc);
+      sc += dpp_zero<0x118, 0xf>(sc);
+      sc += dpp_zero<0x142, 0xa>(sc);
+      const float sEnd = readlane_f(sc, kT - 1);
       if (lane < kT) {
         wdt[t] = dt;
-        wS[t] = s;
-        weS[t] = __builtin_amdgcn_exp2f(s);
-        wXd[t] = dt * __builtin_amdgcn_exp2f(sEnd - s);
+        wS[t] = sc;
+        sw[bf][wave][2][t] = __builtin_amdgcn_exp2f(sc);
+        sw[bf][wave][3][t] = dt * __builtin_amdgcn_exp2f(sEnd - sc);
       }
     }
     // this wave's quarter of the masked matrix (G o L)[t][s] dt_s (+ D on the diagonal), for
-    // t = 16 iq + q, s = 8 g16 + 4 hq + e; its G piece is the one this thread committed
+    // t = 16 iq + q, s = 8 g16 + 4 hq + e
     if constexpr (!STATE) {
       const int iq = wave >> 1, hq = wave & 1;
       const int t = 16 * iq + q;
       const float St = wS[t];
       const f32x4v Ssq = reinterpret_cast<const f32x4v*>(wS)[2 * g16 + hq];
       const f32x4v dtq = reinterpret_cast<const f32x4v*>(wdt)[2 * g16 + hq];
-      const f32x4v gq = Gp[wave * 64 + lane];
+      const f32x4v gq = __builtin_bit_cast(f32x4v, pf_g);
       float m[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -353,53 +313,92 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       const uint32_t l0 = pk_bf16(m[0] - __uint_as_float(h0 << 16), m[1] - __uint_as_float(h0 & 0xffff0000u));
       const uint32_t l1 = pk_bf16(m[2] - __uint_as_float(h1 << 16), m[3] - __uint_as_float(h1 & 0xffff0000u));
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      reinterpret_cast<u32x2*>(smh)[2 * (iq * 64 + lane) + hq] = u32x2{h0, h1};
-      reinterpret_cast<u32x2*>(sml)[2 * (iq * 64 + lane) + hq] = u32x2{l0, l1};
+      reinterpret_cast<u32x2*>(smh[bf])[2 * (iq * 64 + lane) + hq] = u32x2{h0, h1};
+      reinterpret_cast<u32x2*>(sml[bf])[2 * (iq * 64 + lane) + hq] = u32x2{l0, l1};
     }
-    __syncthreads();  // staging and the masked matrix visible to every wave
-    const float eT = weS[kT - 1];
+  };
+
+  // y of one chunk, t = 16 i + 4 g16 + r
+  float yv[2][4];
+  auto store_y = [&](int64_t tc) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t tg = tc + 16 * i + 4 * g16;
+      const float* v = yv[i];
+      if (FULL || (p.vec && tg + 4 <= L)) {
+        if constexpr (sizeof(TOut) == 4) {
+          __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(yr + tg));
+        } else {
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_nontemporal_store(u32x2{pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3])},
+                                      reinterpret_cast<u32x2*>(yr + tg));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tg + r < L) store_one(yr + tg + r, v[r]);
+      }
+    }
+  };
+
+  prefetch(cb);
+  stage(cb, 0);
+  prefetch(cb + 1 < ce ? cb + 1 : cb);
+  __syncthreads();
+  for (int64_t c = cb; c < ce; ++c) {
+    const int bf = (int)((c - cb) & 1);
+    const float* wS = sw[bf][wave][1];
+    const float* weS = sw[bf][wave][2];
+    const float* wXd = sw[bf][wave][3];
+    const u32x4* Cp = sh[bf];                                // [i][ks][lane] (output pass)
+    const u32x4* Bp = sh[bf] + (STATE ? 0 : kCBytes / 16);   // [k][lane]
+    const float sEnd = wS[kT - 1];
+    const float eT = __builtin_amdgcn_exp2f(sEnd);
+    dlog += sEnd;
 
     // u[s = 8 g16 + k][pch]: the exact (bf16) B operand of the masked product; and
     // Xd[s][pch] = dt_s 2^(S_{T-1} - S_s) u_s, the B operand of the state update, split
-    const u32x4 uw = reinterpret_cast<const u32x4*>(su)[64 * wave + lane];
-    const bf16x8 ub = as_bf16x8(uw);
+    const u32x4 uw = su[tid];
     bf16x8 xdhi, xdlo;
     {
       const uint32_t uwv[4] = {uw.x, uw.y, uw.z, uw.w};
+      const f32x4v xd0 = reinterpret_cast<const f32x4v*>(wXd)[2 * g16];
+      const f32x4v xd1 = reinterpret_cast<const f32x4v*>(wXd)[2 * g16 + 1];
       float xd[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        xd[k] = wXd[8 * g16 + k] * ((k & 1) ? bf16_hi(uwv[k / 2]) : bf16_lo(uwv[k / 2]));
+        xd[k] = (k < 4 ? xd0[k] : xd1[k - 4]) * ((k & 1) ? bf16_hi(uwv[k / 2]) : bf16_lo(uwv[k / 2]));
       split8(xd, xdhi, xdlo);
     }
 
     if constexpr (!STATE) {
       // y tiles: t-tile i (rows 16 i + 4 g16 + r), this wave's 16 channels
       f32x4v yacc[2], iacc[2];
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 2; ++i) {
         yacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
         iacc[i] = f32x4v{0.f, 0.f, 0.f, 0.f};
       }
       // within the chunk: the shared masked matrix (hi + lo) times u
-  #pragma unroll
+      const bf16x8 ub = as_bf16x8(uw);
+#pragma unroll
       for (int i = 0; i < 2; ++i) {
-        yacc[i] = mfma(as_bf16x8(smh[i * 64 + lane]), ub, yacc[i]);
-        yacc[i] = mfma(as_bf16x8(sml[i * 64 + lane]), ub, yacc[i]);
+        yacc[i] = mfma(as_bf16x8(smh[bf][i * 64 + lane]), ub, yacc[i]);
+        yacc[i] = mfma(as_bf16x8(sml[bf][i * 64 + lane]), ub, yacc[i]);
       }
       // from the carried state: C[t][n] H[n][pch], n in steps of 32 in the accumulators' order
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         if (2 * ks < nk) {
           float hv[8];
-  #pragma unroll
+#pragma unroll
           for (int r = 0; r < 4; ++r) {
             hv[r] = hacc[2 * ks][r];
             hv[4 + r] = hacc[2 * ks + 1][r];
           }
           bf16x8 hhi, hlo;
           split8(hv, hhi, hlo);
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 2; ++i) {
             const bf16x8 ca = as_bf16x8(Cp[(i * (Np / 32) + ks) * 64 + lane]);
             iacc[i] = mfma(ca, hhi, iacc[i]);
@@ -408,25 +407,24 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         }
       }
       // y = within + 2^S_t (C H) + D u, gated; lane holds t = 16 i + 4 g16 + r of channel pch
-  #pragma unroll
+#pragma unroll
       for (int i = 0; i < 2; ++i) {
         // u (and z) at steps 16 i + 4 g16 + 0..3 of channel pch: four bf16 of one lane-order piece
         const int uo = ((4 * wave + 2 * i + (g16 >> 1)) * 16 + q) * 8 + 4 * (g16 & 1);
-        const uint2 uq = *reinterpret_cast<const uint2*>(su + uo);
+        const uint2 uq = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(su) + uo);
         uint2 zq = uint2{0u, 0u};
-        if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(sz + uo);
+        if constexpr (GATE) zq = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(sz) + uo);
         const uint32_t uwq[2] = {uq.x, uq.y}, zw[2] = {zq.x, zq.y};
         const f32x4v eS = reinterpret_cast<const f32x4v*>(weS)[4 * i + g16];
-  #pragma unroll
+#pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float uu = (r & 1) ? bf16_hi(uwq[r / 2]) : bf16_lo(uwq[r / 2]);
           float yy = yacc[i][r] + eS[r] * iacc[i][r];
           if (!dfold) yy += Dd * uu;
           if constexpr (GATE) yy *= silu_fast((r & 1) ? bf16_hi(zw[r / 2]) : bf16_lo(zw[r / 2]));
-          ypend[i][r] = yy;
+          yv[i][r] = yy;
         }
       }
-      if constexpr (!FULL) store_y(t0);
     }
     // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd
 #pragma unroll
@@ -438,16 +436,22 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         hacc[k] = mfma(ba, xdlo, hacc[k]);
       }
     }
+
+    // stage chunk c + 1 (the last chunk stages itself again, unused), store y, load chunk c + 2
+    const int64_t cn = c + 1 < ce ? c + 1 : c;
+    stage(cn, bf ^ 1);
+    if constexpr (!STATE) store_y(c * kT);
+    prefetch(c + 2 < ce ? c + 2 : cn);
+    __syncthreads();
   }
+
   if constexpr (STATE) {
     // this segment's end state (wave-ordered, as the output pass reads it) and decay
     f32x4v* hl = reinterpret_cast<f32x4v*>(sg.hloc) + (blk * kWaves + wave) * nk * 64 + lane;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (k < nk) hl[k * 64] = hacc[k];
-    if (threadIdx.x == 0) sg.dsum[blk] = dlog;
-  } else if constexpr (FULL) {
-    store_y((ce - 1) * kT);
+    if (tid == 0) sg.dsum[blk] = dlog;
   }
 }
 
@@ -489,6 +493,9 @@ SegPlan seg_plan(const ScanArgs& a) {
   int64_t nseg = 1;
   if (npad32(a.N) % 64 == 0 && rows > 0)
     nseg = std::min<int64_t>((int64_t)kBlocksPerCU * cu_count() / rows, nch / kMinSegChunks);
+#ifdef SS_SSD_SEGS
+  if (npad32(a.N) % 64 == 0) nseg = std::min<int64_t>(SS_SSD_SEGS, nch);  // tuning override
+#endif
   nseg = std::max<int64_t>(nseg, 1);
   const int64_t cps = (nch + nseg - 1) / nseg;
   nseg = (nch + cps - 1) / cps;
