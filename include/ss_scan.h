@@ -72,7 +72,7 @@ typedef struct {
 #define SS_ERR_STRIDE (-4)      /* innermost stride != 1, or a negative stride */
 #define SS_ERR_FLAGS (-5)       /* unknown flag bits, or SS_Z_GATE_SILU without z */
 #define SS_ERR_UNSUPPORTED (-6) /* valid but unsupported size (N > 128, or > 2^31 steps per row) */
-#define SS_ERR_ALIAS (-7)       /* y overlaps an input */
+#define SS_ERR_ALIAS (-7)       /* an output (y, a final state) overlaps an input or another output */
 #define SS_ERR_HIP (-8)         /* a HIP runtime call failed (launch, workspace allocation) */
 
 /*
@@ -85,6 +85,7 @@ typedef struct {
  *   B, C       [batch, groups, N, L]         same dtype as u; groups divides channels
  *   D          [channels] or [heads] f32     optional (NULL or data == NULL): no feed-through
  *   z          [batch, channels, L]          same dtype as u; optional, required by SS_Z_GATE_SILU
+ *                                            (a z of no elements may have data == NULL)
  *   delta_bias [heads] f32                   optional: no bias
  *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU
  *   y          [batch, channels, L]          f32 | bf16, written; must not overlap any input
@@ -93,14 +94,64 @@ typedef struct {
  * N must be 1..128.  L = 0 or batch * channels = 0 is a successful no-op.  The state starts at
  * zero for every (b, d).  Internally the computation is in f32 (bf16 inputs are widened exactly);
  * y in bf16 is rounded to nearest even once.  Scalar-decay calls use a stream-ordered device
- * workspace of batch * groups * L * 16 * ceil(N / 16) floats, allocated and freed on `stream`
- * (SS_ERR_HIP if that allocation fails).
+ * workspace (per-chunk operands of B and C, and the states handed between sequence segments;
+ * O(batch * groups * L * N) bytes), allocated and freed on `stream` (SS_ERR_HIP if that
+ * allocation fails).
  *
  * Returns SS_OK or a negative SS_ERR_* code.
  */
 int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                 const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream);
+
+/*
+ * ss_scan_fwd_state -- ss_scan_fwd that starts from a given state and returns the final one, so
+ * that a long sequence can be scanned in consecutive pieces (chunked prefill, streaming): the
+ * recurrent reading of the method keeps a state of fixed size per channel and carries it from
+ * token to token ("Mamba -- selective state space model" study notes, core points and case 3;
+ * bqwf.cn state-space survey, section 1, the recurrent mode).  Scanning [0, T) and then [T, L)
+ * from the carried state gives the same y as one scan over [0, L), up to rounding.
+ *
+ *   arguments as ss_scan_fwd, and
+ *   h_init     [batch, channels, N] f32      optional (NULL or data == NULL): the state starts
+ *                                            at zero, as in ss_scan_fwd
+ *   h_final    [batch, channels, N] f32      optional: not written.  Written with the state
+ *                                            after step L - 1 (h_init itself when L = 0).
+ *                                            Must not overlap h_init, any input or y
+ *                                            (SS_ERR_ALIAS); use two buffers in turn to carry a
+ *                                            state from call to call.
+ *
+ * The state index n is innermost (stride 1); the other strides are free.  Ownership, errors and
+ * asynchrony are those of ss_scan_fwd.
+ */
+int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                      const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                      const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
+                      ss_tensor* h_final, ss_tensor* y, void* stream);
+
+/*
+ * ss_scan_step -- one decoding step: the recurrence advanced by a single token from a persistent
+ * state, h <- exp(dt A) h + dt B u, y = C h + D u (times silu(z)), the inference mode in which
+ * each new token updates a state of fixed size (study notes, core points and cases 1 and 3).
+ * Equal, up to rounding, to ss_scan_fwd_state over L = 1 with h_init = h_final = h.
+ *
+ *   u          [batch, channels]             f32 | bf16
+ *   delta      [batch, heads]                same dtype as u
+ *   A          [channels, N] or [heads] f32  as in ss_scan_fwd
+ *   B, C       [batch, groups, N]            same dtype as u
+ *   D          [channels] or [heads] f32     optional
+ *   z          [batch, channels]             same dtype as u; optional, required by SS_Z_GATE_SILU
+ *   delta_bias [heads] f32                   optional
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU
+ *   h          [batch, channels, N] f32      read and updated in place (state index innermost)
+ *   y          [batch, channels]             f32 | bf16, written
+ *
+ * h and y must not overlap each other or any input (SS_ERR_ALIAS).  batch * channels = 0 is a
+ * successful no-op.  No workspace.  Errors, ownership and asynchrony as in ss_scan_fwd.
+ */
+int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                 const ss_tensor* delta_bias, uint32_t flags, ss_tensor* h, ss_tensor* y, void* stream);
 
 /* Synchronises `stream` and returns SS_OK, or SS_ERR_HIP if any enqueued work failed. */
 int ss_check(void* stream);

@@ -26,6 +26,16 @@ int64_t numel(const ss_tensor* t) {
   return n;
 }
 
+// passed by the caller: a descriptor with data, or one of no elements (whose data may be NULL)
+bool given(const ss_tensor* t) {
+  if (t == nullptr) return false;
+  if (t->data != nullptr) return true;
+  if (t->ndim < 1 || t->ndim > 4) return false;
+  for (int i = 0; i < t->ndim; ++i)
+    if (t->shape[i] == 0) return true;
+  return false;
+}
+
 int check_basic(const ss_tensor* t, int ndim) {
   if (t->ndim != ndim) return SS_ERR_SHAPE;
   if (t->dtype != SS_F32 && t->dtype != SS_BF16) return SS_ERR_DTYPE;
@@ -60,7 +70,7 @@ const char* ss_strerror(int code) {
     case SS_ERR_STRIDE: return "innermost stride must be 1 and strides non-negative";
     case SS_ERR_FLAGS: return "unknown flag bits, or SS_Z_GATE_SILU without z";
     case SS_ERR_UNSUPPORTED: return "unsupported size (N must be 1..128; at most 2^31 steps per row)";
-    case SS_ERR_ALIAS: return "y overlaps an input";
+    case SS_ERR_ALIAS: return "an output (y, a final state) overlaps an input or another output";
     case SS_ERR_HIP: return "HIP runtime error";
     default: return "unknown error code";
   }
@@ -72,14 +82,34 @@ int ss_check(void* stream) {
   return SS_OK;
 }
 
-int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
-                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
-                const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool overlaps(const ss_tensor* a, const ss_tensor* b) {
+  if (!present(a) || !present(b) || numel(a) == 0 || numel(b) == 0) return false;
+  uintptr_t alo, ahi, blo, bhi;
+  extent(a, &alo, &ahi);
+  extent(b, &blo, &bhi);
+  return alo < bhi && blo < ahi;
+}
+
+// a state tensor [batch, channels, N] f32 (state index innermost)
+int check_state(const ss_tensor* h, int64_t Bt, int64_t Dc, int64_t N) {
+  int rc;
+  if ((rc = check_basic(h, 3))) return rc;
+  if (h->dtype != SS_F32) return SS_ERR_DTYPE;
+  if (h->shape[0] != Bt || h->shape[1] != Dc || h->shape[2] != N) return SS_ERR_SHAPE;
+  return SS_OK;
+}
+
+int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
+                uint32_t flags, const ss_tensor* h_init, ss_tensor* h_final, ss_tensor* y, void* stream) {
   if (!u || !delta || !A || !B || !C || !y) return SS_ERR_NULL;
   if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU)) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
-  if (gate && !present(z)) return SS_ERR_FLAGS;
-  if (!gate && present(z)) return SS_ERR_FLAGS;
+  if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
   if ((rc = check_basic(u, 3)) || (rc = check_basic(delta, 3)) || (rc = check_basic(B, 4)) ||
       (rc = check_basic(C, 4)) || (rc = check_basic(y, 3)))
@@ -113,21 +143,36 @@ int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (present(delta_bias) && delta_bias->shape[0] != H) return SS_ERR_SHAPE;
   if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
   if (L > ((int64_t)1 << 31)) return SS_ERR_UNSUPPORTED;
-  if (L == 0 || Bt * Dc == 0) return SS_OK;  // nothing to compute
-  if (!u->data || !delta->data || !A->data || !B->data || !C->data || !y->data) return SS_ERR_NULL;
+  if (present(h_init) && (rc = check_state(h_init, Bt, Dc, N))) return rc;
+  if (present(h_final) && (rc = check_state(h_final, Bt, Dc, N))) return rc;
+  if (present(h_final) && overlaps(h_final, h_init)) return SS_ERR_ALIAS;
+  if (Bt * Dc == 0) return SS_OK;  // nothing to compute
   if (scalar && G > 1 && (Dc / G) % 64) return SS_ERR_UNSUPPORTED;
 
   // y must not overlap any input
   uintptr_t ylo, yhi;
   extent(y, &ylo, &yhi);
-  const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias};
+  const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias, h_init};
   for (const ss_tensor* t : ins) {
     if (!present(t) || numel(t) == 0) continue;
     uintptr_t lo, hi;
     extent(t, &lo, &hi);
     if (lo < yhi && ylo < hi) return SS_ERR_ALIAS;
+    if (overlaps(h_final, t)) return SS_ERR_ALIAS;
   }
+  if (overlaps(h_final, y)) return SS_ERR_ALIAS;
 
+  if (L == 0) {
+    // no steps: the final state is the initial one (zero without h_init)
+    if (!present(h_final)) return SS_OK;
+    const float* hi = present(h_init) ? static_cast<const float*>(h_init->data) : nullptr;
+    return ss::launch_state_copy(hi, hi ? h_init->stride[0] : 0, hi ? h_init->stride[1] : 0,
+                                 static_cast<float*>(h_final->data), h_final->stride[0], h_final->stride[1], Bt,
+                                 Dc, N, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? SS_OK
+               : SS_ERR_HIP;
+  }
+  if (!u->data || !delta->data || !A->data || !B->data || !C->data || !y->data) return SS_ERR_NULL;
   ss::ScanArgs a{};
   a.u = u->data;
   a.delta = delta->data;
@@ -167,6 +212,12 @@ int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   a.y_sb = y->stride[0];
   a.y_sd = y->stride[1];
   a.A_sd = scalar ? 0 : A->stride[0];
+  a.h_init = present(h_init) ? static_cast<const float*>(h_init->data) : nullptr;
+  a.h_final = present(h_final) ? static_cast<float*>(h_final->data) : nullptr;
+  a.hi_sb = a.h_init ? h_init->stride[0] : 0;
+  a.hi_sd = a.h_init ? h_init->stride[1] : 0;
+  a.hf_sb = a.h_final ? h_final->stride[0] : 0;
+  a.hf_sd = a.h_final ? h_final->stride[1] : 0;
   if (present(D) && D->stride[0] != 1 && D->shape[0] > 1) return SS_ERR_STRIDE;
   if (present(delta_bias) && delta_bias->stride[0] != 1 && delta_bias->shape[0] > 1) return SS_ERR_STRIDE;
   if (scalar && A->stride[0] != 1 && A->shape[0] > 1) return SS_ERR_STRIDE;
@@ -186,6 +237,107 @@ int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   const hipError_t e = mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
   const hipError_t f = hipFreeAsync(ws, s);
   return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream) {
+  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, nullptr, nullptr, y, stream);
+}
+
+int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                      const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                      const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
+                      ss_tensor* h_final, ss_tensor* y, void* stream) {
+  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, h_init, h_final, y, stream);
+}
+
+int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                 const ss_tensor* delta_bias, uint32_t flags, ss_tensor* h, ss_tensor* y, void* stream) {
+  if (!u || !delta || !A || !B || !C || !h || !y) return SS_ERR_NULL;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU)) return SS_ERR_FLAGS;
+  const bool gate = (flags & SS_Z_GATE_SILU) != 0;
+  if (gate != given(z)) return SS_ERR_FLAGS;
+  int rc;
+  if ((rc = check_basic(u, 2)) || (rc = check_basic(delta, 2)) || (rc = check_basic(B, 3)) ||
+      (rc = check_basic(C, 3)) || (rc = check_basic(y, 2)))
+    return rc;
+  if (A->ndim != 1 && A->ndim != 2) return SS_ERR_SHAPE;
+  if ((rc = check_basic(A, A->ndim))) return rc;
+  if (gate && (rc = check_basic(z, 2))) return rc;
+  if (present(D) && (rc = check_basic(D, 1))) return rc;
+  if (present(delta_bias) && (rc = check_basic(delta_bias, 1))) return rc;
+  const int32_t idt = u->dtype;
+  if (delta->dtype != idt || B->dtype != idt || C->dtype != idt || (gate && z->dtype != idt))
+    return SS_ERR_DTYPE;
+  if (A->dtype != SS_F32 || (present(D) && D->dtype != SS_F32) ||
+      (present(delta_bias) && delta_bias->dtype != SS_F32))
+    return SS_ERR_DTYPE;
+  const int64_t Bt = u->shape[0], Dc = u->shape[1];
+  const int64_t H = delta->shape[1], G = B->shape[1], N = B->shape[2];
+  if (delta->shape[0] != Bt || B->shape[0] != Bt) return SS_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (C->shape[i] != B->shape[i]) return SS_ERR_SHAPE;
+  for (int i = 0; i < 2; ++i)
+    if (y->shape[i] != u->shape[i] || (gate && z->shape[i] != u->shape[i])) return SS_ERR_SHAPE;
+  if (H <= 0 || G <= 0 || (Dc > 0 && (Dc % H || Dc % G))) return SS_ERR_SHAPE;
+  const bool scalar = A->ndim == 1;
+  if (scalar ? A->shape[0] != H : (A->shape[0] != Dc || A->shape[1] != N)) return SS_ERR_SHAPE;
+  if (present(D) && D->shape[0] != Dc && D->shape[0] != H) return SS_ERR_SHAPE;
+  if (present(delta_bias) && delta_bias->shape[0] != H) return SS_ERR_SHAPE;
+  if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
+  if ((rc = check_state(h, Bt, Dc, N))) return rc;
+  if (Bt * Dc == 0) return SS_OK;
+  if (!u->data || !delta->data || !A->data || !B->data || !C->data || !y->data || !h->data) return SS_ERR_NULL;
+  if (present(D) && D->stride[0] != 1 && D->shape[0] > 1) return SS_ERR_STRIDE;
+  if (present(delta_bias) && delta_bias->stride[0] != 1 && delta_bias->shape[0] > 1) return SS_ERR_STRIDE;
+  if (scalar && A->stride[0] != 1 && A->shape[0] > 1) return SS_ERR_STRIDE;
+  // y and h are written: neither may overlap an input or the other
+  const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias};
+  for (const ss_tensor* t : ins)
+    if (overlaps(y, t) || overlaps(h, t)) return SS_ERR_ALIAS;
+  if (overlaps(y, h)) return SS_ERR_ALIAS;
+
+  ss::StepArgs a{};
+  a.u = u->data;
+  a.delta = delta->data;
+  a.B = B->data;
+  a.C = C->data;
+  a.z = gate ? z->data : nullptr;
+  a.A = static_cast<const float*>(A->data);
+  a.D = present(D) ? static_cast<const float*>(D->data) : nullptr;
+  a.bias = present(delta_bias) ? static_cast<const float*>(delta_bias->data) : nullptr;
+  a.h = static_cast<float*>(h->data);
+  a.y = y->data;
+  a.batch = Bt;
+  a.channels = Dc;
+  a.N = (int32_t)N;
+  a.heads = (int32_t)H;
+  a.groups = (int32_t)G;
+  a.chan_per_head = (int32_t)(Dc / H);
+  a.chan_per_group = (int32_t)(Dc / G);
+  a.scalar = scalar ? 1 : 0;
+  a.d_per_head = present(D) && D->shape[0] != Dc ? 1 : 0;
+  a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
+  a.in_bf16 = idt == SS_BF16;
+  a.out_bf16 = y->dtype == SS_BF16;
+  a.u_sb = u->stride[0];
+  a.dl_sb = delta->stride[0];
+  a.z_sb = gate ? z->stride[0] : 0;
+  a.B_sb = B->stride[0];
+  a.B_sg = B->stride[1];
+  a.C_sb = C->stride[0];
+  a.C_sg = C->stride[1];
+  a.y_sb = y->stride[0];
+  a.A_sd = scalar ? 0 : A->stride[0];
+  a.h_sb = h->stride[0];
+  a.h_sd = h->stride[1];
+  return ss::launch_step(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 }  // extern "C"

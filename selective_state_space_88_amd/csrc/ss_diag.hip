@@ -392,10 +392,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
   float4* mypar = par + (wave * ROWS + r) * kMaxPairs;
   {
+    // the carried state starts at the caller's initial state, or at zero
     const float* Ar = p.A + d * p.A_sd;
+    const float* hi = p.h_init ? p.h_init + b * p.hi_sb + d * p.hi_sd : nullptr;
     for (int pp = jl; pp < P; pp += LPC) {
       const int n = 2 * pp;
-      mypar[pp] = make_float4(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f, 0.f, 0.f);
+      mypar[pp] = make_float4(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f, hi ? hi[n] : 0.f,
+                              (hi && n + 1 < N) ? hi[n + 1] : 0.f);
     }
   }
   uint32_t* xu = xin[wave][0];
@@ -700,6 +703,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         x_copy(zrow, w + 1, xz);
         carry_ops += NCI;
       }
+    }
+  }
+  // the state after the last step (steps past L are the identity), carried by the row's last
+  // lane into its pair slots
+  if (p.h_final && live) {
+    float* hf = p.h_final + b * p.hf_sb + d * p.hf_sd;
+    for (int pp = jl; pp < P; pp += LPC) {
+      const float4 pv = mypar[pp];
+      hf[2 * pp] = pv.z;
+      if (2 * pp + 1 < N) hf[2 * pp + 1] = pv.w;
     }
   }
 }

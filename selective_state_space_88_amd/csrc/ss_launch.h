@@ -27,7 +27,40 @@ struct ScanArgs {
   int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd;
   int64_t B_sb, B_sg, B_sn, C_sb, C_sg, C_sn;
   int64_t y_sb, y_sd, A_sd;
+  // optional state in / out, [batch, channels, N] f32, state index innermost (stride 1)
+  const float* h_init;    // nullptr: the state starts at zero
+  float* h_final;         // nullptr: not written
+  int64_t hi_sb, hi_sd, hf_sb, hf_sd;
 };
+
+// Arguments of one decoding step (L = 1), already validated.  Strides in elements.
+struct StepArgs {
+  const void* u;          // [batch, channels]
+  const void* delta;      // [batch, heads]
+  const void* B;          // [batch, groups, N]
+  const void* C;
+  const void* z;          // nullptr: no gate
+  const float* A;         // [channels, N] or [heads]
+  const float* D;         // nullable
+  const float* bias;      // nullable
+  float* h;               // [batch, channels, N], read and written in place
+  void* y;                // [batch, channels]
+  int64_t batch, channels;
+  int32_t N, heads, groups;
+  int32_t chan_per_head, chan_per_group;
+  int32_t scalar;         // A per head
+  int32_t d_per_head;
+  int32_t softplus;
+  int32_t in_bf16, out_bf16;
+  int64_t u_sb, dl_sb, z_sb, B_sb, B_sg, C_sb, C_sg, y_sb, A_sd, h_sb, h_sd;
+};
+
+// One step of the recurrence for every (batch, channel): h = exp(dt A) h + dt B u, y = C h + D u.
+hipError_t launch_step(const StepArgs& a, hipStream_t stream);
+
+// dst[b, d, n] = src[b, d, n] (src == nullptr: 0) for a [batch, channels, N] f32 state.
+hipError_t launch_state_copy(const float* src, int64_t s_sb, int64_t s_sd, float* dst, int64_t d_sb,
+                             int64_t d_sd, int64_t batch, int64_t channels, int64_t N, hipStream_t stream);
 
 // Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time.  One
 // kernel, no workspace.

@@ -120,9 +120,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
   const cfloat* Bs = to_constant(wsB + (b * p.groups + g) * L * Npad + wv * kNT);
   const cfloat* Cs = to_constant(wsC + (b * p.groups + g) * L * Npad + wv * kNT);
 
+  // this wave's states wv * kNT + i of the lane's channel, from the caller's initial state or zero
   float h[kNT];
+  {
+    const float* hi = p.h_init ? p.h_init + b * p.hi_sb + dl_ * p.hi_sd : nullptr;
 #pragma unroll
-  for (int i = 0; i < kNT; ++i) h[i] = 0.f;
+    for (int i = 0; i < kNT; ++i) h[i] = (hi && wv * kNT + i < p.N) ? hi[wv * kNT + i] : 0.f;
+  }
 
   for (int64_t tb = 0; tb < L; tb += kT) {
     float av[kT], wv_[kT];
@@ -175,6 +179,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
       }
     }
     __syncthreads();
+  }
+  // the state after the last step (steps past L are the identity)
+  if (p.h_final && d0 + lane < p.channels) {
+    float* hf = p.h_final + b * p.hf_sb + (d0 + lane) * p.hf_sd;
+#pragma unroll
+    for (int i = 0; i < kNT; ++i)
+      if (wv * kNT + i < p.N) hf[wv * kNT + i] = h[i];
   }
 }
 
@@ -229,9 +240,13 @@ __global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p
   const TIn* __restrict__ ur = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
   const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
 
+  // this wave's states wv * kHS + i of the lane's channel, from the caller's initial state or zero
   float h[kHS];
+  {
+    const float* hi = p.h_init ? p.h_init + b * p.hi_sb + d * p.hi_sd : nullptr;
 #pragma unroll
-  for (int i = 0; i < kHS; ++i) h[i] = 0.f;
+    for (int i = 0; i < kHS; ++i) h[i] = (hi && wv * kHS + i < p.N) ? hi[wv * kHS + i] : 0.f;
+  }
 
   for (int64_t tb = 0; tb < L; tb += kHT) {
     if (wv == 0 && lane < kHT) {
@@ -330,6 +345,13 @@ __global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p
       TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
       store_seg<kHT>(yr, t0, L, vec, out);
     }
+  }
+  // the state after the last step (steps past L are the identity)
+  if (p.h_final) {
+    float* hf = p.h_final + b * p.hf_sb + d * p.hf_sd;
+#pragma unroll
+    for (int i = 0; i < kHS; ++i)
+      if (wv * kHS + i < p.N) hf[wv * kHS + i] = h[i];
   }
 }
 

@@ -215,6 +215,18 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   f32x4v hacc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  if (sgi == 0 && p.h_init) {
+    // the first segment starts from the caller's state (both passes; later segments receive
+    // it through the first segment's end state)
+    const float* hi = p.h_init + b * p.hi_sb + (c0 + pch) * p.hi_sd;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int n = 16 * k + 4 * g16 + r;
+        if (k < nk && n < p.N) hacc[k][r] = hi[n];
+      }
+  }
   if constexpr (!STATE) {
     // the state entering this segment, from the state pass's results (j = sgi - 1 first, whose
     // end state enters undecayed)
@@ -452,6 +464,18 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     for (int k = 0; k < 8; ++k)
       if (k < nk) hl[k * 64] = hacc[k];
     if (tid == 0) sg.dsum[blk] = dlog;
+  } else {
+    // the last segment ends with the state after the last step (steps past L are the identity)
+    if (p.h_final && sgi == sg.nseg - 1) {
+      float* hf = p.h_final + b * p.hf_sb + (c0 + pch) * p.hf_sd;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * k + 4 * g16 + r;
+          if (k < nk && n < p.N) hf[n] = hacc[k][r];
+        }
+    }
   }
 }
 

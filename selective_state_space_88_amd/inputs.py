@@ -27,6 +27,7 @@ distributions and flags.
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -215,3 +216,29 @@ def random_problem(seed: int, batch: int, channels: int, length: int, nstate: in
                    in_dtype=in_dtype, u=u, delta=delta, A=A, B=B, C=C, D=Dv, z=z,
                    delta_bias=bias, softplus=softplus, scalar_decay=scalar_decay,
                    meta=dict(seed=seed))
+
+
+def random_state(seed: int, batch: int, channels: int, nstate: int, scale: float = 1.0) -> np.ndarray:
+    """A seeded state h [batch, channels, N] float32 ~ N(0, scale^2), for the state entry points."""
+    rng = np.random.default_rng(seed)
+    return (scale * rng.standard_normal((batch, channels, nstate))).astype(np.float32)
+
+
+def time_slice(p: Problem, t0: int, t1: int) -> Problem:
+    """The same problem restricted to steps [t0, t1) (the per-step tensors are sliced along
+    time; A, D and delta_bias are shared)."""
+    def cut(a):
+        return None if a is None else np.ascontiguousarray(a[..., t0:t1])
+
+    return dataclasses.replace(p, length=t1 - t0, u=cut(p.u), delta=cut(p.delta), B=cut(p.B), C=cut(p.C),
+                               z=cut(p.z), meta=dict(p.meta, time_slice=(t0, t1)))
+
+
+def step_slice(p: Problem, t: int) -> Problem:
+    """Step t of the problem as one decoding step: u, z [batch, channels], delta [batch, heads],
+    B, C [batch, groups, N]."""
+    def at(a):
+        return None if a is None else np.ascontiguousarray(a[..., t])
+
+    return dataclasses.replace(p, length=1, u=at(p.u), delta=at(p.delta), B=at(p.B), C=at(p.C), z=at(p.z),
+                               meta=dict(p.meta, step=t))

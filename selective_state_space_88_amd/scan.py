@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libssscan.so")
 SS_F32, SS_BF16 = 0, 1
 SS_DELTA_SOFTPLUS = 1 << 0
 SS_Z_GATE_SILU = 1 << 1
-EXPORTS = ("ss_scan_fwd", "ss_check", "ss_strerror", "ss_version")
+EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_check", "ss_strerror", "ss_version")
 
 
 class SSTensor(ctypes.Structure):
@@ -28,7 +28,7 @@ class SSTensor(ctypes.Structure):
 
 class ScanError(RuntimeError):
     def __init__(self, code: int, msg: str):
-        super().__init__("ss_scan_fwd failed (%d): %s" % (code, msg))
+        super().__init__("selective-scan call failed (%d): %s" % (code, msg))
         self.code = code
 
 
@@ -45,6 +45,10 @@ def lib() -> ctypes.CDLL:
         P = ctypes.POINTER(SSTensor)
         l.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, ctypes.c_void_p]
         l.ss_scan_fwd.restype = ctypes.c_int
+        l.ss_scan_fwd_state.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, ctypes.c_void_p]
+        l.ss_scan_fwd_state.restype = ctypes.c_int
+        l.ss_scan_step.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, ctypes.c_void_p]
+        l.ss_scan_step.restype = ctypes.c_int
         l.ss_check.argtypes = [ctypes.c_void_p]
         l.ss_check.restype = ctypes.c_int
         l.ss_strerror.argtypes = [ctypes.c_int]
@@ -96,27 +100,73 @@ def call(u, delta, A, B, C, D, z, delta_bias, flags: int, y, stream) -> int:
                              ctypes.c_void_p(stream or 0))
 
 
+def call_state(u, delta, A, B, C, D, z, delta_bias, flags: int, h_init, h_final, y, stream) -> int:
+    """Raw ss_scan_fwd_state call with descriptors (or None); returns the library's code."""
+    return lib().ss_scan_fwd_state(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+                                   _ref(delta_bias), ctypes.c_uint32(flags), _ref(h_init), _ref(h_final),
+                                   _ref(y), ctypes.c_void_p(stream or 0))
+
+
+def call_step(u, delta, A, B, C, D, z, delta_bias, flags: int, h, y, stream) -> int:
+    """Raw ss_scan_step call with descriptors (or None); returns the library's code."""
+    return lib().ss_scan_step(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+                              _ref(delta_bias), ctypes.c_uint32(flags), _ref(h), _ref(y),
+                              ctypes.c_void_p(stream or 0))
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be GPU tensors")
+
+
 def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
              C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, *, softplus: bool = True,
              y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
-             stream: Optional[int] = None) -> torch.Tensor:
+             stream: Optional[int] = None, h_init: Optional[torch.Tensor] = None,
+             h_final: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Selective-scan forward on the GPU through ss_scan_fwd (see include/ss_scan.h).
 
     u, z: [batch, channels, L]; delta: [batch, heads, L]; A: [channels, N] (diagonal) or
     [heads] (scalar decay); B, C: [batch, groups, N, L]; D: [channels] or [heads];
     delta_bias: [heads].  Returns y [batch, channels, L] (float32 unless out_dtype/y say so).
+    With h_init and/or h_final ([batch, channels, N] float32) the call goes through
+    ss_scan_fwd_state: the scan starts from h_init and writes its final state to h_final.
     """
-    for t in (u, delta, A, B, C, D, z, delta_bias):
-        if t is not None and not t.is_cuda:
-            raise ValueError("all tensors must be GPU tensors")
+    _check_cuda(u, delta, A, B, C, D, z, delta_bias, h_init, h_final)
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
-    rc = call(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
-              describe(z), describe(delta_bias), flags, describe(y), stream)
+    args = (describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
+            describe(z), describe(delta_bias), flags)
+    if h_init is None and h_final is None:
+        rc = call(*args, describe(y), stream)
+    else:
+        rc = call_state(*args, describe(h_init), describe(h_final), describe(y), stream)
+    if rc != 0:
+        raise ScanError(rc, strerror(rc))
+    return y
+
+
+def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+              C: torch.Tensor, D: Optional[torch.Tensor], z: Optional[torch.Tensor],
+              delta_bias: Optional[torch.Tensor], h: torch.Tensor, *, softplus: bool = True,
+              y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+              stream: Optional[int] = None) -> torch.Tensor:
+    """One decoding step through ss_scan_step: h (float32 [batch, channels, N]) is updated in
+    place and y [batch, channels] returned.  u, z: [batch, channels]; delta: [batch, heads];
+    B, C: [batch, groups, N]; A, D, delta_bias as in scan_fwd."""
+    _check_cuda(u, delta, A, B, C, D, z, delta_bias, h)
+    if y is None:
+        y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    rc = call_step(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
+                   describe(z), describe(delta_bias), flags, describe(h), describe(y), stream)
     if rc != 0:
         raise ScanError(rc, strerror(rc))
     return y

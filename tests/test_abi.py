@@ -196,3 +196,150 @@ def test_empty_problems_are_noops():
     for kw in (dict(L=0), dict(Bt=0), dict(Dc=0, H=1)):
         p = problem(**kw)
         assert call(p) == 0, kw
+
+
+# ---------------------------------------------------------------- ss_scan_fwd_state
+
+
+def state_args(p, h_init=True, h_final=True, N=4, Bt=2, Dc=8):
+    step = 1 << 24
+    hi = T([Bt, Dc, N], scan.SS_F32, FAKE + 9 * step) if h_init else None
+    hf = T([Bt, Dc, N], scan.SS_F32, FAKE + 10 * step) if h_final else None
+    return hi, hf
+
+
+def call_state(p, hi, hf):
+    return scan.call_state(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                           p["flags"], hi, hf, p["y"], None)
+
+
+def test_state_variant_validates_like_the_scan():
+    p = problem()
+    p["u"] = None
+    assert call_state(p, *state_args(problem())) == -1
+    p = problem()
+    p["delta"].dtype = scan.SS_F32
+    assert call_state(p, *state_args(p)) == -2
+    p = problem(N=129)
+    assert call_state(p, *state_args(p, N=129)) == -6
+
+
+def test_state_shape_and_dtype():
+    p = problem()
+    hi, hf = state_args(p)
+    hi.shape[2] = 5
+    assert call_state(p, hi, hf) == -3
+    hi, hf = state_args(p)
+    hf.shape[0] = 3
+    assert call_state(p, hi, hf) == -3
+    hi, hf = state_args(p)
+    hi.dtype = scan.SS_BF16
+    assert call_state(p, hi, hf) == -2
+    hi, hf = state_args(p)
+    hf.stride[2] = 2
+    assert call_state(p, hi, hf) == -4
+
+
+def test_state_alias_rejected():
+    p = problem()
+    hi, hf = state_args(p)
+    hf.data = hi.data + 16          # final state over the initial one
+    assert call_state(p, hi, hf) == -7
+    hi, hf = state_args(p)
+    hf.data = p["u"].data           # over an input
+    assert call_state(p, hi, hf) == -7
+    hi, hf = state_args(p)
+    hf.data = p["y"].data           # over y
+    assert call_state(p, hi, hf) == -7
+    hi, hf = state_args(p)
+    p["y"].data = hi.data           # y over the initial state
+    assert call_state(p, hi, hf) == -7
+
+
+def test_state_variant_empty_batch_is_a_noop():
+    p = problem(Bt=0)
+    assert call_state(p, *state_args(p, Bt=0)) == 0
+    p = problem(L=0)
+    assert call_state(p, *state_args(p, h_final=False)) == 0   # no final state to write
+
+
+# ---------------------------------------------------------------- ss_scan_step
+
+
+def step_problem(Bt=2, Dc=8, N=4, H=None, G=1, scalar=False, dtype=scan.SS_BF16, gate=True):
+    H = Dc if H is None else H
+    step = 1 << 24
+    p = dict(
+        u=T([Bt, Dc], dtype, FAKE),
+        delta=T([Bt, H], dtype, FAKE + step),
+        A=T([H] if scalar else [Dc, N], scan.SS_F32, FAKE + 2 * step),
+        B=T([Bt, G, N], dtype, FAKE + 3 * step),
+        C=T([Bt, G, N], dtype, FAKE + 4 * step),
+        D=T([Dc], scan.SS_F32, FAKE + 5 * step),
+        z=T([Bt, Dc], dtype, FAKE + 6 * step) if gate else None,
+        delta_bias=T([H], scan.SS_F32, FAKE + 7 * step),
+        h=T([Bt, Dc, N], scan.SS_F32, FAKE + 8 * step),
+        y=T([Bt, Dc], scan.SS_F32, FAKE + 9 * step),
+    )
+    p["flags"] = scan.SS_DELTA_SOFTPLUS | (scan.SS_Z_GATE_SILU if gate else 0)
+    return p
+
+
+def call_step(p):
+    return scan.call_step(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                          p["flags"], p["h"], p["y"], None)
+
+
+def test_step_null_and_flags():
+    for k in ("u", "delta", "A", "B", "C", "h", "y"):
+        p = step_problem()
+        p[k] = None
+        assert call_step(p) == -1, k
+    p = step_problem()
+    p["flags"] |= 1 << 7
+    assert call_step(p) == -5
+    p = step_problem(gate=False)
+    p["flags"] |= scan.SS_Z_GATE_SILU
+    assert call_step(p) == -5
+
+
+@pytest.mark.parametrize("what", ["u_ndim", "delta_batch", "B_N", "h_N", "h_channels", "y_channels", "A_cols"])
+def test_step_shape_errors(what):
+    p = step_problem()
+    if what == "u_ndim":
+        p["u"] = T([2, 8, 1])
+    elif what == "delta_batch":
+        p["delta"] = T([3, 8])
+    elif what == "B_N":
+        p["C"] = T([2, 1, 5])
+    elif what == "h_N":
+        p["h"] = T([2, 8, 5], scan.SS_F32)
+    elif what == "h_channels":
+        p["h"] = T([2, 7, 4], scan.SS_F32)
+    elif what == "y_channels":
+        p["y"] = T([2, 9], scan.SS_F32)
+    elif what == "A_cols":
+        p["A"] = T([8, 5], scan.SS_F32)
+    assert call_step(p) == -3
+
+
+def test_step_dtype_stride_alias_and_sizes():
+    p = step_problem()
+    p["h"].dtype = scan.SS_BF16
+    assert call_step(p) == -2
+    p = step_problem()
+    p["B"].dtype = scan.SS_F32
+    assert call_step(p) == -2
+    p = step_problem()
+    p["h"] = T([2, 8, 4], scan.SS_F32, stride=[64, 8, 2])
+    assert call_step(p) == -4
+    p = step_problem()
+    p["h"].data = p["u"].data
+    assert call_step(p) == -7
+    p = step_problem()
+    p["y"].data = p["h"].data + 4
+    assert call_step(p) == -7
+    p = step_problem(N=129)
+    assert call_step(p) == -6
+    p = step_problem(Bt=0)
+    assert call_step(p) == 0
