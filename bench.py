@@ -124,6 +124,73 @@ def algorithmic_bytes(p, y_bytes):
     return n
 
 
+def decode_bench(args, p, to_dev, dev):
+    """One decoding step per call (ss_scan_step) on the workload's shapes: step 0 of its inputs
+    and a seeded state.  The step reads and writes the f32 state (8 N bytes per row) and reads
+    one token of inputs, so its roofline is HBM; at these sizes a call is also close to the
+    launch latency."""
+    import torch
+
+    from selective_state_space_88_amd import inputs
+    from selective_state_space_88_amd.scan import scan_step
+
+    s = inputs.step_slice(p, 0)
+    t = {k: to_dev(getattr(s, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    h = to_dev(inputs.random_state(7, p.batch, p.channels, p.nstate, scale=0.1))
+    y = torch.empty((p.batch, p.channels), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        scan_step(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], h,
+                  softplus=p.softplus, y=y, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    # steps captured in a HIP graph and replayed, as a serving loop runs them (a Python call per
+    # step would time the host, not the GPU); replays are checked against eager steps in the tests
+    G = 50
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for _ in range(G):
+                scan_step(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], h,
+                          softplus=p.softplus, y=y)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    R = max(1, args.steps // G)
+    K = R * G
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(R):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = e0.elapsed_time(e1) * 1e-3 / K
+    rows = p.batch * p.channels
+    ib = 2 if p.in_dtype == "bf16" else 4
+    nbytes = rows * (8 * p.nstate + ib * (2 if p.gate else 1) + 4)       # state r/w, u (z), y
+    nbytes += p.batch * p.heads * ib + 2 * p.batch * p.groups * p.nstate * ib
+    gbps = nbytes / per_call / 1e9
+    out = {
+        "metric": "selective-scan decode step rows/s (batch*channels per second), 1 GPU",
+        "value": rows * K / wall, "unit": "rows/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": wall / K * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode step, " + describe(p), "batch": p.batch, "channels": p.channels,
+                   "nstate": p.nstate, "heads": p.heads, "kernel": "step_kernel"},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "call_us": per_call * 1e6,
+                     "hbm_algorithmic_bytes_per_call": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +199,9 @@ def main():
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decoding step (ss_scan_step: one token for every (batch, channel) "
+                         "row of the workload's shapes, state updated in place) instead of the scan")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (10^6 B) per step, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -159,6 +229,10 @@ def main():
         if a.dtype == np.uint16:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
         return torch.from_numpy(a).to(dev)
+
+    if args.decode:
+        decode_bench(args, p, to_dev, dev)
+        return
 
     t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
     y = torch.empty(p.u.shape, dtype=torch.float32, device=dev)

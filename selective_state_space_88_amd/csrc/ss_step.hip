@@ -9,17 +9,35 @@
 //
 // Mapping: every (batch, channel) row gets G lanes (a power of two, at most 32, so that a row
 // never leaves its wave), each lane four consecutive states; the row's readout is summed over
-// its lanes with xor shuffles.  The state is read and written in place, coalesced along n.
+// its lanes with xor shuffles.  The state is read and written in place, coalesced along n
+// (16-byte accesses per lane when the rows allow).  Blocks are one wave.
 #include "ss_device.h"
 #include "ss_launch.h"
 
 namespace ss {
 namespace {
 
-constexpr int kStepThreads = 256;
+constexpr int kStepThreads = 64;   // one wave per block: small decode problems still spread over the CUs
 constexpr int kStatesPerLane = 4;
 
-template <typename TIn, typename TOut, bool GATE>
+template <typename T>
+struct Quad;
+template <>
+struct Quad<float> {
+  typedef f32x4 type;
+  static __device__ __forceinline__ float get(const type& v, int i) { return v[i]; }
+};
+template <>
+struct Quad<bf16_t> {
+  typedef uint32_t type __attribute__((ext_vector_type(2)));
+  static __device__ __forceinline__ float get(const type& v, int i) {
+    return (i & 1) ? bf16_hi(v[i >> 1]) : bf16_lo(v[i >> 1]);
+  }
+};
+
+// VEC: N a multiple of 4 and the state and B/C rows aligned for 16-byte (state, f32 B/C) or
+// 8-byte (bf16 B/C) accesses: each lane moves its four states with single loads and stores.
+template <typename TIn, typename TOut, bool GATE, bool VEC>
 __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
   const int tid = threadIdx.x;
   const int64_t rows = p.batch * p.channels;
@@ -38,16 +56,40 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
   const TIn* Cr = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
   float* hr = p.h + b * p.h_sb + d * p.h_sd;
   const float* Ar = p.scalar ? p.A + hd : p.A + d * p.A_sd;
+  const int n0 = kStatesPerLane * j;
 
   float acc = 0.f;
+  if constexpr (VEC) {
+    if (live && n0 < p.N) {
+      typedef typename Quad<TIn>::type QT;
+      const f32x4 hv = *reinterpret_cast<const f32x4*>(hr + n0);
+      const QT bv = *reinterpret_cast<const QT*>(Br + n0);
+      const QT cv = *reinterpret_cast<const QT*>(Cr + n0);
+      f32x4 av;
+      if (p.scalar) {
+        av = f32x4{Ar[0], Ar[0], Ar[0], Ar[0]};
+      } else {
+        av = *reinterpret_cast<const f32x4*>(Ar + n0);
+      }
+      f32x4 hn;
 #pragma unroll
-  for (int i = 0; i < kStatesPerLane; ++i) {
-    const int n = kStatesPerLane * j + i;
-    if (live && n < p.N) {
-      const float a = __builtin_amdgcn_exp2f(dt * ((p.scalar ? Ar[0] : Ar[n]) * kLog2e));
-      const float hn = fmaf(a, hr[n], w * to_f32(Br[n]));
-      hr[n] = hn;
-      acc = fmaf(to_f32(Cr[n]), hn, acc);
+      for (int i = 0; i < kStatesPerLane; ++i) {
+        const float a = __builtin_amdgcn_exp2f(dt * (av[i] * kLog2e));
+        hn[i] = fmaf(a, hv[i], w * Quad<TIn>::get(bv, i));
+        acc = fmaf(Quad<TIn>::get(cv, i), hn[i], acc);
+      }
+      *reinterpret_cast<f32x4*>(hr + n0) = hn;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kStatesPerLane; ++i) {
+      const int n = n0 + i;
+      if (live && n < p.N) {
+        const float a = __builtin_amdgcn_exp2f(dt * ((p.scalar ? Ar[0] : Ar[n]) * kLog2e));
+        const float hn = fmaf(a, hr[n], w * to_f32(Br[n]));
+        hr[n] = hn;
+        acc = fmaf(to_f32(Cr[n]), hn, acc);
+      }
     }
   }
   // the row's readout: its G lanes are an aligned group of the wave
@@ -67,8 +109,19 @@ hipError_t launch_t(const StepArgs& a, hipStream_t s) {
   const int64_t rows = a.batch * a.channels;
   const int64_t rpb = kStepThreads / G;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(kStepThreads);
-  if (a.z) hipLaunchKernelGGL((step_kernel<TIn, TOut, true>), grid, block, 0, s, a, G);
-  else hipLaunchKernelGGL((step_kernel<TIn, TOut, false>), grid, block, 0, s, a, G);
+  // 16-byte state rows and f32 A rows, 16- (f32) or 8-byte (bf16) B/C rows
+  const int64_t qb = 4 * (int64_t)sizeof(TIn);
+  auto al = [](const void* ptr, int64_t bytes) { return reinterpret_cast<uintptr_t>(ptr) % bytes == 0; };
+  const bool vec = a.N % 4 == 0 && al(a.h, 16) && a.h_sb % 4 == 0 && a.h_sd % 4 == 0 && al(a.B, qb) &&
+                   al(a.C, qb) && a.B_sb % 4 == 0 && a.B_sg % 4 == 0 && a.C_sb % 4 == 0 && a.C_sg % 4 == 0 &&
+                   (a.scalar || (al(a.A, 16) && a.A_sd % 4 == 0));
+#define SS_STEP(GT, V) hipLaunchKernelGGL((step_kernel<TIn, TOut, GT, V>), grid, block, 0, s, a, G)
+  if (a.z) {
+    if (vec) SS_STEP(true, true); else SS_STEP(true, false);
+  } else {
+    if (vec) SS_STEP(false, true); else SS_STEP(false, false);
+  }
+#undef SS_STEP
   return hipGetLastError();
 }
 

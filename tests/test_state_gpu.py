@@ -159,3 +159,40 @@ def test_step_bf16_output_and_large_state():
     scale = np.max(np.abs(ry))
     assert np.all(np.abs(y - ry) <= 2.0 ** -8 * np.abs(ry) + 2e-3 * scale)
     assert normwise(h, rh) <= TOL[p.in_dtype]
+
+
+def test_steps_in_a_graph_match_eager():
+    """Decoding steps captured in a HIP graph (the way a serving loop runs them) and replayed
+    several times, with eager work and synchronisation between replays: every replay equals the
+    same steps run eagerly from the same state."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_step
+
+    p = inputs.time_slice(CASES["diag bf16 N16"](), 0, 4)
+    steps = [dev_problem(inputs.step_slice(p, t)) for t in range(4)]
+    h0 = to_dev(inputs.random_state(81, p.batch, p.channels, p.nstate))
+    h = h0.clone()
+    ys = [torch.empty((p.batch, p.channels), device="cuda") for _ in steps]
+
+    def run(hh, outs):
+        for s, y in zip(steps, outs):
+            scan_step(s["u"], s["delta"], s["A"], s["B"], s["C"], s["D"], s["z"], s["delta_bias"], hh, y=y)
+
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            run(h, ys)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        h.copy_(h0)
+        g.replay()
+        torch.cuda.synchronize()
+        h_ref = h0.clone()
+        y_ref = [torch.empty_like(y) for y in ys]
+        run(h_ref, y_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(h, h_ref), rep
+        for a, b in zip(ys, y_ref):
+            assert torch.equal(a, b), rep
