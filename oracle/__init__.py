@@ -45,6 +45,10 @@ class _Problem(ctypes.Structure):
     ]
 
 
+class _Grads(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_void_p) for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0")]
+
+
 def build(force: bool = True) -> str:
     """Compile ss_oracle.c into libssoracle.so with gcc (plain -O2, no fast-math)."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
@@ -67,6 +71,9 @@ def _load():
         lib.sso_scan_fwd.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
         lib.sso_scan_fwd.restype = ctypes.c_int
+        lib.sso_scan_bwd.argtypes = [ctypes.POINTER(_Problem), ctypes.c_void_p, ctypes.POINTER(_Grads),
+                                     ctypes.c_int]
+        lib.sso_scan_bwd.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -170,3 +177,62 @@ def scan_problem(p, *, rows=None, h0=None, return_state=False, threads=None):
     """Run the oracle on a Problem from the seeded input generator."""
     return scan_fwd(p.u, p.delta, p.A, p.B, p.C, p.D, p.z, p.delta_bias, softplus=p.softplus,
                     rows=rows, h0=h0, return_state=return_state, threads=threads)
+
+
+def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
+             D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
+             delta_bias: Optional[np.ndarray] = None, *, dy: np.ndarray, softplus: bool = True,
+             h0: Optional[np.ndarray] = None, threads: Optional[int] = None) -> dict:
+    """Float64 gradients of sum(dy * y) for the forward of ``scan_fwd`` (same arguments; dy is
+    [batch, channels, L]).  Returns a dict with du, ddelta, dA, dB, dC and, when the matching
+    input is given, dD, dz, ddelta_bias; dh0 [batch * channels, N] is the gradient of the
+    initial state.  The definition (the chain rule of the recurrence, reverse in time) is in
+    ss_oracle.c."""
+    u = np.ascontiguousarray(u)
+    delta = np.ascontiguousarray(delta)
+    B = np.ascontiguousarray(B)
+    C = np.ascontiguousarray(C)
+    code = _code(u)
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("z", z)):
+        if t is not None and _code(t) != code:
+            raise TypeError("oracle: %s dtype %s differs from u dtype %s" % (name, t.dtype, u.dtype))
+    if z is not None:
+        z = np.ascontiguousarray(z)
+    Bt, Dc, L = u.shape
+    H = delta.shape[1]
+    G, N = B.shape[1], B.shape[2]
+    if delta.shape != (Bt, H, L) or B.shape != (Bt, G, N, L) or C.shape != B.shape:
+        raise ValueError("oracle: inconsistent shapes")
+    dy64 = np.ascontiguousarray(dy, dtype=np.float64)
+    if dy64.shape != (Bt, Dc, L):
+        raise ValueError("oracle: dy must be [batch, channels, L]")
+    A64 = np.ascontiguousarray(A, dtype=np.float64)
+    a_per_head = 1 if A64.ndim == 1 else 0
+    D64 = None if D is None else np.ascontiguousarray(D, dtype=np.float64)
+    d_per_head = 1 if (D64 is not None and D64.shape == (H,) and H != Dc) else 0
+    bias64 = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float64)
+    h0_64 = None if h0 is None else np.ascontiguousarray(h0, dtype=np.float64).reshape(Bt * Dc, N)
+    out = dict(du=np.empty((Bt, Dc, L)), ddelta=np.empty((Bt, H, L)), dA=np.empty(A64.shape),
+               dB=np.empty((Bt, G, N, L)), dC=np.empty((Bt, G, N, L)),
+               dD=None if D64 is None else np.empty(D64.shape),
+               dz=None if z is None else np.empty((Bt, Dc, L)),
+               ddelta_bias=None if bias64 is None else np.empty((H,)), dh0=np.empty((Bt * Dc, N)))
+
+    def ptr(a):
+        return None if a is None else a.ctypes.data
+
+    prob = _Problem(Bt, Dc, L, N, G, H, code, a_per_head, d_per_head, 1 if softplus else 0,
+                    ptr(u), ptr(delta), ptr(B), ptr(C), ptr(z), ptr(A64), ptr(D64), ptr(bias64),
+                    ptr(h0_64))
+    grads = _Grads(ptr(out["du"]), ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]),
+                   ptr(out["dD"]), ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]))
+    rc = _load().sso_scan_bwd(ctypes.byref(prob), ptr(dy64), ctypes.byref(grads), int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError("oracle backward failed (rc=%d)" % rc)
+    return out
+
+
+def scan_bwd_problem(p, dy, *, h0=None, threads=None) -> dict:
+    """``scan_bwd`` on a Problem from the seeded input generator."""
+    return scan_bwd(p.u, p.delta, p.A, p.B, p.C, p.D, p.z, p.delta_bias, dy=dy, softplus=p.softplus,
+                    h0=h0, threads=threads)

@@ -175,3 +175,208 @@ int sso_scan_fwd(const sso_problem* p, const int64_t* rows, int64_t nrows, doubl
   free(jobs);
   return rc;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Backward (reverse-mode gradient) of the same recurrence, in float64.
+ *
+ * Given dy = dLoss/dy, the gradients of every input follow from the forward definition above by
+ * the chain rule, taken step by step in reverse time order (the pages describe training that
+ * recomputes the states instead of storing them -- bqwf.cn survey, section 2.2 -- but name no
+ * formula; this is the plain derivative).  With s(z) = z sigmoid(z) and y0_t the output before
+ * the gate:
+ *
+ *   dy0_t    = dy_t s(z_t)                      dz_t = dy_t y0_t s'(z_t)
+ *   g_{t,n}  = C_{t,n} dy0_t + a_{t+1,n} g_{t+1,n}        (dLoss/dh_{t,n}; g after the end = 0)
+ *   dC_{t,n} += dy0_t h_{t,n}                   dB_{t,n} += g_{t,n} dt_t u_t
+ *   du_t     = dy0_t D + sum_n g_{t,n} dt_t B_{t,n}       dD += dy0_t u_t
+ *   ddt_t    = sum_n g_{t,n} (h_{t-1,n} a_{t,n} A_n + B_{t,n} u_t)
+ *   dA_n    += sum_t g_{t,n} h_{t-1,n} a_{t,n} dt_t
+ *   dx_t     = ddt_t sigmoid(x_t)  (softplus' ; dx_t = ddt_t without softplus)
+ *   ddelta_t += dx_t                            dbias += dx_t
+ *   dh0_n    = a_{0,n} g_{0,n}                  (gradient of the initial state)
+ *
+ * B, C, A (scalar per head), D (per head), delta and delta_bias are shared between rows; their
+ * gradients are sums over the rows that use them.  Each thread sums its rows into a private
+ * buffer; the buffers are added in thread order at the end (deterministic).
+ */
+
+typedef struct {
+  double* du;      /* [batch, channels, L] */
+  double* ddelta;  /* [batch, heads, L] */
+  double* dA;      /* [channels, N] or [heads] */
+  double* dB;      /* [batch, groups, N, L] */
+  double* dC;      /* [batch, groups, N, L] */
+  double* dD;      /* [channels] or [heads], or NULL */
+  double* dz;      /* [batch, channels, L], or NULL */
+  double* dbias;   /* [heads], or NULL */
+  double* dh0;     /* [batch * channels, N], or NULL */
+} sso_grads;
+
+typedef struct {
+  const sso_problem* p;
+  const double* dy;
+  sso_grads out;       /* shared, per-row outputs (du, dz, dh0) */
+  sso_grads part;      /* this thread's sums (ddelta, dA, dB, dC, dD, dbias) */
+  int tid, nthreads;
+  int status;
+} bjob_t;
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static void bwd_row(const sso_problem* p, const double* dy, int64_t row, double* hs, double* gcur,
+                    const sso_grads* out, const sso_grads* part) {
+  const int64_t L = p->length, N = p->nstate, Dc = p->channels;
+  const int64_t b = row / Dc, d = row % Dc;
+  const int64_t hd = d / (Dc / p->heads);
+  const int64_t g = d / (Dc / p->groups);
+  const int64_t urow = (b * Dc + d) * L;
+  const int64_t drow = (b * p->heads + hd) * L;
+  const int64_t bcrow = (b * p->groups + g) * N * L;
+  const double bias = p->delta_bias ? p->delta_bias[hd] : 0.0;
+  const double dskip = p->D ? p->D[p->d_per_head ? hd : d] : 0.0;
+  /* forward, keeping every state: hs[t + 1][n] = h_{t,n}, hs[0] = initial state */
+  for (int64_t n = 0; n < N; ++n) hs[n] = p->h0 ? p->h0[row * N + n] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    const double x = load(p->delta, p->in_dtype, drow + t) + bias;
+    const double dt = p->softplus ? softplus(x) : x;
+    const double ut = load(p->u, p->in_dtype, urow + t);
+    for (int64_t n = 0; n < N; ++n) {
+      const double an = p->a_per_head ? p->A[hd] : p->A[d * N + n];
+      const double bn = load(p->B, p->in_dtype, bcrow + n * L + t);
+      hs[(t + 1) * N + n] = exp(dt * an) * hs[t * N + n] + dt * bn * ut;
+    }
+  }
+  /* reverse: gcur[n] holds a_{t+1,n} g_{t+1,n} entering step t */
+  for (int64_t n = 0; n < N; ++n) gcur[n] = 0.0;
+  for (int64_t t = L - 1; t >= 0; --t) {
+    const double x = load(p->delta, p->in_dtype, drow + t) + bias;
+    const double dt = p->softplus ? softplus(x) : x;
+    const double ut = load(p->u, p->in_dtype, urow + t);
+    double y0 = dskip * ut;
+    for (int64_t n = 0; n < N; ++n) y0 += load(p->C, p->in_dtype, bcrow + n * L + t) * hs[(t + 1) * N + n];
+    double dy0 = dy[row * L + t];
+    if (p->z) {
+      const double zt = load(p->z, p->in_dtype, urow + t);
+      const double sg = sigmoid(zt);
+      if (out->dz) out->dz[row * L + t] = dy0 * y0 * sg * (1.0 + zt * (1.0 - sg));
+      dy0 *= zt * sg;
+    }
+    double du = dy0 * dskip, ddt = 0.0;
+    if (part->dD) part->dD[p->d_per_head ? hd : d] += dy0 * ut;
+    for (int64_t n = 0; n < N; ++n) {
+      const double an = p->a_per_head ? p->A[hd] : p->A[d * N + n];
+      const double a = exp(dt * an);
+      const double bn = load(p->B, p->in_dtype, bcrow + n * L + t);
+      const double cn = load(p->C, p->in_dtype, bcrow + n * L + t);
+      const double gn = cn * dy0 + gcur[n];
+      const double hprev = hs[t * N + n];
+      part->dC[bcrow + n * L + t] += dy0 * hs[(t + 1) * N + n];
+      part->dB[bcrow + n * L + t] += gn * dt * ut;
+      du += gn * dt * bn;
+      ddt += gn * (hprev * a * an + bn * ut);
+      part->dA[p->a_per_head ? hd : d * N + n] += gn * hprev * a * dt;
+      gcur[n] = a * gn;
+    }
+    out->du[row * L + t] = du;
+    const double dx = p->softplus ? ddt * sigmoid(x) : ddt;
+    part->ddelta[drow + t] += dx;
+    if (part->dbias) part->dbias[hd] += dx;
+  }
+  if (out->dh0)
+    for (int64_t n = 0; n < N; ++n) out->dh0[row * N + n] = gcur[n];
+}
+
+static int64_t grad_sizes(const sso_problem* p, int64_t* n_delta, int64_t* n_A, int64_t* n_BC, int64_t* n_D) {
+  *n_delta = p->batch * p->heads * p->length;
+  *n_A = p->a_per_head ? p->heads : p->channels * p->nstate;
+  *n_BC = p->batch * p->groups * p->nstate * p->length;
+  *n_D = p->d_per_head ? p->heads : p->channels;
+  return *n_delta + *n_A + 2 * *n_BC + *n_D + p->heads;
+}
+
+static void* bworker(void* arg) {
+  bjob_t* j = (bjob_t*)arg;
+  const sso_problem* p = j->p;
+  const int64_t N = p->nstate, L = p->length;
+  double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * (N > 0 ? N : 1)));
+  double* gcur = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+  if (!hs || !gcur) {
+    free(hs);
+    free(gcur);
+    j->status = -1;
+    return NULL;
+  }
+  const int64_t total = p->batch * p->channels;
+  for (int64_t row = j->tid; row < total; row += j->nthreads) bwd_row(p, j->dy, row, hs, gcur, &j->out, &j->part);
+  free(hs);
+  free(gcur);
+  j->status = 0;
+  return NULL;
+}
+
+/* Gradients of sum(dy * y) with respect to every input, for all rows.  dy: [batch, channels, L]
+ * float64.  Outputs (float64, overwritten): du, ddelta, dA, dB, dC required; dD, dz, dbias, dh0
+ * optional (NULL: not computed).  Returns 0, or -1 on a bad argument or allocation failure. */
+int sso_scan_bwd(const sso_problem* p, const double* dy, sso_grads* g, int nthreads) {
+  if (!p || !dy || !g || !g->du || !g->ddelta || !g->dA || !g->dB || !g->dC) return -1;
+  if (!p->u || !p->delta || !p->A || !p->B || !p->C) return -1;
+  if (p->channels <= 0 || p->heads <= 0 || p->groups <= 0 || p->channels % p->heads ||
+      p->channels % p->groups || p->nstate < 0 || p->length < 0 || p->batch < 0)
+    return -1;
+  int64_t n_delta, n_A, n_BC, n_D;
+  const int64_t nsum = grad_sizes(p, &n_delta, &n_A, &n_BC, &n_D);
+  const int64_t total = p->batch * p->channels;
+  memset(g->du, 0, sizeof(double) * (size_t)(total * p->length));
+  memset(g->ddelta, 0, sizeof(double) * (size_t)n_delta);
+  memset(g->dA, 0, sizeof(double) * (size_t)n_A);
+  memset(g->dB, 0, sizeof(double) * (size_t)n_BC);
+  memset(g->dC, 0, sizeof(double) * (size_t)n_BC);
+  if (g->dD) memset(g->dD, 0, sizeof(double) * (size_t)n_D);
+  if (g->dz) memset(g->dz, 0, sizeof(double) * (size_t)(total * p->length));
+  if (g->dbias) memset(g->dbias, 0, sizeof(double) * (size_t)p->heads);
+  if (g->dh0) memset(g->dh0, 0, sizeof(double) * (size_t)(total * p->nstate));
+  if (total == 0 || p->length == 0) return 0;  /* no steps: every gradient is zero */
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > total) nthreads = (int)total;
+  pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  bjob_t* jobs = (bjob_t*)calloc((size_t)nthreads, sizeof(bjob_t));
+  double* sums = (double*)calloc((size_t)(nthreads * nsum), sizeof(double));
+  if (!th || !jobs || !sums) {
+    free(th);
+    free(jobs);
+    free(sums);
+    return -1;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    double* s = sums + (int64_t)i * nsum;
+    sso_grads part = {NULL, s, s + n_delta, s + n_delta + n_A, s + n_delta + n_A + n_BC,
+                      s + n_delta + n_A + 2 * n_BC, NULL, s + n_delta + n_A + 2 * n_BC + n_D, NULL};
+    if (!g->dD) part.dD = NULL;
+    if (!g->dbias) part.dbias = NULL;
+    jobs[i] = (bjob_t){p, dy, *g, part, i, nthreads, -1};
+    if (pthread_create(&th[i], NULL, bworker, &jobs[i]) != 0) {
+      bworker(&jobs[i]);
+      th[i] = 0;
+    }
+  }
+  int rc = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    if (th[i]) pthread_join(th[i], NULL);
+    if (jobs[i].status != 0) rc = -1;
+  }
+  for (int i = 0; i < nthreads && rc == 0; ++i) {
+    const sso_grads* s = &jobs[i].part;
+    for (int64_t k = 0; k < n_delta; ++k) g->ddelta[k] += s->ddelta[k];
+    for (int64_t k = 0; k < n_A; ++k) g->dA[k] += s->dA[k];
+    for (int64_t k = 0; k < n_BC; ++k) g->dB[k] += s->dB[k];
+    for (int64_t k = 0; k < n_BC; ++k) g->dC[k] += s->dC[k];
+    if (g->dD)
+      for (int64_t k = 0; k < n_D; ++k) g->dD[k] += s->dD[k];
+    if (g->dbias)
+      for (int64_t k = 0; k < p->heads; ++k) g->dbias[k] += s->dbias[k];
+  }
+  free(th);
+  free(jobs);
+  free(sums);
+  return rc;
+}
