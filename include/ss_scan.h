@@ -36,7 +36,8 @@
  *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL = the default
  *    stream).  Kernel execution errors surface at stream synchronisation or via ss_check().
  *  - Calls on different streams may run concurrently; the library keeps no per-call global state.
- *  - Results are deterministic: the same inputs give bitwise the same y on every run.
+ *  - Results are deterministic: the same inputs give bitwise the same y on every run (the
+ *    backward's sums over channels and batch are the exception; see ss_scan_bwd).
  */
 #ifndef SS_SCAN_H
 #define SS_SCAN_H
@@ -152,6 +153,42 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
 int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                  const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                  const ss_tensor* delta_bias, uint32_t flags, ss_tensor* h, ss_tensor* y, void* stream);
+
+/*
+ * ss_scan_bwd -- backward of ss_scan_fwd: the gradients of sum(dy * y) with respect to every
+ * input, for training.  The pages train the scan by recomputing its states rather than storing
+ * them (bqwf.cn state-space survey, section 2.2); so does this call: it stores only the state at
+ * the start of every window of 512 steps (a stream-ordered workspace of batch * channels *
+ * ceil(L / 512) * N floats) and recomputes the rest.  Chain rule, with s(z) = z sigmoid(z) and
+ * dy0 = dy s(z):  g_t = C_t dy0_t + exp(dt_{t+1} A) g_{t+1} (the gradient of h_t),
+ * dC_t = dy0_t h_t,  dB_t = g_t dt_t u_t,  du_t = dy0_t D + sum_n g_t dt_t B_t,
+ * ddt_t = sum_n g_t (h_{t-1} exp(dt_t A) A + B_t u_t),  dA = sum_t g_t h_{t-1} exp(dt_t A) dt_t,
+ * ddelta_t = ddt_t sigmoid(delta_t + bias) with softplus (ddt_t without),  dbias = sum ddelta,
+ * dD = sum dy0_t u_t,  dz_t = dy_t y0_t s'(z_t)  (y0: the output before the gate).
+ *
+ *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd, restricted to the diagonal
+ *              decay with one step size per channel: A [channels, N], delta [batch, channels, L]
+ *              (anything else: SS_ERR_UNSUPPORTED), and channels / groups a multiple of 4
+ *   dy         [batch, channels, L]          f32 | bf16: the gradient of the loss at y
+ *   du         [batch, channels, L] f32      written
+ *   ddelta     [batch, channels, L] f32      written (the gradient of the raw delta)
+ *   dA         [channels, N] f32             written
+ *   dB, dC     [batch, groups, N, L] f32     written (summed over each group's channels)
+ *   dD         [channels] f32                written; required exactly when D is given
+ *   dz         [batch, channels, L] f32      written; required exactly with SS_Z_GATE_SILU
+ *   ddelta_bias [channels] f32               optional: written when given
+ *
+ * Every gradient is f32 with innermost stride 1 and must not overlap an input or another
+ * gradient (SS_ERR_ALIAS).  The state starts at zero.  Sums over channels and over the batch
+ * (dA, dB, dC, dD, dbias) are accumulated with atomic adds, so their last bits may differ from
+ * run to run; everything else is deterministic.  Errors, ownership and asynchrony as in
+ * ss_scan_fwd.
+ */
+int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
+                uint32_t flags, const ss_tensor* dy, ss_tensor* du, ss_tensor* ddelta, ss_tensor* dA,
+                ss_tensor* dB, ss_tensor* dC, ss_tensor* dD, ss_tensor* dz, ss_tensor* ddelta_bias,
+                void* stream);
 
 /* Synchronises `stream` and returns SS_OK, or SS_ERR_HIP if any enqueued work failed. */
 int ss_check(void* stream);

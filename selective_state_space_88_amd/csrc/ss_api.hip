@@ -340,4 +340,156 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
   return ss::launch_step(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
+// output gradient tensor: f32, the given shape, innermost stride 1
+static int check_grad(const ss_tensor* t, int ndim, const int64_t* shape) {
+  int rc;
+  if ((rc = check_basic(t, ndim))) return rc;
+  if (t->dtype != SS_F32) return SS_ERR_DTYPE;
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] != shape[i]) return SS_ERR_SHAPE;
+  return SS_OK;
+}
+
+int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
+                uint32_t flags, const ss_tensor* dy, ss_tensor* du, ss_tensor* ddelta, ss_tensor* dA,
+                ss_tensor* dB, ss_tensor* dC, ss_tensor* dD, ss_tensor* dz, ss_tensor* ddelta_bias,
+                void* stream) {
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SS_ERR_NULL;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU)) return SS_ERR_FLAGS;
+  const bool gate = (flags & SS_Z_GATE_SILU) != 0;
+  if (gate != given(z)) return SS_ERR_FLAGS;
+  int rc;
+  if ((rc = check_basic(u, 3)) || (rc = check_basic(delta, 3)) || (rc = check_basic(B, 4)) ||
+      (rc = check_basic(C, 4)) || (rc = check_basic(dy, 3)))
+    return rc;
+  if ((rc = check_basic(A, A->ndim == 2 ? 2 : 1))) return rc;
+  if (gate && (rc = check_basic(z, 3))) return rc;
+  if (present(D) && (rc = check_basic(D, 1))) return rc;
+  if (present(delta_bias) && (rc = check_basic(delta_bias, 1))) return rc;
+  const int32_t idt = u->dtype;
+  if (delta->dtype != idt || B->dtype != idt || C->dtype != idt || (gate && z->dtype != idt)) return SS_ERR_DTYPE;
+  if (A->dtype != SS_F32 || (present(D) && D->dtype != SS_F32) ||
+      (present(delta_bias) && delta_bias->dtype != SS_F32))
+    return SS_ERR_DTYPE;
+  const int64_t Bt = u->shape[0], Dc = u->shape[1], L = u->shape[2];
+  const int64_t H = delta->shape[1], G = B->shape[1], N = B->shape[2];
+  if (delta->shape[0] != Bt || delta->shape[2] != L || B->shape[0] != Bt || B->shape[3] != L) return SS_ERR_SHAPE;
+  for (int i = 0; i < 4; ++i)
+    if (C->shape[i] != B->shape[i]) return SS_ERR_SHAPE;
+  for (int i = 0; i < 3; ++i)
+    if (dy->shape[i] != u->shape[i] || (gate && z->shape[i] != u->shape[i])) return SS_ERR_SHAPE;
+  if (G <= 0 || (Dc > 0 && Dc % G)) return SS_ERR_SHAPE;
+  // the backward covers the diagonal decay with one step size per channel (Mamba-1 layout)
+  if (A->ndim != 2 || H != Dc) return SS_ERR_UNSUPPORTED;
+  if (A->shape[0] != Dc || A->shape[1] != N) return SS_ERR_SHAPE;
+  if (present(D) && D->shape[0] != Dc) return SS_ERR_SHAPE;
+  if (present(delta_bias) && delta_bias->shape[0] != Dc) return SS_ERR_SHAPE;
+  if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
+  if (L > ((int64_t)1 << 31)) return SS_ERR_UNSUPPORTED;
+  if (Dc > 0 && (Dc / G) % 4) return SS_ERR_UNSUPPORTED;
+  if (dy->dtype != SS_F32 && dy->dtype != SS_BF16) return SS_ERR_DTYPE;
+  const int64_t s_x[3] = {Bt, Dc, L}, s_bc[4] = {Bt, G, N, L}, s_a[2] = {Dc, N}, s_d[1] = {Dc};
+  if ((rc = check_grad(du, 3, s_x)) || (rc = check_grad(ddelta, 3, s_x)) || (rc = check_grad(dA, 2, s_a)) ||
+      (rc = check_grad(dB, 4, s_bc)) || (rc = check_grad(dC, 4, s_bc)))
+    return rc;
+  if (present(D) != given(dD)) return SS_ERR_NULL;   // dD exactly when D is given
+  if (gate != given(dz)) return SS_ERR_NULL;         // dz exactly when the gate is on
+  if (given(dD) && (rc = check_grad(dD, 1, s_d))) return rc;
+  if (given(dz) && (rc = check_grad(dz, 3, s_x))) return rc;
+  if (given(ddelta_bias) && (rc = check_grad(ddelta_bias, 1, s_d))) return rc;
+  // outputs overlap neither the inputs nor each other
+  const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias, dy};
+  ss_tensor* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias};
+  for (ss_tensor* o : outs) {
+    for (const ss_tensor* t : ins)
+      if (overlaps(o, t)) return SS_ERR_ALIAS;
+    for (ss_tensor* o2 : outs)
+      if (o2 != o && overlaps(o, o2)) return SS_ERR_ALIAS;
+  }
+  if (Bt * Dc == 0) return SS_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0) {
+    // no steps: the gradients of A, B, C, D and the bias are zero; du, ddelta, dz are empty
+    float* zs[] = {static_cast<float*>(dA->data), present(D) ? static_cast<float*>(dD->data) : nullptr,
+                   present(ddelta_bias) ? static_cast<float*>(ddelta_bias->data) : nullptr};
+    const int64_t rws[] = {Dc, 1, 1}, inn[] = {N, Dc, Dc}, st[] = {dA->stride[0], 0, 0};
+    for (int i = 0; i < 3; ++i)
+      if (zs[i] && ss::launch_state_copy(nullptr, 0, 0, zs[i], 0, st[i], 1, rws[i], inn[i], s) != hipSuccess)
+        return SS_ERR_HIP;
+    return SS_OK;
+  }
+  if (!u->data || !delta->data || !A->data || !B->data || !C->data || !dy->data) return SS_ERR_NULL;
+  if (present(D) && D->stride[0] != 1 && D->shape[0] > 1) return SS_ERR_STRIDE;
+  if (present(delta_bias) && delta_bias->stride[0] != 1 && delta_bias->shape[0] > 1) return SS_ERR_STRIDE;
+  if (given(dD) && dD->stride[0] != 1 && Dc > 1) return SS_ERR_STRIDE;
+  if (given(ddelta_bias) && ddelta_bias->stride[0] != 1 && Dc > 1) return SS_ERR_STRIDE;
+
+  ss::BwdArgs a{};
+  a.u = u->data;
+  a.delta = delta->data;
+  a.B = B->data;
+  a.C = C->data;
+  a.z = gate ? z->data : nullptr;
+  a.A = static_cast<const float*>(A->data);
+  a.D = present(D) ? static_cast<const float*>(D->data) : nullptr;
+  a.bias = present(delta_bias) ? static_cast<const float*>(delta_bias->data) : nullptr;
+  a.dy = dy->data;
+  a.du = static_cast<float*>(du->data);
+  a.ddelta = static_cast<float*>(ddelta->data);
+  a.dA = static_cast<float*>(dA->data);
+  a.dB = static_cast<float*>(dB->data);
+  a.dC = static_cast<float*>(dC->data);
+  a.dD = given(dD) ? static_cast<float*>(dD->data) : nullptr;
+  a.dz = gate ? static_cast<float*>(dz->data) : nullptr;
+  a.dbias = given(ddelta_bias) ? static_cast<float*>(ddelta_bias->data) : nullptr;
+  a.batch = Bt;
+  a.channels = Dc;
+  a.L = L;
+  a.N = (int32_t)N;
+  a.groups = (int32_t)G;
+  a.chan_per_group = (int32_t)(Dc / G);
+  a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
+  a.in_bf16 = idt == SS_BF16;
+  a.dy_bf16 = dy->dtype == SS_BF16;
+  a.u_sb = u->stride[0];
+  a.u_sd = u->stride[1];
+  a.dl_sb = delta->stride[0];
+  a.dl_sh = delta->stride[1];
+  a.z_sb = gate ? z->stride[0] : 0;
+  a.z_sd = gate ? z->stride[1] : 0;
+  a.B_sb = B->stride[0];
+  a.B_sg = B->stride[1];
+  a.B_sn = B->stride[2];
+  a.C_sb = C->stride[0];
+  a.C_sg = C->stride[1];
+  a.C_sn = C->stride[2];
+  a.A_sd = A->stride[0];
+  a.dy_sb = dy->stride[0];
+  a.dy_sd = dy->stride[1];
+  a.du_sb = du->stride[0];
+  a.du_sd = du->stride[1];
+  a.dd_sb = ddelta->stride[0];
+  a.dd_sh = ddelta->stride[1];
+  a.dA_sd = dA->stride[0];
+  a.dB_sb = dB->stride[0];
+  a.dB_sg = dB->stride[1];
+  a.dB_sn = dB->stride[2];
+  a.dC_sb = dC->stride[0];
+  a.dC_sg = dC->stride[1];
+  a.dC_sn = dC->stride[2];
+  a.dz_sb = gate ? dz->stride[0] : 0;
+  a.dz_sd = gate ? dz->stride[1] : 0;
+
+  void* ws = nullptr;
+  const int64_t wsb = ss::bwd_workspace_floats(a) * (int64_t)sizeof(float);
+  if (hipMallocAsync(&ws, (size_t)wsb, s) != hipSuccess) {
+    (void)hipGetLastError();
+    return SS_ERR_HIP;
+  }
+  const hipError_t e = ss::launch_bwd(a, static_cast<float*>(ws), s);
+  const hipError_t f = hipFreeAsync(ws, s);
+  return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
+}
+
 }  // extern "C"

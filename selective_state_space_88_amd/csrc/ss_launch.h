@@ -58,6 +58,32 @@ struct StepArgs {
 // One step of the recurrence for every (batch, channel): h = exp(dt A) h + dt B u, y = C h + D u.
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
+// Arguments of the backward of a diagonal-decay scan (delta per channel), already validated.
+// Inputs as in ScanArgs; dy [batch, channels, L]; every gradient f32, innermost stride 1.
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const void* B;
+  const void* C;
+  const void* z;          // nullptr: no gate
+  const float* A;         // [channels, N]
+  const float* D;         // nullable
+  const float* bias;      // nullable, [channels]
+  const void* dy;
+  float *du, *ddelta, *dA, *dB, *dC;
+  float *dD, *dz, *dbias; // nullable (absent input)
+  int64_t batch, channels, L;
+  int32_t N, groups, chan_per_group;
+  int32_t softplus, in_bf16, dy_bf16;
+  int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, A_sd, dy_sb, dy_sd;
+  int64_t du_sb, du_sd, dd_sb, dd_sh, dA_sd, dB_sb, dB_sg, dB_sn, dC_sb, dC_sg, dC_sn, dz_sb, dz_sd;
+};
+
+// Gradients of sum(dy * y).  `ws` must hold bwd_workspace_floats(a) floats (the states at the
+// start of every window), ordered on `stream`.
+int64_t bwd_workspace_floats(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t stream);
+
 // dst[b, d, n] = src[b, d, n] (src == nullptr: 0) for a [batch, channels, N] f32 state.
 hipError_t launch_state_copy(const float* src, int64_t s_sb, int64_t s_sd, float* dst, int64_t d_sb,
                              int64_t d_sd, int64_t batch, int64_t channels, int64_t N, hipStream_t stream);

@@ -242,3 +242,8 @@ def step_slice(p: Problem, t: int) -> Problem:
 
     return dataclasses.replace(p, length=1, u=at(p.u), delta=at(p.delta), B=at(p.B), C=at(p.C), z=at(p.z),
                                meta=dict(p.meta, step=t))
+
+
+def seeded_normal(seed: int, shape, scale: float = 1.0) -> np.ndarray:
+    """float32 ~ N(0, scale^2) of the given shape (e.g. the upstream gradient dy of a backward)."""
+    return (scale * np.random.default_rng(seed).standard_normal(shape)).astype(np.float32)

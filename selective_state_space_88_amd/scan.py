@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libssscan.so")
 SS_F32, SS_BF16 = 0, 1
 SS_DELTA_SOFTPLUS = 1 << 0
 SS_Z_GATE_SILU = 1 << 1
-EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_check", "ss_strerror", "ss_version")
+EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_check", "ss_strerror",
+           "ss_version")
 
 
 class SSTensor(ctypes.Structure):
@@ -49,6 +50,9 @@ def lib() -> ctypes.CDLL:
         l.ss_scan_fwd_state.restype = ctypes.c_int
         l.ss_scan_step.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, ctypes.c_void_p]
         l.ss_scan_step.restype = ctypes.c_int
+        l.ss_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, P, P, P, P, P, P,
+                                  ctypes.c_void_p]
+        l.ss_scan_bwd.restype = ctypes.c_int
         l.ss_check.argtypes = [ctypes.c_void_p]
         l.ss_check.restype = ctypes.c_int
         l.ss_strerror.argtypes = [ctypes.c_int]
@@ -170,3 +174,32 @@ def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if rc != 0:
         raise ScanError(rc, strerror(rc))
     return y
+
+
+def call_bwd(u, delta, A, B, C, D, z, delta_bias, flags: int, dy, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias,
+             stream) -> int:
+    """Raw ss_scan_bwd call with descriptors (or None); returns the library's code."""
+    return lib().ss_scan_bwd(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z), _ref(delta_bias),
+                             ctypes.c_uint32(flags), _ref(dy), _ref(du), _ref(ddelta), _ref(dA), _ref(dB), _ref(dC),
+                             _ref(dD), _ref(dz), _ref(ddelta_bias), ctypes.c_void_p(stream or 0))
+
+
+def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: Optional[torch.Tensor], z: Optional[torch.Tensor], delta_bias: Optional[torch.Tensor],
+             dy: torch.Tensor, *, softplus: bool = True, stream: Optional[int] = None) -> dict:
+    """Gradients of sum(dy * y) through ss_scan_bwd (diagonal decay, delta per channel).  Returns
+    a dict of float32 tensors du, ddelta, dA, dB, dC and, when the input is given, dD, dz,
+    ddelta_bias."""
+    _check_cuda(u, delta, A, B, C, D, z, delta_bias, dy)
+    f = lambda t: torch.empty(t.shape, dtype=torch.float32, device=u.device)
+    g = dict(du=f(u), ddelta=f(delta), dA=f(A), dB=f(B), dC=f(C), dD=None if D is None else f(D),
+             dz=None if z is None else f(z), ddelta_bias=None if delta_bias is None else f(delta_bias))
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    rc = call_bwd(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D), describe(z),
+                  describe(delta_bias), flags, describe(dy), *(describe(g[k]) for k in
+                  ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias")), stream)
+    if rc != 0:
+        raise ScanError(rc, strerror(rc))
+    return g
