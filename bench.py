@@ -191,6 +191,74 @@ def decode_bench(args, p, to_dev, dev):
     print(json.dumps(out))
 
 
+# Backward ALU work per (t, n), FLOP-equivalents as in the forward: the recomputed decay exp (8)
+# and dt*A (1), dt*u*B (1), the recomputed state FMA (2), the adjoint FMA (2) and its decay
+# product (1), dC (1), dB (1), du (2), ddt (4: two FMAs), dA (2: multiply, FMA) = 25; per
+# element the forward's per-step terms (softplus, gate, D) and their derivatives (~2x).
+def bwd_flop_equiv_per_element(N, softplus, gate):
+    per = 25.0 * N + 2 * 3.0
+    if softplus:
+        per += 2 * (2 * TRANS + 4.0)
+    if gate:
+        per += 2 * (2 * TRANS + 3.0)
+    return per
+
+
+def backward_bench(args, p, to_dev, dev):
+    """ss_scan_bwd on the workload with a seeded upstream gradient dy (f32): the checkpoint pass,
+    the zeroing of the summed gradients and the backward kernel, all inside the timed call."""
+    import torch
+
+    from selective_state_space_88_amd import inputs
+    from selective_state_space_88_amd.scan import scan_bwd
+
+    if p.scalar_decay:
+        print("the backward covers the diagonal workloads (0-3)", file=sys.stderr)
+        sys.exit(2)
+    t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
+    dy = to_dev(inputs.seeded_normal(12, (p.batch, p.channels, p.length)))
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        return scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], dy,
+                        softplus=p.softplus, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])) * 1e-3
+    E = p.batch * p.channels * p.length
+    flops = E * bwd_flop_equiv_per_element(p.nstate, p.softplus, p.gate)
+    ib = 2 if p.in_dtype == "bf16" else 4
+    # reads u, delta, z, dy (f32), B, C; writes du, ddelta, dz (f32) and dB, dC (f32)
+    nbytes = E * (ib * (3 if p.gate else 2) + 4 + 4 * (3 if p.gate else 2))
+    nbytes += p.batch * p.groups * p.nstate * p.length * 2 * (ib + 4)
+    tf = flops / per / 1e12
+    out = {
+        "metric": "selective-scan bwd elems/s (B*D*L/s), 1 GPU", "value": E * K / wall, "unit": "elems/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "backward, " + describe(p), "batch": p.batch, "channels": p.channels,
+                   "seq_len": p.length, "nstate": p.nstate, "kernel": "bwd_kernel"},
+        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": None, "call_ms": per * 1e3,
+                     "flop_equiv_per_call": flops, "hbm_algorithmic_bytes_per_call": nbytes,
+                     "hbm_achieved_GBps": nbytes / per / 1e9},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +270,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time the decoding step (ss_scan_step: one token for every (batch, channel) "
                          "row of the workload's shapes, state updated in place) instead of the scan")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
+                         "gradient dy) on the workload instead of the forward (diagonal workloads)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (10^6 B) per step, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -232,6 +303,9 @@ def main():
 
     if args.decode:
         decode_bench(args, p, to_dev, dev)
+        return
+    if args.backward:
+        backward_bench(args, p, to_dev, dev)
         return
 
     t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}

@@ -134,7 +134,8 @@ template <typename TIn, typename TDy, bool GATE>
 __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int64_t nwin, const float* ckpt) {
   __shared__ float gcar[kBWaves][kBMaxPairs][2];      // adjoint carried into the window from the right
   __shared__ float dAl[kBWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
-  __shared__ float red[kBWaves][4][kBK][64];          // dB (2 states), dC (2 states) per step
+  // dB (2 states), dC (2 states) of the window's steps, step-major ([lane][k] = step lane K + k)
+  __shared__ __attribute__((aligned(16))) float red[kBWaves][4][kBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t quads = p.chan_per_group / kBWaves;
@@ -261,21 +262,22 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         const float v = wave_sum(dAp[s]);
         if (lane == 0 && 2 * pp + s < N) dAl[wave][2 * pp + s] += v;
       }
-      // dB, dC of the pair: summed over the block's 4 channels, then one atomic add per step
+      // dB, dC of the pair: summed over the block's 4 channels, then one atomic add per step;
+      // consecutive lanes add to consecutive steps, so each wave's adds cover two cache lines
 #pragma unroll
-      for (int k = 0; k < kBK; ++k) {
-        red[wave][0][k][lane] = rB[0][k];
-        red[wave][1][k][lane] = rB[1][k];
-        red[wave][2][k][lane] = rC[0][k];
-        red[wave][3][k][lane] = rC[1][k];
+      for (int k = 0; k < kBK; k += 4) {
+        *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{rB[0][k], rB[0][k + 1], rB[0][k + 2], rB[0][k + 3]};
+        *reinterpret_cast<f32x4*>(&red[wave][1][lane * kBK + k]) = f32x4{rB[1][k], rB[1][k + 1], rB[1][k + 2], rB[1][k + 3]};
+        *reinterpret_cast<f32x4*>(&red[wave][2][lane * kBK + k]) = f32x4{rC[0][k], rC[0][k + 1], rC[0][k + 2], rC[0][k + 3]};
+        *reinterpret_cast<f32x4*>(&red[wave][3][lane * kBK + k]) = f32x4{rC[1][k], rC[1][k + 1], rC[1][k + 2], rC[1][k + 3]};
       }
       __syncthreads();
-      for (int i = threadIdx.x; i < 4 * kBK * 64; i += 64 * kBWaves) {
-        const int which = i / (kBK * 64), k = (i / 64) % kBK, l = i % 64;
+      for (int i = threadIdx.x; i < 4 * kBW; i += 64 * kBWaves) {
+        const int which = i / kBW, r = i % kBW;
         const int n = 2 * pp + (which & 1);
-        const int64_t t = w * kBW + (int64_t)l * kBK + k;
+        const int64_t t = w * kBW + r;
         if (n < N && t < L) {
-          const float v = red[0][which][k][l] + red[1][which][k][l] + red[2][which][k][l] + red[3][which][k][l];
+          const float v = red[0][which][r] + red[1][which][r] + red[2][which][r] + red[3][which][r];
           float* dst = (which < 2 ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
           atomicAdd(dst, v);
         }
