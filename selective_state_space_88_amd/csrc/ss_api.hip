@@ -452,6 +452,8 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
   a.in_bf16 = idt == SS_BF16;
   a.dy_bf16 = dy->dtype == SS_BF16;
+  a.vec = aligned16(u) && aligned16(delta) && aligned16(B) && aligned16(C) && aligned16(dy) &&
+          (!gate || aligned16(z));
   a.u_sb = u->stride[0];
   a.u_sd = u->stride[1];
   a.dl_sb = delta->stride[0];

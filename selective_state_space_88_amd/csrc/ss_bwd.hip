@@ -32,41 +32,67 @@ constexpr int kBW = 64 * kBK;        // steps per window
 constexpr int kBWaves = 4;           // channels per block
 constexpr int kBMaxPairs = 64;       // N <= 128
 
-// Inclusive scan of affine maps x -> A x + B over the 64 lanes, composed left to right (lane j
-// ends with the map of lanes 0..j applied in order).
-__device__ __forceinline__ void scan_up(float& A, float& B, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float Ao = __shfl_up(A, off), Bo = __shfl_up(B, off);
-    if (lane >= off) {
-      B = fmaf(A, Bo, B);
-      A = A * Ao;
-    }
-  }
+// DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source (or in masked
+// rows) keep `old`
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWMASK, 0xf, false));
 }
 
-// Inclusive scan composed right to left (lane j ends with the map of lanes 63..j, lane 63's
-// applied first).
+// (A, B) <- (A, B) o (Ao, Bo): this lane's map applied after the other one
+__device__ __forceinline__ void compose(float& A, float& B, float Ao, float Bo) {
+  B = fmaf(A, Bo, B);
+  A = A * Ao;
+}
+
+// Inclusive scan of affine maps x -> A x + B over the 64 lanes, composed left to right (lane j
+// ends with the maps of lanes 0..j, lane 0's applied first): row_shr 1, 2, 4, 8 inside rows of
+// 16 (a lane with no source takes the identity), then row 0's total into row 1 and row 2's into
+// row 3 (row_bcast:15), then lane 31's into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ void scan_up(float& A, float& B) {
+  compose(A, B, dpp_or<0x111, 0xf>(1.f, A), dpp_or<0x111, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x112, 0xf>(1.f, A), dpp_or<0x112, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x114, 0xf>(1.f, A), dpp_or<0x114, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x118, 0xf>(1.f, A), dpp_or<0x118, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x142, 0xa>(1.f, A), dpp_or<0x142, 0xa>(0.f, B));
+  compose(A, B, dpp_or<0x143, 0xc>(1.f, A), dpp_or<0x143, 0xc>(0.f, B));
+}
+
+// Inclusive scan composed right to left (lane j ends with the maps of lanes j..63, lane 63's
+// applied first): row_shl 1, 2, 4, 8 inside rows, then each row composed with the totals of the
+// rows above it (read from their first lanes).
 __device__ __forceinline__ void scan_down(float& A, float& B, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float Ao = __shfl_down(A, off), Bo = __shfl_down(B, off);
-    if (lane + off < 64) {
-      B = fmaf(A, Bo, B);
-      A = A * Ao;
-    }
-  }
+  compose(A, B, dpp_or<0x101, 0xf>(1.f, A), dpp_or<0x101, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x102, 0xf>(1.f, A), dpp_or<0x102, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x104, 0xf>(1.f, A), dpp_or<0x104, 0xf>(0.f, B));
+  compose(A, B, dpp_or<0x108, 0xf>(1.f, A), dpp_or<0x108, 0xf>(0.f, B));
+  const float a1 = readlane_f(A, 16), b1 = readlane_f(B, 16);
+  const float a2 = readlane_f(A, 32), b2 = readlane_f(B, 32);
+  const float a3 = readlane_f(A, 48), b3 = readlane_f(B, 48);
+  // suffixes: rows 3.. (identity for row 3), 2: T3, 1: T2 o T3, 0: T1 o T2 o T3
+  const float s2a = a3, s2b = b3;
+  const float s1a = a2 * s2a, s1b = fmaf(a2, s2b, b2);
+  const float s0a = a1 * s1a, s0b = fmaf(a1, s1b, b1);
+  const int row = lane >> 4;
+  const float Sa = row == 0 ? s0a : row == 1 ? s1a : row == 2 ? s2a : 1.f;
+  const float Sb = row == 0 ? s0b : row == 1 ? s1b : row == 2 ? s2b : 0.f;
+  compose(A, B, Sa, Sb);
+}
+
+// the previous lane's map (lane 0: the identity), and the next lane's (lane 63: the identity)
+__device__ __forceinline__ void shift_up(float& A, float& B) {
+  A = dpp_or<0x138, 0xf>(1.f, A);   // wave_shr:1
+  B = dpp_or<0x138, 0xf>(0.f, B);
+}
+__device__ __forceinline__ void shift_down(float& A, float& B) {
+  A = dpp_or<0x130, 0xf>(1.f, A);   // wave_shl:1
+  B = dpp_or<0x130, 0xf>(0.f, B);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
-}
-
-template <typename TIn>
-__device__ __forceinline__ float ld(const TIn* p, int64_t i, bool ok) {
-  return ok ? to_f32(p[i]) : 0.f;
 }
 
 // Checkpoints: the state of every (row, window, state) at the window's start.
@@ -88,13 +114,15 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
   for (int pp = lane; pp < P; pp += 64) hst[wave][pp][0] = hst[wave][pp][1] = 0.f;
   for (int64_t w = 0; w < nwin; ++w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
-    float dt[kBK], wv[kBK];
+    float dt[kBK], wv[kBK], dv[kBK], uv[kBK];
+    load_seg<kBK>(dr, t0, p.L, p.vec, dv);
+    load_seg<kBK>(ur, t0, p.L, p.vec, uv);
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
       const bool ok = t0 + k < p.L;
-      const float x = ld(dr, t0 + k, ok) + bias;
+      const float x = dv[k] + bias;
       dt[k] = ok ? (p.softplus ? softplus_fast(x) : x) : 0.f;
-      wv[k] = dt[k] * ld(ur, t0 + k, ok);
+      wv[k] = dt[k] * uv[k];
     }
     for (int pp = 0; pp < P; ++pp) {
       float Af[2], Bf[2];
@@ -103,16 +131,18 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
         const int n = 2 * pp + s;
         const bool nv = n < N;
         const float A2 = nv ? p.A[d * p.A_sd + n] * kLog2e : 0.f;
+        float bq[kBK];
+        load_seg<kBK>(Bg + (nv ? n : 0) * p.B_sn, t0, nv ? p.L : 0, p.vec, bq);
         float a = 1.f, h = 0.f;
 #pragma unroll
         for (int k = 0; k < kBK; ++k) {
           const float av = __builtin_amdgcn_exp2f(dt[k] * A2);
-          h = fmaf(av, h, wv[k] * ld(Bg + (nv ? n : 0) * p.B_sn, t0 + k, nv && t0 + k < p.L));
+          h = fmaf(av, h, wv[k] * bq[k]);
           a *= av;
         }
         Af[s] = a;
         Bf[s] = h;
-        scan_up(Af[s], Bf[s], lane);
+        scan_up(Af[s], Bf[s]);
       }
       // the window's start state is stored, and its end state (lane 63's map) carried on
       const float h0 = hst[wave][pp][0], h1 = hst[wave][pp][1];
@@ -163,22 +193,21 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
 
   for (int64_t w = nwin - 1; w >= 0; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
-    float dt[kBK], uu[kBK], wv[kBK], dy0[kBK], y0[kBK], du[kBK], ddt[kBK], sg[kBK], dyv[kBK], zv[kBK];
+    float dt[kBK], uu[kBK], wv[kBK], dy0[kBK], y0[kBK], du[kBK], ddt[kBK], sg[kBK], dyv[kBK], zv[kBK], dv[kBK];
+    load_seg<kBK>(dr, t0, L, p.vec, dv);
+    load_seg<kBK>(ur, t0, L, p.vec, uu);
+    load_seg<kBK>(dyr, t0, L, p.vec, dyv);
+    if constexpr (GATE) load_seg<kBK>(zr, t0, L, p.vec, zv);
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
       const bool ok = t0 + k < L;
-      const float x = ld(dr, t0 + k, ok) + bias;
+      const float x = dv[k] + bias;
       dt[k] = ok ? (p.softplus ? softplus_fast(x) : x) : 0.f;
       // softplus'(x) = sigmoid(x)
       sg[k] = p.softplus ? 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
-      uu[k] = ld(ur, t0 + k, ok);
       wv[k] = dt[k] * uu[k];
-      dyv[k] = ok ? to_f32(dyr[t0 + k]) : 0.f;
       float gz = 1.f;
-      if constexpr (GATE) {
-        zv[k] = ld(zr, t0 + k, ok);
-        gz = silu_fast(zv[k]);
-      }
+      if constexpr (GATE) gz = silu_fast(zv[k]);
       dy0[k] = dyv[k] * gz;
       y0[k] = Dd * uu[k];
       du[k] = dy0[k] * Dd;
@@ -196,13 +225,10 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         const TIn* Br = Bg + (nv ? n : 0) * p.B_sn;
         const TIn* Cr = Cg + (nv ? n : 0) * p.C_sn;
         float av[kBK], bv[kBK], cv[kBK];
+        load_seg<kBK>(Br, t0, nv ? L : 0, p.vec, bv);
+        load_seg<kBK>(Cr, t0, nv ? L : 0, p.vec, cv);
 #pragma unroll
-        for (int k = 0; k < kBK; ++k) {
-          const bool ok = nv && t0 + k < L;
-          av[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
-          bv[k] = ld(Br, t0 + k, ok);
-          cv[k] = ld(Cr, t0 + k, ok);
-        }
+        for (int k = 0; k < kBK; ++k) av[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
         // states: the lane's steps from zero, the scan, then from the incoming state
         float Af = 1.f, Bf = 0.f;
 #pragma unroll
@@ -211,12 +237,9 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
           Af *= av[k];
         }
         const float Pl = Af;   // the lane's total decay (both directions)
-        scan_up(Af, Bf, lane);
-        float Ae = __shfl_up(Af, 1), Be = __shfl_up(Bf, 1);
-        if (lane == 0) {
-          Ae = 1.f;
-          Be = 0.f;
-        }
+        scan_up(Af, Bf);
+        float Ae = Af, Be = Bf;
+        shift_up(Ae, Be);
         const float hw = nv ? ckpt[(row * nwin + w) * N + n] : 0.f;
         float hs[kBK + 1];
         hs[0] = fmaf(Ae, hw, Be);
@@ -232,11 +255,8 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         for (int k = kBK - 1; k >= 0; --k) c = av[k] * fmaf(cv[k], dy0[k], c);
         float Ar = Pl, Br2 = c;
         scan_down(Ar, Br2, lane);
-        float Ad = __shfl_down(Ar, 1), Bd = __shfl_down(Br2, 1);
-        if (lane == 63) {
-          Ad = 1.f;
-          Bd = 0.f;
-        }
+        float Ad = Ar, Bd = Br2;
+        shift_down(Ad, Bd);
         const float Xw = gcar[wave][pp][s];
         c = fmaf(Ad, Xw, Bd);
         float dAs = 0.f;

@@ -75,6 +75,7 @@ struct BwdArgs {
   int64_t batch, channels, L;
   int32_t N, groups, chan_per_group;
   int32_t softplus, in_bf16, dy_bf16;
+  int32_t vec;            // every input time row (and dy's) is 16-byte aligned
   int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, A_sd, dy_sb, dy_sd;
   int64_t du_sb, du_sd, dd_sb, dd_sh, dA_sd, dB_sb, dB_sg, dB_sn, dC_sb, dC_sg, dC_sn, dz_sb, dz_sd;
 };
