@@ -336,7 +336,8 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS>
+// SIO: the call passes an initial and/or a final state (the plain forward compiles without it)
+template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, bool SIO>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
   constexpr StageMode MODE = stage_mode<TIn, VEC>();
@@ -394,7 +395,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   {
     // the carried state starts at the caller's initial state, or at zero
     const float* Ar = p.A + d * p.A_sd;
-    const float* hi = p.h_init ? p.h_init + b * p.hi_sb + d * p.hi_sd : nullptr;
+    const float* hi = (SIO && p.h_init) ? p.h_init + b * p.hi_sb + d * p.hi_sd : nullptr;
     for (int pp = jl; pp < P; pp += LPC) {
       const int n = 2 * pp;
       mypar[pp] = make_float4(Ar[n] * kLog2e, n + 1 < N ? Ar[n + 1] * kLog2e : 0.f, hi ? hi[n] : 0.f,
@@ -707,7 +708,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   }
   // the state after the last step (steps past L are the identity), carried by the row's last
   // lane into its pair slots
-  if (p.h_final && live) {
+  if (SIO && p.h_final && live) {
     float* hf = p.h_final + b * p.hf_sb + d * p.hf_sd;
     for (int pp = jl; pp < P; pp += LPC) {
       const float4 pv = mypar[pp];
@@ -745,12 +746,17 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   // direct-to-LDS loads
   const bool vec = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
-#define SS_LAUNCH(G, V) \
-  hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS>), grid, block, 0, s, a, P, nwin, blocks_per_bg)
+  const bool sio = a.h_init || a.h_final;
+#define SS_LAUNCH(G, V)                                                                                     \
+  if (sio)                                                                                                  \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true>), grid, block, 0, s, a, P, nwin,       \
+                       blocks_per_bg);                                                                      \
+  else                                                                                                      \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, false>), grid, block, 0, s, a, P, nwin, blocks_per_bg)
   if (a.z) {
-    if (vec) SS_LAUNCH(true, true); else SS_LAUNCH(true, false);
+    if (vec) { SS_LAUNCH(true, true); } else { SS_LAUNCH(true, false); }
   } else {
-    if (vec) SS_LAUNCH(false, true); else SS_LAUNCH(false, false);
+    if (vec) { SS_LAUNCH(false, true); } else { SS_LAUNCH(false, false); }
   }
 #undef SS_LAUNCH
   return hipGetLastError();
