@@ -12,7 +12,8 @@
  *   dt_t   = softplus(x_t) = log(1 + exp(x_t))             (if enabled; else dt_t = x_t)
  *   for each state n:
  *     a    = exp(dt_t * A[d, n])                           (A[hd] in the scalar-decay layout)
- *     h_n  = a * h_n + dt_t * B[b, g, n, t] * u[b, d, t]
+ *     h_n  = a * h_n + k_t * B[b, g, n, t] * u[b, d, t]
+ *            k_t = dt_t (exponential-Euler), or (a - 1) / A with zero-order hold
  *   y_t    = sum_n C[b, g, n, t] * h_n + D * u[b, d, t]    (D optional)
  *   y_t   *= z_t / (1 + exp(-z_t))                         (gate optional, z = z[b, d, t])
  *
@@ -60,6 +61,7 @@ typedef struct {
   const double* D;          /* NULL: no feed-through */
   const double* delta_bias; /* NULL: no bias */
   const double* h0;         /* [nrows, nstate] initial state, NULL: zeros */
+  int32_t zoh;              /* 1: zero-order-hold input coefficient (see zoh_coef) */
 } sso_problem;
 
 static double load(const void* p, int32_t dt, int64_t i) {
@@ -73,6 +75,14 @@ static double load(const void* p, int32_t dt, int64_t i) {
 }
 
 static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+
+/* The input coefficient of the discretisation: dt (exponential-Euler, Bbar = dt B), or with
+ * zero-order hold Bbar = (dt A)^-1 (exp(dt A) - 1) dt B = (exp(dt A) - 1) / A B, whose limit
+ * at A = 0 is dt B (omica.com.cn explainer, sections 3 and 5). */
+static double in_coef(const sso_problem* p, double dt, double an) {
+  if (!p->zoh || an == 0.0) return dt;
+  return expm1(dt * an) / an;
+}
 
 typedef struct {
   const sso_problem* p;
@@ -106,7 +116,7 @@ static void run_row(const sso_problem* p, int64_t row, int64_t out_index, double
       const double a = exp(dt * an);
       const double bn = load(p->B, p->in_dtype, bcrow + n * L + t);
       const double cn = load(p->C, p->in_dtype, bcrow + n * L + t);
-      h[n] = a * h[n] + dt * bn * ut;
+      h[n] = a * h[n] + in_coef(p, dt, an) * bn * ut;
       yt += cn * h[n];
     }
     if (p->D) yt += dskip * ut;
@@ -319,6 +329,7 @@ static void* bworker(void* arg) {
  * optional (NULL: not computed).  Returns 0, or -1 on a bad argument or allocation failure. */
 int sso_scan_bwd(const sso_problem* p, const double* dy, sso_grads* g, int nthreads) {
   if (!p || !dy || !g || !g->du || !g->ddelta || !g->dA || !g->dB || !g->dC) return -1;
+  if (p->zoh) return -1; /* the backward is derived for the exponential-Euler coefficient */
   if (!p->u || !p->delta || !p->A || !p->B || !p->C) return -1;
   if (p->channels <= 0 || p->heads <= 0 || p->groups <= 0 || p->channels % p->heads ||
       p->channels % p->groups || p->nstate < 0 || p->length < 0 || p->batch < 0)

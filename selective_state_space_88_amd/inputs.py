@@ -81,6 +81,7 @@ class Problem:
     softplus: bool = True
     scalar_decay: bool = False
     meta: dict = field(default_factory=dict)
+    zoh: bool = False  # zero-order-hold input coefficient instead of exponential-Euler
 
     @property
     def elements(self) -> int:
