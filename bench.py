@@ -270,6 +270,8 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time the decoding step (ss_scan_step: one token for every (batch, channel) "
                          "row of the workload's shapes, state updated in place) instead of the scan")
+    ap.add_argument("--zoh", action="store_true",
+                    help="zero-order-hold input coefficient (SS_ZOH) instead of exponential-Euler")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
                          "gradient dy) on the workload instead of the forward (diagonal workloads)")
@@ -314,7 +316,7 @@ def main():
 
     def step():
         scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                 softplus=p.softplus, y=y, stream=stream.cuda_stream)
+                 softplus=p.softplus, y=y, stream=stream.cuda_stream, zoh=args.zoh)
 
     for _ in range(args.warmup):
         step()
@@ -371,7 +373,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": describe(p),
+            "workload": describe(p) + (", zero-order hold" if args.zoh else ""),
             "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
             "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
             "kernel": kernel,

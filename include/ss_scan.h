@@ -64,6 +64,10 @@ typedef struct {
 /* flags */
 #define SS_DELTA_SOFTPLUS (1u << 0) /* dt = softplus(delta + delta_bias) */
 #define SS_Z_GATE_SILU (1u << 1)    /* y *= silu(z); requires z */
+/* zero-order hold: the input enters as (exp(dt A) - 1) / A * B * u (dt * B * u at A = 0) instead
+ * of the exponential-Euler dt * B * u -- the ZOH discretisation Bbar = (dt A)^-1 (exp(dt A) - I)
+ * dt B of the omica.com.cn explainer, sections 3 and 5.  Forward and decoding step only. */
+#define SS_ZOH (1u << 2)
 
 /* return codes */
 #define SS_OK 0
@@ -88,7 +92,7 @@ typedef struct {
  *   z          [batch, channels, L]          same dtype as u; optional, required by SS_Z_GATE_SILU
  *                                            (a z of no elements may have data == NULL)
  *   delta_bias [heads] f32                   optional: no bias
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH
  *   y          [batch, channels, L]          f32 | bf16, written; must not overlap any input
  *   stream     hipStream_t (as void*), NULL for the default stream
  *
@@ -143,7 +147,7 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
  *   D          [channels] or [heads] f32     optional
  *   z          [batch, channels]             same dtype as u; optional, required by SS_Z_GATE_SILU
  *   delta_bias [heads] f32                   optional
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH
  *   h          [batch, channels, N] f32      read and updated in place (state index innermost)
  *   y          [batch, channels]             f32 | bf16, written
  *
@@ -167,8 +171,9 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * dD = sum dy0_t u_t,  dz_t = dy_t y0_t s'(z_t)  (y0: the output before the gate).
  *
  *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd, restricted to the diagonal
- *              decay with one step size per channel: A [channels, N], delta [batch, channels, L]
- *              (anything else: SS_ERR_UNSUPPORTED), and channels / groups a multiple of 4
+ *              decay with one step size per channel: A [channels, N], delta [batch, channels, L],
+ *              without SS_ZOH (anything else: SS_ERR_UNSUPPORTED), and channels / groups a
+ *              multiple of 4
  *   dy         [batch, channels, L]          f32 | bf16: the gradient of the loss at y
  *   du         [batch, channels, L] f32      written
  *   ddelta     [batch, channels, L] f32      written (the gradient of the raw delta)

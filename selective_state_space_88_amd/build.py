@@ -30,17 +30,36 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 into selective_state_space_88_amd/libssscan.so."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + FLAGS + ["-o", tmp] + srcs
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    if verbose:
-        print(" ".join(cmd))
-        print(res.stderr)
-    os.replace(tmp, LIB)
+    """Compile every HIP source for gfx950 (one hipcc per file, in parallel) and link them into
+    selective_state_space_88_amd/libssscan.so."""
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(CSRC, src.replace(".hip", ".%s.o" % tag))
+        cmd = [hipcc()] + [f for f in FLAGS if f != "-shared"] + ["-c", "-o", obj, os.path.join(CSRC, src)]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    errors = []
+    for cmd, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            errors.append("%s\n%s" % (" ".join(cmd), err))
+        elif verbose:
+            print(" ".join(cmd))
+            print(err)
+    try:
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp = LIB + ".tmp" + tag
+        cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -151,6 +151,24 @@ __device__ __forceinline__ float silu_fast(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
 }
 
+// phi(x) = (exp(x) - 1) / x, phi(0) = 1: the zero-order-hold input coefficient is dt phi(dt A)
+// = (exp(dt A) - 1) / A.  For |x| < 1/2 the Taylor polynomial sum_k x^k / (k + 1)! to degree 7
+// (truncation below 2e-8 relative); elsewhere (e - 1) * rx with e = exp(x) and rx = 1 / x from
+// the caller (there e - 1 is at least 0.39 in size, so its rounding stays near f32's).
+__device__ __forceinline__ float zoh_phi(float x, float e, float rx) {
+  float q = 1.f / 40320.f;
+  q = fmaf(q, x, 1.f / 5040.f);
+  q = fmaf(q, x, 1.f / 720.f);
+  q = fmaf(q, x, 1.f / 120.f);
+  q = fmaf(q, x, 1.f / 24.f);
+  q = fmaf(q, x, 1.f / 6.f);
+  q = fmaf(q, x, 0.5f);
+  q = fmaf(q, x, 1.f);
+  return fabsf(x) < 0.5f ? q : (e - 1.f) * rx;
+}
+
+constexpr float kLn2f = 0.6931471805599453f;
+
 __device__ __forceinline__ float readlane_f(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
 }

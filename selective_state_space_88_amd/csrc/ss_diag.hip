@@ -336,8 +336,9 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// SIO: the call passes an initial and/or a final state (the plain forward compiles without it)
-template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, bool SIO>
+// SIO: the call passes an initial and/or a final state (the plain forward compiles without it).
+// ZOH: zero-order-hold input coefficient (exp(dt A) - 1) / A instead of dt.
+template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, bool SIO, bool ZOH>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
   constexpr StageMode MODE = stage_mode<TIn, VEC>();
@@ -584,16 +585,27 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq);
       }
       float av0[kK], bv0[kK], av1[kK], bv1[kK];
+      float wz0[ZOH ? kK : 1], wz1[ZOH ? kK : 1];
       float h0 = 0.f, h1 = 0.f;
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
         av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
         av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
       }
+      if constexpr (ZOH) {
+        // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
+        const float An0 = pv.x * kLn2f, An1 = pv.y * kLn2f;
+#pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          const float x0 = dt[j] * An0, x1 = dt[j] * An1;
+          wz0[j] = wv[j] * zoh_phi(x0, av0[j], __builtin_amdgcn_rcpf(x0));
+          wz1[j] = wv[j] * zoh_phi(x1, av1[j], __builtin_amdgcn_rcpf(x1));
+        }
+      }
 #pragma unroll
       for (int j = 0; j < kK; ++j) {
-        bv0[j] = wv[j] * bq[j / 4][j % 4];
-        bv1[j] = wv[j] * bq[4 + j / 4][j % 4];
+        bv0[j] = (ZOH ? wz0[j] : wv[j]) * bq[j / 4][j % 4];
+        bv1[j] = (ZOH ? wz1[j] : wv[j]) * bq[4 + j / 4][j % 4];
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
       }
@@ -746,13 +758,19 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   // direct-to-LDS loads
   const bool vec = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
+  // three variants: the plain forward; with state in/out; zero-order hold (state in/out checked
+  // at run time there)
   const bool sio = a.h_init || a.h_final;
 #define SS_LAUNCH(G, V)                                                                                     \
-  if (sio)                                                                                                  \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true>), grid, block, 0, s, a, P, nwin,       \
+  if (a.zoh)                                                                                                \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true, true>), grid, block, 0, s, a, P, nwin, \
+                       blocks_per_bg);                                                                      \
+  else if (sio)                                                                                             \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true, false>), grid, block, 0, s, a, P, nwin, \
                        blocks_per_bg);                                                                      \
   else                                                                                                      \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, false>), grid, block, 0, s, a, P, nwin, blocks_per_bg)
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, false, false>), grid, block, 0, s, a, P, nwin, \
+                       blocks_per_bg)
   if (a.z) {
     if (vec) { SS_LAUNCH(true, true); } else { SS_LAUNCH(true, false); }
   } else {

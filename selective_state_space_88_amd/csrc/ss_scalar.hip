@@ -145,7 +145,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
         float s = p.softplus ? softplus_fast(x) : x;
         if (tb + j >= L) s = 0.f;
         av[j] = __builtin_amdgcn_exp2f(s * An);
-        wv_[j] = s * uv[j];
+        float k = s;  // input coefficient: dt, or with zero-order hold (exp(dt A) - 1) / A
+        if (p.zoh) {
+          const float x = s * An * kLn2f;
+          k = s * zoh_phi(x, av[j], __builtin_amdgcn_rcpf(x));
+        }
+        wv_[j] = k * uv[j];
       }
     }
     float yp[kT];
@@ -256,8 +261,13 @@ __global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p
         const float x = to_f32(dlr[t]) + bias;
         dtv = p.softplus ? softplus_fast(x) : x;
         av = __builtin_amdgcn_exp2f(dtv * An);
+        if (p.zoh) {
+          // input coefficient (exp(dt A) - 1) / A instead of dt
+          const float xz = dtv * An * kLn2f;
+          dtv *= zoh_phi(xz, av, __builtin_amdgcn_rcpf(xz));
+        }
       }
-      dbuf[lane] = dtv;
+      dbuf[lane] = dtv;  // the input coefficient of the step
       abuf[lane] = av;
     }
     // the B/C tile: kHT rows of 2 * Nh floats, contiguous in the workspace

@@ -172,7 +172,8 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   // [w][g][q][8], the B operand of wave w's lane 16 g + q (each wave reads only its own part)
   __shared__ __attribute__((aligned(16))) u32x4 su[64 * kWaves];
   __shared__ __attribute__((aligned(16))) u32x4 sz[GATE ? 64 * kWaves : 1];
-  // per wave: dt, S (log2 of the decay from the chunk's start), 2^S, dt 2^(S_{T-1} - S)
+  // per wave: the input coefficient k (dt, or (exp(dt A) - 1) / A with zero-order hold), S (log2
+  // of the decay from the chunk's start), 2^S, k 2^(S_{T-1} - S)
   __shared__ __attribute__((aligned(16))) float sw[2][kWaves][4][kT];
   // the masked matrix of the chunk (the same for every channel of the head), split into bf16
   // hi and lo parts, as the A operand of t-tile i: [i][lane][8]; wave w computes the quarter
@@ -298,10 +299,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       sc += dpp_zero<0x142, 0xa>(sc);
       const float sEnd = readlane_f(sc, kT - 1);
       if (lane < kT) {
-        wdt[t] = dt;
+        // the input coefficient: dt, or with zero-order hold (exp(dt A) - 1) / A
+        float kz = dt;
+        if (p.zoh) {
+          const float xz = dt * A2 * kLn2f;
+          kz = dt * zoh_phi(xz, __builtin_amdgcn_exp2f(dt * A2), __builtin_amdgcn_rcpf(xz));
+        }
+        wdt[t] = kz;
         wS[t] = sc;
         sw[bf][wave][2][t] = __builtin_amdgcn_exp2f(sc);
-        sw[bf][wave][3][t] = dt * __builtin_amdgcn_exp2f(sEnd - sc);
+        sw[bf][wave][3][t] = kz * __builtin_amdgcn_exp2f(sEnd - sc);
       }
     }
     // this wave's quarter of the masked matrix (G o L)[t][s] dt_s (+ D on the diagonal), for

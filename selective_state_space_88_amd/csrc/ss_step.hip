@@ -75,7 +75,12 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
 #pragma unroll
       for (int i = 0; i < kStatesPerLane; ++i) {
         const float a = __builtin_amdgcn_exp2f(dt * (av[i] * kLog2e));
-        hn[i] = fmaf(a, hv[i], w * Quad<TIn>::get(bv, i));
+        float wi = w;
+        if (p.zoh) {
+          const float x = dt * av[i];
+          wi = w * zoh_phi(x, a, __builtin_amdgcn_rcpf(x));
+        }
+        hn[i] = fmaf(a, hv[i], wi * Quad<TIn>::get(bv, i));
         acc = fmaf(Quad<TIn>::get(cv, i), hn[i], acc);
       }
       *reinterpret_cast<f32x4*>(hr + n0) = hn;
@@ -85,8 +90,14 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
     for (int i = 0; i < kStatesPerLane; ++i) {
       const int n = n0 + i;
       if (live && n < p.N) {
-        const float a = __builtin_amdgcn_exp2f(dt * ((p.scalar ? Ar[0] : Ar[n]) * kLog2e));
-        const float hn = fmaf(a, hr[n], w * to_f32(Br[n]));
+        const float An = p.scalar ? Ar[0] : Ar[n];
+        const float a = __builtin_amdgcn_exp2f(dt * (An * kLog2e));
+        float wi = w;
+        if (p.zoh) {
+          const float x = dt * An;
+          wi = w * zoh_phi(x, a, __builtin_amdgcn_rcpf(x));
+        }
+        const float hn = fmaf(a, hr[n], wi * to_f32(Br[n]));
         hr[n] = hn;
         acc = fmaf(to_f32(Cr[n]), hn, acc);
       }
