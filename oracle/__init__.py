@@ -9,6 +9,7 @@ and shares no code with it.
 
     dt_t = softplus(delta_t + bias)          (optional softplus, optional bias)
     h_t  = exp(dt_t * A) * h_{t-1} + k_t * B_t * u_t      k_t = dt_t, or (exp(dt_t A) - 1) / A (zoh)
+                    (or the exponential-trapezoidal rule with ``trapezoid``: see ss_oracle.c)
     y_t  = C_t . h_t + D * u_t               (optional D)
     y_t *= silu(z_t)                         (optional gate)
 
@@ -41,7 +42,7 @@ class _Problem(ctypes.Structure):
         ("u", ctypes.c_void_p), ("delta", ctypes.c_void_p), ("B", ctypes.c_void_p),
         ("C", ctypes.c_void_p), ("z", ctypes.c_void_p),
         ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("delta_bias", ctypes.c_void_p),
-        ("h0", ctypes.c_void_p), ("zoh", ctypes.c_int32),
+        ("h0", ctypes.c_void_p), ("zoh", ctypes.c_int32), ("trap", ctypes.c_int32),
     ]
 
 
@@ -99,7 +100,8 @@ def scan_fwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: 
              D: Optional[np.ndarray] = None, z: Optional[np.ndarray] = None,
              delta_bias: Optional[np.ndarray] = None, *, softplus: bool = True,
              rows: Optional[Sequence[int]] = None, h0: Optional[np.ndarray] = None,
-             return_state: bool = False, threads: Optional[int] = None, zoh: bool = False):
+             return_state: bool = False, threads: Optional[int] = None, zoh: bool = False,
+             trapezoid: bool = False):
     """Float64 reference output.
 
     Shapes: u, z [batch, channels, L]; delta [batch, heads, L]; A [channels, N] or [heads]
@@ -163,7 +165,7 @@ def scan_fwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: 
 
     prob = _Problem(Bt, Dc, L, N, G, H, code, a_per_head, d_per_head, 1 if softplus else 0,
                     ptr(u), ptr(delta), ptr(B), ptr(C), ptr(z), ptr(A64), ptr(D64), ptr(bias64),
-                    ptr(h0_64), 1 if zoh else 0)
+                    ptr(h0_64), 1 if zoh else 0, 1 if trapezoid else 0)
     rc = _load().sso_scan_fwd(ctypes.byref(prob), ptr(rows_arr), nrows, ptr(y), ptr(hf),
                               int(threads or default_threads()))
     if rc != 0:
@@ -177,7 +179,7 @@ def scan_problem(p, *, rows=None, h0=None, return_state=False, threads=None):
     """Run the oracle on a Problem from the seeded input generator."""
     return scan_fwd(p.u, p.delta, p.A, p.B, p.C, p.D, p.z, p.delta_bias, softplus=p.softplus,
                     rows=rows, h0=h0, return_state=return_state, threads=threads,
-                    zoh=getattr(p, "zoh", False))
+                    zoh=getattr(p, "zoh", False), trapezoid=getattr(p, "trapezoid", False))
 
 
 def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: np.ndarray,
@@ -224,7 +226,7 @@ def scan_bwd(u: np.ndarray, delta: np.ndarray, A: np.ndarray, B: np.ndarray, C: 
 
     prob = _Problem(Bt, Dc, L, N, G, H, code, a_per_head, d_per_head, 1 if softplus else 0,
                     ptr(u), ptr(delta), ptr(B), ptr(C), ptr(z), ptr(A64), ptr(D64), ptr(bias64),
-                    ptr(h0_64), 0)
+                    ptr(h0_64), 0, 0)
     grads = _Grads(ptr(out["du"]), ptr(out["ddelta"]), ptr(out["dA"]), ptr(out["dB"]), ptr(out["dC"]),
                    ptr(out["dD"]), ptr(out["dz"]), ptr(out["ddelta_bias"]), ptr(out["dh0"]))
     rc = _load().sso_scan_bwd(ctypes.byref(prob), ptr(dy64), ctypes.byref(grads), int(threads or default_threads()))

@@ -61,7 +61,8 @@ typedef struct {
   const double* D;          /* NULL: no feed-through */
   const double* delta_bias; /* NULL: no bias */
   const double* h0;         /* [nrows, nstate] initial state, NULL: zeros */
-  int32_t zoh;              /* 1: zero-order-hold input coefficient (see zoh_coef) */
+  int32_t zoh;              /* 1: zero-order-hold input coefficient (see in_coef) */
+  int32_t trap;             /* 1: exponential-trapezoidal rule (see run_row) */
 } sso_problem;
 
 static double load(const void* p, int32_t dt, int64_t i) {
@@ -94,6 +95,12 @@ typedef struct {
   int status;
 } job_t;
 
+/* The exponential-trapezoidal rule (omica.com.cn explainer, section 6.3, the recurrence of
+ * Mamba-3) averages the input of the current and the previous step:
+ *   h_t = a_t h_{t-1} + 1/2 (e_t + a_t e_{t-1}),   e_t = k_t B_t u_t  (k_t the input coefficient),
+ * with nothing before the first step.  The state passed in and out of a call (h0, h_final) is
+ * h + 1/2 e of the step before / the last step, the quantity that carries the rule across a
+ * boundary (it lets a sequence be scanned in pieces); run_row keeps h and the previous e. */
 static void run_row(const sso_problem* p, int64_t row, int64_t out_index, double* h, double* y,
                     double* h_final) {
   const int64_t L = p->length, N = p->nstate, Dc = p->channels;
@@ -103,7 +110,11 @@ static void run_row(const sso_problem* p, int64_t row, int64_t out_index, double
   const int64_t urow = (b * Dc + d) * L;
   const int64_t drow = (b * p->heads + hd) * L;
   const int64_t bcrow = (b * p->groups + g) * N * L;
-  for (int64_t n = 0; n < N; ++n) h[n] = p->h0 ? p->h0[out_index * N + n] : 0.0;
+  /* h[n]: the state; h[N + n]: the previous step's input term e (trapezoidal rule only) */
+  for (int64_t n = 0; n < N; ++n) {
+    h[n] = p->h0 ? p->h0[out_index * N + n] : 0.0;
+    h[N + n] = 0.0;
+  }
   const double bias = p->delta_bias ? p->delta_bias[hd] : 0.0;
   const double dskip = p->D ? p->D[p->d_per_head ? hd : d] : 0.0;
   for (int64_t t = 0; t < L; ++t) {
@@ -116,7 +127,13 @@ static void run_row(const sso_problem* p, int64_t row, int64_t out_index, double
       const double a = exp(dt * an);
       const double bn = load(p->B, p->in_dtype, bcrow + n * L + t);
       const double cn = load(p->C, p->in_dtype, bcrow + n * L + t);
-      h[n] = a * h[n] + in_coef(p, dt, an) * bn * ut;
+      const double e = in_coef(p, dt, an) * bn * ut;
+      if (p->trap) {
+        h[n] = a * h[n] + 0.5 * (e + a * h[N + n]);
+        h[N + n] = e;
+      } else {
+        h[n] = a * h[n] + e;
+      }
       yt += cn * h[n];
     }
     if (p->D) yt += dskip * ut;
@@ -127,12 +144,12 @@ static void run_row(const sso_problem* p, int64_t row, int64_t out_index, double
     y[out_index * L + t] = yt;
   }
   if (h_final)
-    for (int64_t n = 0; n < N; ++n) h_final[out_index * N + n] = h[n];
+    for (int64_t n = 0; n < N; ++n) h_final[out_index * N + n] = h[n] + (p->trap ? 0.5 * h[N + n] : 0.0);
 }
 
 static void* worker(void* arg) {
   job_t* j = (job_t*)arg;
-  double* h = (double*)malloc(sizeof(double) * (size_t)(j->p->nstate > 0 ? j->p->nstate : 1));
+  double* h = (double*)malloc(sizeof(double) * (size_t)(j->p->nstate > 0 ? 2 * j->p->nstate : 1));
   if (!h) {
     j->status = -1;
     return NULL;
@@ -329,7 +346,7 @@ static void* bworker(void* arg) {
  * optional (NULL: not computed).  Returns 0, or -1 on a bad argument or allocation failure. */
 int sso_scan_bwd(const sso_problem* p, const double* dy, sso_grads* g, int nthreads) {
   if (!p || !dy || !g || !g->du || !g->ddelta || !g->dA || !g->dB || !g->dC) return -1;
-  if (p->zoh) return -1; /* the backward is derived for the exponential-Euler coefficient */
+  if (p->zoh || p->trap) return -1; /* the backward is derived for the exponential-Euler rule */
   if (!p->u || !p->delta || !p->A || !p->B || !p->C) return -1;
   if (p->channels <= 0 || p->heads <= 0 || p->groups <= 0 || p->channels % p->heads ||
       p->channels % p->groups || p->nstate < 0 || p->length < 0 || p->batch < 0)

@@ -82,6 +82,7 @@ class Problem:
     scalar_decay: bool = False
     meta: dict = field(default_factory=dict)
     zoh: bool = False  # zero-order-hold input coefficient instead of exponential-Euler
+    trapezoid: bool = False  # exponential-trapezoidal rule
 
     @property
     def elements(self) -> int:
