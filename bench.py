@@ -272,6 +272,8 @@ def main():
                          "row of the workload's shapes, state updated in place) instead of the scan")
     ap.add_argument("--zoh", action="store_true",
                     help="zero-order-hold input coefficient (SS_ZOH) instead of exponential-Euler")
+    ap.add_argument("--trapezoid", action="store_true",
+                    help="exponential-trapezoidal rule (SS_TRAPEZOID) instead of exponential-Euler")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
                          "gradient dy) on the workload instead of the forward (diagonal workloads)")
@@ -316,7 +318,8 @@ def main():
 
     def step():
         scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                 softplus=p.softplus, y=y, stream=stream.cuda_stream, zoh=args.zoh)
+                 softplus=p.softplus, y=y, stream=stream.cuda_stream, zoh=args.zoh,
+                 trapezoid=args.trapezoid)
 
     for _ in range(args.warmup):
         step()
@@ -373,7 +376,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": describe(p) + (", zero-order hold" if args.zoh else ""),
+            "workload": describe(p) + (", zero-order hold" if args.zoh else "") +
+                        (", exponential-trapezoidal" if args.trapezoid else ""),
             "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
             "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
             "kernel": kernel,

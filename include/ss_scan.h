@@ -68,6 +68,11 @@ typedef struct {
  * of the exponential-Euler dt * B * u -- the ZOH discretisation Bbar = (dt A)^-1 (exp(dt A) - I)
  * dt B of the omica.com.cn explainer, sections 3 and 5.  Forward and decoding step only. */
 #define SS_ZOH (1u << 2)
+/* exponential-trapezoidal rule: h_t = exp(dt_t A) h_{t-1} + (e_t + exp(dt_t A) e_{t-1}) / 2 with
+ * e_t = Bbar_t u_t (the explainer's Mamba-3 recurrence, section 6.3).  The state passed in and
+ * out (h_init, h_final, the decoding state) is h_t + e_t / 2 of the step before / the last step,
+ * which carries the rule across call boundaries.  Forward and decoding step only. */
+#define SS_TRAPEZOID (1u << 3)
 
 /* return codes */
 #define SS_OK 0
@@ -92,7 +97,7 @@ typedef struct {
  *   z          [batch, channels, L]          same dtype as u; optional, required by SS_Z_GATE_SILU
  *                                            (a z of no elements may have data == NULL)
  *   delta_bias [heads] f32                   optional: no bias
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID
  *   y          [batch, channels, L]          f32 | bf16, written; must not overlap any input
  *   stream     hipStream_t (as void*), NULL for the default stream
  *
@@ -147,7 +152,7 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
  *   D          [channels] or [heads] f32     optional
  *   z          [batch, channels]             same dtype as u; optional, required by SS_Z_GATE_SILU
  *   delta_bias [heads] f32                   optional
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID
  *   h          [batch, channels, N] f32      read and updated in place (state index innermost)
  *   y          [batch, channels]             f32 | bf16, written
  *
@@ -172,8 +177,8 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  *
  *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd, restricted to the diagonal
  *              decay with one step size per channel: A [channels, N], delta [batch, channels, L],
- *              without SS_ZOH (anything else: SS_ERR_UNSUPPORTED), and channels / groups a
- *              multiple of 4
+ *              without SS_ZOH or SS_TRAPEZOID (anything else: SS_ERR_UNSUPPORTED), and
+ *              channels / groups a multiple of 4
  *   dy         [batch, channels, L]          f32 | bf16: the gradient of the loss at y
  *   du         [batch, channels, L] f32      written
  *   ddelta     [batch, channels, L] f32      written (the gradient of the raw delta)

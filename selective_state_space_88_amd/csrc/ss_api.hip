@@ -107,7 +107,7 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
                 uint32_t flags, const ss_tensor* h_init, ss_tensor* h_final, ss_tensor* y, void* stream) {
   if (!u || !delta || !A || !B || !C || !y) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH)) return SS_ERR_FLAGS;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -194,6 +194,7 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   a.d_per_head = present(D) && D->shape[0] != Dc ? 1 : 0;
   a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
   a.zoh = (flags & SS_ZOH) ? 1 : 0;
+  a.trap = (flags & SS_TRAPEZOID) ? 1 : 0;
   a.in_bf16 = idt == SS_BF16;
   a.out_bf16 = y->dtype == SS_BF16;
   a.vec = aligned16(u) && aligned16(delta) && aligned16(B) && aligned16(C) && aligned16(y) &&
@@ -261,7 +262,7 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
                  const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                  const ss_tensor* delta_bias, uint32_t flags, ss_tensor* h, ss_tensor* y, void* stream) {
   if (!u || !delta || !A || !B || !C || !h || !y) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH)) return SS_ERR_FLAGS;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -324,6 +325,7 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
   a.chan_per_group = (int32_t)(Dc / G);
   a.scalar = scalar ? 1 : 0;
   a.zoh = (flags & SS_ZOH) ? 1 : 0;
+  a.trap = (flags & SS_TRAPEZOID) ? 1 : 0;
   a.d_per_head = present(D) && D->shape[0] != Dc ? 1 : 0;
   a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
   a.in_bf16 = idt == SS_BF16;
@@ -358,7 +360,7 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
                 ss_tensor* dB, ss_tensor* dC, ss_tensor* dD, ss_tensor* dz, ss_tensor* ddelta_bias,
                 void* stream) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH)) return SS_ERR_FLAGS;
+  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -383,8 +385,8 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
     if (dy->shape[i] != u->shape[i] || (gate && z->shape[i] != u->shape[i])) return SS_ERR_SHAPE;
   if (G <= 0 || (Dc > 0 && Dc % G)) return SS_ERR_SHAPE;
   // the backward covers the diagonal decay with one step size per channel (Mamba-1 layout), with
-  // the exponential-Euler input coefficient
-  if (A->ndim != 2 || H != Dc || (flags & SS_ZOH)) return SS_ERR_UNSUPPORTED;
+  // the exponential-Euler rule
+  if (A->ndim != 2 || H != Dc || (flags & (SS_ZOH | SS_TRAPEZOID))) return SS_ERR_UNSUPPORTED;
   if (A->shape[0] != Dc || A->shape[1] != N) return SS_ERR_SHAPE;
   if (present(D) && D->shape[0] != Dc) return SS_ERR_SHAPE;
   if (present(delta_bias) && delta_bias->shape[0] != Dc) return SS_ERR_SHAPE;

@@ -336,19 +336,24 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
-// SIO: the call passes an initial and/or a final state (the plain forward compiles without it).
-// ZOH: zero-order-hold input coefficient (exp(dt A) - 1) / A instead of dt.
-template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, bool SIO, bool ZOH>
+// MODE bits (the plain forward, MODE 0, compiles without them):
+//   kSIO   the call passes an initial and/or a final state;
+//   kZOH   zero-order-hold input coefficient (exp(dt A) - 1) / A instead of dt;
+//   kTRAP  exponential-trapezoidal rule: the scan runs the state k = h + e/2, which obeys the
+//          Euler recurrence k_t = a_t k_{t-1} + e_t, and y reads C (k - e/2).
+constexpr int kSIO = 1, kZOH = 2, kTRAP = 4;
+template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, int MODE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
-  constexpr StageMode MODE = stage_mode<TIn, VEC>();
+  constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
+  constexpr StageMode SMODE = stage_mode<TIn, VEC>();
   constexpr int LPC = 64 / ROWS;                     // lanes per channel row
   constexpr int W = win_steps<ROWS>();               // steps per window of a channel
   constexpr int SLOT = slot_floats<ROWS>();          // floats of one f32 stage
-  constexpr int NF = MODE == StageMode::kDirect ? 3 : 2;       // f32 ring slots
-  constexpr int AHEAD = MODE == StageMode::kWiden ? 3 : 2;     // stages copied ahead of use
+  constexpr int NF = SMODE == StageMode::kDirect ? 3 : 2;       // f32 ring slots
+  constexpr int AHEAD = SMODE == StageMode::kWiden ? 3 : 2;     // stages copied ahead of use
   constexpr int ROWB = W * (int)sizeof(TIn);                   // bytes of one stage row
-  constexpr int NDMA = MODE == StageMode::kWiden ? ROWB / 1024 : W / 256;  // copies per wave per stage
+  constexpr int NDMA = SMODE == StageMode::kWiden ? ROWB / 1024 : W / 256;  // copies per wave per stage
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
   constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
@@ -356,8 +361,8 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   constexpr int CPT = W / 512;                       // 8-step chunks widened per thread per stage
   static_assert(ROWS == 1 || ROWS == 2, "1 or 2 channels per wave");
   __shared__ __attribute__((aligned(16))) float fring[NF][SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t rring[MODE == StageMode::kWiden ? 3 : 1]
-                                                       [MODE == StageMode::kWiden ? ROWB : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t rring[SMODE == StageMode::kWiden ? 3 : 1]
+                                                       [SMODE == StageMode::kWiden ? ROWB : 4];
   // per wave: u, delta, z of one window, and y on its way out
   __shared__ __attribute__((aligned(16))) uint32_t xin[kWaves][3][kSegWords];
   __shared__ __attribute__((aligned(16))) uint32_t ystg[kWaves][NCO * 256];
@@ -426,7 +431,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
         __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(row ? row + t_first : Bg), (short)0,
                                           row ? 0x7fffffff : 0, 0x00020000);
     const int64_t lim = L - t_first;  // steps of this window inside the row
-    if constexpr (MODE == StageMode::kWiden) {
+    if constexpr (SMODE == StageMode::kWiden) {
       uint32_t* dst = rring[qs % 3] + wave * (ROWB / 4);
 #pragma unroll
       for (int c = 0; c < NDMA; ++c) {
@@ -453,7 +458,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       const int k = (int)threadIdx.x + 256 * m;
       const int rr = k / (W / 8), cc = k % (W / 8);
       float v[8];
-      if constexpr (MODE == StageMode::kWiden) {
+      if constexpr (SMODE == StageMode::kWiden) {
         const uint32_t wd[4] = {raw[m].x, raw[m].y, raw[m].z, raw[m].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -484,7 +489,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     x_copy(drow, 0, xd);
     if constexpr (GATE) x_copy(zrow, 0, xz);
   }
-  if constexpr (MODE == StageMode::kWiden) {
+  if constexpr (SMODE == StageMode::kWiden) {
     for (int qs = 0; qs < 3 && qs < Qt; ++qs) stage_copy(qs);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
@@ -494,7 +499,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       stage_widen(0, 0, raw);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  } else if constexpr (MODE == StageMode::kDirect) {
+  } else if constexpr (SMODE == StageMode::kDirect) {
     for (int qs = 0; qs < 2 && qs < Qt; ++qs) stage_copy(qs);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
   } else {
@@ -560,22 +565,22 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     for (int pp = 0; pp < P; ++pp) {
       // copies of a later stage, and (kWiden, kElementwise) the next stage into f32
       int allow = pp == 0 ? boundary_ops : 0;
-      if constexpr (MODE != StageMode::kElementwise) {
+      if constexpr (SMODE != StageMode::kElementwise) {
         if (q + AHEAD < Qt) {
           stage_copy(q + AHEAD);
           allow += NDMA;
         }
       }
-      if constexpr (MODE == StageMode::kElementwise)
+      if constexpr (SMODE == StageMode::kElementwise)
         if (q + 1 < Qt) stage_widen(q + 1, (q + 1) & 1, nullptr);
-      const int fs = MODE == StageMode::kDirect ? q % 3 : (q & 1);
+      const int fs = SMODE == StageMode::kDirect ? q % 3 : (q & 1);
       const float4 pv = mypar[pp];  // (A pair, carried state pair) of this lane's channel
       // this lane's B values of both states: quad i of row r of the slot is at byte offset
       // 4 W r + 16 (i LPC + j) from the slot
       const uint32_t lbase = lds_addr(fring[fs]) + 16u * (uint32_t)jl;
       constexpr int QS = 16 * LPC;
       f32x4 bq[8];  // B of state 2p (quads 0-3), then of state 2p + 1
-      if constexpr (MODE == StageMode::kWiden) {
+      if constexpr (SMODE == StageMode::kWiden) {
         // with this thread's raw chunks of the next stage, widened right after
         u32x4 raw[CPT];
         lds_read8_plus<CPT, 0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(
@@ -622,8 +627,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       for (int j = 0; j < kK; ++j) {
         h0 = fmaf(av0[j], h0, bv0[j]);
         h1 = fmaf(av1[j], h1, bv1[j]);
-        yv[j] = fmaf(cq[j / 4][j % 4], h0, yv[j]);
-        yv[j] = fmaf(cq[4 + j / 4][j % 4], h1, yv[j]);
+        if constexpr (TRAP) {
+          yv[j] = fmaf(cq[j / 4][j % 4], fmaf(-0.5f, bv0[j], h0), yv[j]);
+          yv[j] = fmaf(cq[4 + j / 4][j % 4], fmaf(-0.5f, bv1[j], h1), yv[j]);
+        } else {
+          yv[j] = fmaf(cq[j / 4][j % 4], h0, yv[j]);
+          yv[j] = fmaf(cq[4 + j / 4][j % 4], h1, yv[j]);
+        }
       }
       // the window's end state (the row's last lane) starts the same pair in the next window
       if (jl == LPC - 1) *reinterpret_cast<float2*>(&mypar[pp].z) = make_float2(h0, h1);
@@ -637,7 +647,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     // epilogue: gate, store, then this slot's z for the next window.  Only the stage copy
     // issued by the last pair may still be in flight here: everything before it (this
     // window's z and the next window's u and delta) has landed.
-    if (MODE != StageMode::kElementwise && q - 1 + AHEAD < Qt) {
+    if (SMODE != StageMode::kElementwise && q - 1 + AHEAD < Qt) {
       if constexpr (NDMA == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
       else if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -758,25 +768,26 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   // direct-to-LDS loads
   const bool vec = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
-  // three variants: the plain forward; with state in/out; zero-order hold (state in/out checked
-  // at run time there)
-  const bool sio = a.h_init || a.h_final;
-#define SS_LAUNCH(G, V)                                                                                     \
-  if (a.zoh)                                                                                                \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true, true>), grid, block, 0, s, a, P, nwin, \
-                       blocks_per_bg);                                                                      \
-  else if (sio)                                                                                             \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, true, false>), grid, block, 0, s, a, P, nwin, \
-                       blocks_per_bg);                                                                      \
-  else                                                                                                      \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, false, false>), grid, block, 0, s, a, P, nwin, \
-                       blocks_per_bg)
+  // the plain forward, or (state in/out checked at run time) with state in/out, zero-order hold
+  // and/or the trapezoidal rule
+  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0);
+#define SS_M(G, V, M)                                                                                        \
+  case M:                                                                                                    \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, M>), grid, block, 0, s, a, P, nwin, blocks_per_bg); \
+    break;
+#define SS_LAUNCH(G, V)                                                                                      \
+  switch (mode) {                                                                                            \
+    SS_M(G, V, 0) SS_M(G, V, kSIO) SS_M(G, V, kSIO | kZOH) SS_M(G, V, kSIO | kTRAP)                          \
+    SS_M(G, V, kSIO | kZOH | kTRAP)                                                                          \
+    default: return hipErrorInvalidValue;                                                                    \
+  }
   if (a.z) {
     if (vec) { SS_LAUNCH(true, true); } else { SS_LAUNCH(true, false); }
   } else {
     if (vec) { SS_LAUNCH(false, true); } else { SS_LAUNCH(false, false); }
   }
 #undef SS_LAUNCH
+#undef SS_M
   return hipGetLastError();
 }
 

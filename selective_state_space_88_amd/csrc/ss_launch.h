@@ -29,6 +29,7 @@ struct ScanArgs {
   int64_t y_sb, y_sd, A_sd;
   // optional state in / out, [batch, channels, N] f32, state index innermost (stride 1)
   int32_t zoh;            // zero-order-hold input coefficient (exp(dt A) - 1) / A instead of dt
+  int32_t trap;           // exponential-trapezoidal rule: y read from h - e/2 (the state is h + e/2)
   const float* h_init;    // nullptr: the state starts at zero
   float* h_final;         // nullptr: not written
   int64_t hi_sb, hi_sd, hf_sb, hf_sd;
@@ -51,6 +52,7 @@ struct StepArgs {
   int32_t chan_per_head, chan_per_group;
   int32_t scalar;         // A per head
   int32_t zoh;            // zero-order-hold input coefficient
+  int32_t trap;           // exponential-trapezoidal rule
   int32_t d_per_head;
   int32_t softplus;
   int32_t in_bf16, out_bf16;

@@ -127,6 +127,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
 #pragma unroll
     for (int i = 0; i < kNT; ++i) h[i] = (hi && wv * kNT + i < p.N) ? hi[wv * kNT + i] : 0.f;
   }
+  const float th = p.trap ? 0.5f : 0.f;
 
   for (int64_t tb = 0; tb < L; tb += kT) {
     float av[kT], wv_[kT];
@@ -162,8 +163,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
       float acc = 0.f;
 #pragma unroll
       for (int i = 0; i < kNT; ++i) {
-        h[i] = fmaf(av[j], h[i], wv_[j] * bt[i]);
-        acc = fmaf(ct[i], h[i], acc);
+        const float e = wv_[j] * bt[i];
+        h[i] = fmaf(av[j], h[i], e);
+        // trapezoidal rule: h carries k = h + e/2; y reads k - e/2
+        acc = fmaf(ct[i], fmaf(-th, e, h[i]), acc);
       }
       yp[j] = acc;
     }
@@ -252,6 +255,7 @@ __global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p
 #pragma unroll
     for (int i = 0; i < kHS; ++i) h[i] = (hi && wv * kHS + i < p.N) ? hi[wv * kHS + i] : 0.f;
   }
+  const float th = p.trap ? 0.5f : 0.f;
 
   for (int64_t tb = 0; tb < L; tb += kHT) {
     if (wv == 0 && lane < kHT) {
@@ -317,8 +321,10 @@ __global__ __launch_bounds__(64 * kHMaxWaves) void scalar_head_kernel(ScanArgs p
       float sum = 0.f;
 #pragma unroll
       for (int i = 0; i < kHS; ++i) {
-        h[i] = fmaf(a, h[i], w * Bj[i]);
-        sum = fmaf(Cj[i], h[i], sum);
+        const float e = w * Bj[i];
+        h[i] = fmaf(a, h[i], e);
+        // trapezoidal rule: h carries k = h + e/2; y reads k - e/2
+        sum = fmaf(Cj[i], fmaf(-th, e, h[i]), sum);
       }
       acc[j] = sum;
     }

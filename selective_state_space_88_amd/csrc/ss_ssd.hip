@@ -326,7 +326,9 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         const int s = 8 * g16 + 4 * hq + e;
         // (the record holds 0 above the diagonal; the exponent is masked there too, where it
         // may be large and positive)
-        m[e] = gq[e] * dtq[e] * __builtin_amdgcn_exp2f(s <= t ? St - Ssq[e] : -INFINITY) + (s == t ? Dfold : 0.f);
+        // (the trapezoidal rule reads y from h - e/2, i.e. halves the diagonal's input term)
+        const float tw = (s == t && p.trap) ? 0.5f : 1.f;
+        m[e] = tw * gq[e] * dtq[e] * __builtin_amdgcn_exp2f(s <= t ? St - Ssq[e] : -INFINITY) + (s == t ? Dfold : 0.f);
       }
       const uint32_t h0 = pk_bf16(m[0], m[1]), h1 = pk_bf16(m[2], m[3]);
       const uint32_t l0 = pk_bf16(m[0] - __uint_as_float(h0 << 16), m[1] - __uint_as_float(h0 & 0xffff0000u));

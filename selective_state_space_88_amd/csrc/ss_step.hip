@@ -80,8 +80,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
           const float x = dt * av[i];
           wi = w * zoh_phi(x, a, __builtin_amdgcn_rcpf(x));
         }
-        hn[i] = fmaf(a, hv[i], wi * Quad<TIn>::get(bv, i));
-        acc = fmaf(Quad<TIn>::get(cv, i), hn[i], acc);
+        const float e = wi * Quad<TIn>::get(bv, i);
+        hn[i] = fmaf(a, hv[i], e);
+        // trapezoidal rule: the state is k = h + e/2, y reads k - e/2
+        acc = fmaf(Quad<TIn>::get(cv, i), p.trap ? fmaf(-0.5f, e, hn[i]) : hn[i], acc);
       }
       *reinterpret_cast<f32x4*>(hr + n0) = hn;
     }
@@ -97,9 +99,10 @@ __global__ __launch_bounds__(kStepThreads) void step_kernel(StepArgs p, int G) {
           const float x = dt * An;
           wi = w * zoh_phi(x, a, __builtin_amdgcn_rcpf(x));
         }
-        const float hn = fmaf(a, hr[n], wi * to_f32(Br[n]));
+        const float e = wi * to_f32(Br[n]);
+        const float hn = fmaf(a, hr[n], e);
         hr[n] = hn;
-        acc = fmaf(to_f32(Cr[n]), hn, acc);
+        acc = fmaf(to_f32(Cr[n]), p.trap ? fmaf(-0.5f, e, hn) : hn, acc);
       }
     }
   }

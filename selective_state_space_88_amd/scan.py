@@ -19,6 +19,7 @@ SS_F32, SS_BF16 = 0, 1
 SS_DELTA_SOFTPLUS = 1 << 0
 SS_Z_GATE_SILU = 1 << 1
 SS_ZOH = 1 << 2
+SS_TRAPEZOID = 1 << 3
 EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_check", "ss_strerror",
            "ss_version")
 
@@ -130,7 +131,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              delta_bias: Optional[torch.Tensor] = None, *, softplus: bool = True,
              y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
              stream: Optional[int] = None, h_init: Optional[torch.Tensor] = None,
-             h_final: Optional[torch.Tensor] = None, zoh: bool = False) -> torch.Tensor:
+             h_final: Optional[torch.Tensor] = None, zoh: bool = False,
+             trapezoid: bool = False) -> torch.Tensor:
     """Selective-scan forward on the GPU through ss_scan_fwd (see include/ss_scan.h).
 
     u, z: [batch, channels, L]; delta: [batch, heads, L]; A: [channels, N] (diagonal) or
@@ -138,13 +140,14 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     delta_bias: [heads].  Returns y [batch, channels, L] (float32 unless out_dtype/y say so).
     With h_init and/or h_final ([batch, channels, N] float32) the call goes through
     ss_scan_fwd_state: the scan starts from h_init and writes its final state to h_final.
-    ``zoh`` selects the zero-order-hold input coefficient (SS_ZOH).
+    ``zoh`` selects the zero-order-hold input coefficient (SS_ZOH), ``trapezoid`` the
+    exponential-trapezoidal rule (SS_TRAPEZOID).
     """
     _check_cuda(u, delta, A, B, C, D, z, delta_bias, h_init, h_final)
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
-        (SS_ZOH if zoh else 0)
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     args = (describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
@@ -162,7 +165,7 @@ def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               C: torch.Tensor, D: Optional[torch.Tensor], z: Optional[torch.Tensor],
               delta_bias: Optional[torch.Tensor], h: torch.Tensor, *, softplus: bool = True,
               y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
-              stream: Optional[int] = None, zoh: bool = False) -> torch.Tensor:
+              stream: Optional[int] = None, zoh: bool = False, trapezoid: bool = False) -> torch.Tensor:
     """One decoding step through ss_scan_step: h (float32 [batch, channels, N]) is updated in
     place and y [batch, channels] returned.  u, z: [batch, channels]; delta: [batch, heads];
     B, C: [batch, groups, N]; A, D, delta_bias as in scan_fwd."""
@@ -170,7 +173,7 @@ def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
-        (SS_ZOH if zoh else 0)
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     rc = call_step(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),

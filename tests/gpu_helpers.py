@@ -43,7 +43,8 @@ def run_hip(p, out_dtype=None, dev=None):
 
     t = dev if dev is not None else dev_problem(p)
     y = scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                 softplus=p.softplus, out_dtype=out_dtype or torch.float32, zoh=getattr(p, "zoh", False))
+                 softplus=p.softplus, out_dtype=out_dtype or torch.float32, zoh=getattr(p, "zoh", False),
+                 trapezoid=getattr(p, "trapezoid", False))
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
