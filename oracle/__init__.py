@@ -239,3 +239,32 @@ def scan_bwd_problem(p, dy, *, h0=None, threads=None) -> dict:
     """``scan_bwd`` on a Problem from the seeded input generator."""
     return scan_bwd(p.u, p.delta, p.A, p.B, p.C, p.D, p.z, p.delta_bias, dy=dy, softplus=p.softplus,
                     h0=h0, threads=threads)
+
+
+def conv1d(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None, *, state: Optional[np.ndarray] = None,
+           silu: bool = False, return_state: bool = False):
+    """Float64 causal depthwise convolution (see ss_oracle.c): x [batch, channels, L] (float32,
+    float64 or bf16 bits), w [channels, W], bias [channels], state [batch, channels, W - 1] (the
+    inputs before t = 0, oldest first).  Returns out [batch, channels, L] (and the last W - 1
+    inputs with ``return_state``)."""
+    lib = _load()
+    if not hasattr(lib, "_conv_bound"):
+        lib.sso_conv1d.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+        lib.sso_conv1d.restype = ctypes.c_int
+        lib._conv_bound = True
+    x = np.ascontiguousarray(x)
+    Bt, Dc, L = x.shape
+    w64 = np.ascontiguousarray(w, dtype=np.float64)
+    W = w64.shape[1]
+    b64 = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+    s64 = None if state is None else np.ascontiguousarray(state, dtype=np.float64).reshape(Bt * Dc, W - 1)
+    out = np.empty((Bt, Dc, L))
+    so = np.empty((Bt, Dc, max(W - 1, 0)))
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.sso_conv1d(Bt, Dc, L, _code(x), ptr(x), ptr(w64), W, ptr(b64), ptr(s64), 1 if silu else 0, ptr(out),
+                        ptr(so))
+    if rc != 0:
+        raise RuntimeError("oracle conv1d failed (rc=%d)" % rc)
+    return (out, so) if return_state else out

@@ -408,3 +408,41 @@ int sso_scan_bwd(const sso_problem* p, const double* dy, sso_grads* g, int nthre
   free(sums);
   return rc;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Causal depthwise convolution in front of the scan (each Mamba block has a causal 1-D
+ * convolution that adds local context before the selective SSM: bqwf.cn survey, section 3.1;
+ * the decoding state then keeps the last few inputs: study notes, pitfalls).  Per (b, d):
+ *
+ *   out_t = bias_d + sum_{j=0}^{W-1} w[d, j] * x_{t - (W-1) + j}      (w[d, W-1] on the newest)
+ *   out_t = out_t * sigmoid(out_t)                                    (if silu)
+ *
+ * with x_{-W+1..-1} from `state` ([rows, W-1], oldest first) or zero; the last W-1 inputs are
+ * returned in `state_out`.  x: [batch, channels, L] (dtype as in sso_problem), w: [channels, W],
+ * out: [batch, channels, L] float64. */
+int sso_conv1d(int64_t batch, int64_t channels, int64_t L, int32_t dtype, const void* x, const double* w,
+               int64_t W, const double* bias, const double* state, int32_t silu, double* out, double* state_out) {
+  if (!x || !w || !out || W < 1 || batch < 0 || channels < 0 || L < 0) return -1;
+  for (int64_t r = 0; r < batch * channels; ++r) {
+    const int64_t d = r % channels;
+    for (int64_t t = 0; t < L; ++t) {
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t j = 0; j < W; ++j) {
+        const int64_t s = t - (W - 1) + j;
+        double xv = 0.0;
+        if (s >= 0) xv = load(x, dtype, r * L + s);
+        else if (state) xv = state[r * (W - 1) + (W - 1) + s];   /* s = -(W-1) .. -1 */
+        acc += w[d * W + j] * xv;
+      }
+      if (silu) acc = acc / (1.0 + exp(-acc));
+      out[r * L + t] = acc;
+    }
+    if (state_out)
+      for (int64_t j = 0; j < W - 1; ++j) {
+        const int64_t s = L - (W - 1) + j;
+        state_out[r * (W - 1) + j] = s >= 0 ? load(x, dtype, r * L + s)
+                                            : (state ? state[r * (W - 1) + (W - 1) + s] : 0.0);
+      }
+  }
+  return 0;
+}
