@@ -55,7 +55,7 @@ def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
 
 # source file of each scan kernel
 KERNEL_SOURCE = {"diag_fwd_kernel": "ss_diag.hip", "scalar_head_kernel": "ss_scalar.hip",
-                 "ssd_scan_kernel": "ss_ssd.hip"}
+                 "ssd_scan_kernel": "ss_ssd.hip", "conv1d_kernel": "ss_conv.hip"}
 
 
 def scan_kernel(p):
@@ -80,14 +80,15 @@ def kernel_source_digest(kernel):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def stored_traffic(kernel, workload, digest):
+def stored_traffic(kernel, workload, digest, mode=None):
     """HBM bytes per launch from the committed counter summary, if it was taken on this source.
 
-    The summary (profiles/traffic_<kernel>_w<workload>.txt) holds `key: value` lines written
+    The summary (profiles/traffic_<kernel>[_<mode>]_w<workload>.txt) holds `key: value` lines written
     from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE), each scaled by the same counter's
     reading for a plain copy of known size in the same process.
     """
-    path = os.path.join(ROOT, "profiles", "traffic_%s_w%d.txt" % (kernel, workload))
+    tag = "" if mode is None else "_" + mode
+    path = os.path.join(ROOT, "profiles", "traffic_%s%s_w%d.txt" % (kernel, tag, workload))
     if not os.path.exists(path):
         return None
     vals = {}
@@ -122,6 +123,22 @@ def algorithmic_bytes(p, y_bytes):
     n += p.A.size * 4 + (p.D.size * 4 if p.D is not None else 0)
     n += p.delta_bias.size * 4 if p.delta_bias is not None else 0
     return n
+
+
+def copy_calibration(args, dev):
+    """A plain streaming kernel of known size: the elementwise multiply reads and writes
+    copy_calibration * 10^6 bytes per launch (its own kernel name in the profile)."""
+    import torch
+
+    if not args.copy_calibration:
+        return
+    n = args.copy_calibration * 1000000 // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def decode_bench(args, p, to_dev, dev):
@@ -259,6 +276,62 @@ def backward_bench(args, p, to_dev, dev):
     print(json.dumps(out))
 
 
+def conv_bench(args, p, to_dev, dev):
+    """ss_conv1d (causal depthwise convolution, silu on, W taps) on the workload's scan input
+    shape: x = the workload's u (bf16 or f32), f32 taps and bias drawn as in the tests, out in
+    the input dtype (the scan's next input).  It reads x and writes out once, so its roofline is
+    HBM."""
+    import torch
+
+    from selective_state_space_88_amd import inputs
+    from selective_state_space_88_amd.scan import conv1d
+
+    W = args.conv_width
+    c = inputs.random_conv(31, 1, p.channels, 0, W, with_state=False)
+    x = to_dev(p.u)
+    w, b = to_dev(c["w"]), to_dev(c["bias"])
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        conv1d(x, w, b, silu=True, out=out, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    copy_calibration(args, dev)
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = e0.elapsed_time(e1) * 1e-3 / K
+    E = p.batch * p.channels * p.length
+    ib = 2 if p.in_dtype == "bf16" else 4
+    nbytes = 2 * E * ib + p.channels * (W + 1) * 4
+    gbps = nbytes / per / 1e9
+    traffic = stored_traffic("conv1d_kernel", args.workload, kernel_source_digest("conv1d_kernel"),
+                             mode="conv")
+    out_line = {
+        "metric": "causal conv1d elems/s (B*D*L/s), 1 GPU", "value": E * K / wall, "unit": "elems/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "causal depthwise conv (W=%d, bias, silu) on the scan input of %s, out %s"
+                               % (W, p.name, p.in_dtype),
+                   "batch": p.batch, "channels": p.channels, "seq_len": p.length, "width": W,
+                   "kernel": "conv1d_kernel"},
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic, "launch_ms": per * 1e3,
+                     "hbm_algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out_line))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,6 +350,10 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
                          "gradient dy) on the workload instead of the forward (diagonal workloads)")
+    ap.add_argument("--conv", action="store_true",
+                    help="time the causal depthwise convolution in front of the scan (ss_conv1d, silu) "
+                         "on the workload's scan input instead of the scan")
+    ap.add_argument("--conv-width", type=int, default=4, help="taps of --conv (1..8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (10^6 B) per step, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -311,6 +388,9 @@ def main():
     if args.backward:
         backward_bench(args, p, to_dev, dev)
         return
+    if args.conv:
+        conv_bench(args, p, to_dev, dev)
+        return
 
     t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
     y = torch.empty(p.u.shape, dtype=torch.float32, device=dev)
@@ -325,16 +405,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    if args.copy_calibration:
-        # a plain streaming kernel of known size: the elementwise multiply reads and writes
-        # copy_calibration * 10^6 bytes per launch (its own kernel name in the profile)
-        n = args.copy_calibration * 1000000 // 4
-        src = torch.ones(n, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args, dev)
 
     # timed region: K back-to-back steps, bracketed by device synchronisation
     K = args.steps

@@ -1,5 +1,5 @@
 /*
- * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan forward library (libssscan.so).
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan library (libssscan.so).
  *
  * The operation is the S6 selective-scan forward.  For batch b, channel d and time t:
  *
@@ -81,7 +81,7 @@ typedef struct {
 #define SS_ERR_SHAPE (-3)       /* inconsistent shapes */
 #define SS_ERR_STRIDE (-4)      /* innermost stride != 1, or a negative stride */
 #define SS_ERR_FLAGS (-5)       /* unknown flag bits, or SS_Z_GATE_SILU without z */
-#define SS_ERR_UNSUPPORTED (-6) /* valid but unsupported size (N > 128, or > 2^31 steps per row) */
+#define SS_ERR_UNSUPPORTED (-6) /* valid but unsupported size (N > 128, > 2^31 steps per row, conv width > 8) */
 #define SS_ERR_ALIAS (-7)       /* an output (y, a final state) overlaps an input or another output */
 #define SS_ERR_HIP (-8)         /* a HIP runtime call failed (launch, workspace allocation) */
 
@@ -199,6 +199,47 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
                 uint32_t flags, const ss_tensor* dy, ss_tensor* du, ss_tensor* ddelta, ss_tensor* dA,
                 ss_tensor* dB, ss_tensor* dC, ss_tensor* dD, ss_tensor* dz, ss_tensor* ddelta_bias,
                 void* stream);
+
+/* flags of ss_conv1d */
+#define SS_CONV_SILU (1u << 0) /* out = out * sigmoid(out) */
+
+/*
+ * ss_conv1d -- causal depthwise convolution along time: the short convolution that each Mamba
+ * block applies to the scan's input before the selective SSM, adding local context (bqwf.cn
+ * state-space survey, section 3.1; the omica.com.cn explainer, section 6.3, places it before the
+ * SSM in Mamba-1 and -2, which the trapezoidal rule of SS_TRAPEZOID makes unnecessary); in
+ * decoding the block keeps the last inputs as a state next to the SSM's (the "Mamba -- selective
+ * state space model" study notes, pitfalls).  For batch b,
+ * channel d and time t, with the inputs before t = 0 taken from state_in (zero without it):
+ *
+ *   out[b, d, t] = bias[d] + sum_{j=0}^{W-1} weight[d, j] * x[b, d, t - (W-1) + j]
+ *   out[b, d, t] *= sigmoid(out[b, d, t])                             if SS_CONV_SILU
+ *
+ * (weight[d, W-1] multiplies the newest input).  The pages give no width, padding or activation:
+ * a causal window of W taps per channel, the inputs before the sequence taken as zero, and silu
+ * as an option are the reading taken.
+ *
+ *   x          [batch, channels, L]          f32 | bf16
+ *   weight     [channels, W] f32             W = 1..8 (larger: SS_ERR_UNSUPPORTED; so is
+ *                                            batch * channels * ceil(L / 8) >= 2^32 - 256)
+ *   bias       [channels] f32                optional (NULL or data == NULL)
+ *   state_in   [batch, channels, W-1] f32    optional: x at t = -(W-1) .. -1, oldest first
+ *   state_out  [batch, channels, W-1] f32    optional: written with the last W - 1 inputs of
+ *                                            state_in followed by x (so the next call continues
+ *                                            the sequence; with L < W - 1 part of it comes from
+ *                                            state_in).  Must not overlap any other tensor,
+ *                                            state_in included (SS_ERR_ALIAS): use two buffers
+ *                                            in turn.
+ *   flags      SS_CONV_SILU
+ *   out        [batch, channels, L]          f32 | bf16, written; must not overlap an input
+ *
+ * The arithmetic is f32 (bf16 inputs widened exactly; out in bf16 rounded once), the taps summed
+ * from the newest input back, so a sequence convolved in pieces with the state carried gives
+ * bitwise the out of one call.  L = 0 (state_out = state_in) and batch * channels = 0 are
+ * valid.  No workspace.  Errors, ownership and asynchrony as in ss_scan_fwd.
+ */
+int ss_conv1d(const ss_tensor* x, const ss_tensor* weight, const ss_tensor* bias, const ss_tensor* state_in,
+              ss_tensor* state_out, uint32_t flags, ss_tensor* out, void* stream);
 
 /* Synchronises `stream` and returns SS_OK, or SS_ERR_HIP if any enqueued work failed. */
 int ss_check(void* stream);

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssscan.so")
-SOURCES = ["ss_api.hip", "ss_diag.hip", "ss_scalar.hip", "ss_ssd.hip", "ss_step.hip", "ss_bwd.hip"]
+SOURCES = ["ss_api.hip", "ss_diag.hip", "ss_scalar.hip", "ss_ssd.hip", "ss_step.hip", "ss_bwd.hip",
+           "ss_conv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -69,7 +69,8 @@ const char* ss_strerror(int code) {
     case SS_ERR_SHAPE: return "inconsistent tensor shapes";
     case SS_ERR_STRIDE: return "innermost stride must be 1 and strides non-negative";
     case SS_ERR_FLAGS: return "unknown flag bits, or SS_Z_GATE_SILU without z";
-    case SS_ERR_UNSUPPORTED: return "unsupported size (N must be 1..128; at most 2^31 steps per row)";
+    case SS_ERR_UNSUPPORTED:
+      return "unsupported size (N must be 1..128; at most 2^31 steps per row; conv width 1..8)";
     case SS_ERR_ALIAS: return "an output (y, a final state) overlaps an input or another output";
     case SS_ERR_HIP: return "HIP runtime error";
     default: return "unknown error code";
@@ -497,6 +498,62 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   const hipError_t e = ss::launch_bwd(a, static_cast<float*>(ws), s);
   const hipError_t f = hipFreeAsync(ws, s);
   return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
+}
+
+int ss_conv1d(const ss_tensor* x, const ss_tensor* weight, const ss_tensor* bias, const ss_tensor* state_in,
+              ss_tensor* state_out, uint32_t flags, ss_tensor* out, void* stream) {
+  if (!x || !weight || !out) return SS_ERR_NULL;
+  if (flags & ~(uint32_t)SS_CONV_SILU) return SS_ERR_FLAGS;
+  int rc;
+  if ((rc = check_basic(x, 3)) || (rc = check_basic(out, 3)) || (rc = check_basic(weight, 2))) return rc;
+  if (present(bias) && (rc = check_basic(bias, 1))) return rc;
+  if (weight->dtype != SS_F32 || (present(bias) && bias->dtype != SS_F32)) return SS_ERR_DTYPE;
+  const int64_t Bt = x->shape[0], Dc = x->shape[1], L = x->shape[2], W = weight->shape[1];
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != x->shape[i]) return SS_ERR_SHAPE;
+  if (weight->shape[0] != Dc || W < 1) return SS_ERR_SHAPE;
+  if (present(bias) && bias->shape[0] != Dc) return SS_ERR_SHAPE;
+  if (W > 8) return SS_ERR_UNSUPPORTED;
+  if (present(state_in) && (rc = check_state(state_in, Bt, Dc, W - 1))) return rc;
+  if (present(state_out) && (rc = check_state(state_out, Bt, Dc, W - 1))) return rc;
+  if (Bt * Dc == 0) return SS_OK;
+  // one thread per 8 steps of a row, in a one-dimensional grid (below 2^32 threads)
+  if ((L + 7) / 8 > (((int64_t)1 << 32) - 256) / (Bt * Dc)) return SS_ERR_UNSUPPORTED;
+  if ((L > 0 && (!x->data || !out->data)) || (Dc > 0 && !weight->data)) return SS_ERR_NULL;
+  if (present(bias) && bias->stride[0] != 1 && bias->shape[0] > 1) return SS_ERR_STRIDE;
+  // out and state_out are written: neither may overlap an input or the other
+  const ss_tensor* ins[] = {x, weight, bias, state_in};
+  for (const ss_tensor* t : ins)
+    if (overlaps(out, t) || overlaps(state_out, t)) return SS_ERR_ALIAS;
+  if (overlaps(out, state_out)) return SS_ERR_ALIAS;
+  const bool has_in = present(state_in) && W > 1, has_out = present(state_out) && W > 1;
+  if (L == 0 && !has_out) return SS_OK;
+
+  ss::ConvArgs a{};
+  a.x = x->data;
+  a.w = static_cast<const float*>(weight->data);
+  a.bias = present(bias) ? static_cast<const float*>(bias->data) : nullptr;
+  a.state_in = has_in ? static_cast<const float*>(state_in->data) : nullptr;
+  a.state_out = has_out ? static_cast<float*>(state_out->data) : nullptr;
+  a.out = out->data;
+  a.batch = Bt;
+  a.channels = Dc;
+  a.L = L;
+  a.W = (int32_t)W;
+  a.silu = (flags & SS_CONV_SILU) ? 1 : 0;
+  a.x_bf16 = x->dtype == SS_BF16;
+  a.out_bf16 = out->dtype == SS_BF16;
+  a.vec = L > 0 && aligned16(x) && aligned16(out);
+  a.x_sb = x->stride[0];
+  a.x_sd = x->stride[1];
+  a.o_sb = out->stride[0];
+  a.o_sd = out->stride[1];
+  a.w_sd = weight->stride[0];
+  a.si_sb = has_in ? state_in->stride[0] : 0;
+  a.si_sd = has_in ? state_in->stride[1] : 0;
+  a.so_sb = has_out ? state_out->stride[0] : 0;
+  a.so_sd = has_out ? state_out->stride[1] : 0;
+  return ss::launch_conv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 }  // extern "C"

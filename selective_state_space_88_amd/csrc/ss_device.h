@@ -27,6 +27,14 @@ __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
 
 // f32 -> bf16, round to nearest even (NaN stays a quiet NaN).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+
+// two f32 -> two bf16 (round to nearest even), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2));
+}
+
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
@@ -106,10 +114,10 @@ __device__ __forceinline__ void store_seg(bf16_t* __restrict__ p, int64_t t0, in
 #pragma unroll
     for (int i = 0; i < K / 8; ++i) {
       u32x4 w;
-      w.x = f32_to_bf16_bits(v[8 * i + 0]) | (f32_to_bf16_bits(v[8 * i + 1]) << 16);
-      w.y = f32_to_bf16_bits(v[8 * i + 2]) | (f32_to_bf16_bits(v[8 * i + 3]) << 16);
-      w.z = f32_to_bf16_bits(v[8 * i + 4]) | (f32_to_bf16_bits(v[8 * i + 5]) << 16);
-      w.w = f32_to_bf16_bits(v[8 * i + 6]) | (f32_to_bf16_bits(v[8 * i + 7]) << 16);
+      w.x = pk_bf16(v[8 * i + 0], v[8 * i + 1]);
+      w.y = pk_bf16(v[8 * i + 2], v[8 * i + 3]);
+      w.z = pk_bf16(v[8 * i + 4], v[8 * i + 5]);
+      w.w = pk_bf16(v[8 * i + 6], v[8 * i + 7]);
       __builtin_nontemporal_store(w, q + i);
     }
   } else {

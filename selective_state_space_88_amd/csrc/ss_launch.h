@@ -93,6 +93,26 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t stream);
 hipError_t launch_state_copy(const float* src, int64_t s_sb, int64_t s_sd, float* dst, int64_t d_sb,
                              int64_t d_sd, int64_t batch, int64_t channels, int64_t N, hipStream_t stream);
 
+// Arguments of a causal depthwise convolution along time, already validated.  Strides in
+// elements, time stride 1.
+struct ConvArgs {
+  const void* x;          // [batch, channels, L]
+  const float* w;         // [channels, W]
+  const float* bias;      // nullable, [channels]
+  const float* state_in;  // nullable, [batch, channels, W - 1]: x_{-(W-1)} .. x_{-1}
+  float* state_out;       // nullable, [batch, channels, W - 1]: the last W - 1 inputs
+  void* out;              // [batch, channels, L]
+  int64_t batch, channels, L;
+  int32_t W;              // 1 .. 8
+  int32_t silu, x_bf16, out_bf16;
+  int32_t vec;            // x and out rows 16-byte aligned
+  int64_t x_sb, x_sd, o_sb, o_sd, w_sd, si_sb, si_sd, so_sb, so_sd;
+  int64_t pieces, total;  // set by launch_conv: 8-step pieces per row, and in all
+};
+
+// out_t = bias + sum_j w[j] x_{t-(W-1)+j} (optionally silu) for every (batch, channel) row.
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+
 // Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time.  One
 // kernel, no workspace.
 hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);

@@ -51,13 +51,6 @@ __host__ __device__ inline int64_t rec_bytes(int Np) { return (int64_t)kT * kT *
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-
-// two f32 -> two bf16 (round to nearest even), one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2v{a, b}, bf16x2));
-}
 
 // x = hi + lo, both bf16 (round to nearest even), for eight values; the conversions go in
 // pairs (converting the elements one by one takes one instruction each)

@@ -249,3 +249,19 @@ def step_slice(p: Problem, t: int) -> Problem:
 def seeded_normal(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     """float32 ~ N(0, scale^2) of the given shape (e.g. the upstream gradient dy of a backward)."""
     return (scale * np.random.default_rng(seed).standard_normal(shape)).astype(np.float32)
+
+
+def random_conv(seed: int, batch: int, channels: int, length: int, width: int, *, in_dtype: str = "bf16",
+                with_bias: bool = True, with_state: bool = True) -> dict:
+    """Inputs of the causal depthwise convolution in front of the scan: x [batch, channels, L] ~ N(0, 1)
+    (encoded as ``in_dtype``), weight [channels, W] and bias [channels] ~ U(-1/sqrt(W), 1/sqrt(W))
+    (the usual fan-in initialisation of a depthwise convolution), and a state [batch, channels, W - 1]
+    ~ N(0, 1) float32 (the inputs before the sequence).  Drawn in that order from
+    ``numpy.random.default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    x = _normal(rng, (batch, channels, length), 1.0, in_dtype)
+    bound = 1.0 / np.sqrt(width)
+    w = rng.uniform(-bound, bound, size=(channels, width)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=channels).astype(np.float32) if with_bias else None
+    state = rng.standard_normal((batch, channels, width - 1), dtype=np.float32) if with_state else None
+    return dict(x=x, w=w, bias=bias, state=state)

@@ -20,8 +20,9 @@ SS_DELTA_SOFTPLUS = 1 << 0
 SS_Z_GATE_SILU = 1 << 1
 SS_ZOH = 1 << 2
 SS_TRAPEZOID = 1 << 3
-EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_check", "ss_strerror",
-           "ss_version")
+SS_CONV_SILU = 1 << 0   # flag of ss_conv1d
+EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_conv1d", "ss_check",
+           "ss_strerror", "ss_version")
 
 
 class SSTensor(ctypes.Structure):
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         l.ss_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, P, P, P, P, P, P,
                                   ctypes.c_void_p]
         l.ss_scan_bwd.restype = ctypes.c_int
+        l.ss_conv1d.argtypes = [P, P, P, P, P, ctypes.c_uint32, P, ctypes.c_void_p]
+        l.ss_conv1d.restype = ctypes.c_int
         l.ss_check.argtypes = [ctypes.c_void_p]
         l.ss_check.restype = ctypes.c_int
         l.ss_strerror.argtypes = [ctypes.c_int]
@@ -210,3 +213,29 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     if rc != 0:
         raise ScanError(rc, strerror(rc))
     return g
+
+
+def call_conv(x, weight, bias, state_in, state_out, flags: int, out, stream) -> int:
+    """Raw ss_conv1d call with descriptors (or None); returns the library's code."""
+    return lib().ss_conv1d(_ref(x), _ref(weight), _ref(bias), _ref(state_in), _ref(state_out),
+                           ctypes.c_uint32(flags), _ref(out), ctypes.c_void_p(stream or 0))
+
+
+def conv1d(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None, *,
+           state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+           silu: bool = False, out: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+           stream: Optional[int] = None) -> torch.Tensor:
+    """Causal depthwise convolution through ss_conv1d: x [batch, channels, L], weight [channels, W]
+    (float32, W <= 8), bias [channels]; state_in / state_out [batch, channels, W - 1] float32 hold
+    the inputs before the sequence / receive its last W - 1 inputs.  Returns out [batch, channels, L]
+    (silu applied when ``silu``)."""
+    _check_cuda(x, weight, bias, state_in, state_out)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = call_conv(describe(x), describe(weight), describe(bias), describe(state_in), describe(state_out),
+                   SS_CONV_SILU if silu else 0, describe(out), stream)
+    if rc != 0:
+        raise ScanError(rc, strerror(rc))
+    return out

@@ -343,3 +343,91 @@ def test_step_dtype_stride_alias_and_sizes():
     assert call_step(p) == -6
     p = step_problem(Bt=0)
     assert call_step(p) == 0
+
+
+def conv_problem(Bt=2, Dc=8, L=32, W=4, dtype=scan.SS_BF16, base=FAKE, states=True):
+    step = 1 << 24
+    return dict(
+        x=T([Bt, Dc, L], dtype, base),
+        w=T([Dc, W], scan.SS_F32, base + step),
+        bias=T([Dc], scan.SS_F32, base + 2 * step),
+        si=T([Bt, Dc, W - 1], scan.SS_F32, base + 3 * step) if states else None,
+        so=T([Bt, Dc, W - 1], scan.SS_F32, base + 4 * step) if states else None,
+        flags=scan.SS_CONV_SILU,
+        out=T([Bt, Dc, L], dtype, base + 5 * step),
+    )
+
+
+def call_conv(p):
+    return scan.call_conv(p["x"], p["w"], p["bias"], p["si"], p["so"], p["flags"], p["out"], None)
+
+
+def test_conv_null_flags_and_dtypes():
+    for k in ("x", "w", "out"):
+        p = conv_problem()
+        p[k] = None
+        assert call_conv(p) == -1, k
+    p = conv_problem()
+    p["x"].data = None
+    assert call_conv(p) == -1
+    p = conv_problem()
+    p["flags"] = 1 << 1
+    assert call_conv(p) == -5
+    for k in ("w", "bias", "si", "so"):
+        p = conv_problem()
+        p[k].dtype = scan.SS_BF16
+        assert call_conv(p) == -2, k
+
+
+@pytest.mark.parametrize("what", ["out_L", "out_rank", "w_channels", "w_zero_width", "bias", "si", "so"])
+def test_conv_shape_errors(what):
+    p = conv_problem()
+    if what == "out_L":
+        p["out"] = T([2, 8, 31], scan.SS_BF16, p["out"].data)
+    elif what == "out_rank":
+        p["out"] = T([2, 8, 32, 1], scan.SS_BF16, p["out"].data)
+    elif what == "w_channels":
+        p["w"] = T([7, 4], scan.SS_F32, p["w"].data)
+    elif what == "w_zero_width":
+        p["w"] = T([8, 0], scan.SS_F32, p["w"].data)
+    elif what == "bias":
+        p["bias"] = T([4], scan.SS_F32, p["bias"].data)
+    elif what == "si":
+        p["si"] = T([2, 8, 4], scan.SS_F32, p["si"].data)
+    else:
+        p["so"] = T([2, 8, 2], scan.SS_F32, p["so"].data)
+    assert call_conv(p) == -3
+
+
+def test_conv_stride_alias_and_sizes():
+    p = conv_problem()
+    p["x"] = T([2, 8, 32], scan.SS_BF16, p["x"].data, stride=[512, 64, 2])
+    assert call_conv(p) == -4
+    p = conv_problem()
+    p["w"] = T([8, 4], scan.SS_F32, p["w"].data, stride=[8, 2])
+    assert call_conv(p) == -4
+    p = conv_problem()
+    p["out"].data = p["x"].data + 64
+    assert call_conv(p) == -7
+    p = conv_problem()
+    p["so"].data = p["si"].data   # the state is not updated in place
+    assert call_conv(p) == -7
+    p = conv_problem()
+    p["so"].data = p["out"].data
+    assert call_conv(p) == -7
+    p = conv_problem(W=9)
+    assert call_conv(p) == -6
+    p = conv_problem(Bt=1 << 20, Dc=1 << 12, L=64)   # more than 2^32 threads of 8 steps
+    assert call_conv(p) == -6
+
+
+def test_conv_empty_problems_are_noops():
+    assert call_conv(conv_problem(Bt=0)) == 0
+    assert call_conv(conv_problem(Dc=0)) == 0
+    # L = 0 without a state to write: nothing to do, even with NULL data
+    p = conv_problem(L=0, states=False)
+    p["x"].data = None
+    p["out"].data = None
+    assert call_conv(p) == 0
+    # W = 1 has an empty state: L = 0 stays a no-op
+    assert call_conv(conv_problem(L=0, W=1)) == 0

@@ -1,0 +1,163 @@
+"""The causal depthwise convolution (ss_conv1d) on the GPU against the oracle's float64
+convolution: every width 1..8, bf16 and f32 inputs and outputs, with and without bias, silu and
+the carried state, ragged lengths, strided (unaligned) rows, the state out, and sampled rows of the
+full-size layer.  A sequence convolved in pieces with the state carried must equal one call bitwise.
+
+Bar: per element |out - ref| <= 1.1 (W + 2) 2^-23 S + 8 2^-23 |ref| (+ 2^-8 |ref| for a bf16 out), with
+S = |bias| + sum_j |w_j x_j| (the oracle on absolute values): W + 1 f32 roundings of a chain of fused
+multiply-adds (each at most 2^-24 of the running magnitude, which S bounds), a factor below 1.1 for
+silu's slope, a few units in the last place of its exp2 and reciprocal, and one bf16 rounding of the
+output (half a unit of 2^-8)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import say, to_dev, torch_dev
+from selective_state_space_88_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -23
+
+
+def expected(c, silu, state=True, bias=True):
+    x = c["x"]
+    st = c["state"] if (state and c["state"] is not None) else None
+    b = c["bias"] if (bias and c["bias"] is not None) else None
+    out, so = oracle.conv1d(x, c["w"], b, state=st, silu=silu, return_state=True)
+    xa = np.abs(inputs.to_f32(x).astype(np.float64))
+    S = oracle.conv1d(xa, np.abs(c["w"]), None if b is None else np.abs(b),
+                      state=None if st is None else np.abs(st))
+    return out, so, S
+
+
+def check(got, ref, S, W, bf16_out):
+    bound = 1.1 * (W + 2) * EPS * S + 8 * EPS * np.abs(ref)
+    if bf16_out:
+        bound = bound + 2.0 ** -8 * np.abs(ref)
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(bound, 1e-300))) if err.size else 0.0
+    assert np.all(err <= bound), "max err/bound %.3f" % worst
+    return worst
+
+
+def run(c, silu, state=True, bias=True, out_dtype=None, state_out=True):
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import conv1d
+
+    x = to_dev(c["x"])
+    W = c["w"].shape[1]
+    si = to_dev(c["state"]) if (state and c["state"] is not None) else None
+    so = torch.full((x.shape[0], x.shape[1], W - 1), float("nan"), device="cuda") if state_out else None
+    out = conv1d(x, to_dev(c["w"]), to_dev(c["bias"]) if bias else None, state_in=si, state_out=so, silu=silu,
+                 out_dtype=out_dtype or torch.float32)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), (None if so is None else so.cpu().numpy())
+
+
+@pytest.mark.parametrize("W", range(1, 9))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_every_width(W, dtype):
+    c = inputs.random_conv(900 + W, 2, 24, 333, W, in_dtype=dtype)
+    for silu in (False, True):
+        got, so = run(c, silu)
+        ref, rso, S = expected(c, silu)
+        worst = check(got, ref, S, W, False)
+        np.testing.assert_array_equal(so, rso.astype(np.float32))
+        say("[conv] W=%d %s silu=%d: err/bound %.3f" % (W, dtype, silu, worst))
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 7, 8, 9, 63, 64, 65, 511, 2049])
+def test_conv_ragged_lengths(L):
+    """Lengths around the 8-step pieces and the 64-lane waves (pieces of neighbouring rows share a
+    wave); the state reaches into state_in when L < W - 1."""
+    torch = torch_dev()
+    c = inputs.random_conv(950 + L, 3, 7, L, 6)
+    got, so = run(c, True, out_dtype=torch.bfloat16)
+    ref, rso, S = expected(c, True)
+    check(got, ref, S, 6, True)
+    np.testing.assert_array_equal(so, rso.astype(np.float32))
+
+
+@pytest.mark.parametrize("bias,state", [(False, False), (True, False), (False, True)])
+def test_conv_optional_inputs(bias, state):
+    c = inputs.random_conv(970, 2, 16, 200, 4, in_dtype="f32")
+    got, so = run(c, False, state=state, bias=bias)
+    ref, rso, S = expected(c, False, state=state, bias=bias)
+    check(got, ref, S, 4, False)
+    np.testing.assert_array_equal(so, rso.astype(np.float32))
+
+
+def test_conv_strided_unaligned_rows():
+    """x and out as views with odd row strides and offsets (no 16-byte vector access)."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import conv1d
+
+    c = inputs.random_conv(971, 2, 10, 101, 4)
+    big = torch.zeros((2, 10, 107), dtype=torch.bfloat16, device="cuda")
+    x = big[:, :, 3:104]
+    x.copy_(to_dev(c["x"]))
+    obig = torch.full((2, 11, 103), float("nan"), device="cuda")
+    out = obig[:, 1:, 1:102]
+    conv1d(x, to_dev(c["w"]), to_dev(c["bias"]), state_in=to_dev(c["state"]), silu=True, out=out)
+    torch.cuda.synchronize()
+    ref, _, S = expected(c, True)
+    check(out.cpu().numpy().astype(np.float64), ref, S, 4, False)
+    # nothing outside the view was written
+    assert torch.isnan(obig[:, 0]).all() and torch.isnan(obig[:, :, 0]).all() and torch.isnan(obig[:, :, 102:]).all()
+
+
+@pytest.mark.parametrize("W", [2, 4, 8])
+def test_conv_pieces_and_tokens_bitwise(W):
+    """A sequence convolved in uneven pieces, then token by token (decoding), with the state carried in
+    two buffers used in turn, equals one call on the whole sequence bitwise."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import conv1d
+
+    c = inputs.random_conv(980 + W, 2, 40, 300, W)
+    x = to_dev(c["x"])
+    w, b = to_dev(c["w"]), to_dev(c["bias"])
+    s0 = to_dev(c["state"])
+    full = conv1d(x, w, b, state_in=s0, silu=True)
+    cuts = [0, 1, 5, 64, 130, 200] + list(range(201, 211)) + [300]
+    bufs = [torch.empty_like(s0), torch.empty_like(s0)]
+    st, outs = s0, []
+    for i in range(len(cuts) - 1):
+        nxt = bufs[i % 2]
+        outs.append(conv1d(x[:, :, cuts[i]:cuts[i + 1]].contiguous(), w, b, state_in=st, state_out=nxt, silu=True))
+        st = nxt
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs, -1), full)
+    assert torch.equal(st, x[:, :, 300 - (W - 1):].float())
+
+
+def test_conv_empty_length_passes_the_state_through():
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import conv1d
+
+    c = inputs.random_conv(990, 2, 5, 0, 5)
+    so = torch.full((2, 5, 4), float("nan"), device="cuda")
+    out = conv1d(to_dev(c["x"]), to_dev(c["w"]), state_in=to_dev(c["state"]), state_out=so)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 5, 0)
+    np.testing.assert_array_equal(so.cpu().numpy(), c["state"])
+    so.fill_(float("nan"))
+    conv1d(to_dev(c["x"]), to_dev(c["w"]), state_out=so)
+    torch.cuda.synchronize()
+    assert (so.cpu().numpy() == 0).all()
+
+
+def test_conv_full_size_layer_sampled_rows():
+    """The 130M-class layer (batch 8, 1536 channels, L 2048, bf16, W = 4, silu) in the launch the
+    benchmark times; 48 sampled rows against the oracle (rows are independent)."""
+    torch = torch_dev()
+    c = inputs.random_conv(1001, 8, 1536, 2048, 4, with_state=False)
+    got, _ = run(c, True, state=False, out_dtype=torch.bfloat16, state_out=False)
+    rng = np.random.default_rng(7)
+    flat = rng.choice(8 * 1536, size=48, replace=False)
+    rows = (flat // 1536, flat % 1536)
+    # the sampled rows as one batch of 48 channels, each with its own taps and bias
+    sample = dict(x=c["x"][rows][None], w=c["w"][rows[1]], bias=c["bias"][rows[1]], state=None)
+    ref, _, S = expected(sample, True, state=False)
+    worst = check(got[rows][None], ref, S, 4, True)
+    say("[conv] full-size layer, 48 sampled rows: err/bound %.3f" % worst)
