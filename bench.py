@@ -212,8 +212,9 @@ def decode_bench(args, p, to_dev, dev):
 # and dt*A (1), dt*u*B (1), the recomputed state FMA (2), the adjoint FMA (2) and its decay
 # product (1), dC (1), dB (1), du (2), ddt (4: two FMAs), dA (2: multiply, FMA) = 25; per
 # element the forward's per-step terms (softplus, gate, D) and their derivatives (~2x).
-def bwd_flop_equiv_per_element(N, softplus, gate):
-    per = 25.0 * N + 2 * 3.0
+def bwd_flop_equiv_per_element(N, softplus, gate, scalar_decay=False):
+    # scalar decay: the exp and dt*A are per step, not per (t, n)
+    per = (16.0 * N + TRANS + 1.0 if scalar_decay else 25.0 * N) + 2 * 3.0
     if softplus:
         per += 2 * (2 * TRANS + 4.0)
     if gate:
@@ -229,9 +230,6 @@ def backward_bench(args, p, to_dev, dev):
     from selective_state_space_88_amd import inputs
     from selective_state_space_88_amd.scan import scan_bwd
 
-    if p.scalar_decay:
-        print("the backward covers the diagonal workloads (0-3)", file=sys.stderr)
-        sys.exit(2)
     t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
     dy = to_dev(inputs.seeded_normal(12, (p.batch, p.channels, p.length)))
     stream = torch.cuda.current_stream(dev)
@@ -255,10 +253,11 @@ def backward_bench(args, p, to_dev, dev):
     wall = time.perf_counter() - t0
     per = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])) * 1e-3
     E = p.batch * p.channels * p.length
-    flops = E * bwd_flop_equiv_per_element(p.nstate, p.softplus, p.gate)
+    flops = E * bwd_flop_equiv_per_element(p.nstate, p.softplus, p.gate, p.scalar_decay)
     ib = 2 if p.in_dtype == "bf16" else 4
-    # reads u, delta, z, dy (f32), B, C; writes du, ddelta, dz (f32) and dB, dC (f32)
-    nbytes = E * (ib * (3 if p.gate else 2) + 4 + 4 * (3 if p.gate else 2))
+    # reads u, z, dy (f32), delta, B, C; writes du, dz, ddelta (f32) and dB, dC (f32)
+    nbytes = E * (ib * (2 if p.gate else 1) + 4 + 4 * (2 if p.gate else 1))
+    nbytes += p.batch * p.heads * p.length * (ib + 4)
     nbytes += p.batch * p.groups * p.nstate * p.length * 2 * (ib + 4)
     tf = flops / per / 1e12
     out = {
@@ -349,7 +348,7 @@ def main():
                     help="exponential-trapezoidal rule (SS_TRAPEZOID) instead of exponential-Euler")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
-                         "gradient dy) on the workload instead of the forward (diagonal workloads)")
+                         "gradient dy) on the workload instead of the forward")
     ap.add_argument("--conv", action="store_true",
                     help="time the causal depthwise convolution in front of the scan (ss_conv1d, silu) "
                          "on the workload's scan input instead of the scan")

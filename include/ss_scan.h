@@ -175,24 +175,25 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * ddelta_t = ddt_t sigmoid(delta_t + bias) with softplus (ddt_t without),  dbias = sum ddelta,
  * dD = sum dy0_t u_t,  dz_t = dy_t y0_t s'(z_t)  (y0: the output before the gate).
  *
- *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd, restricted to the diagonal
- *              decay with one step size per channel: A [channels, N], delta [batch, channels, L],
- *              without SS_ZOH or SS_TRAPEZOID (anything else: SS_ERR_UNSUPPORTED), and
- *              channels / groups a multiple of 4
+ *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd (diagonal A [channels, N] or
+ *              scalar A [heads], delta per channel or per head), without SS_ZOH or SS_TRAPEZOID
+ *              (SS_ERR_UNSUPPORTED), and channels / groups a multiple of 4 (SS_ERR_UNSUPPORTED)
  *   dy         [batch, channels, L]          f32 | bf16: the gradient of the loss at y
  *   du         [batch, channels, L] f32      written
- *   ddelta     [batch, channels, L] f32      written (the gradient of the raw delta)
- *   dA         [channels, N] f32             written
+ *   ddelta     [batch, heads, L] f32         written (the gradient of the raw delta; summed over
+ *                                            the head's channels)
+ *   dA         f32, the shape of A           written (scalar decay: summed over the head's channels
+ *                                            and states)
  *   dB, dC     [batch, groups, N, L] f32     written (summed over each group's channels)
- *   dD         [channels] f32                written; required exactly when D is given
+ *   dD         f32, the shape of D           written; required exactly when D is given
  *   dz         [batch, channels, L] f32      written; required exactly with SS_Z_GATE_SILU
- *   ddelta_bias [channels] f32               optional: written when given
+ *   ddelta_bias [heads] f32                  optional: written when given
  *
  * Every gradient is f32 with innermost stride 1 and must not overlap an input or another
  * gradient (SS_ERR_ALIAS).  The state starts at zero.  Sums over channels and over the batch
- * (dA, dB, dC, dD, dbias) are accumulated with atomic adds, so their last bits may differ from
- * run to run; everything else is deterministic.  Errors, ownership and asynchrony as in
- * ss_scan_fwd.
+ * (dA, dB, dC, dD, dbias, and ddelta when a head has several channels) are accumulated with
+ * atomic adds, so their last bits may differ from run to run; everything else is deterministic.
+ * Errors, ownership and asynchrony as in ss_scan_fwd.
  */
 int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,

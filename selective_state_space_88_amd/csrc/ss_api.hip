@@ -384,26 +384,29 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
     if (C->shape[i] != B->shape[i]) return SS_ERR_SHAPE;
   for (int i = 0; i < 3; ++i)
     if (dy->shape[i] != u->shape[i] || (gate && z->shape[i] != u->shape[i])) return SS_ERR_SHAPE;
-  if (G <= 0 || (Dc > 0 && Dc % G)) return SS_ERR_SHAPE;
-  // the backward covers the diagonal decay with one step size per channel (Mamba-1 layout), with
-  // the exponential-Euler rule
-  if (A->ndim != 2 || H != Dc || (flags & (SS_ZOH | SS_TRAPEZOID))) return SS_ERR_UNSUPPORTED;
-  if (A->shape[0] != Dc || A->shape[1] != N) return SS_ERR_SHAPE;
-  if (present(D) && D->shape[0] != Dc) return SS_ERR_SHAPE;
-  if (present(delta_bias) && delta_bias->shape[0] != Dc) return SS_ERR_SHAPE;
+  if (H <= 0 || G <= 0 || (Dc > 0 && (Dc % G || Dc % H))) return SS_ERR_SHAPE;
+  const bool scalar = A->ndim == 1;
+  if (scalar ? A->shape[0] != H : (A->shape[0] != Dc || A->shape[1] != N)) return SS_ERR_SHAPE;
+  if (present(D) && D->shape[0] != Dc && D->shape[0] != H) return SS_ERR_SHAPE;
+  if (present(delta_bias) && delta_bias->shape[0] != H) return SS_ERR_SHAPE;
+  // the backward is written for the exponential-Euler rule
+  if (flags & (SS_ZOH | SS_TRAPEZOID)) return SS_ERR_UNSUPPORTED;
   if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
   if (L > ((int64_t)1 << 31)) return SS_ERR_UNSUPPORTED;
   if (Dc > 0 && (Dc / G) % 4) return SS_ERR_UNSUPPORTED;
   if (dy->dtype != SS_F32 && dy->dtype != SS_BF16) return SS_ERR_DTYPE;
-  const int64_t s_x[3] = {Bt, Dc, L}, s_bc[4] = {Bt, G, N, L}, s_a[2] = {Dc, N}, s_d[1] = {Dc};
-  if ((rc = check_grad(du, 3, s_x)) || (rc = check_grad(ddelta, 3, s_x)) || (rc = check_grad(dA, 2, s_a)) ||
-      (rc = check_grad(dB, 4, s_bc)) || (rc = check_grad(dC, 4, s_bc)))
+  const int64_t nD = present(D) ? D->shape[0] : Dc;
+  const int64_t s_x[3] = {Bt, Dc, L}, s_dl[3] = {Bt, H, L}, s_bc[4] = {Bt, G, N, L}, s_a[2] = {Dc, N}, s_h[1] = {H},
+                s_d[1] = {nD};
+  if ((rc = check_grad(du, 3, s_x)) || (rc = check_grad(ddelta, 3, s_dl)) ||
+      (rc = scalar ? check_grad(dA, 1, s_h) : check_grad(dA, 2, s_a)) || (rc = check_grad(dB, 4, s_bc)) ||
+      (rc = check_grad(dC, 4, s_bc)))
     return rc;
   if (present(D) != given(dD)) return SS_ERR_NULL;   // dD exactly when D is given
   if (gate != given(dz)) return SS_ERR_NULL;         // dz exactly when the gate is on
   if (given(dD) && (rc = check_grad(dD, 1, s_d))) return rc;
   if (given(dz) && (rc = check_grad(dz, 3, s_x))) return rc;
-  if (given(ddelta_bias) && (rc = check_grad(ddelta_bias, 1, s_d))) return rc;
+  if (given(ddelta_bias) && (rc = check_grad(ddelta_bias, 1, s_h))) return rc;
   // outputs overlap neither the inputs nor each other
   const ss_tensor* ins[] = {u, delta, A, B, C, D, z, delta_bias, dy};
   ss_tensor* outs[] = {du, ddelta, dA, dB, dC, dD, dz, ddelta_bias};
@@ -418,8 +421,9 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (L == 0) {
     // no steps: the gradients of A, B, C, D and the bias are zero; du, ddelta, dz are empty
     float* zs[] = {static_cast<float*>(dA->data), present(D) ? static_cast<float*>(dD->data) : nullptr,
-                   present(ddelta_bias) ? static_cast<float*>(ddelta_bias->data) : nullptr};
-    const int64_t rws[] = {Dc, 1, 1}, inn[] = {N, Dc, Dc}, st[] = {dA->stride[0], 0, 0};
+                   given(ddelta_bias) ? static_cast<float*>(ddelta_bias->data) : nullptr};
+    const int64_t rws[] = {scalar ? 1 : Dc, 1, 1}, inn[] = {scalar ? H : N, nD, H},
+                  st[] = {scalar ? 0 : dA->stride[0], 0, 0};
     for (int i = 0; i < 3; ++i)
       if (zs[i] && ss::launch_state_copy(nullptr, 0, 0, zs[i], 0, st[i], 1, rws[i], inn[i], s) != hipSuccess)
         return SS_ERR_HIP;
@@ -428,8 +432,6 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (!u->data || !delta->data || !A->data || !B->data || !C->data || !dy->data) return SS_ERR_NULL;
   if (present(D) && D->stride[0] != 1 && D->shape[0] > 1) return SS_ERR_STRIDE;
   if (present(delta_bias) && delta_bias->stride[0] != 1 && delta_bias->shape[0] > 1) return SS_ERR_STRIDE;
-  if (given(dD) && dD->stride[0] != 1 && Dc > 1) return SS_ERR_STRIDE;
-  if (given(ddelta_bias) && ddelta_bias->stride[0] != 1 && Dc > 1) return SS_ERR_STRIDE;
 
   ss::BwdArgs a{};
   a.u = u->data;
@@ -455,6 +457,10 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   a.N = (int32_t)N;
   a.groups = (int32_t)G;
   a.chan_per_group = (int32_t)(Dc / G);
+  a.heads = (int32_t)H;
+  a.chan_per_head = (int32_t)(Dc / H);
+  a.scalar = scalar ? 1 : 0;
+  a.d_per_head = present(D) && nD != Dc ? 1 : 0;
   a.softplus = (flags & SS_DELTA_SOFTPLUS) ? 1 : 0;
   a.in_bf16 = idt == SS_BF16;
   a.dy_bf16 = dy->dtype == SS_BF16;

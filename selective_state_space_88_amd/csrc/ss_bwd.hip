@@ -1,4 +1,4 @@
-// ss_bwd.hip -- backward of the diagonal selective scan (gradients of every input), gfx950.
+// ss_bwd.hip -- backward of the selective scan (gradients of every input), gfx950.
 //
 // The pages train the scan by recomputing its states instead of storing them (bqwf.cn
 // state-space survey, section 2.2).  Here: a checkpoint pass stores each row's state at the
@@ -11,6 +11,10 @@
 //   ddt_t += g_t (h_{t-1} a_t A + B_t u_t),  dA += g_t h_{t-1} a_t dt_t,
 // and per step dz_t = dy_t y0_t s'(z_t), du_t += dy0_t D, dD += dy0_t u_t,
 // ddelta_t = ddt_t sigmoid(x_t) (softplus'), dbias += ddelta_t.
+//
+// With heads (a step size, and optionally a scalar decay A_h, shared by a head's channels) the
+// per-head gradients ddelta, dbias, dA (and dD when D is per head) are summed over the head's
+// channels; with a scalar decay exp(dt A_h) is computed once per step for all N states.
 //
 // Mapping (as in the forward kernel): a wave owns one channel, lane j the K consecutive steps
 // t0 + jK .. t0 + jK + K - 1 of a window; states go by pairs.  Inside a window both recurrences
@@ -96,7 +100,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Checkpoints: the state of every (row, window, state) at the window's start.
-template <typename TIn>
+template <typename TIn, bool SCALAR>
 __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P, int64_t nwin, float* ckpt) {
   __shared__ float hst[kBWaves][kBMaxPairs][2];
   const int lane = threadIdx.x & 63;
@@ -105,12 +109,12 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
   const bool live = row < p.batch * p.channels;
   const int64_t rr = live ? row : 0;
   const int64_t b = rr / p.channels, d = rr % p.channels;
-  const int64_t g = d / p.chan_per_group;
+  const int64_t g = d / p.chan_per_group, hd = d / p.chan_per_head;
   const int N = p.N;
   const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
-  const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + d * p.dl_sh;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
   const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
-  const float bias = p.bias ? p.bias[d] : 0.f;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
   for (int pp = lane; pp < P; pp += 64) hst[wave][pp][0] = hst[wave][pp][1] = 0.f;
   for (int64_t w = 0; w < nwin; ++w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
@@ -124,19 +128,26 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
       dt[k] = ok ? (p.softplus ? softplus_fast(x) : x) : 0.f;
       wv[k] = dt[k] * uv[k];
     }
+    // scalar decay: one exp per step for every state
+    float ah[kBK];
+    if constexpr (SCALAR) {
+      const float A2 = p.A[hd] * kLog2e;
+#pragma unroll
+      for (int k = 0; k < kBK; ++k) ah[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
+    }
     for (int pp = 0; pp < P; ++pp) {
       float Af[2], Bf[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int n = 2 * pp + s;
         const bool nv = n < N;
-        const float A2 = nv ? p.A[d * p.A_sd + n] * kLog2e : 0.f;
+        const float A2 = (nv && !SCALAR) ? p.A[d * p.A_sd + n] * kLog2e : 0.f;
         float bq[kBK];
         load_seg<kBK>(Bg + (nv ? n : 0) * p.B_sn, t0, nv ? p.L : 0, p.vec, bq);
         float a = 1.f, h = 0.f;
 #pragma unroll
         for (int k = 0; k < kBK; ++k) {
-          const float av = __builtin_amdgcn_exp2f(dt[k] * A2);
+          const float av = SCALAR ? ah[k] : __builtin_amdgcn_exp2f(dt[k] * A2);
           h = fmaf(av, h, wv[k] * bq[k]);
           a *= av;
         }
@@ -160,7 +171,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
   }
 }
 
-template <typename TIn, typename TDy, bool GATE>
+template <typename TIn, typename TDy, bool GATE, bool SCALAR>
 __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int64_t nwin, const float* ckpt) {
   __shared__ float gcar[kBWaves][kBMaxPairs][2];      // adjoint carried into the window from the right
   __shared__ float dAl[kBWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
@@ -173,18 +184,19 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
   const int64_t b = bg / p.groups, g = bg % p.groups;
   const int64_t d = g * p.chan_per_group + qd * kBWaves + wave;
   const int64_t row = b * p.channels + d;
+  const int64_t hd = d / p.chan_per_head;
   const int N = p.N;
   const int64_t L = p.L;
   const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
-  const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + d * p.dl_sh;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
   const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
   const TDy* dyr = static_cast<const TDy*>(p.dy) + b * p.dy_sb + d * p.dy_sd;
   const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
   const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
   float* dBg = p.dB + b * p.dB_sb + g * p.dB_sg;
   float* dCg = p.dC + b * p.dC_sb + g * p.dC_sg;
-  const float bias = p.bias ? p.bias[d] : 0.f;
-  const float Dd = p.D ? p.D[d] : 0.f;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
   for (int i = lane; i < 2 * kBMaxPairs; i += 64) {
     gcar[wave][i / 2][i % 2] = 0.f;
     dAl[wave][i] = 0.f;
@@ -213,6 +225,13 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
       du[k] = dy0[k] * Dd;
       ddt[k] = 0.f;
     }
+    // scalar decay: one exp per step for every state
+    float ah[kBK];
+    if constexpr (SCALAR) {
+      const float A2 = p.A[hd] * kLog2e;
+#pragma unroll
+      for (int k = 0; k < kBK; ++k) ah[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
+    }
     for (int pp = 0; pp < P; ++pp) {
       float rB[2][kBK], rC[2][kBK];
       float dAp[2];
@@ -220,7 +239,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
       for (int s = 0; s < 2; ++s) {
         const int n = 2 * pp + s;
         const bool nv = n < N;
-        const float An = nv ? p.A[d * p.A_sd + n] : 0.f;
+        const float An = SCALAR ? p.A[hd] : (nv ? p.A[d * p.A_sd + n] : 0.f);
         const float A2 = An * kLog2e;
         const TIn* Br = Bg + (nv ? n : 0) * p.B_sn;
         const TIn* Cr = Cg + (nv ? n : 0) * p.C_sn;
@@ -228,7 +247,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         load_seg<kBK>(Br, t0, nv ? L : 0, p.vec, bv);
         load_seg<kBK>(Cr, t0, nv ? L : 0, p.vec, cv);
 #pragma unroll
-        for (int k = 0; k < kBK; ++k) av[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
+        for (int k = 0; k < kBK; ++k) av[k] = SCALAR ? ah[k] : __builtin_amdgcn_exp2f(dt[k] * A2);
         // states: the lane's steps from zero, the scan, then from the incoming state
         float Af = 1.f, Bf = 0.f;
 #pragma unroll
@@ -280,7 +299,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const float v = wave_sum(dAp[s]);
-        if (lane == 0 && 2 * pp + s < N) dAl[wave][2 * pp + s] += v;
+        if (lane == 0 && 2 * pp + s < N) dAl[wave][SCALAR ? 0 : 2 * pp + s] += v;
       }
       // dB, dC of the pair: summed over the block's 4 channels, then one atomic add per step;
       // consecutive lanes add to consecutive steps, so each wave's adds cover two cache lines
@@ -306,13 +325,35 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
     }
     // per-step outputs of the window
     float* dur = p.du + b * p.du_sb + d * p.du_sd;
-    float* ddr = p.ddelta + b * p.dd_sb + d * p.dd_sh;
+    float* ddr = p.ddelta + b * p.dd_sb + hd * p.dd_sh;
+    float dxs[kBK];
+#pragma unroll
+    for (int k = 0; k < kBK; ++k) dxs[k] = t0 + k < L ? ddt[k] * sg[k] : 0.f;
+    if (p.chan_per_head == 1) {
+#pragma unroll
+      for (int k = 0; k < kBK; ++k)
+        if (t0 + k < L) ddr[t0 + k] = dxs[k];
+    } else if (p.chan_per_head % kBWaves == 0) {
+      // the block's 4 channels share the head: summed through LDS, one atomic add per step
+#pragma unroll
+      for (int k = 0; k < kBK; k += 4)
+        *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{dxs[k], dxs[k + 1], dxs[k + 2], dxs[k + 3]};
+      __syncthreads();
+      for (int i = threadIdx.x; i < kBW; i += 64 * kBWaves) {
+        const int64_t t = w * kBW + i;
+        if (t < L) atomicAdd(ddr + t, red[0][0][i] + red[1][0][i] + red[2][0][i] + red[3][0][i]);
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int k = 0; k < kBK; ++k)
+        if (t0 + k < L) atomicAdd(ddr + t0 + k, dxs[k]);
+    }
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
       if (t0 + k < L) {
-        const float dx = ddt[k] * sg[k];
+        const float dx = dxs[k];
         dur[t0 + k] = du[k];
-        ddr[t0 + k] = dx;
         dbacc += dx;
         dDacc = fmaf(dy0[k], uu[k], dDacc);
         if constexpr (GATE) {
@@ -326,10 +367,12 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
   // per-channel sums (over this batch row's steps): dA, dD, dbias, added across the batch
   const float dDs = wave_sum(dDacc), dbs = wave_sum(dbacc);
   if (lane == 0) {
-    if (p.dD) atomicAdd(p.dD + d, dDs);
-    if (p.dbias) atomicAdd(p.dbias + d, dbs);
+    if (p.dD) atomicAdd(p.dD + (p.d_per_head ? hd : d), dDs);
+    if (p.dbias) atomicAdd(p.dbias + hd, dbs);
+    if (SCALAR) atomicAdd(p.dA + hd, dAl[wave][0]);
   }
-  for (int n = lane; n < N; n += 64) atomicAdd(p.dA + d * p.dA_sd + n, dAl[wave][n]);
+  if (!SCALAR)
+    for (int n = lane; n < N; n += 64) atomicAdd(p.dA + d * p.dA_sd + n, dAl[wave][n]);
 }
 
 // p[i0 * s0 + i1 * s1 + i2 * s2 + i3] = 0 over [n0, n1, n2, n3] (innermost stride 1)
@@ -356,20 +399,26 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
     hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 8192)), dim3(256), 0, s,
                        ptr, n0, n1, n2, n3, s0, s1, s2);
   };
-  zero4(a.dD, 1, 1, 1, a.channels, 0, 0, 0);
-  zero4(a.dbias, 1, 1, 1, a.channels, 0, 0, 0);
-  zero4(a.dA, 1, 1, a.channels, a.N, 0, 0, a.dA_sd);
+  zero4(a.dD, 1, 1, 1, a.d_per_head ? a.heads : a.channels, 0, 0, 0);
+  zero4(a.dbias, 1, 1, 1, a.heads, 0, 0, 0);
+  if (a.scalar) zero4(a.dA, 1, 1, 1, a.heads, 0, 0, 0);
+  else zero4(a.dA, 1, 1, a.channels, a.N, 0, 0, a.dA_sd);
+  // a head's channels add into its step-size gradient
+  if (a.chan_per_head > 1) zero4(a.ddelta, a.batch, 1, a.heads, a.L, a.dd_sb, 0, a.dd_sh);
   zero4(a.dB, a.batch, a.groups, a.N, a.L, a.dB_sb, a.dB_sg, a.dB_sn);
   zero4(a.dC, a.batch, a.groups, a.N, a.L, a.dC_sb, a.dC_sg, a.dC_sn);
-  hipLaunchKernelGGL((bwd_ckpt_kernel<TIn>), dim3((unsigned)((rows + kBWaves - 1) / kBWaves)), dim3(64 * kBWaves),
-                     0, s, a, P, nwin, ws);
-  const int64_t blocks = a.batch * a.groups * (a.chan_per_group / kBWaves);
-  if (a.z)
-    hipLaunchKernelGGL((bwd_kernel<TIn, TDy, true>), dim3((unsigned)blocks), dim3(64 * kBWaves), 0, s, a, P, nwin,
-                       static_cast<const float*>(ws));
-  else
-    hipLaunchKernelGGL((bwd_kernel<TIn, TDy, false>), dim3((unsigned)blocks), dim3(64 * kBWaves), 0, s, a, P, nwin,
-                       static_cast<const float*>(ws));
+  const dim3 cgrid((unsigned)((rows + kBWaves - 1) / kBWaves)), block(64 * kBWaves);
+  if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
+  else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
+  const dim3 grid((unsigned)(a.batch * a.groups * (a.chan_per_group / kBWaves)));
+  const float* ck = ws;
+#define SS_BWD(GT, SC) hipLaunchKernelGGL((bwd_kernel<TIn, TDy, GT, SC>), grid, block, 0, s, a, P, nwin, ck)
+  if (a.z) {
+    if (a.scalar) SS_BWD(true, true); else SS_BWD(true, false);
+  } else {
+    if (a.scalar) SS_BWD(false, true); else SS_BWD(false, false);
+  }
+#undef SS_BWD
   return hipGetLastError();
 }
 

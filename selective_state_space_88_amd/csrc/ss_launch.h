@@ -62,8 +62,8 @@ struct StepArgs {
 // One step of the recurrence for every (batch, channel): h = exp(dt A) h + dt B u, y = C h + D u.
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
-// Arguments of the backward of a diagonal-decay scan (delta per channel), already validated.
-// Inputs as in ScanArgs; dy [batch, channels, L]; every gradient f32, innermost stride 1.
+// Arguments of the backward of a scan, already validated.  Inputs as in ScanArgs; dy [batch,
+// channels, L]; every gradient f32 with the shape of its input, innermost stride 1.
 struct BwdArgs {
   const void* u;
   const void* delta;
@@ -78,6 +78,9 @@ struct BwdArgs {
   float *dD, *dz, *dbias; // nullable (absent input)
   int64_t batch, channels, L;
   int32_t N, groups, chan_per_group;
+  int32_t heads, chan_per_head;
+  int32_t scalar;         // A [heads]: one decay per head shared by its states
+  int32_t d_per_head;     // D (and dD) indexed by head
   int32_t softplus, in_bf16, dy_bf16;
   int32_t vec;            // every input time row (and dy's) is 16-byte aligned
   int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, A_sd, dy_sb, dy_sd;

@@ -431,3 +431,80 @@ def test_conv_empty_problems_are_noops():
     assert call_conv(p) == 0
     # W = 1 has an empty state: L = 0 stays a no-op
     assert call_conv(conv_problem(L=0, W=1)) == 0
+
+
+def bwd_problem(scalar=False, heads=None, **kw):
+    p = problem(scalar=scalar, H=heads, **kw)
+    Bt, Dc, L = p["u"].shape[0], p["u"].shape[1], p["u"].shape[2]
+    H = p["delta"].shape[1]
+    N, G = p["B"].shape[2], p["B"].shape[1]
+    base = FAKE + 16 * (1 << 24)
+    step = 1 << 24
+    p["D"] = T([H if scalar else Dc], scan.SS_F32, FAKE + 5 * step)
+    g = dict(
+        dy=T([Bt, Dc, L], scan.SS_F32, base),
+        du=T([Bt, Dc, L], scan.SS_F32, base + step),
+        ddelta=T([Bt, H, L], scan.SS_F32, base + 2 * step),
+        dA=T([H] if scalar else [Dc, N], scan.SS_F32, base + 3 * step),
+        dB=T([Bt, G, N, L], scan.SS_F32, base + 4 * step),
+        dC=T([Bt, G, N, L], scan.SS_F32, base + 5 * step),
+        dD=T([H if scalar else Dc], scan.SS_F32, base + 6 * step),
+        dz=T([Bt, Dc, L], scan.SS_F32, base + 7 * step),
+        ddelta_bias=T([H], scan.SS_F32, base + 8 * step),
+    )
+    p.update(g)
+    return p
+
+
+def call_bwd(p):
+    return scan.call_bwd(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"], p["flags"],
+                         p["dy"], p["du"], p["ddelta"], p["dA"], p["dB"], p["dC"], p["dD"], p["dz"], p["ddelta_bias"],
+                         None)
+
+
+def test_bwd_empty_batch_is_a_noop_for_every_layout():
+    """Valid descriptors of every supported layout pass validation (an empty batch enqueues nothing)."""
+    assert call_bwd(bwd_problem(Bt=0)) == 0
+    assert call_bwd(bwd_problem(Bt=0, Dc=16, heads=4)) == 0                       # delta per head
+    assert call_bwd(bwd_problem(Bt=0, Dc=128, heads=2, scalar=True)) == 0         # scalar decay
+
+
+def test_bwd_gradient_shapes_follow_the_inputs():
+    p = bwd_problem(Dc=16, heads=4)
+    p["ddelta"] = T([2, 16, 32], scan.SS_F32, p["ddelta"].data)   # per channel, but delta is per head
+    assert call_bwd(p) == -3
+    p = bwd_problem(Dc=128, heads=2, scalar=True)
+    p["dA"] = T([128, 4], scan.SS_F32, p["dA"].data)             # A is [heads]
+    assert call_bwd(p) == -3
+    p = bwd_problem(Dc=128, heads=2, scalar=True)
+    p["dD"] = T([128], scan.SS_F32, p["dD"].data)                # D is [heads]
+    assert call_bwd(p) == -3
+    p = bwd_problem(Dc=128, heads=2, scalar=True)
+    p["ddelta_bias"] = T([128], scan.SS_F32, p["ddelta_bias"].data)
+    assert call_bwd(p) == -3
+
+
+def test_bwd_unsupported_and_errors():
+    p = bwd_problem()
+    p["flags"] |= scan.SS_ZOH
+    assert call_bwd(p) == -6
+    p = bwd_problem()
+    p["flags"] |= scan.SS_TRAPEZOID
+    assert call_bwd(p) == -6
+    assert call_bwd(bwd_problem(Dc=6)) == -6          # channels per group not a multiple of 4
+    assert call_bwd(bwd_problem(N=129)) == -6
+    p = bwd_problem()
+    p["dD"] = None                                     # D given: dD required
+    assert call_bwd(p) == -1
+    p = bwd_problem()
+    p["dz"] = None                                     # gate on: dz required
+    assert call_bwd(p) == -1
+    p = bwd_problem()
+    p["dA"].dtype = scan.SS_BF16
+    assert call_bwd(p) == -2
+    p = bwd_problem()
+    p["du"].data = p["u"].data                          # a gradient over an input
+    assert call_bwd(p) == -7
+    p = bwd_problem()
+    p["dB"].data = p["du"].data + 8                     # two gradients overlapping
+    assert call_bwd(p) == -7

@@ -73,14 +73,31 @@ def test_bf16_upstream_gradient():
     check_bwd(inputs.random_problem(730, 1, 8, 300, 16), "dy bf16", dy_dtype=torch.bfloat16)
 
 
-def test_backward_errors():
-    """Unsupported layouts are rejected before anything runs."""
-    torch = torch_dev()
-    from selective_state_space_88_amd.scan import ScanError, scan_bwd
+@pytest.mark.parametrize("case", ["scalar N16 bf16", "scalar N128 f32", "scalar head of 4", "scalar head of 2",
+                                  "diag heads of 4", "diag heads of 2", "scalar groups 2", "scalar no bias"])
+def test_gradients_with_heads(case):
+    """Step sizes shared by a head's channels (delta [batch, heads, L]) with a diagonal A, and the
+    scalar decay A [heads] with D per head: per-head gradients summed over the head's channels
+    (through LDS when the block's 4 channels share a head, by per-channel atomics otherwise)."""
+    mk = {
+        "scalar N16 bf16": lambda: inputs.random_problem(750, 2, 128, 700, 16, heads=2, scalar_decay=True),
+        "scalar N128 f32": lambda: inputs.random_problem(751, 1, 64, 600, 128, heads=1, scalar_decay=True,
+                                                         in_dtype="f32", gate=False),
+        "scalar head of 4": lambda: inputs.random_problem(752, 2, 16, 530, 8, heads=4, scalar_decay=True,
+                                                          in_dtype="f32"),
+        "scalar head of 2": lambda: inputs.random_problem(753, 1, 8, 300, 5, heads=4, scalar_decay=True,
+                                                          in_dtype="f32"),
+        "diag heads of 4": lambda: inputs.random_problem(754, 2, 16, 777, 16, heads=4, in_dtype="f32"),
+        "diag heads of 2": lambda: inputs.random_problem(755, 1, 8, 300, 4, heads=4, in_dtype="f32", gate=False),
+        "scalar groups 2": lambda: inputs.random_problem(756, 1, 32, 520, 16, heads=4, groups=2, scalar_decay=True,
+                                                         in_dtype="f32"),
+        "scalar no bias": lambda: inputs.random_problem(757, 1, 16, 400, 16, heads=2, scalar_decay=True,
+                                                        in_dtype="f32", softplus=False, with_D=False),
+    }
+    check_bwd(mk[case](), case)
 
-    p = inputs.random_problem(740, 1, 128, 64, 16, heads=2, scalar_decay=True)
-    t = dev_problem(p)
-    dy = torch.zeros((1, 128, 64), device="cuda")
-    with pytest.raises(ScanError) as e:
-        scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], dy)
-    assert e.value.code == -6
+
+def test_workload_4_layer_shapes_reduced():
+    """The scalar-decay multi-head layer's distributions (A_h = -U(1, 16), N 128, heads of 64
+    channels, no gate) at 4 heads and L 2048."""
+    check_bwd(inputs.make(4, batch=1, heads=4, length=2048), "workload-4 shapes, 1x(4x64)x2048")
