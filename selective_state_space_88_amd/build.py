@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssscan.so")
 SOURCES = ["ss_api.hip", "ss_diag.hip", "ss_scalar.hip", "ss_ssd.hip", "ss_step.hip", "ss_bwd.hip",
-           "ss_conv.hip"]
+           "ss_ssd_bwd.hip", "ss_conv.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

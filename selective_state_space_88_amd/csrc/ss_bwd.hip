@@ -407,6 +407,7 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   if (a.chan_per_head > 1) zero4(a.ddelta, a.batch, 1, a.heads, a.L, a.dd_sb, 0, a.dd_sh);
   zero4(a.dB, a.batch, a.groups, a.N, a.L, a.dB_sb, a.dB_sg, a.dB_sn);
   zero4(a.dC, a.batch, a.groups, a.N, a.L, a.dC_sb, a.dC_sg, a.dC_sn);
+  if (ssd_bwd_path(a)) return launch_ssd_bwd(a, ws, s);
   const dim3 cgrid((unsigned)((rows + kBWaves - 1) / kBWaves)), block(64 * kBWaves);
   if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
   else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
@@ -425,6 +426,7 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
 }  // namespace
 
 int64_t bwd_workspace_floats(const BwdArgs& a) {
+  if (ssd_bwd_path(a)) return ssd_bwd_workspace_floats(a);
   return a.batch * a.channels * ((a.L + kBW - 1) / kBW) * a.N;
 }
 

@@ -88,9 +88,15 @@ struct BwdArgs {
 };
 
 // Gradients of sum(dy * y).  `ws` must hold bwd_workspace_floats(a) floats (the states at the
-// start of every window), ordered on `stream`.
+// start of every window, or of every chunk on the matrix path), ordered on `stream`.
 int64_t bwd_workspace_floats(const BwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t stream);
+
+// Scalar decay without a gate, heads and B/C groups in whole 64-channel slabs: the backward in the
+// chunked matrix form on fp32 MFMA (launched by launch_bwd, after the summed gradients are zeroed).
+bool ssd_bwd_path(const BwdArgs& a);
+int64_t ssd_bwd_workspace_floats(const BwdArgs& a);
+hipError_t launch_ssd_bwd(const BwdArgs& a, float* ws, hipStream_t stream);
 
 // dst[b, d, n] = src[b, d, n] (src == nullptr: 0) for a [batch, channels, N] f32 state.
 hipError_t launch_state_copy(const float* src, int64_t s_sb, int64_t s_sd, float* dst, int64_t d_sb,

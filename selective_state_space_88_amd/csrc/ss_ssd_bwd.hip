@@ -1,0 +1,536 @@
+// ss_ssd_bwd.hip -- backward of the scalar-decay scan in the chunked matrix form (gfx950, fp32 MFMA).
+//
+// With one decay per head (a_t = exp(dt_t A_h) shared by the head's channels and states; the
+// Mamba-2 layout of the bqwf.cn survey, section 3.2, and the omica.com.cn explainer, section 6.2)
+// the recurrence over a chunk of T steps is a handful of dense products, the state-space duality
+// the pages describe.  With s_i the cumulative log decay inside the chunk (s_i includes step i),
+// x_j = dt_j u_j (one value per channel p), H0 the state before the chunk and R the adjoint that
+// reaches the chunk's last step from the right (R = a g of the next chunk's first step):
+//   h_i = e^{s_i} H0 + sum_{j<=i} e^{s_i - s_j} x_j B_j^T
+//   g_i = sum_{k>=i} e^{s_k - s_i} dy_k C_k^T + e^{s_{T-1} - s_i} R            (g = dLoss/dh)
+// and the gradients of the chunk are, with DX = dY X^T, CB = C B^T, M1 = L o DX (L_kj =
+// e^{s_k - s_j} for k >= j, else 0):
+//   dC = diag(e^s) (dY H0) + M1 B                dB = M1^T C + diag(e^{s_{T-1} - s}) (X R)
+//   dX = (L o CB)^T dY + diag(e^{s_{T-1} - s}) B R^T,   du = dt dX + D dy
+//   R  <- e^{s_{T-1}} R + dY^T diag(e^s) C      (the adjoint handed to the previous chunk)
+// The decay's gradient a_j dLoss/da_j = <g_j, a_j h_{j-1}> = <g_j, h_j> - x_j . dx_j, where
+//   <g_j, h_j> = sum_{k>=j>=i} e^{s_k - s_i} DX_ki CB_ki + sum_{k>=j} e^{s_k} (dY H0)_k . C_k
+//              + sum_{i<=j} e^{s_{T-1} - s_i} (X R)_i . B_i + e^{s_{T-1}} <R, H0>,
+// gives ddt_j = u_j . dx_j + A a_j dLoss/da_j and dA = sum_j dt_j a_j dLoss/da_j.
+//
+// Two passes per (batch, head, 64-channel slab): the first walks the chunks forward and stores
+// every chunk's starting state H0 (f32, [N][64]); the second walks them in reverse carrying R in
+// MFMA accumulators.  Every product is v_mfma_f32_16x16x4_f32 on operands staged in LDS with the
+// contracted index contiguous (each lane reads four consecutive k with one 16-byte read; the
+// order of k inside a block of 16 is permuted the same way on both operands).  dB and dC are
+// summed over the group's heads with atomic adds; per-head sums (ddelta over slabs, dA, dD,
+// dbias) likewise.  No gate (the gated layout takes the per-channel kernel).
+#include "ss_device.h"
+#include "ss_launch.h"
+
+namespace ss {
+namespace {
+
+constexpr int kCT = 32;            // steps per chunk
+constexpr int kCP = 64;            // channels per block (a slab)
+constexpr int kThr = 256;          // 4 waves
+constexpr int kSP = kCP + 4;       // LDS row stride of [.][64] operands (floats)
+constexpr int kST = kCT + 4;       // LDS row stride of [.][32] operands
+
+__device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc[t] += A[i][0..K) . Bt_t[j][0..K) for NT 16x16 tiles sharing their 16 rows of A: lane l takes
+// row i = l % 16 of A and row j = l % 16 of tile t's Bt = B + t * bstep.  Rows are k-contiguous
+// and 16-byte aligned; lane l supplies k = 16 kb + 4 (l / 16) + m to MFMA m of block kb.  With
+// SCALE, A's k-th column is multiplied by sc[k] on the way.
+template <int K, int NT, bool SCALE = false>
+__device__ __forceinline__ void mm(const float* A, int lda, const float* B, int ldb, int bstep, int lane,
+                                   f32x4 (&acc)[NT], const float* sc = nullptr) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* a = A + r * lda + 4 * q;
+  const float* b = B + r * ldb + 4 * q;
+#pragma unroll
+  for (int kb = 0; kb < K / 16; ++kb) {
+    f32x4 av = *reinterpret_cast<const f32x4*>(a + 16 * kb);
+    if constexpr (SCALE) {
+      const f32x4 s = *reinterpret_cast<const f32x4*>(sc + 16 * kb + 4 * q);
+      av = av * s;
+    }
+    f32x4 bv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bv[t] = *reinterpret_cast<const f32x4*>(b + t * bstep + 16 * kb);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mma4(av[m], bv[t][m], acc[t]);
+  }
+}
+
+// sum over the 16 lanes of each row of 16 (lanes with the same l / 16)
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+
+__device__ __forceinline__ float wave_total(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+struct Blk {
+  int64_t b, h, g, d0;
+};
+
+__device__ __forceinline__ Blk block_of(const BwdArgs& p) {
+  const int slabs = p.chan_per_head / kCP;
+  const int64_t blk = blockIdx.x;
+  const int64_t bh = blk / slabs, slab = blk % slabs;
+  Blk r;
+  r.b = bh / p.heads;
+  r.h = bh % p.heads;
+  r.d0 = r.h * p.chan_per_head + slab * kCP;
+  r.g = r.d0 / p.chan_per_group;
+  return r;
+}
+
+// step size of step t (0 past the end)
+template <typename TIn>
+__device__ __forceinline__ float step_dt(const BwdArgs& p, const TIn* dr, int64_t t, float bias, float* sig) {
+  if (t >= p.L) {
+    if (sig) *sig = 0.f;
+    return 0.f;
+  }
+  const float x = to_f32(dr[t]) + bias;
+  if (sig) *sig = p.softplus ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+  return p.softplus ? softplus_fast(x) : x;
+}
+
+// Pass 1: the state before every chunk, [blocks][chunks][NP][64] f32 ([n][p]).
+template <typename TIn, int NT>
+__global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch, float* __restrict__ ws) {
+  constexpr int NP = 16 * NT;
+  __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // x^T [p][t]
+  __shared__ __attribute__((aligned(16))) float wb[NP * kST];    // e^{s_{T-1} - s_t} B [n][t]
+  __shared__ float ss2[kCT];                                     // cumulative log2 decay
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const Blk k = block_of(p);
+  const int N = p.N;
+  const float A2 = p.A[k.h] * kLog2e;
+  const float bias = p.bias ? p.bias[k.h] : 0.f;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + k.b * p.dl_sb + k.h * p.dl_sh;
+  const TIn* ub = static_cast<const TIn*>(p.u) + k.b * p.u_sb + k.d0 * p.u_sd;
+  const TIn* Bb = static_cast<const TIn*>(p.B) + k.b * p.B_sb + k.g * p.B_sg;
+  float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  f32x4 H[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) H[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t c = 0; c < nch; ++c) {
+    // the state before chunk c: lane holds H[p = 16 wave + 4 (l / 16) + r][n = 16 j + l % 16]
+    float* hc = wsb + c * NP * kCP;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      *reinterpret_cast<f32x4*>(hc + (16 * j + (lane & 15)) * kCP + 16 * wave + 4 * (lane >> 4)) = H[j];
+    if (c == nch - 1) break;
+    const int64_t t0 = c * kCT;
+    if (wave == 0) {
+      float s = lane < kCT ? step_dt(p, dr, t0 + lane, bias, nullptr) * A2 : 0.f;
+#pragma unroll
+      for (int off = 1; off < kCT; off <<= 1) {
+        const float v = __shfl_up(s, off);
+        if (lane >= off) s += v;
+      }
+      if (lane < kCT) ss2[lane] = s;
+    }
+    {
+      // x^T: thread (p = tid / 4, steps 8 (tid % 4) ..)
+      const int pp = tid >> 2, tt = 8 * (tid & 3);
+      float v[8];
+      load_seg<8>(ub + pp * p.u_sd, t0 + tt, p.L, p.vec, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] *= step_dt(p, dr, t0 + tt + e, bias, nullptr);
+      *reinterpret_cast<f32x4*>(xt + pp * kST + tt) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(xt + pp * kST + tt + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();   // ss2 ready
+    for (int i = tid; i < NP * 2; i += kThr) {
+      const int n = i >> 1, tt = 16 * (i & 1);
+      float v[16];
+      if (n < N) {
+        load_seg<16>(Bb + n * p.B_sn, t0 + tt, p.L, p.vec, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[e] = 0.f;
+      }
+      const float send = ss2[kCT - 1];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] *= __builtin_amdgcn_exp2f(send - ss2[tt + e]);
+#pragma unroll
+      for (int e = 0; e < 16; e += 4)
+        *reinterpret_cast<f32x4*>(wb + n * kST + tt + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    }
+    __syncthreads();
+    const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) H[j] = H[j] * dec;
+    mm<kCT, NT>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
+    __syncthreads();   // xt, wb, ss2 are rewritten by the next chunk
+  }
+}
+
+// Pass 2: the chunks in reverse.
+template <typename TIn, typename TDy, int NT>
+__global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws) {
+  constexpr int NP = 16 * NT;
+  constexpr int NH = NT / 2;   // [T x N] tiles per wave (two waves per 16 rows; NT >= 2)
+  __shared__ __attribute__((aligned(16))) float xn[kCT * kSP];    // x [t][p]
+  __shared__ __attribute__((aligned(16))) float dyn[kCT * kSP];   // dy [t][p]
+  __shared__ __attribute__((aligned(16))) float dyt[kCP * kST];   // dy [p][t]
+  __shared__ __attribute__((aligned(16))) float bnt[NP * kST];    // B [n][t]
+  __shared__ __attribute__((aligned(16))) float cnt[NP * kST];    // C [n][t]
+  __shared__ __attribute__((aligned(16))) float rnp[NP * kSP];    // R [n][p]
+  __shared__ __attribute__((aligned(16))) float hnp[NP * kSP];    // H0 [n][p]
+  __shared__ __attribute__((aligned(16))) float m1[kCT * kST];    // M1 [k][j]
+  __shared__ __attribute__((aligned(16))) float m1t[kCT * kST];   // M1^T [j][k]
+  __shared__ __attribute__((aligned(16))) float lcbt[kCT * kST];  // (L o CB)^T [j][k]
+  __shared__ __attribute__((aligned(16))) float wm[kCT * kST];    // M1 o CB [k][i], then its row prefix sums
+  __shared__ __attribute__((aligned(16))) float ses[kCT];         // e^{s_t}
+  __shared__ float ss2[kCT], ser[kCT], sdt[kCT], ssig[kCT];
+  __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rh0[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, l16 = lane & 15;
+  const Blk k = block_of(p);
+  const int N = p.N;
+  const int64_t L = p.L;
+  const float Ah = p.A[k.h], A2 = Ah * kLog2e;
+  const float bias = p.bias ? p.bias[k.h] : 0.f;
+  const int slabs = p.chan_per_head / kCP;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + k.b * p.dl_sb + k.h * p.dl_sh;
+  const TIn* ub = static_cast<const TIn*>(p.u) + k.b * p.u_sb + k.d0 * p.u_sd;
+  const TDy* yb = static_cast<const TDy*>(p.dy) + k.b * p.dy_sb + k.d0 * p.dy_sd;
+  const TIn* Bb = static_cast<const TIn*>(p.B) + k.b * p.B_sb + k.g * p.B_sg;
+  const TIn* Cb = static_cast<const TIn*>(p.C) + k.b * p.C_sb + k.g * p.C_sg;
+  float* dBb = p.dB + k.b * p.dB_sb + k.g * p.dB_sg;
+  float* dCb = p.dC + k.b * p.dC_sb + k.g * p.dC_sg;
+  float* dub = p.du + k.b * p.du_sb + k.d0 * p.du_sd;
+  float* ddb = p.ddelta + k.b * p.dd_sb + k.h * p.dd_sh;
+  const float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  const int ti = wave >> 1, half = wave & 1;   // 16-step row block and column half of this wave
+  // D of the channels this lane's dX tiles cover
+  float Dp[2];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt) {
+    const int pch = 16 * (2 * half + pt) + l16;
+    Dp[pt] = p.D ? p.D[p.d_per_head ? k.h : k.d0 + pch] : 0.f;
+  }
+  f32x4 R[NT];   // R[p = 16 wave + 4 q + r][n = 16 j + l16]
+#pragma unroll
+  for (int j = 0; j < NT; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dDl[2] = {0.f, 0.f};
+  float dAacc = 0.f, dbacc = 0.f;
+
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t t0 = c * kCT;
+    // ---- staging
+    if (wave == 0) {
+      float sg = 0.f;
+      const float dt = lane < kCT ? step_dt(p, dr, t0 + lane, bias, &sg) : 0.f;
+      float s = dt * A2;
+#pragma unroll
+      for (int off = 1; off < kCT; off <<= 1) {
+        const float v = __shfl_up(s, off);
+        if (lane >= off) s += v;
+      }
+      const float send = __shfl(s, kCT - 1);
+      if (lane < kCT) {
+        ss2[lane] = s;
+        sdt[lane] = dt;
+        ssig[lane] = sg;
+        ses[lane] = __builtin_amdgcn_exp2f(s);
+        ser[lane] = __builtin_amdgcn_exp2f(send - s);
+      }
+    }
+    {
+      // x and dy of the slab: thread (p = tid / 4, steps 8 (tid % 4) ..)
+      const int pp = tid >> 2, tt = 8 * (tid & 3);
+      float v[8], w[8];
+      load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, v);
+      load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        xn[(tt + e) * kSP + pp] = v[e] * step_dt(p, dr, t0 + tt + e, bias, nullptr);
+        dyn[(tt + e) * kSP + pp] = w[e];
+      }
+      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{w[4], w[5], w[6], w[7]};
+    }
+    for (int i = tid; i < NP * 4; i += kThr) {
+      // B and C rows: (n = i / 4, steps 8 (i % 4) ..); rows past N are zero
+      const int n = i >> 2, tt = 8 * (i & 3);
+      float v[8], w[8];
+      if (n < N) {
+        load_seg<8>(Bb + n * p.B_sn, t0 + tt, L, p.vec, v);
+        load_seg<8>(Cb + n * p.C_sn, t0 + tt, L, p.vec, w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = w[e] = 0.f;
+      }
+      *reinterpret_cast<f32x4*>(bnt + n * kST + tt) = f32x4{v[0], v[1], v[2], v[3]};
+      *reinterpret_cast<f32x4*>(bnt + n * kST + tt + 4) = f32x4{v[4], v[5], v[6], v[7]};
+      *reinterpret_cast<f32x4*>(cnt + n * kST + tt) = f32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<f32x4*>(cnt + n * kST + tt + 4) = f32x4{w[4], w[5], w[6], w[7]};
+    }
+    {
+      // H0 of the chunk into LDS; R (the carry from the right) too
+      const float* hc = wsb + c * NP * kCP;
+      for (int i = tid; i < NP * kCP / 4; i += kThr) {
+        const int n = i / (kCP / 4), pq = 4 * (i % (kCP / 4));
+        *reinterpret_cast<f32x4*>(hnp + n * kSP + pq) = *reinterpret_cast<const f32x4*>(hc + n * kCP + pq);
+      }
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        *reinterpret_cast<f32x4*>(rnp + (16 * j + l16) * kSP + 16 * wave + 4 * q) = R[j];
+    }
+    __syncthreads();
+
+    // ---- DX = dY X^T and CB = C B^T (one 16x16 tile each per wave), then the masked matrices
+    {
+      f32x4 dx[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      mm<kCP, 1>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
+      f32x4 cb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NT; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int n = 16 * kb + 4 * q + m;
+          cb = mma4(cnt[n * kST + 16 * ti + l16], bnt[n * kST + 16 * half + l16], cb);
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * q + r, s = 16 * half + l16;   // row k = t, column j = s
+        const float e = t >= s ? __builtin_amdgcn_exp2f(ss2[t] - ss2[s]) : 0.f;
+        const float mv = e * dx[0][r];
+        m1[t * kST + s] = mv;
+        m1t[s * kST + t] = mv;
+        lcbt[s * kST + t] = e * cb[r];
+        wm[t * kST + s] = mv * cb[r];
+      }
+    }
+    // ---- dY H0 and X R ([T x N] tiles: rows 16 ti, columns 16 (half NH + j))
+    f32x4 yh[NH], xr[NH];
+#pragma unroll
+    for (int j = 0; j < NH; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nj0 = half * NH;
+    mm<kCP, NH>(dyn + 16 * ti * kSP, kSP, hnp + 16 * nj0 * kSP, kSP, 16 * kSP, lane, yh);
+    mm<kCP, NH>(xn + 16 * ti * kSP, kSP, rnp + 16 * nj0 * kSP, kSP, 16 * kSP, lane, xr);
+    {
+      // alpha_t = e^{s_t} (dY H0)_t . C_t and beta_t = e^{s_{T-1} - s_t} (X R)_t . B_t, partial over
+      // this wave's columns
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * ti + 4 * q + r;
+        float a = 0.f, bsum = 0.f;
+#pragma unroll
+        for (int j = 0; j < NH; ++j) {
+          const int n = 16 * (nj0 + j) + l16;
+          a = fmaf(yh[j][r], cnt[n * kST + t], a);
+          bsum = fmaf(xr[j][r], bnt[n * kST + t], bsum);
+        }
+        a = row16_sum(a);
+        bsum = row16_sum(bsum);
+        if (l16 == 0) {
+          alp[half][t] = a * ses[t];
+          bet[half][t] = bsum * ser[t];
+        }
+      }
+      // <R, H0> over this wave's rows of R
+      float rh = 0.f;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(hnp + (16 * j + l16) * kSP + 16 * wave + 4 * q);
+        rh = fmaf(R[j][0], hv[0], fmaf(R[j][1], hv[1], fmaf(R[j][2], hv[2], fmaf(R[j][3], hv[3], rh))));
+      }
+      rh = wave_total(rh);
+      if (lane == 0) rh0[wave] = rh;
+    }
+    __syncthreads();   // m1, m1t, lcbt, wm, alp, bet, rh0 ready
+
+    // ---- dC = diag(e^s) dY H0 + M1 B and dB = diag(e^{s_{T-1} - s}) X R + M1^T C, added to the group's
+    {
+#pragma unroll
+      for (int j = 0; j < NH; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * ti + 4 * q + r;
+          yh[j][r] *= ses[t];
+          xr[j][r] *= ser[t];
+        }
+      mm<kCT, NH>(m1 + 16 * ti * kST, kST, bnt + 16 * nj0 * kST, kST, 16 * kST, lane, yh);
+      mm<kCT, NH>(m1t + 16 * ti * kST, kST, cnt + 16 * nj0 * kST, kST, 16 * kST, lane, xr);
+#pragma unroll
+      for (int j = 0; j < NH; ++j) {
+        const int n = 16 * (nj0 + j) + l16;
+        if (n < N) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int64_t t = t0 + 16 * ti + 4 * q + r;
+            if (t < L) {
+              atomicAdd(dCb + n * p.dC_sn + t, yh[j][r]);
+              atomicAdd(dBb + n * p.dB_sn + t, xr[j][r]);
+            }
+          }
+        }
+      }
+    }
+
+    // ---- dX = diag(e^{s_{T-1} - s}) B R^T + (L o CB)^T dY ([T x 64]: rows 16 ti, columns 16 (2 half + pt))
+    {
+      f32x4 dxa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kb = 0; kb < NT; ++kb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int n = 16 * kb + 4 * q + m;
+          const float a = bnt[n * kST + 16 * ti + l16];
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) dxa[pt] = mma4(a, rnp[n * kSP + 16 * (2 * half + pt) + l16], dxa[pt]);
+        }
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dxa[pt][r] *= ser[16 * ti + 4 * q + r];
+      mm<kCT, 2>(lcbt + 16 * ti * kST, kST, dyt + 16 * (2 * half) * kST, kST, 16 * kST, lane, dxa);
+      // du = dt dX + D dy; u . dX per step; dD
+      float ud[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const int pch = 16 * (2 * half + pt) + l16;
+        const TIn* urow = ub + pch * p.u_sd;
+        float* durow = dub + pch * p.du_sd;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tl = 16 * ti + 4 * q + r;
+          const int64_t t = t0 + tl;
+          if (t < L) {
+            const float dyv = dyn[tl * kSP + pch];
+            const float uv = to_f32(urow[t]);
+            durow[t] = fmaf(sdt[tl], dxa[pt][r], Dp[pt] * dyv);
+            ud[r] = fmaf(uv, dxa[pt][r], ud[r]);
+            dDl[pt] = fmaf(dyv, uv, dDl[pt]);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = row16_sum(ud[r]);
+        if (l16 == 0) udp[half][16 * ti + 4 * q + r] = v;
+      }
+    }
+
+    // ---- R <- e^{s_{T-1}} R + dY^T diag(e^s) C
+    {
+      const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) R[j] = R[j] * dec;
+      mm<kCT, NT, true>(dyt + 16 * wave * kST, kST, cnt, kST, 16 * kST, lane, R, ses);
+    }
+
+    // ---- the decay's gradient per step
+    if (tid < kCT) {
+      // row prefix sums of M1 o CB: wm[k][i] <- sum_{i' <= i} wm[k][i']
+      float acc = 0.f;
+      for (int i = 0; i <= tid; ++i) {   // only i <= k is non-zero
+        acc += wm[tid * kST + i];
+        wm[tid * kST + i] = acc;
+      }
+      for (int i = tid + 1; i < kCT; ++i) wm[tid * kST + i] = acc;
+    }
+    __syncthreads();   // udp, wm prefix sums ready
+    if (tid < kCT) {
+      const int j = tid;
+      float t1 = 0.f, t2 = 0.f, t3 = 0.f;
+      for (int kk = j; kk < kCT; ++kk) {
+        t1 += wm[kk * kST + j];
+        t2 += alp[0][kk] + alp[1][kk];
+      }
+      for (int i = 0; i <= j; ++i) t3 += bet[0][i] + bet[1][i];
+      const float t4 = __builtin_amdgcn_exp2f(ss2[kCT - 1]) * (rh0[0] + rh0[1] + rh0[2] + rh0[3]);
+      const float gh = t1 + t2 + t3 + t4;
+      const float ud = udp[0][j] + udp[1][j];
+      const float dt = sdt[j];
+      const float qa = gh - dt * ud;                 // a_j dLoss/da_j
+      const float ddt = fmaf(Ah, qa, ud);
+      const float dx = ddt * ssig[j];
+      if (t0 + j < L) {
+        if (slabs == 1) ddb[t0 + j] = dx;
+        else atomicAdd(ddb + t0 + j, dx);
+        dAacc = fmaf(dt, qa, dAacc);
+        dbacc += dx;
+      }
+    }
+    __syncthreads();   // every LDS buffer is restaged by the next chunk
+  }
+
+  // per-head and per-channel sums
+  if (wave == 0) {
+    const float dA = wave_total(dAacc), db = wave_total(dbacc);
+    if (lane == 0) {
+      atomicAdd(p.dA + k.h, dA);
+      if (p.dbias) atomicAdd(p.dbias + k.h, db);
+    }
+  }
+  if (p.dD) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      float v = dDl[pt];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (p.d_per_head) {
+        v = row16_sum(v);
+        if (lane == 0) atomicAdd(p.dD + k.h, v);
+      } else if (q == 0) {
+        atomicAdd(p.dD + k.d0 + 16 * (2 * half + pt) + l16, v);
+      }
+    }
+  }
+}
+
+template <typename TIn, typename TDy, int NT>
+hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
+  const int64_t nch = (a.L + kCT - 1) / kCT;
+  const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
+  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), grid, block, 0, s, a, nch, ws);
+  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, block, 0, s, a, nch, static_cast<const float*>(ws));
+  return hipGetLastError();
+}
+
+template <typename TIn, typename TDy>
+hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
+  if (a.N <= 32) return launch_nt<TIn, TDy, 2>(a, ws, s);
+  if (a.N <= 64) return launch_nt<TIn, TDy, 4>(a, ws, s);
+  return launch_nt<TIn, TDy, 8>(a, ws, s);
+}
+
+}  // namespace
+
+bool ssd_bwd_path(const BwdArgs& a) {
+  return a.scalar && !a.z && a.chan_per_head % kCP == 0 && a.chan_per_group % kCP == 0 && a.N <= 128 && a.L > 0;
+}
+
+int64_t ssd_bwd_workspace_floats(const BwdArgs& a) {
+  const int64_t np = a.N <= 32 ? 32 : a.N <= 64 ? 64 : 128;
+  const int64_t nch = (a.L + kCT - 1) / kCT;
+  return a.batch * a.heads * (a.chan_per_head / kCP) * nch * np * kCP;
+}
+
+hipError_t launch_ssd_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
+  if (a.in_bf16) return a.dy_bf16 ? launch_t<bf16_t, bf16_t>(a, ws, s) : launch_t<bf16_t, float>(a, ws, s);
+  return a.dy_bf16 ? launch_t<float, bf16_t>(a, ws, s) : launch_t<float, float>(a, ws, s);
+}
+
+}  // namespace ss

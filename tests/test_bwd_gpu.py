@@ -101,3 +101,41 @@ def test_workload_4_layer_shapes_reduced():
     """The scalar-decay multi-head layer's distributions (A_h = -U(1, 16), N 128, heads of 64
     channels, no gate) at 4 heads and L 2048."""
     check_bwd(inputs.make(4, batch=1, heads=4, length=2048), "workload-4 shapes, 1x(4x64)x2048")
+
+
+MATRIX_CASES = {
+    # scalar decay, no gate, heads and groups in whole 64-channel slabs: the chunked matrix form
+    "N16 bf16 L700": lambda: inputs.random_problem(760, 2, 128, 700, 16, heads=2, scalar_decay=True, gate=False),
+    "N128 f32 L600": lambda: inputs.random_problem(761, 1, 64, 600, 128, heads=1, scalar_decay=True,
+                                                   in_dtype="f32", gate=False),
+    "N33 f32 ragged": lambda: inputs.random_problem(762, 2, 64, 97, 33, heads=1, scalar_decay=True, in_dtype="f32",
+                                                    gate=False),
+    "N1 one step": lambda: inputs.random_problem(763, 1, 64, 1, 1, heads=1, scalar_decay=True, in_dtype="f32",
+                                                 gate=False),
+    "N64 L31": lambda: inputs.random_problem(764, 1, 128, 31, 64, heads=2, scalar_decay=True, in_dtype="f32",
+                                             gate=False),
+    "two slabs per head": lambda: inputs.random_problem(765, 1, 256, 300, 16, heads=2, scalar_decay=True,
+                                                        in_dtype="f32", gate=False),
+    "two groups": lambda: inputs.random_problem(766, 1, 256, 200, 32, heads=4, groups=2, scalar_decay=True,
+                                                in_dtype="f32", gate=False),
+    "no softplus, no D": lambda: inputs.random_problem(767, 1, 128, 333, 16, heads=2, scalar_decay=True,
+                                                       in_dtype="f32", gate=False, softplus=False, with_D=False),
+    "no bias": lambda: inputs.random_problem(768, 1, 64, 257, 16, heads=1, scalar_decay=True, in_dtype="f32",
+                                             gate=False, with_bias=False),
+    "long decay-free": lambda: inputs.random_problem(769, 1, 64, 1500, 16, heads=1, scalar_decay=True,
+                                                     in_dtype="f32", gate=False, dt=(1e-4, 1e-3)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MATRIX_CASES))
+def test_matrix_backward(case):
+    """The scalar-decay backward in the chunked matrix form (fp32 MFMA): ragged chunk tails, N from
+    1 to 128 (padded to 32, 64, 128), heads of two slabs (ddelta summed by atomics), two B/C groups,
+    D per head, softplus off, slow decays (states carried across many chunks)."""
+    check_bwd(MATRIX_CASES[case](), "matrix " + case)
+
+
+def test_matrix_backward_bf16_dy():
+    torch = torch_dev()
+    check_bwd(inputs.random_problem(770, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=False), "matrix dy bf16",
+              dy_dtype=torch.bfloat16)
