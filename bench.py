@@ -29,6 +29,7 @@ METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 
 HBM_PEAK_GBPS = 8000.0
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 128 FP32 FMA lanes/clk x 2 FLOP x 2.4 GHz
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
+FP32_MATRIX_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak
 
 # ALU work model, per element (one (b, d, t)), in FP32 FLOP-equivalents: an FMA is 2, a
 # multiply or add 1, and a transcendental (v_exp/v_log/v_rcp, which issues at a quarter of the
@@ -260,18 +261,38 @@ def backward_bench(args, p, to_dev, dev):
     nbytes += p.batch * p.heads * p.length * (ib + 4)
     nbytes += p.batch * p.groups * p.nstate * p.length * 2 * (ib + 4)
     tf = flops / per / 1e12
+    P = p.channels // p.heads
+    matrix = p.scalar_decay and not p.gate and P % 64 == 0 and (p.channels // p.groups) % 64 == 0
     out = {
         "metric": "selective-scan bwd elems/s (B*D*L/s), 1 GPU", "value": E * K / wall, "unit": "elems/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "backward, " + describe(p), "batch": p.batch, "channels": p.channels,
-                   "seq_len": p.length, "nstate": p.nstate, "kernel": "bwd_kernel"},
+                   "seq_len": p.length, "nstate": p.nstate,
+                   "kernel": "ssdb_main_kernel" if matrix else "bwd_kernel"},
         "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": None, "call_ms": per * 1e3,
                      "flop_equiv_per_call": flops, "hbm_algorithmic_bytes_per_call": nbytes,
                      "hbm_achieved_GBps": nbytes / per / 1e9},
         "cpu_baseline": None,
     }
+    if matrix:
+        # The scalar-decay backward is a chain of dense contractions on v_mfma_f32_16x16x4_f32
+        # (2048 flops each), so its roofline is the fp32 matrix peak.  Per (batch, head, 64-channel
+        # slab, 32-step chunk) each of 4 waves issues 32 + 40 NT in the reverse pass and 8 NT in the
+        # forward pass (NT = 16-state tiles: 2, 4 or 8), and per (batch, group, chunk) C B^T takes
+        # 4 NT per wave; the time is the whole call.
+        NT = 2 if p.nstate <= 32 else 4 if p.nstate <= 64 else 8
+        nch = (p.length + 31) // 32
+        blocks = p.batch * p.heads * (P // 64)
+        mf = (blocks * nch * 4 * (32 + 48 * NT) + p.batch * p.groups * nch * 4 * 4 * NT) * 2048.0
+        rl = out["roofline"]
+        out["roofline"] = {
+            "bound": "mfma", "achieved": mf / per / 1e12, "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": mf / per / 1e12 / FP32_MATRIX_PEAK_TFLOPS, "traffic": None, "call_ms": rl["call_ms"],
+            "mfma_flops_per_call": mf, "alu_flop_equiv_per_call": flops, "alu_equiv_TFLOPs": tf,
+            "hbm_algorithmic_bytes_per_call": nbytes, "hbm_achieved_GBps": nbytes / per / 1e9,
+        }
     print(json.dumps(out))
 
 

@@ -18,6 +18,10 @@
 //              + sum_{i<=j} e^{s_{T-1} - s_i} (X R)_i . B_i + e^{s_{T-1}} <R, H0>,
 // gives ddt_j = u_j . dx_j + A a_j dLoss/da_j and dA = sum_j dt_j a_j dLoss/da_j.
 //
+// The first term is a sum over the rectangle k >= j >= i of W = M1 o CB; it equals the prefix sum of
+// W's column sums minus the exclusive prefix sum of its row sums, so every per-step quantity is a
+// scan over the chunk's 32 steps.  u is staged raw and dt folded into the products' epilogues.
+//
 // Two passes per (batch, head, 64-channel slab): the first walks the chunks forward and stores
 // every chunk's starting state H0 (f32, [N][64]); the second walks them in reverse carrying R in
 // MFMA accumulators.  Every product is v_mfma_f32_16x16x4_f32 on operands staged in LDS with the
@@ -68,6 +72,27 @@ __device__ __forceinline__ void mm(const float* A, int lda, const float* B, int 
   }
 }
 
+// As mm with K = 64, Bt a [rows][64] array swizzled as swz (rows 16 t + l % 16 of tile t).
+template <int NT>
+__device__ __forceinline__ void mm_swz(const float* A, int lda, const float* Bsw, int lane, f32x4 (&acc)[NT]) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* a = A + r * lda + 4 * q;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(a + 16 * kb);
+    f32x4 bv[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = 16 * t + r;
+      bv[t] = *reinterpret_cast<const f32x4*>(Bsw + n * 64 + 4 * ((4 * kb + q) ^ r));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = mma4(av[m], bv[t][m], acc[t]);
+  }
+}
+
 // sum over the 16 lanes of each row of 16 (lanes with the same l / 16)
 __device__ __forceinline__ float row16_sum(float v) {
   v += __shfl_xor(v, 1);
@@ -99,109 +124,152 @@ __device__ __forceinline__ Blk block_of(const BwdArgs& p) {
   return r;
 }
 
-// step size of step t (0 past the end)
-template <typename TIn>
-__device__ __forceinline__ float step_dt(const BwdArgs& p, const TIn* dr, int64_t t, float bias, float* sig) {
-  if (t >= p.L) {
-    if (sig) *sig = 0.f;
-    return 0.f;
-  }
-  const float x = to_f32(dr[t]) + bias;
-  if (sig) *sig = p.softplus ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
-  return p.softplus ? softplus_fast(x) : x;
+// One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes from `src` land at lds + 16 i
+// (lds is wave-uniform).  Completion is observed with s_waitcnt vmcnt.
+__device__ __forceinline__ void dma16(const float* src, float* lds) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
-// Pass 1: the state before every chunk, [blocks][chunks][NP][64] f32 ([n][p]).
+// Offset (floats) of granule g (4 floats) of row n in a [rows][64] array whose rows keep granule
+// g at position g ^ (n % 16): sixteen lanes reading the same granule of sixteen rows hit
+// different banks.
+__device__ __forceinline__ int swz(int n, int g) { return n * kCP + 4 * (g ^ (n & 15)); }
+
+// Pass 1: the state before every chunk, [blocks][chunks][NP][64] f32 (row n holds H0[0..63][n],
+// swizzled as swz), and C B^T of every chunk, [batch][groups][chunks][4 tiles][64 lanes][4] in the
+// lane order of the reverse pass's 16x16 tiles; a group's chunks are shared out over its blocks.
 template <typename TIn, int NT>
-__global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch, float* __restrict__ ws) {
+__global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch, float* __restrict__ ws,
+                                                          float* __restrict__ cbws) {
   constexpr int NP = 16 * NT;
-  __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // x^T [p][t]
-  __shared__ __attribute__((aligned(16))) float wb[NP * kST];    // e^{s_{T-1} - s_t} B [n][t]
-  __shared__ float ss2[kCT];                                     // cumulative log2 decay
+  constexpr int kSN = NP + 4;
+  __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // u^T [p][t]
+  __shared__ __attribute__((aligned(16))) float wb[NP * kST];    // e^{s_{T-1} - s_t} dt_t B [n][t]
+  __shared__ __attribute__((aligned(16))) float ctn[kCT * kSN];  // C [t][n] (chunks whose C B^T this block forms)
+  __shared__ __attribute__((aligned(16))) float btn[kCT * kSN];  // B [t][n]
+  __shared__ float ss2[kCT], sdt[kCT];                           // cumulative log2 decay, dt
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int q = lane >> 4, l16 = lane & 15;
   const Blk k = block_of(p);
   const int N = p.N;
+  const int64_t L = p.L;
   const float A2 = p.A[k.h] * kLog2e;
   const float bias = p.bias ? p.bias[k.h] : 0.f;
   const TIn* dr = static_cast<const TIn*>(p.delta) + k.b * p.dl_sb + k.h * p.dl_sh;
   const TIn* ub = static_cast<const TIn*>(p.u) + k.b * p.u_sb + k.d0 * p.u_sd;
   const TIn* Bb = static_cast<const TIn*>(p.B) + k.b * p.B_sb + k.g * p.B_sg;
+  const TIn* Cb = static_cast<const TIn*>(p.C) + k.b * p.C_sb + k.g * p.C_sg;
   float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  float* cbg = cbws + (k.b * p.groups + k.g) * nch * 1024;
+  const int ng = p.chan_per_group / kCP;                    // blocks sharing the group's B, C
+  const int gi = (int)((k.d0 % p.chan_per_group) / kCP);
+  // this thread's share of a chunk's loads: u (row pp, 8 steps from tt); B (row bn, 16 steps from bt)
+  const int pp = tid >> 2, tt = 8 * (tid & 3);
+  const int bn = tid >> 1, bt = 16 * (tid & 1);
+  float pu[8], pbv[16], pdl = 0.f;
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * kCT;
+    load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu);
+    if (bn < N) {
+      load_seg<16>(Bb + bn * p.B_sn, t0 + bt, L, p.vec, pbv);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) pbv[e] = 0.f;
+    }
+    if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
+  };
+  fetch(0);
   f32x4 H[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) H[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int64_t c = 0; c < nch; ++c) {
-    // the state before chunk c: lane holds H[p = 16 wave + 4 (l / 16) + r][n = 16 j + l % 16]
+    // the state before chunk c: lane holds H[p = 16 wave + 4 q + r][n = 16 j + l16], granule 4 wave + q
     float* hc = wsb + c * NP * kCP;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      *reinterpret_cast<f32x4*>(hc + (16 * j + (lane & 15)) * kCP + 16 * wave + 4 * (lane >> 4)) = H[j];
-    if (c == nch - 1) break;
+    for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(hc + swz(16 * j + l16, 4 * wave + q)) = H[j];
+    const bool cbjob = c % ng == gi;
+    if (c == nch - 1 && !cbjob) break;
     const int64_t t0 = c * kCT;
     if (wave == 0) {
-      float s = lane < kCT ? step_dt(p, dr, t0 + lane, bias, nullptr) * A2 : 0.f;
+      const float x = pdl + bias;
+      const float dt = (lane < kCT && t0 + lane < L) ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+      float s = dt * A2;
 #pragma unroll
       for (int off = 1; off < kCT; off <<= 1) {
         const float v = __shfl_up(s, off);
         if (lane >= off) s += v;
       }
-      if (lane < kCT) ss2[lane] = s;
-    }
-    {
-      // x^T: thread (p = tid / 4, steps 8 (tid % 4) ..)
-      const int pp = tid >> 2, tt = 8 * (tid & 3);
-      float v[8];
-      load_seg<8>(ub + pp * p.u_sd, t0 + tt, p.L, p.vec, v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] *= step_dt(p, dr, t0 + tt + e, bias, nullptr);
-      *reinterpret_cast<f32x4*>(xt + pp * kST + tt) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(xt + pp * kST + tt + 4) = f32x4{v[4], v[5], v[6], v[7]};
-    }
-    __syncthreads();   // ss2 ready
-    for (int i = tid; i < NP * 2; i += kThr) {
-      const int n = i >> 1, tt = 16 * (i & 1);
-      float v[16];
-      if (n < N) {
-        load_seg<16>(Bb + n * p.B_sn, t0 + tt, p.L, p.vec, v);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) v[e] = 0.f;
+      if (lane < kCT) {
+        ss2[lane] = s;
+        sdt[lane] = dt;
       }
+    }
+    *reinterpret_cast<f32x4*>(xt + pp * kST + tt) = f32x4{pu[0], pu[1], pu[2], pu[3]};
+    *reinterpret_cast<f32x4*>(xt + pp * kST + tt + 4) = f32x4{pu[4], pu[5], pu[6], pu[7]};
+    if (cbjob) {
+      // this chunk's C and B with n contiguous, for C B^T
+      for (int i = tid; i < NP * 4; i += kThr) {
+        const int n = i >> 2, t8 = 8 * (i & 3);
+        float v[8], w[8];
+        if (n < N) {
+          load_seg<8>(Cb + n * p.C_sn, t0 + t8, L, p.vec, v);
+          load_seg<8>(Bb + n * p.B_sn, t0 + t8, L, p.vec, w);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = w[e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ctn[(t8 + e) * kSN + n] = v[e];
+          btn[(t8 + e) * kSN + n] = w[e];
+        }
+      }
+    }
+    __syncthreads();   // ss2, sdt, xt, ctn, btn ready
+    if (bn < NP) {
       const float send = ss2[kCT - 1];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) v[e] *= __builtin_amdgcn_exp2f(send - ss2[tt + e]);
+      for (int e = 0; e < 16; ++e) pbv[e] *= sdt[bt + e] * __builtin_amdgcn_exp2f(send - ss2[bt + e]);
 #pragma unroll
       for (int e = 0; e < 16; e += 4)
-        *reinterpret_cast<f32x4*>(wb + n * kST + tt + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
+        *reinterpret_cast<f32x4*>(wb + bn * kST + bt + e) = f32x4{pbv[e], pbv[e + 1], pbv[e + 2], pbv[e + 3]};
     }
-    __syncthreads();
+    if (c + 1 < nch) fetch(c + 1);   // the next chunk's loads run under this chunk's products
+    if (cbjob) {
+      f32x4 cb[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+      mm<NP, 1>(ctn + 16 * (wave >> 1) * kSN, kSN, btn + 16 * (wave & 1) * kSN, kSN, 0, lane, cb);
+      *reinterpret_cast<f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4) = cb[0];
+    }
+    __syncthreads();   // wb ready
+    if (c == nch - 1) break;
     const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
 #pragma unroll
     for (int j = 0; j < NT; ++j) H[j] = H[j] * dec;
     mm<kCT, NT>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
-    __syncthreads();   // xt, wb, ss2 are rewritten by the next chunk
+    __syncthreads();   // xt, wb, ss2, ctn, btn are rewritten by the next chunk
   }
 }
 
 // Pass 2: the chunks in reverse.
 template <typename TIn, typename TDy, int NT>
-__global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws) {
+__global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws,
+                                                         const float* __restrict__ cbws) {
   constexpr int NP = 16 * NT;
   constexpr int NH = NT / 2;   // [T x N] tiles per wave (two waves per 16 rows; NT >= 2)
-  __shared__ __attribute__((aligned(16))) float xn[kCT * kSP];    // x [t][p]
+  __shared__ __attribute__((aligned(16))) float xn[kCT * kSP];    // u [t][p]
   __shared__ __attribute__((aligned(16))) float dyn[kCT * kSP];   // dy [t][p]
   __shared__ __attribute__((aligned(16))) float dyt[kCP * kST];   // dy [p][t]
   __shared__ __attribute__((aligned(16))) float bnt[NP * kST];    // B [n][t]
   __shared__ __attribute__((aligned(16))) float cnt[NP * kST];    // C [n][t]
   __shared__ __attribute__((aligned(16))) float rnp[NP * kSP];    // R [n][p]
-  __shared__ __attribute__((aligned(16))) float hnp[NP * kSP];    // H0 [n][p]
+  __shared__ __attribute__((aligned(16))) float hnp[NP * kCP];    // H0 [n][p], swizzled (copied straight from pass 1)
   __shared__ __attribute__((aligned(16))) float m1[kCT * kST];    // M1 [k][j]
   __shared__ __attribute__((aligned(16))) float m1t[kCT * kST];   // M1^T [j][k]
   __shared__ __attribute__((aligned(16))) float lcbt[kCT * kST];  // (L o CB)^T [j][k]
-  __shared__ __attribute__((aligned(16))) float wm[kCT * kST];    // M1 o CB [k][i], then its row prefix sums
   __shared__ __attribute__((aligned(16))) float ses[kCT];         // e^{s_t}
   __shared__ float ss2[kCT], ser[kCT], sdt[kCT], ssig[kCT];
-  __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rh0[4];
+  __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rowp[2][kCT], colp[2][kCT], rh0[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const Blk k = block_of(p);
@@ -220,7 +288,38 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
   float* dub = p.du + k.b * p.du_sb + k.d0 * p.du_sd;
   float* ddb = p.ddelta + k.b * p.dd_sb + k.h * p.dd_sh;
   const float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  const float* cbg = cbws + (k.b * p.groups + k.g) * nch * 1024;
   const int ti = wave >> 1, half = wave & 1;   // 16-step row block and column half of this wave
+  // H0 of chunk c into hnp: NP / 4 copies of 1 KB, shared out over the waves
+  auto h0_copy = [&](int64_t c) {
+    const float* hc = wsb + c * NP * kCP;
+    for (int i = wave; i < NP / 4; i += 4) dma16(hc + i * 256 + 4 * lane, hnp + i * 256);
+  };
+  h0_copy(nch - 1);
+  // this thread's share of a chunk's loads, fetched one chunk ahead: u and dy (row pp, 8 steps
+  // from tt), B and C (BCI items of 8 steps), the raw step (wave 0)
+  constexpr int BCI = (NP * 4 + kThr - 1) / kThr;
+  const int pp = tid >> 2, tt = 8 * (tid & 3);
+  float pu[8], py[8], pb[BCI][8], pc[BCI][8], pdl = 0.f;
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * kCT;
+    load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu);
+    load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, py);
+#pragma unroll
+    for (int it = 0; it < BCI; ++it) {
+      const int i = tid + it * kThr;
+      const int n = i >> 2, t8 = 8 * (i & 3);
+      if (i < NP * 4 && n < N) {
+        load_seg<8>(Bb + n * p.B_sn, t0 + t8, L, p.vec, pb[it]);
+        load_seg<8>(Cb + n * p.C_sn, t0 + t8, L, p.vec, pc[it]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[it][e] = pc[it][e] = 0.f;
+      }
+    }
+    if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
+  };
+  fetch(nch - 1);
   // D of the channels this lane's dX tiles cover
   float Dp[2];
 #pragma unroll
@@ -236,10 +335,12 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
 
   for (int64_t c = nch - 1; c >= 0; --c) {
     const int64_t t0 = c * kCT;
-    // ---- staging
+    // ---- staging (from the registers fetched during the previous chunk)
     if (wave == 0) {
-      float sg = 0.f;
-      const float dt = lane < kCT ? step_dt(p, dr, t0 + lane, bias, &sg) : 0.f;
+      const bool live = lane < kCT && t0 + lane < L;
+      const float x = pdl + bias;
+      const float dt = live ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+      const float sg = live ? (p.softplus ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f) : 0.f;
       float s = dt * A2;
 #pragma unroll
       for (int off = 1; off < kCT; off <<= 1) {
@@ -255,79 +356,71 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
         ser[lane] = __builtin_amdgcn_exp2f(send - s);
       }
     }
-    {
-      // x and dy of the slab: thread (p = tid / 4, steps 8 (tid % 4) ..)
-      const int pp = tid >> 2, tt = 8 * (tid & 3);
-      float v[8], w[8];
-      load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, v);
-      load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, w);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        xn[(tt + e) * kSP + pp] = v[e] * step_dt(p, dr, t0 + tt + e, bias, nullptr);
-        dyn[(tt + e) * kSP + pp] = w[e];
-      }
-      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{w[4], w[5], w[6], w[7]};
+    for (int e = 0; e < 8; ++e) {
+      xn[(tt + e) * kSP + pp] = pu[e];
+      dyn[(tt + e) * kSP + pp] = py[e];
     }
-    for (int i = tid; i < NP * 4; i += kThr) {
-      // B and C rows: (n = i / 4, steps 8 (i % 4) ..); rows past N are zero
-      const int n = i >> 2, tt = 8 * (i & 3);
-      float v[8], w[8];
-      if (n < N) {
-        load_seg<8>(Bb + n * p.B_sn, t0 + tt, L, p.vec, v);
-        load_seg<8>(Cb + n * p.C_sn, t0 + tt, L, p.vec, w);
-      } else {
+    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{py[0], py[1], py[2], py[3]};
+    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{py[4], py[5], py[6], py[7]};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = w[e] = 0.f;
+    for (int it = 0; it < BCI; ++it) {
+      const int i = tid + it * kThr;
+      if (i < NP * 4) {
+        const int n = i >> 2, t8 = 8 * (i & 3);
+        const float* v = pb[it];
+        const float* w = pc[it];
+        *reinterpret_cast<f32x4*>(bnt + n * kST + t8) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(bnt + n * kST + t8 + 4) = f32x4{v[4], v[5], v[6], v[7]};
+        *reinterpret_cast<f32x4*>(cnt + n * kST + t8) = f32x4{w[0], w[1], w[2], w[3]};
+        *reinterpret_cast<f32x4*>(cnt + n * kST + t8 + 4) = f32x4{w[4], w[5], w[6], w[7]};
       }
-      *reinterpret_cast<f32x4*>(bnt + n * kST + tt) = f32x4{v[0], v[1], v[2], v[3]};
-      *reinterpret_cast<f32x4*>(bnt + n * kST + tt + 4) = f32x4{v[4], v[5], v[6], v[7]};
-      *reinterpret_cast<f32x4*>(cnt + n * kST + tt) = f32x4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<f32x4*>(cnt + n * kST + tt + 4) = f32x4{w[4], w[5], w[6], w[7]};
     }
-    {
-      // H0 of the chunk into LDS; R (the carry from the right) too
-      const float* hc = wsb + c * NP * kCP;
-      for (int i = tid; i < NP * kCP / 4; i += kThr) {
-        const int n = i / (kCP / 4), pq = 4 * (i % (kCP / 4));
-        *reinterpret_cast<f32x4*>(hnp + n * kSP + pq) = *reinterpret_cast<const f32x4*>(hc + n * kCP + pq);
-      }
+    // R (the carry from the right) into LDS
 #pragma unroll
-      for (int j = 0; j < NT; ++j)
-        *reinterpret_cast<f32x4*>(rnp + (16 * j + l16) * kSP + 16 * wave + 4 * q) = R[j];
-    }
+    for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(rnp + (16 * j + l16) * kSP + 16 * wave + 4 * q) = R[j];
+    // this wave's tile of C B^T (formed by pass 1)
+    const f32x4 cb = *reinterpret_cast<const f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4);
+    // the copies of H0 into hnp have landed (this wave's), then everyone's
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
     // ---- DX = dY X^T and CB = C B^T (one 16x16 tile each per wave), then the masked matrices
     {
       f32x4 dx[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       mm<kCP, 1>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
-      f32x4 cb = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NT; ++kb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int n = 16 * kb + 4 * q + m;
-          cb = mma4(cnt[n * kST + 16 * ti + l16], bnt[n * kST + 16 * half + l16], cb);
-        }
+      const int s = 16 * half + l16;   // column j = s of this lane; rows k = t below
+      const float dts = sdt[s];
+      float csum = 0.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * ti + 4 * q + r, s = 16 * half + l16;   // row k = t, column j = s
+        const int t = 16 * ti + 4 * q + r;
         const float e = t >= s ? __builtin_amdgcn_exp2f(ss2[t] - ss2[s]) : 0.f;
-        const float mv = e * dx[0][r];
+        const float mv = e * dx[0][r] * dts;   // X = diag(dt) U
         m1[t * kST + s] = mv;
         m1t[s * kST + t] = mv;
         lcbt[s * kST + t] = e * cb[r];
-        wm[t * kST + s] = mv * cb[r];
+        // W = M1 o CB: this tile's part of row t's and column s's sums
+        const float wv = mv * cb[r];
+        csum += wv;
+        const float rs = row16_sum(wv);
+        if (l16 == 0) rowp[half][t] = rs;
       }
+      csum += __shfl_xor(csum, 16);
+      csum += __shfl_xor(csum, 32);
+      if (q == 0) colp[ti][s] = csum;
     }
     // ---- dY H0 and X R ([T x N] tiles: rows 16 ti, columns 16 (half NH + j))
     f32x4 yh[NH], xr[NH];
 #pragma unroll
     for (int j = 0; j < NH; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nj0 = half * NH;
-    mm<kCP, NH>(dyn + 16 * ti * kSP, kSP, hnp + 16 * nj0 * kSP, kSP, 16 * kSP, lane, yh);
+    mm_swz<NH>(dyn + 16 * ti * kSP, kSP, hnp + 16 * nj0 * kCP, lane, yh);
     mm<kCP, NH>(xn + 16 * ti * kSP, kSP, rnp + 16 * nj0 * kSP, kSP, 16 * kSP, lane, xr);
+#pragma unroll
+    for (int j = 0; j < NH; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) xr[j][r] *= sdt[16 * ti + 4 * q + r];   // X R = diag(dt) U R
     {
       // alpha_t = e^{s_t} (dY H0)_t . C_t and beta_t = e^{s_{T-1} - s_t} (X R)_t . B_t, partial over
       // this wave's columns
@@ -352,13 +445,17 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       float rh = 0.f;
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const f32x4 hv = *reinterpret_cast<const f32x4*>(hnp + (16 * j + l16) * kSP + 16 * wave + 4 * q);
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(hnp + swz(16 * j + l16, 4 * wave + q));
         rh = fmaf(R[j][0], hv[0], fmaf(R[j][1], hv[1], fmaf(R[j][2], hv[2], fmaf(R[j][3], hv[3], rh))));
       }
       rh = wave_total(rh);
       if (lane == 0) rh0[wave] = rh;
     }
-    __syncthreads();   // m1, m1t, lcbt, wm, alp, bet, rh0 ready
+    __syncthreads();   // m1, m1t, lcbt, row and column sums, alp, bet, rh0 ready; hnp no longer read
+    if (c > 0) {
+      h0_copy(c - 1);   // lands while this chunk's second half runs
+      fetch(c - 1);
+    }
 
     // ---- dC = diag(e^s) dY H0 + M1 B and dB = diag(e^{s_{T-1} - s}) X R + M1^T C, added to the group's
     {
@@ -391,15 +488,26 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
     // ---- dX = diag(e^{s_{T-1} - s}) B R^T + (L o CB)^T dY ([T x 64]: rows 16 ti, columns 16 (2 half + pt))
     {
       f32x4 dxa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kb = 0; kb < NT; ++kb)
+      // B R^T over n: the operands of block kb + 1 are read while block kb's products run
+      float oa[2][4], ob[2][2][4];
+      auto rd = [&](int kb, int s) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int n = 16 * kb + 4 * q + m;
-          const float a = bnt[n * kST + 16 * ti + l16];
+          oa[s][m] = bnt[n * kST + 16 * ti + l16];
 #pragma unroll
-          for (int pt = 0; pt < 2; ++pt) dxa[pt] = mma4(a, rnp[n * kSP + 16 * (2 * half + pt) + l16], dxa[pt]);
+          for (int pt = 0; pt < 2; ++pt) ob[s][pt][m] = rnp[n * kSP + 16 * (2 * half + pt) + l16];
         }
+      };
+      rd(0, 0);
+#pragma unroll
+      for (int kb = 0; kb < NT; ++kb) {
+        if (kb + 1 < NT) rd(kb + 1, (kb + 1) & 1);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int pt = 0; pt < 2; ++pt) dxa[pt] = mma4(oa[kb & 1][m], ob[kb & 1][pt][m], dxa[pt]);
+      }
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
@@ -410,7 +518,6 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const int pch = 16 * (2 * half + pt) + l16;
-        const TIn* urow = ub + pch * p.u_sd;
         float* durow = dub + pch * p.du_sd;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -418,7 +525,7 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
           const int64_t t = t0 + tl;
           if (t < L) {
             const float dyv = dyn[tl * kSP + pch];
-            const float uv = to_f32(urow[t]);
+            const float uv = xn[tl * kSP + pch];
             durow[t] = fmaf(sdt[tl], dxa[pt][r], Dp[pt] * dyv);
             ud[r] = fmaf(uv, dxa[pt][r], ud[r]);
             dDl[pt] = fmaf(dyv, uv, dDl[pt]);
@@ -440,25 +547,27 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       mm<kCT, NT, true>(dyt + 16 * wave * kST, kST, cnt, kST, 16 * kST, lane, R, ses);
     }
 
-    // ---- the decay's gradient per step
-    if (tid < kCT) {
-      // row prefix sums of M1 o CB: wm[k][i] <- sum_{i' <= i} wm[k][i']
-      float acc = 0.f;
-      for (int i = 0; i <= tid; ++i) {   // only i <= k is non-zero
-        acc += wm[tid * kST + i];
-        wm[tid * kST + i] = acc;
-      }
-      for (int i = tid + 1; i < kCT; ++i) wm[tid * kST + i] = acc;
-    }
-    __syncthreads();   // udp, wm prefix sums ready
-    if (tid < kCT) {
-      const int j = tid;
-      float t1 = 0.f, t2 = 0.f, t3 = 0.f;
-      for (int kk = j; kk < kCT; ++kk) {
-        t1 += wm[kk * kST + j];
-        t2 += alp[0][kk] + alp[1][kk];
-      }
-      for (int i = 0; i <= j; ++i) t3 += bet[0][i] + bet[1][i];
+    // ---- the decay's gradient per step (wave 0; lane j = step j; scans over the 32 steps)
+    __syncthreads();   // udp ready
+    if (wave == 0) {
+      const int j = lane & (kCT - 1);
+      const bool lo = lane < kCT;
+      // inclusive prefix sums over lanes 0..31 (lanes 32..63 repeat them and are ignored)
+      auto scan = [&](float v) {
+#pragma unroll
+        for (int off = 1; off < kCT; off <<= 1) {
+          const float w = __shfl_up(v, off);
+          if (j >= off) v += w;
+        }
+        return v;
+      };
+      const float col = colp[0][j] + colp[1][j], row = rowp[0][j] + rowp[1][j];
+      const float al = alp[0][j] + alp[1][j], be = bet[0][j] + bet[1][j];
+      const float pcol = scan(col), prow = scan(row), pal = scan(al), pbe = scan(be);
+      const float altot = __shfl(pal, kCT - 1);
+      const float t1 = pcol - (prow - row);     // sum over k >= j >= i of W_ki
+      const float t2 = altot - (pal - al);      // sum over k >= j of alpha_k
+      const float t3 = pbe;                     // sum over i <= j of beta_i
       const float t4 = __builtin_amdgcn_exp2f(ss2[kCT - 1]) * (rh0[0] + rh0[1] + rh0[2] + rh0[3]);
       const float gh = t1 + t2 + t3 + t4;
       const float ud = udp[0][j] + udp[1][j];
@@ -466,7 +575,7 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       const float qa = gh - dt * ud;                 // a_j dLoss/da_j
       const float ddt = fmaf(Ah, qa, ud);
       const float dx = ddt * ssig[j];
-      if (t0 + j < L) {
+      if (lo && t0 + j < L) {
         if (slabs == 1) ddb[t0 + j] = dx;
         else atomicAdd(ddb + t0 + j, dx);
         dAacc = fmaf(dt, qa, dAacc);
@@ -504,8 +613,10 @@ template <typename TIn, typename TDy, int NT>
 hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
   const int64_t nch = (a.L + kCT - 1) / kCT;
   const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
-  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), grid, block, 0, s, a, nch, ws);
-  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, block, 0, s, a, nch, static_cast<const float*>(ws));
+  float* cbws = ws + a.batch * a.heads * (a.chan_per_head / kCP) * nch * (16 * NT) * kCP;
+  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), grid, block, 0, s, a, nch, ws, cbws);
+  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, block, 0, s, a, nch, static_cast<const float*>(ws),
+                     static_cast<const float*>(cbws));
   return hipGetLastError();
 }
 
@@ -525,7 +636,8 @@ bool ssd_bwd_path(const BwdArgs& a) {
 int64_t ssd_bwd_workspace_floats(const BwdArgs& a) {
   const int64_t np = a.N <= 32 ? 32 : a.N <= 64 ? 64 : 128;
   const int64_t nch = (a.L + kCT - 1) / kCT;
-  return a.batch * a.heads * (a.chan_per_head / kCP) * nch * np * kCP;
+  // chunk states, then C B^T of every (batch, group, chunk)
+  return a.batch * a.heads * (a.chan_per_head / kCP) * nch * np * kCP + a.batch * a.groups * nch * 1024;
 }
 
 hipError_t launch_ssd_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
