@@ -93,18 +93,39 @@ __device__ __forceinline__ void mm_swz(const float* A, int lda, const float* Bsw
   }
 }
 
-// sum over the 16 lanes of each row of 16 (lanes with the same l / 16)
+// DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source keep `old`
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ float dpp(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWMASK, 0xf, false));
+}
+
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// sum over each row of 16 lanes (lanes with the same l / 16), in every lane: row_ror 8, 4, 2, 1
 __device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1);
-  v += __shfl_xor(v, 2);
-  v += __shfl_xor(v, 4);
-  v += __shfl_xor(v, 8);
+  v += dpp<0x128>(0.f, v);
+  v += dpp<0x124>(0.f, v);
+  v += dpp<0x122>(0.f, v);
+  v += dpp<0x121>(0.f, v);
   return v;
 }
 
+// sum over the wave (wave-uniform)
 __device__ __forceinline__ float wave_total(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = row16_sum(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+
+// inclusive prefix sum over lanes 0..31 (and, separately, over lanes 32..63): row_shr 1, 2, 4, 8
+// within rows of 16, then row_bcast:15 adds the last lane of rows 0 and 2 to rows 1 and 3
+__device__ __forceinline__ float scan32(float v) {
+  v += dpp<0x111>(0.f, v);
+  v += dpp<0x112>(0.f, v);
+  v += dpp<0x114>(0.f, v);
+  v += dpp<0x118>(0.f, v);
+  v += dpp<0x142, 0xa>(0.f, v);
   return v;
 }
 
@@ -194,12 +215,7 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
     if (wave == 0) {
       const float x = pdl + bias;
       const float dt = (lane < kCT && t0 + lane < L) ? (p.softplus ? softplus_fast(x) : x) : 0.f;
-      float s = dt * A2;
-#pragma unroll
-      for (int off = 1; off < kCT; off <<= 1) {
-        const float v = __shfl_up(s, off);
-        if (lane >= off) s += v;
-      }
+      const float s = scan32(dt * A2);
       if (lane < kCT) {
         ss2[lane] = s;
         sdt[lane] = dt;
@@ -341,13 +357,8 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       const float x = pdl + bias;
       const float dt = live ? (p.softplus ? softplus_fast(x) : x) : 0.f;
       const float sg = live ? (p.softplus ? __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f) : 0.f;
-      float s = dt * A2;
-#pragma unroll
-      for (int off = 1; off < kCT; off <<= 1) {
-        const float v = __shfl_up(s, off);
-        if (lane >= off) s += v;
-      }
-      const float send = __shfl(s, kCT - 1);
+      const float s = scan32(dt * A2);
+      const float send = lane_f(s, kCT - 1);
       if (lane < kCT) {
         ss2[lane] = s;
         sdt[lane] = dt;
@@ -553,18 +564,10 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       const int j = lane & (kCT - 1);
       const bool lo = lane < kCT;
       // inclusive prefix sums over lanes 0..31 (lanes 32..63 repeat them and are ignored)
-      auto scan = [&](float v) {
-#pragma unroll
-        for (int off = 1; off < kCT; off <<= 1) {
-          const float w = __shfl_up(v, off);
-          if (j >= off) v += w;
-        }
-        return v;
-      };
       const float col = colp[0][j] + colp[1][j], row = rowp[0][j] + rowp[1][j];
       const float al = alp[0][j] + alp[1][j], be = bet[0][j] + bet[1][j];
-      const float pcol = scan(col), prow = scan(row), pal = scan(al), pbe = scan(be);
-      const float altot = __shfl(pal, kCT - 1);
+      const float pcol = scan32(col), prow = scan32(row), pal = scan32(al), pbe = scan32(be);
+      const float altot = lane_f(pal, kCT - 1);
       const float t1 = pcol - (prow - row);     // sum over k >= j >= i of W_ki
       const float t2 = altot - (pal - al);      // sum over k >= j of alpha_k
       const float t3 = pbe;                     // sum over i <= j of beta_i
