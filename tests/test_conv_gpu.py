@@ -161,3 +161,37 @@ def test_conv_full_size_layer_sampled_rows():
     ref, _, S = expected(sample, True, state=False)
     worst = check(got[rows][None], ref, S, 4, True)
     say("[conv] full-size layer, 48 sampled rows: err/bound %.3f" % worst)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_conv_then_scan_matches_the_oracle_chain(dtype):
+    """The block's order: the convolution (W = 4, silu) produces the scan's input u, then the scan
+    runs on it.  The GPU chain (ss_conv1d writing u in the input dtype, then ss_scan_fwd) against
+    the oracle's convolution followed by the oracle's scan on the same rounded u."""
+    torch = torch_dev()
+    import dataclasses
+
+    from conftest import normwise
+    from selective_state_space_88_amd.scan import conv1d, scan_fwd
+
+    p = inputs.random_problem(995, 2, 24, 600, 16, in_dtype=dtype)
+    c = inputs.random_conv(996, 2, 24, 600, 4, in_dtype=dtype, with_state=False)
+    x = to_dev(c["x"])
+    u = conv1d(x, to_dev(c["w"]), to_dev(c["bias"]), silu=True, out_dtype=x.dtype)
+    t = {k: to_dev(getattr(p, k)) for k in ("delta", "A", "B", "C", "D", "z", "delta_bias")}
+    y = scan_fwd(u, t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], softplus=p.softplus)
+    torch.cuda.synchronize()
+    # the oracle chain: its convolution, rounded to the scan's input dtype as the GPU stores it
+    ref_u = oracle.conv1d(c["x"], c["w"], c["bias"], silu=True)
+    u32 = ref_u.astype(np.float32)
+    u_in = inputs.f32_to_bf16_bits(u32).reshape(u32.shape) if dtype == "bf16" else u32
+    gu = u.float().cpu().numpy()
+    # the stored u agrees with the oracle's to within one rounding of the input dtype
+    tol_u = 2.0 ** -8 if dtype == "bf16" else 1e-6
+    assert np.max(np.abs(gu - inputs.to_f32(u_in))) <= tol_u * (np.max(np.abs(u32)) + 1e-30) * 2
+    # the scan on the GPU's own u against the oracle's scan on the same u
+    gp = dataclasses.replace(p, u=(inputs.f32_to_bf16_bits(gu).reshape(gu.shape) if dtype == "bf16" else gu))
+    ref = oracle.scan_problem(gp)
+    err = normwise(y.cpu().numpy(), ref)
+    say("[conv->scan] %s: normwise %.3e" % (dtype, err))
+    assert err <= (2e-3 if dtype == "bf16" else 1e-5)
