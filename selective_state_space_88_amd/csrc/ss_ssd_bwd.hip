@@ -29,6 +29,8 @@
 // order of k inside a block of 16 is permuted the same way on both operands).  dB and dC are
 // summed over the group's heads with atomic adds; per-head sums (ddelta over slabs, dA, dD,
 // dbias) likewise.  No gate (the gated layout takes the per-channel kernel).
+#include <type_traits>
+
 #include "ss_device.h"
 #include "ss_launch.h"
 
@@ -133,9 +135,8 @@ struct Blk {
   int64_t b, h, g, d0;
 };
 
-__device__ __forceinline__ Blk block_of(const BwdArgs& p) {
+__device__ __forceinline__ Blk block_of(const BwdArgs& p, int64_t blk) {
   const int slabs = p.chan_per_head / kCP;
-  const int64_t blk = blockIdx.x;
   const int64_t bh = blk / slabs, slab = blk % slabs;
   Blk r;
   r.b = bh / p.heads;
@@ -160,19 +161,24 @@ __device__ __forceinline__ int swz(int n, int g) { return n * kCP + 4 * (g ^ (n 
 // Pass 1: the state before every chunk, [blocks][chunks][NP][64] f32 (row n holds H0[0..63][n],
 // swizzled as swz), and C B^T of every chunk, [batch][groups][chunks][4 tiles][64 lanes][4] in the
 // lane order of the reverse pass's 16x16 tiles; a group's chunks are shared out over its blocks.
+// The states evolve independently, so each (batch, head, slab) takes two blocks, one per half of
+// the states (more blocks than CUs on the multi-head layers).
 template <typename TIn, int NT>
 __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch, float* __restrict__ ws,
                                                           float* __restrict__ cbws) {
   constexpr int NP = 16 * NT;
+  constexpr int NH = NT / 2, NPH = NP / 2;   // this block's state tiles and states
   constexpr int kSN = NP + 4;
   __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // u^T [p][t]
-  __shared__ __attribute__((aligned(16))) float wb[NP * kST];    // e^{s_{T-1} - s_t} dt_t B [n][t]
+  __shared__ __attribute__((aligned(16))) float wb[NPH * kST];   // e^{s_{T-1} - s_t} dt_t B [n][t], this half
   __shared__ __attribute__((aligned(16))) float ctn[kCT * kSN];  // C [t][n] (chunks whose C B^T this block forms)
   __shared__ __attribute__((aligned(16))) float btn[kCT * kSN];  // B [t][n]
   __shared__ float ss2[kCT], sdt[kCT];                           // cumulative log2 decay, dt
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const Blk k = block_of(p);
+  const int64_t bx = blockIdx.x >> 1;
+  const int nh = blockIdx.x & 1;             // half of the states: rows nh NPH ..
+  const Blk k = block_of(p, bx);
   const int N = p.N;
   const int64_t L = p.L;
   const float A2 = p.A[k.h] * kLog2e;
@@ -181,39 +187,49 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
   const TIn* ub = static_cast<const TIn*>(p.u) + k.b * p.u_sb + k.d0 * p.u_sd;
   const TIn* Bb = static_cast<const TIn*>(p.B) + k.b * p.B_sb + k.g * p.B_sg;
   const TIn* Cb = static_cast<const TIn*>(p.C) + k.b * p.C_sb + k.g * p.C_sg;
-  float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  float* wsb = ws + bx * nch * NP * kCP;
   float* cbg = cbws + (k.b * p.groups + k.g) * nch * 1024;
   const int ng = p.chan_per_group / kCP;                    // blocks sharing the group's B, C
   const int gi = (int)((k.d0 % p.chan_per_group) / kCP);
-  // this thread's share of a chunk's loads: u (row pp, 8 steps from tt); B (row bn, 16 steps from bt)
+  // this thread's share of a chunk's loads: u (row pp, 8 steps from tt); B (row nh NPH + bn of
+  // the half, 16 steps from bt)
   const int pp = tid >> 2, tt = 8 * (tid & 3);
-  const int bn = tid >> 1, bt = 16 * (tid & 1);
-  float pu[8], pbv[16], pdl = 0.f;
-  auto fetch = [&](int64_t c) {
+  const int bn = tid >> 1, bt = 16 * (tid & 1), bnr = nh * NPH + bn;
+  // two register sets, so that a chunk's loads are issued two chunks ahead of their use
+  float pu[2][8], pbv[2][16], pdl[2] = {0.f, 0.f};
+  auto fetch = [&](int64_t c, auto S) {
+    constexpr int r = decltype(S)::value;
     const int64_t t0 = c * kCT;
-    load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu);
-    if (bn < N) {
-      load_seg<16>(Bb + bn * p.B_sn, t0 + bt, L, p.vec, pbv);
+    load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu[r]);
+    if (bn < NPH && bnr < N) {
+      load_seg<16>(Bb + bnr * p.B_sn, t0 + bt, L, p.vec, pbv[r]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pbv[e] = 0.f;
+      for (int e = 0; e < 16; ++e) pbv[r][e] = 0.f;
     }
-    if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
+    if (wave == 0) pdl[r] = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
   };
-  fetch(0);
-  f32x4 H[NT];
+  const std::integral_constant<int, 0> set0{};
+  const std::integral_constant<int, 1> set1{};
+  fetch(0, set0);
+  if (nch > 1) fetch(1, set1);
+  f32x4 H[NH];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) H[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t c = 0; c < nch; ++c) {
-    // the state before chunk c: lane holds H[p = 16 wave + 4 q + r][n = 16 j + l16], granule 4 wave + q
+  for (int j = 0; j < NH; ++j) H[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // chunk c from register set S; false once the walk is over
+  auto step = [&](int64_t c, auto S) -> bool {
+    constexpr int r = decltype(S)::value;
+    // the state before chunk c: lane holds H[p = 16 wave + 4 q + r'][n = NPH nh + 16 j + l16],
+    // granule 4 wave + q
     float* hc = wsb + c * NP * kCP;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(hc + swz(16 * j + l16, 4 * wave + q)) = H[j];
-    const bool cbjob = c % ng == gi;
-    if (c == nch - 1 && !cbjob) break;
+    for (int j = 0; j < NH; ++j)
+      *reinterpret_cast<f32x4*>(hc + swz(nh * NPH + 16 * j + l16, 4 * wave + q)) = H[j];
+    const bool cbjob = nh == 0 && c % ng == gi;
+    if (c == nch - 1 && !cbjob) return false;
     const int64_t t0 = c * kCT;
     if (wave == 0) {
-      const float x = pdl + bias;
+      const float x = pdl[r] + bias;
       const float dt = (lane < kCT && t0 + lane < L) ? (p.softplus ? softplus_fast(x) : x) : 0.f;
       const float s = scan32(dt * A2);
       if (lane < kCT) {
@@ -221,8 +237,8 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
         sdt[lane] = dt;
       }
     }
-    *reinterpret_cast<f32x4*>(xt + pp * kST + tt) = f32x4{pu[0], pu[1], pu[2], pu[3]};
-    *reinterpret_cast<f32x4*>(xt + pp * kST + tt + 4) = f32x4{pu[4], pu[5], pu[6], pu[7]};
+    *reinterpret_cast<f32x4*>(xt + pp * kST + tt) = f32x4{pu[r][0], pu[r][1], pu[r][2], pu[r][3]};
+    *reinterpret_cast<f32x4*>(xt + pp * kST + tt + 4) = f32x4{pu[r][4], pu[r][5], pu[r][6], pu[r][7]};
     if (cbjob) {
       // this chunk's C and B with n contiguous, for C B^T
       for (int i = tid; i < NP * 4; i += kThr) {
@@ -243,27 +259,33 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
       }
     }
     __syncthreads();   // ss2, sdt, xt, ctn, btn ready
-    if (bn < NP) {
+    if (bn < NPH) {
       const float send = ss2[kCT - 1];
+      float* v = pbv[r];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pbv[e] *= sdt[bt + e] * __builtin_amdgcn_exp2f(send - ss2[bt + e]);
+      for (int e = 0; e < 16; ++e) v[e] *= sdt[bt + e] * __builtin_amdgcn_exp2f(send - ss2[bt + e]);
 #pragma unroll
       for (int e = 0; e < 16; e += 4)
-        *reinterpret_cast<f32x4*>(wb + bn * kST + bt + e) = f32x4{pbv[e], pbv[e + 1], pbv[e + 2], pbv[e + 3]};
+        *reinterpret_cast<f32x4*>(wb + bn * kST + bt + e) = f32x4{v[e], v[e + 1], v[e + 2], v[e + 3]};
     }
-    if (c + 1 < nch) fetch(c + 1);   // the next chunk's loads run under this chunk's products
+    if (c + 2 < nch) fetch(c + 2, S);   // this set's next chunk
     if (cbjob) {
       f32x4 cb[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       mm<NP, 1>(ctn + 16 * (wave >> 1) * kSN, kSN, btn + 16 * (wave & 1) * kSN, kSN, 0, lane, cb);
       *reinterpret_cast<f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4) = cb[0];
     }
     __syncthreads();   // wb ready
-    if (c == nch - 1) break;
+    if (c == nch - 1) return false;
     const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) H[j] = H[j] * dec;
-    mm<kCT, NT>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
+    for (int j = 0; j < NH; ++j) H[j] = H[j] * dec;
+    mm<kCT, NH>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
     __syncthreads();   // xt, wb, ss2, ctn, btn are rewritten by the next chunk
+    return true;
+  };
+  for (int64_t c = 0; c < nch; c += 2) {
+    if (!step(c, set0)) break;
+    if (c + 1 >= nch || !step(c + 1, set1)) break;
   }
 }
 
@@ -288,7 +310,7 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
   __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rowp[2][kCT], colp[2][kCT], rh0[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const Blk k = block_of(p);
+  const Blk k = block_of(p, blockIdx.x);
   const int N = p.N;
   const int64_t L = p.L;
   const float Ah = p.A[k.h], A2 = Ah * kLog2e;
@@ -617,7 +639,7 @@ hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
   const int64_t nch = (a.L + kCT - 1) / kCT;
   const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
   float* cbws = ws + a.batch * a.heads * (a.chan_per_head / kCP) * nch * (16 * NT) * kCP;
-  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), grid, block, 0, s, a, nch, ws, cbws);
+  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), dim3(2 * grid.x), block, 0, s, a, nch, ws, cbws);
   hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, block, 0, s, a, nch, static_cast<const float*>(ws),
                      static_cast<const float*>(cbws));
   return hipGetLastError();
