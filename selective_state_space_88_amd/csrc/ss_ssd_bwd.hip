@@ -306,7 +306,8 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
   __shared__ __attribute__((aligned(16))) float m1t[kCT * kST];   // M1^T [j][k]
   __shared__ __attribute__((aligned(16))) float lcbt[kCT * kST];  // (L o CB)^T [j][k]
   __shared__ __attribute__((aligned(16))) float ses[kCT];         // e^{s_t}
-  __shared__ float ss2[kCT], ser[kCT], sdt[kCT], ssig[kCT];
+  __shared__ __attribute__((aligned(16))) float sdt[kCT];
+  __shared__ float ss2[kCT], ser[kCT], ssig[kCT];
   __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rowp[2][kCT], colp[2][kCT], rh0[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
@@ -547,22 +548,30 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
         for (int r = 0; r < 4; ++r) dxa[pt][r] *= ser[16 * ti + 4 * q + r];
       mm<kCT, 2>(lcbt + 16 * ti * kST, kST, dyt + 16 * (2 * half) * kST, kST, 16 * kST, lane, dxa);
       // du = dt dX + D dy; u . dX per step; dD
+      // (the lane's 4 steps of a channel are consecutive: one 16-byte store when whole and aligned)
       float ud[4] = {0.f, 0.f, 0.f, 0.f};
+      const int tl0 = 16 * ti + 4 * q;
+      const f32x4 dt4 = *reinterpret_cast<const f32x4*>(sdt + tl0);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         const int pch = 16 * (2 * half + pt) + l16;
-        float* durow = dub + pch * p.du_sd;
+        float* dst = dub + pch * p.du_sd + t0 + tl0;
+        const f32x4 dy4 = *reinterpret_cast<const f32x4*>(dyt + pch * kST + tl0);
+        f32x4 du4;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int tl = 16 * ti + 4 * q + r;
-          const int64_t t = t0 + tl;
-          if (t < L) {
-            const float dyv = dyn[tl * kSP + pch];
-            const float uv = xn[tl * kSP + pch];
-            durow[t] = fmaf(sdt[tl], dxa[pt][r], Dp[pt] * dyv);
-            ud[r] = fmaf(uv, dxa[pt][r], ud[r]);
-            dDl[pt] = fmaf(dyv, uv, dDl[pt]);
-          }
+          const bool live = t0 + tl0 + r < L;
+          const float uv = live ? xn[(tl0 + r) * kSP + pch] : 0.f;
+          du4[r] = fmaf(dt4[r], dxa[pt][r], Dp[pt] * dy4[r]);
+          ud[r] = fmaf(uv, dxa[pt][r], ud[r]);
+          dDl[pt] = fmaf(dy4[r], uv, dDl[pt]);
+        }
+        if (t0 + tl0 + 4 <= L && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+          *reinterpret_cast<f32x4*>(dst) = du4;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (t0 + tl0 + r < L) dst[r] = du4[r];
         }
       }
 #pragma unroll
