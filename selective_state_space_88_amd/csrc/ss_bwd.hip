@@ -94,9 +94,13 @@ __device__ __forceinline__ void shift_down(float& A, float& B) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  // each row of 16 lanes summed by row_ror 8, 4, 2, 1 (every lane gets its row's total), then
+  // the four row totals
+  v += dpp_or<0x128, 0xf>(0.f, v);
+  v += dpp_or<0x124, 0xf>(0.f, v);
+  v += dpp_or<0x122, 0xf>(0.f, v);
+  v += dpp_or<0x121, 0xf>(0.f, v);
+  return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
 
 // Checkpoints: the state of every (row, window, state) at the window's start.
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
         c[2 * pp] = h0;
         if (2 * pp + 1 < N) c[2 * pp + 1] = h1;
       }
-      const float e0 = __shfl(fmaf(Af[0], h0, Bf[0]), 63), e1 = __shfl(fmaf(Af[1], h1, Bf[1]), 63);
+      const float e0 = readlane_f(fmaf(Af[0], h0, Bf[0]), 63), e1 = readlane_f(fmaf(Af[1], h1, Bf[1]), 63);
       if (lane == 0) {
         hst[wave][pp][0] = e0;
         hst[wave][pp][1] = e1;
@@ -177,6 +181,9 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
   __shared__ float dAl[kBWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
   // dB (2 states), dC (2 states) of the window's steps, step-major ([lane][k] = step lane K + k)
   __shared__ __attribute__((aligned(16))) float red[kBWaves][4][kBW];
+  // B (2 states) and C (2 states) of a pair's window, shared by the block's 4 channels; two
+  // buffers: the next pair's rows are loaded while this pair runs
+  __shared__ __attribute__((aligned(16))) float bcs[2][4][kBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t quads = p.chan_per_group / kBWaves;
@@ -202,6 +209,27 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
     dAl[wave][i] = 0.f;
   }
   float dDacc = 0.f, dbacc = 0.f;
+  // thread t stages row t / 64 (B of state 2 pp, of 2 pp + 1, C of 2 pp, of 2 pp + 1), the steps
+  // of lane t % 64; rows past N and steps past L are zero
+  const int srow = threadIdx.x >> 6, sseg = threadIdx.x & 63;
+  auto bc_load = [&](int64_t ww, int pq, float (&v)[kBK]) {
+    const int n = 2 * pq + (srow & 1);
+    const bool nv = n < N;
+    const TIn* src = srow < 2 ? Bg + (nv ? n : 0) * p.B_sn : Cg + (nv ? n : 0) * p.C_sn;
+    load_seg<kBK>(src, ww * kBW + (int64_t)kBK * sseg, nv ? L : 0, p.vec, v);
+  };
+  auto bc_store = [&](int bf, const float (&v)[kBK]) {
+    float* dst = &bcs[bf][srow][kBK * sseg];
+    *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+  };
+  {
+    float v[kBK];
+    bc_load(nwin - 1, 0, v);
+    bc_store(0, v);
+  }
+  __syncthreads();
+  int buf = 0;
 
   for (int64_t w = nwin - 1; w >= 0; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
@@ -233,6 +261,10 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
       for (int k = 0; k < kBK; ++k) ah[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
     }
     for (int pp = 0; pp < P; ++pp) {
+      // the next pair's B and C rows (the first pair of the window to the left after the last)
+      const bool more = pp + 1 < P || w > 0;
+      float nbc[kBK];
+      if (more) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
       float rB[2][kBK], rC[2][kBK];
       float dAp[2];
 #pragma unroll
@@ -241,11 +273,20 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         const bool nv = n < N;
         const float An = SCALAR ? p.A[hd] : (nv ? p.A[d * p.A_sd + n] : 0.f);
         const float A2 = An * kLog2e;
-        const TIn* Br = Bg + (nv ? n : 0) * p.B_sn;
-        const TIn* Cr = Cg + (nv ? n : 0) * p.C_sn;
         float av[kBK], bv[kBK], cv[kBK];
-        load_seg<kBK>(Br, t0, nv ? L : 0, p.vec, bv);
-        load_seg<kBK>(Cr, t0, nv ? L : 0, p.vec, cv);
+        {
+          const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bcs[buf][s][kBK * lane]);
+          const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bcs[buf][s][kBK * lane + 4]);
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&bcs[buf][2 + s][kBK * lane]);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&bcs[buf][2 + s][kBK * lane + 4]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            bv[k] = b0[k];
+            bv[4 + k] = b1[k];
+            cv[k] = c0[k];
+            cv[4 + k] = c1[k];
+          }
+        }
 #pragma unroll
         for (int k = 0; k < kBK; ++k) av[k] = SCALAR ? ah[k] : __builtin_amdgcn_exp2f(dt[k] * A2);
         // states: the lane's steps from zero, the scan, then from the incoming state
@@ -291,7 +332,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
           c = av[k] * gk;
         }
         // the adjoint carried into the previous window: lane 0's value after its first step
-        const float cl = __shfl(c, 0);
+        const float cl = readlane_f(c, 0);
         if (lane == 0) gcar[wave][pp][s] = cl;
         dAp[s] = dAs;
       }
@@ -310,6 +351,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         *reinterpret_cast<f32x4*>(&red[wave][2][lane * kBK + k]) = f32x4{rC[0][k], rC[0][k + 1], rC[0][k + 2], rC[0][k + 3]};
         *reinterpret_cast<f32x4*>(&red[wave][3][lane * kBK + k]) = f32x4{rC[1][k], rC[1][k + 1], rC[1][k + 2], rC[1][k + 3]};
       }
+      if (more) bc_store(buf ^ 1, nbc);
       __syncthreads();
       for (int i = threadIdx.x; i < 4 * kBW; i += 64 * kBWaves) {
         const int which = i / kBW, r = i % kBW;
@@ -322,6 +364,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
         }
       }
       __syncthreads();
+      buf ^= 1;
     }
     // per-step outputs of the window
     float* dur = p.du + b * p.du_sb + d * p.du_sd;
