@@ -33,7 +33,8 @@ namespace {
 
 constexpr int kBK = 8;               // steps per lane
 constexpr int kBW = 64 * kBK;        // steps per window
-constexpr int kBWaves = 4;           // channels per block
+constexpr int kBWaves = 4;           // channels (rows) per block of the checkpoint kernel
+constexpr int kMWaves = 8;           // channels per block of the backward kernel (of one B/C group)
 constexpr int kBMaxPairs = 64;       // N <= 128
 
 // DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source (or in masked
@@ -176,20 +177,24 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
 }
 
 template <typename TIn, typename TDy, bool GATE, bool SCALAR>
-__global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int64_t nwin, const float* ckpt) {
-  __shared__ float gcar[kBWaves][kBMaxPairs][2];      // adjoint carried into the window from the right
-  __shared__ float dAl[kBWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
+__global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int64_t nwin, const float* ckpt) {
+  __shared__ float gcar[kMWaves][kBMaxPairs][2];      // adjoint carried into the window from the right
+  __shared__ float dAl[kMWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
   // dB (2 states), dC (2 states) of the window's steps, step-major ([lane][k] = step lane K + k)
-  __shared__ __attribute__((aligned(16))) float red[kBWaves][4][kBW];
-  // B (2 states) and C (2 states) of a pair's window, shared by the block's 4 channels; two
+  __shared__ __attribute__((aligned(16))) float red[kMWaves][4][kBW];
+  // B (2 states) and C (2 states) of a pair's window, shared by the block's channels; two
   // buffers: the next pair's rows are loaded while this pair runs
   __shared__ __attribute__((aligned(16))) float bcs[2][4][kBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t quads = p.chan_per_group / kBWaves;
-  const int64_t bg = blockIdx.x / quads, qd = blockIdx.x % quads;
+  // blocks of 8 channels of one group; when the group's channels are 4 mod 8, the last block's
+  // last 4 waves work on a copy of a valid channel and contribute nothing
+  const int64_t cblocks = (p.chan_per_group + kMWaves - 1) / kMWaves;
+  const int64_t bg = blockIdx.x / cblocks, qd = blockIdx.x % cblocks;
   const int64_t b = bg / p.groups, g = bg % p.groups;
-  const int64_t d = g * p.chan_per_group + qd * kBWaves + wave;
+  const int64_t ci = qd * kMWaves + wave;
+  const bool valid = ci < p.chan_per_group;
+  const int64_t d = g * p.chan_per_group + (valid ? ci : p.chan_per_group - 1);
   const int64_t row = b * p.channels + d;
   const int64_t hd = d / p.chan_per_head;
   const int N = p.N;
@@ -214,11 +219,12 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
   const int srow = threadIdx.x >> 6, sseg = threadIdx.x & 63;
   auto bc_load = [&](int64_t ww, int pq, float (&v)[kBK]) {
     const int n = 2 * pq + (srow & 1);
-    const bool nv = n < N;
+    const bool nv = n < N && srow < 4;
     const TIn* src = srow < 2 ? Bg + (nv ? n : 0) * p.B_sn : Cg + (nv ? n : 0) * p.C_sn;
     load_seg<kBK>(src, ww * kBW + (int64_t)kBK * sseg, nv ? L : 0, p.vec, v);
   };
   auto bc_store = [&](int bf, const float (&v)[kBK]) {
+    if (srow >= 4) return;   // four rows, one per wave of the first four
     float* dst = &bcs[bf][srow][kBK * sseg];
     *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -340,10 +346,14 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const float v = wave_sum(dAp[s]);
-        if (lane == 0 && 2 * pp + s < N) dAl[wave][SCALAR ? 0 : 2 * pp + s] += v;
+        if (lane == 0 && valid && 2 * pp + s < N) dAl[wave][SCALAR ? 0 : 2 * pp + s] += v;
       }
-      // dB, dC of the pair: summed over the block's 4 channels, then one atomic add per step;
+      // dB, dC of the pair: summed over the block's 8 channels, then one atomic add per step;
       // consecutive lanes add to consecutive steps, so each wave's adds cover two cache lines
+      if (!valid) {
+#pragma unroll
+        for (int k = 0; k < kBK; ++k) rB[0][k] = rB[1][k] = rC[0][k] = rC[1][k] = 0.f;
+      }
 #pragma unroll
       for (int k = 0; k < kBK; k += 4) {
         *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{rB[0][k], rB[0][k + 1], rB[0][k + 2], rB[0][k + 3]};
@@ -353,12 +363,14 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
       }
       if (more) bc_store(buf ^ 1, nbc);
       __syncthreads();
-      for (int i = threadIdx.x; i < 4 * kBW; i += 64 * kBWaves) {
+      for (int i = threadIdx.x; i < 4 * kBW; i += 64 * kMWaves) {
         const int which = i / kBW, r = i % kBW;
         const int n = 2 * pp + (which & 1);
         const int64_t t = w * kBW + r;
         if (n < N && t < L) {
-          const float v = red[0][which][r] + red[1][which][r] + red[2][which][r] + red[3][which][r];
+          float v = 0.f;
+#pragma unroll
+          for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[wv2][which][r];
           float* dst = (which < 2 ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
           atomicAdd(dst, v);
         }
@@ -371,30 +383,33 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
     float* ddr = p.ddelta + b * p.dd_sb + hd * p.dd_sh;
     float dxs[kBK];
 #pragma unroll
-    for (int k = 0; k < kBK; ++k) dxs[k] = t0 + k < L ? ddt[k] * sg[k] : 0.f;
-    if (p.chan_per_head == 1) {
-#pragma unroll
-      for (int k = 0; k < kBK; ++k)
-        if (t0 + k < L) ddr[t0 + k] = dxs[k];
-    } else if (p.chan_per_head % kBWaves == 0) {
-      // the block's 4 channels share the head: summed through LDS, one atomic add per step
+    for (int k = 0; k < kBK; ++k) dxs[k] = (valid && t0 + k < L) ? ddt[k] * sg[k] : 0.f;
+    if (p.chan_per_head % kMWaves == 0 && p.chan_per_group % kMWaves == 0) {
+      // the block's 8 channels share the head: summed through LDS, one atomic add per step
 #pragma unroll
       for (int k = 0; k < kBK; k += 4)
         *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{dxs[k], dxs[k + 1], dxs[k + 2], dxs[k + 3]};
       __syncthreads();
-      for (int i = threadIdx.x; i < kBW; i += 64 * kBWaves) {
+      for (int i = threadIdx.x; i < kBW; i += 64 * kMWaves) {
         const int64_t t = w * kBW + i;
-        if (t < L) atomicAdd(ddr + t, red[0][0][i] + red[1][0][i] + red[2][0][i] + red[3][0][i]);
+        float v = 0.f;
+#pragma unroll
+        for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[wv2][0][i];
+        if (t < L) atomicAdd(ddr + t, v);
       }
       __syncthreads();
-    } else {
+    } else if (valid && p.chan_per_head == 1) {
+#pragma unroll
+      for (int k = 0; k < kBK; ++k)
+        if (t0 + k < L) ddr[t0 + k] = dxs[k];
+    } else if (valid) {
 #pragma unroll
       for (int k = 0; k < kBK; ++k)
         if (t0 + k < L) atomicAdd(ddr + t0 + k, dxs[k]);
     }
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
-      if (t0 + k < L) {
+      if (valid && t0 + k < L) {
         const float dx = dxs[k];
         dur[t0 + k] = du[k];
         dbacc += dx;
@@ -409,6 +424,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_kernel(BwdArgs p, int P, int
   }
   // per-channel sums (over this batch row's steps): dA, dD, dbias, added across the batch
   const float dDs = wave_sum(dDacc), dbs = wave_sum(dbacc);
+  if (!valid) return;
   if (lane == 0) {
     if (p.dD) atomicAdd(p.dD + (p.d_per_head ? hd : d), dDs);
     if (p.dbias) atomicAdd(p.dbias + hd, dbs);
@@ -454,9 +470,10 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   const dim3 cgrid((unsigned)((rows + kBWaves - 1) / kBWaves)), block(64 * kBWaves);
   if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
   else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
-  const dim3 grid((unsigned)(a.batch * a.groups * (a.chan_per_group / kBWaves)));
+  const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves)));
+  const dim3 mblock(64 * kMWaves);
   const float* ck = ws;
-#define SS_BWD(GT, SC) hipLaunchKernelGGL((bwd_kernel<TIn, TDy, GT, SC>), grid, block, 0, s, a, P, nwin, ck)
+#define SS_BWD(GT, SC) hipLaunchKernelGGL((bwd_kernel<TIn, TDy, GT, SC>), grid, mblock, 0, s, a, P, nwin, ck)
   if (a.z) {
     if (a.scalar) SS_BWD(true, true); else SS_BWD(true, false);
   } else {

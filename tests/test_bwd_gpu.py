@@ -139,3 +139,16 @@ def test_matrix_backward_bf16_dy():
     torch = torch_dev()
     check_bwd(inputs.random_problem(770, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=False), "matrix dy bf16",
               dy_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", ["12 channels", "two groups of 4", "heads of 4 in groups of 12"])
+def test_gradients_partial_channel_blocks(case):
+    """The per-channel kernel takes 8 channels of a group per block: groups of 4 mod 8 channels leave
+    the last block's last 4 waves without a channel (they must contribute nothing)."""
+    mk = {
+        "12 channels": lambda: inputs.random_problem(780, 2, 12, 530, 16, in_dtype="f32"),
+        "two groups of 4": lambda: inputs.random_problem(781, 1, 8, 300, 8, groups=2, in_dtype="f32"),
+        "heads of 4 in groups of 12": lambda: inputs.random_problem(782, 1, 12, 400, 16, heads=3, in_dtype="f32",
+                                                                    gate=False),
+    }
+    check_bwd(mk[case](), case)
