@@ -152,3 +152,68 @@ def test_gradients_partial_channel_blocks(case):
                                                                     gate=False),
     }
     check_bwd(mk[case](), case)
+
+
+def _compare(g, ref, pairs, label, tol):
+    errs = {}
+    for name, got_ix, ref_key in pairs:
+        if ref[ref_key] is None:
+            continue
+        got = g[name][got_ix].cpu().numpy().astype(np.float64)
+        errs[name] = normwise(got, ref[ref_key])
+    say("[bwd] %s: %s" % (label, " ".join("%s %.2e" % kv for kv in errs.items())))
+    bad = {k: v for k, v in errs.items() if v > tol}
+    assert not bad, (label, bad)
+
+
+def test_workload_1_full_size_sampled_channels():
+    """The 130M-class layer at full size (8x1536x2048, N 16, gate) in the launch the benchmark times;
+    the per-channel gradients (du, ddelta, dz, dA, dD, ddelta_bias) of 6 sampled channels against
+    the oracle run on those channels alone (they depend only on their own inputs and the shared B, C)."""
+    import dataclasses
+
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_bwd
+
+    p = inputs.make(1)
+    dy = inputs.seeded_normal(12, (p.batch, p.channels, p.length))
+    t = dev_problem(p)
+    g = scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], to_dev(dy),
+                 softplus=p.softplus)
+    torch.cuda.synchronize()
+    ch = np.array(sorted({0, p.channels - 1, 700} | set(np.random.default_rng(5).choice(p.channels, 3, False))))
+    sub = dataclasses.replace(p, channels=len(ch), heads=len(ch), u=p.u[:, ch], delta=p.delta[:, ch], z=p.z[:, ch],
+                              A=p.A[ch], D=p.D[ch], delta_bias=p.delta_bias[ch])
+    ref = oracle.scan_bwd_problem(sub, np.ascontiguousarray(dy[:, ch]))
+    c = torch.as_tensor(ch, device="cuda")
+    pairs = [("du", (slice(None), c), "du"), ("ddelta", (slice(None), c), "ddelta"), ("dz", (slice(None), c), "dz"),
+             ("dA", c, "dA"), ("dD", c, "dD"), ("ddelta_bias", c, "ddelta_bias")]
+    _compare(g, ref, pairs, "workload 1 full size, channels %s" % ch.tolist(), TOL["bf16"])
+
+
+def test_workload_4_full_size_sampled_heads():
+    """The scalar-decay multi-head layer at full size (2x(80x64)x8192, N 128) through the matrix-form
+    backward; the per-head gradients (du of the head's channels, ddelta, dA, dD, ddelta_bias) of 2
+    sampled heads against the oracle run on those heads alone."""
+    import dataclasses
+
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_bwd
+
+    p = inputs.make(4)
+    P = p.channels // p.heads
+    dy = inputs.seeded_normal(13, (p.batch, p.channels, p.length))
+    t = dev_problem(p)
+    g = scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], to_dev(dy),
+                 softplus=p.softplus)
+    torch.cuda.synchronize()
+    hs = np.array([0, 57])
+    ch = np.concatenate([np.arange(h * P, (h + 1) * P) for h in hs])
+    sub = dataclasses.replace(p, channels=len(ch), heads=len(hs), u=p.u[:, ch], delta=p.delta[:, hs],
+                              A=p.A[hs], D=p.D[hs], delta_bias=p.delta_bias[hs])
+    ref = oracle.scan_bwd_problem(sub, np.ascontiguousarray(dy[:, ch]))
+    c = torch.as_tensor(ch, device="cuda")
+    h = torch.as_tensor(hs, device="cuda")
+    pairs = [("du", (slice(None), c), "du"), ("ddelta", (slice(None), h), "ddelta"), ("dA", h, "dA"),
+             ("dD", h, "dD"), ("ddelta_bias", h, "ddelta_bias")]
+    _compare(g, ref, pairs, "workload 4 full size, heads %s" % hs.tolist(), TOL["bf16"])
