@@ -289,12 +289,18 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
   }
 }
 
-// Pass 2: the chunks in reverse.
+// Pass 2: the chunks in reverse, 8 waves (two per SIMD, so that one wave's LDS and MFMA waits
+// are covered by the other's work).  Tiles per wave w: DX and C B^T (w < 4: rows 16 (w / 2),
+// columns 16 (w % 2)); [T x N] products dY H0, X R, dC, dB (rows 16 (w % 2), state tiles
+// from NB (w / 2)); dX (rows 16 (w % 2), channels 16 (w / 2)); R (channels 16 (w % 4), state
+// tiles from NR (w / 4)).
+constexpr int kThrB = 512;
 template <typename TIn, typename TDy, int NT>
-__global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws,
-                                                         const float* __restrict__ cbws) {
+__global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws,
+                                                          const float* __restrict__ cbws) {
   constexpr int NP = 16 * NT;
-  constexpr int NH = NT / 2;   // [T x N] tiles per wave (two waves per 16 rows; NT >= 2)
+  constexpr int NB = NT >= 4 ? NT / 4 : 1;   // [T x N] state tiles per wave
+  constexpr int NR = NT / 2;                 // R state tiles per wave
   __shared__ __attribute__((aligned(16))) float xn[kCT * kSP];    // u [t][p]
   __shared__ __attribute__((aligned(16))) float dyn[kCT * kSP];   // dy [t][p]
   __shared__ __attribute__((aligned(16))) float dyt[kCP * kST];   // dy [p][t]
@@ -308,7 +314,7 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
   __shared__ __attribute__((aligned(16))) float ses[kCT];         // e^{s_t}
   __shared__ __attribute__((aligned(16))) float sdt[kCT];
   __shared__ float ss2[kCT], ser[kCT], ssig[kCT];
-  __shared__ float alp[2][kCT], bet[2][kCT], udp[2][kCT], rowp[2][kCT], colp[2][kCT], rh0[4];
+  __shared__ float alp[4][kCT], bet[4][kCT], udp[4][kCT], rowp[2][kCT], colp[2][kCT], rh0[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const Blk k = block_of(p, blockIdx.x);
@@ -328,48 +334,47 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
   float* ddb = p.ddelta + k.b * p.dd_sb + k.h * p.dd_sh;
   const float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
   const float* cbg = cbws + (k.b * p.groups + k.g) * nch * 1024;
-  const int ti = wave >> 1, half = wave & 1;   // 16-step row block and column half of this wave
+  const int w2 = wave & 1, wg = wave >> 1;      // row block of 16 steps, and a group of four
+  const bool dxw = wave < 4;                    // the waves forming DX and C B^T
+  const bool bcw = NT >= 4 || wave < 4;         // the waves with [T x N] tiles
+  const int nb0 = wg * NB;                      // first [T x N] state tile
+  const int rpi = wave & 3, nr0 = (wave >> 2) * NR;   // R: channel tile, first state tile
   // H0 of chunk c into hnp: NP / 4 copies of 1 KB, shared out over the waves
   auto h0_copy = [&](int64_t c) {
     const float* hc = wsb + c * NP * kCP;
-    for (int i = wave; i < NP / 4; i += 4) dma16(hc + i * 256 + 4 * lane, hnp + i * 256);
+    for (int i = wave; i < NP / 4; i += 8) dma16(hc + i * 256 + 4 * lane, hnp + i * 256);
   };
   h0_copy(nch - 1);
-  // this thread's share of a chunk's loads, fetched one chunk ahead: u and dy (row pp, 8 steps
-  // from tt), B and C (BCI items of 8 steps), the raw step (wave 0)
-  constexpr int BCI = (NP * 4 + kThr - 1) / kThr;
-  const int pp = tid >> 2, tt = 8 * (tid & 3);
-  float pu[8], py[8], pb[BCI][8], pc[BCI][8], pdl = 0.f;
+  // this thread's share of a chunk's loads, fetched one chunk ahead: u and dy (threads < 256: row
+  // pp, 8 steps from tt), B and C (row bn, 8 steps from bt8), the raw step (wave 0)
+  const int pp = (tid & 255) >> 2, tt = 8 * (tid & 3);
+  const bool uth = tid < 256;
+  const int bn = tid >> 2, bt8 = 8 * (tid & 3);
+  const bool bth = bn < NP;
+  float pu[8], py[8], pb[8], pc[8], pdl = 0.f;
   auto fetch = [&](int64_t c) {
     const int64_t t0 = c * kCT;
-    load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu);
-    load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, py);
+    if (uth) {
+      load_seg<8>(ub + pp * p.u_sd, t0 + tt, L, p.vec, pu);
+      load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, py);
+    }
+    if (bth && bn < N) {
+      load_seg<8>(Bb + bn * p.B_sn, t0 + bt8, L, p.vec, pb);
+      load_seg<8>(Cb + bn * p.C_sn, t0 + bt8, L, p.vec, pc);
+    } else {
 #pragma unroll
-    for (int it = 0; it < BCI; ++it) {
-      const int i = tid + it * kThr;
-      const int n = i >> 2, t8 = 8 * (i & 3);
-      if (i < NP * 4 && n < N) {
-        load_seg<8>(Bb + n * p.B_sn, t0 + t8, L, p.vec, pb[it]);
-        load_seg<8>(Cb + n * p.C_sn, t0 + t8, L, p.vec, pc[it]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[it][e] = pc[it][e] = 0.f;
-      }
+      for (int e = 0; e < 8; ++e) pb[e] = pc[e] = 0.f;
     }
     if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
   };
   fetch(nch - 1);
-  // D of the channels this lane's dX tiles cover
-  float Dp[2];
+  // D of the channel this lane's dX tile covers
+  const int pch = 16 * wg + l16;
+  const float Dp = p.D ? p.D[p.d_per_head ? k.h : k.d0 + pch] : 0.f;
+  f32x4 R[NR];   // R[p = 16 rpi + 4 q + r][n = 16 (nr0 + j) + l16]
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
-    const int pch = 16 * (2 * half + pt) + l16;
-    Dp[pt] = p.D ? p.D[p.d_per_head ? k.h : k.d0 + pch] : 0.f;
-  }
-  f32x4 R[NT];   // R[p = 16 wave + 4 q + r][n = 16 j + l16]
-#pragma unroll
-  for (int j = 0; j < NT; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float dDl[2] = {0.f, 0.f};
+  for (int j = 0; j < NR; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dDl = 0.f;
   float dAacc = 0.f, dbacc = 0.f;
 
   for (int64_t c = nch - 1; c >= 0; --c) {
@@ -390,37 +395,36 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
         ser[lane] = __builtin_amdgcn_exp2f(send - s);
       }
     }
+    if (uth) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      xn[(tt + e) * kSP + pp] = pu[e];
-      dyn[(tt + e) * kSP + pp] = py[e];
-    }
-    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{py[0], py[1], py[2], py[3]};
-    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{py[4], py[5], py[6], py[7]};
-#pragma unroll
-    for (int it = 0; it < BCI; ++it) {
-      const int i = tid + it * kThr;
-      if (i < NP * 4) {
-        const int n = i >> 2, t8 = 8 * (i & 3);
-        const float* v = pb[it];
-        const float* w = pc[it];
-        *reinterpret_cast<f32x4*>(bnt + n * kST + t8) = f32x4{v[0], v[1], v[2], v[3]};
-        *reinterpret_cast<f32x4*>(bnt + n * kST + t8 + 4) = f32x4{v[4], v[5], v[6], v[7]};
-        *reinterpret_cast<f32x4*>(cnt + n * kST + t8) = f32x4{w[0], w[1], w[2], w[3]};
-        *reinterpret_cast<f32x4*>(cnt + n * kST + t8 + 4) = f32x4{w[4], w[5], w[6], w[7]};
+      for (int e = 0; e < 8; ++e) {
+        xn[(tt + e) * kSP + pp] = pu[e];
+        dyn[(tt + e) * kSP + pp] = py[e];
       }
+      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{py[0], py[1], py[2], py[3]};
+      *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{py[4], py[5], py[6], py[7]};
+    }
+    if (bth) {
+      *reinterpret_cast<f32x4*>(bnt + bn * kST + bt8) = f32x4{pb[0], pb[1], pb[2], pb[3]};
+      *reinterpret_cast<f32x4*>(bnt + bn * kST + bt8 + 4) = f32x4{pb[4], pb[5], pb[6], pb[7]};
+      *reinterpret_cast<f32x4*>(cnt + bn * kST + bt8) = f32x4{pc[0], pc[1], pc[2], pc[3]};
+      *reinterpret_cast<f32x4*>(cnt + bn * kST + bt8 + 4) = f32x4{pc[4], pc[5], pc[6], pc[7]};
     }
     // R (the carry from the right) into LDS
 #pragma unroll
-    for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4*>(rnp + (16 * j + l16) * kSP + 16 * wave + 4 * q) = R[j];
+    for (int j = 0; j < NR; ++j)
+      *reinterpret_cast<f32x4*>(rnp + (16 * (nr0 + j) + l16) * kSP + 16 * rpi + 4 * q) = R[j];
     // this wave's tile of C B^T (formed by pass 1)
-    const f32x4 cb = *reinterpret_cast<const f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4);
+    f32x4 cb = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (dxw) cb = *reinterpret_cast<const f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4);
     // the copies of H0 into hnp have landed (this wave's), then everyone's
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
-    // ---- DX = dY X^T and CB = C B^T (one 16x16 tile each per wave), then the masked matrices
-    {
+    // ---- DX = dY X^T and CB = C B^T (waves 0..3: rows 16 (w / 2), columns 16 (w % 2)), then the
+    // masked matrices
+    if (dxw) {
+      const int ti = wave >> 1, half = wave & 1;
       f32x4 dx[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       mm<kCP, 1>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
       const int s = 16 * half + l16;   // column j = s of this lane; rows k = t below
@@ -444,42 +448,45 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       csum += __shfl_xor(csum, 32);
       if (q == 0) colp[ti][s] = csum;
     }
-    // ---- dY H0 and X R ([T x N] tiles: rows 16 ti, columns 16 (half NH + j))
-    f32x4 yh[NH], xr[NH];
+    // ---- dY H0 and X R ([T x N] tiles: rows 16 w2, state tiles nb0 ..)
+    f32x4 yh[NB], xr[NB];
 #pragma unroll
-    for (int j = 0; j < NH; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int nj0 = half * NH;
-    mm_swz<NH>(dyn + 16 * ti * kSP, kSP, hnp + 16 * nj0 * kCP, lane, yh);
-    mm<kCP, NH>(xn + 16 * ti * kSP, kSP, rnp + 16 * nj0 * kSP, kSP, 16 * kSP, lane, xr);
+    for (int j = 0; j < NB; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (bcw) {
+      mm_swz<NB>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
+      mm<kCP, NB>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
 #pragma unroll
-    for (int j = 0; j < NH; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) xr[j][r] *= sdt[16 * ti + 4 * q + r];   // X R = diag(dt) U R
-    {
+        for (int r = 0; r < 4; ++r) xr[j][r] *= sdt[16 * w2 + 4 * q + r];   // X R = diag(dt) U R
       // alpha_t = e^{s_t} (dY H0)_t . C_t and beta_t = e^{s_{T-1} - s_t} (X R)_t . B_t, partial over
-      // this wave's columns
+      // this wave's state tiles
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = 16 * ti + 4 * q + r;
+        const int t = 16 * w2 + 4 * q + r;
         float a = 0.f, bsum = 0.f;
 #pragma unroll
-        for (int j = 0; j < NH; ++j) {
-          const int n = 16 * (nj0 + j) + l16;
+        for (int j = 0; j < NB; ++j) {
+          const int n = 16 * (nb0 + j) + l16;
           a = fmaf(yh[j][r], cnt[n * kST + t], a);
           bsum = fmaf(xr[j][r], bnt[n * kST + t], bsum);
         }
         a = row16_sum(a);
         bsum = row16_sum(bsum);
         if (l16 == 0) {
-          alp[half][t] = a * ses[t];
-          bet[half][t] = bsum * ser[t];
+          alp[wg][t] = a * ses[t];
+          bet[wg][t] = bsum * ser[t];
         }
       }
-      // <R, H0> over this wave's rows of R
+    } else {
+      if (lane < kCT) alp[wg][lane] = bet[wg][lane] = 0.f;
+    }
+    {
+      // <R, H0> over this wave's tiles of R
       float rh = 0.f;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const f32x4 hv = *reinterpret_cast<const f32x4*>(hnp + swz(16 * j + l16, 4 * wave + q));
+      for (int j = 0; j < NR; ++j) {
+        const f32x4 hv = *reinterpret_cast<const f32x4*>(hnp + swz(16 * (nr0 + j) + l16, 4 * rpi + q));
         rh = fmaf(R[j][0], hv[0], fmaf(R[j][1], hv[1], fmaf(R[j][2], hv[2], fmaf(R[j][3], hv[3], rh))));
       }
       rh = wave_total(rh);
@@ -492,24 +499,24 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
     }
 
     // ---- dC = diag(e^s) dY H0 + M1 B and dB = diag(e^{s_{T-1} - s}) X R + M1^T C, added to the group's
-    {
+    if (bcw) {
 #pragma unroll
-      for (int j = 0; j < NH; ++j)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * ti + 4 * q + r;
+          const int t = 16 * w2 + 4 * q + r;
           yh[j][r] *= ses[t];
           xr[j][r] *= ser[t];
         }
-      mm<kCT, NH>(m1 + 16 * ti * kST, kST, bnt + 16 * nj0 * kST, kST, 16 * kST, lane, yh);
-      mm<kCT, NH>(m1t + 16 * ti * kST, kST, cnt + 16 * nj0 * kST, kST, 16 * kST, lane, xr);
+      mm<kCT, NB>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
+      mm<kCT, NB>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
 #pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        const int n = 16 * (nj0 + j) + l16;
+      for (int j = 0; j < NB; ++j) {
+        const int n = 16 * (nb0 + j) + l16;
         if (n < N) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 16 * ti + 4 * q + r;
+            const int64_t t = t0 + 16 * w2 + 4 * q + r;
             if (t < L) {
               atomicAdd(dCb + n * p.dC_sn + t, yh[j][r]);
               atomicAdd(dBb + n * p.dB_sn + t, xr[j][r]);
@@ -519,18 +526,17 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       }
     }
 
-    // ---- dX = diag(e^{s_{T-1} - s}) B R^T + (L o CB)^T dY ([T x 64]: rows 16 ti, columns 16 (2 half + pt))
+    // ---- dX = diag(e^{s_{T-1} - s}) B R^T + (L o CB)^T dY (rows 16 w2, channels 16 wg)
     {
-      f32x4 dxa[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      f32x4 dxa[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
       // B R^T over n: the operands of block kb + 1 are read while block kb's products run
-      float oa[2][4], ob[2][2][4];
+      float oa[2][4], ob[2][4];
       auto rd = [&](int kb, int s) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int n = 16 * kb + 4 * q + m;
-          oa[s][m] = bnt[n * kST + 16 * ti + l16];
-#pragma unroll
-          for (int pt = 0; pt < 2; ++pt) ob[s][pt][m] = rnp[n * kSP + 16 * (2 * half + pt) + l16];
+          oa[s][m] = bnt[n * kST + 16 * w2 + l16];
+          ob[s][m] = rnp[n * kSP + pch];
         }
       };
       rd(0, 0);
@@ -538,46 +544,38 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       for (int kb = 0; kb < NT; ++kb) {
         if (kb + 1 < NT) rd(kb + 1, (kb + 1) & 1);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int pt = 0; pt < 2; ++pt) dxa[pt] = mma4(oa[kb & 1][m], ob[kb & 1][pt][m], dxa[pt]);
+        for (int m = 0; m < 4; ++m) dxa[0] = mma4(oa[kb & 1][m], ob[kb & 1][m], dxa[0]);
       }
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) dxa[pt][r] *= ser[16 * ti + 4 * q + r];
-      mm<kCT, 2>(lcbt + 16 * ti * kST, kST, dyt + 16 * (2 * half) * kST, kST, 16 * kST, lane, dxa);
+      for (int r = 0; r < 4; ++r) dxa[0][r] *= ser[16 * w2 + 4 * q + r];
+      mm<kCT, 1>(lcbt + 16 * w2 * kST, kST, dyt + 16 * wg * kST, kST, 0, lane, dxa);
       // du = dt dX + D dy; u . dX per step; dD
       // (the lane's 4 steps of a channel are consecutive: one 16-byte store when whole and aligned)
-      float ud[4] = {0.f, 0.f, 0.f, 0.f};
-      const int tl0 = 16 * ti + 4 * q;
+      const int tl0 = 16 * w2 + 4 * q;
       const f32x4 dt4 = *reinterpret_cast<const f32x4*>(sdt + tl0);
+      float* dst = dub + pch * p.du_sd + t0 + tl0;
+      const f32x4 dy4 = *reinterpret_cast<const f32x4*>(dyt + pch * kST + tl0);
+      f32x4 du4;
+      float ud[4];
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        const int pch = 16 * (2 * half + pt) + l16;
-        float* dst = dub + pch * p.du_sd + t0 + tl0;
-        const f32x4 dy4 = *reinterpret_cast<const f32x4*>(dyt + pch * kST + tl0);
-        f32x4 du4;
+      for (int r = 0; r < 4; ++r) {
+        const bool live = t0 + tl0 + r < L;
+        const float uv = live ? xn[(tl0 + r) * kSP + pch] : 0.f;
+        du4[r] = fmaf(dt4[r], dxa[0][r], Dp * dy4[r]);
+        ud[r] = uv * dxa[0][r];
+        dDl = fmaf(dy4[r], uv, dDl);
+      }
+      if (t0 + tl0 + 4 <= L && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<f32x4*>(dst) = du4;
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool live = t0 + tl0 + r < L;
-          const float uv = live ? xn[(tl0 + r) * kSP + pch] : 0.f;
-          du4[r] = fmaf(dt4[r], dxa[pt][r], Dp[pt] * dy4[r]);
-          ud[r] = fmaf(uv, dxa[pt][r], ud[r]);
-          dDl[pt] = fmaf(dy4[r], uv, dDl[pt]);
-        }
-        if (t0 + tl0 + 4 <= L && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-          *reinterpret_cast<f32x4*>(dst) = du4;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (t0 + tl0 + r < L) dst[r] = du4[r];
-        }
+        for (int r = 0; r < 4; ++r)
+          if (t0 + tl0 + r < L) dst[r] = du4[r];
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = row16_sum(ud[r]);
-        if (l16 == 0) udp[half][16 * ti + 4 * q + r] = v;
+        if (l16 == 0) udp[wg][tl0 + r] = v;
       }
     }
 
@@ -585,8 +583,8 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
     {
       const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) R[j] = R[j] * dec;
-      mm<kCT, NT, true>(dyt + 16 * wave * kST, kST, cnt, kST, 16 * kST, lane, R, ses);
+      for (int j = 0; j < NR; ++j) R[j] = R[j] * dec;
+      mm<kCT, NR, true>(dyt + 16 * rpi * kST, kST, cnt + 16 * nr0 * kST, kST, 16 * kST, lane, R, ses);
     }
 
     // ---- the decay's gradient per step (wave 0; lane j = step j; scans over the 32 steps)
@@ -596,15 +594,17 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
       const bool lo = lane < kCT;
       // inclusive prefix sums over lanes 0..31 (lanes 32..63 repeat them and are ignored)
       const float col = colp[0][j] + colp[1][j], row = rowp[0][j] + rowp[1][j];
-      const float al = alp[0][j] + alp[1][j], be = bet[0][j] + bet[1][j];
+      const float al = (alp[0][j] + alp[1][j]) + (alp[2][j] + alp[3][j]);
+      const float be = (bet[0][j] + bet[1][j]) + (bet[2][j] + bet[3][j]);
       const float pcol = scan32(col), prow = scan32(row), pal = scan32(al), pbe = scan32(be);
       const float altot = lane_f(pal, kCT - 1);
       const float t1 = pcol - (prow - row);     // sum over k >= j >= i of W_ki
       const float t2 = altot - (pal - al);      // sum over k >= j of alpha_k
       const float t3 = pbe;                     // sum over i <= j of beta_i
-      const float t4 = __builtin_amdgcn_exp2f(ss2[kCT - 1]) * (rh0[0] + rh0[1] + rh0[2] + rh0[3]);
+      const float rhs = ((rh0[0] + rh0[1]) + (rh0[2] + rh0[3])) + ((rh0[4] + rh0[5]) + (rh0[6] + rh0[7]));
+      const float t4 = __builtin_amdgcn_exp2f(ss2[kCT - 1]) * rhs;
       const float gh = t1 + t2 + t3 + t4;
-      const float ud = udp[0][j] + udp[1][j];
+      const float ud = (udp[0][j] + udp[1][j]) + (udp[2][j] + udp[3][j]);
       const float dt = sdt[j];
       const float qa = gh - dt * ud;                 // a_j dLoss/da_j
       const float ddt = fmaf(Ah, qa, ud);
@@ -628,17 +628,14 @@ __global__ __launch_bounds__(kThr) void ssdb_main_kernel(BwdArgs p, int64_t nch,
     }
   }
   if (p.dD) {
-#pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      float v = dDl[pt];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      if (p.d_per_head) {
-        v = row16_sum(v);
-        if (lane == 0) atomicAdd(p.dD + k.h, v);
-      } else if (q == 0) {
-        atomicAdd(p.dD + k.d0 + 16 * (2 * half + pt) + l16, v);
-      }
+    float v = dDl;
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (p.d_per_head) {
+      v = row16_sum(v);
+      if (lane == 0) atomicAdd(p.dD + k.h, v);
+    } else if (q == 0) {
+      atomicAdd(p.dD + k.d0 + pch, v);
     }
   }
 }
@@ -649,8 +646,8 @@ hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
   float* cbws = ws + a.batch * a.heads * (a.chan_per_head / kCP) * nch * (16 * NT) * kCP;
   hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), dim3(2 * grid.x), block, 0, s, a, nch, ws, cbws);
-  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, block, 0, s, a, nch, static_cast<const float*>(ws),
-                     static_cast<const float*>(cbws));
+  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, dim3(kThrB), 0, s, a, nch,
+                     static_cast<const float*>(ws), static_cast<const float*>(cbws));
   return hipGetLastError();
 }
 
