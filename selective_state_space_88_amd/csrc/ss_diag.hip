@@ -18,9 +18,13 @@
 //    aggregates with a DPP scan (row_shr within rows of 16 lanes, row_bcast across them, then
 //    a shift for the exclusive prefix), and each lane re-runs its K steps from the true
 //    incoming state to form h_t and accumulate y_t += C_{t,n} h_t.  The two states of a pair
-//    are independent chains, which the wave interleaves (and whose two scans fill each other's
-//    DPP wait states).  Two channels per wave means a shorter scan and half the B/C traffic per
-//    channel; one means more waves for short batches; the launch picks;
+//    are independent chains.  With one channel per wave (few rows, so few waves) the wave
+//    interleaves them (their two scans fill each other's DPP wait states); with two channels
+//    per wave (many rows) it runs them one after the other, which keeps the kernel within a
+//    third of the register file and the block within a third of the LDS, i.e. three waves per
+//    SIMD whose work covers each other's waits.  Two channels per wave also means a shorter scan
+//    and half the B/C traffic per channel; one means more waves for short batches; the launch
+//    picks;
 //  - B and C are shared by every channel of a (batch, group).  Per state pair and window they
 //    are copied into LDS with direct-to-LDS loads (buffer_load ... lds) several pairs ahead of
 //    use, so the copies never pass through registers and overlap the arithmetic, and widened
@@ -42,7 +46,6 @@ namespace {
 
 constexpr int kWaves = 4;                   // waves per block
 constexpr int kK = 16;                      // steps per lane
-constexpr int kMaxPairs = 64;               // N <= 128
 
 // Steps per window of one channel and floats of one f32 pair stage (B, C of state 2p, then of
 // state 2p + 1).
@@ -141,6 +144,68 @@ __device__ __forceinline__ void row_exclusive_scan2(float& a0, float& b0, float&
   b1 = eb1;
 }
 
+// The same for one state: one exclusive scan of (a, b) within each row of 64 / ROWS lanes, with
+// this lane's four C quads of that state read (at cbase + the given offsets) while it runs.  A
+// single chain leaves one instruction between a VALU write and the next DPP read of the same
+// VGPR, so each step ends with an s_nop that supplies the second wait state.
+template <int ROWS, int O0, int O1, int O2, int O3>
+__device__ __forceinline__ void row_exclusive_scan1(float& a, float& bb, uint32_t cbase, f32x4 (&c)[4]) {
+  float ea, eb;
+#define SS_STEP1(CTRL)                                  \
+  "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n"               \
+  "v_mul_f32_dpp %0, %0, %0 " CTRL "\n"                \
+  "s_nop 0\n"
+#define SS_SCAN16_1                                     \
+  "s_nop 1\n"                                          \
+  SS_STEP1("row_shr:1 row_mask:0xf bank_mask:0xf")      \
+  SS_STEP1("row_shr:2 row_mask:0xf bank_mask:0xf")      \
+  SS_STEP1("row_shr:4 row_mask:0xf bank_mask:0xf")      \
+  SS_STEP1("row_shr:8 row_mask:0xf bank_mask:0xf")
+#define SS_IDENT1                                       \
+  "v_mov_b32 %2, 1.0\n"                                \
+  "v_mov_b32 %3, 0\n"
+#define SS_SHIFT1(CTRL)                                 \
+  "v_mov_b32_dpp %2, %0 " CTRL "\n"                    \
+  "v_mov_b32_dpp %3, %1 " CTRL "\n"
+#define SS_LOADC1                                       \
+  "ds_read_b128 %4, %8 offset:%9\n"                    \
+  "ds_read_b128 %5, %8 offset:%10\n"                   \
+  "ds_read_b128 %6, %8 offset:%11\n"                   \
+  "ds_read_b128 %7, %8 offset:%12\n"
+#define SS_OPS1                                                                                 \
+  : "+v"(a), "+v"(bb), "=&v"(ea), "=&v"(eb), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]) \
+  : "v"(cbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+  if constexpr (ROWS == 1) {
+    asm volatile(SS_LOADC1
+                 SS_SCAN16_1
+                 SS_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                 SS_STEP1("row_bcast:31 row_mask:0xc bank_mask:0xf")
+                 SS_IDENT1
+                 SS_SHIFT1("wave_shr:1 row_mask:0xf bank_mask:0xf")
+                 "s_waitcnt lgkmcnt(0)\n"
+                 SS_OPS1);
+  } else if constexpr (ROWS == 2) {
+    asm volatile(SS_LOADC1
+                 SS_SCAN16_1
+                 SS_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf")
+                 SS_IDENT1
+                 SS_SHIFT1("row_bcast:15 row_mask:0xa bank_mask:0x1")
+                 SS_SHIFT1("row_shr:1 row_mask:0xf bank_mask:0xf")
+                 "s_waitcnt lgkmcnt(0)\n"
+                 SS_OPS1);
+  } else {
+    static_assert(ROWS == 1 || ROWS == 2, "1 or 2 channels per wave");
+  }
+#undef SS_OPS1
+#undef SS_LOADC1
+#undef SS_SHIFT1
+#undef SS_IDENT1
+#undef SS_SCAN16_1
+#undef SS_STEP1
+  a = ea;
+  bb = eb;
+}
+
 // One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes from `src` land at
 // lds_base + 16 i (lds_base is wave-uniform).
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
@@ -171,33 +236,39 @@ struct Seg {
   uint32_t w[kWords];
 };
 
-// lds_read8 plus CPT (1 or 2) 16-byte reads at rbase + 4 KB m, in the same statement.
+// lds_read8 plus CPT (1 or 2) 16-byte reads at rbase + 4 KB m and one at pbase (the pair's
+// parameters), in the same statement.
 template <int CPT, int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
-__device__ __forceinline__ void lds_read8_plus(uint32_t base, f32x4 (&v)[8], uint32_t rbase, u32x4 (&raw)[CPT]) {
+__device__ __forceinline__ void lds_read8_plus(uint32_t base, f32x4 (&v)[8], uint32_t rbase, u32x4 (&raw)[CPT],
+                                               uint32_t pbase, f32x4& pv) {
   if constexpr (CPT == 1) {
     asm volatile(
-        "ds_read_b128 %8, %10\n\t"
-        "ds_read_b128 %0, %9 offset:%11\n\tds_read_b128 %1, %9 offset:%12\n\t"
-        "ds_read_b128 %2, %9 offset:%13\n\tds_read_b128 %3, %9 offset:%14\n\t"
-        "ds_read_b128 %4, %9 offset:%15\n\tds_read_b128 %5, %9 offset:%16\n\t"
-        "ds_read_b128 %6, %9 offset:%17\n\tds_read_b128 %7, %9 offset:%18\n\t"
+        "ds_read_b128 %9, %12\n\t"
+        "ds_read_b128 %8, %11\n\t"
+        "ds_read_b128 %0, %10 offset:%13\n\tds_read_b128 %1, %10 offset:%14\n\t"
+        "ds_read_b128 %2, %10 offset:%15\n\tds_read_b128 %3, %10 offset:%16\n\t"
+        "ds_read_b128 %4, %10 offset:%17\n\tds_read_b128 %5, %10 offset:%18\n\t"
+        "ds_read_b128 %6, %10 offset:%19\n\tds_read_b128 %7, %10 offset:%20\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-          "=&v"(raw[0])
-        : "v"(base), "v"(rbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+          "=&v"(raw[0]), "=&v"(pv)
+        : "v"(base), "v"(rbase), "v"(pbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6),
+          "n"(O7)
         : "memory");
   } else {
     static_assert(CPT == 2, "one or two chunks");
     asm volatile(
-        "ds_read_b128 %8, %11\n\tds_read_b128 %9, %11 offset:4096\n\t"
-        "ds_read_b128 %0, %10 offset:%12\n\tds_read_b128 %1, %10 offset:%13\n\t"
-        "ds_read_b128 %2, %10 offset:%14\n\tds_read_b128 %3, %10 offset:%15\n\t"
-        "ds_read_b128 %4, %10 offset:%16\n\tds_read_b128 %5, %10 offset:%17\n\t"
-        "ds_read_b128 %6, %10 offset:%18\n\tds_read_b128 %7, %10 offset:%19\n\t"
+        "ds_read_b128 %10, %13\n\t"
+        "ds_read_b128 %8, %12\n\tds_read_b128 %9, %12 offset:4096\n\t"
+        "ds_read_b128 %0, %11 offset:%14\n\tds_read_b128 %1, %11 offset:%15\n\t"
+        "ds_read_b128 %2, %11 offset:%16\n\tds_read_b128 %3, %11 offset:%17\n\t"
+        "ds_read_b128 %4, %11 offset:%18\n\tds_read_b128 %5, %11 offset:%19\n\t"
+        "ds_read_b128 %6, %11 offset:%20\n\tds_read_b128 %7, %11 offset:%21\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
-          "=&v"(raw[0]), "=&v"(raw[1])
-        : "v"(base), "v"(rbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+          "=&v"(raw[0]), "=&v"(raw[1]), "=&v"(pv)
+        : "v"(base), "v"(rbase), "v"(pbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6),
+          "n"(O7)
         : "memory");
   }
 }
@@ -205,6 +276,12 @@ __device__ __forceinline__ void lds_read8_plus(uint32_t base, f32x4 (&v)[8], uin
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The carried state pair (.z, .w) of one pair's parameters, written through asm: a plain store
+// would make the compiler wait for every copy in flight first.
+__device__ __forceinline__ void par_state_write(float4* pp, float h0, float h1) {
+  asm volatile("ds_write_b64 %0, %1 offset:8" ::"v"(lds_addr(pp)), "v"(f32x2v{h0, h1}) : "memory");
 }
 
 // Two 16-byte LDS reads, waited for in the same statement.  The slots they read are filled by
@@ -226,21 +303,22 @@ __device__ __forceinline__ u32x4 lds_read1(const void* p0) {
   return v;
 }
 
-// Eight 16-byte LDS reads at base + the given byte offsets, waited for in the same statement
-// (for the same reason as lds_read2).
+// Eight 16-byte LDS reads at base + the given byte offsets and one at pbase (the pair's
+// parameters), waited for in the same statement (for the same reason as lds_read2).
 template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
-__device__ __forceinline__ void lds_read8(uint32_t base, f32x4 (&v)[8]) {
+__device__ __forceinline__ void lds_read8(uint32_t base, f32x4 (&v)[8], uint32_t pbase, f32x4& pv) {
   asm volatile(
-      "ds_read_b128 %0, %8 offset:%9\n\tds_read_b128 %1, %8 offset:%10\n\t"
-      "ds_read_b128 %2, %8 offset:%11\n\tds_read_b128 %3, %8 offset:%12\n\t"
-      "ds_read_b128 %4, %8 offset:%13\n\tds_read_b128 %5, %8 offset:%14\n\t"
-      "ds_read_b128 %6, %8 offset:%15\n\tds_read_b128 %7, %8 offset:%16\n\t"
+      "ds_read_b128 %8, %10\n\t"
+      "ds_read_b128 %0, %9 offset:%11\n\tds_read_b128 %1, %9 offset:%12\n\t"
+      "ds_read_b128 %2, %9 offset:%13\n\tds_read_b128 %3, %9 offset:%14\n\t"
+      "ds_read_b128 %4, %9 offset:%15\n\tds_read_b128 %5, %9 offset:%16\n\t"
+      "ds_read_b128 %6, %9 offset:%17\n\tds_read_b128 %7, %9 offset:%18\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-      : "v"(base), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7]),
+        "=&v"(pv)
+      : "v"(base), "v"(pbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3), "n"(O4), "n"(O5), "n"(O6), "n"(O7)
       : "memory");
 }
-
 
 template <typename TIn>
 __device__ __forceinline__ void seg_read(const uint32_t* slot, int lane, Seg<TIn>& s) {
@@ -311,8 +389,9 @@ __device__ __forceinline__ void seg_fill(const TIn* row, int64_t t0, int64_t L, 
 // as f32, row r's quad i (steps 4i..4i+3 of a lane) of lane j at float r W + (i LPC + j) 4, so
 // that every ds_read_b128 of a wave reads consecutive LDS.  How a stage gets there:
 //  - bf16 inputs, 16-byte rows: the four rows are copied raw (each wave one row, 16 bytes a
-//    lane, direct-to-LDS buffer loads) into a 3-slot raw ring three stages ahead of use; one
-//    stage ahead of use the block widens them into a 2-slot f32 ring (each thread 8 steps);
+//    lane, direct-to-LDS buffer loads) into a raw ring of AHEAD slots AHEAD stages ahead of
+//    use (3 with one channel per wave, 2 with two); one stage ahead of use the block widens
+//    them into a 2-slot f32 ring (each thread 8 steps);
 //  - f32 inputs, 16-byte rows: copied straight into the f32 layout, into a 3-slot f32 ring two
 //    stages ahead of use;
 //  - anything else: loaded element by element and widened into the 2-slot f32 ring one stage
@@ -343,15 +422,25 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
 //          Euler recurrence k_t = a_t k_{t-1} + e_t, and y reads C (k - e/2).
 constexpr int kSIO = 1, kZOH = 2, kTRAP = 4;
 template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, int MODE>
-__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))) void diag_fwd_kernel(
+__global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROWS == 2 && sizeof(TIn) == 2 ? 3 : 2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
   constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
   constexpr StageMode SMODE = stage_mode<TIn, VEC>();
   constexpr int LPC = 64 / ROWS;                     // lanes per channel row
   constexpr int W = win_steps<ROWS>();               // steps per window of a channel
   constexpr int SLOT = slot_floats<ROWS>();          // floats of one f32 stage
+  // Two channels per wave (many rows) runs three waves per SIMD: the two states of a pair then
+  // go one after the other (SPLIT), which keeps the registers within a third of the file, and
+  // the raw ring has two slots, which keeps the block's LDS within a third of the CU's.  One
+  // channel per wave (few rows, few waves) keeps both states in flight at once for the
+  // instruction-level parallelism, and copies the raw stages three pairs ahead; so do f32
+  // inputs, whose per-wave input slots are twice as large and allow only two blocks per CU.
+  constexpr bool SPLIT = ROWS == 2 && sizeof(TIn) == 2;
   constexpr int NF = SMODE == StageMode::kDirect ? 3 : 2;       // f32 ring slots
-  constexpr int AHEAD = SMODE == StageMode::kWiden ? 3 : 2;     // stages copied ahead of use
+  constexpr int AHEAD = SMODE == StageMode::kWiden ? (SPLIT ? 2 : 3) : 2;   // stages copied ahead of use
+  // (the copy that the next pair's widening or reading needs was issued by this pair when
+  // AHEAD is 2 in kWiden, by the pair before otherwise)
+  constexpr bool NEED_LAST = SMODE == StageMode::kWiden && AHEAD == 2;
   constexpr int ROWB = W * (int)sizeof(TIn);                   // bytes of one stage row
   constexpr int NDMA = SMODE == StageMode::kWiden ? ROWB / 1024 : W / 256;  // copies per wave per stage
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
@@ -361,15 +450,15 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   constexpr int CPT = W / 512;                       // 8-step chunks widened per thread per stage
   static_assert(ROWS == 1 || ROWS == 2, "1 or 2 channels per wave");
   __shared__ __attribute__((aligned(16))) float fring[NF][SLOT];
-  __shared__ __attribute__((aligned(16))) uint32_t rring[SMODE == StageMode::kWiden ? 3 : 1]
+  __shared__ __attribute__((aligned(16))) uint32_t rring[SMODE == StageMode::kWiden ? AHEAD : 1]
                                                        [SMODE == StageMode::kWiden ? ROWB : 4];
-  // per wave: u, delta, z of one window, and y on its way out
+  // per wave: u, delta, z of one window (y leaves through the z slot once z has been read)
   __shared__ __attribute__((aligned(16))) uint32_t xin[kWaves][3][kSegWords];
-  __shared__ __attribute__((aligned(16))) uint32_t ystg[kWaves][NCO * 256];
-  // per (wave, row, pair): (A_2p, A_2p+1) * log2 e and the carried state of the pair.  A
-  // static array: the compiler then knows the copies in flight cannot write it, and reads of
-  // it need not wait for them.
-  __shared__ float4 par[kWaves * ROWS * kMaxPairs];
+  // per (wave, row, pair): (A_2p, A_2p+1) * log2 e and the carried state of the pair, sized
+  // by the launch (kWaves * ROWS * pairs).  Read in the pair loop through asm with the B values:
+  // the compiler cannot tell that the copies in flight do not write this array, and would wait
+  // for all of them before a plain read.
+  extern __shared__ float4 par[];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -391,13 +480,17 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
   const TIn* urow = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
   const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
   const TIn* zrow = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
-  const float bias = p.bias ? p.bias[hd] : 0.f;
-  const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
+  float bias = p.bias ? p.bias[hd] : 0.f;
+  float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
+  // complete these loads here, through a statement that redefines both values: otherwise the
+  // compiler waits for them at their first use inside the window loop, i.e. for every copy in
+  // flight there, once per window
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(bias), "+v"(Dd));
   const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
   const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
   const int Qt = (int)(nwin * P);  // pair stages of this block, in order (window-major)
 
-  float4* mypar = par + (wave * ROWS + r) * kMaxPairs;
+  float4* mypar = par + (wave * ROWS + r) * P;
   {
     // the carried state starts at the caller's initial state, or at zero
     const float* Ar = p.A + d * p.A_sd;
@@ -432,7 +525,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
                                           row ? 0x7fffffff : 0, 0x00020000);
     const int64_t lim = L - t_first;  // steps of this window inside the row
     if constexpr (SMODE == StageMode::kWiden) {
-      uint32_t* dst = rring[qs % 3] + wave * (ROWB / 4);
+      uint32_t* dst = rring[qs % AHEAD] + wave * (ROWB / 4);
 #pragma unroll
       for (int c = 0; c < NDMA; ++c) {
         const int64_t tl = (int64_t)(c * 64 + lane) * 8;  // 8 bf16 a lane
@@ -490,7 +583,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
     if constexpr (GATE) x_copy(zrow, 0, xz);
   }
   if constexpr (SMODE == StageMode::kWiden) {
-    for (int qs = 0; qs < 3 && qs < Qt; ++qs) stage_copy(qs);
+    for (int qs = 0; qs < AHEAD && qs < Qt; ++qs) stage_copy(qs);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     {
       u32x4 raw[CPT];
@@ -564,79 +657,128 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
 
     for (int pp = 0; pp < P; ++pp) {
       // copies of a later stage, and (kWiden, kElementwise) the next stage into f32
-      int allow = pp == 0 ? boundary_ops : 0;
+      // memory operations issued after the copy the next pair needs (NEED_LAST: none)
+      int allow = (!NEED_LAST && pp == 0) ? boundary_ops : 0;
       if constexpr (SMODE != StageMode::kElementwise) {
         if (q + AHEAD < Qt) {
           stage_copy(q + AHEAD);
-          allow += NDMA;
+          if (!NEED_LAST) allow += NDMA;
         }
       }
       if constexpr (SMODE == StageMode::kElementwise)
         if (q + 1 < Qt) stage_widen(q + 1, (q + 1) & 1, nullptr);
       const int fs = SMODE == StageMode::kDirect ? q % 3 : (q & 1);
-      const float4 pv = mypar[pp];  // (A pair, carried state pair) of this lane's channel
       // this lane's B values of both states: quad i of row r of the slot is at byte offset
       // 4 W r + 16 (i LPC + j) from the slot
       const uint32_t lbase = lds_addr(fring[fs]) + 16u * (uint32_t)jl;
       constexpr int QS = 16 * LPC;
       f32x4 bq[8];  // B of state 2p (quads 0-3), then of state 2p + 1
+      f32x4 pq;     // (A pair, carried state pair) of this lane's channel
       if constexpr (SMODE == StageMode::kWiden) {
         // with this thread's raw chunks of the next stage, widened right after
         u32x4 raw[CPT];
         lds_read8_plus<CPT, 0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(
-            lbase, bq, lds_addr(rring[(q + 1) % 3]) + 16u * threadIdx.x, raw);
+            lbase, bq, lds_addr(rring[(q + 1) % AHEAD]) + 16u * threadIdx.x, raw, lds_addr(mypar + pp), pq);
         if (q + 1 < Qt) stage_widen(q + 1, (q + 1) & 1, raw);
       } else {
-        lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq);
+        lds_read8<0, QS, 2 * QS, 3 * QS, 8 * W, 8 * W + QS, 8 * W + 2 * QS, 8 * W + 3 * QS>(lbase, bq,
+                                                                                        lds_addr(mypar + pp), pq);
       }
-      float av0[kK], bv0[kK], av1[kK], bv1[kK];
-      float wz0[ZOH ? kK : 1], wz1[ZOH ? kK : 1];
-      float h0 = 0.f, h1 = 0.f;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
-        av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
-      }
-      if constexpr (ZOH) {
-        // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
-        const float An0 = pv.x * kLn2f, An1 = pv.y * kLn2f;
-#pragma unroll
+      const float4 pv = make_float4(pq[0], pq[1], pq[2], pq[3]);
+      if constexpr (SPLIT) {
+        // the two states one after the other (the registers of one state's K decays and inputs
+        // are reused by the next)
+        float hend[2];
+  #pragma unroll
+        for (int si = 0; si < 2; ++si) {
+          const float An = si ? pv.y : pv.x;   // A_n log2 e
+          float av[kK], bv[kK];
+          float h = 0.f;
+  #pragma unroll
+          for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
+          if constexpr (ZOH) {
+            // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
+            const float Anl = An * kLn2f;
+  #pragma unroll
+            for (int j = 0; j < kK; ++j) {
+              const float x = dt[j] * Anl;
+              bv[j] = wv[j] * zoh_phi(x, av[j], __builtin_amdgcn_rcpf(x)) * bq[4 * si + j / 4][j % 4];
+            }
+          } else {
+  #pragma unroll
+            for (int j = 0; j < kK; ++j) bv[j] = wv[j] * bq[4 * si + j / 4][j % 4];
+          }
+  #pragma unroll
+          for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
+          // lane aggregate: decay over the lane's K steps and the lane's state from zero; the
+          // scan, with this lane's C values of the state read while it runs
+          float sa = __builtin_amdgcn_exp2f(sdt * An), sb = h;
+          f32x4 cq[4];
+          if (si == 0)
+            row_exclusive_scan1<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS>(sa, sb, lbase, cq);
+          else
+            row_exclusive_scan1<ROWS, 12 * W, 12 * W + QS, 12 * W + 2 * QS, 12 * W + 3 * QS>(sa, sb, lbase, cq);
+          h = fmaf(sa, si ? pv.w : pv.z, sb);
+  #pragma unroll
+          for (int j = 0; j < kK; ++j) {
+            h = fmaf(av[j], h, bv[j]);
+            if constexpr (TRAP) yv[j] = fmaf(cq[j / 4][j % 4], fmaf(-0.5f, bv[j], h), yv[j]);
+            else yv[j] = fmaf(cq[j / 4][j % 4], h, yv[j]);
+          }
+          hend[si] = h;
+        }
+        // the window's end state (the row's last lane) starts the same pair in the next window
+        if (jl == LPC - 1) par_state_write(mypar + pp, hend[0], hend[1]);
+      } else {
+        float av0[kK], bv0[kK], av1[kK], bv1[kK];
+        float wz0[ZOH ? kK : 1], wz1[ZOH ? kK : 1];
+        float h0 = 0.f, h1 = 0.f;
+  #pragma unroll
         for (int j = 0; j < kK; ++j) {
-          const float x0 = dt[j] * An0, x1 = dt[j] * An1;
-          wz0[j] = wv[j] * zoh_phi(x0, av0[j], __builtin_amdgcn_rcpf(x0));
-          wz1[j] = wv[j] * zoh_phi(x1, av1[j], __builtin_amdgcn_rcpf(x1));
+          av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
+          av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
         }
-      }
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        bv0[j] = (ZOH ? wz0[j] : wv[j]) * bq[j / 4][j % 4];
-        bv1[j] = (ZOH ? wz1[j] : wv[j]) * bq[4 + j / 4][j % 4];
-        h0 = fmaf(av0[j], h0, bv0[j]);
-        h1 = fmaf(av1[j], h1, bv1[j]);
-      }
-      // lane aggregates: decay over the lane's K steps and the lane's state from zero
-      float sa0 = __builtin_amdgcn_exp2f(sdt * pv.x), sb0 = h0;
-      float sa1 = __builtin_amdgcn_exp2f(sdt * pv.y), sb1 = h1;
-      // the scan, with this lane's C values of both states read while it runs
-      f32x4 cq[8];
-      row_exclusive_scan2<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS, 12 * W, 12 * W + QS,
-                          12 * W + 2 * QS, 12 * W + 3 * QS>(sa0, sb0, sa1, sb1, lbase, cq);
-      h0 = fmaf(sa0, pv.z, sb0);
-      h1 = fmaf(sa1, pv.w, sb1);
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        h0 = fmaf(av0[j], h0, bv0[j]);
-        h1 = fmaf(av1[j], h1, bv1[j]);
-        if constexpr (TRAP) {
-          yv[j] = fmaf(cq[j / 4][j % 4], fmaf(-0.5f, bv0[j], h0), yv[j]);
-          yv[j] = fmaf(cq[4 + j / 4][j % 4], fmaf(-0.5f, bv1[j], h1), yv[j]);
-        } else {
-          yv[j] = fmaf(cq[j / 4][j % 4], h0, yv[j]);
-          yv[j] = fmaf(cq[4 + j / 4][j % 4], h1, yv[j]);
+        if constexpr (ZOH) {
+          // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
+          const float An0 = pv.x * kLn2f, An1 = pv.y * kLn2f;
+  #pragma unroll
+          for (int j = 0; j < kK; ++j) {
+            const float x0 = dt[j] * An0, x1 = dt[j] * An1;
+            wz0[j] = wv[j] * zoh_phi(x0, av0[j], __builtin_amdgcn_rcpf(x0));
+            wz1[j] = wv[j] * zoh_phi(x1, av1[j], __builtin_amdgcn_rcpf(x1));
+          }
         }
+  #pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          bv0[j] = (ZOH ? wz0[j] : wv[j]) * bq[j / 4][j % 4];
+          bv1[j] = (ZOH ? wz1[j] : wv[j]) * bq[4 + j / 4][j % 4];
+          h0 = fmaf(av0[j], h0, bv0[j]);
+          h1 = fmaf(av1[j], h1, bv1[j]);
+        }
+        // lane aggregates: decay over the lane's K steps and the lane's state from zero
+        float sa0 = __builtin_amdgcn_exp2f(sdt * pv.x), sb0 = h0;
+        float sa1 = __builtin_amdgcn_exp2f(sdt * pv.y), sb1 = h1;
+        // the scan, with this lane's C values of both states read while it runs
+        f32x4 cq[8];
+        row_exclusive_scan2<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS, 12 * W, 12 * W + QS,
+                            12 * W + 2 * QS, 12 * W + 3 * QS>(sa0, sb0, sa1, sb1, lbase, cq);
+        h0 = fmaf(sa0, pv.z, sb0);
+        h1 = fmaf(sa1, pv.w, sb1);
+  #pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          h0 = fmaf(av0[j], h0, bv0[j]);
+          h1 = fmaf(av1[j], h1, bv1[j]);
+          if constexpr (TRAP) {
+            yv[j] = fmaf(cq[j / 4][j % 4], fmaf(-0.5f, bv0[j], h0), yv[j]);
+            yv[j] = fmaf(cq[4 + j / 4][j % 4], fmaf(-0.5f, bv1[j], h1), yv[j]);
+          } else {
+            yv[j] = fmaf(cq[j / 4][j % 4], h0, yv[j]);
+            yv[j] = fmaf(cq[4 + j / 4][j % 4], h1, yv[j]);
+          }
+        }
+        // the window's end state (the row's last lane) starts the same pair in the next window
+        if (jl == LPC - 1) par_state_write(mypar + pp, h0, h1);
       }
-      // the window's end state (the row's last lane) starts the same pair in the next window
-      if (jl == LPC - 1) *reinterpret_cast<float2*>(&mypar[pp].z) = make_float2(h0, h1);
       // The copies the next iteration reads (kDirect: stage q + 1; kWiden: stage q + 2, which
       // it widens) have landed, this wave's and, after the barrier, everyone's; and every
       // wave is done with the slots the next iteration overwrites.
@@ -667,52 +809,66 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2))
       // y.  Lane granule c (steps 4c.. of a f32 lane, 8c.. of a bf16 lane) is granule
       // g = NCO lane + c of the wave's window; it is kept at g ^ ((g >> 4) & (NCO - 1)) so that
       // neither the writes nor the reads conflict on banks, and store instruction i has lane
-      // l take granule 64 i + l, i.e. granule (64 i + l) mod GPR of row (64 i + l) / GPR.
+      // l take granule 64 i + l, i.e. granule (64 i + l) mod GPR of row (64 i + l) / GPR.  The
+      // wave's z slot (read above) holds YP granules, so y goes through it in NPASS passes of
+      // 64 / NPASS lanes' granules each.
       // (written and read through asm: plain C++ here would make the compiler wait for every
       // copy in flight)
-      const uint32_t sbase = lds_addr(ystg[wave]);
+      constexpr int YP = kSegWords / 4;                     // granules in the slot
+      constexpr int NPASS = NCO * 64 > YP ? NCO * 64 / YP : 1;
+      constexpr int IPP = NCO / NPASS;                       // store instructions per pass
+      static_assert(NCO % NPASS == 0 && NCO * 64 <= NPASS * YP, "y fits the slot in whole passes");
+      const uint32_t sbase = lds_addr(xz);
 #pragma unroll
-      for (int c = 0; c < NCO; ++c) {
-        u32x4 gr;
-        if constexpr (sizeof(TOut) == 4) {
-          gr = u32x4{__float_as_uint(yv[4 * c]), __float_as_uint(yv[4 * c + 1]), __float_as_uint(yv[4 * c + 2]),
-                     __float_as_uint(yv[4 * c + 3])};
-        } else {
-          uint32_t wd[4];
+      for (int h = 0; h < NPASS; ++h) {
+        if (lane / (64 / NPASS) == h) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            wd[e] = f32_to_bf16_bits(yv[8 * c + 2 * e]) | (f32_to_bf16_bits(yv[8 * c + 2 * e + 1]) << 16);
-          gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
+          for (int c = 0; c < NCO; ++c) {
+            u32x4 gr;
+            if constexpr (sizeof(TOut) == 4) {
+              gr = u32x4{__float_as_uint(yv[4 * c]), __float_as_uint(yv[4 * c + 1]), __float_as_uint(yv[4 * c + 2]),
+                         __float_as_uint(yv[4 * c + 3])};
+            } else {
+              uint32_t wd[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                wd[e] = f32_to_bf16_bits(yv[8 * c + 2 * e]) | (f32_to_bf16_bits(yv[8 * c + 2 * e + 1]) << 16);
+              gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
+            }
+            const int gi = NCO * lane + c - 64 * IPP * h;   // granule within the pass
+            const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
+            asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
+          }
         }
-        const int gi = NCO * lane + c;
-        const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
-        asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
-      }
-      // granule 64 i + l sits at 64 i + (l ^ ((l >> 4) & (NCO - 1))): one base, offsets 1 KB i
-      u32x4 yo[NCO];
-      {
-        const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
-        if constexpr (NCO == 4)
-          asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
-                       "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
-                       "s_waitcnt lgkmcnt(0)"
-                       : "=&v"(yo[0]), "=&v"(yo[1]), "=&v"(yo[2]), "=&v"(yo[3])
-                       : "v"(a)
-                       : "memory");
-        else
-          asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-                       : "=&v"(yo[0]), "=&v"(yo[1])
-                       : "v"(a)
-                       : "memory");
-      }
+        // granule 64 i + l of the pass sits at 64 i + (l ^ ((l >> 4) & (NCO - 1))): one base,
+        // offsets 1 KB i
+        u32x4 yo[IPP];
+        {
+          const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
+          if constexpr (IPP == 4)
+            asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+                         "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+                         "s_waitcnt lgkmcnt(0)"
+                         : "=&v"(yo[0]), "=&v"(yo[1]), "=&v"(yo[2]), "=&v"(yo[3])
+                         : "v"(a)
+                         : "memory");
+          else if constexpr (IPP == 2)
+            asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                         : "=&v"(yo[0]), "=&v"(yo[1])
+                         : "v"(a)
+                         : "memory");
+          else
+            asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(yo[0]) : "v"(a) : "memory");
+        }
 #pragma unroll
-      for (int i = 0; i < NCO; ++i) {
-        const int gi = 64 * i + lane;
-        const int row = gi / GPR;
-        const u32x4 v = yo[i];
-        if (local0 + row < cpg) {
-          TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + (g * cpg + local0 + row) * p.y_sd;
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(yr + w0) + gi % GPR);
+        for (int ii = 0; ii < IPP; ++ii) {
+          const int gi = 64 * (IPP * h + ii) + lane;
+          const int row = gi / GPR;
+          const u32x4 v = yo[ii];
+          if (local0 + row < cpg) {
+            TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + (g * cpg + local0 + row) * p.y_sd;
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(yr + w0) + gi % GPR);
+          }
         }
       }
       if (wave_live) carry_ops += NCO;  // exactly NCO store instructions were issued
@@ -768,12 +924,13 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   // direct-to-LDS loads
   const bool vec = a.vec && a.L % (16 / (int64_t)sizeof(TIn)) == 0;
   const dim3 grid((unsigned)blocks), block(64 * kWaves);
+  const size_t par_bytes = sizeof(float4) * kWaves * ROWS * P;   // the per-pair parameters
   // the plain forward, or (state in/out checked at run time) with state in/out, zero-order hold
   // and/or the trapezoidal rule
   const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0);
 #define SS_M(G, V, M)                                                                                        \
   case M:                                                                                                    \
-    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, M>), grid, block, 0, s, a, P, nwin, blocks_per_bg); \
+    hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, M>), grid, block, par_bytes, s, a, P, nwin, blocks_per_bg); \
     break;
 #define SS_LAUNCH(G, V)                                                                                      \
   switch (mode) {                                                                                            \
