@@ -355,8 +355,11 @@ def conv_bench(args, p, to_dev, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU's clock ramps up over the first tens of milliseconds of sustained work (workload 1:
+    # 0.142 ms per launch over 100 back-to-back launches, 0.129 over 1000), so the defaults warm
+    # up for ~25 ms and time ~0.13 s of steady state.
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=3)
@@ -387,7 +390,7 @@ def main():
     import torch
 
     from selective_state_space_88_amd import inputs
-    from selective_state_space_88_amd.scan import scan_fwd
+    from selective_state_space_88_amd.scan import fwd_launcher
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -416,10 +419,11 @@ def main():
     y = torch.empty(p.u.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"],
-                 softplus=p.softplus, y=y, stream=stream.cuda_stream, zoh=args.zoh,
-                 trapezoid=args.trapezoid)
+    # one ss_scan_fwd call per step, its descriptors built once (the per-call marshalling of
+    # scan_fwd takes host time comparable to the kernel, which would leave the GPU idle between
+    # launches)
+    step = fwd_launcher(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], y,
+                        softplus=p.softplus, stream=stream.cuda_stream, zoh=args.zoh, trapezoid=args.trapezoid)
 
     for _ in range(args.warmup):
         step()
@@ -427,20 +431,20 @@ def main():
 
     copy_calibration(args, dev)
 
-    # timed region: K back-to-back steps, bracketed by device synchronisation
+    # timed region: K back-to-back steps, bracketed by device synchronisation; HIP events on the
+    # launch stream around the K launches give the kernel's average duration (the step is that
+    # one kernel)
     K = args.steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e_start.record(stream)
     for i in range(K):
-        starts[i].record(stream)
         step()
-        ends[i].record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_launch_s = float(np.mean(launch_ms)) * 1e-3
+    avg_launch_s = e_start.elapsed_time(e_end) * 1e-3 / K
 
     E = p.batch * p.channels * p.length
     value = E * K / wall

@@ -164,6 +164,35 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     return y
 
 
+def fwd_launcher(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                 C: torch.Tensor, D: Optional[torch.Tensor], z: Optional[torch.Tensor],
+                 delta_bias: Optional[torch.Tensor], y: torch.Tensor, *, softplus: bool = True,
+                 stream: Optional[int] = None, zoh: bool = False, trapezoid: bool = False):
+    """The same ss_scan_fwd call as scan_fwd, with its descriptors built once: returns a
+    function of no arguments that launches the scan on these tensors (which it keeps alive) and
+    raises ScanError on a failing code.  For loops that repeat one call on the same buffers,
+    where per-call argument marshalling would otherwise cost more host time than the kernel."""
+    _check_cuda(u, delta, A, B, C, D, z, delta_bias, y)
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    keep = (u, delta, A, B, C, D, z, delta_bias, y)
+    descs = [describe(t) for t in keep]
+    refs = [_ref(d) for d in descs]
+    fn = lib().ss_scan_fwd
+    cflags, cstream = ctypes.c_uint32(flags), ctypes.c_void_p(stream or 0)
+    args = tuple(refs[:8]) + (cflags, refs[8], cstream)
+
+    def launch() -> None:
+        rc = fn(*args)
+        if rc != 0:
+            raise ScanError(rc, strerror(rc))
+
+    launch.keep = (keep, descs)   # the tensors and descriptors live as long as the launcher
+    return launch
+
+
 def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
               C: torch.Tensor, D: Optional[torch.Tensor], z: Optional[torch.Tensor],
               delta_bias: Optional[torch.Tensor], h: torch.Tensor, *, softplus: bool = True,

@@ -238,6 +238,28 @@ def test_error_leaves_output_untouched():
     assert torch.all(y == 7.0)
 
 
+def test_prepared_launcher_matches_scan_fwd():
+    """fwd_launcher (descriptors built once, as bench.py times it) makes the same call as
+    scan_fwd: identical y on every repeat, and a failing call raises."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import ScanError, fwd_launcher, scan_fwd
+
+    p = inputs.make(1, batch=2, channels=24, length=2 * 1024 + 512)
+    say("[parity] prepared launcher: batch=%d channels=%d L=%d" % (p.batch, p.channels, p.length))
+    t = dev_problem(p)
+    ref = scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+    y = torch.full_like(ref, 5.0)
+    launch = fwd_launcher(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], y)
+    for _ in range(3):
+        launch()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref)
+    bad = fwd_launcher(t["u"], t["delta"], t["A"][:, :3].contiguous(), t["B"], t["C"], t["D"], t["z"],
+                       t["delta_bias"], y)
+    with pytest.raises(ScanError):
+        bad()
+
+
 # ---------------------------------------------------------------- full-size workloads
 def sample_rows(p, k, seed):
     total = p.batch * p.channels
