@@ -50,27 +50,74 @@ __device__ __forceinline__ void compose(float& A, float& B, float Ao, float Bo) 
   A = A * Ao;
 }
 
-// Inclusive scan of affine maps x -> A x + B over the 64 lanes, composed left to right (lane j
-// ends with the maps of lanes 0..j, lane 0's applied first): row_shr 1, 2, 4, 8 inside rows of
-// 16 (a lane with no source takes the identity), then row 0's total into row 1 and row 2's into
-// row 3 (row_bcast:15), then lane 31's into rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ void scan_up(float& A, float& B) {
-  compose(A, B, dpp_or<0x111, 0xf>(1.f, A), dpp_or<0x111, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x112, 0xf>(1.f, A), dpp_or<0x112, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x114, 0xf>(1.f, A), dpp_or<0x114, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x118, 0xf>(1.f, A), dpp_or<0x118, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x142, 0xa>(1.f, A), dpp_or<0x142, 0xa>(0.f, B));
-  compose(A, B, dpp_or<0x143, 0xc>(1.f, A), dpp_or<0x143, 0xc>(0.f, B));
+// the next lane's map (lane 63: the identity)
+__device__ __forceinline__ void shift_down(float& A, float& B) {
+  A = dpp_or<0x130, 0xf>(1.f, A);   // wave_shl:1
+  B = dpp_or<0x130, 0xf>(0.f, B);
 }
 
-// Inclusive scan composed right to left (lane j ends with the maps of lanes j..63, lane 63's
-// applied first): row_shl 1, 2, 4, 8 inside rows, then each row composed with the totals of the
-// rows above it (read from their first lanes).
-__device__ __forceinline__ void scan_down(float& A, float& B, int lane) {
-  compose(A, B, dpp_or<0x101, 0xf>(1.f, A), dpp_or<0x101, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x102, 0xf>(1.f, A), dpp_or<0x102, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x104, 0xf>(1.f, A), dpp_or<0x104, 0xf>(0.f, B));
-  compose(A, B, dpp_or<0x108, 0xf>(1.f, A), dpp_or<0x108, 0xf>(0.f, B));
+// One scan step on both halves of the map with fused DPP instructions: B += B[src] A, then
+// A *= A[src] (the source lane's map applied first).  A lane whose source is outside its row
+// (row_shr/row_shl) or whose row is masked off is not written, i.e. composes with the identity.
+// The trailing s_nop supplies the second wait state between a VALU write and the next DPP
+// read of the same VGPR (the single chain leaves only one instruction between them).
+#define SS_BSTEP(CTRL)                                  \
+  "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n"               \
+  "v_mul_f32_dpp %0, %0, %0 " CTRL "\n"                \
+  "s_nop 0\n"
+
+// Exclusive left-to-right scan of the lanes' maps over the 64 lanes: lane j ends with the maps
+// of lanes 0..j-1 composed (lane 0: the identity).  Inclusive within rows of 16 by row_shr
+// 1, 2, 4, 8, then rows 0 and 2 into rows 1 and 3 (row_bcast:15), lane 31 into rows 2 and 3
+// (row_bcast:31), then a shift by one lane (wave_shr:1) onto the identity.
+__device__ __forceinline__ void scan_up_exclusive(float& A, float& B) {
+  float ea, eb;
+  asm volatile("s_nop 1\n"
+               SS_BSTEP("row_shr:1 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:2 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:4 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:8 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_bcast:15 row_mask:0xa bank_mask:0xf")
+               SS_BSTEP("row_bcast:31 row_mask:0xc bank_mask:0xf")
+               "v_mov_b32 %2, 1.0\n"
+               "v_mov_b32 %3, 0\n"
+               "v_mov_b32_dpp %2, %0 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+               "v_mov_b32_dpp %3, %1 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+               : "+v"(A), "+v"(B), "=&v"(ea), "=&v"(eb));
+  A = ea;
+  B = eb;
+}
+
+// Inclusive left-to-right scan over the 64 lanes (the steps of scan_up_exclusive without the
+// final shift): lane j ends with the maps of lanes 0..j composed.
+__device__ __forceinline__ void scan_up_inclusive(float& A, float& B) {
+  asm volatile("s_nop 1\n"
+               SS_BSTEP("row_shr:1 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:2 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:4 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shr:8 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_bcast:15 row_mask:0xa bank_mask:0xf")
+               SS_BSTEP("row_bcast:31 row_mask:0xc bank_mask:0xf")
+               : "+v"(A), "+v"(B));
+}
+
+// Inclusive right-to-left scan within each row of 16 lanes (row_shl 1, 2, 4, 8): lane j ends
+// with the maps of lanes j..(end of its row), the highest lane's applied first.
+__device__ __forceinline__ void scan_down_rows(float& A, float& B) {
+  asm volatile("s_nop 1\n"
+               SS_BSTEP("row_shl:1 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shl:2 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shl:4 row_mask:0xf bank_mask:0xf")
+               SS_BSTEP("row_shl:8 row_mask:0xf bank_mask:0xf")
+               : "+v"(A), "+v"(B));
+}
+#undef SS_BSTEP
+
+// Inclusive right-to-left scan over the 64 lanes (lane j ends with the maps of lanes j..63, lane
+// 63's applied first): within rows by fused DPP, then each row composed with the totals of the
+// rows above it (read from their first lanes)
+__device__ __forceinline__ void scan_down_fused(float& A, float& B, int lane) {
+  scan_down_rows(A, B);
   const float a1 = readlane_f(A, 16), b1 = readlane_f(B, 16);
   const float a2 = readlane_f(A, 32), b2 = readlane_f(B, 32);
   const float a3 = readlane_f(A, 48), b3 = readlane_f(B, 48);
@@ -82,16 +129,6 @@ __device__ __forceinline__ void scan_down(float& A, float& B, int lane) {
   const float Sa = row == 0 ? s0a : row == 1 ? s1a : row == 2 ? s2a : 1.f;
   const float Sb = row == 0 ? s0b : row == 1 ? s1b : row == 2 ? s2b : 0.f;
   compose(A, B, Sa, Sb);
-}
-
-// the previous lane's map (lane 0: the identity), and the next lane's (lane 63: the identity)
-__device__ __forceinline__ void shift_up(float& A, float& B) {
-  A = dpp_or<0x138, 0xf>(1.f, A);   // wave_shr:1
-  B = dpp_or<0x138, 0xf>(0.f, B);
-}
-__device__ __forceinline__ void shift_down(float& A, float& B) {
-  A = dpp_or<0x130, 0xf>(1.f, A);   // wave_shl:1
-  B = dpp_or<0x130, 0xf>(0.f, B);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -158,7 +195,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
         }
         Af[s] = a;
         Bf[s] = h;
-        scan_up(Af[s], Bf[s]);
+        scan_up_inclusive(Af[s], Bf[s]);
       }
       // the window's start state is stored, and its end state (lane 63's map) carried on
       const float h0 = hst[wave][pp][0], h1 = hst[wave][pp][1];
@@ -303,9 +340,8 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
           Af *= av[k];
         }
         const float Pl = Af;   // the lane's total decay (both directions)
-        scan_up(Af, Bf);
         float Ae = Af, Be = Bf;
-        shift_up(Ae, Be);
+        scan_up_exclusive(Ae, Be);
         const float hw = nv ? ckpt[(row * nwin + w) * N + n] : 0.f;
         float hs[kBK + 1];
         hs[0] = fmaf(Ae, hw, Be);
@@ -320,7 +356,7 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
 #pragma unroll
         for (int k = kBK - 1; k >= 0; --k) c = av[k] * fmaf(cv[k], dy0[k], c);
         float Ar = Pl, Br2 = c;
-        scan_down(Ar, Br2, lane);
+        scan_down_fused(Ar, Br2, lane);
         float Ad = Ar, Bd = Br2;
         shift_down(Ad, Bd);
         const float Xw = gcar[wave][pp][s];
