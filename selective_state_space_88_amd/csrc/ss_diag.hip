@@ -144,13 +144,18 @@ __device__ __forceinline__ void row_exclusive_scan2(float& a0, float& b0, float&
   b1 = eb1;
 }
 
-// The same for one state: one exclusive scan of (a, b) within each row of 64 / ROWS lanes, with
-// this lane's four C quads of that state read (at cbase + the given offsets) while it runs.  A
-// single chain leaves one instruction between a VALU write and the next DPP read of the same
-// VGPR, so each step ends with an s_nop that supplies the second wait state.
+// The same for one state, returning this lane's incoming state: an inclusive scan of (a, b)
+// within each row of 64 / ROWS lanes gives every lane the map of its row's lanes up to itself,
+// applied to the carried state (carry: the row's state before the window) that is the state
+// at the end of the lane's steps, and a shift by one lane within the row (its first lane
+// taking the carried state itself) makes it the state before them.  This lane's four C quads
+// of the state (at cbase + the given offsets) are read while the scan runs.  A single chain
+// leaves one instruction between a VALU write and the next DPP read of the same VGPR, so each
+// step ends with an s_nop that supplies the second wait state.
 template <int ROWS, int O0, int O1, int O2, int O3>
-__device__ __forceinline__ void row_exclusive_scan1(float& a, float& bb, uint32_t cbase, f32x4 (&c)[4]) {
-  float ea, eb;
+__device__ __forceinline__ float row_incoming_state1(float a, float bb, float carry, uint32_t cbase,
+                                                     f32x4 (&c)[4]) {
+  float he, hs;
 #define SS_STEP1(CTRL)                                  \
   "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n"               \
   "v_mul_f32_dpp %0, %0, %0 " CTRL "\n"                \
@@ -161,36 +166,37 @@ __device__ __forceinline__ void row_exclusive_scan1(float& a, float& bb, uint32_
   SS_STEP1("row_shr:2 row_mask:0xf bank_mask:0xf")      \
   SS_STEP1("row_shr:4 row_mask:0xf bank_mask:0xf")      \
   SS_STEP1("row_shr:8 row_mask:0xf bank_mask:0xf")
-#define SS_IDENT1                                       \
-  "v_mov_b32 %2, 1.0\n"                                \
-  "v_mov_b32 %3, 0\n"
-#define SS_SHIFT1(CTRL)                                 \
-  "v_mov_b32_dpp %2, %0 " CTRL "\n"                    \
-  "v_mov_b32_dpp %3, %1 " CTRL "\n"
+#define SS_END1                                         \
+  "v_fma_f32 %2, %0, %8, %1\n"                         \
+  "v_mov_b32 %3, %8\n"                                 \
+  "s_nop 0\n"
 #define SS_LOADC1                                       \
-  "ds_read_b128 %4, %8 offset:%9\n"                    \
-  "ds_read_b128 %5, %8 offset:%10\n"                   \
-  "ds_read_b128 %6, %8 offset:%11\n"                   \
-  "ds_read_b128 %7, %8 offset:%12\n"
+  "ds_read_b128 %4, %9 offset:%10\n"                   \
+  "ds_read_b128 %5, %9 offset:%11\n"                   \
+  "ds_read_b128 %6, %9 offset:%12\n"                   \
+  "ds_read_b128 %7, %9 offset:%13\n"
 #define SS_OPS1                                                                                 \
-  : "+v"(a), "+v"(bb), "=&v"(ea), "=&v"(eb), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]) \
-  : "v"(cbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
+  : "+v"(a), "+v"(bb), "=&v"(he), "=&v"(hs), "=&v"(c[0]), "=&v"(c[1]), "=&v"(c[2]), "=&v"(c[3]) \
+  : "v"(carry), "v"(cbase), "n"(O0), "n"(O1), "n"(O2), "n"(O3)
   if constexpr (ROWS == 1) {
     asm volatile(SS_LOADC1
                  SS_SCAN16_1
                  SS_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf")
                  SS_STEP1("row_bcast:31 row_mask:0xc bank_mask:0xf")
-                 SS_IDENT1
-                 SS_SHIFT1("wave_shr:1 row_mask:0xf bank_mask:0xf")
+                 SS_END1
+                 "v_mov_b32_dpp %3, %2 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
                  "s_waitcnt lgkmcnt(0)\n"
                  SS_OPS1);
   } else if constexpr (ROWS == 2) {
+    // the second half of a 32-lane row starts from lane 15 of the first (row_bcast:15 on the
+    // first four lanes of DPP rows 1 and 3), the other lanes from the lane below (row_shr:1;
+    // the first lane of each DPP row has no source there and keeps what it has)
     asm volatile(SS_LOADC1
                  SS_SCAN16_1
                  SS_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf")
-                 SS_IDENT1
-                 SS_SHIFT1("row_bcast:15 row_mask:0xa bank_mask:0x1")
-                 SS_SHIFT1("row_shr:1 row_mask:0xf bank_mask:0xf")
+                 SS_END1
+                 "v_mov_b32_dpp %3, %2 row_bcast:15 row_mask:0xa bank_mask:0x1\n"
+                 "v_mov_b32_dpp %3, %2 row_shr:1 row_mask:0xf bank_mask:0xf\n"
                  "s_waitcnt lgkmcnt(0)\n"
                  SS_OPS1);
   } else {
@@ -198,12 +204,10 @@ __device__ __forceinline__ void row_exclusive_scan1(float& a, float& bb, uint32_
   }
 #undef SS_OPS1
 #undef SS_LOADC1
-#undef SS_SHIFT1
-#undef SS_IDENT1
+#undef SS_END1
 #undef SS_SCAN16_1
 #undef SS_STEP1
-  a = ea;
-  bb = eb;
+  return hs;
 }
 
 // One direct-to-LDS copy of 16 bytes per lane: lane i's 16 bytes from `src` land at
@@ -689,37 +693,38 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
         // the two states one after the other (the registers of one state's K decays and inputs
         // are reused by the next)
         float hend[2];
-  #pragma unroll
+#pragma unroll
         for (int si = 0; si < 2; ++si) {
           const float An = si ? pv.y : pv.x;   // A_n log2 e
           float av[kK], bv[kK];
           float h = 0.f;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
           if constexpr (ZOH) {
             // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
             const float Anl = An * kLn2f;
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < kK; ++j) {
               const float x = dt[j] * Anl;
               bv[j] = wv[j] * zoh_phi(x, av[j], __builtin_amdgcn_rcpf(x)) * bq[4 * si + j / 4][j % 4];
             }
           } else {
-  #pragma unroll
+#pragma unroll
             for (int j = 0; j < kK; ++j) bv[j] = wv[j] * bq[4 * si + j / 4][j % 4];
           }
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
           // lane aggregate: decay over the lane's K steps and the lane's state from zero; the
           // scan, with this lane's C values of the state read while it runs
           float sa = __builtin_amdgcn_exp2f(sdt * An), sb = h;
           f32x4 cq[4];
+          const float carry = si ? pv.w : pv.z;
           if (si == 0)
-            row_exclusive_scan1<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS>(sa, sb, lbase, cq);
+            h = row_incoming_state1<ROWS, 4 * W, 4 * W + QS, 4 * W + 2 * QS, 4 * W + 3 * QS>(sa, sb, carry, lbase, cq);
           else
-            row_exclusive_scan1<ROWS, 12 * W, 12 * W + QS, 12 * W + 2 * QS, 12 * W + 3 * QS>(sa, sb, lbase, cq);
-          h = fmaf(sa, si ? pv.w : pv.z, sb);
-  #pragma unroll
+            h = row_incoming_state1<ROWS, 12 * W, 12 * W + QS, 12 * W + 2 * QS, 12 * W + 3 * QS>(sa, sb, carry, lbase,
+                                                                                                cq);
+#pragma unroll
           for (int j = 0; j < kK; ++j) {
             h = fmaf(av[j], h, bv[j]);
             if constexpr (TRAP) yv[j] = fmaf(cq[j / 4][j % 4], fmaf(-0.5f, bv[j], h), yv[j]);
@@ -733,7 +738,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
         float av0[kK], bv0[kK], av1[kK], bv1[kK];
         float wz0[ZOH ? kK : 1], wz1[ZOH ? kK : 1];
         float h0 = 0.f, h1 = 0.f;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kK; ++j) {
           av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
           av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
@@ -741,14 +746,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
         if constexpr (ZOH) {
           // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
           const float An0 = pv.x * kLn2f, An1 = pv.y * kLn2f;
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < kK; ++j) {
             const float x0 = dt[j] * An0, x1 = dt[j] * An1;
             wz0[j] = wv[j] * zoh_phi(x0, av0[j], __builtin_amdgcn_rcpf(x0));
             wz1[j] = wv[j] * zoh_phi(x1, av1[j], __builtin_amdgcn_rcpf(x1));
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kK; ++j) {
           bv0[j] = (ZOH ? wz0[j] : wv[j]) * bq[j / 4][j % 4];
           bv1[j] = (ZOH ? wz1[j] : wv[j]) * bq[4 + j / 4][j % 4];
@@ -764,7 +769,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
                             12 * W + 2 * QS, 12 * W + 3 * QS>(sa0, sb0, sa1, sb1, lbase, cq);
         h0 = fmaf(sa0, pv.z, sb0);
         h1 = fmaf(sa1, pv.w, sb1);
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < kK; ++j) {
           h0 = fmaf(av0[j], h0, bv0[j]);
           h1 = fmaf(av1[j], h1, bv1[j]);
