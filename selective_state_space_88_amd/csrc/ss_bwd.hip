@@ -277,6 +277,7 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
   for (int64_t w = nwin - 1; w >= 0; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
     float dt[kBK], uu[kBK], wv[kBK], dy0[kBK], y0[kBK], du[kBK], ddt[kBK], sg[kBK], dyv[kBK], zv[kBK], dv[kBK];
+    float sdt = 0.f;   // the lane's steps' total step size
     load_seg<kBK>(dr, t0, L, p.vec, dv);
     load_seg<kBK>(ur, t0, L, p.vec, uu);
     load_seg<kBK>(dyr, t0, L, p.vec, dyv);
@@ -293,8 +294,9 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
       if constexpr (GATE) gz = silu_fast(zv[k]);
       dy0[k] = dyv[k] * gz;
       y0[k] = Dd * uu[k];
-      du[k] = dy0[k] * Dd;
+      du[k] = 0.f;   // here: sum over the states of g_t B_t (du and ddt take it once per step below)
       ddt[k] = 0.f;
+      sdt += dt[k];
     }
     // scalar decay: one exp per step for every state
     float ah[kBK];
@@ -333,12 +335,9 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
 #pragma unroll
         for (int k = 0; k < kBK; ++k) av[k] = SCALAR ? ah[k] : __builtin_amdgcn_exp2f(dt[k] * A2);
         // states: the lane's steps from zero, the scan, then from the incoming state
-        float Af = 1.f, Bf = 0.f;
+        float Af = __builtin_amdgcn_exp2f(sdt * A2), Bf = 0.f;   // the decay over the lane's steps
 #pragma unroll
-        for (int k = 0; k < kBK; ++k) {
-          Bf = fmaf(av[k], Bf, wv[k] * bv[k]);
-          Af *= av[k];
-        }
+        for (int k = 0; k < kBK; ++k) Bf = fmaf(av[k], Bf, wv[k] * bv[k]);
         const float Pl = Af;   // the lane's total decay (both directions)
         float Ae = Af, Be = Bf;
         scan_up_exclusive(Ae, Be);
@@ -367,9 +366,9 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
           const float gk = fmaf(cv[k], dy0[k], c);
           rC[s][k] = dy0[k] * hs[k + 1];
           rB[s][k] = gk * wv[k];
-          du[k] = fmaf(gk * dt[k], bv[k], du[k]);
+          du[k] = fmaf(gk, bv[k], du[k]);
           const float gha = gk * hs[k] * av[k];
-          ddt[k] = fmaf(gha, An, fmaf(gk * bv[k], uu[k], ddt[k]));
+          ddt[k] = fmaf(gha, An, ddt[k]);
           dAs = fmaf(gha, dt[k], dAs);
           c = av[k] * gk;
         }
@@ -419,7 +418,13 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
     float* ddr = p.ddelta + b * p.dd_sb + hd * p.dd_sh;
     float dxs[kBK];
 #pragma unroll
-    for (int k = 0; k < kBK; ++k) dxs[k] = (valid && t0 + k < L) ? ddt[k] * sg[k] : 0.f;
+    for (int k = 0; k < kBK; ++k) {
+      // with gB = sum_n g B: du = dt gB + D dy0 and ddt += u gB
+      const float gB = du[k];
+      du[k] = fmaf(dt[k], gB, dy0[k] * Dd);
+      ddt[k] = fmaf(uu[k], gB, ddt[k]);
+      dxs[k] = (valid && t0 + k < L) ? ddt[k] * sg[k] : 0.f;
+    }
     if (p.chan_per_head % kMWaves == 0 && p.chan_per_group % kMWaves == 0) {
       // the block's 8 channels share the head: summed through LDS, one atomic add per step
 #pragma unroll
