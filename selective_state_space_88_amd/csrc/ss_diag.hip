@@ -903,13 +903,16 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
 
 int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
 
-// Channels per wave: two when that still leaves several rounds of waves for the chip's
-// 2048 two-per-SIMD slots (so that the last, partial round stays a small part of the run).
+// Channels per wave: one while every row still gets its own wave in a single round of one
+// block of four waves per CU (one channel per wave fits one such block per CU in LDS); beyond
+// that two, which run three waves per SIMD.  Measured on workload-1-shaped rows: 1024 rows 0.023
+// ms with one channel per wave against 0.039 with two; 1280 rows 0.043 against 0.039; 6144 rows
+// 0.131 against 0.069.
 int rows_of(const ScanArgs& a) {
 #ifdef SS_DIAG_ROWS
   return SS_DIAG_ROWS;
 #else
-  return a.batch * a.channels >= 2 * 2048 * 3 ? 2 : 1;
+  return a.batch * a.channels > (int64_t)kWaves * cu_count() ? 2 : 1;
 #endif
 }
 

@@ -122,6 +122,9 @@ struct ConvArgs {
 // out_t = bias + sum_j w[j] x_{t-(W-1)+j} (optionally silu) for every (batch, channel) row.
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int cu_count();
+
 // Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time.  One
 // kernel, no workspace.
 hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);

@@ -487,11 +487,6 @@ bool ssd_path(const ScanArgs& a) {
   return a.in_bf16 && a.chan_per_head % kSlab == 0 && a.chan_per_group % kSlab == 0;
 }
 
-namespace {
-
-constexpr int kBlocksPerCU = 3;     // resident scan blocks per CU (VGPRs: three waves per SIMD)
-constexpr int64_t kMinSegChunks = 16;
-
 // compute units of the current device (cached per device)
 int cu_count() {
   static std::atomic<int> cache[64];
@@ -504,6 +499,11 @@ int cu_count() {
   }
   return v;
 }
+
+namespace {
+
+constexpr int kBlocksPerCU = 3;     // resident scan blocks per CU (VGPRs: three waves per SIMD)
+constexpr int64_t kMinSegChunks = 16;
 
 struct SegPlan {
   int64_t cps;
