@@ -502,7 +502,12 @@ int cu_count() {
 
 namespace {
 
-constexpr int kBlocksPerCU = 3;     // resident scan blocks per CU (VGPRs: three waves per SIMD)
+// Blocks per CU the segments aim for.  Two output-pass blocks fit per CU (VGPRs and AGPRs
+// share one register file: ~192 per lane, two waves per SIMD), and two rounds of them measured
+// best: on workload 4 (160 rows of 256 chunks) 3 segments 0.321 ms, 4: 0.337, 6: 0.307,
+// 8: 0.305, 12: 0.315, 16: 0.345 (shorter segments shorten the last round; more of them
+// lengthen the state pass).
+constexpr int kBlocksPerCU = 4;
 constexpr int64_t kMinSegChunks = 16;
 
 struct SegPlan {
@@ -511,7 +516,7 @@ struct SegPlan {
   int64_t rows;
 };
 
-// enough segments to give every CU kBlocksPerCU blocks, none shorter than kMinSegChunks
+// enough segments to give every CU about kBlocksPerCU blocks, none shorter than kMinSegChunks
 // chunks (the state pass stages the B part in whole 16-byte pieces per thread: Np of 64, 128)
 SegPlan seg_plan(const ScanArgs& a) {
   const int64_t nch = nchunks_of(a);
