@@ -282,6 +282,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
+// The zero-order-hold input coefficient (exp(dt A) - 1) / A of one (step, state), from
+// x = dt A, the decay e = exp(x) already computed and rA = 1 / A (A = 0 gives x = 0).  Where
+// |x| < 1/8, dt phi(x) with phi(x) = expm1(x) / x from its Taylor polynomial to degree 5
+// (truncation below 1e-9 relative); elsewhere e rA - rA, whose relative error from e's
+// rounding is at most 2^-23 / (1 - e^(-1/8)) ~ 1e-6.  (No per-step reciprocal: dt cancels.)
+__device__ __forceinline__ float zoh_coef(float dt, float x, float e, float rA) {
+  float q = 1.f / 720.f;
+  q = fmaf(q, x, 1.f / 120.f);
+  q = fmaf(q, x, 1.f / 24.f);
+  q = fmaf(q, x, 1.f / 6.f);
+  q = fmaf(q, x, 0.5f);
+  q = fmaf(q, x, 1.f);
+  return fabsf(x) < 0.125f ? dt * q : fmaf(e, rA, -rA);
+}
+
 // The carried state pair (.z, .w) of one pair's parameters, written through asm: a plain store
 // would make the compiler wait for every copy in flight first.
 __device__ __forceinline__ void par_state_write(float4* pp, float h0, float h1) {
@@ -629,7 +644,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
           const float sp = p.softplus ? softplus_fast(x) : x;
           const float uu = seg_get<TIn>(su, j);
           dt[j] = sp;
-          wv[j] = sp * uu;
+          wv[j] = ZOH ? uu : sp * uu;   // (zero-order hold: u, its coefficient already holds dt)
           yv[j] = Dd * uu;
           sdt += sp;
         }
@@ -642,7 +657,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
           const float sp = j < rem ? (p.softplus ? softplus_fast(x) : x) : 0.f;
           const float uu = j < rem ? seg_get<TIn>(su, j) : 0.f;
           dt[j] = sp;
-          wv[j] = sp * uu;
+          wv[j] = ZOH ? uu : sp * uu;   // (zero-order hold: u, its coefficient already holds dt)
           yv[j] = Dd * uu;
           sdt += sp;
         }
@@ -701,13 +716,11 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
 #pragma unroll
           for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
           if constexpr (ZOH) {
-            // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
-            const float Anl = An * kLn2f;
+            // u B times (exp(dt A) - 1) / A, from the decays just computed
+            const float Anl = An * kLn2f, rA = __builtin_amdgcn_rcpf(Anl);
 #pragma unroll
-            for (int j = 0; j < kK; ++j) {
-              const float x = dt[j] * Anl;
-              bv[j] = wv[j] * zoh_phi(x, av[j], __builtin_amdgcn_rcpf(x)) * bq[4 * si + j / 4][j % 4];
-            }
+            for (int j = 0; j < kK; ++j)
+              bv[j] = zoh_coef(dt[j], dt[j] * Anl, av[j], rA) * wv[j] * bq[4 * si + j / 4][j % 4];
           } else {
 #pragma unroll
             for (int j = 0; j < kK; ++j) bv[j] = wv[j] * bq[4 * si + j / 4][j % 4];
@@ -744,13 +757,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
           av1[j] = __builtin_amdgcn_exp2f(dt[j] * pv.y);
         }
         if constexpr (ZOH) {
-          // dt u B times phi(dt A) = (exp(dt A) - 1) / (dt A), from the decays just computed
+          // u times (exp(dt A) - 1) / A, from the decays just computed
           const float An0 = pv.x * kLn2f, An1 = pv.y * kLn2f;
+          const float rA0 = __builtin_amdgcn_rcpf(An0), rA1 = __builtin_amdgcn_rcpf(An1);
 #pragma unroll
           for (int j = 0; j < kK; ++j) {
-            const float x0 = dt[j] * An0, x1 = dt[j] * An1;
-            wz0[j] = wv[j] * zoh_phi(x0, av0[j], __builtin_amdgcn_rcpf(x0));
-            wz1[j] = wv[j] * zoh_phi(x1, av1[j], __builtin_amdgcn_rcpf(x1));
+            wz0[j] = zoh_coef(dt[j], dt[j] * An0, av0[j], rA0) * wv[j];
+            wz1[j] = zoh_coef(dt[j], dt[j] * An1, av1[j], rA1) * wv[j];
           }
         }
 #pragma unroll
