@@ -32,6 +32,9 @@ CASES = {
     "1024 rows": lambda: inputs.random_problem(1203, 2, 512, 600, 16),
     # heads of several channels sharing a step size, two B/C groups
     "heads and groups": lambda: inputs.random_problem(1204, 2, 640, 777, 16, heads=160, groups=2),
+    # the largest state (64 pairs: 8 KB of per-pair parameters, two blocks per CU) and an odd one
+    "N128": lambda: inputs.random_problem(1205, 1, 1100, 300, 128, gate=False),
+    "N33": lambda: inputs.random_problem(1206, 1, 1100, 515, 33),
 }
 
 
