@@ -56,7 +56,8 @@ def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
 
 # source file of each scan kernel
 KERNEL_SOURCE = {"diag_fwd_kernel": "ss_diag.hip", "scalar_head_kernel": "ss_scalar.hip",
-                 "ssd_scan_kernel": "ss_ssd.hip", "conv1d_kernel": "ss_conv.hip"}
+                 "ssd_scan_kernel": "ss_ssd.hip", "conv1d_kernel": "ss_conv.hip",
+                 "bwd_kernel": "ss_bwd.hip", "ssdb_main_kernel": "ss_ssd_bwd.hip"}
 
 
 def scan_kernel(p):
@@ -242,6 +243,7 @@ def backward_bench(args, p, to_dev, dev):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    copy_calibration(args, dev)
     K = args.steps
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -263,15 +265,17 @@ def backward_bench(args, p, to_dev, dev):
     tf = flops / per / 1e12
     P = p.channels // p.heads
     matrix = p.scalar_decay and not p.gate and P % 64 == 0 and (p.channels // p.groups) % 64 == 0
+    dominant = "ssdb_main_kernel" if matrix else "bwd_kernel"
+    traffic = stored_traffic(dominant, args.workload, kernel_source_digest(dominant), mode="backward")
     out = {
         "metric": "selective-scan bwd elems/s (B*D*L/s), 1 GPU", "value": E * K / wall, "unit": "elems/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": wall / K * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": "backward, " + describe(p), "batch": p.batch, "channels": p.channels,
                    "seq_len": p.length, "nstate": p.nstate,
-                   "kernel": "ssdb_main_kernel" if matrix else "bwd_kernel"},
+                   "kernel": dominant},
         "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": None, "call_ms": per * 1e3,
+                     "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "call_ms": per * 1e3,
                      "flop_equiv_per_call": flops, "hbm_algorithmic_bytes_per_call": nbytes,
                      "hbm_achieved_GBps": nbytes / per / 1e9},
         "cpu_baseline": None,
@@ -289,7 +293,7 @@ def backward_bench(args, p, to_dev, dev):
         rl = out["roofline"]
         out["roofline"] = {
             "bound": "mfma", "achieved": mf / per / 1e12, "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": mf / per / 1e12 / FP32_MATRIX_PEAK_TFLOPS, "traffic": None, "call_ms": rl["call_ms"],
+            "frac": mf / per / 1e12 / FP32_MATRIX_PEAK_TFLOPS, "traffic": traffic, "call_ms": rl["call_ms"],
             "mfma_flops_per_call": mf, "alu_flop_equiv_per_call": flops, "alu_equiv_TFLOPs": tf,
             "hbm_algorithmic_bytes_per_call": nbytes, "hbm_achieved_GBps": nbytes / per / 1e9,
         }

@@ -50,8 +50,9 @@ __device__ __forceinline__ f32x4 mma4(float a, float b, f32x4 c) {
 // acc[t] += A[i][0..K) . Bt_t[j][0..K) for NT 16x16 tiles sharing their 16 rows of A: lane l takes
 // row i = l % 16 of A and row j = l % 16 of tile t's Bt = B + t * bstep.  Rows are k-contiguous
 // and 16-byte aligned; lane l supplies k = 16 kb + 4 (l / 16) + m to MFMA m of block kb.  With
-// SCALE, A's k-th column is multiplied by sc[k] on the way.
-template <int K, int NT, bool SCALE = false>
+// SCALE, A's k-th column is multiplied by sc[k] on the way.  With TR the tiles come out transposed
+// (acc[t] += Bt_t . A^T): lane l then holds column i = l % 16 and rows j = 4 (l / 16) + m.
+template <int K, int NT, bool SCALE = false, bool TR = false>
 __device__ __forceinline__ void mm(const float* A, int lda, const float* B, int ldb, int bstep, int lane,
                                    f32x4 (&acc)[NT], const float* sc = nullptr) {
   const int r = lane & 15, q = lane >> 4;
@@ -70,12 +71,12 @@ __device__ __forceinline__ void mm(const float* A, int lda, const float* B, int 
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mma4(av[m], bv[t][m], acc[t]);
+      for (int t = 0; t < NT; ++t) acc[t] = TR ? mma4(bv[t][m], av[m], acc[t]) : mma4(av[m], bv[t][m], acc[t]);
   }
 }
 
 // As mm with K = 64, Bt a [rows][64] array swizzled as swz (rows 16 t + l % 16 of tile t).
-template <int NT>
+template <int NT, bool TR = false>
 __device__ __forceinline__ void mm_swz(const float* A, int lda, const float* Bsw, int lane, f32x4 (&acc)[NT]) {
   const int r = lane & 15, q = lane >> 4;
   const float* a = A + r * lda + 4 * q;
@@ -91,7 +92,7 @@ __device__ __forceinline__ void mm_swz(const float* A, int lda, const float* Bsw
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = mma4(av[m], bv[t][m], acc[t]);
+      for (int t = 0; t < NT; ++t) acc[t] = TR ? mma4(bv[t][m], av[m], acc[t]) : mma4(av[m], bv[t][m], acc[t]);
   }
 }
 
@@ -448,35 +449,39 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
       csum += __shfl_xor(csum, 32);
       if (q == 0) colp[ti][s] = csum;
     }
-    // ---- dY H0 and X R ([T x N] tiles: rows 16 w2, state tiles nb0 ..)
+    // ---- dY H0 and X R, as transposed [N x T] tiles (state tiles nb0 .., steps 16 w2 ..): lane l
+    // holds step 16 w2 + l % 16 and states 16 (nb0 + j) + 4 (l / 16) + r, so that the sums into dB
+    // and dC below run along time (16 consecutive steps per row of lanes)
     f32x4 yh[NB], xr[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int tw = 16 * w2 + l16;   // this lane's step within the chunk
     if (bcw) {
-      mm_swz<NB>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
-      mm<kCP, NB>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
+      mm_swz<NB, true>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
+      mm<kCP, NB, false, true>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
+      const float dtw = sdt[tw];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) xr[j][r] *= sdt[16 * w2 + 4 * q + r];   // X R = diag(dt) U R
+        for (int r = 0; r < 4; ++r) xr[j][r] *= dtw;   // X R = diag(dt) U R
       // alpha_t = e^{s_t} (dY H0)_t . C_t and beta_t = e^{s_{T-1} - s_t} (X R)_t . B_t, partial over
-      // this wave's state tiles
+      // this wave's state tiles: a lane's own states, then the four rows of lanes
+      float a = 0.f, bsum = 0.f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w2 + 4 * q + r;
-        float a = 0.f, bsum = 0.f;
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int n = 16 * (nb0 + j) + l16;
-          a = fmaf(yh[j][r], cnt[n * kST + t], a);
-          bsum = fmaf(xr[j][r], bnt[n * kST + t], bsum);
+        for (int r = 0; r < 4; ++r) {
+          const int n = 16 * (nb0 + j) + 4 * q + r;
+          a = fmaf(yh[j][r], cnt[n * kST + tw], a);
+          bsum = fmaf(xr[j][r], bnt[n * kST + tw], bsum);
         }
-        a = row16_sum(a);
-        bsum = row16_sum(bsum);
-        if (l16 == 0) {
-          alp[wg][t] = a * ses[t];
-          bet[wg][t] = bsum * ser[t];
-        }
+      a += __shfl_xor(a, 16);
+      bsum += __shfl_xor(bsum, 16);
+      a += __shfl_xor(a, 32);
+      bsum += __shfl_xor(bsum, 32);
+      if (q == 0) {
+        alp[wg][tw] = a * ses[tw];
+        bet[wg][tw] = bsum * ser[tw];
       }
     } else {
       if (lane < kCT) alp[wg][lane] = bet[wg][lane] = 0.f;
@@ -500,29 +505,28 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
 
     // ---- dC = diag(e^s) dY H0 + M1 B and dB = diag(e^{s_{T-1} - s}) X R + M1^T C, added to the group's
     if (bcw) {
+      const float esw = ses[tw], erw = ser[tw];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int t = 16 * w2 + 4 * q + r;
-          yh[j][r] *= ses[t];
-          xr[j][r] *= ser[t];
+          yh[j][r] *= esw;
+          xr[j][r] *= erw;
         }
-      mm<kCT, NB>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
-      mm<kCT, NB>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
+      mm<kCT, NB, false, true>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
+      mm<kCT, NB, false, true>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
+      const int64_t t = t0 + tw;
+      if (t < L) {
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int n = 16 * (nb0 + j) + l16;
-        if (n < N) {
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 16 * w2 + 4 * q + r;
-            if (t < L) {
+            const int n = 16 * (nb0 + j) + 4 * q + r;
+            if (n < N) {
               atomicAdd(dCb + n * p.dC_sn + t, yh[j][r]);
               atomicAdd(dBb + n * p.dB_sn + t, xr[j][r]);
             }
           }
-        }
       }
     }
 
