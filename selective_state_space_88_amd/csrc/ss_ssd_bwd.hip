@@ -162,23 +162,27 @@ __device__ __forceinline__ int swz(int n, int g) { return n * kCP + 4 * (g ^ (n 
 // Pass 1: the state before every chunk, [blocks][chunks][NP][64] f32 (row n holds H0[0..63][n],
 // swizzled as swz), and C B^T of every chunk, [batch][groups][chunks][4 tiles][64 lanes][4] in the
 // lane order of the reverse pass's 16x16 tiles; a group's chunks are shared out over its blocks.
-// The states evolve independently, so each (batch, head, slab) takes two blocks, one per half of
-// the states (more blocks than CUs on the multi-head layers).
+// The states evolve independently, so each (batch, head, slab) takes kStateSplit blocks, one per
+// share of the states (more blocks than CUs on the multi-head layers, and with 128 states two or
+// three blocks per CU to cover each other's waits).
+template <int NT>
+constexpr int kStateSplit = NT >= 8 ? 4 : 2;
 template <typename TIn, int NT>
 __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch, float* __restrict__ ws,
                                                           float* __restrict__ cbws) {
   constexpr int NP = 16 * NT;
-  constexpr int NH = NT / 2, NPH = NP / 2;   // this block's state tiles and states
+  constexpr int SPL = kStateSplit<NT>;
+  constexpr int NH = NT / SPL, NPH = NP / SPL;   // this block's state tiles and states
   constexpr int kSN = NP + 4;
   __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // u^T [p][t]
-  __shared__ __attribute__((aligned(16))) float wb[NPH * kST];   // e^{s_{T-1} - s_t} dt_t B [n][t], this half
+  __shared__ __attribute__((aligned(16))) float wb[NPH * kST];   // e^{s_{T-1} - s_t} dt_t B [n][t], this share
   __shared__ __attribute__((aligned(16))) float ctn[kCT * kSN];  // C [t][n] (chunks whose C B^T this block forms)
   __shared__ __attribute__((aligned(16))) float btn[kCT * kSN];  // B [t][n]
   __shared__ float ss2[kCT], sdt[kCT];                           // cumulative log2 decay, dt
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const int64_t bx = blockIdx.x >> 1;
-  const int nh = blockIdx.x & 1;             // half of the states: rows nh NPH ..
+  const int64_t bx = blockIdx.x / SPL;
+  const int nh = blockIdx.x % SPL;           // share of the states: rows nh NPH ..
   const Blk k = block_of(p, bx);
   const int N = p.N;
   const int64_t L = p.L;
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
   const int ng = p.chan_per_group / kCP;                    // blocks sharing the group's B, C
   const int gi = (int)((k.d0 % p.chan_per_group) / kCP);
   // this thread's share of a chunk's loads: u (row pp, 8 steps from tt); B (row nh NPH + bn of
-  // the half, 16 steps from bt)
+  // the share, 16 steps from bt)
   const int pp = tid >> 2, tt = 8 * (tid & 3);
   const int bn = tid >> 1, bt = 16 * (tid & 1), bnr = nh * NPH + bn;
   // two register sets, so that a chunk's loads are issued two chunks ahead of their use
@@ -649,7 +653,7 @@ hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
   const int64_t nch = (a.L + kCT - 1) / kCT;
   const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
   float* cbws = ws + a.batch * a.heads * (a.chan_per_head / kCP) * nch * (16 * NT) * kCP;
-  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), dim3(2 * grid.x), block, 0, s, a, nch, ws, cbws);
+  hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), dim3(kStateSplit<NT> * grid.x), block, 0, s, a, nch, ws, cbws);
   hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, dim3(kThrB), 0, s, a, nch,
                      static_cast<const float*>(ws), static_cast<const float*>(cbws));
   return hipGetLastError();
