@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Selective-scan forward benchmark on one MI355X.
 
-One step = one ss_scan_fwd call over the whole Mamba-130M-like layer (batch 8, 1536 channels,
-L 2048, N 16; bf16 u/delta/z/B/C, f32 A/D/delta_bias, softplus and silu gate on, y in f32),
-inputs resident in HBM.  Prints one JSON line:
+One step = one ss_scan_fwd call over a whole synthetic layer, inputs resident in HBM.  The
+default layer is the largest single-GPU configuration of the benchmark set, the long-sequence
+layer (batch 1, 1024 channels, L = 1,048,576, N 16; bf16 u/delta/z/B/C, f32 A/D/delta_bias,
+softplus and silu gate on, y in f32).  Prints one JSON line:
 
   value         elements (batch*channels*L) per second over the K timed steps
-  roofline      the scan kernel against the VALU (ALU) ceiling, and its HBM rate
-  cpu_baseline  the CPU oracle (float64, all host cores) on the same workload
+  roofline      the dominant kernel against the HBM roofline (8 TB/s): algorithmic bytes per
+                launch / the launch's average duration (HIP events on the launch stream); the
+                plain-ALU ceiling of the method's arithmetic is reported beside it
+  cpu_baseline  the CPU oracle (float64, all host cores) on a bounded sample of the same layer
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload 0-4] [--no-cpu-baseline]
+                       [--report FILE]   (also measure workloads 1-4 and write one JSON line each)
 """
 import argparse
 import json
@@ -27,31 +31,38 @@ METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 
 
 # MI355X published peaks
 HBM_PEAK_GBPS = 8000.0
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # 256 CU x 128 FP32 FMA lanes/clk x 2 FLOP x 2.4 GHz
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # packed FP32 vector peak (this build emits no packed FP32)
+MALL_BYTES = 256 * 2 ** 20       # Infinity Cache (last-level cache in front of HBM)
 
-# ALU work model, per element (one (b, d, t)), in FP32 FLOP-equivalents: an FMA is 2, a
-# multiply or add 1, and a transcendental (v_exp/v_log/v_rcp, which issues at a quarter of the
-# FMA rate on gfx950) 8, i.e. the four FMA issue slots it occupies.  The counts are the
-# method's own operations (the minimum any implementation performs), not the kernel's
-# instruction count: per (t, n) one exp, dt*A, (dt*u)*B, the state FMA and the readout FMA.
-TRANS = 8.0
+# Plain-ALU ceiling of the method's arithmetic (the competing bound of the diagonal path).
+# Unpacked VALU issue: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 3.93e13 lane-operations/s; a
+# transcendental (v_exp/v_log/v_rcp) takes TRANS_SLOTS issue slots of an FMA (quarter rate).
+VALU_LANE_OPS = 256 * 64 * 2.4e9
+TRANS_SLOTS = 4.0
 
 
-def flop_equiv_per_element(N, softplus, gate, scalar_decay, P=64):
-    if scalar_decay:
-        # per (t, p, n): dt*u*B multiply 1, state FMA 2, readout FMA 2; the decay exp is per head
-        per = 5.0 * N + (TRANS + 1.0) / P
+def alu_slots_per_element(p):
+    """Issue slots per element (one (b, d, t)) of the method's own operations, the minimum any
+    implementation performs: per (t, n) an exp and four FP32 operations (dt*A, (dt*u)*B, the
+    state FMA, the readout FMA); per element ~14 FP32 operations (bias, dt*u, D*u, the softplus
+    and gate arithmetic) and the softplus's two and the gate's two transcendentals.  Scalar
+    decay (one exp per head and step, shared by its P channels): per (t, p, n) the input
+    multiply, the state FMA and the readout FMA."""
+    if p.scalar_decay:
+        P = p.channels // p.heads
+        per = 3.0 * p.nstate + 8.0 + TRANS_SLOTS * (1.0 + (2.0 if p.softplus else 0.0)) / P
     else:
-        # per (t, n): exp 8, dt*A 1, (dt*u)*B 1, state FMA 2, readout FMA 2
-        per = 14.0 * N
-    per += 1.0 + 2.0  # dt*u, D*u FMA
-    if softplus:
-        per += 2 * TRANS + 4.0  # exp, log1p, bias add, max, adds
-    if gate:
-        per += 2 * TRANS + 3.0  # exp, reciprocal, add, two multiplies
+        per = p.nstate * (TRANS_SLOTS + 4.0) + 14.0 + TRANS_SLOTS * (2.0 if p.softplus else 0.0)
+    if p.gate:
+        per += 2 * TRANS_SLOTS
     return per
+
+
+# Backward ALU work in FP32 FLOP-equivalents (an FMA 2, a transcendental 8 = its four FMA slots),
+# reported against the packed FP32 peak (see backward_bench).
+TRANS = 8.0
 
 
 # source file of each scan kernel
@@ -362,9 +373,13 @@ def main():
     # The GPU's clock ramps up over the first tens of milliseconds of sustained work (workload 1:
     # 0.142 ms per launch over 100 back-to-back launches, 0.129 over 1000), so the defaults warm
     # up for ~25 ms and time ~0.13 s of steady state.
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--workload", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 30 on the 1M-step layer, 1000 on the others)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: 10 on the 1M-step layer, 200 on the others)")
+    ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--report", metavar="FILE", default=None,
+                    help="also measure workloads 1-4 (forward) and write one JSON line per workload to FILE")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-repeats", type=int, default=3)
     ap.add_argument("--decode", action="store_true",
@@ -400,6 +415,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    big = args.workload == 3
+    if args.steps is None:
+        args.steps = 30 if big else 1000
+    if args.warmup is None:
+        args.warmup = 10 if big else 200
     p = inputs.make(args.workload)
 
     def to_dev(a):
@@ -419,47 +439,108 @@ def main():
         conv_bench(args, p, to_dev, dev)
         return
 
+    out = forward_line(args, p, args.workload, to_dev, dev, steps=args.steps, warmup=args.warmup,
+                       cpu=not args.no_cpu_baseline)
+    if args.report:
+        # the per-workload report: every large workload measured the same way, one JSON line each
+        with open(args.report, "w") as f:
+            for k in (1, 2, 3, 4):
+                if k == args.workload:
+                    line = out
+                else:
+                    q = inputs.make(k)
+                    line = forward_line(args, q, k, to_dev, dev, steps=REPORT_STEPS[k], warmup=REPORT_WARMUP[k],
+                                        cpu=False)
+                    del q
+                f.write(json.dumps(line) + "\n")
+                f.flush()
+                print("report: workload %d %.3f ms per launch, HBM %.3f of peak" %
+                      (k, line["roofline"]["launch_ms"], line["roofline"]["frac"]), file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+
+
+# steps and warm-up launches of the per-workload report (about 0.2 s of timed work each)
+REPORT_STEPS = {1: 1000, 2: 400, 3: 20, 4: 600}
+REPORT_WARMUP = {1: 200, 2: 100, 3: 5, 4: 100}
+
+
+def forward_line(args, p, workload, to_dev, dev, *, steps, warmup, cpu):
+    """Measure one workload's forward and return its JSON record.
+
+    Timed region: `steps` back-to-back ss_scan_fwd calls (descriptors built once), bracketed by
+    device synchronisation, with HIP events on the launch stream around them: their span / steps
+    is the average launch duration used for the roofline.  Then the same number of launches each
+    between its own event pair (median and min per launch) and, when the layer's bytes fit the
+    256 MB Infinity Cache a few times over, launches each preceded by a 1 GiB write that evicts
+    it (cold median and min)."""
+    import torch
+
+    from selective_state_space_88_amd.scan import fwd_launcher
+
     t = {k: to_dev(getattr(p, k)) for k in ("u", "delta", "A", "B", "C", "D", "z", "delta_bias")}
     y = torch.empty(p.u.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     # one ss_scan_fwd call per step, its descriptors built once (the per-call marshalling of
-    # scan_fwd takes host time comparable to the kernel, which would leave the GPU idle between
-    # launches)
+    # scan_fwd takes host time comparable to a short kernel, which would leave the GPU idle
+    # between launches)
     step = fwd_launcher(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], y,
                         softplus=p.softplus, stream=stream.cuda_stream, zoh=args.zoh, trapezoid=args.trapezoid)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     copy_calibration(args, dev)
 
-    # timed region: K back-to-back steps, bracketed by device synchronisation; HIP events on the
-    # launch stream around the K launches give the kernel's average duration (the step is that
-    # one kernel)
-    K = args.steps
+    # timed region: K back-to-back steps
+    K = steps
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e_start.record(stream)
-    for i in range(K):
+    for _ in range(K):
         step()
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg_launch_s = e_start.elapsed_time(e_end) * 1e-3 / K
 
+    # per-launch events: median and min
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in ev])
+
+    nbytes = algorithmic_bytes(p, 4)
+    cold = None
+    if nbytes <= 4 * MALL_BYTES:
+        scratch = torch.empty(2 ** 28, dtype=torch.float32, device=dev)   # 1 GiB
+        R = max(10, min(50, K))
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+        for a, b in cev:
+            scratch.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        cper = np.array([a.elapsed_time(b) for a, b in cev])
+        cold = {"reps": R, "median_ms": float(np.median(cper)), "min_ms": float(np.min(cper)),
+                "eviction": "1 GiB written before each launch"}
+        del scratch
+
     E = p.batch * p.channels * p.length
     value = E * K / wall
-    nbytes = algorithmic_bytes(p, 4)
-    flops = E * flop_equiv_per_element(p.nstate, p.softplus, p.gate, p.scalar_decay,
-                                       P=p.channels // p.heads)
-    alu_tflops = flops / avg_launch_s / 1e12
     hbm_gbps = nbytes / avg_launch_s / 1e9
+    slots = alu_slots_per_element(p)
+    alu_floor_s = E * slots / VALU_LANE_OPS
     # the kernel that dominates the step (the diagonal path is that one kernel alone)
     kernel = scan_kernel(p)
-    traffic = stored_traffic(kernel, args.workload, kernel_source_digest(kernel))
+    traffic = stored_traffic(kernel, workload, kernel_source_digest(kernel))
+    copy_peak = stored_copy_peak()
 
     out = {
         "metric": METRIC,
@@ -467,7 +548,7 @@ def main():
         "unit": "elems/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": wall / K * 1e3,
         "higher_is_better": True,
         "scaling": "weak",
@@ -478,56 +559,54 @@ def main():
             "workload": describe(p) + (", zero-order hold" if args.zoh else "") +
                         (", exponential-trapezoidal" if args.trapezoid else ""),
             "batch": p.batch, "channels": p.channels, "seq_len": p.length, "nstate": p.nstate,
-            "heads": p.heads, "inputs": p.in_dtype, "y": "f32",
+            "heads": p.heads, "inputs": p.in_dtype, "y": "f32", "arithmetic": "f32",
             "kernel": kernel,
         },
         "roofline": {
-            "bound": "alu",
-            "achieved": alu_tflops,
-            "peak": FP32_VECTOR_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
+            "bound": "hbm",
+            "achieved": hbm_gbps,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": hbm_gbps / HBM_PEAK_GBPS,
             "traffic": traffic,
             "launch_ms": avg_launch_s * 1e3,
-            "flop_equiv_per_launch": flops,
+            "launch_ms_median": float(np.median(per)),
+            "launch_ms_min": float(np.min(per)),
+            "cold": cold if cold is not None else
+            "not needed: %.2f GB per launch against a %d MB cache" % (nbytes / 1e9, MALL_BYTES >> 20),
             "hbm_algorithmic_bytes_per_launch": nbytes,
-            "hbm_achieved_GBps": hbm_gbps,
-            "hbm_frac": hbm_gbps / HBM_PEAK_GBPS,
+            "frac_of_copy_peak": (hbm_gbps / copy_peak) if copy_peak else None,
+            "copy_peak_GBps": copy_peak,
+            "alu": {"slots_per_element": slots, "lane_ops_per_s": VALU_LANE_OPS,
+                    "floor_ms": alu_floor_s * 1e3, "frac": alu_floor_s / avg_launch_s},
         },
         "cpu_baseline": None,
     }
 
     if kernel == "ssd_scan_kernel":
-        # The matrix form is a dense contraction on v_mfma_f32_16x16x32_bf16 (16*16*32*2 flops
-        # each), so its roofline is the bf16 matrix peak.  Per (batch, head, 64-channel slab,
-        # 32-step chunk) each of 4 waves issues 4 for the masked product, Np/8 for the readout
-        # from the carried state and Np/8 for the state update (Np = N padded to a multiple of
-        # 32), counting the bf16 hi/lo split passes; the state pass that hands state between
-        # sequence segments is not counted.  The time is the whole call (pre-pass, state pass
-        # and output pass), so the rate is a lower bound for the output pass.  The ALU figures
-        # are kept beside it: the matrix form does less than the recurrence's own arithmetic.
+        # The matrix form is a chain of dense contractions on v_mfma_f32_16x16x32_bf16
+        # (16*16*32*2 flops each).  Per (batch, head, 64-channel slab, 32-step chunk) each of 4
+        # waves issues 4 for the masked product, Np/8 for the readout from the carried state and
+        # Np/8 for the state update (Np = N padded to a multiple of 32), counting the bf16 hi/lo
+        # split passes; the state pass that hands state between sequence segments is not counted.
+        # Its arithmetic intensity (flops per algorithmic byte) is below the ridge point of the
+        # bf16 matrix peak over HBM (2500 / 8 = 312), so HBM stays its roofline; the matrix-core
+        # rate is reported beside it.
         Np = (p.nstate + 31) // 32 * 32
         nch = (p.length + 31) // 32
         mf = p.batch * p.heads * (p.channels // p.heads // 64) * nch * 4 * (4 + Np // 4) * 16384.0
-        mf_tflops = mf / avg_launch_s / 1e12
-        rl = out["roofline"]
-        out["roofline"] = {
-            "bound": "mfma", "achieved": mf_tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": mf_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-            "launch_ms": rl["launch_ms"], "mfma_flops_per_launch": mf,
-            "alu_flop_equiv_per_launch": flops, "alu_equiv_TFLOPs": alu_tflops,
-            "alu_equiv_frac": alu_tflops / FP32_VECTOR_PEAK_TFLOPS,
-            "hbm_algorithmic_bytes_per_launch": nbytes, "hbm_achieved_GBps": hbm_gbps,
-            "hbm_frac": hbm_gbps / HBM_PEAK_GBPS,
-        }
+        out["roofline"]["mfma"] = {"flops_per_launch": mf, "achieved_TFLOPs": mf / avg_launch_s / 1e12,
+                                   "peak_TFLOPs": BF16_MFMA_PEAK_TFLOPS,
+                                   "frac": mf / avg_launch_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                                   "flops_per_byte": mf / nbytes}
 
-    if not args.no_cpu_baseline:
+    if cpu:
         import oracle
 
         cores = oracle.default_threads()
         # bounded sample: the whole workload when it is small, else a prefix of its rows
         total_rows = p.batch * p.channels
-        budget = 2.0e9  # state-steps (t, n) per repeat: a few seconds on a few dozen cores
+        budget = 6.0e9  # state-steps (t, n) per repeat: a few seconds on a few dozen cores
         nrows = int(min(total_rows, max(1, budget // (p.length * p.nstate))))
         rows = np.arange(nrows, dtype=np.int64) if nrows < total_rows else None
         best = None
@@ -546,7 +625,23 @@ def main():
                       % ("all" if rows is None else str(nrows), total_rows, p.length, p.nstate,
                          max(1, args.cpu_repeats), cores),
         }
-    print(json.dumps(out), flush=True)
+    return out
+
+
+def stored_copy_peak():
+    """The measured HBM copy rate (GB/s, bytes read + written) from the committed probe summary
+    profiles/probe_hbm_copy.txt, if present."""
+    path = os.path.join(ROOT, "profiles", "probe_hbm_copy.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("copy_GBps:"):
+                try:
+                    return float(line.split(":", 1)[1])
+                except ValueError:
+                    return None
+    return None
 
 
 if __name__ == "__main__":

@@ -64,15 +64,21 @@ typedef struct {
 /* flags */
 #define SS_DELTA_SOFTPLUS (1u << 0) /* dt = softplus(delta + delta_bias) */
 #define SS_Z_GATE_SILU (1u << 1)    /* y *= silu(z); requires z */
+/* a request for bitwise run-to-run reproducibility.  Every forward path (ss_scan_fwd,
+ * ss_scan_fwd_state, ss_scan_step) is deterministic by construction -- each output is one fixed
+ * chain of f32 operations, with no atomics and no order that depends on scheduling -- so there
+ * the flag changes nothing.  ss_scan_bwd sums over channels and batch with atomic adds and
+ * rejects it with SS_ERR_UNSUPPORTED. */
+#define SS_DETERMINISTIC (1u << 2)
 /* zero-order hold: the input enters as (exp(dt A) - 1) / A * B * u (dt * B * u at A = 0) instead
  * of the exponential-Euler dt * B * u -- the ZOH discretisation Bbar = (dt A)^-1 (exp(dt A) - I)
  * dt B of the omica.com.cn explainer, sections 3 and 5.  Forward and decoding step only. */
-#define SS_ZOH (1u << 2)
+#define SS_ZOH (1u << 3)
 /* exponential-trapezoidal rule: h_t = exp(dt_t A) h_{t-1} + (e_t + exp(dt_t A) e_{t-1}) / 2 with
  * e_t = Bbar_t u_t (the explainer's Mamba-3 recurrence, section 6.3).  The state passed in and
  * out (h_init, h_final, the decoding state) is h_t + e_t / 2 of the step before / the last step,
  * which carries the rule across call boundaries.  Forward and decoding step only. */
-#define SS_TRAPEZOID (1u << 3)
+#define SS_TRAPEZOID (1u << 4)
 
 /* return codes */
 #define SS_OK 0
@@ -97,7 +103,7 @@ typedef struct {
  *   z          [batch, channels, L]          same dtype as u; optional, required by SS_Z_GATE_SILU
  *                                            (a z of no elements may have data == NULL)
  *   delta_bias [heads] f32                   optional: no bias
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_DETERMINISTIC | SS_ZOH | SS_TRAPEZOID
  *   y          [batch, channels, L]          f32 | bf16, written; must not overlap any input
  *   stream     hipStream_t (as void*), NULL for the default stream
  *
@@ -105,8 +111,11 @@ typedef struct {
  * zero for every (b, d).  Internally the computation is in f32 (bf16 inputs are widened exactly);
  * y in bf16 is rounded to nearest even once.  Scalar-decay calls use a stream-ordered device
  * workspace (per-chunk operands of B and C, and the states handed between sequence segments;
- * O(batch * groups * L * N) bytes), allocated and freed on `stream` (SS_ERR_HIP if that
- * allocation fails).
+ * O(batch * groups * L * N) bytes), allocated and freed on `stream` from a memory pool that the
+ * library keeps on each device and never shrinks, so repeated calls reuse it without a device
+ * allocation (SS_ERR_HIP, with nothing enqueued, if the allocation fails; the environment
+ * variable SS_FAULT=alloc forces that failure for tests).  Diagonal-decay calls use no
+ * workspace.
  *
  * Returns SS_OK or a negative SS_ERR_* code.
  */
@@ -152,7 +161,7 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
  *   D          [channels] or [heads] f32     optional
  *   z          [batch, channels]             same dtype as u; optional, required by SS_Z_GATE_SILU
  *   delta_bias [heads] f32                   optional
- *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID
+ *   flags      SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_DETERMINISTIC | SS_ZOH | SS_TRAPEZOID
  *   h          [batch, channels, N] f32      read and updated in place (state index innermost)
  *   y          [batch, channels]             f32 | bf16, written
  *
@@ -168,7 +177,7 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * input, for training.  The pages train the scan by recomputing its states rather than storing
  * them (bqwf.cn state-space survey, section 2.2); so does this call: it stores only the state at
  * the start of every window of 512 steps (a stream-ordered workspace of batch * channels *
- * ceil(L / 512) * N floats) and recomputes the rest.  Chain rule, with s(z) = z sigmoid(z) and
+ * ceil(L / 512) * N floats, from the pool described at ss_scan_fwd) and recomputes the rest.  Chain rule, with s(z) = z sigmoid(z) and
  * dy0 = dy s(z):  g_t = C_t dy0_t + exp(dt_{t+1} A) g_{t+1} (the gradient of h_t),
  * dC_t = dy0_t h_t,  dB_t = g_t dt_t u_t,  du_t = dy0_t D + sum_n g_t dt_t B_t,
  * ddt_t = sum_n g_t (h_{t-1} exp(dt_t A) A + B_t u_t),  dA = sum_t g_t h_{t-1} exp(dt_t A) dt_t,
@@ -176,8 +185,9 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * dD = sum dy0_t u_t,  dz_t = dy_t y0_t s'(z_t)  (y0: the output before the gate).
  *
  *   u, delta, A, B, C, D, z, delta_bias, flags    as in ss_scan_fwd (diagonal A [channels, N] or
- *              scalar A [heads], delta per channel or per head), without SS_ZOH or SS_TRAPEZOID
- *              (SS_ERR_UNSUPPORTED), and channels / groups a multiple of 4 (SS_ERR_UNSUPPORTED)
+ *              scalar A [heads], delta per channel or per head), without SS_ZOH, SS_TRAPEZOID or
+ *              SS_DETERMINISTIC (SS_ERR_UNSUPPORTED: the summed gradients use atomic adds), and
+ *              channels / groups a multiple of 4 (SS_ERR_UNSUPPORTED)
  *   dy         [batch, channels, L]          f32 | bf16: the gradient of the loss at y
  *   du         [batch, channels, L] f32      written
  *   ddelta     [batch, heads, L] f32         written (the gradient of the raw delta; summed over

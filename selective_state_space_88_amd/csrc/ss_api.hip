@@ -2,11 +2,19 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
 
 #include "../../include/ss_scan.h"
 #include "ss_launch.h"
 
 namespace {
+
+// flag bits every scan entry point knows (SS_DETERMINISTIC is satisfied by construction on the
+// forward paths and rejected by the backward)
+constexpr uint32_t kScanFlags = SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_DETERMINISTIC | SS_ZOH | SS_TRAPEZOID;
 
 bool present(const ss_tensor* t) { return t != nullptr && t->data != nullptr; }
 
@@ -53,6 +61,48 @@ bool aligned16(const ss_tensor* t) {
   for (int i = 0; i + 1 < t->ndim; ++i)
     if (t->shape[i] > 1 && (t->stride[i] * es) % 16) return false;
   return true;
+}
+
+// Stream-ordered workspace from a memory pool the library owns on each device.  The pool keeps
+// freed blocks (its release threshold is "never"), so a call repeated on a stream reuses the
+// same memory without a device allocation.  SS_FAULT=alloc in the environment makes the
+// allocation fail, so that the failure path (SS_ERR_HIP, nothing enqueued, y untouched) can be
+// exercised.
+constexpr int kMaxDevices = 64;
+
+hipError_t ws_pool(hipMemPool_t* pool) {
+  static std::mutex mu;
+  static hipMemPool_t pools[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t p = nullptr;
+    if ((e = hipMemPoolCreate(&p, &props)) != hipSuccess) return e;
+    uint64_t keep = UINT64_MAX;
+    if ((e = hipMemPoolSetAttribute(p, hipMemPoolAttrReleaseThreshold, &keep)) != hipSuccess) {
+      (void)hipMemPoolDestroy(p);
+      return e;
+    }
+    pools[dev] = p;
+  }
+  *pool = pools[dev];
+  return hipSuccess;
+}
+
+hipError_t ws_alloc(void** ws, size_t bytes, hipStream_t s) {
+  const char* fault = getenv("SS_FAULT");
+  if (fault && strcmp(fault, "alloc") == 0) return hipErrorOutOfMemory;
+  hipMemPool_t pool;
+  hipError_t e = ws_pool(&pool);
+  if (e != hipSuccess) return e;
+  return hipMallocFromPoolAsync(ws, bytes, pool, s);
 }
 
 }  // namespace
@@ -108,7 +158,7 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
                 uint32_t flags, const ss_tensor* h_init, ss_tensor* h_final, ss_tensor* y, void* stream) {
   if (!u || !delta || !A || !B || !C || !y) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
+  if (flags & ~kScanFlags) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -148,7 +198,6 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (present(h_final) && (rc = check_state(h_final, Bt, Dc, N))) return rc;
   if (present(h_final) && overlaps(h_final, h_init)) return SS_ERR_ALIAS;
   if (Bt * Dc == 0) return SS_OK;  // nothing to compute
-  if (scalar && G > 1 && (Dc / G) % 64) return SS_ERR_UNSUPPORTED;
 
   // y must not overlap any input
   uintptr_t ylo, yhi;
@@ -233,7 +282,7 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   const bool mfma = ss::ssd_path(a);
   void* ws = nullptr;
   const int64_t wsb = mfma ? ss::ssd_workspace_bytes(a) : ss::scalar_workspace_floats(a) * (int64_t)sizeof(float);
-  if (hipMallocAsync(&ws, (size_t)wsb, s) != hipSuccess) {
+  if (ws_alloc(&ws, (size_t)wsb, s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
   }
@@ -263,7 +312,7 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
                  const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                  const ss_tensor* delta_bias, uint32_t flags, ss_tensor* h, ss_tensor* y, void* stream) {
   if (!u || !delta || !A || !B || !C || !h || !y) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
+  if (flags & ~kScanFlags) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -361,7 +410,7 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
                 ss_tensor* dB, ss_tensor* dC, ss_tensor* dD, ss_tensor* dz, ss_tensor* ddelta_bias,
                 void* stream) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SS_ERR_NULL;
-  if (flags & ~(uint32_t)(SS_DELTA_SOFTPLUS | SS_Z_GATE_SILU | SS_ZOH | SS_TRAPEZOID)) return SS_ERR_FLAGS;
+  if (flags & ~kScanFlags) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
   if (gate != given(z)) return SS_ERR_FLAGS;
   int rc;
@@ -389,8 +438,9 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (scalar ? A->shape[0] != H : (A->shape[0] != Dc || A->shape[1] != N)) return SS_ERR_SHAPE;
   if (present(D) && D->shape[0] != Dc && D->shape[0] != H) return SS_ERR_SHAPE;
   if (present(delta_bias) && delta_bias->shape[0] != H) return SS_ERR_SHAPE;
-  // the backward is written for the exponential-Euler rule
-  if (flags & (SS_ZOH | SS_TRAPEZOID)) return SS_ERR_UNSUPPORTED;
+  // the backward is written for the exponential-Euler rule, and its sums over channels and
+  // batch are atomic adds (not reproducible to the last bit)
+  if (flags & (SS_ZOH | SS_TRAPEZOID | SS_DETERMINISTIC)) return SS_ERR_UNSUPPORTED;
   if (N < 1 || N > 128) return SS_ERR_UNSUPPORTED;
   if (L > ((int64_t)1 << 31)) return SS_ERR_UNSUPPORTED;
   if (Dc > 0 && (Dc / G) % 4) return SS_ERR_UNSUPPORTED;
@@ -497,7 +547,7 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
 
   void* ws = nullptr;
   const int64_t wsb = ss::bwd_workspace_floats(a) * (int64_t)sizeof(float);
-  if (hipMallocAsync(&ws, (size_t)wsb, s) != hipSuccess) {
+  if (ws_alloc(&ws, (size_t)wsb, s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
   }

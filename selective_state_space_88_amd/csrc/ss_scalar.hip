@@ -25,7 +25,10 @@ constexpr int kMaxWaves = 8;
 int npad_of(int N) { return (N + kNT - 1) / kNT * kNT; }
 
 // The head-uniform path: every head's channels fill whole 64-lane waves.
-bool head_path(const ScanArgs& a) { return a.chan_per_head % 64 == 0 && a.channels % 64 == 0; }
+// (each block of 64 channels then lies in one head and one B/C group)
+bool head_path(const ScanArgs& a) {
+  return a.chan_per_head % 64 == 0 && a.chan_per_group % 64 == 0 && a.channels % 64 == 0;
+}
 
 // B, C [batch, groups, N, L] (strided, bf16/f32)  ->  ws [batch, groups, L, Npad] f32,
 // zero for n >= N.  One block transposes 64 steps x Npad states through LDS.
@@ -103,13 +106,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwaves = blockDim.x >> 6;
-  const int64_t cblocks = (p.channels + 63) / 64;
-  const int64_t b = blockIdx.x / cblocks;
-  const int64_t d0 = (blockIdx.x % cblocks) * 64;
+  // a block holds up to 64 channels of one (batch, B/C group)
+  const int64_t cpg = p.chan_per_group;
+  const int64_t cblocks = (cpg + 63) / 64;
+  const int64_t bg = blockIdx.x / cblocks;
+  const int64_t b = bg / p.groups, g = bg % p.groups;
+  const int64_t d0 = g * cpg + (blockIdx.x % cblocks) * 64;
+  const int64_t dend = (g + 1) * cpg;  // the group's last channel + 1
   const int64_t L = p.L;
-  const int64_t dl_ = d0 + lane < p.channels ? d0 + lane : p.channels - 1;  // clamp idle lanes
+  const int64_t dl_ = d0 + lane < dend ? d0 + lane : dend - 1;  // clamp idle lanes
   const int64_t hd = dl_ / p.chan_per_head;
-  const int64_t g = d0 / p.chan_per_group;  // uniform: checked on the host
 
   const TIn* __restrict__ u = static_cast<const TIn*>(p.u) + b * p.u_sb + dl_ * p.u_sd;
   const TIn* __restrict__ dlr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
     for (int idx = threadIdx.x; idx < 64 * kT; idx += blockDim.x) {
       const int c = idx / kT, j = idx % kT;
       const int64_t d = d0 + c, t = tb + j;
-      if (d < p.channels && t < L) {
+      if (d < dend && t < L) {
         float s = 0.f;
         for (int w = 0; w < nwaves; ++w) s += part[w][c][j];
         const int64_t hdc = d / p.chan_per_head;
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void scalar_fwd_kernel(ScanArgs p,
     __syncthreads();
   }
   // the state after the last step (steps past L are the identity)
-  if (p.h_final && d0 + lane < p.channels) {
+  if (p.h_final && d0 + lane < dend) {
     float* hf = p.h_final + b * p.hf_sb + (d0 + lane) * p.hf_sd;
 #pragma unroll
     for (int i = 0; i < kNT; ++i)
@@ -406,7 +412,7 @@ hipError_t launch_t(const ScanArgs& a, float* ws, hipStream_t s) {
   if (e != hipSuccess) return e;
   e = transpose<TIn>(a, a.C, a.C_sb, a.C_sg, a.C_sn, ws + plane, s);
   if (e != hipSuccess) return e;
-  const int64_t blocks = a.batch * ((a.channels + 63) / 64);
+  const int64_t blocks = a.batch * a.groups * ((a.chan_per_group + 63) / 64);
   const dim3 block(64 * (Npad / kNT));
   if (a.z)
     hipLaunchKernelGGL((scalar_fwd_kernel<TIn, TOut, true>), dim3((unsigned)blocks), block, 0, s, a,

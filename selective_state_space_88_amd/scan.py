@@ -18,8 +18,9 @@ LIB_PATH = os.path.join(HERE, "libssscan.so")
 SS_F32, SS_BF16 = 0, 1
 SS_DELTA_SOFTPLUS = 1 << 0
 SS_Z_GATE_SILU = 1 << 1
-SS_ZOH = 1 << 2
-SS_TRAPEZOID = 1 << 3
+SS_DETERMINISTIC = 1 << 2   # forward paths are deterministic by construction; the backward rejects it
+SS_ZOH = 1 << 3
+SS_TRAPEZOID = 1 << 4
 SS_CONV_SILU = 1 << 0   # flag of ss_conv1d
 EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_conv1d", "ss_check",
            "ss_strerror", "ss_version")
@@ -70,6 +71,11 @@ def lib() -> ctypes.CDLL:
 
 def strerror(code: int) -> str:
     return lib().ss_strerror(code).decode()
+
+
+def check(stream: Optional[int] = None) -> int:
+    """ss_check: synchronise ``stream`` and return SS_OK (0) or SS_ERR_HIP if enqueued work failed."""
+    return lib().ss_check(ctypes.c_void_p(stream or 0))
 
 
 def version() -> int:
@@ -135,7 +141,7 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
              y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
              stream: Optional[int] = None, h_init: Optional[torch.Tensor] = None,
              h_final: Optional[torch.Tensor] = None, zoh: bool = False,
-             trapezoid: bool = False) -> torch.Tensor:
+             trapezoid: bool = False, deterministic: bool = False) -> torch.Tensor:
     """Selective-scan forward on the GPU through ss_scan_fwd (see include/ss_scan.h).
 
     u, z: [batch, channels, L]; delta: [batch, heads, L]; A: [channels, N] (diagonal) or
@@ -144,13 +150,14 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
     With h_init and/or h_final ([batch, channels, N] float32) the call goes through
     ss_scan_fwd_state: the scan starts from h_init and writes its final state to h_final.
     ``zoh`` selects the zero-order-hold input coefficient (SS_ZOH), ``trapezoid`` the
-    exponential-trapezoidal rule (SS_TRAPEZOID).
+    exponential-trapezoidal rule (SS_TRAPEZOID); ``deterministic`` passes SS_DETERMINISTIC (the
+    forward is bitwise reproducible either way).
     """
     _check_cuda(u, delta, A, B, C, D, z, delta_bias, h_init, h_final)
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
-        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0) | (SS_DETERMINISTIC if deterministic else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     args = (describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
@@ -197,7 +204,8 @@ def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
               C: torch.Tensor, D: Optional[torch.Tensor], z: Optional[torch.Tensor],
               delta_bias: Optional[torch.Tensor], h: torch.Tensor, *, softplus: bool = True,
               y: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
-              stream: Optional[int] = None, zoh: bool = False, trapezoid: bool = False) -> torch.Tensor:
+              stream: Optional[int] = None, zoh: bool = False, trapezoid: bool = False,
+              deterministic: bool = False) -> torch.Tensor:
     """One decoding step through ss_scan_step: h (float32 [batch, channels, N]) is updated in
     place and y [batch, channels] returned.  u, z: [batch, channels]; delta: [batch, heads];
     B, C: [batch, groups, N]; A, D, delta_bias as in scan_fwd."""
@@ -205,7 +213,7 @@ def scan_step(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Te
     if y is None:
         y = torch.empty(u.shape, dtype=out_dtype, device=u.device)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
-        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0) | (SS_DETERMINISTIC if deterministic else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     rc = call_step(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
@@ -225,15 +233,17 @@ def call_bwd(u, delta, A, B, C, D, z, delta_bias, flags: int, dy, du, ddelta, dA
 
 def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
              D: Optional[torch.Tensor], z: Optional[torch.Tensor], delta_bias: Optional[torch.Tensor],
-             dy: torch.Tensor, *, softplus: bool = True, stream: Optional[int] = None) -> dict:
-    """Gradients of sum(dy * y) through ss_scan_bwd (diagonal decay, delta per channel).  Returns
-    a dict of float32 tensors du, ddelta, dA, dB, dC and, when the input is given, dD, dz,
-    ddelta_bias."""
+             dy: torch.Tensor, *, softplus: bool = True, stream: Optional[int] = None,
+             deterministic: bool = False) -> dict:
+    """Gradients of sum(dy * y) through ss_scan_bwd.  Returns a dict of float32 tensors du, ddelta,
+    dA, dB, dC and, when the input is given, dD, dz, ddelta_bias.  ``deterministic`` passes
+    SS_DETERMINISTIC, which the backward rejects (its summed gradients use atomic adds)."""
     _check_cuda(u, delta, A, B, C, D, z, delta_bias, dy)
     f = lambda t: torch.empty(t.shape, dtype=torch.float32, device=u.device)
     g = dict(du=f(u), ddelta=f(delta), dA=f(A), dB=f(B), dC=f(C), dD=None if D is None else f(D),
              dz=None if z is None else f(z), ddelta_bias=None if delta_bias is None else f(delta_bias))
-    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0)
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
+        (SS_DETERMINISTIC if deterministic else 0)
     if stream is None:
         stream = torch.cuda.current_stream(u.device).cuda_stream
     rc = call_bwd(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D), describe(z),

@@ -177,9 +177,33 @@ def test_unsupported_state_size():
     assert call(p) == -6
 
 
-def test_scalar_decay_groups_must_align_with_waves():
-    p = problem(Dc=64, H=8, G=2, scalar=True)
-    assert call(p) == -6
+def test_flag_bits_match_the_header():
+    text = open(HEADER).read()
+    bits = dict(re.findall(r"#define (SS_\w+) \(1u << (\d+)\)", text))
+    for name in ("SS_DELTA_SOFTPLUS", "SS_Z_GATE_SILU", "SS_DETERMINISTIC", "SS_ZOH", "SS_TRAPEZOID"):
+        assert getattr(scan, name) == 1 << int(bits[name]), name
+    # the planned ABI's bit 2 is the determinism request, not a discretisation
+    assert scan.SS_DETERMINISTIC == 1 << 2
+    assert len({scan.SS_DELTA_SOFTPLUS, scan.SS_Z_GATE_SILU, scan.SS_DETERMINISTIC, scan.SS_ZOH,
+                scan.SS_TRAPEZOID}) == 5
+
+
+def test_deterministic_flag_is_accepted_by_the_forward_paths():
+    # empty problems pass validation and enqueue nothing: the flag is known to every forward
+    for kw in (dict(L=0), dict(Bt=0)):
+        p = problem(**kw)
+        p["flags"] |= scan.SS_DETERMINISTIC
+        assert call(p) == 0, kw
+    p = step_problem(Bt=0)
+    p["flags"] |= scan.SS_DETERMINISTIC
+    assert call_step(p) == 0
+
+
+def test_scalar_decay_groups_need_not_align_with_waves():
+    # two B/C groups of 32 channels: valid (a block of the sequential kernel stays in one group);
+    # checked here on an empty batch, and on the GPU in the parity tests
+    p = problem(Bt=0, Dc=64, H=8, G=2, scalar=True)
+    assert call(p) == 0
 
 
 def test_alias_rejected():
@@ -491,6 +515,9 @@ def test_bwd_unsupported_and_errors():
     p = bwd_problem()
     p["flags"] |= scan.SS_TRAPEZOID
     assert call_bwd(p) == -6
+    p = bwd_problem()
+    p["flags"] |= scan.SS_DETERMINISTIC                # its sums are atomic adds
+    assert call_bwd(p) == -6
     assert call_bwd(bwd_problem(Dc=6)) == -6          # channels per group not a multiple of 4
     assert call_bwd(bwd_problem(N=129)) == -6
     p = bwd_problem()
@@ -508,3 +535,11 @@ def test_bwd_unsupported_and_errors():
     p = bwd_problem()
     p["dB"].data = p["du"].data + 8                     # two gradients overlapping
     assert call_bwd(p) == -7
+
+
+def test_check_reports_the_device_state():
+    # ss_check synchronises the stream: SS_OK with a GPU (nothing failed), SS_ERR_HIP without one
+    import torch
+
+    rc = scan.check(None)
+    assert rc == (0 if torch.cuda.is_available() else -8)

@@ -9,7 +9,9 @@ no loop structure with the recurrence, and invariants of the recurrence:
   P2  constant Delta, B, C (time-invariant): each state is a first-order IIR filter
       (scipy.signal.lfilter); the impulse response is C . exp(Delta A)^t Delta B.
   P3  tiny sizes: the materialised state and output from the pairwise decay form
-      h_t = sum_{s<=t} exp(A (S_t - S_s)) Delta_s B_s u_s with S the running sum of Delta.
+      h_t = sum_{s<=t} exp(A (S_t - S_s)) Delta_s B_s u_s with S the running sum of Delta;
+      also with a diagonal A and Delta per head (heads < channels), where the layout equals
+      the per-channel one with Delta repeated over the head's channels (and P1 with heads).
   P4  L = 1 closed form.
   P5  decay underflow (Delta*A << 0): memoryless output.
   P6  linearity in u; P7 causality; P8 channel-permutation equivariance;
@@ -173,6 +175,41 @@ def test_p3_matches_materialised_pairwise_form(G, softplus):
     yref, h = pairwise_reference(p)
     assert normwise(y, yref) < 1e-12
     assert normwise(hf.reshape(2, 4, 3), h[..., -1]) < 1e-12
+
+
+def test_p3_diagonal_A_with_step_sizes_per_head():
+    """Diagonal A [channels, N] with delta (and its bias) shared by each head's channels (heads <
+    channels): the materialised pairwise form, and the per-channel layout with delta repeated
+    over the head's channels."""
+    rng = np.random.default_rng(15)
+    Hh, P, N = 3, 4, 5
+    p = rand_problem(rng, Bt=2, Dc=Hh * P, H=Hh, L=37, N=N, G=1, with_z=True)
+    assert p["A"].shape == (Hh * P, N)
+    y, hf = run(p, return_state=True)
+    yref, h = pairwise_reference(p)
+    assert normwise(y, yref) < 1e-12
+    assert normwise(hf.reshape(2, Hh * P, N), h[..., -1]) < 1e-12
+    head = np.arange(Hh * P) // P
+    q = dict(p, delta=p["delta"][:, head], delta_bias=p["delta_bias"][head])
+    assert normwise(y, run(q)) < 1e-15
+
+
+def test_p1_zero_A_with_step_sizes_per_head():
+    """A = 0 with delta per head: each channel's state is the prefix sum of its head's
+    dt * B * u (numpy.cumsum), two B/C groups."""
+    rng = np.random.default_rng(16)
+    Hh, P, G = 2, 3, 2
+    p = rand_problem(rng, Bt=2, Dc=Hh * P, H=Hh, L=41, N=4, G=G)
+    p["A"] = np.zeros_like(p["A"])
+    y = run(p)
+    dt = step_sizes(p)  # [Bt, H, L]
+    Dc = Hh * P
+    ref = np.empty_like(y)
+    for d in range(Dc):
+        hd, g = d // P, d // (Dc // G)
+        h = np.cumsum(dt[:, hd, None, :] * p["B"][:, g] * p["u"][:, d, None, :], axis=-1)  # [Bt, N, L]
+        ref[:, d] = np.sum(p["C"][:, g] * h, axis=1) + p["D"][d] * p["u"][:, d]
+    assert normwise(y, ref) < 1e-12
 
 
 def test_p3_row_selection_and_initial_state_zero():

@@ -1,9 +1,20 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle, on the GPU.
 
-Metric: normwise relative error max|y - y_ref| / max|y_ref| over the compared outputs, with
-y written in f32.  Bars: 1e-5 for f32 inputs, 2e-3 for bf16 inputs (both sides consume the
-same bf16 bits, so the error is f32-vs-f64 arithmetic only).  y written in bf16 is checked
-against |y - y_ref| <= 2^-8 |y_ref| + 2e-3 max|y_ref| (one rounding to bf16 on top).
+Gate: normwise relative error max|y - y_ref| / max|y_ref| over the compared outputs, with y
+written in f32.  Bars (rtol): 1e-5 for f32 inputs, 2e-3 for bf16 inputs (both sides consume the
+same bf16 bits, so the error is f32-vs-f64 arithmetic only).  Also asserted for every case:
+  - the same metric for each (batch, channel) row on its own (the worst row is reported);
+  - elementwise |y - y_ref| <= rtol |y_ref| + atol, atol = max(1e-6, 1e-2 rtol) max|y_ref|.  The
+    absolute term covers outputs near zero, where y is a difference of larger terms (C.h + D u,
+    or silu(z) -> 0): there f32 rounding alone is ~1e-7 of the scale (a float32 evaluation of the
+    recurrence in numpy measures 0.7e-7 to 1.3e-7 normwise on these workloads), and the scalar-
+    decay matrix form, whose products split f32 operands into two bf16 parts (relative error
+    ~2^-17 each), ~5e-6; 1e-6 (f32 inputs) and 2e-5 (bf16 inputs) leave margins of ~8 and ~4.
+Reported only: the elementwise relative error over outputs with |y_ref| >= 1e-2 rms(y_ref); with
+f32 inputs that exceeds 1e-5 even for an exact float32 evaluation (5e-6 to 5e-5 measured), so it
+is a diagnostic, not a gate.
+y written in bf16 is checked against |y - y_ref| <= 2^-8 |y_ref| + 2e-3 max|y_ref| (one rounding
+to bf16 on top).
 """
 import dataclasses
 
@@ -27,14 +38,40 @@ def check(p, label, rows=None, out_dtype=None):
     y = run_hip(p, out_dtype=out_dtype)
     if rows is None:
         ref = oracle.scan_problem(p)
-        err = normwise(y, ref)
+        got = y
     else:
         ref = oracle.scan_problem(p, rows=rows)
-        err = normwise(y.reshape(-1, p.length)[rows], ref)
-    say("[parity] %s: normwise error %.3e (bar %.0e)" % (label, err, TOL[p.in_dtype]))
+        got = y.reshape(-1, p.length)[rows]
+    rtol = TOL[p.in_dtype]
+    err = normwise(got, ref)
+    d = diagnostics(got, ref, p.length, rtol)
+    say("[parity] %s: normwise error %.3e (bar %.0e); worst row %.3e; elementwise excess %.3e; "
+        "elementwise relative (|ref| >= 1e-2 rms) %.3e" % (label, err, rtol, d["worst_row"], d["excess"], d["floored"]))
     assert np.all(np.isfinite(y))
-    assert err <= TOL[p.in_dtype], (label, err)
+    assert err <= rtol, (label, err)
+    assert d["worst_row"] <= rtol, (label, d["worst_row"])
+    assert d["excess"] <= 0, (label, d["excess"])
     return y, ref
+
+
+def diagnostics(got, ref, L, rtol):
+    """Per-row normwise error (worst row), the excess of |y - ref| over rtol |ref| + atol with
+    atol = max(1e-6, 1e-2 rtol) max|ref| (<= 0 passes), and the elementwise relative error over
+    |ref| >= 1e-2 rms(ref)."""
+    g = np.asarray(got, dtype=np.float64).reshape(-1, max(L, 1))
+    r = np.asarray(ref, dtype=np.float64).reshape(-1, max(L, 1))
+    if r.size == 0:
+        return dict(worst_row=0.0, excess=0.0, floored=0.0)
+    diff = np.abs(g - r)
+    rmax = np.max(np.abs(r), axis=1)
+    dmax = np.max(diff, axis=1)
+    worst = float(np.max(np.where(rmax > 0, dmax / np.where(rmax > 0, rmax, 1.0), dmax)))
+    scale = float(np.max(np.abs(r)))
+    excess = float(np.max(diff - (rtol * np.abs(r) + max(1e-6, 1e-2 * rtol) * scale)))
+    rms = float(np.sqrt(np.mean(r * r)))
+    m = np.abs(r) >= 1e-2 * rms
+    floored = float(np.max(diff[m] / np.abs(r[m]))) if np.any(m) else 0.0
+    return dict(worst_row=worst, excess=excess, floored=floored)
 
 
 def test_tiny_fp32_workload():
