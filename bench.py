@@ -367,6 +367,101 @@ def conv_bench(args, p, to_dev, dev):
     print(json.dumps(out_line))
 
 
+PROBE_KINDS = {0: "v_mul_f32", 1: "v_fma_f32", 2: "v_exp_f32", 3: "v_mul_f32_dpp",
+               4: "v_exp_f32 + v_fma_f32 alternating", 5: "one v_exp_f32 in four (three v_fma_f32)"}
+
+
+def probe_bench(args, dev):
+    """Ceiling probes (libssprobe.so, include/ss_probe.h): cycles per wave64 instruction per SIMD
+    for the instruction kinds the diagonal scan is made of, at 1 to 8 waves per SIMD, and the HBM
+    rates of a streaming copy and a streaming read of 1 GiB.  Prints one JSON line; with
+    --probe-out DIR also writes the text summaries DIR/probe_valu.txt and DIR/probe_hbm_copy.txt."""
+    import ctypes
+
+    import torch
+
+    path = os.path.join(ROOT, "selective_state_space_88_amd", "libssprobe.so")
+    if not os.path.exists(path):
+        print("libssprobe.so is not built (run selective_state_space_88_amd/build.py)", file=sys.stderr)
+        sys.exit(1)
+    lib = ctypes.CDLL(path)
+    lib.ssp_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_void_p]
+    lib.ssp_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.ssp_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    stream = torch.cuda.current_stream(dev)
+    sid = stream.cuda_stream
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    iters = 4000
+    valu = {}
+    clocks = []
+    for kind, name in PROBE_KINDS.items():
+        for w in (1, 2, 3, 4, 8):
+            blocks = cus * w   # 4 waves per block: w waves per SIMD
+            out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+            clk = torch.zeros(2, dtype=torch.int64, device=dev)
+            run = lambda: lib.ssp_valu(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                                       ctypes.c_void_p(clk.data_ptr()), ctypes.c_void_p(sid))
+            assert run() == 0
+            sec = timed(run, 5)
+            c = clk.cpu().tolist()
+            hz = c[0] / c[1] * 1e8 if c[1] else 0.0
+            clocks.append(hz)
+            per_simd = w * iters * 32     # instructions issued by each SIMD
+            valu.setdefault(name, {})[w] = {"ns_per_instr": sec * 1e9 / per_simd,
+                                            "cycles_per_instr": sec * hz / per_simd, "clock_GHz": hz / 1e9}
+            del out, clk
+    # HBM: 1 GiB streams, 8 blocks of 256 threads per CU (grid-stride)
+    n16 = (1 << 30) // 16
+    src = torch.ones(n16 * 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    blocks = cus * 8
+    red = torch.empty(blocks * 256, dtype=torch.int32, device=dev)
+    t_copy = timed(lambda: lib.ssp_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                        n16, blocks, ctypes.c_void_p(sid)), 20)
+    t_read = timed(lambda: lib.ssp_read(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(red.data_ptr()),
+                                        n16, blocks, ctypes.c_void_p(sid)), 20)
+    copy_gbps = 2 * n16 * 16 / t_copy / 1e9
+    read_gbps = n16 * 16 / t_read / 1e9
+    out = {"metric": "ceiling probes", "device": props.name, "compute_units": cus,
+           "clock_GHz_median": float(np.median(clocks)) / 1e9, "valu": valu,
+           "hbm": {"copy_GBps": copy_gbps, "read_GBps": read_gbps, "bytes_per_copy": 2 * n16 * 16,
+                   "frac_of_8TBps_copy": copy_gbps / HBM_PEAK_GBPS, "frac_of_8TBps_read": read_gbps / HBM_PEAK_GBPS}}
+    print(json.dumps(out), flush=True)
+    if args.probe_out:
+        cmd = "python3 bench.py --probe --probe-out profiles"
+        with open(os.path.join(args.probe_out, "probe_valu.txt"), "w") as f:
+            f.write("# VALU issue probes on %s (%d CUs), libssprobe.so (include/ss_probe.h)\n" % (props.name, cus))
+            f.write("# command (from the repository root): %s\n" % cmd)
+            f.write("# cycles per wave64 instruction per SIMD (independent instructions, no dependency "
+                    "stalls), at 1-8 waves per SIMD;\n# clock from s_memtime / s_memrealtime in the run\n")
+            f.write("%-40s %s\n" % ("instruction", "  ".join("w=%d" % w for w in (1, 2, 3, 4, 8))))
+            for name, row in valu.items():
+                f.write("%-40s %s\n" % (name, "  ".join("%5.2f" % row[w]["cycles_per_instr"] for w in (1, 2, 3, 4, 8))))
+            f.write("clock_GHz_median: %.3f\n" % (float(np.median(clocks)) / 1e9))
+        with open(os.path.join(args.probe_out, "probe_hbm_copy.txt"), "w") as f:
+            f.write("# HBM streaming probes on %s, libssprobe.so: 1 GiB, 16-byte nontemporal accesses, "
+                    "%d blocks of 256 threads\n" % (props.name, blocks))
+            f.write("# command (from the repository root): %s\n" % cmd)
+            f.write("copy_GBps: %.1f\n" % copy_gbps)
+            f.write("read_GBps: %.1f\n" % read_gbps)
+            f.write("copy_frac_of_8000: %.3f\n" % (copy_gbps / HBM_PEAK_GBPS))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +491,10 @@ def main():
                     help="time the causal depthwise convolution in front of the scan (ss_conv1d, silu) "
                          "on the workload's scan input instead of the scan")
     ap.add_argument("--conv-width", type=int, default=4, help="taps of --conv (1..8)")
+    ap.add_argument("--probe", action="store_true",
+                    help="run the ceiling probes (VALU issue costs, HBM copy and read rates) instead of the scan")
+    ap.add_argument("--probe-out", metavar="DIR", default=None,
+                    help="with --probe: write the summaries probe_valu.txt and probe_hbm_copy.txt into DIR")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="also run a plain device copy of MB megabytes (10^6 B) per step, so that "
                          "HBM byte counters can be scaled against a kernel of known traffic")
@@ -415,6 +514,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.probe:
+        probe_bench(args, dev)
+        return
     big = args.workload == 3
     if args.steps is None:
         args.steps = 30 if big else 1000

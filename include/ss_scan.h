@@ -90,6 +90,11 @@ typedef struct {
 #define SS_ERR_UNSUPPORTED (-6) /* valid but unsupported size (N > 128, > 2^31 steps per row, conv width > 8) */
 #define SS_ERR_ALIAS (-7)       /* an output (y, a final state) overlaps an input or another output */
 #define SS_ERR_HIP (-8)         /* a HIP runtime call failed (launch, workspace allocation) */
+/* reported by ss_check only: inside a kernel, a wave's bounded wait for another wave of its
+ * block ran out of polls (never expected; the environment variable SS_SPIN_LIMIT lowers the
+ * bound for tests).  The wave went on instead of hanging, so the results of the calls since the
+ * previous ss_check are wrong. */
+#define SS_ERR_DEADLOCK (-9)
 
 /*
  * ss_scan_fwd -- selective-scan forward, y = S6(u, delta, A, B, C, D, z, delta_bias).
@@ -252,7 +257,9 @@ int ss_scan_bwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
 int ss_conv1d(const ss_tensor* x, const ss_tensor* weight, const ss_tensor* bias, const ss_tensor* state_in,
               ss_tensor* state_out, uint32_t flags, ss_tensor* out, void* stream);
 
-/* Synchronises `stream` and returns SS_OK, or SS_ERR_HIP if any enqueued work failed. */
+/* Synchronises `stream` and returns SS_OK, SS_ERR_HIP if any enqueued work failed, or
+ * SS_ERR_DEADLOCK if a kernel's bounded wait ran out since the previous check (on the current
+ * device; the record is cleared). */
 int ss_check(void* stream);
 
 /* Static, NUL-terminated description of a return code (never NULL). */

@@ -11,6 +11,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssscan.so")
 SOURCES = ["ss_api.hip", "ss_diag.hip", "ss_scalar.hip", "ss_ssd.hip", "ss_step.hip", "ss_bwd.hip",
            "ss_ssd_bwd.hip", "ss_conv.hip"]
+# the ceiling probes (include/ss_probe.h): a measurement library of its own
+PROBE_LIB = os.path.join(HERE, "libssprobe.so")
+PROBE_SOURCES = ["ss_probe.hip"]
 ARCH = "gfx950"
 
 FLAGS = [
@@ -32,10 +35,15 @@ def hipcc() -> str:
 
 def build(verbose: bool = False) -> str:
     """Compile every HIP source for gfx950 (one hipcc per file, in parallel) and link them into
-    selective_state_space_88_amd/libssscan.so."""
+    selective_state_space_88_amd/libssscan.so, and the probes into libssprobe.so."""
+    _link(SOURCES + PROBE_SOURCES, {LIB: SOURCES, PROBE_LIB: PROBE_SOURCES}, verbose)
+    return LIB
+
+
+def _link(sources, libs, verbose):
     tag = "%d" % os.getpid()
     objs, procs = [], []
-    for src in SOURCES:
+    for src in sources:
         obj = os.path.join(CSRC, src.replace(".hip", ".%s.o" % tag))
         cmd = [hipcc()] + [f for f in FLAGS if f != "-shared"] + ["-c", "-o", obj, os.path.join(CSRC, src)]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
@@ -51,17 +59,18 @@ def build(verbose: bool = False) -> str:
     try:
         if errors:
             raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
-        tmp = LIB + ".tmp" + tag
-        cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-        os.replace(tmp, LIB)
+        obj_of = dict(zip(sources, objs))
+        for lib, srcs in libs.items():
+            tmp = lib + ".tmp" + tag
+            cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + [obj_of[x] for x in srcs]
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+            os.replace(tmp, lib)
     finally:
         for o in objs:
             if os.path.exists(o):
                 os.remove(o)
-    return LIB
 
 
 if __name__ == "__main__":

@@ -123,6 +123,8 @@ const char* ss_strerror(int code) {
       return "unsupported size (N must be 1..128; at most 2^31 steps per row; conv width 1..8)";
     case SS_ERR_ALIAS: return "an output (y, a final state) overlaps an input or another output";
     case SS_ERR_HIP: return "HIP runtime error";
+    case SS_ERR_DEADLOCK:
+      return "a bounded wait between the waves of a kernel ran out: results since the last check are wrong";
     default: return "unknown error code";
   }
 }
@@ -130,7 +132,9 @@ const char* ss_strerror(int code) {
 int ss_check(void* stream) {
   if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return SS_ERR_HIP;
   if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
-  return SS_OK;
+  int failed = 0;
+  if (ss::take_spin_error(&failed) != hipSuccess) return SS_ERR_HIP;
+  return failed ? SS_ERR_DEADLOCK : SS_OK;
 }
 
 }  // extern "C"

@@ -36,6 +36,8 @@
 //    memory operations, loads and stores alike, in issue order), never for what it issued after;
 //  - softplus, D*u and the silu gate are fused; u, delta, z and y stream through HBM once, y
 //    leaving through LDS so that every store instruction writes whole rows of consecutive y.
+#include <stdlib.h>
+
 #include <algorithm>
 
 #include "ss_device.h"
@@ -206,6 +208,31 @@ __device__ __forceinline__ float row_incoming_state1(float a, float bb, float ca
 #undef SS_LOADC1
 #undef SS_END1
 #undef SS_SCAN16_1
+#undef SS_STEP1
+  return hs;
+}
+
+// The same for a 64-lane row with nothing read alongside: this lane's incoming state, from the
+// lane aggregate (a, bb) and the row's carried state.
+__device__ __forceinline__ float row_incoming_state(float a, float bb, float carry) {
+  float he, hs;
+#define SS_STEP1(CTRL)                                  \
+  "v_fmac_f32_dpp %1, %1, %0 " CTRL "\n"               \
+  "v_mul_f32_dpp %0, %0, %0 " CTRL "\n"                \
+  "s_nop 0\n"
+  asm volatile("s_nop 1\n"
+               SS_STEP1("row_shr:1 row_mask:0xf bank_mask:0xf")
+               SS_STEP1("row_shr:2 row_mask:0xf bank_mask:0xf")
+               SS_STEP1("row_shr:4 row_mask:0xf bank_mask:0xf")
+               SS_STEP1("row_shr:8 row_mask:0xf bank_mask:0xf")
+               SS_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf")
+               SS_STEP1("row_bcast:31 row_mask:0xc bank_mask:0xf")
+               "v_fma_f32 %2, %0, %4, %1\n"
+               "v_mov_b32 %3, %4\n"
+               "s_nop 0\n"
+               "v_mov_b32_dpp %3, %2 wave_shr:1 row_mask:0xf bank_mask:0xf\n"
+               : "+v"(a), "+v"(bb), "=&v"(he), "=&v"(hs)
+               : "v"(carry));
 #undef SS_STEP1
   return hs;
 }
@@ -914,6 +941,481 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Few rows, long sequences: several windows of a channel in flight ("window slots").
+//
+// When the (batch, channel) rows fit one round of one wave per SIMD (batch x channels <= 4 x CU
+// count, e.g. the 1024 rows of a layer of a million steps), the kernel above gives each row one
+// wave, which walks its windows in order: one wave per SIMD, and a wave on its own issues at
+// best one instruction every few clocks.  Here each channel gets kSlots waves.  Slot k takes
+// windows k, k + kSlots, k + 2 kSlots, ..., one state per step; the state at the end of window w
+// (state n) is the carried state of window w + 1 (state n), which belongs to the next slot.  The
+// slots therefore run skewed: slot k handles state n of its r-th window at step r N + n + k D
+// (the skew D with 1 <= D <= (N - 1) / 2), so the carried state it reads was written D steps
+// earlier by slot k - 1 (for slot 0: N - 2 D steps earlier, by the last slot in the round
+// before).  One LDS word per (channel, state) holds it, and each wave publishes the steps it has
+// completed: a wave waits only for the wave that writes the carried state it reads, which is
+// normally D steps ahead.  Every write of a word is read by the next slot before the following
+// write (each writer has itself waited, through the chain of slots, for the reader of the
+// previous value).  No exp is evaluated twice; this is the associative scan's carry between
+// chunks (study notes, history: the work-efficient parallel scan; bqwf.cn survey, section 2.2)
+// with the chunks' order kept by the schedule instead of a look-back.
+//
+// Each wave fetches its own lanes' steps of B_n and C_n (bf16) and widens them itself, so the
+// waves of a block share nothing but the carried states: no shared staging and no barrier in
+// the loop.  Both are copied direct-to-LDS into per-wave slots, lane j's 16 steps as two 16-byte
+// words 1 KB apart (conflict-free reads): B, needed first (the lane pass), one step ahead into a
+// ring of two; C, needed at the end of the step (the readout), at the step's start.  u, delta
+// and z of a slot's next window are copied into per-wave LDS slots while the current window
+// runs.  Every wait on the copies is explicit (vmcnt retires a wave's memory operations in issue
+// order), and every read of copied LDS is inline asm that waits for itself.  A block is kSlotCh channels
+// x kSlots slots = 12 waves (3 per SIMD).  Needs bf16 inputs, 16-byte aligned rows, L a multiple
+// of 8 (the direct-to-LDS copies and 16-byte loads) and N >= 3 (the skew).
+constexpr int kSlots = 3;                  // windows in flight per channel
+constexpr int kSlotCh = 4;                 // channels per block
+constexpr int kSlotWaves = kSlots * kSlotCh;
+constexpr int kSlotRing = 2;               // B ring slots per wave (copied one step ahead)
+
+__device__ __forceinline__ void lds_write_f32(uint32_t addr, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+
+// Set (never cleared by a kernel) when a bounded wait between the waves of a block ran out of
+// polls; read and cleared by the host (take_spin_error).  One per device.
+__device__ int g_spin_error;
+
+// s_waitcnt vmcnt(n) for the counts the window-slot kernel uses (anything else waits for all).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+#define SS_W(k) \
+  case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+    SS_W(2) SS_W(4) SS_W(6) SS_W(8) SS_W(10)
+#undef SS_W
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+  }
+}
+
+// A wave's published progress word, read now (not cached in a register: the asm is volatile)
+// and made wave-uniform.
+__device__ __forceinline__ uint32_t progress_one(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Poll until ready() or `limit` polls have failed; in the latter case record the failure in
+// g_spin_error and return (the kernel goes on and ends; its results are then wrong, which the
+// host reports).  A wait can therefore never hang the GPU.
+template <typename F>
+__device__ __forceinline__ void spin_until(F ready, uint32_t limit) {
+  for (uint32_t i = 0; !ready(); ++i) {
+    if (i >= limit) {
+      if ((threadIdx.x & 63) == 0) atomicOr(&g_spin_error, 1);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// This lane's B words of a step (two 16-byte LDS reads at bb, bb + 1 KB), the state's A log2 e
+// and carried state (LDS words at pa, pc), read and waited for in one statement (read through
+// plain C++, the compiler would wait for every copy in flight first).  Likewise this lane's C
+// words (c_reads).
+__device__ __forceinline__ void slot_reads(uint32_t bb, u32x4& b0, u32x4& b1, uint32_t pa, uint32_t pc, float& An,
+                                           float& carry) {
+  asm volatile(
+      "ds_read_b32 %2, %5\n\tds_read_b32 %3, %6\n\t"
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(b0), "=&v"(b1), "=&v"(An), "=&v"(carry)
+      : "v"(bb), "v"(pa), "v"(pc)
+      : "memory");
+}
+
+__device__ __forceinline__ void c_reads(uint32_t cb, u32x4& c0, u32x4& c1) {
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(c0), "=&v"(c1)
+               : "v"(cb)
+               : "memory");
+}
+
+// A slot's place in its schedule: q = s - k D counts its (window, state) steps (q < 0: not
+// started), n = q mod N the state and w = (q div N) kSlots + k the window; ob and oc are the
+// element offsets of its B and C rows' window (n B_sn + w W, n C_sn + w W), kept up to date
+// with additions.
+struct SlotPos {
+  int q, n;
+  int64_t w, ob, oc;
+};
+
+template <typename TOut, bool GATE, int MODE>
+__global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu(3))) void diag_slots_kernel(
+    ScanArgs p, int64_t nwin, int64_t blocks_per_bg, int skew, int nsteps, uint32_t spin_limit) {
+  using TIn = bf16_t;
+  constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
+  constexpr int W = 64 * kK;                         // steps per window
+  constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
+  constexpr int kSegWords = NCI * 256;
+  constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
+  constexpr int GPR = 64 * NCO;                      // 16-byte granules of y per window
+  // per wave: u, delta, z of its slot's current window (y leaves through the z slot)
+  __shared__ __attribute__((aligned(16))) uint32_t xin[kSlotWaves][3][kSegWords];
+  // per wave: B of this and the next step, then C of this step; lane j's 16 steps at words 4 j
+  // (8 steps) and 256 + 4 j
+  __shared__ __attribute__((aligned(16))) uint32_t bring[kSlotWaves][kSlotRing + 1][512];
+  // steps completed by each wave (wave k kSlotCh + c)
+  __shared__ uint32_t prog[kSlotWaves];
+  // [kSlotCh][N] A_n log2 e of the block's channels, then [kSlotCh][N] their carried states
+  extern __shared__ float sp[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k = wave / kSlotCh;    // slot
+  const int c = wave % kSlotCh;    // channel of the block
+  const int64_t L = p.L;
+  const int N = p.N;
+  const int64_t bg = blockIdx.x / blocks_per_bg, blk = blockIdx.x % blocks_per_bg;
+  const int64_t b = bg / p.groups, g = bg % p.groups;
+  const int64_t cpg = p.chan_per_group;
+  const int64_t local = blk * kSlotCh + c;
+  const bool live = local < cpg;                      // (else a copy of a valid channel, not stored)
+  const int64_t d = g * cpg + (live ? local : cpg - 1);
+  const int64_t hd = d / p.chan_per_head;
+  const TIn* urow = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
+  const TIn* drow = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
+  const TIn* zrow = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
+  float bias = p.bias ? p.bias[hd] : 0.f;
+  float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
+  asm volatile("s_waitcnt vmcnt(0)" : "+v"(bias), "+v"(Dd));
+  const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
+  const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
+  if (k == 0) {
+    // the carried state starts at the caller's initial state, or at zero
+    const float* Ar = p.A + d * p.A_sd;
+    const float* hi = (SIO && p.h_init) ? p.h_init + b * p.hi_sb + d * p.hi_sd : nullptr;
+    for (int n = lane; n < N; n += 64) {
+      sp[c * N + n] = Ar[n] * kLog2e;
+      sp[(kSlotCh + c) * N + n] = hi ? hi[n] : 0.f;
+    }
+  }
+  if (lane == 0) prog[wave] = 0;
+  const uint32_t pa0 = lds_addr(sp + c * N);                // this channel's A log2 e
+  const uint32_t pc0 = lds_addr(sp + (kSlotCh + c) * N);    // this channel's carried states
+  // the wave that writes the carried states this wave reads (the previous slot's, same channel)
+  const uint32_t prog_prev = lds_addr(&prog[((k + kSlots - 1) % kSlots) * kSlotCh + c]);
+  const uint32_t prog_mine = lds_addr(&prog[wave]);
+  uint32_t* xu = xin[wave][0];
+  uint32_t* xd = xin[wave][1];
+  uint32_t* xz = xin[wave][2];
+  auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
+    seg_dma<TIn>(row, w * W + (int64_t)lane * kK, L, slot);
+  };
+
+  auto pos_at = [&](int s) {
+    SlotPos ps;
+    ps.q = s - k * skew;
+    const int r = ps.q >= 0 ? ps.q / N : 0;
+    ps.n = ps.q >= 0 ? ps.q - r * N : 0;
+    ps.w = (int64_t)r * kSlots + k;
+    ps.ob = ps.n * p.B_sn + ps.w * W;
+    ps.oc = ps.n * p.C_sn + ps.w * W;
+    return ps;
+  };
+  const int64_t wrap_b = (int64_t)kSlots * W - (int64_t)N * p.B_sn;   // from state N - 1 to the next window's 0
+  const int64_t wrap_c = (int64_t)kSlots * W - (int64_t)N * p.C_sn;
+  auto advance = [&](SlotPos& ps) {
+    if (++ps.q > 0) {
+      ps.ob += p.B_sn;
+      ps.oc += p.C_sn;
+      if (++ps.n == N) {
+        ps.n = 0;
+        ps.w += kSlots;
+        ps.ob += wrap_b;
+        ps.oc += wrap_c;
+      }
+    }
+  };
+  // B (or C) of a slot's (window, state) into slot `slot`: two direct-to-LDS buffer copies
+  // through a resource over the window's part of the row, so that lane j's offset (32 j bytes)
+  // never changes and the addressing is scalar; lane j's steps 16 j .. 16 j + 7 land at word
+  // 4 j, the next 8 at word 256 + 4 j.  Steps past L lie outside the resource and read as zero
+  // (L is a multiple of 8: no copy straddles the end); a slot without a window there copies
+  // nothing (a resource of no bytes).
+  // (the second copy's +16 bytes go into the lane's offset: an instruction offset would move
+  // the LDS destination too)
+  const uint32_t lane_off = 32u * (uint32_t)lane, lane_off2 = lane_off + 16u;
+  auto copy_row = [&](const SlotPos& ps, const TIn* base, int64_t off, int slot) {
+    const bool act = ps.q >= 0 && ps.w < nwin;
+    const int64_t rem = L - ps.w * W;
+    const uint32_t bytes = act ? (uint32_t)(rem < W ? rem : W) * (uint32_t)sizeof(TIn) : 0u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(act ? base + off : base), (short)0, (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&bring[wave][slot][0], 16,
+                                             lane_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&bring[wave][slot][256],
+                                             16, lane_off2, 0, 0, 0);
+  };
+
+  // preamble: each slot's first window of inputs
+  if (k < nwin) {
+    x_copy(urow, k, xu);
+    x_copy(drow, k, xd);
+    if constexpr (GATE) x_copy(zrow, k, xz);
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  float dt[kK], wv[kK], yv[kK];
+  float sdt = 0.f;
+#pragma unroll
+  for (int j = 0; j < kK; ++j) dt[j] = wv[j] = yv[j] = 0.f;
+
+  // One step, its B in ring slot `slot`.  First the copies of this step's C and the next
+  // step's B; then a wait until this step's B (copied one step ago) has landed: at most the
+  // memory operations the previous step issued after that copy (`after`: the window's u and delta
+  // copies, y stores and z copy; -1 for an unknown count) and these four may be in flight.
+  // Everything older has landed too (the u, delta and z copies, one window ago).
+  int after = 0;
+  auto step = [&](int s, SlotPos& cur, SlotPos& ahead, int slot) {
+    copy_row(cur, Cg, cur.oc, kSlotRing);
+    copy_row(ahead, Bg, ahead.ob, slot ^ 1);
+    if (after == 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else wait_vmcnt(after < 0 ? 0 : after + 4);
+    after = 0;
+    if (cur.q >= 0 && cur.w < nwin) {
+      const int n = cur.n;
+      const int64_t w = cur.w;
+      const int64_t w0 = w * W;
+      const int64_t t0 = w0 + (int64_t)lane * kK;
+      const bool full = w0 + W <= L;
+      if (n == 0) {
+        // the window's step sizes from u and delta (copied one window ago)
+        Seg<TIn> su, sd;
+        seg_read<TIn>(xu, lane, su);
+        seg_read<TIn>(xd, lane, sd);
+#pragma unroll
+        for (int j = 0; j < kK; ++j) dt[j] = seg_get<TIn>(sd, j) + bias;
+        if (p.softplus) {
+#pragma unroll
+          for (int j = 0; j < kK; ++j) dt[j] = softplus_fast(dt[j]);
+        }
+        if (!full) {
+          // steps past the end are the identity (a = 1, b = 0); rem is 0, 8 or at least 16 (t0
+          // and L are multiples of 8), so whole words of u are in or out
+          const int rem = (int)(L - t0 < 0 ? 0 : (L - t0 > kK ? kK : L - t0));   // steps inside L
+#pragma unroll
+          for (int j = 0; j < kK; ++j) dt[j] = j < rem ? dt[j] : 0.f;
+#pragma unroll
+          for (int i = 0; i < kK / 2; ++i) su.w[i] = 2 * i < rem ? su.w[i] : 0u;
+        }
+        sdt = 0.f;
+#pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          const float uu = seg_get<TIn>(su, j);
+          wv[j] = ZOH ? uu : dt[j] * uu;   // (zero-order hold: u, its coefficient already holds dt)
+          yv[j] = Dd * uu;
+          sdt += dt[j];
+        }
+        // the slot's next window's u and delta into the slots just read
+        if (w + kSlots < nwin) {
+          x_copy(urow, w + kSlots, xu);
+          x_copy(drow, w + kSlots, xd);
+          after += 2 * NCI;
+        }
+      }
+      // the carried state of state n was written (by the previous slot) D steps ago, or N - 2 D
+      // steps ago for slot 0 (by the last slot, in the round before); the first window starts
+      // from the initial state
+      if (w > 0) {
+        const int src = k ? s - skew : s - N + (kSlots - 1) * skew;
+        spin_until([&] { return progress_one(prog_prev) >= (uint32_t)(src + 1); }, spin_limit);
+      }
+      float An, carry;
+      u32x4 b0, b1;
+      slot_reads(lds_addr(&bring[wave][slot][0]) + 16u * (uint32_t)lane, b0, b1, pa0 + 4u * (uint32_t)n,
+                 pc0 + 4u * (uint32_t)n, An, carry);
+      const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float av[kK], bv[kK];
+      float h = 0.f;
+#pragma unroll
+      for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
+      if constexpr (ZOH) {
+        // u B times (exp(dt A) - 1) / A, from the decays just computed
+        const float Anl = An * kLn2f, rA = __builtin_amdgcn_rcpf(Anl);
+#pragma unroll
+        for (int j = 0; j < kK; ++j) {
+          const float Bj = (j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]);
+          bv[j] = zoh_coef(dt[j], dt[j] * Anl, av[j], rA) * wv[j] * Bj;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kK; ++j) bv[j] = wv[j] * ((j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]));
+      }
+#pragma unroll
+      for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
+      // lane aggregate (decay over the lane's steps, state from zero), then the row's scan from
+      // the carried state
+      h = row_incoming_state(__builtin_amdgcn_exp2f(sdt * An), h, carry);
+      // this step's C has landed once at most what was issued after it (the next step's B, and
+      // the window's u and delta at its first step) is in flight
+      wait_vmcnt(2 + after);
+      u32x4 c0, c1;
+      c_reads(lds_addr(&bring[wave][kSlotRing][0]) + 16u * (uint32_t)lane, c0, c1);
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        const float Cj = (j & 1) ? bf16_hi(cw[j / 2]) : bf16_lo(cw[j / 2]);
+        h = fmaf(av[j], h, bv[j]);
+        if constexpr (TRAP) yv[j] = fmaf(Cj, fmaf(-0.5f, bv[j], h), yv[j]);
+        else yv[j] = fmaf(Cj, h, yv[j]);
+      }
+      // the window's end state carries state n into the next window (the next slot)
+      if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)n, h);
+
+      if (n == N - 1) {
+        // epilogue: gate (z copied one window ago), store, then this slot's z for its next window
+        if constexpr (GATE) {
+          Seg<TIn> sz;
+          seg_read<TIn>(xz, lane, sz);
+#pragma unroll
+          for (int j = 0; j < kK; ++j) yv[j] *= silu_fast(seg_get<TIn>(sz, j));
+        }
+        if (full) {
+          // through LDS, so that each store instruction writes whole runs of consecutive y
+          // (the same granule order and swizzle as the kernel above, one channel per wave)
+          constexpr int YP = kSegWords / 4;                     // granules in the slot
+          constexpr int NPASS = NCO * 64 > YP ? NCO * 64 / YP : 1;
+          constexpr int IPP = NCO / NPASS;                       // store instructions per pass
+          static_assert(NCO % NPASS == 0 && NCO * 64 <= NPASS * YP, "y fits the slot in whole passes");
+          const uint32_t sbase = lds_addr(xz);
+          TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
+#pragma unroll
+          for (int hh = 0; hh < NPASS; ++hh) {
+            if (lane / (64 / NPASS) == hh) {
+#pragma unroll
+              for (int cc = 0; cc < NCO; ++cc) {
+                u32x4 gr;
+                if constexpr (sizeof(TOut) == 4) {
+                  gr = u32x4{__float_as_uint(yv[4 * cc]), __float_as_uint(yv[4 * cc + 1]),
+                             __float_as_uint(yv[4 * cc + 2]), __float_as_uint(yv[4 * cc + 3])};
+                } else {
+                  uint32_t wd[4];
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    wd[e] = f32_to_bf16_bits(yv[8 * cc + 2 * e]) | (f32_to_bf16_bits(yv[8 * cc + 2 * e + 1]) << 16);
+                  gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
+                }
+                const int gi = NCO * lane + cc - 64 * IPP * hh;   // granule within the pass
+                const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
+                asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
+              }
+            }
+            u32x4 yo[IPP];
+            {
+              const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
+              if constexpr (IPP == 2)
+                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                             : "=&v"(yo[0]), "=&v"(yo[1])
+                             : "v"(a)
+                             : "memory");
+              else
+                asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(yo[0]) : "v"(a) : "memory");
+            }
+            if (live) {
+#pragma unroll
+              for (int ii = 0; ii < IPP; ++ii) {
+                const int gi = 64 * (IPP * hh + ii) + lane;
+                __builtin_nontemporal_store(yo[ii], reinterpret_cast<u32x4*>(yr + w0) + gi % GPR);
+              }
+            }
+          }
+          if (live) after += NCO;
+        } else if (live) {
+          TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
+          store_seg<kK>(y, t0, L, false, yv);
+          after = -1;   // an unknown number of element stores
+        }
+        if constexpr (GATE) {
+          if (w + kSlots < nwin) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            x_copy(zrow, w + kSlots, xz);
+            if (after >= 0) after += NCI;
+          }
+        }
+      }
+    }
+    // this wave's LDS writes (the carried state) are done; then it says so
+    asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(prog_mine), "v"((uint32_t)(s + 1)) : "memory");
+    advance(cur);
+    advance(ahead);
+  };
+
+  // the first step's B; then steps in pairs (static ring slots)
+  SlotPos cur = pos_at(0), ahead = pos_at(1);
+  copy_row(cur, Bg, cur.ob, 0);
+  static_assert(kSlotRing == 2, "two steps per turn");
+  for (int s = 0; s < nsteps; s += kSlotRing) {
+    step(s, cur, ahead, 0);
+    if (s + 1 < nsteps) step(s + 1, cur, ahead, 1);
+  }
+  // the state after the last step (steps past L are the identity)
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  if (SIO && p.h_final && live && k == 0) {
+    float* hf = p.h_final + b * p.hf_sb + d * p.hf_sd;
+    for (int n = lane; n < N; n += 64) hf[n] = sp[(kSlotCh + c) * N + n];
+  }
+}
+
+// The window-slot kernel serves few rows (at most one round of one wave per SIMD) with at least
+// kSlots windows, bf16 inputs in 16-byte aligned rows and N >= 3.
+bool slots_path(const ScanArgs& a) {
+#ifdef SS_DIAG_NO_SLOTS
+  return false;
+#else
+  return a.in_bf16 && a.vec && a.L % 8 == 0 && a.N >= 3 &&
+         a.batch * a.channels <= (int64_t)kWaves * cu_count() && (a.L + 64 * kK - 1) / (64 * kK) >= kSlots;
+#endif
+}
+
+template <typename TOut>
+hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
+  constexpr int64_t W = 64 * kK;
+  const int64_t nwin = (a.L + W - 1) / W;
+  const int skew = std::max(1, a.N / 3);   // <= (N - 1) / 2 for N >= 3
+  int64_t steps = 0;
+  for (int k = 0; k < kSlots && k < nwin; ++k) {
+    const int64_t windows = (nwin - k + kSlots - 1) / kSlots;
+    steps = std::max(steps, windows * a.N + (int64_t)k * skew);
+  }
+  const int64_t blocks_per_bg = (a.chan_per_group + kSlotCh - 1) / kSlotCh;
+  const int64_t blocks = a.batch * a.groups * blocks_per_bg;
+  const size_t dyn = sizeof(float) * 2 * kSlotCh * a.N;
+  const dim3 grid((unsigned)blocks), block(64 * kSlotWaves);
+  // polls of a wait between waves before it gives up (each poll sleeps ~64 clocks: ~0.5 s in
+  // all, against ~1 us per step); SS_SPIN_LIMIT in the environment lowers it, so that tests can
+  // force the failure path
+  uint32_t spin_limit = 1u << 24;
+  if (const char* e = getenv("SS_SPIN_LIMIT")) spin_limit = (uint32_t)strtoul(e, nullptr, 10);
+  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0);
+#define SS_M(G, M)                                                                                          \
+  case M:                                                                                                   \
+    hipLaunchKernelGGL((diag_slots_kernel<TOut, G, M>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,  \
+                       (int)steps, spin_limit);                                                             \
+    break;
+#define SS_LAUNCH(G)                                                                                        \
+  switch (mode) {                                                                                           \
+    SS_M(G, 0) SS_M(G, kSIO) SS_M(G, kSIO | kZOH) SS_M(G, kSIO | kTRAP) SS_M(G, kSIO | kZOH | kTRAP)        \
+    default: return hipErrorInvalidValue;                                                                   \
+  }
+  if (a.z) {
+    SS_LAUNCH(true);
+  } else {
+    SS_LAUNCH(false);
+  }
+#undef SS_LAUNCH
+#undef SS_M
+  return hipGetLastError();
+}
+
 int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
 
 // Channels per wave: one while every row still gets its own wave in a single round of one
@@ -976,7 +1478,19 @@ hipError_t launch_t(const ScanArgs& a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t take_spin_error(int* failed) {
+  int v = 0;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_spin_error), sizeof(int));
+  if (e == hipSuccess && v) {
+    const int zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_spin_error), &zero, sizeof(int));
+  }
+  *failed = v;
+  return e;
+}
+
 hipError_t launch_diag(const ScanArgs& a, hipStream_t s) {
+  if (slots_path(a)) return a.out_bf16 ? launch_slots<bf16_t>(a, s) : launch_slots<float>(a, s);
   if (a.in_bf16) return a.out_bf16 ? launch_t<bf16_t, bf16_t>(a, s) : launch_t<bf16_t, float>(a, s);
   return a.out_bf16 ? launch_t<float, bf16_t>(a, s) : launch_t<float, float>(a, s);
 }

@@ -125,9 +125,13 @@ hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 // Compute units of the current device (cached per device; 256 if the query fails).
 int cu_count();
 
-// Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time.  One
-// kernel, no workspace.
+// Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time; few rows
+// take several windows of each row in flight.  One kernel, no workspace.
 hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
+
+// Whether a bounded wait between the waves of a block has run out since the last call (then
+// the results of the calls in between are wrong); clears the record.  Synchronous.
+hipError_t take_spin_error(int* failed);
 
 // Scalar decay A [heads]: lanes along channels, 16 states per wave.  `ws` must hold
 // scalar_workspace_floats(a) floats of device memory, ordered on `stream`.

@@ -74,7 +74,8 @@ def strerror(code: int) -> str:
 
 
 def check(stream: Optional[int] = None) -> int:
-    """ss_check: synchronise ``stream`` and return SS_OK (0) or SS_ERR_HIP if enqueued work failed."""
+    """ss_check: synchronise ``stream`` and return SS_OK (0), SS_ERR_HIP (-8) if enqueued work failed,
+    or SS_ERR_DEADLOCK (-9) if a kernel's bounded wait between waves ran out since the last check."""
     return lib().ss_check(ctypes.c_void_p(stream or 0))
 
 

@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert scan.version() == 100
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert scan.strerror(code)
     assert scan.strerror(-99) == "unknown error code"
 
@@ -543,3 +543,17 @@ def test_check_reports_the_device_state():
 
     rc = scan.check(None)
     assert rc == (0 if torch.cuda.is_available() else -8)
+
+
+def test_probe_library_exports_its_header():
+    """libssprobe.so (the ceiling probes used by bench.py --probe) exports what include/ss_probe.h
+    declares."""
+    path = os.path.join(os.path.dirname(scan.LIB_PATH), "libssprobe.so")
+    if not os.path.exists(path):
+        pytest.skip("libssprobe.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ss_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"^\s*\w+\s*\**\s*(ssp_\w+)\s*\(", text, flags=re.M)))
+    assert names == ["ssp_copy", "ssp_read", "ssp_valu"]
+    lib = ctypes.CDLL(path)
+    for n in names:
+        assert hasattr(lib, n), n
