@@ -948,33 +948,36 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
 // count, e.g. the 1024 rows of a layer of a million steps), the kernel above gives each row one
 // wave, which walks its windows in order: one wave per SIMD, and a wave on its own issues at
 // best one instruction every few clocks.  Here each channel gets kSlots waves.  Slot k takes
-// windows k, k + kSlots, k + 2 kSlots, ..., one state per step; the state at the end of window w
-// (state n) is the carried state of window w + 1 (state n), which belongs to the next slot.  The
-// slots therefore run skewed: slot k handles state n of its r-th window at step r N + n + k D
-// (the skew D with 1 <= D <= (N - 1) / 2), so the carried state it reads was written D steps
-// earlier by slot k - 1 (for slot 0: N - 2 D steps earlier, by the last slot in the round
-// before).  One LDS word per (channel, state) holds it, and each wave publishes the steps it has
-// completed: a wave waits only for the wave that writes the carried state it reads, which is
-// normally D steps ahead.  Every write of a word is read by the next slot before the following
-// write (each writer has itself waited, through the chain of slots, for the reader of the
-// previous value).  No exp is evaluated twice; this is the associative scan's carry between
-// chunks (study notes, history: the work-efficient parallel scan; bqwf.cn survey, section 2.2)
-// with the chunks' order kept by the schedule instead of a look-back.
+// windows k, k + kSlots, k + 2 kSlots, ..., two states per step (Ns = ceil(N / 2) steps per
+// window); the state at the end of window w (state n) is the carried state of window w + 1
+// (state n), which belongs to the next slot.  The slots therefore run skewed: slot k handles
+// pair np of its r-th window at step r Ns + np + k D (the skew D with 1 <= D <= (Ns - 1) / 2),
+// so the carried states it reads were written D steps earlier by slot k - 1 (for slot 0:
+// Ns - 2 D steps earlier, by the last slot in the round before).  One LDS word per (channel,
+// state) holds them, and each wave publishes the steps it has completed: a wave waits only for
+// the wave that writes the carried states it reads, which is normally D steps ahead.  Every
+// write of a word is read by the next slot before the following write (each writer has itself
+// waited, through the chain of slots, for the reader of the previous value).  No exp is
+// evaluated twice; this is the associative scan's carry between chunks (study notes, history:
+// the work-efficient parallel scan; bqwf.cn survey, section 2.2) with the chunks' order kept by
+// the schedule instead of a look-back.
 //
-// Each wave fetches its own lanes' steps of B_n and C_n (bf16) and widens them itself, so the
-// waves of a block share nothing but the carried states: no shared staging and no barrier in
-// the loop.  Both are copied direct-to-LDS into per-wave slots, lane j's 16 steps as two 16-byte
-// words 1 KB apart (conflict-free reads): B, needed first (the lane pass), one step ahead into a
-// ring of two; C, needed at the end of the step (the readout), at the step's start.  u, delta
-// and z of a slot's next window are copied into per-wave LDS slots while the current window
-// runs.  Every wait on the copies is explicit (vmcnt retires a wave's memory operations in issue
-// order), and every read of copied LDS is inline asm that waits for itself.  A block is kSlotCh channels
-// x kSlots slots = 12 waves (3 per SIMD).  Needs bf16 inputs, 16-byte aligned rows, L a multiple
-// of 8 (the direct-to-LDS copies and 16-byte loads) and N >= 3 (the skew).
+// Each wave fetches its own lanes' steps of B and C (bf16) for the step's two states and widens
+// them itself, so the waves of a block share nothing but the carried states: no shared staging
+// and no barrier in the loop.  Both are copied direct-to-LDS into per-wave areas, lane j's 16
+// steps of a state as two 16-byte words 1 KB apart (conflict-free reads): B of the next step as
+// soon as this step's B is in registers, C of this step at its start (needed at the readouts).
+// u and delta go through two per-wave LDS slots: at a window's first step the wave reads u and
+// delta and copies the window's z into u's slot and the next window's delta into delta's; at the
+// window's last step it reads z and copies the next window's u into u's slot.  y leaves through
+// the C area.  Every wait on the copies is
+// explicit (vmcnt retires a wave's memory operations in issue order), and every read of copied
+// LDS is inline asm that waits for itself.  A block is kSlotCh channels x kSlots slots = 12
+// waves (3 per SIMD).  Needs bf16 inputs, 16-byte aligned rows, L a multiple of 8 (the
+// direct-to-LDS copies) and N >= 5 (the skew).
 constexpr int kSlots = 3;                  // windows in flight per channel
 constexpr int kSlotCh = 4;                 // channels per block
 constexpr int kSlotWaves = kSlots * kSlotCh;
-constexpr int kSlotRing = 2;               // B ring slots per wave (copied one step ahead)
 
 __device__ __forceinline__ void lds_write_f32(uint32_t addr, float v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
@@ -989,7 +992,7 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   switch (n) {
 #define SS_W(k) \
   case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
-    SS_W(2) SS_W(4) SS_W(6) SS_W(8) SS_W(10)
+    SS_W(4) SS_W(6) SS_W(8) SS_W(10) SS_W(12)
 #undef SS_W
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
   }
@@ -1017,21 +1020,24 @@ __device__ __forceinline__ void spin_until(F ready, uint32_t limit) {
   }
 }
 
-// This lane's B words of a step (two 16-byte LDS reads at bb, bb + 1 KB), the state's A log2 e
-// and carried state (LDS words at pa, pc), read and waited for in one statement (read through
-// plain C++, the compiler would wait for every copy in flight first).  Likewise this lane's C
-// words (c_reads).
-__device__ __forceinline__ void slot_reads(uint32_t bb, u32x4& b0, u32x4& b1, uint32_t pa, uint32_t pc, float& An,
-                                           float& carry) {
+// This lane's B words of the step's two states (16-byte LDS reads at bb + 0, 1, 2, 3 KB), and
+// the states' A log2 e and carried states (LDS words at pa0, pa1, pc0, pc1), read and waited for
+// in one statement (read through plain C++, the compiler would wait for every copy in flight
+// first).
+__device__ __forceinline__ void slot_reads(uint32_t bb, u32x4 (&bq)[4], uint32_t pa0, uint32_t pa1, uint32_t pc0,
+                                           uint32_t pc1, float (&An)[2], float (&carry)[2]) {
   asm volatile(
-      "ds_read_b32 %2, %5\n\tds_read_b32 %3, %6\n\t"
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+      "ds_read_b32 %4, %9\n\tds_read_b32 %5, %10\n\tds_read_b32 %6, %11\n\tds_read_b32 %7, %12\n\t"
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\tds_read_b128 %3, %8 offset:3072\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(b0), "=&v"(b1), "=&v"(An), "=&v"(carry)
-      : "v"(bb), "v"(pa), "v"(pc)
+      : "=&v"(bq[0]), "=&v"(bq[1]), "=&v"(bq[2]), "=&v"(bq[3]), "=&v"(An[0]), "=&v"(An[1]), "=&v"(carry[0]),
+        "=&v"(carry[1])
+      : "v"(bb), "v"(pa0), "v"(pa1), "v"(pc0), "v"(pc1)
       : "memory");
 }
 
+// This lane's C words of one state (16-byte LDS reads at cb, cb + 1 KB).
 __device__ __forceinline__ void c_reads(uint32_t cb, u32x4& c0, u32x4& c1) {
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
                : "=&v"(c0), "=&v"(c1)
@@ -1039,12 +1045,12 @@ __device__ __forceinline__ void c_reads(uint32_t cb, u32x4& c0, u32x4& c1) {
                : "memory");
 }
 
-// A slot's place in its schedule: q = s - k D counts its (window, state) steps (q < 0: not
-// started), n = q mod N the state and w = (q div N) kSlots + k the window; ob and oc are the
-// element offsets of its B and C rows' window (n B_sn + w W, n C_sn + w W), kept up to date
-// with additions.
+// A slot's place in its schedule: q = s - k D counts its steps (q < 0: not started), np = q mod
+// Ns the step's pair of states (2 np, 2 np + 1) and w = (q div Ns) kSlots + k the window; ob and
+// oc are the element offsets of its first B and C row's window (2 np B_sn + w W, likewise),
+// kept up to date with additions.
 struct SlotPos {
-  int q, n;
+  int q, np;
   int64_t w, ob, oc;
 };
 
@@ -1058,11 +1064,11 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   constexpr int kSegWords = NCI * 256;
   constexpr int NCO = kK * (int)sizeof(TOut) / 16;   // 16-byte stores per lane of y
   constexpr int GPR = 64 * NCO;                      // 16-byte granules of y per window
-  // per wave: u, delta, z of its slot's current window (y leaves through the z slot)
-  __shared__ __attribute__((aligned(16))) uint32_t xin[kSlotWaves][3][kSegWords];
-  // per wave: B of this and the next step, then C of this step; lane j's 16 steps at words 4 j
-  // (8 steps) and 256 + 4 j
-  __shared__ __attribute__((aligned(16))) uint32_t bring[kSlotWaves][kSlotRing + 1][512];
+  // per wave: u (then z) and delta of its slot's window (see above)
+  __shared__ __attribute__((aligned(16))) uint32_t xin[kSlotWaves][2][kSegWords];
+  // per wave: B of the step's two states (words 0-511, 512-1023), then C of them (1024-2047);
+  // lane j's 16 steps of a state at words 4 j (8 steps) and 256 + 4 j of its 512
+  __shared__ __attribute__((aligned(16))) uint32_t bc[kSlotWaves][2048];
   // steps completed by each wave (wave k kSlotCh + c)
   __shared__ uint32_t prog[kSlotWaves];
   // [kSlotCh][N] A_n log2 e of the block's channels, then [kSlotCh][N] their carried states
@@ -1074,6 +1080,7 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   const int c = wave % kSlotCh;    // channel of the block
   const int64_t L = p.L;
   const int N = p.N;
+  const int Ns = (N + 1) / 2;      // steps per window
   const int64_t bg = blockIdx.x / blocks_per_bg, blk = blockIdx.x % blocks_per_bg;
   const int64_t b = bg / p.groups, g = bg % p.groups;
   const int64_t cpg = p.chan_per_group;
@@ -1106,7 +1113,8 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   const uint32_t prog_mine = lds_addr(&prog[wave]);
   uint32_t* xu = xin[wave][0];
   uint32_t* xd = xin[wave][1];
-  uint32_t* xz = xin[wave][2];
+  const uint32_t bcb = lds_addr(&bc[wave][0]) + 16u * (uint32_t)lane;   // this lane's B words
+  const uint32_t ccb = bcb + 4096u;                                      // and C words
   auto x_copy = [&](const TIn* row, int64_t w, uint32_t* slot) {
     seg_dma<TIn>(row, w * W + (int64_t)lane * kK, L, slot);
   };
@@ -1114,80 +1122,128 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   auto pos_at = [&](int s) {
     SlotPos ps;
     ps.q = s - k * skew;
-    const int r = ps.q >= 0 ? ps.q / N : 0;
-    ps.n = ps.q >= 0 ? ps.q - r * N : 0;
+    const int r = ps.q >= 0 ? ps.q / Ns : 0;
+    ps.np = ps.q >= 0 ? ps.q - r * Ns : 0;
     ps.w = (int64_t)r * kSlots + k;
-    ps.ob = ps.n * p.B_sn + ps.w * W;
-    ps.oc = ps.n * p.C_sn + ps.w * W;
+    ps.ob = 2 * ps.np * p.B_sn + ps.w * W;
+    ps.oc = 2 * ps.np * p.C_sn + ps.w * W;
     return ps;
   };
-  const int64_t wrap_b = (int64_t)kSlots * W - (int64_t)N * p.B_sn;   // from state N - 1 to the next window's 0
-  const int64_t wrap_c = (int64_t)kSlots * W - (int64_t)N * p.C_sn;
+  // from the last pair of a window to the next window's first
+  const int64_t wrap_b = (int64_t)kSlots * W - 2 * (int64_t)Ns * p.B_sn;
+  const int64_t wrap_c = (int64_t)kSlots * W - 2 * (int64_t)Ns * p.C_sn;
   auto advance = [&](SlotPos& ps) {
     if (++ps.q > 0) {
-      ps.ob += p.B_sn;
-      ps.oc += p.C_sn;
-      if (++ps.n == N) {
-        ps.n = 0;
+      ps.ob += 2 * p.B_sn;
+      ps.oc += 2 * p.C_sn;
+      if (++ps.np == Ns) {
+        ps.np = 0;
         ps.w += kSlots;
         ps.ob += wrap_b;
         ps.oc += wrap_c;
       }
     }
   };
-  // B (or C) of a slot's (window, state) into slot `slot`: two direct-to-LDS buffer copies
-  // through a resource over the window's part of the row, so that lane j's offset (32 j bytes)
-  // never changes and the addressing is scalar; lane j's steps 16 j .. 16 j + 7 land at word
-  // 4 j, the next 8 at word 256 + 4 j.  Steps past L lie outside the resource and read as zero
-  // (L is a multiple of 8: no copy straddles the end); a slot without a window there copies
-  // nothing (a resource of no bytes).
-  // (the second copy's +16 bytes go into the lane's offset: an instruction offset would move
-  // the LDS destination too)
+  // B (or C) of a position's two states into this wave's area at word `dst`: per state two
+  // direct-to-LDS buffer copies through a resource over the window's part of the row, so that
+  // lane j's offsets (32 j and 32 j + 16 bytes; an instruction offset would move the LDS
+  // destination too) never change and the addressing is scalar; lane j's steps 16 j .. 16 j + 7
+  // land at word 4 j of the state's 512, the next 8 at 256 + 4 j.  Steps past L lie outside the
+  // resource and read as zero (L is a multiple of 8: no copy straddles the end); a state >= N,
+  // or a slot without a window there, copies nothing (a resource of no bytes).
   const uint32_t lane_off = 32u * (uint32_t)lane, lane_off2 = lane_off + 16u;
-  auto copy_row = [&](const SlotPos& ps, const TIn* base, int64_t off, int slot) {
+  auto copy_pair = [&](const SlotPos& ps, const TIn* base, int64_t off, int64_t sn, int dst) {
     const bool act = ps.q >= 0 && ps.w < nwin;
     const int64_t rem = L - ps.w * W;
     const uint32_t bytes = act ? (uint32_t)(rem < W ? rem : W) * (uint32_t)sizeof(TIn) : 0u;
-    const __amdgpu_buffer_rsrc_t rs =
+    const bool two = 2 * ps.np + 1 < N;
+    const __amdgpu_buffer_rsrc_t r0 =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<TIn*>(act ? base + off : base), (short)0, (int)bytes, 0x00020000);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&bring[wave][slot][0], 16,
-                                             lane_off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)&bring[wave][slot][256],
-                                             16, lane_off2, 0, 0, 0);
+    const __amdgpu_buffer_rsrc_t r1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<TIn*>(act && two ? base + off + sn : base), (short)0, two ? (int)bytes : 0, 0x00020000);
+    auto* l = (__attribute__((address_space(3))) uint32_t*)&bc[wave][dst];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, l, 16, lane_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r0, l + 256, 16, lane_off2, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, l + 512, 16, lane_off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r1, l + 768, 16, lane_off2, 0, 0, 0);
   };
 
-  // preamble: each slot's first window of inputs
+  // preamble: each slot's first window of u and delta, and its first step's B
+  SlotPos cur = pos_at(0), nxt = pos_at(1);
   if (k < nwin) {
     x_copy(urow, k, xu);
     x_copy(drow, k, xd);
-    if constexpr (GATE) x_copy(zrow, k, xz);
   }
+  copy_pair(cur, Bg, cur.ob, p.B_sn, 0);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   float dt[kK], wv[kK], yv[kK];
   float sdt = 0.f;
 #pragma unroll
   for (int j = 0; j < kK; ++j) dt[j] = wv[j] = yv[j] = 0.f;
-
-  // One step, its B in ring slot `slot`.  First the copies of this step's C and the next
-  // step's B; then a wait until this step's B (copied one step ago) has landed: at most the
-  // memory operations the previous step issued after that copy (`after`: the window's u and delta
-  // copies, y stores and z copy; -1 for an unknown count) and these four may be in flight.
-  // Everything older has landed too (the u, delta and z copies, one window ago).
+  // memory operations the previous step issued after its copy of this step's B (its y stores;
+  // -1 for an unknown number)
   int after = 0;
-  auto step = [&](int s, SlotPos& cur, SlotPos& ahead, int slot) {
-    copy_row(cur, Cg, cur.oc, kSlotRing);
-    copy_row(ahead, Bg, ahead.ob, slot ^ 1);
-    if (after == 0) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+
+  // one state of the step: lane pass from B words bw, the row's scan from the carried state, C
+  // words from LDS (landed), the readout into yv; returns the window's end state (lane 63)
+  auto one_state = [&](const uint32_t (&bw)[8], float An, float carry, uint32_t cwaddr) {
+    float av[kK], bv[kK];
+    float h = 0.f;
+#pragma unroll
+    for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
+    if constexpr (ZOH) {
+      // u B times (exp(dt A) - 1) / A, from the decays just computed
+      const float Anl = An * kLn2f, rA = __builtin_amdgcn_rcpf(Anl);
+#pragma unroll
+      for (int j = 0; j < kK; ++j) {
+        const float Bj = (j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]);
+        bv[j] = zoh_coef(dt[j], dt[j] * Anl, av[j], rA) * wv[j] * Bj;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kK; ++j) bv[j] = wv[j] * ((j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]));
+    }
+#pragma unroll
+    for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
+    // lane aggregate (decay over the lane's steps, state from zero), then the row's scan from
+    // the carried state
+    h = row_incoming_state(__builtin_amdgcn_exp2f(sdt * An), h, carry);
+    u32x4 c0, c1;
+    c_reads(cwaddr, c0, c1);
+    const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+    for (int j = 0; j < kK; ++j) {
+      const float Cj = (j & 1) ? bf16_hi(cw[j / 2]) : bf16_lo(cw[j / 2]);
+      h = fmaf(av[j], h, bv[j]);
+      if constexpr (TRAP) yv[j] = fmaf(Cj, fmaf(-0.5f, bv[j], h), yv[j]);
+      else yv[j] = fmaf(Cj, h, yv[j]);
+    }
+    return h;
+  };
+
+  for (int s = 0; s < nsteps; ++s) {
+    const bool act = cur.q >= 0 && cur.w < nwin;
+    const int np = cur.np;
+    const int64_t w = cur.w;
+    const int64_t w0 = w * W;
+    const int64_t t0 = w0 + (int64_t)lane * kK;
+    const bool full = w0 + W <= L;
+    const bool epi = act && np == Ns - 1;
+    // this step's C; then everything issued before it has landed except what the previous step
+    // issued after its copy of this step's B (its y stores and u copy) -- all of it at a window's
+    // first step, whose u was copied at the previous step
+    copy_pair(cur, Cg, cur.oc, p.C_sn, 1024);
+    if (after == 0 || (act && np == 0)) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else wait_vmcnt(after < 0 ? 0 : after + 4);
     after = 0;
-    if (cur.q >= 0 && cur.w < nwin) {
-      const int n = cur.n;
-      const int64_t w = cur.w;
-      const int64_t w0 = w * W;
-      const int64_t t0 = w0 + (int64_t)lane * kK;
-      const bool full = w0 + W <= L;
-      if (n == 0) {
+    int issued = 0;   // memory operations issued after this step's C copies, before its readouts
+    u32x4 bq[4] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    float An[2] = {0.f, 0.f}, carry[2] = {0.f, 0.f};
+    const int n0 = 2 * np;
+    const bool two = n0 + 1 < N;
+    if (act) {
+      if (np == 0) {
         // the window's step sizes from u and delta (copied one window ago)
         Seg<TIn> su, sd;
         seg_read<TIn>(xu, lane, su);
@@ -1215,147 +1271,116 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
           yv[j] = Dd * uu;
           sdt += dt[j];
         }
-        // the slot's next window's u and delta into the slots just read
+        // the window's z into u's slot, the slot's next window's delta into delta's
+        if constexpr (GATE) {
+          x_copy(zrow, w, xu);
+          issued += NCI;
+        }
         if (w + kSlots < nwin) {
-          x_copy(urow, w + kSlots, xu);
           x_copy(drow, w + kSlots, xd);
-          after += 2 * NCI;
+          issued += NCI;
         }
       }
-      // the carried state of state n was written (by the previous slot) D steps ago, or N - 2 D
-      // steps ago for slot 0 (by the last slot, in the round before); the first window starts
-      // from the initial state
+      // the carried states of this step's pair were written (by the previous slot) D steps ago,
+      // or Ns - 2 D steps ago for slot 0 (by the last slot, in the round before); the first
+      // window starts from the initial state
       if (w > 0) {
-        const int src = k ? s - skew : s - N + (kSlots - 1) * skew;
+        const int src = k ? s - skew : s - Ns + (kSlots - 1) * skew;
         spin_until([&] { return progress_one(prog_prev) >= (uint32_t)(src + 1); }, spin_limit);
       }
-      float An, carry;
-      u32x4 b0, b1;
-      slot_reads(lds_addr(&bring[wave][slot][0]) + 16u * (uint32_t)lane, b0, b1, pa0 + 4u * (uint32_t)n,
-                 pc0 + 4u * (uint32_t)n, An, carry);
-      const uint32_t bw[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-      float av[kK], bv[kK];
-      float h = 0.f;
-#pragma unroll
-      for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
-      if constexpr (ZOH) {
-        // u B times (exp(dt A) - 1) / A, from the decays just computed
-        const float Anl = An * kLn2f, rA = __builtin_amdgcn_rcpf(Anl);
-#pragma unroll
-        for (int j = 0; j < kK; ++j) {
-          const float Bj = (j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]);
-          bv[j] = zoh_coef(dt[j], dt[j] * Anl, av[j], rA) * wv[j] * Bj;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < kK; ++j) bv[j] = wv[j] * ((j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]));
+      const int n1 = two ? n0 + 1 : n0;
+      slot_reads(bcb, bq, pa0 + 4u * (uint32_t)n0, pa0 + 4u * (uint32_t)n1, pc0 + 4u * (uint32_t)n0,
+                 pc0 + 4u * (uint32_t)n1, An, carry);
+    }
+    // the next step's B into the area just read
+    copy_pair(nxt, Bg, nxt.ob, p.B_sn, 0);
+    issued += 4;
+    if (act) {
+      // this step's C has landed once at most what was issued after it (z, the u and delta
+      // copies, the next step's B) is in flight
+      wait_vmcnt(issued);
+      {
+        const uint32_t bw[8] = {bq[0].x, bq[0].y, bq[0].z, bq[0].w, bq[1].x, bq[1].y, bq[1].z, bq[1].w};
+        const float h = one_state(bw, An[0], carry[0], ccb);
+        // the window's end state carries state n into the next window (the next slot)
+        if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)n0, h);
       }
-#pragma unroll
-      for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
-      // lane aggregate (decay over the lane's steps, state from zero), then the row's scan from
-      // the carried state
-      h = row_incoming_state(__builtin_amdgcn_exp2f(sdt * An), h, carry);
-      // this step's C has landed once at most what was issued after it (the next step's B, and
-      // the window's u and delta at its first step) is in flight
-      wait_vmcnt(2 + after);
-      u32x4 c0, c1;
-      c_reads(lds_addr(&bring[wave][kSlotRing][0]) + 16u * (uint32_t)lane, c0, c1);
-      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-      for (int j = 0; j < kK; ++j) {
-        const float Cj = (j & 1) ? bf16_hi(cw[j / 2]) : bf16_lo(cw[j / 2]);
-        h = fmaf(av[j], h, bv[j]);
-        if constexpr (TRAP) yv[j] = fmaf(Cj, fmaf(-0.5f, bv[j], h), yv[j]);
-        else yv[j] = fmaf(Cj, h, yv[j]);
+      if (two) {
+        const uint32_t bw[8] = {bq[2].x, bq[2].y, bq[2].z, bq[2].w, bq[3].x, bq[3].y, bq[3].z, bq[3].w};
+        const float h = one_state(bw, An[1], carry[1], ccb + 2048u);
+        if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)(n0 + 1), h);
       }
-      // the window's end state carries state n into the next window (the next slot)
-      if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)n, h);
 
-      if (n == N - 1) {
-        // epilogue: gate (z copied one window ago), store, then this slot's z for its next window
+      if (epi) {
+        // epilogue: gate (z copied at the window's first step), then y through the C area (read
+        // above), stored; then the slot's next window's u into u's slot
         if constexpr (GATE) {
           Seg<TIn> sz;
-          seg_read<TIn>(xz, lane, sz);
+          seg_read<TIn>(xu, lane, sz);
 #pragma unroll
           for (int j = 0; j < kK; ++j) yv[j] *= silu_fast(seg_get<TIn>(sz, j));
         }
         if (full) {
-          // through LDS, so that each store instruction writes whole runs of consecutive y
-          // (the same granule order and swizzle as the kernel above, one channel per wave)
-          constexpr int YP = kSegWords / 4;                     // granules in the slot
-          constexpr int NPASS = NCO * 64 > YP ? NCO * 64 / YP : 1;
-          constexpr int IPP = NCO / NPASS;                       // store instructions per pass
-          static_assert(NCO % NPASS == 0 && NCO * 64 <= NPASS * YP, "y fits the slot in whole passes");
-          const uint32_t sbase = lds_addr(xz);
+          // each store instruction writes whole runs of consecutive y: lane granule cc (steps
+          // 4 cc.. of a f32 lane, 8 cc.. of a bf16 lane) is granule gi = NCO lane + cc of the
+          // window, kept at gi ^ ((gi >> 4) & (NCO - 1)) so that neither the writes nor the reads
+          // conflict on banks; store instruction ii has lane l take granule 64 ii + l
+          const uint32_t sbase = lds_addr(&bc[wave][1024]);
           TOut* __restrict__ yr = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
 #pragma unroll
-          for (int hh = 0; hh < NPASS; ++hh) {
-            if (lane / (64 / NPASS) == hh) {
+          for (int cc = 0; cc < NCO; ++cc) {
+            u32x4 gr;
+            if constexpr (sizeof(TOut) == 4) {
+              gr = u32x4{__float_as_uint(yv[4 * cc]), __float_as_uint(yv[4 * cc + 1]), __float_as_uint(yv[4 * cc + 2]),
+                         __float_as_uint(yv[4 * cc + 3])};
+            } else {
+              uint32_t wd[4];
 #pragma unroll
-              for (int cc = 0; cc < NCO; ++cc) {
-                u32x4 gr;
-                if constexpr (sizeof(TOut) == 4) {
-                  gr = u32x4{__float_as_uint(yv[4 * cc]), __float_as_uint(yv[4 * cc + 1]),
-                             __float_as_uint(yv[4 * cc + 2]), __float_as_uint(yv[4 * cc + 3])};
-                } else {
-                  uint32_t wd[4];
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    wd[e] = f32_to_bf16_bits(yv[8 * cc + 2 * e]) | (f32_to_bf16_bits(yv[8 * cc + 2 * e + 1]) << 16);
-                  gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
-                }
-                const int gi = NCO * lane + cc - 64 * IPP * hh;   // granule within the pass
-                const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
-                asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
-              }
+              for (int e = 0; e < 4; ++e)
+                wd[e] = f32_to_bf16_bits(yv[8 * cc + 2 * e]) | (f32_to_bf16_bits(yv[8 * cc + 2 * e + 1]) << 16);
+              gr = u32x4{wd[0], wd[1], wd[2], wd[3]};
             }
-            u32x4 yo[IPP];
-            {
-              const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
-              if constexpr (IPP == 2)
-                asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
-                             : "=&v"(yo[0]), "=&v"(yo[1])
-                             : "v"(a)
-                             : "memory");
-              else
-                asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(yo[0]) : "v"(a) : "memory");
-            }
-            if (live) {
-#pragma unroll
-              for (int ii = 0; ii < IPP; ++ii) {
-                const int gi = 64 * (IPP * hh + ii) + lane;
-                __builtin_nontemporal_store(yo[ii], reinterpret_cast<u32x4*>(yr + w0) + gi % GPR);
-              }
-            }
+            const int gi = NCO * lane + cc;
+            const uint32_t a = sbase + 16u * (uint32_t)(gi ^ ((gi >> 4) & (NCO - 1)));
+            asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(gr) : "memory");
           }
-          if (live) after += NCO;
+          u32x4 yo[NCO];
+          {
+            const uint32_t a = sbase + 16u * (uint32_t)(lane ^ ((lane >> 4) & (NCO - 1)));
+            if constexpr (NCO == 4)
+              asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\t"
+                           "ds_read_b128 %2, %4 offset:2048\n\tds_read_b128 %3, %4 offset:3072\n\t"
+                           "s_waitcnt lgkmcnt(0)"
+                           : "=&v"(yo[0]), "=&v"(yo[1]), "=&v"(yo[2]), "=&v"(yo[3])
+                           : "v"(a)
+                           : "memory");
+            else
+              asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                           : "=&v"(yo[0]), "=&v"(yo[1])
+                           : "v"(a)
+                           : "memory");
+          }
+          if (live) {
+#pragma unroll
+            for (int ii = 0; ii < NCO; ++ii)
+              __builtin_nontemporal_store(yo[ii], reinterpret_cast<u32x4*>(yr + w0) + (64 * ii + lane) % GPR);
+            after = NCO;
+          }
         } else if (live) {
           TOut* __restrict__ y = static_cast<TOut*>(p.y) + b * p.y_sb + d * p.y_sd;
           store_seg<kK>(y, t0, L, false, yv);
           after = -1;   // an unknown number of element stores
         }
-        if constexpr (GATE) {
-          if (w + kSlots < nwin) {
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            x_copy(zrow, w + kSlots, xz);
-            if (after >= 0) after += NCI;
-          }
+        if (w + kSlots < nwin) {
+          x_copy(urow, w + kSlots, xu);
+          if (after >= 0) after += NCI;
         }
       }
     }
-    // this wave's LDS writes (the carried state) are done; then it says so
+    // this wave's LDS writes (the carried states, the y staging) are done; then it says so
     asm volatile("s_waitcnt lgkmcnt(0)\n\tds_write_b32 %0, %1" ::"v"(prog_mine), "v"((uint32_t)(s + 1)) : "memory");
     advance(cur);
-    advance(ahead);
-  };
-
-  // the first step's B; then steps in pairs (static ring slots)
-  SlotPos cur = pos_at(0), ahead = pos_at(1);
-  copy_row(cur, Bg, cur.ob, 0);
-  static_assert(kSlotRing == 2, "two steps per turn");
-  for (int s = 0; s < nsteps; s += kSlotRing) {
-    step(s, cur, ahead, 0);
-    if (s + 1 < nsteps) step(s + 1, cur, ahead, 1);
+    advance(nxt);
   }
   // the state after the last step (steps past L are the identity)
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -1366,12 +1391,12 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
 }
 
 // The window-slot kernel serves few rows (at most one round of one wave per SIMD) with at least
-// kSlots windows, bf16 inputs in 16-byte aligned rows and N >= 3.
+// kSlots windows, bf16 inputs in 16-byte aligned rows and N >= 5.
 bool slots_path(const ScanArgs& a) {
 #ifdef SS_DIAG_NO_SLOTS
   return false;
 #else
-  return a.in_bf16 && a.vec && a.L % 8 == 0 && a.N >= 3 &&
+  return a.in_bf16 && a.vec && a.L % 8 == 0 && a.N >= 5 &&
          a.batch * a.channels <= (int64_t)kWaves * cu_count() && (a.L + 64 * kK - 1) / (64 * kK) >= kSlots;
 #endif
 }
@@ -1380,11 +1405,12 @@ template <typename TOut>
 hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
   constexpr int64_t W = 64 * kK;
   const int64_t nwin = (a.L + W - 1) / W;
-  const int skew = std::max(1, a.N / 3);   // <= (N - 1) / 2 for N >= 3
+  const int ns = (a.N + 1) / 2;            // steps per window (two states a step)
+  const int skew = std::max(1, ns / 3);    // <= (ns - 1) / 2 for ns >= 3
   int64_t steps = 0;
   for (int k = 0; k < kSlots && k < nwin; ++k) {
     const int64_t windows = (nwin - k + kSlots - 1) / kSlots;
-    steps = std::max(steps, windows * a.N + (int64_t)k * skew);
+    steps = std::max(steps, windows * ns + (int64_t)k * skew);
   }
   const int64_t blocks_per_bg = (a.chan_per_group + kSlotCh - 1) / kSlotCh;
   const int64_t blocks = a.batch * a.groups * blocks_per_bg;

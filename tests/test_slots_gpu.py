@@ -1,9 +1,10 @@
 """Parity of the diagonal kernel's window-slot layout (GPU): few (batch, channel) rows, each with
-three windows of 1024 steps in flight, the carried state handed from slot to slot through LDS.
+three windows of 1024 steps in flight, two states a step, the carried state handed from slot to
+slot through LDS.
 
 The launch takes that layout for bf16 inputs with 16-byte aligned rows, L a multiple of 8 and at
-least three windows, N >= 3, when the rows fit one wave per SIMD (4 x the compute units: 1024 on
-MI355X).  These cases cover the skew (N from 3 to 128), lengths around whole rounds of the
+least three windows, N >= 5, when the rows fit one wave per SIMD (4 x the compute units: 1024 on
+MI355X).  These cases cover the skew (N from 5 to 128, odd and even), lengths around whole rounds of the
 three slots and with a partial last window, a last block with fewer than four channels, heads and
 groups, every mode, the state in and out, y in bf16, bitwise determinism and causality across
 slot boundaries, and a wait between waves forced to run out (reported by ss_check, no hang).
@@ -30,10 +31,11 @@ CASES = {
     "N16 3 windows": lambda: inputs.random_problem(1300, 1, 8, 3072, 16),
     # a partial last window (L a multiple of 8, not of 1024), several rounds
     "N16 ragged": lambda: inputs.random_problem(1301, 2, 6, 5 * 1024 + 264, 16),
-    # the smallest N with a skew (skew 1) and others around the skew's bounds
-    "N3": lambda: inputs.random_problem(1302, 1, 5, 4096 + 8, 3),
-    "N4": lambda: inputs.random_problem(1303, 1, 4, 7 * 1024, 4, gate=False),
+    # the smallest N with a skew (three steps of two states, skew 1; the last step's second
+    # state absent) and others around the skew's bounds
     "N5": lambda: inputs.random_problem(1304, 1, 9, 4 * 1024 + 512, 5),
+    "N6": lambda: inputs.random_problem(1302, 1, 5, 4096 + 8, 6),
+    "N7": lambda: inputs.random_problem(1303, 1, 4, 7 * 1024, 7, gate=False),
     "N17": lambda: inputs.random_problem(1305, 1, 7, 6 * 1024 + 8, 17),
     "N64": lambda: inputs.random_problem(1306, 1, 4, 3 * 1024 + 1000, 64),
     "N128": lambda: inputs.random_problem(1307, 1, 3, 4 * 1024, 128, gate=False),
