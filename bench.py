@@ -66,15 +66,21 @@ TRANS = 8.0
 
 
 # source file of each scan kernel
-KERNEL_SOURCE = {"diag_fwd_kernel": "ss_diag.hip", "scalar_head_kernel": "ss_scalar.hip",
+KERNEL_SOURCE = {"diag_fwd_kernel": "ss_diag.hip", "diag_slots_kernel": "ss_diag.hip",
+                 "scalar_head_kernel": "ss_scalar.hip",
                  "ssd_scan_kernel": "ss_ssd.hip", "conv1d_kernel": "ss_conv.hip",
                  "bwd_kernel": "ss_bwd.hip", "ssdb_main_kernel": "ss_ssd_bwd.hip"}
 
 
-def scan_kernel(p):
+def scan_kernel(p, cus=256):
     """Name of the kernel that dominates one call on this workload (the library's own choice:
-    scalar decay with bf16 inputs and heads of a multiple of 64 channels takes the matrix form)."""
+    scalar decay with bf16 inputs and heads of a multiple of 64 channels takes the matrix form; a
+    diagonal decay with bf16 inputs, N >= 5, at least three 1024-step windows and at most one row
+    per SIMD (4 x `cus` rows) takes the window-slot kernel; the bench's rows are aligned)."""
     if not p.scalar_decay:
+        if (p.in_dtype == "bf16" and p.nstate >= 5 and p.length % 8 == 0 and (p.length + 1023) // 1024 >= 3
+                and p.batch * p.channels <= 4 * cus):
+            return "diag_slots_kernel"
         return "diag_fwd_kernel"
     P = p.channels // p.heads
     cpg = p.channels // p.groups
@@ -640,7 +646,7 @@ def forward_line(args, p, workload, to_dev, dev, *, steps, warmup, cpu):
     slots = alu_slots_per_element(p)
     alu_floor_s = E * slots / VALU_LANE_OPS
     # the kernel that dominates the step (the diagonal path is that one kernel alone)
-    kernel = scan_kernel(p)
+    kernel = scan_kernel(p, torch.cuda.get_device_properties(dev).multi_processor_count)
     traffic = stored_traffic(kernel, workload, kernel_source_digest(kernel))
     copy_peak = stored_copy_peak()
 
@@ -686,6 +692,9 @@ def forward_line(args, p, workload, to_dev, dev, *, steps, warmup, cpu):
     }
 
     if kernel == "ssd_scan_kernel":
+        # the VALU model counts per-(t, p, n) FP32 operations that the matrix form does on the
+        # matrix cores instead: it bounds nothing here
+        del out["roofline"]["alu"]
         # The matrix form is a chain of dense contractions on v_mfma_f32_16x16x32_bf16
         # (16*16*32*2 flops each).  Per (batch, head, 64-channel slab, 32-step chunk) each of 4
         # waves issues 4 for the masked product, Np/8 for the readout from the carried state and
