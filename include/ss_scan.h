@@ -95,6 +95,9 @@ typedef struct {
  * bound for tests).  The wave went on instead of hanging, so the results of the calls since the
  * previous ss_check are wrong. */
 #define SS_ERR_DEADLOCK (-9)
+/* ss_scan_fwd_noalloc only: the call needs more scratch than that entry point's static buffer
+ * (SS_NOALLOC_SCRATCH_BYTES) holds.  Nothing was enqueued and y is untouched. */
+#define SS_ERR_SCRATCH (-10)
 
 /*
  * ss_scan_fwd -- selective-scan forward, y = S6(u, delta, A, B, C, D, z, delta_bias).
@@ -152,6 +155,27 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
                       const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                       const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
                       ss_tensor* h_final, ss_tensor* y, void* stream);
+
+/*
+ * ss_scan_fwd_noalloc -- ss_scan_fwd_state for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * results, validation and asynchrony as ss_scan_fwd_state; it calls no hipMalloc, hipFree or
+ * allocating library routine.
+ *
+ * The scratch that scalar-decay calls need (the per-chunk operands of B and C and the states
+ * handed between sequence segments, which ss_scan_fwd_state takes from its memory pool) comes
+ * instead from one static device array of SS_NOALLOC_SCRATCH_BYTES (64 MiB), which each GPU
+ * the library runs on holds until the process ends.  A call whose scratch would exceed it
+ * returns SS_ERR_SCRATCH (nothing enqueued, y untouched); diagonal-decay calls use no scratch
+ * and have no such limit.  Every call on one GPU shares that GPU's array and leaves its contents
+ * behind (every byte a call reads, it wrote first): calls that overlap on one GPU -- on two
+ * streams, or from two host threads -- race and give wrong results; order them on one stream.
+ */
+#define SS_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int ss_scan_fwd_noalloc(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                        const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                        const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
+                        ss_tensor* h_final, ss_tensor* y, void* stream);
 
 /*
  * ss_scan_step -- one decoding step: the recurrence advanced by a single token from a persistent

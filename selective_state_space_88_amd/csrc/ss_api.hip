@@ -1,4 +1,4 @@
-// ss_api.hip -- C ABI of libssscan.so: validation, dispatch, workspace.  See include/ss_scan.h.
+// ss_api.hip -- C ABI of libssscan.so: validation, dispatch, workspace (pooled, or static scratch).  See include/ss_scan.h.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -105,6 +105,30 @@ hipError_t ws_alloc(void** ws, size_t bytes, hipStream_t s) {
   return hipMallocFromPoolAsync(ws, bytes, pool, s);
 }
 
+// Scratch of ss_scan_fwd_noalloc: one static array per device, which the code object reserves
+// when it is loaded on that device.  In host code `scratch` names a host-side stand-in, not
+// device memory: kernels get the device address, looked up once per device (with that device
+// current) and kept.
+static __device__ __align__(256) uint8_t scratch[SS_NOALLOC_SCRATCH_BYTES];
+
+hipError_t scratch_address(void** ptr) {
+  static std::mutex mu;
+  static void* addrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addrs[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addrs[dev] = p;
+  }
+  *ptr = addrs[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -125,6 +149,7 @@ const char* ss_strerror(int code) {
     case SS_ERR_HIP: return "HIP runtime error";
     case SS_ERR_DEADLOCK:
       return "a bounded wait between the waves of a kernel ran out: results since the last check are wrong";
+    case SS_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point's static buffer holds";
     default: return "unknown error code";
   }
 }
@@ -160,7 +185,8 @@ int check_state(const ss_tensor* h, int64_t Bt, int64_t Dc, int64_t N) {
 
 int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z, const ss_tensor* delta_bias,
-                uint32_t flags, const ss_tensor* h_init, ss_tensor* h_final, ss_tensor* y, void* stream) {
+                uint32_t flags, const ss_tensor* h_init, ss_tensor* h_final, ss_tensor* y, void* stream,
+                bool noalloc) {
   if (!u || !delta || !A || !B || !C || !y) return SS_ERR_NULL;
   if (flags & ~kScanFlags) return SS_ERR_FLAGS;
   const bool gate = (flags & SS_Z_GATE_SILU) != 0;
@@ -286,6 +312,16 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   const bool mfma = ss::ssd_path(a);
   void* ws = nullptr;
   const int64_t wsb = mfma ? ss::ssd_workspace_bytes(a) : ss::scalar_workspace_floats(a) * (int64_t)sizeof(float);
+  if (noalloc) {
+    // the static scratch: every byte the kernels read they write first, so nothing is cleared
+    if (wsb > (int64_t)SS_NOALLOC_SCRATCH_BYTES) return SS_ERR_SCRATCH;
+    if (scratch_address(&ws) != hipSuccess) {
+      (void)hipGetLastError();
+      return SS_ERR_HIP;
+    }
+    const hipError_t e = mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
+    return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+  }
   if (ws_alloc(&ws, (size_t)wsb, s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
@@ -302,14 +338,21 @@ extern "C" {
 int ss_scan_fwd(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                 const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                 const ss_tensor* delta_bias, uint32_t flags, ss_tensor* y, void* stream) {
-  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, nullptr, nullptr, y, stream);
+  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, nullptr, nullptr, y, stream, false);
 }
 
 int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
                       const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
                       const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
                       ss_tensor* h_final, ss_tensor* y, void* stream) {
-  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, h_init, h_final, y, stream);
+  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, h_init, h_final, y, stream, false);
+}
+
+int ss_scan_fwd_noalloc(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,
+                        const ss_tensor* C, const ss_tensor* D, const ss_tensor* z,
+                        const ss_tensor* delta_bias, uint32_t flags, const ss_tensor* h_init,
+                        ss_tensor* h_final, ss_tensor* y, void* stream) {
+  return scan_common(u, delta, A, B, C, D, z, delta_bias, flags, h_init, h_final, y, stream, true);
 }
 
 int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, const ss_tensor* B,

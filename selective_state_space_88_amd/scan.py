@@ -22,8 +22,10 @@ SS_DETERMINISTIC = 1 << 2   # forward paths are deterministic by construction; t
 SS_ZOH = 1 << 3
 SS_TRAPEZOID = 1 << 4
 SS_CONV_SILU = 1 << 0   # flag of ss_conv1d
-EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_step", "ss_scan_bwd", "ss_conv1d", "ss_check",
-           "ss_strerror", "ss_version")
+SS_ERR_SCRATCH = -10
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the static scratch of ss_scan_fwd_noalloc, per device
+EXPORTS = ("ss_scan_fwd", "ss_scan_fwd_state", "ss_scan_fwd_noalloc", "ss_scan_step", "ss_scan_bwd",
+           "ss_conv1d", "ss_check", "ss_strerror", "ss_version")
 
 
 class SSTensor(ctypes.Structure):
@@ -52,6 +54,8 @@ def lib() -> ctypes.CDLL:
         l.ss_scan_fwd.restype = ctypes.c_int
         l.ss_scan_fwd_state.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, ctypes.c_void_p]
         l.ss_scan_fwd_state.restype = ctypes.c_int
+        l.ss_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, ctypes.c_void_p]
+        l.ss_scan_fwd_noalloc.restype = ctypes.c_int
         l.ss_scan_step.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, ctypes.c_void_p]
         l.ss_scan_step.restype = ctypes.c_int
         l.ss_scan_bwd.argtypes = [P, P, P, P, P, P, P, P, ctypes.c_uint32, P, P, P, P, P, P, P, P, P,
@@ -123,6 +127,13 @@ def call_state(u, delta, A, B, C, D, z, delta_bias, flags: int, h_init, h_final,
                                    _ref(y), ctypes.c_void_p(stream or 0))
 
 
+def call_noalloc(u, delta, A, B, C, D, z, delta_bias, flags: int, h_init, h_final, y, stream) -> int:
+    """Raw ss_scan_fwd_noalloc call with descriptors (or None); returns the library's code."""
+    return lib().ss_scan_fwd_noalloc(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
+                                     _ref(delta_bias), ctypes.c_uint32(flags), _ref(h_init), _ref(h_final),
+                                     _ref(y), ctypes.c_void_p(stream or 0))
+
+
 def call_step(u, delta, A, B, C, D, z, delta_bias, flags: int, h, y, stream) -> int:
     """Raw ss_scan_step call with descriptors (or None); returns the library's code."""
     return lib().ss_scan_step(_ref(u), _ref(delta), _ref(A), _ref(B), _ref(C), _ref(D), _ref(z),
@@ -167,6 +178,28 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Ten
         rc = call(*args, describe(y), stream)
     else:
         rc = call_state(*args, describe(h_init), describe(h_final), describe(y), stream)
+    if rc != 0:
+        raise ScanError(rc, strerror(rc))
+    return y
+
+
+def scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                     C: torch.Tensor, y: torch.Tensor, D: Optional[torch.Tensor] = None,
+                     z: Optional[torch.Tensor] = None, delta_bias: Optional[torch.Tensor] = None, *,
+                     softplus: bool = True, stream: Optional[int] = None,
+                     h_init: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
+                     zoh: bool = False, trapezoid: bool = False) -> torch.Tensor:
+    """scan_fwd through ss_scan_fwd_noalloc: the caller passes y, and the library allocates
+    nothing (its scalar-decay scratch is a static 64 MiB array per device; larger calls raise
+    ScanError with code SS_ERR_SCRATCH).  Calls that overlap on one GPU race on that scratch."""
+    _check_cuda(u, delta, A, B, C, D, z, delta_bias, h_init, h_final, y)
+    flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
+        (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(u.device).cuda_stream
+    rc = call_noalloc(describe(u), describe(delta), describe(A), describe(B), describe(C), describe(D),
+                      describe(z), describe(delta_bias), flags, describe(h_init), describe(h_final),
+                      describe(y), stream)
     if rc != 0:
         raise ScanError(rc, strerror(rc))
     return y

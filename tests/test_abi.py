@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     assert scan.version() == 100
-    for code in range(-9, 1):
+    for code in range(-10, 1):
         assert scan.strerror(code)
     assert scan.strerror(-99) == "unknown error code"
 
@@ -285,6 +285,30 @@ def test_state_variant_empty_batch_is_a_noop():
     assert call_state(p, *state_args(p, Bt=0)) == 0
     p = problem(L=0)
     assert call_state(p, *state_args(p, h_final=False)) == 0   # no final state to write
+
+
+def call_noalloc(p, hi, hf):
+    return scan.call_noalloc(p["u"], p["delta"], p["A"], p["B"], p["C"], p["D"], p["z"], p["delta_bias"],
+                             p["flags"], hi, hf, p["y"], None)
+
+
+def test_noalloc_variant_validates_like_the_state_variant():
+    """ss_scan_fwd_noalloc runs the same checks before it touches its scratch."""
+    p = problem()
+    p["u"] = None
+    assert call_noalloc(p, *state_args(problem())) == -1
+    p = problem()
+    p["delta"].dtype = scan.SS_F32
+    assert call_noalloc(p, *state_args(p)) == -2
+    p = problem(N=129)
+    assert call_noalloc(p, *state_args(p, N=129)) == -6
+    p = problem()
+    hi, hf = state_args(p)
+    hf.data = hi.data + 16
+    assert call_noalloc(p, hi, hf) == -7
+    p = problem(Bt=0)
+    assert call_noalloc(p, *state_args(p, Bt=0)) == 0
+    assert scan.strerror(scan.SS_ERR_SCRATCH) != "unknown error code"
 
 
 # ---------------------------------------------------------------- ss_scan_step
