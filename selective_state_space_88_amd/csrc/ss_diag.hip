@@ -739,7 +739,6 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
         for (int si = 0; si < 2; ++si) {
           const float An = si ? pv.y : pv.x;   // A_n log2 e
           float av[kK], bv[kK];
-          float h = 0.f;
 #pragma unroll
           for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
           if constexpr (ZOH) {
@@ -752,8 +751,10 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
 #pragma unroll
             for (int j = 0; j < kK; ++j) bv[j] = wv[j] * bq[4 * si + j / 4][j % 4];
           }
+          // the lane's steps from a zero state (the first step's decay multiplies zero)
+          float h = bv[0];
 #pragma unroll
-          for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
+          for (int j = 1; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
           // lane aggregate: decay over the lane's K steps and the lane's state from zero; the
           // scan, with this lane's C values of the state read while it runs
           float sa = __builtin_amdgcn_exp2f(sdt * An), sb = h;
@@ -777,7 +778,7 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
       } else {
         float av0[kK], bv0[kK], av1[kK], bv1[kK];
         float wz0[ZOH ? kK : 1], wz1[ZOH ? kK : 1];
-        float h0 = 0.f, h1 = 0.f;
+        float h0, h1;
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
           av0[j] = __builtin_amdgcn_exp2f(dt[j] * pv.x);
@@ -793,12 +794,13 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
             wz1[j] = zoh_coef(dt[j], dt[j] * An1, av1[j], rA1) * wv[j];
           }
         }
+        // the lane's steps from a zero state (the first step's decay multiplies zero)
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
           bv0[j] = (ZOH ? wz0[j] : wv[j]) * bq[j / 4][j % 4];
           bv1[j] = (ZOH ? wz1[j] : wv[j]) * bq[4 + j / 4][j % 4];
-          h0 = fmaf(av0[j], h0, bv0[j]);
-          h1 = fmaf(av1[j], h1, bv1[j]);
+          h0 = j ? fmaf(av0[j], h0, bv0[j]) : bv0[j];
+          h1 = j ? fmaf(av1[j], h1, bv1[j]) : bv1[j];
         }
         // lane aggregates: decay over the lane's K steps and the lane's state from zero
         float sa0 = __builtin_amdgcn_exp2f(sdt * pv.x), sb0 = h0;
@@ -1189,7 +1191,6 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   // words from LDS (landed), the readout into yv; returns the window's end state (lane 63)
   auto one_state = [&](const uint32_t (&bw)[8], float An, float carry, uint32_t cwaddr) {
     float av[kK], bv[kK];
-    float h = 0.f;
 #pragma unroll
     for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
     if constexpr (ZOH) {
@@ -1204,8 +1205,10 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
       for (int j = 0; j < kK; ++j) bv[j] = wv[j] * ((j & 1) ? bf16_hi(bw[j / 2]) : bf16_lo(bw[j / 2]));
     }
+    // the lane's steps from a zero state (the first step's decay multiplies zero)
+    float h = bv[0];
 #pragma unroll
-    for (int j = 0; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
+    for (int j = 1; j < kK; ++j) h = fmaf(av[j], h, bv[j]);
     // lane aggregate (decay over the lane's steps, state from zero), then the row's scan from
     // the carried state
     h = row_incoming_state(__builtin_amdgcn_exp2f(sdt * An), h, carry);
