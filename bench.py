@@ -493,6 +493,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (ss_scan_bwd: gradients of every input for an upstream "
                          "gradient dy) on the workload instead of the forward")
+    ap.add_argument("--gate", action="store_true",
+                    help="with --backward on the scalar-decay workload: add a silu gate on a seeded z "
+                         "(the layout the workload itself leaves ungated)")
     ap.add_argument("--conv", action="store_true",
                     help="time the causal depthwise convolution in front of the scan (ss_conv1d, silu) "
                          "on the workload's scan input instead of the scan")
@@ -528,7 +531,7 @@ def main():
         args.steps = 30 if big else 1000
     if args.warmup is None:
         args.warmup = 10 if big else 200
-    p = inputs.make(args.workload)
+    p = inputs.make(args.workload, gate=True) if args.gate else inputs.make(args.workload)
 
     def to_dev(a):
         if a is None:

@@ -487,6 +487,24 @@ __global__ __launch_bounds__(256) void zero4_kernel(float* __restrict__ p, int64
   }
 }
 
+// The gate of a layer whose ungated backward is the matrix form: dz = dy y0 s'(z), and y0 (the
+// output before the gate, recomputed by the forward into `y0`, [batch, channels, L] contiguous)
+// replaced in place by dy0 = dy s(z), the gradient the ungated backward takes.
+template <typename TIn, typename TDy>
+__global__ __launch_bounds__(256) void gate_bwd_kernel(BwdArgs p, float* __restrict__ y0) {
+  const int64_t total = p.batch * p.channels * p.L;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t t = i % p.L, r = i / p.L;
+    const int64_t d = r % p.channels, b = r / p.channels;
+    const float zz = to_f32(static_cast<const TIn*>(p.z)[b * p.z_sb + d * p.z_sd + t]);
+    const float g = to_f32(static_cast<const TDy*>(p.dy)[b * p.dy_sb + d * p.dy_sd + t]);
+    // s(z) = z sigmoid(z), s'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+    const float sgz = 1.f / (1.f + __builtin_amdgcn_exp2f(-zz * kLog2e));
+    p.dz[b * p.dz_sb + d * p.dz_sd + t] = g * y0[i] * sgz * fmaf(zz, 1.f - sgz, 1.f);
+    y0[i] = g * (zz * sgz);
+  }
+}
+
 template <typename TIn, typename TDy>
 hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   const int P = (a.N + 1) / 2;
@@ -524,14 +542,103 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A gated layer whose ungated backward is the matrix form (scalar decay, heads and groups in
+// whole 64-channel slabs) composes three steps on one workspace: the forward without the gate
+// recomputes y0 = C h + D u (the output before the gate) into f32 rows; an elementwise kernel
+// writes dz and turns y0 into dy0 = dy s(z); the ungated matrix-form backward runs on dy0.
+bool gated_matrix_path(const BwdArgs& a) {
+  BwdArgs b = a;
+  b.z = nullptr;
+  return a.z && ssd_bwd_path(b);
+}
+
+constexpr int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
+
+// the forward without the gate, y0 into `y0` ([batch, channels, L] f32, contiguous)
+ScanArgs ungated_forward(const BwdArgs& a, float* y0) {
+  ScanArgs f{};
+  f.u = a.u;
+  f.delta = a.delta;
+  f.B = a.B;
+  f.C = a.C;
+  f.z = nullptr;
+  f.A = a.A;
+  f.D = a.D;
+  f.bias = a.bias;
+  f.y = y0;
+  f.batch = a.batch;
+  f.channels = a.channels;
+  f.L = a.L;
+  f.N = a.N;
+  f.heads = a.heads;
+  f.groups = a.groups;
+  f.chan_per_head = a.chan_per_head;
+  f.chan_per_group = a.chan_per_group;
+  f.d_per_head = a.d_per_head;
+  f.softplus = a.softplus;
+  f.in_bf16 = a.in_bf16;
+  f.out_bf16 = 0;
+  f.vec = a.vec && a.L % 4 == 0;   // y0's rows are L floats from a 256-byte aligned base
+  f.u_sb = a.u_sb;
+  f.u_sd = a.u_sd;
+  f.dl_sb = a.dl_sb;
+  f.dl_sh = a.dl_sh;
+  f.B_sb = a.B_sb;
+  f.B_sg = a.B_sg;
+  f.B_sn = a.B_sn;
+  f.C_sb = a.C_sb;
+  f.C_sg = a.C_sg;
+  f.C_sn = a.C_sn;
+  f.y_sb = a.channels * a.L;
+  f.y_sd = a.L;
+  f.A_sd = 0;   // one decay per head
+  return f;
+}
+
+int64_t forward_ws_floats(const ScanArgs& f) {
+  return ssd_path(f) ? (ssd_workspace_bytes(f) + 3) / 4 : scalar_workspace_floats(f);
+}
+
 }  // namespace
 
 int64_t bwd_workspace_floats(const BwdArgs& a) {
+  if (gated_matrix_path(a)) {
+    BwdArgs b = a;
+    b.z = nullptr;
+    const int64_t ny = round64(a.batch * a.channels * a.L);
+    return ny + round64(forward_ws_floats(ungated_forward(a, nullptr))) + ssd_bwd_workspace_floats(b);
+  }
   if (ssd_bwd_path(a)) return ssd_bwd_workspace_floats(a);
   return a.batch * a.channels * ((a.L + kBW - 1) / kBW) * a.N;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
+  if (gated_matrix_path(a)) {
+    float* y0 = ws;
+    float* fws = y0 + round64(a.batch * a.channels * a.L);
+    const ScanArgs f = ungated_forward(a, y0);
+    float* bws = fws + round64(forward_ws_floats(f));
+    hipError_t e = ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
+    if (e != hipSuccess) return e;
+    const int64_t total = a.batch * a.channels * a.L;
+    const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 16384));
+#define SS_GATE(TI, TD) hipLaunchKernelGGL((gate_bwd_kernel<TI, TD>), grid, dim3(256), 0, s, a, y0)
+    if (a.in_bf16) {
+      if (a.dy_bf16) SS_GATE(bf16_t, bf16_t); else SS_GATE(bf16_t, float);
+    } else {
+      if (a.dy_bf16) SS_GATE(float, bf16_t); else SS_GATE(float, float);
+    }
+#undef SS_GATE
+    BwdArgs b = a;
+    b.z = nullptr;
+    b.dz = nullptr;
+    b.dy = y0;
+    b.dy_bf16 = 0;
+    b.dy_sb = a.channels * a.L;
+    b.dy_sd = a.L;
+    b.vec = a.vec && a.L % 4 == 0;
+    return launch_bwd(b, bws, s);
+  }
   if (a.in_bf16) return a.dy_bf16 ? launch_t<bf16_t, bf16_t>(a, ws, s) : launch_t<bf16_t, float>(a, ws, s);
   return a.dy_bf16 ? launch_t<float, bf16_t>(a, ws, s) : launch_t<float, float>(a, ws, s);
 }

@@ -135,6 +135,33 @@ def test_matrix_backward(case):
     check_bwd(MATRIX_CASES[case](), "matrix " + case)
 
 
+GATED_MATRIX_CASES = {
+    # scalar decay with a gate, heads and groups in whole 64-channel slabs: the forward without
+    # the gate recomputes y0, an elementwise pass gives dz and dy0 = dy s(z), then the matrix form
+    "N16 bf16 L700": lambda: inputs.random_problem(780, 2, 128, 700, 16, heads=2, scalar_decay=True, gate=True),
+    "N128 f32 L600": lambda: inputs.random_problem(781, 1, 64, 600, 128, heads=1, scalar_decay=True,
+                                                   in_dtype="f32", gate=True),
+    "N33 f32 ragged": lambda: inputs.random_problem(782, 2, 64, 97, 33, heads=1, scalar_decay=True, in_dtype="f32",
+                                                    gate=True),
+    "two groups": lambda: inputs.random_problem(783, 1, 256, 200, 32, heads=4, groups=2, scalar_decay=True,
+                                                in_dtype="f32", gate=True),
+    "no softplus, no D": lambda: inputs.random_problem(784, 1, 128, 333, 16, heads=2, scalar_decay=True,
+                                                       in_dtype="f32", gate=True, softplus=False, with_D=False),
+    "N64 bf16 L1": lambda: inputs.random_problem(785, 1, 64, 1, 64, heads=1, scalar_decay=True, gate=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(GATED_MATRIX_CASES))
+def test_gated_matrix_backward(case):
+    check_bwd(GATED_MATRIX_CASES[case](), "gated matrix " + case)
+
+
+def test_gated_matrix_backward_bf16_dy():
+    torch = torch_dev()
+    check_bwd(inputs.random_problem(786, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=True),
+              "gated matrix dy bf16", dy_dtype=torch.bfloat16)
+
+
 def test_matrix_backward_bf16_dy():
     torch = torch_dev()
     check_bwd(inputs.random_problem(770, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=False), "matrix dy bf16",
@@ -189,6 +216,36 @@ def test_workload_1_full_size_sampled_channels():
     pairs = [("du", (slice(None), c), "du"), ("ddelta", (slice(None), c), "ddelta"), ("dz", (slice(None), c), "dz"),
              ("dA", c, "dA"), ("dD", c, "dD"), ("ddelta_bias", c, "ddelta_bias")]
     _compare(g, ref, pairs, "workload 1 full size, channels %s" % ch.tolist(), TOL["bf16"])
+
+
+def test_workload_4_gated_full_size_sampled_heads():
+    """The scalar-decay multi-head layer at full size with a silu gate on z: the composed
+    gated path (forward recompute, gate pass, matrix-form backward); du, dz, ddelta, dA, dD and
+    ddelta_bias of 2 sampled heads against the oracle run on those heads alone."""
+    import dataclasses
+
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_bwd
+
+    p = inputs.make(4, gate=True)
+    P = p.channels // p.heads
+    dy = inputs.seeded_normal(14, (p.batch, p.channels, p.length))
+    say("[bwd] workload 4 gated full size: batch=%d channels=%d L=%d N=%d" % (p.batch, p.channels, p.length,
+                                                                           p.nstate))
+    t = dev_problem(p)
+    g = scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], to_dev(dy),
+                 softplus=p.softplus)
+    torch.cuda.synchronize()
+    hs = np.array([3, 79])
+    ch = np.concatenate([np.arange(h * P, (h + 1) * P) for h in hs])
+    sub = dataclasses.replace(p, channels=len(ch), heads=len(hs), u=p.u[:, ch], delta=p.delta[:, hs],
+                              A=p.A[hs], D=p.D[hs], delta_bias=p.delta_bias[hs], z=p.z[:, ch])
+    ref = oracle.scan_bwd_problem(sub, np.ascontiguousarray(dy[:, ch]))
+    c = torch.as_tensor(ch, device="cuda")
+    h = torch.as_tensor(hs, device="cuda")
+    pairs = [("du", (slice(None), c), "du"), ("dz", (slice(None), c), "dz"), ("ddelta", (slice(None), h), "ddelta"),
+             ("dA", h, "dA"), ("dD", h, "dD"), ("ddelta_bias", h, "ddelta_bias")]
+    _compare(g, ref, pairs, "workload 4 gated full size, heads %s" % hs.tolist(), TOL["bf16"])
 
 
 def test_workload_4_full_size_sampled_heads():
