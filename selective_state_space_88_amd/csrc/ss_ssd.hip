@@ -94,19 +94,38 @@ __global__ __launch_bounds__(256) void ssd_prep_kernel(ScanArgs p, uint8_t* __re
     sC[n][t] = in ? to_f32(Cg[n * p.C_sn + t0 + t]) : 0.f;
   }
   __syncthreads();
+  // G[t][s] = sum_n C[t][n] B[s][n] on the matrix cores (products of bf16 values are exact in
+  // f32): wave w computes the 16 x 16 tile (t-tile w / 2, s-tile w % 2), its operands the staged
+  // values' top 16 bits (each a bf16 held exactly in f32)
+  __shared__ float sG[kT][kT + 1];
+  {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int ti = w >> 1, si = w & 1, g = l >> 4, r16 = l & 15;
+    f32x4v acc = f32x4v{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < Np / 32; ++ks) {
+      uint32_t a[4], bb[4];
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int n0 = 32 * ks + 8 * g + 2 * k2;
+        a[k2] = (__float_as_uint(sC[n0][16 * ti + r16]) >> 16) | (__float_as_uint(sC[n0 + 1][16 * ti + r16]) & 0xffff0000u);
+        bb[k2] = (__float_as_uint(sB[n0][16 * si + r16]) >> 16) | (__float_as_uint(sB[n0 + 1][16 * si + r16]) & 0xffff0000u);
+      }
+      acc = mfma(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}), as_bf16x8(u32x4{bb[0], bb[1], bb[2], bb[3]}), acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sG[16 * ti + 4 * g + r][16 * si + r16] = acc[r];
+  }
+  __syncthreads();
   // the record holds every operand in the order the scan's MFMA lanes read it (lane l =
   // 16 g + q holds row q, K slots 8 g .. 8 g + 7), so that each wave reads it as contiguous
   // 16-byte pieces with no LDS bank conflicts
   uint8_t* rec = ws + bgc * rec_bytes(Np);
-  // G [i][half][lane][4] f32: (G o causal)[t = 16 i + q][s = 8 g + 4 half + e], where
-  // G[t][s] = sum_n C[t][n] B[s][n] (products of bf16 values are exact in f32)
+  // G [i][half][lane][4] f32: (G o causal)[t = 16 i + q][s = 8 g + 4 half + e]
   float* Gp = reinterpret_cast<float*>(rec);
   for (int i = threadIdx.x; i < kT * kT; i += 256) {
     const int e = i & 3, l = (i >> 2) & 63, half = (i >> 8) & 1, ti = i >> 9;
     const int t = 16 * ti + (l & 15), s = 8 * (l >> 4) + 4 * half + e;
-    float acc = 0.f;
-    for (int n = 0; n < Np; ++n) acc = fmaf(sC[n][t], sB[n][s], acc);
-    Gp[i] = s <= t ? acc : 0.f;
+    Gp[i] = s <= t ? sG[t][s] : 0.f;
   }
   // C [i][ks][lane][8] bf16: C[t = 16 i + q][n], with K slot e of lane group g holding
   // n = 32 ks + 4 g + (e % 4) + 16 (e / 4) (the order of the state accumulators' rows)
