@@ -33,7 +33,7 @@ METRIC = "selective-scan fwd elems/s (B·D·L/s) + achieved HBM GB/s vs peak, 1 
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0   # dense bf16 matrix-core peak
 FP32_MATRIX_PEAK_TFLOPS = 157.3  # dense fp32 matrix-core peak
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # packed FP32 vector peak (this build emits no packed FP32)
+FP32_VECTOR_UNPACKED_TFLOPS = 78.6  # FP32 FMA without packed FP32 (which this build compiles out)
 MALL_BYTES = 256 * 2 ** 20       # Infinity Cache (last-level cache in front of HBM)
 
 # Plain-ALU ceiling of the method's arithmetic (the competing bound of the diagonal path).
@@ -59,10 +59,6 @@ def alu_slots_per_element(p):
         per += 2 * TRANS_SLOTS
     return per
 
-
-# Backward ALU work in FP32 FLOP-equivalents (an FMA 2, a transcendental 8 = its four FMA slots),
-# reported against the packed FP32 peak (see backward_bench).
-TRANS = 8.0
 
 
 # source file of each scan kernel
@@ -231,13 +227,18 @@ def decode_bench(args, p, to_dev, dev):
 # and dt*A (1), dt*u*B (1), the recomputed state FMA (2), the adjoint FMA (2) and its decay
 # product (1), dC (1), dB (1), du (2), ddt (4: two FMAs), dA (2: multiply, FMA) = 25; per
 # element the forward's per-step terms (softplus, gate, D) and their derivatives (~2x).
-def bwd_flop_equiv_per_element(N, softplus, gate, scalar_decay=False):
-    # scalar decay: the exp and dt*A are per step, not per (t, n)
-    per = (16.0 * N + TRANS + 1.0 if scalar_decay else 25.0 * N) + 2 * 3.0
+def bwd_alu_slots_per_element(N, softplus, gate, scalar_decay=False):
+    """VALU issue slots per element of the backward's own operations (a transcendental = 4): per
+    (t, n) the recomputed state (exp, dt A, dt u B, the FMA: 7), the adjoint (its FMA and the
+    decay: 2) and the gradient terms (dC, dB, du, g h a, ddt, dA: 7), plus the readout of the
+    output before the gate when there is one; scalar decay takes the exp and dt A once per step.
+    Per element: du/ddt/dD/dbias (5), softplus and its derivative, silu and its derivative."""
+    per_tn = (11.0 if scalar_decay else 16.0) + (1.0 if gate else 0.0)
+    per = per_tn * N + (TRANS_SLOTS + 1.0 if scalar_decay else 0.0) + 5.0
     if softplus:
-        per += 2 * (2 * TRANS + 4.0)
+        per += (2 * TRANS_SLOTS + 4.0) + (2 * TRANS_SLOTS + 2.0)
     if gate:
-        per += 2 * (2 * TRANS + 3.0)
+        per += (2 * TRANS_SLOTS + 3.0) + (2 * TRANS_SLOTS + 5.0)
     return per
 
 
@@ -273,7 +274,10 @@ def backward_bench(args, p, to_dev, dev):
     wall = time.perf_counter() - t0
     per = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)])) * 1e-3
     E = p.batch * p.channels * p.length
-    flops = E * bwd_flop_equiv_per_element(p.nstate, p.softplus, p.gate, p.scalar_decay)
+    # FMA-equivalent flops: every VALU slot counted as one FMA (2 flops), against the unpacked
+    # FP32 FMA rate (packed FP32 is compiled out)
+    slots = bwd_alu_slots_per_element(p.nstate, p.softplus, p.gate, p.scalar_decay)
+    flops = 2.0 * E * slots
     ib = 2 if p.in_dtype == "bf16" else 4
     # reads u, z, dy (f32), delta, B, C; writes du, dz, ddelta (f32) and dB, dC (f32)
     nbytes = E * (ib * (2 if p.gate else 1) + 4 + 4 * (2 if p.gate else 1))
@@ -281,7 +285,7 @@ def backward_bench(args, p, to_dev, dev):
     nbytes += p.batch * p.groups * p.nstate * p.length * 2 * (ib + 4)
     tf = flops / per / 1e12
     P = p.channels // p.heads
-    matrix = p.scalar_decay and not p.gate and P % 64 == 0 and (p.channels // p.groups) % 64 == 0
+    matrix = p.scalar_decay and P % 64 == 0 and (p.channels // p.groups) % 64 == 0
     dominant = "ssdb_main_kernel" if matrix else "bwd_kernel"
     traffic = stored_traffic(dominant, args.workload, kernel_source_digest(dominant), mode="backward")
     out = {
@@ -291,9 +295,10 @@ def backward_bench(args, p, to_dev, dev):
         "config": {"workload": "backward, " + describe(p), "batch": p.batch, "channels": p.channels,
                    "seq_len": p.length, "nstate": p.nstate,
                    "kernel": dominant},
-        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP32_VECTOR_PEAK_TFLOPS, "traffic": traffic, "call_ms": per * 1e3,
-                     "flop_equiv_per_call": flops, "hbm_algorithmic_bytes_per_call": nbytes,
+        "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_VECTOR_UNPACKED_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP32_VECTOR_UNPACKED_TFLOPS, "traffic": traffic, "call_ms": per * 1e3,
+                     "valu_slots_per_element": slots, "flop_equiv_per_call": flops,
+                     "hbm_algorithmic_bytes_per_call": nbytes,
                      "hbm_achieved_GBps": nbytes / per / 1e9},
         "cpu_baseline": None,
     }
