@@ -210,8 +210,9 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * Scalar-decay calls whose heads and B/C groups are whole 64-channel slabs take the chunked
  * matrix form instead, whose workspace holds the state at the start of every 32-step chunk
  * (batch * channels * ceil(L / 32) * N' floats, N' = N rounded up to 32, 64 or 128) and C B^T
- * per chunk; with a gate that form first recomputes the output before the gate into the
- * workspace (batch * channels * L floats more).  Chain rule, with s(z) = z sigmoid(z) and
+ * per chunk.  With a gate, either form first recomputes the output before the gate into the
+ * workspace (batch * channels * L floats more) and takes dz and dy s(z) from it in a pass of its
+ * own.  Chain rule, with s(z) = z sigmoid(z) and
  * dy0 = dy s(z):  g_t = C_t dy0_t + exp(dt_{t+1} A) g_{t+1} (the gradient of h_t),
  * dC_t = dy0_t h_t,  dB_t = g_t dt_t u_t,  du_t = dy0_t D + sum_n g_t dt_t B_t,
  * ddt_t = sum_n g_t (h_{t-1} exp(dt_t A) A + B_t u_t),  dA = sum_t g_t h_{t-1} exp(dt_t A) dt_t,

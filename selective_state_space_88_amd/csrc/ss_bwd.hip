@@ -9,19 +9,20 @@
 // the gate s(z) = z sigmoid(z):
 //   dC_t += dy0_t h_t,  dB_t += g_t dt_t u_t,  du_t += g_t dt_t B_t,
 //   ddt_t += g_t (h_{t-1} a_t A + B_t u_t),  dA += g_t h_{t-1} a_t dt_t,
-// and per step dz_t = dy_t y0_t s'(z_t), du_t += dy0_t D, dD += dy0_t u_t,
-// ddelta_t = ddt_t sigmoid(x_t) (softplus'), dbias += ddelta_t.
+// and per step du_t += dy0_t D, dD += dy0_t u_t, ddelta_t = ddt_t sigmoid(x_t) (softplus'),
+// dbias += ddelta_t.  The gate itself (dz_t = dy_t y0_t s'(z_t) and dy0) is a pass of its own
+// between a forward recompute of y0 and this kernel (see launch_bwd).
 //
 // With heads (a step size, and optionally a scalar decay A_h, shared by a head's channels) the
 // per-head gradients ddelta, dbias, dA (and dD when D is per head) are summed over the head's
 // channels; with a scalar decay exp(dt A_h) is computed once per step for all N states.
 //
 // Mapping (as in the forward kernel): a wave owns one channel, lane j the K consecutive steps
-// t0 + jK .. t0 + jK + K - 1 of a window; states go by pairs.  Inside a window both recurrences
+// t0 + jK .. t0 + jK + K - 1 of a window; states go one at a time.  Inside a window both recurrences
 // are scans of affine maps over the lanes: the states forward (x -> a x + b composed left to
 // right), the adjoint backward (composed right to left); each lane runs its K steps from zero,
 // the lanes' maps are combined by a shuffle scan, and each lane re-runs its steps from its true
-// incoming value.  A block holds 4 channels of one (batch, B/C group): their dB and dC
+// incoming value.  A block holds 8 channels of one (batch, B/C group): their dB and dC
 // contributions are summed through LDS before one atomic add per (state, step).
 #include <algorithm>
 
@@ -36,6 +37,7 @@ constexpr int kBW = 64 * kBK;        // steps per window
 constexpr int kBWaves = 4;           // channels (rows) per block of the checkpoint kernel
 constexpr int kMWaves = 8;           // channels per block of the backward kernel (of one B/C group)
 constexpr int kBMaxPairs = 64;       // N <= 128
+constexpr int kBwdSP = 1;            // states per group of the backward kernel's state loop
 
 // DPP move of v with control CTRL on the rows in ROWMASK; lanes with no source (or in masked
 // rows) keep `old`
@@ -213,15 +215,20 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
   }
 }
 
-template <typename TIn, typename TDy, bool GATE, bool SCALAR>
-__global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int64_t nwin, const float* ckpt) {
-  __shared__ float gcar[kMWaves][kBMaxPairs][2];      // adjoint carried into the window from the right
+// The backward of the ungated scan (a gated layer reaches it through launch_bwd with dy0 = dy
+// s(z) as its upstream gradient).  SP: states per group (1 or 2), the unit of the state loop (P
+// groups); one state at a time keeps the kernel within 128 VGPRs, i.e. two 8-wave blocks (four
+// waves per SIMD) per CU.
+template <typename TIn, typename TDy, bool SCALAR, int SP>
+__global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP == 1 ? 4 : 1))) void bwd_kernel(
+    BwdArgs p, int P, int64_t nwin, const float* ckpt) {
+  __shared__ float gcar[kMWaves][2 * kBMaxPairs];     // adjoint carried into the window from the right
   __shared__ float dAl[kMWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
-  // dB (2 states), dC (2 states) of the window's steps, step-major ([lane][k] = step lane K + k)
-  __shared__ __attribute__((aligned(16))) float red[kMWaves][4][kBW];
-  // B (2 states) and C (2 states) of a pair's window, shared by the block's channels; two
-  // buffers: the next pair's rows are loaded while this pair runs
-  __shared__ __attribute__((aligned(16))) float bcs[2][4][kBW];
+  // dB (SP states), dC (SP states) of the window's steps, step-major ([lane][k] = step lane K + k)
+  __shared__ __attribute__((aligned(16))) float red[kMWaves][2 * SP][kBW];
+  // B (SP states) and C (SP states) of a group's window, shared by the block's channels; two
+  // buffers: the next group's rows are loaded while this group runs
+  __shared__ __attribute__((aligned(16))) float bcs[2][2 * SP][kBW];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // blocks of 8 channels of one group; when the group's channels are 4 mod 8, the last block's
@@ -238,7 +245,6 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
   const int64_t L = p.L;
   const TIn* ur = static_cast<const TIn*>(p.u) + b * p.u_sb + d * p.u_sd;
   const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
-  const TIn* zr = GATE ? static_cast<const TIn*>(p.z) + b * p.z_sb + d * p.z_sd : nullptr;
   const TDy* dyr = static_cast<const TDy*>(p.dy) + b * p.dy_sb + d * p.dy_sd;
   const TIn* Bg = static_cast<const TIn*>(p.B) + b * p.B_sb + g * p.B_sg;
   const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
@@ -247,21 +253,21 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
   const float bias = p.bias ? p.bias[hd] : 0.f;
   const float Dd = p.D ? p.D[p.d_per_head ? hd : d] : 0.f;
   for (int i = lane; i < 2 * kBMaxPairs; i += 64) {
-    gcar[wave][i / 2][i % 2] = 0.f;
+    gcar[wave][i] = 0.f;
     dAl[wave][i] = 0.f;
   }
   float dDacc = 0.f, dbacc = 0.f;
-  // thread t stages row t / 64 (B of state 2 pp, of 2 pp + 1, C of 2 pp, of 2 pp + 1), the steps
-  // of lane t % 64; rows past N and steps past L are zero
+  // thread t stages row t / 64 (B of states SP pp .. SP pp + SP - 1, then C of the same), the
+  // steps of lane t % 64; rows past N and steps past L are zero
   const int srow = threadIdx.x >> 6, sseg = threadIdx.x & 63;
   auto bc_load = [&](int64_t ww, int pq, float (&v)[kBK]) {
-    const int n = 2 * pq + (srow & 1);
-    const bool nv = n < N && srow < 4;
-    const TIn* src = srow < 2 ? Bg + (nv ? n : 0) * p.B_sn : Cg + (nv ? n : 0) * p.C_sn;
+    const int n = SP * pq + (srow % SP);
+    const bool nv = n < N && srow < 2 * SP;
+    const TIn* src = srow < SP ? Bg + (nv ? n : 0) * p.B_sn : Cg + (nv ? n : 0) * p.C_sn;
     load_seg<kBK>(src, ww * kBW + (int64_t)kBK * sseg, nv ? L : 0, p.vec, v);
   };
   auto bc_store = [&](int bf, const float (&v)[kBK]) {
-    if (srow >= 4) return;   // four rows, one per wave of the first four
+    if (srow >= 2 * SP) return;   // 2 SP rows, one per wave of the first 2 SP
     float* dst = &bcs[bf][srow][kBK * sseg];
     *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -276,24 +282,23 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
 
   for (int64_t w = nwin - 1; w >= 0; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
-    float dt[kBK], uu[kBK], wv[kBK], dy0[kBK], y0[kBK], du[kBK], ddt[kBK], sg[kBK], dyv[kBK], zv[kBK], dv[kBK];
+    // (u and delta are loaded again at the window's end rather than kept across the state loop)
+    float dt[kBK], wv[kBK], dy0[kBK], du[kBK], ddt[kBK];
     float sdt = 0.f;   // the lane's steps' total step size
-    load_seg<kBK>(dr, t0, L, p.vec, dv);
-    load_seg<kBK>(ur, t0, L, p.vec, uu);
-    load_seg<kBK>(dyr, t0, L, p.vec, dyv);
-    if constexpr (GATE) load_seg<kBK>(zr, t0, L, p.vec, zv);
+    {
+      float dv[kBK], uu[kBK];
+      load_seg<kBK>(dr, t0, L, p.vec, dv);
+      load_seg<kBK>(ur, t0, L, p.vec, uu);
+#pragma unroll
+      for (int k = 0; k < kBK; ++k) {
+        const float x = dv[k] + bias;
+        dt[k] = t0 + k < L ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+        wv[k] = dt[k] * uu[k];
+      }
+    }
+    load_seg<kBK>(dyr, t0, L, p.vec, dy0);
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
-      const bool ok = t0 + k < L;
-      const float x = dv[k] + bias;
-      dt[k] = ok ? (p.softplus ? softplus_fast(x) : x) : 0.f;
-      // softplus'(x) = sigmoid(x)
-      sg[k] = p.softplus ? 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
-      wv[k] = dt[k] * uu[k];
-      float gz = 1.f;
-      if constexpr (GATE) gz = silu_fast(zv[k]);
-      dy0[k] = dyv[k] * gz;
-      y0[k] = Dd * uu[k];
       du[k] = 0.f;   // here: sum over the states of g_t B_t (du and ddt take it once per step below)
       ddt[k] = 0.f;
       sdt += dt[k];
@@ -310,11 +315,11 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
       const bool more = pp + 1 < P || w > 0;
       float nbc[kBK];
       if (more) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
-      float rB[2][kBK], rC[2][kBK];
-      float dAp[2];
+      float rB[SP][kBK], rC[SP][kBK];
+      float dAp[SP];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int n = 2 * pp + s;
+      for (int s = 0; s < SP; ++s) {
+        const int n = SP * pp + s;
         const bool nv = n < N;
         const float An = SCALAR ? p.A[hd] : (nv ? p.A[d * p.A_sd + n] : 0.f);
         const float A2 = An * kLog2e;
@@ -322,8 +327,8 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
         {
           const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bcs[buf][s][kBK * lane]);
           const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bcs[buf][s][kBK * lane + 4]);
-          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&bcs[buf][2 + s][kBK * lane]);
-          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&bcs[buf][2 + s][kBK * lane + 4]);
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(&bcs[buf][SP + s][kBK * lane]);
+          const f32x4 c1 = *reinterpret_cast<const f32x4*>(&bcs[buf][SP + s][kBK * lane + 4]);
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             bv[k] = b0[k];
@@ -347,7 +352,6 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
 #pragma unroll
         for (int k = 0; k < kBK; ++k) {
           hs[k + 1] = fmaf(av[k], hs[k], wv[k] * bv[k]);
-          y0[k] = fmaf(cv[k], hs[k + 1], y0[k]);
         }
         // adjoint: the lane's steps from zero (right to left), the scan, then from the value
         // carried in from the right
@@ -358,7 +362,7 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
         scan_down_fused(Ar, Br2, lane);
         float Ad = Ar, Bd = Br2;
         shift_down(Ad, Bd);
-        const float Xw = gcar[wave][pp][s];
+        const float Xw = gcar[wave][n];
         c = fmaf(Ad, Xw, Bd);
         float dAs = 0.f;
 #pragma unroll
@@ -374,39 +378,42 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
         }
         // the adjoint carried into the previous window: lane 0's value after its first step
         const float cl = readlane_f(c, 0);
-        if (lane == 0) gcar[wave][pp][s] = cl;
+        if (lane == 0) gcar[wave][n] = cl;
         dAp[s] = dAs;
       }
       // dA of the pair: summed over the wave's lanes into the wave's partial sums
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int s = 0; s < SP; ++s) {
         const float v = wave_sum(dAp[s]);
-        if (lane == 0 && valid && 2 * pp + s < N) dAl[wave][SCALAR ? 0 : 2 * pp + s] += v;
+        if (lane == 0 && valid && SP * pp + s < N) dAl[wave][SCALAR ? 0 : SP * pp + s] += v;
       }
       // dB, dC of the pair: summed over the block's 8 channels, then one atomic add per step;
       // consecutive lanes add to consecutive steps, so each wave's adds cover two cache lines
       if (!valid) {
 #pragma unroll
-        for (int k = 0; k < kBK; ++k) rB[0][k] = rB[1][k] = rC[0][k] = rC[1][k] = 0.f;
+        for (int s = 0; s < SP; ++s)
+#pragma unroll
+          for (int k = 0; k < kBK; ++k) rB[s][k] = rC[s][k] = 0.f;
       }
 #pragma unroll
-      for (int k = 0; k < kBK; k += 4) {
-        *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{rB[0][k], rB[0][k + 1], rB[0][k + 2], rB[0][k + 3]};
-        *reinterpret_cast<f32x4*>(&red[wave][1][lane * kBK + k]) = f32x4{rB[1][k], rB[1][k + 1], rB[1][k + 2], rB[1][k + 3]};
-        *reinterpret_cast<f32x4*>(&red[wave][2][lane * kBK + k]) = f32x4{rC[0][k], rC[0][k + 1], rC[0][k + 2], rC[0][k + 3]};
-        *reinterpret_cast<f32x4*>(&red[wave][3][lane * kBK + k]) = f32x4{rC[1][k], rC[1][k + 1], rC[1][k + 2], rC[1][k + 3]};
-      }
+      for (int s = 0; s < SP; ++s)
+#pragma unroll
+        for (int k = 0; k < kBK; k += 4) {
+          *reinterpret_cast<f32x4*>(&red[wave][s][lane * kBK + k]) = f32x4{rB[s][k], rB[s][k + 1], rB[s][k + 2], rB[s][k + 3]};
+          *reinterpret_cast<f32x4*>(&red[wave][SP + s][lane * kBK + k]) =
+              f32x4{rC[s][k], rC[s][k + 1], rC[s][k + 2], rC[s][k + 3]};
+        }
       if (more) bc_store(buf ^ 1, nbc);
       __syncthreads();
-      for (int i = threadIdx.x; i < 4 * kBW; i += 64 * kMWaves) {
+      for (int i = threadIdx.x; i < 2 * SP * kBW; i += 64 * kMWaves) {
         const int which = i / kBW, r = i % kBW;
-        const int n = 2 * pp + (which & 1);
+        const int n = SP * pp + (which % SP);
         const int64_t t = w * kBW + r;
         if (n < N && t < L) {
           float v = 0.f;
 #pragma unroll
           for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[wv2][which][r];
-          float* dst = (which < 2 ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
+          float* dst = (which < SP ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
           atomicAdd(dst, v);
         }
       }
@@ -416,14 +423,22 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
     // per-step outputs of the window
     float* dur = p.du + b * p.du_sb + d * p.du_sd;
     float* ddr = p.ddelta + b * p.dd_sb + hd * p.dd_sh;
-    float dxs[kBK];
+    float dxs[kBK], uu[kBK];
+    {
+      float dv[kBK];
+      load_seg<kBK>(dr, t0, L, p.vec, dv);
+      load_seg<kBK>(ur, t0, L, p.vec, uu);
 #pragma unroll
-    for (int k = 0; k < kBK; ++k) {
-      // with gB = sum_n g B: du = dt gB + D dy0 and ddt += u gB
-      const float gB = du[k];
-      du[k] = fmaf(dt[k], gB, dy0[k] * Dd);
-      ddt[k] = fmaf(uu[k], gB, ddt[k]);
-      dxs[k] = (valid && t0 + k < L) ? ddt[k] * sg[k] : 0.f;
+      for (int k = 0; k < kBK; ++k) {
+        // softplus'(x) = sigmoid(x)
+        const float x = dv[k] + bias;
+        const float sg = p.softplus ? 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.f;
+        // with gB = sum_n g B: du = dt gB + D dy0 and ddt += u gB
+        const float gB = du[k];
+        du[k] = fmaf(dt[k], gB, dy0[k] * Dd);
+        ddt[k] = fmaf(uu[k], gB, ddt[k]);
+        dxs[k] = (valid && t0 + k < L) ? ddt[k] * sg : 0.f;
+      }
     }
     if (p.chan_per_head % kMWaves == 0 && p.chan_per_group % kMWaves == 0) {
       // the block's 8 channels share the head: summed through LDS, one atomic add per step
@@ -455,11 +470,6 @@ __global__ __launch_bounds__(64 * kMWaves) void bwd_kernel(BwdArgs p, int P, int
         dur[t0 + k] = du[k];
         dbacc += dx;
         dDacc = fmaf(dy0[k], uu[k], dDacc);
-        if constexpr (GATE) {
-          // s'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
-          const float sgz = 1.f / (1.f + __builtin_amdgcn_exp2f(-zv[k] * kLog2e));
-          p.dz[b * p.dz_sb + d * p.dz_sd + t0 + k] = dyv[k] * y0[k] * sgz * fmaf(zv[k], 1.f - sgz, 1.f);
-        }
       }
     }
   }
@@ -487,9 +497,9 @@ __global__ __launch_bounds__(256) void zero4_kernel(float* __restrict__ p, int64
   }
 }
 
-// The gate of a layer whose ungated backward is the matrix form: dz = dy y0 s'(z), and y0 (the
-// output before the gate, recomputed by the forward into `y0`, [batch, channels, L] contiguous)
-// replaced in place by dy0 = dy s(z), the gradient the ungated backward takes.
+// The gate's backward: dz = dy y0 s'(z), and y0 (the output before the gate, recomputed by the
+// forward into `y0`, [batch, channels, L] contiguous) replaced in place by dy0 = dy s(z), the
+// gradient the ungated backward takes.
 template <typename TIn, typename TDy>
 __global__ __launch_bounds__(256) void gate_bwd_kernel(BwdArgs p, float* __restrict__ y0) {
   const int64_t total = p.batch * p.channels * p.L;
@@ -532,24 +542,20 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves)));
   const dim3 mblock(64 * kMWaves);
   const float* ck = ws;
-#define SS_BWD(GT, SC) hipLaunchKernelGGL((bwd_kernel<TIn, TDy, GT, SC>), grid, mblock, 0, s, a, P, nwin, ck)
-  if (a.z) {
-    if (a.scalar) SS_BWD(true, true); else SS_BWD(true, false);
-  } else {
-    if (a.scalar) SS_BWD(false, true); else SS_BWD(false, false);
-  }
+#define SS_BWD(SC) \
+  hipLaunchKernelGGL((bwd_kernel<TIn, TDy, SC, kBwdSP>), grid, mblock, 0, s, a, (a.N + kBwdSP - 1) / kBwdSP, nwin, ck)
+  // (a gated call arrives here ungated: launch_bwd composes the gate around this kernel)
+  if (a.scalar) SS_BWD(true); else SS_BWD(false);
 #undef SS_BWD
   return hipGetLastError();
 }
 
-// A gated layer whose ungated backward is the matrix form (scalar decay, heads and groups in
-// whole 64-channel slabs) composes three steps on one workspace: the forward without the gate
-// recomputes y0 = C h + D u (the output before the gate) into f32 rows; an elementwise kernel
-// writes dz and turns y0 into dy0 = dy s(z); the ungated matrix-form backward runs on dy0.
-bool gated_matrix_path(const BwdArgs& a) {
-  BwdArgs b = a;
-  b.z = nullptr;
-  return a.z && ssd_bwd_path(b);
+// A gated layer composes three steps on one workspace: the forward without the gate recomputes
+// y0 = C h + D u (the output before the gate) into f32 rows; an elementwise kernel writes dz and
+// turns y0 into dy0 = dy s(z); the ungated backward (matrix form or per channel) runs on dy0.
+// The gate multiplies C h + D u as a whole, so dy0 is the ungated layer's whole upstream gradient.
+bool gated_path(const BwdArgs& a) {
+  return a.z != nullptr;
 }
 
 constexpr int64_t round64(int64_t n) { return (n + 63) / 64 * 64; }
@@ -591,34 +597,36 @@ ScanArgs ungated_forward(const BwdArgs& a, float* y0) {
   f.C_sn = a.C_sn;
   f.y_sb = a.channels * a.L;
   f.y_sd = a.L;
-  f.A_sd = 0;   // one decay per head
+  f.A_sd = a.scalar ? 0 : a.A_sd;
   return f;
 }
 
-int64_t forward_ws_floats(const ScanArgs& f) {
+// diagonal decay (A [channels, N]) takes no workspace
+int64_t forward_ws_floats(const ScanArgs& f, bool scalar) {
+  if (!scalar) return 0;
   return ssd_path(f) ? (ssd_workspace_bytes(f) + 3) / 4 : scalar_workspace_floats(f);
 }
 
 }  // namespace
 
 int64_t bwd_workspace_floats(const BwdArgs& a) {
-  if (gated_matrix_path(a)) {
+  if (gated_path(a)) {
     BwdArgs b = a;
     b.z = nullptr;
     const int64_t ny = round64(a.batch * a.channels * a.L);
-    return ny + round64(forward_ws_floats(ungated_forward(a, nullptr))) + ssd_bwd_workspace_floats(b);
+    return ny + round64(forward_ws_floats(ungated_forward(a, nullptr), a.scalar)) + bwd_workspace_floats(b);
   }
   if (ssd_bwd_path(a)) return ssd_bwd_workspace_floats(a);
   return a.batch * a.channels * ((a.L + kBW - 1) / kBW) * a.N;
 }
 
 hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
-  if (gated_matrix_path(a)) {
+  if (gated_path(a)) {
     float* y0 = ws;
     float* fws = y0 + round64(a.batch * a.channels * a.L);
     const ScanArgs f = ungated_forward(a, y0);
-    float* bws = fws + round64(forward_ws_floats(f));
-    hipError_t e = ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
+    float* bws = fws + round64(forward_ws_floats(f, a.scalar));
+    hipError_t e = !a.scalar ? launch_diag(f, s) : ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
     if (e != hipSuccess) return e;
     const int64_t total = a.batch * a.channels * a.L;
     const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 16384));
