@@ -537,8 +537,10 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   zero4(a.dC, a.batch, a.groups, a.N, a.L, a.dC_sb, a.dC_sg, a.dC_sn);
   if (ssd_bwd_path(a)) return launch_ssd_bwd(a, ws, s);
   const dim3 cgrid((unsigned)((rows + kBWaves - 1) / kBWaves)), block(64 * kBWaves);
-  if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
-  else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
+  if (!a.ckpt_ready) {
+    if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
+    else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
+  }
   const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves)));
   const dim3 mblock(64 * kMWaves);
   const float* ck = ws;
@@ -624,8 +626,17 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
   if (gated_path(a)) {
     float* y0 = ws;
     float* fws = y0 + round64(a.batch * a.channels * a.L);
-    const ScanArgs f = ungated_forward(a, y0);
+    ScanArgs f = ungated_forward(a, y0);
     float* bws = fws + round64(forward_ws_floats(f, a.scalar));
+    // a diagonal decay's forward also stores the per-channel backward's checkpoints (at the
+    // start of its workspace), which then needs no checkpoint pass of its own
+    BwdArgs b = a;
+    b.z = nullptr;
+    const bool fwd_ckpt = !a.scalar && !ssd_bwd_path(b);
+    if (fwd_ckpt) {
+      f.ckpt = bws;
+      f.ckpt_nwin = (a.L + kBW - 1) / kBW;
+    }
     hipError_t e = !a.scalar ? launch_diag(f, s) : ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
     if (e != hipSuccess) return e;
     const int64_t total = a.batch * a.channels * a.L;
@@ -637,9 +648,8 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
       if (a.dy_bf16) SS_GATE(float, bf16_t); else SS_GATE(float, float);
     }
 #undef SS_GATE
-    BwdArgs b = a;
-    b.z = nullptr;
     b.dz = nullptr;
+    b.ckpt_ready = fwd_ckpt ? 1 : 0;
     b.dy = y0;
     b.dy_bf16 = 0;
     b.dy_sb = a.channels * a.L;

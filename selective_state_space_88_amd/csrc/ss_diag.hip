@@ -466,11 +466,13 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
 //   kZOH   zero-order-hold input coefficient (exp(dt A) - 1) / A instead of dt;
 //   kTRAP  exponential-trapezoidal rule: the scan runs the state k = h + e/2, which obeys the
 //          Euler recurrence k_t = a_t k_{t-1} + e_t, and y reads C (k - e/2).
-constexpr int kSIO = 1, kZOH = 2, kTRAP = 4;
+// kCKPT: also store the backward's checkpoints (ScanArgs::ckpt); only with none of the others
+constexpr int kSIO = 1, kZOH = 2, kTRAP = 4, kCKPT = 8;
 template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, int MODE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROWS == 2 && sizeof(TIn) == 2 ? 3 : 2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
   constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
+  constexpr bool CKPT = (MODE & kCKPT) != 0;
   constexpr StageMode SMODE = stage_mode<TIn, VEC>();
   constexpr int LPC = 64 / ROWS;                     // lanes per channel row
   constexpr int W = win_steps<ROWS>();               // steps per window of a channel
@@ -731,6 +733,12 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
                                                                                         lds_addr(mypar + pp), pq);
       }
       const float4 pv = make_float4(pq[0], pq[1], pq[2], pq[3]);
+      // the backward's checkpoints: the carried states are the states at the window's start
+      if (CKPT && live && jl == 0) {
+        float* ck = p.ckpt + ((b * p.channels + d) * p.ckpt_nwin + w * (W / 512)) * N + 2 * pp;
+        ck[0] = pv.z;
+        if (2 * pp + 1 < N) ck[1] = pv.w;
+      }
       if constexpr (SPLIT) {
         // the two states one after the other (the registers of one state's K decays and inputs
         // are reused by the next)
@@ -811,6 +819,14 @@ __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROW
                             12 * W + 2 * QS, 12 * W + 3 * QS>(sa0, sb0, sa1, sb1, lbase, cq);
         h0 = fmaf(sa0, pv.z, sb0);
         h1 = fmaf(sa1, pv.w, sb1);
+        if constexpr (CKPT && W == 1024) {
+          // (64-lane rows: lane 32's incoming states are the states 512 steps into the window)
+          if (live && jl == 32 && 2 * w + 1 < p.ckpt_nwin) {
+            float* ck = p.ckpt + ((b * p.channels + d) * p.ckpt_nwin + 2 * w + 1) * N + 2 * pp;
+            ck[0] = h0;
+            if (2 * pp + 1 < N) ck[1] = h1;
+          }
+        }
 #pragma unroll
         for (int j = 0; j < kK; ++j) {
           h0 = fmaf(av0[j], h0, bv0[j]);
@@ -1061,6 +1077,7 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
     ScanArgs p, int64_t nwin, int64_t blocks_per_bg, int skew, int nsteps, uint32_t spin_limit) {
   using TIn = bf16_t;
   constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
+  constexpr bool CKPT = (MODE & kCKPT) != 0;
   constexpr int W = 64 * kK;                         // steps per window
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
@@ -1189,7 +1206,8 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
 
   // one state of the step: lane pass from B words bw, the row's scan from the carried state, C
   // words from LDS (landed), the readout into yv; returns the window's end state (lane 63)
-  auto one_state = [&](const uint32_t (&bw)[8], float An, float carry, uint32_t cwaddr) {
+  // (ck: this state's checkpoint 512 steps into the window, or nullptr)
+  auto one_state = [&](const uint32_t (&bw)[8], float An, float carry, uint32_t cwaddr, float* ck) {
     float av[kK], bv[kK];
 #pragma unroll
     for (int j = 0; j < kK; ++j) av[j] = __builtin_amdgcn_exp2f(dt[j] * An);
@@ -1212,6 +1230,8 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
     // lane aggregate (decay over the lane's steps, state from zero), then the row's scan from
     // the carried state
     h = row_incoming_state(__builtin_amdgcn_exp2f(sdt * An), h, carry);
+    // (lane 32's incoming state is the state 512 steps into the window)
+    if (CKPT && ck && lane == 32) *ck = h;
     u32x4 c0, c1;
     c_reads(cwaddr, c0, c1);
     const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
@@ -1302,15 +1322,25 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
       // this step's C has landed once at most what was issued after it (z, the u and delta
       // copies, the next step's B) is in flight
       wait_vmcnt(issued);
+      // the backward's checkpoints: the window's start (the carried states) and 512 steps in
+      float* ck0 = nullptr;
+      if (CKPT && live) {
+        float* ck = p.ckpt + ((b * p.channels + d) * p.ckpt_nwin + 2 * w) * N + n0;
+        if (lane == 0) {
+          ck[0] = carry[0];
+          if (two) ck[1] = carry[1];
+        }
+        if (2 * w + 1 < p.ckpt_nwin) ck0 = ck + N;
+      }
       {
         const uint32_t bw[8] = {bq[0].x, bq[0].y, bq[0].z, bq[0].w, bq[1].x, bq[1].y, bq[1].z, bq[1].w};
-        const float h = one_state(bw, An[0], carry[0], ccb);
+        const float h = one_state(bw, An[0], carry[0], ccb, ck0);
         // the window's end state carries state n into the next window (the next slot)
         if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)n0, h);
       }
       if (two) {
         const uint32_t bw[8] = {bq[2].x, bq[2].y, bq[2].z, bq[2].w, bq[3].x, bq[3].y, bq[3].z, bq[3].w};
-        const float h = one_state(bw, An[1], carry[1], ccb + 2048u);
+        const float h = one_state(bw, An[1], carry[1], ccb + 2048u, ck0 ? ck0 + 1 : nullptr);
         if (lane == 63) lds_write_f32(pc0 + 4u * (uint32_t)(n0 + 1), h);
       }
 
@@ -1424,7 +1454,8 @@ hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
   // force the failure path
   uint32_t spin_limit = 1u << 24;
   if (const char* e = getenv("SS_SPIN_LIMIT")) spin_limit = (uint32_t)strtoul(e, nullptr, 10);
-  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0);
+  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0) |
+                   (a.ckpt ? kCKPT : 0);
 #define SS_M(G, M)                                                                                          \
   case M:                                                                                                   \
     hipLaunchKernelGGL((diag_slots_kernel<TOut, G, M>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,  \
@@ -1435,7 +1466,12 @@ hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
     SS_M(G, 0) SS_M(G, kSIO) SS_M(G, kSIO | kZOH) SS_M(G, kSIO | kTRAP) SS_M(G, kSIO | kZOH | kTRAP)        \
     default: return hipErrorInvalidValue;                                                                   \
   }
-  if (a.z) {
+  if (mode == kCKPT) {
+    // (the backward's recompute: no gate, f32 y)
+    if (a.z || sizeof(TOut) != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kCKPT>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,
+                       (int)steps, spin_limit);
+  } else if (a.z) {
     SS_LAUNCH(true);
   } else {
     SS_LAUNCH(false);
@@ -1479,7 +1515,8 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
   const size_t par_bytes = sizeof(float4) * kWaves * ROWS * P;   // the per-pair parameters
   // the plain forward, or (state in/out checked at run time) with state in/out, zero-order hold
   // and/or the trapezoidal rule
-  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0);
+  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0) |
+                   (a.ckpt ? kCKPT : 0);
 #define SS_M(G, V, M)                                                                                        \
   case M:                                                                                                    \
     hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, G, V, ROWS, M>), grid, block, par_bytes, s, a, P, nwin, blocks_per_bg); \
@@ -1490,7 +1527,12 @@ hipError_t launch_r(const ScanArgs& a, hipStream_t s) {
     SS_M(G, V, kSIO | kZOH | kTRAP)                                                                          \
     default: return hipErrorInvalidValue;                                                                    \
   }
-  if (a.z) {
+  if (mode == kCKPT) {
+    // (the backward's recompute: no gate, f32 y)
+    if (a.z || sizeof(TOut) != 4) return hipErrorInvalidValue;
+    if (vec) hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, false, true, ROWS, kCKPT>), grid, block, par_bytes, s, a, P, nwin, blocks_per_bg);
+    else hipLaunchKernelGGL((diag_fwd_kernel<TIn, TOut, false, false, ROWS, kCKPT>), grid, block, par_bytes, s, a, P, nwin, blocks_per_bg);
+  } else if (a.z) {
     if (vec) { SS_LAUNCH(true, true); } else { SS_LAUNCH(true, false); }
   } else {
     if (vec) { SS_LAUNCH(false, true); } else { SS_LAUNCH(false, false); }

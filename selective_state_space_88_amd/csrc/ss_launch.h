@@ -33,6 +33,11 @@ struct ScanArgs {
   const float* h_init;    // nullptr: the state starts at zero
   float* h_final;         // nullptr: not written
   int64_t hi_sb, hi_sd, hf_sb, hf_sd;
+  // diagonal decay only, for the backward: when set, the state at the start of every 512 steps
+  // (checkpoint c of (b, d) at ckpt[((b channels + d) ckpt_nwin + c) N + n], ckpt_nwin =
+  // ceil(L / 512)), as the backward's checkpoint pass would store it
+  float* ckpt;
+  int64_t ckpt_nwin;
 };
 
 // Arguments of one decoding step (L = 1), already validated.  Strides in elements.
@@ -83,6 +88,7 @@ struct BwdArgs {
   int32_t d_per_head;     // D (and dD) indexed by head
   int32_t softplus, in_bf16, dy_bf16;
   int32_t vec;            // every input time row (and dy's) is 16-byte aligned
+  int32_t ckpt_ready;     // the per-channel path's checkpoints are already in the workspace
   int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, A_sd, dy_sb, dy_sd;
   int64_t du_sb, du_sd, dd_sb, dd_sh, dA_sd, dB_sb, dB_sg, dB_sn, dC_sb, dC_sg, dC_sn, dz_sb, dz_sd;
 };

@@ -156,6 +156,19 @@ def test_gated_matrix_backward(case):
     check_bwd(GATED_MATRIX_CASES[case](), "gated matrix " + case)
 
 
+@pytest.mark.parametrize("case", ["slots", "one channel per wave", "two channels per wave"])
+def test_gated_backward_checkpoints_from_the_forward(case):
+    """A gated diagonal layer's backward takes its checkpoints (the state every 512 steps) from
+    the forward that recomputes the output before the gate: from the window-slot kernel (few
+    rows, at least three 1024-step windows; a partial last window), from one channel per wave
+    (1024-step windows: the window's start and 512 steps in) and from two channels per wave
+    (512-step windows)."""
+    p = {"slots": lambda: inputs.random_problem(790, 1, 8, 4 * 1024 + 264, 16, gate=True),
+         "one channel per wave": lambda: inputs.random_problem(791, 2, 8, 2048 + 520, 12, gate=True, in_dtype="f32"),
+         "two channels per wave": lambda: inputs.random_problem(792, 1, 4608, 1024 + 96, 6, gate=True)}[case]()
+    check_bwd(p, "gated checkpoints from the forward: " + case)
+
+
 def test_gated_matrix_backward_bf16_dy():
     torch = torch_dev()
     check_bwd(inputs.random_problem(786, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=True),
