@@ -220,6 +220,77 @@ def random_problem(seed: int, batch: int, channels: int, length: int, nstate: in
                    meta=dict(seed=seed))
 
 
+def device_problem(seed: int, batch: int, channels: int, length: int, nstate: int, *,
+                   heads: Optional[int] = None, groups: int = 1, scalar_decay: bool = False,
+                   gate: bool = True, dt: tuple = (1e-4, 1e-2), bc_scale: Optional[float] = None,
+                   device="cuda", rows_per_draw: int = 32):
+    """A bf16 problem too large to draw on the host (more than 2^31 elements), drawn on `device`.
+
+    u, delta_raw, z ~ N(0, 1) and B, C ~ N(0, 1) bc_scale (default 1/sqrt(N)) come from torch's
+    generator on the device seeded with `seed`, drawn in that order as float32, `rows_per_draw`
+    time rows at a time, and rounded to bf16 (round to nearest even).  The small parameters come
+    from ``numpy.random.default_rng(seed)`` as in the workloads: A[d, n] = -(n + 1) (or A[h] =
+    -U(1, 16) per head with scalar decay), D ~ N(0, 1) per channel (per head with scalar
+    decay), delta_bias = inv_softplus(dt) with dt log-uniform in ``dt``, one per head.
+
+    Returns (tensors, p): the device tensors by argument name, and a Problem holding the small
+    parameters (its per-step arrays are None; ``device_row`` copies rows back for the oracle).
+    """
+    import torch
+
+    H = channels if heads is None else heads
+    Bt, Dc, L, N, G = batch, channels, length, nstate, groups
+    scale = (1.0 / np.sqrt(N)) if bc_scale is None else bc_scale
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+
+    def draw(shape, sc):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = out.view(-1, shape[-1])
+        for r in range(0, flat.shape[0], rows_per_draw):
+            x = torch.randn((min(rows_per_draw, flat.shape[0] - r), shape[-1]), generator=gen, device=device,
+                            dtype=torch.float32)
+            flat[r:r + x.shape[0]] = (x * sc if sc != 1.0 else x).to(torch.bfloat16)
+        return out
+
+    t = dict(u=draw((Bt, Dc, L), 1.0), delta=draw((Bt, H, L), 1.0), z=draw((Bt, Dc, L), 1.0) if gate else None)
+    t["B"] = draw((Bt, G, N, L), scale)
+    t["C"] = draw((Bt, G, N, L), scale)
+    rng = np.random.default_rng(seed)
+    dts = np.exp(rng.uniform(np.log(dt[0]), np.log(dt[1]), size=H))
+    bias = np.log(np.expm1(dts)).astype(np.float32)
+    Dv = rng.standard_normal(H if scalar_decay else Dc, dtype=np.float32)
+    if scalar_decay:
+        A = (-rng.uniform(1.0, 16.0, size=H)).astype(np.float32)
+    else:
+        A = np.tile(-np.arange(1, N + 1, dtype=np.float32), (Dc, 1))
+    t.update(A=torch.from_numpy(A).to(device), D=torch.from_numpy(Dv).to(device),
+             delta_bias=torch.from_numpy(bias).to(device))
+    p = Problem(name="device", batch=Bt, channels=Dc, length=L, nstate=N, groups=G, heads=H, in_dtype="bf16",
+                u=None, delta=None, A=A, B=None, C=None, D=Dv, z=None, delta_bias=bias, softplus=True,
+                scalar_decay=scalar_decay, meta=dict(seed=seed, device_drawn=True))
+    return t, p
+
+
+def device_row(t: dict, p: Problem, b: int, d: int) -> Problem:
+    """Row (b, d) of a device-drawn problem as a one-channel host Problem (the same bf16 bits)."""
+    import torch
+
+    def bits(x):
+        return x.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    h = d // (p.channels // p.heads)
+    g = d // (p.channels // p.groups)
+    one = lambda x: None if x is None else bits(x[b:b + 1, d:d + 1])
+    A = p.A[h:h + 1] if p.scalar_decay else p.A[d:d + 1]
+    Dv = p.D[h:h + 1] if p.scalar_decay else p.D[d:d + 1]
+    return Problem(name="device row", batch=1, channels=1, length=p.length, nstate=p.nstate, groups=1, heads=1,
+                   in_dtype="bf16", u=one(t["u"]), delta=bits(t["delta"][b:b + 1, h:h + 1]),
+                   A=np.ascontiguousarray(A), B=bits(t["B"][b:b + 1, g:g + 1]), C=bits(t["C"][b:b + 1, g:g + 1]),
+                   D=np.ascontiguousarray(Dv), z=one(t["z"]), delta_bias=np.ascontiguousarray(p.delta_bias[h:h + 1]),
+                   softplus=True, scalar_decay=p.scalar_decay, meta=dict(p.meta, row=(b, d)))
+
+
 def random_state(seed: int, batch: int, channels: int, nstate: int, scale: float = 1.0) -> np.ndarray:
     """A seeded state h [batch, channels, N] float32 ~ N(0, scale^2), for the state entry points."""
     rng = np.random.default_rng(seed)

@@ -50,3 +50,26 @@ def test_shapes_and_dtypes():
     r = inputs.make(3, channels=8, length=4096)
     scale = np.std(inputs.to_f32(r.B))
     assert 0.2 < scale < 0.3  # N(0,1)/sqrt(16)
+
+
+def test_device_drawn_rows_are_the_same_bits():
+    """device_problem / device_row (drawn here on the CPU device): the one-channel row problem
+    holds exactly the bits of the drawn tensors at (b, d), its head's step row and its group's B
+    and C, and the parameters of its channel (head with scalar decay)."""
+    torch = pytest.importorskip("torch")
+    t, p = inputs.device_problem(11, 2, 8, 40, 6, groups=2, device="cpu", rows_per_draw=3)
+    bits = lambda x: x.view(torch.int16).numpy().view(np.uint16)
+    assert t["u"].dtype == torch.bfloat16 and tuple(t["B"].shape) == (2, 2, 6, 40)
+    assert np.array_equal(p.A[5], -np.arange(1, 7, dtype=np.float32))
+    r = inputs.device_row(t, p, 1, 5)
+    assert np.array_equal(r.u[0, 0], bits(t["u"][1, 5])) and np.array_equal(r.z[0, 0], bits(t["z"][1, 5]))
+    assert np.array_equal(r.delta[0, 0], bits(t["delta"][1, 5]))
+    assert np.array_equal(r.B[0, 0], bits(t["B"][1, 1])) and np.array_equal(r.C[0, 0], bits(t["C"][1, 1]))
+    assert r.D[0] == p.D[5] and r.delta_bias[0] == p.delta_bias[5] and np.array_equal(r.A[0], p.A[5])
+    # B, C ~ N(0, 1/N); the stream is reproducible
+    t2, _ = inputs.device_problem(11, 2, 8, 40, 6, groups=2, device="cpu", rows_per_draw=3)
+    assert torch.equal(t["C"], t2["C"])
+    s, q = inputs.device_problem(12, 1, 8, 16, 4, heads=2, scalar_decay=True, gate=False, device="cpu")
+    assert s["z"] is None and q.A.shape == (2,) and np.all(q.A <= -1.0) and np.all(q.A >= -16.0)
+    rq = inputs.device_row(s, q, 0, 7)
+    assert np.array_equal(rq.delta[0, 0], bits(s["delta"][0, 1])) and rq.A[0] == q.A[1] and rq.D[0] == q.D[1]

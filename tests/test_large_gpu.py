@@ -1,0 +1,63 @@
+"""Parity of the HIP path on tensors of more than 2^31 elements (GPU).
+
+Element offsets past 2^31, and byte offsets of y past 2^32, in each forward layout: the window
+slots (few rows, long sequences), one row per wave (many rows), and the scalar-decay matrix form.
+The inputs are drawn on the device (inputs.device_problem: too large to draw on the host in
+seconds); the rows compared are copied back bit for bit and run through the oracle: the first
+row, the row that holds flat element 2^31, and the last row.  Bars as in test_parity_gpu
+(normwise 2e-3 for bf16 inputs, plus the per-row and elementwise checks).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from conftest import normwise
+from gpu_helpers import say, torch_dev
+from selective_state_space_88_amd import inputs
+from test_parity_gpu import diagnostics
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+CASES = {
+    # 1024 rows of 2^21 + 8 steps: the window-slot layout (rows <= 4 x 256 CUs)
+    "window slots 1x1024x2097160 N16": dict(seed=2101, batch=1, channels=1024, length=(1 << 21) + 8, nstate=16),
+    # 2048 rows of 2^20 + 8 steps: one row per wave
+    "rows 2x1024x1048584 N16": dict(seed=2102, batch=2, channels=1024, length=(1 << 20) + 8, nstate=16),
+    # 2 x 80 heads x 64 channels x 2^18 steps, N 128: the matrix form
+    "matrix form 2x(80x64)x262144 N128": dict(seed=2103, batch=2, channels=80 * 64, length=1 << 18, nstate=128,
+                                              heads=80, scalar_decay=True, gate=False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_more_than_2_31_elements(case):
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_fwd
+
+    kw = dict(CASES[case])
+    seed = kw.pop("seed")
+    Bt, Dc, L = kw["batch"], kw["channels"], kw["length"]
+    assert Bt * Dc * L > 2 ** 31
+    say("[large] %s: drawing %.3g elements per input on the device (seed %d)" % (case, Bt * Dc * L, seed))
+    t, p = inputs.device_problem(seed, **kw)
+    y = scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], softplus=True)
+    torch.cuda.synchronize()
+    say("[large] %s: scan done" % case)
+    flat_row = (2 ** 31) // L
+    rows = sorted({0, flat_row, Bt * Dc - 1})
+    try:
+        for r in rows:
+            b, d = divmod(r, Dc)
+            rp = inputs.device_row(t, p, b, d)
+            ref = oracle.scan_problem(rp).reshape(-1)
+            got = y[b, d].cpu().numpy().astype(np.float64)
+            err = normwise(got, ref)
+            dg = diagnostics(got, ref, L, TOL)
+            say("[large] %s: row (%d, %d): normwise %.3e, elementwise excess %.3e" % (case, b, d, err, dg["excess"]))
+            assert np.all(np.isfinite(got)), (case, b, d)
+            assert err <= TOL and dg["excess"] <= 0, (case, b, d, err, dg)
+    finally:
+        del y, t
+        torch.cuda.empty_cache()
