@@ -272,6 +272,22 @@ def device_problem(seed: int, batch: int, channels: int, length: int, nstate: in
     return t, p
 
 
+def device_normal(seed: int, shape, device="cuda", rows_per_draw: int = 32):
+    """float32 ~ N(0, 1) of the given shape drawn on `device` (torch's generator seeded with
+    `seed`, `rows_per_draw` rows of the last dimension at a time): e.g. the upstream gradient of
+    a backward over a device-drawn problem."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.float32, device=device)
+    flat = out.view(-1, shape[-1])
+    for r in range(0, flat.shape[0], rows_per_draw):
+        n = min(rows_per_draw, flat.shape[0] - r)
+        flat[r:r + n] = torch.randn((n, shape[-1]), generator=gen, device=device, dtype=torch.float32)
+    return out
+
+
 def device_row(t: dict, p: Problem, b: int, d: int) -> Problem:
     """Row (b, d) of a device-drawn problem as a one-channel host Problem (the same bf16 bits)."""
     import torch

@@ -61,3 +61,59 @@ def test_more_than_2_31_elements(case):
     finally:
         del y, t
         torch.cuda.empty_cache()
+
+
+BWD_CASES = {
+    # the composed gated path: forward recompute on the window slots (with the checkpoints), the
+    # gate pass, the per-channel backward
+    "window slots gated 1x1024x2097160 N16": dict(seed=2111, batch=1, channels=1024, length=(1 << 21) + 8,
+                                                  nstate=16),
+    # the matrix-form backward
+    "matrix form 2x(80x64)x262144 N128": dict(seed=2113, batch=2, channels=80 * 64, length=1 << 18, nstate=128,
+                                              heads=80, scalar_decay=True, gate=False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BWD_CASES))
+def test_backward_more_than_2_31_elements(case):
+    """The gradients of sampled rows against the oracle run on each row alone: with a step size
+    per channel every per-channel gradient (du, ddelta, dz, dA, dD, ddelta_bias) depends only on
+    the row and the shared B, C; with one step size per head of 64 channels only du does (the
+    others sum over the head)."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_bwd
+
+    kw = dict(BWD_CASES[case])
+    seed = kw.pop("seed")
+    Bt, Dc, L = kw["batch"], kw["channels"], kw["length"]
+    assert Bt * Dc * L > 2 ** 31
+    say("[large bwd] %s: drawing %.3g elements per input on the device (seed %d)" % (case, Bt * Dc * L, seed))
+    t, p = inputs.device_problem(seed, **kw)
+    dy = inputs.device_normal(seed + 1, (Bt, Dc, L))
+    g = scan_bwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], dy, softplus=True)
+    torch.cuda.synchronize()
+    say("[large bwd] %s: backward done" % case)
+    rows = sorted({0, (2 ** 31) // L, Bt * Dc - 1})
+    if p.scalar_decay:
+        rows = rows[:2]
+    try:
+        for r in rows:
+            b, d = divmod(r, Dc)
+            rp = inputs.device_row(t, p, b, d)
+            ref = oracle.scan_bwd_problem(rp, dy[b:b + 1, d:d + 1].cpu().numpy())
+            pairs = [("du", g["du"][b, d], ref["du"])]
+            if not p.scalar_decay:
+                pairs += [("ddelta", g["ddelta"][b, d], ref["ddelta"]), ("dz", g["dz"][b, d], ref["dz"]),
+                          ("dA", g["dA"][d], ref["dA"]), ("dD", g["dD"][d], ref["dD"]),
+                          ("ddelta_bias", g["ddelta_bias"][d], ref["ddelta_bias"])]
+            errs = {}
+            for name, got, want in pairs:
+                got = got.cpu().numpy().astype(np.float64).reshape(-1)
+                assert np.all(np.isfinite(got)), (case, b, d, name)
+                errs[name] = normwise(got, np.asarray(want, dtype=np.float64).reshape(-1))
+            say("[large bwd] %s: row (%d, %d): %s" % (case, b, d, " ".join("%s %.2e" % kv for kv in errs.items())))
+            bad = {k: v for k, v in errs.items() if v > TOL}
+            assert not bad, (case, b, d, bad)
+    finally:
+        del g, t, dy
+        torch.cuda.empty_cache()
