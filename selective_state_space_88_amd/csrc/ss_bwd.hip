@@ -311,7 +311,7 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
       for (int k = 0; k < kBK; ++k) ah[k] = __builtin_amdgcn_exp2f(dt[k] * A2);
     }
     for (int pp = 0; pp < P; ++pp) {
-      // the next pair's B and C rows (the first pair of the window to the left after the last)
+      // the next group's B and C rows (the first group of the window to the left after the last)
       const bool more = pp + 1 < P || w > 0;
       float nbc[kBK];
       if (more) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
@@ -381,13 +381,13 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
         if (lane == 0) gcar[wave][n] = cl;
         dAp[s] = dAs;
       }
-      // dA of the pair: summed over the wave's lanes into the wave's partial sums
+      // dA of the group's SP states: summed over the wave's lanes into the wave's partial sums
 #pragma unroll
       for (int s = 0; s < SP; ++s) {
         const float v = wave_sum(dAp[s]);
         if (lane == 0 && valid && SP * pp + s < N) dAl[wave][SCALAR ? 0 : SP * pp + s] += v;
       }
-      // dB, dC of the pair: summed over the block's 8 channels, then one atomic add per step;
+      // dB, dC of the group's states: summed over the block's 8 channels, then one atomic add per step;
       // consecutive lanes add to consecutive steps, so each wave's adds cover two cache lines
       if (!valid) {
 #pragma unroll
