@@ -467,7 +467,8 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
 //   kTRAP  exponential-trapezoidal rule: the scan runs the state k = h + e/2, which obeys the
 //          Euler recurrence k_t = a_t k_{t-1} + e_t, and y reads C (k - e/2).
 // kCKPT: also store the backward's checkpoints (ScanArgs::ckpt); only with none of the others
-constexpr int kSIO = 1, kZOH = 2, kTRAP = 4, kCKPT = 8;
+// kPERT: (window-slot kernel, plain or with kCKPT) the timing stress of perturb_wait
+constexpr int kSIO = 1, kZOH = 2, kTRAP = 4, kCKPT = 8, kPERT = 16;
 template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, int MODE>
 __global__ __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(ROWS == 2 && sizeof(TIn) == 2 ? 3 : 2))) void diag_fwd_kernel(
     ScanArgs p, int npairs, int64_t nwin, int64_t blocks_per_bg) {
@@ -1024,6 +1025,19 @@ __device__ __forceinline__ uint32_t progress_one(uint32_t addr) {
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Timing stress (race detection): with `perturb` set, a wave sleeps a pseudo-random number of
+// ~64-clock rounds at each step, 0-7, and now and then 64 (a wave held up for a whole step), a
+// different pattern for every (block, wave, step).  The results must not change: each wave reads
+// another's data only behind the waits above, whatever the order the waves arrive in.
+__device__ __forceinline__ void perturb_wait(uint32_t perturb, int s, int wave) {
+  uint32_t h = (uint32_t)s * 0x9E3779B1u ^ ((uint32_t)wave * 0x85EBCA6Bu) ^ (blockIdx.x * 0xC2B2AE35u) ^ perturb;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const uint32_t n = (h & 0x3F0u) == 0 ? 64u : (h & 7u);
+  for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(1);
+}
+
 // Poll until ready() or `limit` polls have failed; in the latter case record the failure in
 // g_spin_error and return (the kernel goes on and ends; its results are then wrong, which the
 // host reports).  A wait can therefore never hang the GPU.
@@ -1074,10 +1088,12 @@ struct SlotPos {
 
 template <typename TOut, bool GATE, int MODE>
 __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu(3))) void diag_slots_kernel(
-    ScanArgs p, int64_t nwin, int64_t blocks_per_bg, int skew, int nsteps, uint32_t spin_limit) {
+    ScanArgs p, int64_t nwin, int64_t blocks_per_bg, int skew, int nsteps, uint32_t spin_limit,
+    uint32_t perturb) {
   using TIn = bf16_t;
   constexpr bool SIO = (MODE & kSIO) != 0, ZOH = (MODE & kZOH) != 0, TRAP = (MODE & kTRAP) != 0;
   constexpr bool CKPT = (MODE & kCKPT) != 0;
+  constexpr bool PERT = (MODE & kPERT) != 0;          // the timing stress (perturb_wait)
   constexpr int W = 64 * kK;                         // steps per window
   constexpr int NCI = Seg<TIn>::kChunks;             // 16-byte copies per lane per input row
   constexpr int kSegWords = NCI * 256;
@@ -1246,6 +1262,7 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
   };
 
   for (int s = 0; s < nsteps; ++s) {
+    if constexpr (PERT) perturb_wait(perturb, s, wave);
     const bool act = cur.q >= 0 && cur.w < nwin;
     const int np = cur.np;
     const int64_t w = cur.w;
@@ -1454,23 +1471,33 @@ hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
   // force the failure path
   uint32_t spin_limit = 1u << 24;
   if (const char* e = getenv("SS_SPIN_LIMIT")) spin_limit = (uint32_t)strtoul(e, nullptr, 10);
-  const int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0) |
-                   (a.ckpt ? kCKPT : 0);
+  // SS_PERTURB=<nonzero seed> in the environment turns on the timing stress (perturb_wait), a
+  // compile-time variant of the plain and the checkpointing kernels (other modes run without it)
+  uint32_t perturb = 0;
+  if (const char* e = getenv("SS_PERTURB")) perturb = (uint32_t)strtoul(e, nullptr, 10);
+  int mode = ((a.h_init || a.h_final || a.zoh || a.trap) ? kSIO : 0) | (a.zoh ? kZOH : 0) | (a.trap ? kTRAP : 0) |
+             (a.ckpt ? kCKPT : 0);
+  if (perturb && (mode == 0 || mode == kCKPT)) mode |= kPERT;
 #define SS_M(G, M)                                                                                          \
   case M:                                                                                                   \
     hipLaunchKernelGGL((diag_slots_kernel<TOut, G, M>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,  \
-                       (int)steps, spin_limit);                                                             \
+                       (int)steps, spin_limit, perturb);                                                    \
     break;
 #define SS_LAUNCH(G)                                                                                        \
   switch (mode) {                                                                                           \
     SS_M(G, 0) SS_M(G, kSIO) SS_M(G, kSIO | kZOH) SS_M(G, kSIO | kTRAP) SS_M(G, kSIO | kZOH | kTRAP)        \
+    SS_M(G, kPERT)                                                                                          \
     default: return hipErrorInvalidValue;                                                                   \
   }
-  if (mode == kCKPT) {
+  if (mode & kCKPT) {
     // (the backward's recompute: no gate, f32 y)
     if (a.z || sizeof(TOut) != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kCKPT>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,
-                       (int)steps, spin_limit);
+    if (mode & kPERT)
+      hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kCKPT | kPERT>), grid, block, dyn, s, a, nwin, blocks_per_bg,
+                         skew, (int)steps, spin_limit, perturb);
+    else
+      hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kCKPT>), grid, block, dyn, s, a, nwin, blocks_per_bg, skew,
+                         (int)steps, spin_limit, perturb);
   } else if (a.z) {
     SS_LAUNCH(true);
   } else {

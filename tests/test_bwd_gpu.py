@@ -169,6 +169,19 @@ def test_gated_backward_checkpoints_from_the_forward(case):
     check_bwd(p, "gated checkpoints from the forward: " + case)
 
 
+def test_gated_backward_checkpoints_under_timing_stress():
+    """The window-slot forward that stores the checkpoints, run with SS_PERTURB (every wave
+    sleeps a pseudo-random time at each step): the gradients still match the oracle."""
+    import os
+
+    os.environ["SS_PERTURB"] = "7"
+    try:
+        check_bwd(inputs.random_problem(793, 1, 8, 5 * 1024 + 264, 16, gate=True),
+                  "gated checkpoints from the window slots, timing stress")
+    finally:
+        del os.environ["SS_PERTURB"]
+
+
 def test_gated_matrix_backward_bf16_dy():
     torch = torch_dev()
     check_bwd(inputs.random_problem(786, 1, 128, 400, 16, heads=2, scalar_decay=True, gate=True),

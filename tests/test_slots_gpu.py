@@ -193,3 +193,49 @@ def test_slots_forced_wait_failure_is_reported():
     err = normwise(y.cpu().numpy().reshape(-1, p.length)[[0, 63]], ref)
     say("[slots] after the forced failure: normwise %.3e" % err)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("case", ["N16 ragged", "N5", "N17", "N128", "heads and groups"])
+def test_slots_timing_stress(case):
+    """SS_PERTURB=<seed> makes every wave sleep a pseudo-random time at each step (now and then
+    a whole step), so the waves reach their waits in orders the normal run rarely produces: the
+    output stays bitwise that of the normal run, for three seeds, and no wait runs out."""
+    import os
+
+    torch = torch_dev()
+    from selective_state_space_88_amd import scan
+
+    p = CASES[case]()
+    say("[slots] timing stress %s: channels=%d L=%d N=%d" % (case, p.channels, p.length, p.nstate))
+    t = dev_problem(p)
+    y0 = run_hip(p, dev=t)
+    for seed in (1, 2, 3):
+        os.environ["SS_PERTURB"] = str(seed)
+        try:
+            y = run_hip(p, dev=t)
+        finally:
+            del os.environ["SS_PERTURB"]
+        same = np.array_equal(y, y0)
+        say("[slots] timing stress %s seed %d: bitwise equal %s" % (case, seed, same))
+        assert same, (case, seed)
+    assert scan.check(torch.cuda.current_stream().cuda_stream) == 0
+
+
+def test_slots_stable_over_100_runs():
+    """100 launches on the same inputs give bitwise the same y (the hand-over between slots has
+    no order-dependent arithmetic)."""
+    torch = torch_dev()
+    from selective_state_space_88_amd.scan import scan_fwd
+
+    p = inputs.make(3, batch=1, channels=64, length=16 * 1024)
+    say("[slots] 100 runs: channels=%d L=%d" % (p.channels, p.length))
+    t = dev_problem(p)
+    first = scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"])
+    y = torch.empty_like(first)
+    bad = 0
+    for _ in range(99):
+        scan_fwd(t["u"], t["delta"], t["A"], t["B"], t["C"], t["D"], t["z"], t["delta_bias"], y=y)
+        bad += int(not torch.equal(y, first))
+    torch.cuda.synchronize()
+    say("[slots] 100 runs: %d differ from the first" % bad)
+    assert bad == 0
