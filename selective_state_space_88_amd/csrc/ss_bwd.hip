@@ -485,15 +485,30 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
     for (int n = lane; n < N; n += 64) atomicAdd(p.dA + d * p.dA_sd + n, dAl[wave][n]);
 }
 
-// p[i0 * s0 + i1 * s1 + i2 * s2 + i3] = 0 over [n0, n1, n2, n3] (innermost stride 1)
-__global__ __launch_bounds__(256) void zero4_kernel(float* __restrict__ p, int64_t n0, int64_t n1, int64_t n2,
-                                                    int64_t n3, int64_t s0, int64_t s1, int64_t s2) {
-  const int64_t total = n0 * n1 * n2 * n3;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int64_t i3 = i % n3, r = i / n3;
-    const int64_t i2 = r % n2, r2 = r / n2;
-    const int64_t i1 = r2 % n1, i0 = r2 / n1;
-    p[i0 * s0 + i1 * s1 + i2 * s2 + i3] = 0.f;
+// Up to kZeroJobs float regions set to zero by one launch: region k is p[i0 s0 + i1 s1 + i2 s2 +
+// i3] over [n0, n1, n2, n3] (innermost stride 1).  The summed gradients start at zero; a kernel
+// rather than a memset, so that a caller may capture the call in a graph.
+constexpr int kZeroJobs = 6;
+struct ZeroJobs {
+  float* p[kZeroJobs];
+  int64_t n[kZeroJobs][4];
+  int64_t st[kZeroJobs][3];
+  int count;
+};
+
+__global__ __launch_bounds__(256) void zero_kernel(ZeroJobs z) {
+#pragma unroll
+  for (int k = 0; k < kZeroJobs; ++k) {
+    if (k >= z.count) break;
+    const int64_t n1 = z.n[k][1], n2 = z.n[k][2], n3 = z.n[k][3];
+    const int64_t total = z.n[k][0] * n1 * n2 * n3;
+    float* const p = z.p[k];
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+      const int64_t i3 = i % n3, r = i / n3;
+      const int64_t i2 = r % n2, r2 = r / n2;
+      const int64_t i1 = r2 % n1, i0 = r2 / n1;
+      p[i0 * z.st[k][0] + i1 * z.st[k][1] + i2 * z.st[k][2] + i3] = 0.f;
+    }
   }
 }
 
@@ -520,12 +535,18 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   const int P = (a.N + 1) / 2;
   const int64_t nwin = (a.L + kBW - 1) / kBW;
   const int64_t rows = a.batch * a.channels;
-  // the summed gradients start at zero (a kernel, not a memset: callers may capture this)
+  // the summed gradients start at zero (one kernel for all of them, not a memset: callers may
+  // capture this)
+  ZeroJobs zj{};
+  int64_t zmax = 0;
   auto zero4 = [&](float* ptr, int64_t n0, int64_t n1, int64_t n2, int64_t n3, int64_t s0, int64_t s1, int64_t s2) {
     const int64_t total = n0 * n1 * n2 * n3;
     if (!ptr || total == 0) return;
-    hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)std::min<int64_t>((total + 255) / 256, 8192)), dim3(256), 0, s,
-                       ptr, n0, n1, n2, n3, s0, s1, s2);
+    const int k = zj.count++;
+    zj.p[k] = ptr;
+    zj.n[k][0] = n0, zj.n[k][1] = n1, zj.n[k][2] = n2, zj.n[k][3] = n3;
+    zj.st[k][0] = s0, zj.st[k][1] = s1, zj.st[k][2] = s2;
+    zmax = std::max(zmax, total);
   };
   zero4(a.dD, 1, 1, 1, a.d_per_head ? a.heads : a.channels, 0, 0, 0);
   zero4(a.dbias, 1, 1, 1, a.heads, 0, 0, 0);
@@ -535,6 +556,8 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   if (a.chan_per_head > 1) zero4(a.ddelta, a.batch, 1, a.heads, a.L, a.dd_sb, 0, a.dd_sh);
   zero4(a.dB, a.batch, a.groups, a.N, a.L, a.dB_sb, a.dB_sg, a.dB_sn);
   zero4(a.dC, a.batch, a.groups, a.N, a.L, a.dC_sb, a.dC_sg, a.dC_sn);
+  if (zj.count)
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<int64_t>((zmax + 255) / 256, 8192)), dim3(256), 0, s, zj);
   if (ssd_bwd_path(a)) return launch_ssd_bwd(a, ws, s);
   const dim3 cgrid((unsigned)((rows + kBWaves - 1) / kBWaves)), block(64 * kBWaves);
   if (!a.ckpt_ready) {
