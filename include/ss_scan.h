@@ -211,8 +211,9 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * matrix form instead, whose workspace holds the state at the start of every 32-step chunk
  * (batch * channels * ceil(L / 32) * N' floats, N' = N rounded up to 32, 64 or 128) and C B^T
  * per chunk.  With a gate, either form first recomputes the output before the gate into the
- * workspace (batch * channels * L floats more) and takes dz and dy s(z) from it in a pass of its
- * own.  Chain rule, with s(z) = z sigmoid(z) and
+ * workspace (batch * channels * L floats more); the per-channel kernel takes dz and dy s(z) from
+ * it where it reads dy, the matrix form in a pass of its own.  Chain rule, with s(z) =
+ * z sigmoid(z) and
  * dy0 = dy s(z):  g_t = C_t dy0_t + exp(dt_{t+1} A) g_{t+1} (the gradient of h_t),
  * dC_t = dy0_t h_t,  dB_t = g_t dt_t u_t,  du_t = dy0_t D + sum_n g_t dt_t B_t,
  * ddt_t = sum_n g_t (h_{t-1} exp(dt_t A) A + B_t u_t),  dA = sum_t g_t h_{t-1} exp(dt_t A) dt_t,

@@ -219,7 +219,22 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
 // s(z) as its upstream gradient).  SP: states per group (1 or 2), the unit of the state loop (P
 // groups); one state at a time keeps the kernel within 128 VGPRs, i.e. two 8-wave blocks (four
 // waves per SIMD) per CU.
-template <typename TIn, typename TDy, bool SCALAR, int SP>
+// This lane's kBK consecutive per-step outputs v at row + t0 (steps past L not written): two
+// 16-byte nontemporal stores when the row segment is 16-byte aligned and whole, else one store
+// per step.
+__device__ __forceinline__ void store_steps(float* row, int64_t t0, int64_t L, const float (&v)[kBK]) {
+  float* q = row + t0;
+  if (t0 + kBK <= L && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(q));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(q) + 1);
+  } else {
+#pragma unroll
+    for (int k = 0; k < kBK; ++k)
+      if (t0 + k < L) q[k] = v[k];
+  }
+}
+
+template <typename TIn, typename TDy, bool SCALAR, int SP, bool FGATE>
 __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP == 1 ? 4 : 1))) void bwd_kernel(
     BwdArgs p, int P, int64_t nwin, const float* ckpt) {
   __shared__ float gcar[kMWaves][2 * kBMaxPairs];     // adjoint carried into the window from the right
@@ -297,6 +312,21 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
       }
     }
     load_seg<kBK>(dyr, t0, L, p.vec, dy0);
+    if constexpr (FGATE) {
+      // the gate: dz = dy y0 s'(z) written here, and the kernel runs on dy0 = dy s(z) (s(z) =
+      // z sigmoid(z), s'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))))
+      float zz[kBK], yy[kBK];
+      load_seg<kBK>(static_cast<const TIn*>(p.gz) + b * p.z_sb + d * p.z_sd, t0, L, p.vec, zz);
+      load_seg<kBK>(p.gy0 + row * L, t0, L, p.y0_vec, yy);
+      float dzv[kBK];
+#pragma unroll
+      for (int k = 0; k < kBK; ++k) {
+        const float sgz = 1.f / (1.f + __builtin_amdgcn_exp2f(-zz[k] * kLog2e));
+        dzv[k] = dy0[k] * yy[k] * sgz * fmaf(zz[k], 1.f - sgz, 1.f);
+        dy0[k] = dy0[k] * (zz[k] * sgz);
+      }
+      if (valid) store_steps(p.dz + b * p.dz_sb + d * p.dz_sd, t0, L, dzv);
+    }
 #pragma unroll
     for (int k = 0; k < kBK; ++k) {
       du[k] = 0.f;   // here: sum over the states of g_t B_t (du and ddt take it once per step below)
@@ -455,21 +485,20 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
       }
       __syncthreads();
     } else if (valid && p.chan_per_head == 1) {
-#pragma unroll
-      for (int k = 0; k < kBK; ++k)
-        if (t0 + k < L) ddr[t0 + k] = dxs[k];
+      store_steps(ddr, t0, L, dxs);
     } else if (valid) {
 #pragma unroll
       for (int k = 0; k < kBK; ++k)
         if (t0 + k < L) atomicAdd(ddr + t0 + k, dxs[k]);
     }
+    if (valid) {
+      store_steps(dur, t0, L, du);
 #pragma unroll
-    for (int k = 0; k < kBK; ++k) {
-      if (valid && t0 + k < L) {
-        const float dx = dxs[k];
-        dur[t0 + k] = du[k];
-        dbacc += dx;
-        dDacc = fmaf(dy0[k], uu[k], dDacc);
+      for (int k = 0; k < kBK; ++k) {
+        if (t0 + k < L) {
+          dbacc += dxs[k];
+          dDacc = fmaf(dy0[k], uu[k], dDacc);
+        }
       }
     }
   }
@@ -567,18 +596,25 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves)));
   const dim3 mblock(64 * kMWaves);
   const float* ck = ws;
-#define SS_BWD(SC) \
-  hipLaunchKernelGGL((bwd_kernel<TIn, TDy, SC, kBwdSP>), grid, mblock, 0, s, a, (a.N + kBwdSP - 1) / kBwdSP, nwin, ck)
-  // (a gated call arrives here ungated: launch_bwd composes the gate around this kernel)
-  if (a.scalar) SS_BWD(true); else SS_BWD(false);
+#define SS_BWD(SC, FG)                                                                                   \
+  hipLaunchKernelGGL((bwd_kernel<TIn, TDy, SC, kBwdSP, FG>), grid, mblock, 0, s, a, (a.N + kBwdSP - 1) / kBwdSP, \
+                     nwin, ck)
+  // (a gated call arrives here with z taken apart by launch_bwd: gz and gy0 set, the gate folded in)
+  if (a.gz) {
+    if (a.scalar) SS_BWD(true, true); else SS_BWD(false, true);
+  } else {
+    if (a.scalar) SS_BWD(true, false); else SS_BWD(false, false);
+  }
 #undef SS_BWD
   return hipGetLastError();
 }
 
-// A gated layer composes three steps on one workspace: the forward without the gate recomputes
-// y0 = C h + D u (the output before the gate) into f32 rows; an elementwise kernel writes dz and
-// turns y0 into dy0 = dy s(z); the ungated backward (matrix form or per channel) runs on dy0.
-// The gate multiplies C h + D u as a whole, so dy0 is the ungated layer's whole upstream gradient.
+// A gated layer composes the ungated backward with the gate: the forward without the gate
+// recomputes y0 = C h + D u (the output before the gate) into f32 rows; dz = dy y0 s'(z) and
+// dy0 = dy s(z) follow elementwise, and the ungated backward runs on dy0.  The gate multiplies
+// C h + D u as a whole, so dy0 is the ungated layer's whole upstream gradient.  The per-channel
+// kernel computes dz and dy0 itself where it loads dy; the matrix form gets dy0 from an
+// elementwise pass that overwrites y0.
 bool gated_path(const BwdArgs& a) {
   return a.z != nullptr;
 }
@@ -662,6 +698,15 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
     }
     hipError_t e = !a.scalar ? launch_diag(f, s) : ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
     if (e != hipSuccess) return e;
+    b.ckpt_ready = fwd_ckpt ? 1 : 0;
+    if (!ssd_bwd_path(b)) {
+      // the per-channel kernel takes the gate itself (dz and dy0 where it loads dy): no pass of
+      // its own, y0 read once
+      b.gz = a.z;
+      b.gy0 = y0;
+      b.y0_vec = a.L % 4 == 0;
+      return launch_bwd(b, bws, s);
+    }
     const int64_t total = a.batch * a.channels * a.L;
     const dim3 grid((unsigned)std::min<int64_t>((total + 255) / 256, 16384));
 #define SS_GATE(TI, TD) hipLaunchKernelGGL((gate_bwd_kernel<TI, TD>), grid, dim3(256), 0, s, a, y0)
@@ -672,7 +717,6 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
     }
 #undef SS_GATE
     b.dz = nullptr;
-    b.ckpt_ready = fwd_ckpt ? 1 : 0;
     b.dy = y0;
     b.dy_bf16 = 0;
     b.dy_sb = a.channels * a.L;

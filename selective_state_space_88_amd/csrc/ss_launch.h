@@ -89,6 +89,12 @@ struct BwdArgs {
   int32_t softplus, in_bf16, dy_bf16;
   int32_t vec;            // every input time row (and dy's) is 16-byte aligned
   int32_t ckpt_ready;     // the per-channel path's checkpoints are already in the workspace
+  int32_t y0_vec;         // gy0's rows are 16-byte aligned
+  // the gate folded into the per-channel kernel (set by launch_bwd for a gated call; z is then
+  // nullptr): gz is the gate input (strides z_sb, z_sd), gy0 the output before the gate
+  // ([batch, channels, L] f32, contiguous); the kernel writes dz and runs on dy0 = dy s(z)
+  const void* gz;
+  const float* gy0;
   int64_t u_sb, u_sd, dl_sb, dl_sh, z_sb, z_sd, B_sb, B_sg, B_sn, C_sb, C_sg, C_sn, A_sd, dy_sb, dy_sd;
   int64_t du_sb, du_sd, dd_sb, dd_sh, dA_sd, dB_sb, dB_sg, dB_sn, dC_sb, dC_sg, dC_sn, dz_sb, dz_sd;
 };
