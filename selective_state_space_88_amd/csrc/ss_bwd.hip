@@ -240,7 +240,9 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
   __shared__ float gcar[kMWaves][2 * kBMaxPairs];     // adjoint carried into the window from the right
   __shared__ float dAl[kMWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
   // dB (SP states), dC (SP states) of the window's steps, step-major ([lane][k] = step lane K + k)
-  __shared__ __attribute__((aligned(16))) float red[kMWaves][2 * SP][kBW];
+  // (two buffers, alternating by state, so that one barrier per state orders both the writes
+  // before the sums and the sums before the next writes to the same buffer)
+  __shared__ __attribute__((aligned(16))) float red[2][kMWaves][2 * SP][kBW];
   // B (SP states) and C (SP states) of a group's window, shared by the block's channels; two
   // buffers: the next group's rows are loaded while this group runs
   __shared__ __attribute__((aligned(16))) float bcs[2][2 * SP][kBW];
@@ -294,6 +296,7 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
   }
   __syncthreads();
   int buf = 0;
+  int rb = 0;   // the reduction buffer of the current state
 
   for (int64_t w = nwin - 1; w >= 0; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
@@ -429,8 +432,8 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
       for (int s = 0; s < SP; ++s)
 #pragma unroll
         for (int k = 0; k < kBK; k += 4) {
-          *reinterpret_cast<f32x4*>(&red[wave][s][lane * kBK + k]) = f32x4{rB[s][k], rB[s][k + 1], rB[s][k + 2], rB[s][k + 3]};
-          *reinterpret_cast<f32x4*>(&red[wave][SP + s][lane * kBK + k]) =
+          *reinterpret_cast<f32x4*>(&red[rb][wave][s][lane * kBK + k]) = f32x4{rB[s][k], rB[s][k + 1], rB[s][k + 2], rB[s][k + 3]};
+          *reinterpret_cast<f32x4*>(&red[rb][wave][SP + s][lane * kBK + k]) =
               f32x4{rC[s][k], rC[s][k + 1], rC[s][k + 2], rC[s][k + 3]};
         }
       if (more) bc_store(buf ^ 1, nbc);
@@ -442,13 +445,15 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
         if (n < N && t < L) {
           float v = 0.f;
 #pragma unroll
-          for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[wv2][which][r];
+          for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[rb][wv2][which][r];
           float* dst = (which < SP ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
           atomicAdd(dst, v);
         }
       }
-      __syncthreads();
+      // (no second barrier: the next state writes the other buffer, and this one again only
+      // after the next state's barrier, which every thread reaches after these sums)
       buf ^= 1;
+      rb ^= 1;
     }
     // per-step outputs of the window
     float* dur = p.du + b * p.du_sb + d * p.du_sd;
@@ -474,13 +479,13 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
       // the block's 8 channels share the head: summed through LDS, one atomic add per step
 #pragma unroll
       for (int k = 0; k < kBK; k += 4)
-        *reinterpret_cast<f32x4*>(&red[wave][0][lane * kBK + k]) = f32x4{dxs[k], dxs[k + 1], dxs[k + 2], dxs[k + 3]};
+        *reinterpret_cast<f32x4*>(&red[rb][wave][0][lane * kBK + k]) = f32x4{dxs[k], dxs[k + 1], dxs[k + 2], dxs[k + 3]};
       __syncthreads();
       for (int i = threadIdx.x; i < kBW; i += 64 * kMWaves) {
         const int64_t t = w * kBW + i;
         float v = 0.f;
 #pragma unroll
-        for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[wv2][0][i];
+        for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[rb][wv2][0][i];
         if (t < L) atomicAdd(ddr + t, v);
       }
       __syncthreads();
