@@ -303,19 +303,35 @@ def backward_bench(args, p, to_dev, dev):
         "cpu_baseline": None,
     }
     if matrix:
-        # The scalar-decay backward is a chain of dense contractions on v_mfma_f32_16x16x4_f32
-        # (2048 flops each), so its roofline is the fp32 matrix peak.  Per (batch, head, 64-channel
-        # slab, 32-step chunk) each of 4 waves issues 32 + 40 NT in the reverse pass and 8 NT in the
-        # forward pass (NT = 16-state tiles: 2, 4 or 8), and per (batch, group, chunk) C B^T takes
-        # 4 NT per wave; the time is the whole call.
+        # The scalar-decay backward is a chain of dense contractions on the matrix cores, so its
+        # roofline is the matrix peak of the dtype it runs in; the work is the MFMA instructions
+        # executed (split passes counted), the time the whole call.  NT = 16-state tiles (2, 4
+        # or 8), NB = max(NT / 4, 1), NR = NT / 2; per (batch, head, 64-channel slab, 32-step chunk)
+        # the reverse pass runs 8 waves (the [T x N] tiles on all 8 when NT >= 4, else on 4) and
+        # the forward pass SPL blocks of 4 waves (SPL = 4 for NT = 8, else 2; NH = NT / SPL tiles
+        # each); C B^T takes 4 waves per (batch, group, chunk).
         NT = 2 if p.nstate <= 32 else 4 if p.nstate <= 64 else 8
         nch = (p.length + 31) // 32
         blocks = p.batch * p.heads * (P // 64)
-        mf = (blocks * nch * 4 * (32 + 48 * NT) + p.batch * p.groups * nch * 4 * 4 * NT) * 2048.0
+        NB, NR = max(NT // 4, 1), NT // 2
+        bcw = 8 if NT >= 4 else 4
+        SPL = 4 if NT >= 8 else 2
+        if p.in_dtype == "bf16":
+            # v_mfma_f32_16x16x32_bf16 (16384 flops): an f32 operand split in hi and lo costs a
+            # product three instructions (two when the other operand is bf16 already: u, B, C)
+            rev = 4 * 2 * 2 + bcw * (2 * NB * 3 + 2 * NB * 2 + 2 * NB * 2) + 8 * (NT // 2 * 2 + 3 + NR * 2)
+            fwd = SPL * 4 * (NT // SPL) * 2
+            cbt = 4 * (16 * NT // 32)
+            mf = (blocks * nch * (rev + fwd) + p.batch * p.groups * nch * cbt) * 16384.0
+            peak = BF16_MFMA_PEAK_TFLOPS
+        else:
+            # v_mfma_f32_16x16x4_f32 (2048 flops each)
+            mf = (blocks * nch * 4 * (32 + 48 * NT) + p.batch * p.groups * nch * 4 * 4 * NT) * 2048.0
+            peak = FP32_MATRIX_PEAK_TFLOPS
         rl = out["roofline"]
         out["roofline"] = {
-            "bound": "mfma", "achieved": mf / per / 1e12, "peak": FP32_MATRIX_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": mf / per / 1e12 / FP32_MATRIX_PEAK_TFLOPS, "traffic": traffic, "call_ms": rl["call_ms"],
+            "bound": "mfma", "achieved": mf / per / 1e12, "peak": peak, "unit": "TFLOP/s",
+            "frac": mf / per / 1e12 / peak, "traffic": traffic, "call_ms": rl["call_ms"],
             "mfma_flops_per_call": mf, "alu_flop_equiv_per_call": flops, "alu_equiv_TFLOPs": tf,
             "hbm_algorithmic_bytes_per_call": nbytes, "hbm_achieved_GBps": nbytes / per / 1e9,
         }

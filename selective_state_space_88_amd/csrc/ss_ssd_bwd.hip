@@ -1,4 +1,4 @@
-// ss_ssd_bwd.hip -- backward of the scalar-decay scan in the chunked matrix form (gfx950, fp32 MFMA).
+// ss_ssd_bwd.hip -- backward of the scalar-decay scan in the chunked matrix form (gfx950, MFMA).
 //
 // With one decay per head (a_t = exp(dt_t A_h) shared by the head's channels and states; the
 // Mamba-2 layout of the bqwf.cn survey, section 3.2, and the omica.com.cn explainer, section 6.2)
@@ -24,11 +24,14 @@
 //
 // Two passes per (batch, head, 64-channel slab): the first walks the chunks forward and stores
 // every chunk's starting state H0 (f32, [N][64]); the second walks them in reverse carrying R in
-// MFMA accumulators.  Every product is v_mfma_f32_16x16x4_f32 on operands staged in LDS with the
-// contracted index contiguous (each lane reads four consecutive k with one 16-byte read; the
-// order of k inside a block of 16 is permuted the same way on both operands).  dB and dC are
-// summed over the group's heads with atomic adds; per-head sums (ddelta over slabs, dA, dD,
-// dbias) likewise.  No gate (the gated layout takes the per-channel kernel).
+// MFMA accumulators.  The products read operands staged in LDS with the contracted index
+// contiguous.  With bf16 inputs they run on v_mfma_f32_16x16x32_bf16, each f32 operand split into
+// bf16 hi and lo parts (three products, two when the other operand is bf16 already: u, B, C);
+// with f32 inputs on v_mfma_f32_16x16x4_f32 (each lane reads four consecutive k with one 16-byte
+// read; the order of k inside a block of 16 is permuted the same way on both operands).  dB and
+// dC are summed over the group's heads with atomic adds; per-head sums (ddelta over slabs, dA,
+// dD, dbias) likewise.  A gated layer arrives here on dy s(z), with the gate composed around
+// this backward by the caller.
 #include <type_traits>
 
 #include "ss_device.h"
@@ -93,6 +96,112 @@ __device__ __forceinline__ void mm_swz(const float* A, int lda, const float* Bsw
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[t] = TR ? mma4(bv[t][m], av[m], acc[t]) : mma4(av[m], bv[t][m], acc[t]);
+  }
+}
+
+// ---- the same products on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16, bf16 inputs only).
+// An f32 operand is split x = hi + lo (both bf16, round to nearest even; |x - hi - lo| <= 2^-18 |x|)
+// and a product takes hi.hi + hi.lo + lo.hi (the dropped lo.lo is below 2^-16 of it); an operand
+// that holds bf16 values exactly (u, B, C) is packed as it is and needs no lo.  Lane l supplies
+// k = 32 kb + 8 (l / 16) + 0..7 of its rows (the f32 form above permutes k the same way on both
+// operands, so the sums are the same products in another order); the accumulator layout is the
+// f32 form's.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+struct Split8 {
+  bf16x8 hi, lo;
+};
+
+// eight values -> bf16 hi (and lo unless EXACT, where the values are bf16 already)
+template <bool EXACT>
+__device__ __forceinline__ Split8 split8(const float (&x)[8]) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (EXACT) {
+      h[j] = (__float_as_uint(x[2 * j]) >> 16) | (__float_as_uint(x[2 * j + 1]) & 0xffff0000u);
+      l[j] = 0u;
+    } else {
+      h[j] = pk_bf16(x[2 * j], x[2 * j + 1]);
+      l[j] = pk_bf16(x[2 * j] - __uint_as_float(h[j] << 16), x[2 * j + 1] - __uint_as_float(h[j] & 0xffff0000u));
+    }
+  }
+  Split8 r;
+  r.hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+  r.lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
+  return r;
+}
+
+// acc += a . b over 32 k of one lane's pair of operands (TR: acc += b . a)
+template <bool AX, bool BX, bool TR>
+__device__ __forceinline__ f32x4 mma3(const Split8& a, const Split8& b, f32x4 acc) {
+  const bf16x8& ah = a.hi;
+  const bf16x8& bh = b.hi;
+  acc = TR ? mma32(bh, ah, acc) : mma32(ah, bh, acc);
+  if constexpr (!BX) acc = TR ? mma32(b.lo, ah, acc) : mma32(ah, b.lo, acc);
+  if constexpr (!AX) acc = TR ? mma32(bh, a.lo, acc) : mma32(a.lo, bh, acc);
+  return acc;
+}
+
+__device__ __forceinline__ void read8(const float* p, float (&v)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+
+// mm on the bf16 matrix cores; AX / BX: A / B hold bf16 values exactly
+template <int K, int NT, bool AX, bool BX, bool SCALE = false, bool TR = false>
+__device__ __forceinline__ void mm3(const float* A, int lda, const float* B, int ldb, int bstep, int lane,
+                                    f32x4 (&acc)[NT], const float* sc = nullptr) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* a = A + r * lda + 8 * q;
+  const float* b = B + r * ldb + 8 * q;
+#pragma unroll
+  for (int kb = 0; kb < K / 32; ++kb) {
+    float av[8];
+    read8(a + 32 * kb, av);
+    if constexpr (SCALE) {
+      float s8[8];
+      read8(sc + 32 * kb + 8 * q, s8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) av[i] *= s8[i];
+    }
+    const Split8 as = split8<AX && !SCALE>(av);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float bv[8];
+      read8(b + t * bstep + 32 * kb, bv);
+      acc[t] = mma3<AX && !SCALE, BX, TR>(as, split8<BX>(bv), acc[t]);
+    }
+  }
+}
+
+// mm_swz on the bf16 matrix cores (K = 64, Bsw swizzled as swz; A and B both split)
+template <int NT, bool TR = false>
+__device__ __forceinline__ void mm3_swz(const float* A, int lda, const float* Bsw, int lane, f32x4 (&acc)[NT]) {
+  const int r = lane & 15, q = lane >> 4;
+  const float* a = A + r * lda + 8 * q;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float av[8];
+    read8(a + 32 * kb, av);
+    const Split8 as = split8<false>(av);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = 16 * t + r;
+      // granules 8 kb + 2 q and 8 kb + 2 q + 1 of row n
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(Bsw + n * 64 + 4 * ((8 * kb + 2 * q) ^ r));
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(Bsw + n * 64 + 4 * ((8 * kb + 2 * q + 1) ^ r));
+      const float bv[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      acc[t] = mma3<false, false, TR>(as, split8<false>(bv), acc[t]);
+    }
   }
 }
 
@@ -174,6 +283,8 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
   constexpr int SPL = kStateSplit<NT>;
   constexpr int NH = NT / SPL, NPH = NP / SPL;   // this block's state tiles and states
   constexpr int kSN = NP + 4;
+  // bf16 inputs: the products on the bf16 matrix cores (mm3), else fp32 MFMA
+  constexpr bool B3 = std::is_same<TIn, bf16_t>::value;
   __shared__ __attribute__((aligned(16))) float xt[kCP * kST];   // u^T [p][t]
   __shared__ __attribute__((aligned(16))) float wb[NPH * kST];   // e^{s_{T-1} - s_t} dt_t B [n][t], this share
   __shared__ __attribute__((aligned(16))) float ctn[kCT * kSN];  // C [t][n] (chunks whose C B^T this block forms)
@@ -276,7 +387,8 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
     if (c + 2 < nch) fetch(c + 2, S);   // this set's next chunk
     if (cbjob) {
       f32x4 cb[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      mm<NP, 1>(ctn + 16 * (wave >> 1) * kSN, kSN, btn + 16 * (wave & 1) * kSN, kSN, 0, lane, cb);
+      if constexpr (B3) mm3<NP, 1, true, true>(ctn + 16 * (wave >> 1) * kSN, kSN, btn + 16 * (wave & 1) * kSN, kSN, 0, lane, cb);
+      else mm<NP, 1>(ctn + 16 * (wave >> 1) * kSN, kSN, btn + 16 * (wave & 1) * kSN, kSN, 0, lane, cb);
       *reinterpret_cast<f32x4*>(cbg + c * 1024 + (wave * 64 + lane) * 4) = cb[0];
     }
     __syncthreads();   // wb ready
@@ -284,7 +396,8 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
     const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
 #pragma unroll
     for (int j = 0; j < NH; ++j) H[j] = H[j] * dec;
-    mm<kCT, NH>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
+    if constexpr (B3) mm3<kCT, NH, true, false>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
+    else mm<kCT, NH>(xt + 16 * wave * kST, kST, wb, kST, 16 * kST, lane, H);
     __syncthreads();   // xt, wb, ss2, ctn, btn are rewritten by the next chunk
     return true;
   };
@@ -306,6 +419,8 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
   constexpr int NP = 16 * NT;
   constexpr int NB = NT >= 4 ? NT / 4 : 1;   // [T x N] state tiles per wave
   constexpr int NR = NT / 2;                 // R state tiles per wave
+  // bf16 inputs: the products on the bf16 matrix cores (mm3: split f32 operands), else fp32 MFMA
+  constexpr bool B3 = std::is_same<TIn, bf16_t>::value;
   __shared__ __attribute__((aligned(16))) float xn[kCT * kSP];    // u [t][p]
   __shared__ __attribute__((aligned(16))) float dyn[kCT * kSP];   // dy [t][p]
   __shared__ __attribute__((aligned(16))) float dyt[kCP * kST];   // dy [p][t]
@@ -431,7 +546,8 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
     if (dxw) {
       const int ti = wave >> 1, half = wave & 1;
       f32x4 dx[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      mm<kCP, 1>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
+      if constexpr (B3) mm3<kCP, 1, false, true>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
+      else mm<kCP, 1>(dyn + 16 * ti * kSP, kSP, xn + 16 * half * kSP, kSP, 0, lane, dx);
       const int s = 16 * half + l16;   // column j = s of this lane; rows k = t below
       const float dts = sdt[s];
       float csum = 0.f;
@@ -461,8 +577,13 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
     for (int j = 0; j < NB; ++j) yh[j] = xr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int tw = 16 * w2 + l16;   // this lane's step within the chunk
     if (bcw) {
-      mm_swz<NB, true>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
-      mm<kCP, NB, false, true>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
+      if constexpr (B3) {
+        mm3_swz<NB, true>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
+        mm3<kCP, NB, true, false, false, true>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
+      } else {
+        mm_swz<NB, true>(dyn + 16 * w2 * kSP, kSP, hnp + 16 * nb0 * kCP, lane, yh);
+        mm<kCP, NB, false, true>(xn + 16 * w2 * kSP, kSP, rnp + 16 * nb0 * kSP, kSP, 16 * kSP, lane, xr);
+      }
       const float dtw = sdt[tw];
 #pragma unroll
       for (int j = 0; j < NB; ++j)
@@ -517,8 +638,13 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
           yh[j][r] *= esw;
           xr[j][r] *= erw;
         }
-      mm<kCT, NB, false, true>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
-      mm<kCT, NB, false, true>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
+      if constexpr (B3) {
+        mm3<kCT, NB, false, true, false, true>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
+        mm3<kCT, NB, false, true, false, true>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
+      } else {
+        mm<kCT, NB, false, true>(m1 + 16 * w2 * kST, kST, bnt + 16 * nb0 * kST, kST, 16 * kST, lane, yh);
+        mm<kCT, NB, false, true>(m1t + 16 * w2 * kST, kST, cnt + 16 * nb0 * kST, kST, 16 * kST, lane, xr);
+      }
       const int64_t t = t0 + tw;
       if (t < L) {
 #pragma unroll
@@ -537,26 +663,42 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
     // ---- dX = diag(e^{s_{T-1} - s}) B R^T + (L o CB)^T dY (rows 16 w2, channels 16 wg)
     {
       f32x4 dxa[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-      // B R^T over n: the operands of block kb + 1 are read while block kb's products run
-      float oa[2][4], ob[2][4];
-      auto rd = [&](int kb, int s) {
+      if constexpr (B3) {
+        // B R^T over n, 32 states at a time (B exact in bf16, R split)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int n = 16 * kb + 4 * q + m;
-          oa[s][m] = bnt[n * kST + 16 * w2 + l16];
-          ob[s][m] = rnp[n * kSP + pch];
+        for (int kb = 0; kb < NT / 2; ++kb) {
+          float oa[8], ob[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const int n = 32 * kb + 8 * q + m;
+            oa[m] = bnt[n * kST + 16 * w2 + l16];
+            ob[m] = rnp[n * kSP + pch];
+          }
+          dxa[0] = mma3<true, false, false>(split8<true>(oa), split8<false>(ob), dxa[0]);
         }
-      };
-      rd(0, 0);
+      } else {
+        // B R^T over n: the operands of block kb + 1 are read while block kb's products run
+        float oa[2][4], ob[2][4];
+        auto rd = [&](int kb, int s) {
 #pragma unroll
-      for (int kb = 0; kb < NT; ++kb) {
-        if (kb + 1 < NT) rd(kb + 1, (kb + 1) & 1);
+          for (int m = 0; m < 4; ++m) {
+            const int n = 16 * kb + 4 * q + m;
+            oa[s][m] = bnt[n * kST + 16 * w2 + l16];
+            ob[s][m] = rnp[n * kSP + pch];
+          }
+        };
+        rd(0, 0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) dxa[0] = mma4(oa[kb & 1][m], ob[kb & 1][m], dxa[0]);
+        for (int kb = 0; kb < NT; ++kb) {
+          if (kb + 1 < NT) rd(kb + 1, (kb + 1) & 1);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) dxa[0] = mma4(oa[kb & 1][m], ob[kb & 1][m], dxa[0]);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) dxa[0][r] *= ser[16 * w2 + 4 * q + r];
-      mm<kCT, 1>(lcbt + 16 * w2 * kST, kST, dyt + 16 * wg * kST, kST, 0, lane, dxa);
+      if constexpr (B3) mm3<kCT, 1, false, false>(lcbt + 16 * w2 * kST, kST, dyt + 16 * wg * kST, kST, 0, lane, dxa);
+      else mm<kCT, 1>(lcbt + 16 * w2 * kST, kST, dyt + 16 * wg * kST, kST, 0, lane, dxa);
       // du = dt dX + D dy; u . dX per step; dD
       // (the lane's 4 steps of a channel are consecutive: one 16-byte store when whole and aligned)
       const int tl0 = 16 * w2 + 4 * q;
@@ -592,7 +734,10 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
       const float dec = __builtin_amdgcn_exp2f(ss2[kCT - 1]);
 #pragma unroll
       for (int j = 0; j < NR; ++j) R[j] = R[j] * dec;
-      mm<kCT, NR, true>(dyt + 16 * rpi * kST, kST, cnt + 16 * nr0 * kST, kST, 16 * kST, lane, R, ses);
+      if constexpr (B3)
+        mm3<kCT, NR, false, true, true>(dyt + 16 * rpi * kST, kST, cnt + 16 * nr0 * kST, kST, 16 * kST, lane, R, ses);
+      else
+        mm<kCT, NR, true>(dyt + 16 * rpi * kST, kST, cnt + 16 * nr0 * kST, kST, 16 * kST, lane, R, ses);
     }
 
     // ---- the decay's gradient per step (wave 0; lane j = step j; scans over the 32 steps)
