@@ -228,10 +228,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   f32x4v hacc[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) hacc[k] = f32x4v{0.f, 0.f, 0.f, 0.f};
-  if (sgi == 0 && p.h_init) {
-    // the first segment starts from the caller's state (both passes; later segments receive
-    // it through the first segment's end state)
-    const float* hi = p.h_init + b * p.hi_sb + (c0 + pch) * p.hi_sd;
+  // the first segment starts from the caller's state (later segments receive it through the
+  // first segment's end state); the state pass adds it, decayed over the segment, at its end
+  const float* const hinit = (sgi == 0 && p.h_init) ? p.h_init + b * p.hi_sb + (c0 + pch) * p.hi_sd : nullptr;
+  if (!STATE && hinit) {
+    const float* hi = hinit;
 #pragma unroll
     for (int k = 0; k < 8; ++k)
 #pragma unroll
@@ -254,7 +255,11 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
       lg += sg.dsum[sb];
     }
   }
-  float dlog = 0.f;   // log2 decay over the chunks done so far (state pass)
+  // log2 decay over the chunks done so far.  The state pass walks its segment's chunks in
+  // reverse, so that when a chunk is staged dlog is the decay from its end to the segment's
+  // end: folded into the chunk's step weights (Xd), it makes the segment's end state the plain
+  // sum of the chunks' B^T Xd, with no rescaling of the state per chunk.
+  float dlog = 0.f;
 
   // registers holding the next chunk to stage
   // u / z piece of this thread: channel 16 (tid / 64) + tid % 16, steps 8 ((tid / 16) % 4) + 0..7
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         wdt[t] = kz;
         wS[t] = sc;
         sw[bf][wave][2][t] = __builtin_amdgcn_exp2f(sc);
-        sw[bf][wave][3][t] = kz * __builtin_amdgcn_exp2f(sEnd - sc);
+        sw[bf][wave][3][t] = kz * __builtin_amdgcn_exp2f(sEnd - sc + (STATE ? dlog : 0.f));
       }
     }
     // this wave's quarter of the masked matrix (G o L)[t][s] dt_s (+ D on the diagonal), for
@@ -374,12 +379,16 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
     }
   };
 
-  prefetch(cb);
-  stage(cb, 0);
-  prefetch(cb + 1 < ce ? cb + 1 : cb);
+  // i-th chunk of the walk: in order (output pass), in reverse (state pass)
+  const int64_t nc = ce - cb;
+  auto chunk_at = [&](int64_t i) -> int64_t { return STATE ? ce - 1 - i : cb + i; };
+  prefetch(chunk_at(0));
+  stage(chunk_at(0), 0);
+  prefetch(chunk_at(1 < nc ? 1 : 0));
   __syncthreads();
-  for (int64_t c = cb; c < ce; ++c) {
-    const int bf = (int)((c - cb) & 1);
+  for (int64_t i = 0; i < nc; ++i) {
+    const int64_t c = chunk_at(i);
+    const int bf = (int)(i & 1);
     const float* wS = sw[bf][wave][1];
     const float* weS = sw[bf][wave][2];
     const float* wXd = sw[bf][wave][3];
@@ -459,31 +468,44 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
         }
       }
     }
-    // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd
+    // carry the state over the chunk: H = 2^S_{T-1} H + B^T Xd (state pass: H += B^T Xd, Xd
+    // already decayed to the segment's end)
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (k < nk) {
-        hacc[k] = hacc[k] * eT;
+        if constexpr (!STATE) hacc[k] = hacc[k] * eT;
         const bf16x8 ba = as_bf16x8(Bp[k * 64 + lane]);
         hacc[k] = mfma(ba, xdhi, hacc[k]);
         hacc[k] = mfma(ba, xdlo, hacc[k]);
       }
     }
 
-    // stage chunk c + 1 (the last chunk stages itself again, unused), store y, load chunk c + 2
-    const int64_t cn = c + 1 < ce ? c + 1 : c;
-    stage(cn, bf ^ 1);
+    // stage the walk's next chunk (the last chunk stages itself again, unused), store y, load
+    // the one after
+    const int64_t i1 = i + 1 < nc ? i + 1 : i;
+    stage(chunk_at(i1), bf ^ 1);
     if constexpr (!STATE) store_y(c * kT);
-    prefetch(c + 2 < ce ? c + 2 : cn);
+    prefetch(chunk_at(i + 2 < nc ? i + 2 : i1));
     __syncthreads();
   }
 
   if constexpr (STATE) {
     // this segment's end state (wave-ordered, as the output pass reads it) and decay
+    // (with the caller's state decayed over the whole segment)
     f32x4v* hl = reinterpret_cast<f32x4v*>(sg.hloc) + (blk * kWaves + wave) * nk * 64 + lane;
+    const float fin = __builtin_amdgcn_exp2f(dlog);
 #pragma unroll
     for (int k = 0; k < 8; ++k)
-      if (k < nk) hl[k * 64] = hacc[k];
+      if (k < nk) {
+        if (hinit) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int n = 16 * k + 4 * g16 + r;
+            if (n < p.N) hacc[k][r] += fin * hinit[n];
+          }
+        }
+        hl[k * 64] = hacc[k];
+      }
     if (tid == 0) sg.dsum[blk] = dlog;
   } else {
     // the last segment ends with the state after the last step (steps past L are the identity)
