@@ -243,16 +243,31 @@ __global__ __launch_bounds__(64 * kWaves) void ssd_scan_kernel(ScanArgs p, const
   }
   if constexpr (!STATE) {
     // the state entering this segment, from the state pass's results (j = sgi - 1 first, whose
-    // end state enters undecayed)
+    // end state enters undecayed); segment j - 1's end state is loaded while segment j's is
+    // added, so that the reads do not wait for each other one segment at a time
+    auto hand = [&](int64_t j) {
+      return reinterpret_cast<const f32x4v*>(sg.hloc) + ((j * rows + row) * kWaves + wave) * nk * 64 + lane;
+    };
+    f32x4v cur[8], nxt[8];
+    if (sgi > 0) {
+      const f32x4v* hl = hand(sgi - 1);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cur[k] = k < nk ? hl[k * 64] : f32x4v{0.f, 0.f, 0.f, 0.f};
+    }
     float lg = 0.f;
     for (int64_t j = sgi - 1; j >= 0; --j) {
-      const int64_t sb = j * rows + row;   // state-pass block of segment j of this row
+      if (j > 0) {
+        const f32x4v* hl = hand(j - 1);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) nxt[k] = k < nk ? hl[k * 64] : f32x4v{0.f, 0.f, 0.f, 0.f};
+      }
       const float f = __builtin_amdgcn_exp2f(lg);
-      const f32x4v* hl = reinterpret_cast<const f32x4v*>(sg.hloc) + (sb * kWaves + wave) * nk * 64 + lane;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        if (k < nk) hacc[k] += f * hl[k * 64];
-      lg += sg.dsum[sb];
+        if (k < nk) hacc[k] += f * cur[k];
+      lg += sg.dsum[j * rows + row];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cur[k] = nxt[k];
     }
   }
   // log2 decay over the chunks done so far.  The state pass walks its segment's chunks in
