@@ -24,6 +24,13 @@
 // the lanes' maps are combined by a shuffle scan, and each lane re-runs its steps from its true
 // incoming value.  A block holds 8 channels of one (batch, B/C group): their dB and dC
 // contributions are summed through LDS before one atomic add per (state, step).
+//
+// Few rows with long sequences (fewer 8-channel blocks than two per CU) cut each row's windows
+// into sequence segments, one block per (8 channels, segment), so that the CUs fill without
+// adding to the dB/dC atomics.  A segment starts from the adjoint the segments to its right
+// hand it: a pre-pass (bwd_seg_kernel) computes each segment's own part of the adjoint entering
+// it from the right and its total step size, and the backward block combines those of the
+// segments to its right before its walk (bwd_kernel's prologue).
 #include <algorithm>
 
 #include "ss_device.h"
@@ -215,6 +222,121 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
   }
 }
 
+// Sequence segments.  Segment j of a row covers windows [j wps, (j + 1) wps).  With the adjoint
+// recurrence g_t = C_t dy0_t + a_{t+1} g_{t+1}, the value a block carries into a window from the
+// right is a_t g_t at the first step t of the window after it.  Segment j's own part of that value
+// at its start s_j (the dy0 of its steps only) is
+//   Lj[n] = sum_{t in seg j} (prod_{s = s_j .. t} a_{s,n}) C_{t,n} dy0_t,
+// its decay Dj[n] = prod_{s in seg j} a_{s,n} = 2^(A_n log2 e Sj) with Sj its total step size,
+// and the value entering segment k from the right is R(k) = D_{k+1} R(k+1) + L_{k+1}, R(last) = 0.
+constexpr int kSegMaxN = 32;          // the segmented path serves N <= 32 (states in registers)
+constexpr int64_t kSegMinWin = 4;     // segments of at least 4 windows (2048 steps)
+
+struct BwdSegs {
+  int64_t wps;   // windows per segment
+  int32_t nseg;  // segments per row
+};
+
+// as many segments as give two 8-channel blocks per CU, none shorter than kSegMinWin windows
+BwdSegs bwd_seg_plan(const BwdArgs& a) {
+  const int64_t nwin = (a.L + kBW - 1) / kBW;
+  const int64_t blocks = a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves);
+  int64_t S = 1;
+  if (a.N <= kSegMaxN && blocks > 0)
+    S = std::min<int64_t>((2 * (int64_t)cu_count() + blocks - 1) / blocks, nwin / kSegMinWin);
+  S = std::max<int64_t>(S, 1);
+  const int64_t wps = std::max<int64_t>((nwin + S - 1) / S, 1);
+  return {wps, (int32_t)std::max<int64_t>((nwin + wps - 1) / wps, 1)};
+}
+
+// Per (row, segment j >= 1), one wave: Lj[0..N) and Sj into segw[(row nseg + j) (N + 1) + ..].
+// Lane l takes the kBK steps t0 + l kBK .. of each window of the segment, walked left to right;
+// the product of the decays from the segment's start to step t is 2^(A_n log2 e (S_w + s_t)),
+// S_w the step sizes before the window (carried as the factor dp = 2^(A_n log2 e S_w), one exp
+// per window) and s_t those of the window up to t (a prefix sum over the lanes), so that no
+// exponent grows with the segment's length.
+template <typename TIn, typename TDy, bool SCALAR, bool FGATE, int NS>
+__global__ __launch_bounds__(256) void bwd_seg_kernel(BwdArgs p, int64_t wps, int nseg, float* __restrict__ segw) {
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t rows = p.batch * p.channels;
+  if (gw >= rows * (nseg - 1)) return;
+  const int64_t row = gw / (nseg - 1);
+  const int j = 1 + (int)(gw % (nseg - 1));
+  const int64_t b = row / p.channels, d = row % p.channels;
+  const int64_t g = d / p.chan_per_group, hd = d / p.chan_per_head;
+  const int N = p.N;
+  const int64_t L = p.L;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + b * p.dl_sb + hd * p.dl_sh;
+  const TDy* dyr = static_cast<const TDy*>(p.dy) + b * p.dy_sb + d * p.dy_sd;
+  const TIn* zr = FGATE ? static_cast<const TIn*>(p.gz) + b * p.z_sb + d * p.z_sd : nullptr;
+  const TIn* Cg = static_cast<const TIn*>(p.C) + b * p.C_sb + g * p.C_sg;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  float A2[NS], acc[NS], dp[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    A2[n] = n < N ? (SCALAR ? p.A[hd] : p.A[d * p.A_sd + n]) * kLog2e : 0.f;
+    acc[n] = 0.f;
+    dp[n] = 1.f;
+  }
+  const int64_t nwin = (L + kBW - 1) / kBW;
+  const int64_t wb = (int64_t)j * wps, we = std::min<int64_t>(nwin, wb + wps);
+  float stot = 0.f;
+  for (int64_t w = wb; w < we; ++w) {
+    const int64_t t0 = w * kBW + (int64_t)lane * kBK;
+    float dv[kBK], dy0[kBK];
+    load_seg<kBK>(dr, t0, L, p.vec, dv);
+    load_seg<kBK>(dyr, t0, L, p.vec, dy0);
+    if constexpr (FGATE) {
+      // dy0 = dy s(z), s(z) = z sigmoid(z)
+      float zz[kBK];
+      load_seg<kBK>(zr, t0, L, p.vec, zz);
+#pragma unroll
+      for (int k = 0; k < kBK; ++k)
+        dy0[k] *= zz[k] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz[k] * kLog2e));
+    }
+    // step sizes summed from the window's start: within the lane, then over the lanes before it
+    float cs[kBK], run = 0.f;
+#pragma unroll
+    for (int k = 0; k < kBK; ++k) {
+      const float x = dv[k] + bias;
+      run += t0 + k < L ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+      cs[k] = run;
+    }
+    float inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const float ex = inc - run;
+    const float wtot = readlane_f(inc, 63);
+#pragma unroll
+    for (int n = 0; n < NS; ++n) {
+      if (n < N) {
+        float cv[kBK];
+        load_seg<kBK>(Cg + n * p.C_sn, t0, L, p.vec, cv);
+        float sacc = 0.f;
+#pragma unroll
+        for (int k = 0; k < kBK; ++k)
+          sacc = fmaf(__builtin_amdgcn_exp2f(A2[n] * (ex + cs[k])), cv[k] * dy0[k], sacc);
+        acc[n] = fmaf(dp[n], sacc, acc[n]);
+        dp[n] *= __builtin_amdgcn_exp2f(A2[n] * wtot);
+      }
+    }
+    stot += wtot;
+  }
+  float* out = segw + (row * nseg + j) * (N + 1);
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < N) {
+      const float v = wave_sum(acc[n]);
+      if (lane == 0) out[n] = v;
+    }
+  }
+  if (lane == 0) out[N] = stot;
+}
+
 // The backward of the ungated scan (a gated layer reaches it through launch_bwd with dy0 = dy
 // s(z) as its upstream gradient).  SP: states per group (1 or 2), the unit of the state loop (P
 // groups); one state at a time keeps the kernel within 128 VGPRs, i.e. two 8-wave blocks (four
@@ -236,7 +358,7 @@ __device__ __forceinline__ void store_steps(float* row, int64_t t0, int64_t L, c
 
 template <typename TIn, typename TDy, bool SCALAR, int SP, bool FGATE>
 __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP == 1 ? 4 : 1))) void bwd_kernel(
-    BwdArgs p, int P, int64_t nwin, const float* ckpt) {
+    BwdArgs p, int P, int64_t nwin, const float* ckpt, int64_t wps, int nseg, const float* __restrict__ segw) {
   __shared__ float gcar[kMWaves][2 * kBMaxPairs];     // adjoint carried into the window from the right
   __shared__ float dAl[kMWaves][2 * kBMaxPairs];      // dA partial sums of the wave's channel
   // dB (SP states), dC (SP states) of the window's steps, step-major ([lane][k] = step lane K + k)
@@ -250,8 +372,12 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // blocks of 8 channels of one group; when the group's channels are 4 mod 8, the last block's
   // last 4 waves work on a copy of a valid channel and contribute nothing
+  // block = segment * (batch * groups * cblocks) + channel block; the segment's windows [wlo, whi)
   const int64_t cblocks = (p.chan_per_group + kMWaves - 1) / kMWaves;
-  const int64_t bg = blockIdx.x / cblocks, qd = blockIdx.x % cblocks;
+  const int64_t nblk = p.batch * p.groups * cblocks;
+  const int64_t kseg = blockIdx.x / nblk, bx = blockIdx.x % nblk;
+  const int64_t wlo = kseg * wps, whi = std::min<int64_t>(nwin, wlo + wps);
+  const int64_t bg = bx / cblocks, qd = bx % cblocks;
   const int64_t b = bg / p.groups, g = bg % p.groups;
   const int64_t ci = qd * kMWaves + wave;
   const bool valid = ci < p.chan_per_group;
@@ -273,6 +399,18 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
     gcar[wave][i] = 0.f;
     dAl[wave][i] = 0.f;
   }
+  if (kseg + 1 < nseg) {
+    // the adjoint entering the segment from the right: R(k) = D_{k+1} R(k+1) + L_{k+1}
+    for (int n = lane; n < N; n += 64) {
+      const float A2n = (SCALAR ? p.A[hd] : p.A[d * p.A_sd + n]) * kLog2e;
+      float R = 0.f;
+      for (int64_t jj = nseg - 1; jj > kseg; --jj) {
+        const float* sj = segw + (row * nseg + jj) * (N + 1);
+        R = fmaf(__builtin_amdgcn_exp2f(A2n * sj[N]), R, sj[n]);
+      }
+      gcar[wave][n] = R;
+    }
+  }
   float dDacc = 0.f, dbacc = 0.f;
   // thread t stages row t / 64 (B of states SP pp .. SP pp + SP - 1, then C of the same), the
   // steps of lane t % 64; rows past N and steps past L are zero
@@ -291,14 +429,14 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
   };
   {
     float v[kBK];
-    bc_load(nwin - 1, 0, v);
+    bc_load(whi - 1, 0, v);
     bc_store(0, v);
   }
   __syncthreads();
   int buf = 0;
   int rb = 0;   // the reduction buffer of the current state
 
-  for (int64_t w = nwin - 1; w >= 0; --w) {
+  for (int64_t w = whi - 1; w >= wlo; --w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
     // (u and delta are loaded again at the window's end rather than kept across the state loop)
     float dt[kBK], wv[kBK], dy0[kBK], du[kBK], ddt[kBK];
@@ -345,7 +483,7 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
     }
     for (int pp = 0; pp < P; ++pp) {
       // the next group's B and C rows (the first group of the window to the left after the last)
-      const bool more = pp + 1 < P || w > 0;
+      const bool more = pp + 1 < P || w > wlo;
       float nbc[kBK];
       if (more) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
       float rB[SP][kBK], rC[SP][kBK];
@@ -598,12 +736,29 @@ hipError_t launch_t(const BwdArgs& a, float* ws, hipStream_t s) {
     if (a.scalar) hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, true>), cgrid, block, 0, s, a, P, nwin, ws);
     else hipLaunchKernelGGL((bwd_ckpt_kernel<TIn, false>), cgrid, block, 0, s, a, P, nwin, ws);
   }
-  const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves)));
+  // sequence segments: the pre-pass's results follow the checkpoints in the workspace
+  const BwdSegs sp = bwd_seg_plan(a);
+  float* segw = ws + rows * nwin * a.N;
+  if (sp.nseg > 1) {
+    const dim3 sgrid((unsigned)((rows * (sp.nseg - 1) + 3) / 4));
+#define SS_SEG(SC, FG)                                                                                     \
+  do {                                                                                                     \
+    if (a.N <= 16) hipLaunchKernelGGL((bwd_seg_kernel<TIn, TDy, SC, FG, 16>), sgrid, dim3(256), 0, s, a, sp.wps, sp.nseg, segw); \
+    else hipLaunchKernelGGL((bwd_seg_kernel<TIn, TDy, SC, FG, kSegMaxN>), sgrid, dim3(256), 0, s, a, sp.wps, sp.nseg, segw); \
+  } while (0)
+    if (a.gz) {
+      if (a.scalar) SS_SEG(true, true); else SS_SEG(false, true);
+    } else {
+      if (a.scalar) SS_SEG(true, false); else SS_SEG(false, false);
+    }
+#undef SS_SEG
+  }
+  const dim3 grid((unsigned)(a.batch * a.groups * ((a.chan_per_group + kMWaves - 1) / kMWaves) * sp.nseg));
   const dim3 mblock(64 * kMWaves);
   const float* ck = ws;
 #define SS_BWD(SC, FG)                                                                                   \
   hipLaunchKernelGGL((bwd_kernel<TIn, TDy, SC, kBwdSP, FG>), grid, mblock, 0, s, a, (a.N + kBwdSP - 1) / kBwdSP, \
-                     nwin, ck)
+                     nwin, ck, sp.wps, sp.nseg, segw)
   // (a gated call arrives here with z taken apart by launch_bwd: gz and gy0 set, the gate folded in)
   if (a.gz) {
     if (a.scalar) SS_BWD(true, true); else SS_BWD(false, true);
@@ -683,7 +838,10 @@ int64_t bwd_workspace_floats(const BwdArgs& a) {
     return ny + round64(forward_ws_floats(ungated_forward(a, nullptr), a.scalar)) + bwd_workspace_floats(b);
   }
   if (ssd_bwd_path(a)) return ssd_bwd_workspace_floats(a);
-  return a.batch * a.channels * ((a.L + kBW - 1) / kBW) * a.N;
+  // the checkpoints, then (with sequence segments) the pre-pass's N + 1 floats per (row, segment)
+  const BwdSegs sp = bwd_seg_plan(a);
+  const int64_t rows = a.batch * a.channels;
+  return rows * ((a.L + kBW - 1) / kBW) * a.N + (sp.nseg > 1 ? rows * sp.nseg * (a.N + 1) : 0);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {

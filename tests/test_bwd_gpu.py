@@ -194,6 +194,27 @@ def test_matrix_backward_bf16_dy():
               dy_dtype=torch.bfloat16)
 
 
+SEGMENT_CASES = {
+    # (rows of 8-channel blocks, windows of 512 steps): 1 block, 40 windows -> 8 segments of 5
+    "gated bf16 N16": lambda: inputs.random_problem(7301, 1, 8, 20000, 16, gate=True),
+    # 2 blocks, 20 windows (ragged last window) -> 5 segments of 4
+    "f32 N7 ragged": lambda: inputs.random_problem(7302, 1, 16, 10001, 7, in_dtype="f32", gate=False),
+    # scalar decay per head on the per-channel kernel (f32), 32 states: 12 windows -> 3 segments
+    "scalar heads of 4 f32 N32": lambda: inputs.random_problem(7303, 1, 8, 6000, 32, heads=2, scalar_decay=True,
+                                                               in_dtype="f32", gate=False),
+    # two B/C groups (2 blocks), 18 windows -> 4 segments of 5 (the last of 3)
+    "two groups bf16 N16": lambda: inputs.random_problem(7304, 1, 16, 9000, 16, groups=2, gate=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SEGMENT_CASES))
+def test_gradients_sequence_segments(case):
+    """Few rows with long sequences: the per-channel backward cuts each row into sequence
+    segments (enough for two 8-channel blocks per CU, each at least 4 windows of 512 steps), every
+    segment started from the adjoint that the segments to its right hand over."""
+    check_bwd(SEGMENT_CASES[case](), "segments: " + case)
+
+
 @pytest.mark.parametrize("case", ["12 channels", "two groups of 4", "heads of 4 in groups of 12"])
 def test_gradients_partial_channel_blocks(case):
     """The per-channel kernel takes 8 channels of a group per block: groups of 4 mod 8 channels leave
