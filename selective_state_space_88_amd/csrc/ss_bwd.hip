@@ -483,9 +483,10 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
     }
     for (int pp = 0; pp < P; ++pp) {
       // the next group's B and C rows (the first group of the window to the left after the last)
+      // (only the first 2 SP waves stage rows: the others skip the load and its bounds checks)
       const bool more = pp + 1 < P || w > wlo;
       float nbc[kBK];
-      if (more) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
+      if (more && srow < 2 * SP) bc_load(pp + 1 < P ? w : w - 1, pp + 1 < P ? pp + 1 : 0, nbc);
       float rB[SP][kBK], rC[SP][kBK];
       float dAp[SP];
 #pragma unroll
@@ -576,16 +577,21 @@ __global__ __launch_bounds__(64 * kMWaves) __attribute__((amdgpu_waves_per_eu(SP
         }
       if (more) bc_store(buf ^ 1, nbc);
       __syncthreads();
-      for (int i = threadIdx.x; i < 2 * SP * kBW; i += 64 * kMWaves) {
-        const int which = i / kBW, r = i % kBW;
-        const int n = SP * pp + (which % SP);
-        const int64_t t = w * kBW + r;
-        if (n < N && t < L) {
-          float v = 0.f;
+      // one step per thread (kBW = 64 kMWaves), one row of dB or dC per pass: the row's base is
+      // uniform
+      static_assert(kBW == 64 * kMWaves, "one step per thread");
+      {
+        const int64_t t = w * kBW + (int64_t)threadIdx.x;
 #pragma unroll
-          for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[rb][wv2][which][r];
-          float* dst = (which < SP ? dBg + n * p.dB_sn : dCg + n * p.dC_sn) + t;
-          atomicAdd(dst, v);
+        for (int which = 0; which < 2 * SP; ++which) {
+          const int n = SP * pp + (which % SP);
+          if (n < N && t < L) {
+            float v = 0.f;
+#pragma unroll
+            for (int wv2 = 0; wv2 < kMWaves; ++wv2) v += red[rb][wv2][which][threadIdx.x];
+            float* const base = which < SP ? dBg + n * p.dB_sn : dCg + n * p.dC_sn;
+            atomicAdd(base + t, v);
+          }
         }
       }
       // (no second barrier: the next state writes the other buffer, and this one again only
