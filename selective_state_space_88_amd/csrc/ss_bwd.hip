@@ -32,6 +32,7 @@
 // it from the right and its total step size, and the backward block combines those of the
 // segments to its right before its walk (bwd_kernel's prologue).
 #include <algorithm>
+#include <type_traits>
 
 #include "ss_device.h"
 #include "ss_launch.h"
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
 // and the value entering segment k from the right is R(k) = D_{k+1} R(k+1) + L_{k+1}, R(last) = 0.
 constexpr int kSegMaxN = 32;          // the segmented path serves N <= 32 (states in registers)
 constexpr int64_t kSegMinWin = 4;     // segments of at least 4 windows (2048 steps)
+constexpr int kSegG = 8;              // states whose C rows the pre-pass loads together
 
 struct BwdSegs {
   int64_t wps;   // windows per segment
@@ -247,6 +249,41 @@ BwdSegs bwd_seg_plan(const BwdArgs& a) {
   S = std::max<int64_t>(S, 1);
   const int64_t wps = std::max<int64_t>((nwin + S - 1) / S, 1);
   return {wps, (int32_t)std::max<int64_t>((nwin + wps - 1) / wps, 1)};
+}
+
+// kBK steps of an aligned row lying wholly inside L, as the raw words of one or two 16-byte loads
+// (issued by raw_load, widened by raw_widen: a group of loads can be issued before any waits)
+template <typename T>
+struct RawSteps;
+template <>
+struct RawSteps<bf16_t> {
+  u32x4 v;
+};
+template <>
+struct RawSteps<float> {
+  f32x4 a, b;
+};
+__device__ __forceinline__ void raw_load(const bf16_t* p, RawSteps<bf16_t>& r) {
+  r.v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void raw_load(const float* p, RawSteps<float>& r) {
+  r.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  r.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p) + 1);
+}
+__device__ __forceinline__ void raw_widen(const RawSteps<bf16_t>& r, float (&o)[kBK]) {
+  const uint32_t w[4] = {r.v.x, r.v.y, r.v.z, r.v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[2 * e] = bf16_lo(w[e]);
+    o[2 * e + 1] = bf16_hi(w[e]);
+  }
+}
+__device__ __forceinline__ void raw_widen(const RawSteps<float>& r, float (&o)[kBK]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o[e] = r.a[e];
+    o[4 + e] = r.b[e];
+  }
 }
 
 // Per (row, segment j >= 1), one wave: Lj[0..N) and Sj into segw[(row nseg + j) (N + 1) + ..].
@@ -284,13 +321,25 @@ __global__ __launch_bounds__(256) void bwd_seg_kernel(BwdArgs p, int64_t wps, in
   float stot = 0.f;
   for (int64_t w = wb; w < we; ++w) {
     const int64_t t0 = w * kBW + (int64_t)lane * kBK;
-    float dv[kBK], dy0[kBK];
-    load_seg<kBK>(dr, t0, L, p.vec, dv);
-    load_seg<kBK>(dyr, t0, L, p.vec, dy0);
+    // a whole window of aligned rows takes its loads back to back (wave-uniform)
+    const bool whole = p.vec && (w + 1) * kBW <= L;
+    float dv[kBK], dy0[kBK], zz[kBK];
+    if (whole) {
+      RawSteps<TIn> rd, rz;
+      RawSteps<TDy> ry;
+      raw_load(dr + t0, rd);
+      raw_load(dyr + t0, ry);
+      if constexpr (FGATE) raw_load(zr + t0, rz);
+      raw_widen(rd, dv);
+      raw_widen(ry, dy0);
+      if constexpr (FGATE) raw_widen(rz, zz);
+    } else {
+      load_seg<kBK>(dr, t0, L, p.vec, dv);
+      load_seg<kBK>(dyr, t0, L, p.vec, dy0);
+      if constexpr (FGATE) load_seg<kBK>(zr, t0, L, p.vec, zz);
+    }
     if constexpr (FGATE) {
       // dy0 = dy s(z), s(z) = z sigmoid(z)
-      float zz[kBK];
-      load_seg<kBK>(zr, t0, L, p.vec, zz);
 #pragma unroll
       for (int k = 0; k < kBK; ++k)
         dy0[k] *= zz[k] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-zz[k] * kLog2e));
@@ -312,16 +361,36 @@ __global__ __launch_bounds__(256) void bwd_seg_kernel(BwdArgs p, int64_t wps, in
     const float ex = inc - run;
     const float wtot = readlane_f(inc, 63);
 #pragma unroll
-    for (int n = 0; n < NS; ++n) {
-      if (n < N) {
-        float cv[kBK];
-        load_seg<kBK>(Cg + n * p.C_sn, t0, L, p.vec, cv);
-        float sacc = 0.f;
+    for (int k = 0; k < kBK; ++k) cs[k] += ex;
+    // the C rows of kSegG states are loaded together (rows past N repeat the last one, unused),
+    // so that a window waits for them once per group rather than once per state
 #pragma unroll
-        for (int k = 0; k < kBK; ++k)
-          sacc = fmaf(__builtin_amdgcn_exp2f(A2[n] * (ex + cs[k])), cv[k] * dy0[k], sacc);
-        acc[n] = fmaf(dp[n], sacc, acc[n]);
-        dp[n] *= __builtin_amdgcn_exp2f(A2[n] * wtot);
+    for (int n0 = 0; n0 < NS; n0 += kSegG) {
+      if (n0 < N) {
+        float cv[kSegG][kBK];
+        if (whole) {
+          RawSteps<TIn> raw[kSegG];
+#pragma unroll
+          for (int i = 0; i < kSegG; ++i) raw_load(Cg + (int64_t)(n0 + i < N ? n0 + i : N - 1) * p.C_sn + t0, raw[i]);
+#pragma unroll
+          for (int i = 0; i < kSegG; ++i) raw_widen(raw[i], cv[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < kSegG; ++i)
+            load_seg<kBK>(Cg + (int64_t)(n0 + i < N ? n0 + i : N - 1) * p.C_sn, t0, L, p.vec, cv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < kSegG; ++i) {
+          const int n = n0 + i;
+          if (n < N) {
+            float sacc = 0.f;
+#pragma unroll
+            for (int k = 0; k < kBK; ++k)
+              sacc = fmaf(__builtin_amdgcn_exp2f(A2[n] * cs[k]), cv[i][k] * dy0[k], sacc);
+            acc[n] = fmaf(dp[n], sacc, acc[n]);
+            dp[n] *= __builtin_amdgcn_exp2f(A2[n] * wtot);
+          }
+        }
       }
     }
     stot += wtot;
