@@ -407,6 +407,113 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
   }
 }
 
+// Sequence segments of pass 2.  With fewer (batch, head, slab) rows than about five per CU, each
+// row's chunks are cut into segments of cps chunks, one pass-2 block per (row, segment), so that
+// every CU has blocks to run.  Walking chunk c leaves R <- D_c R + Q_c (D_c = 2^(A log2 e dt-sum
+// of c), Q_c = dY^T diag(e^s) C), so segment j's own part of the R it hands to the segment on its
+// left, and its decay, are
+//   Lj = sum_{t in seg j} 2^(A log2 e S_t) dY_t^T C_t,   Dj = 2^(A log2 e S_end)
+// with S_t the step sizes summed from the segment's first step to t; the R entering segment k
+// from the right is R(k) = D_{k+1} R(k+1) + L_{k+1}, R(last) = 0.  The pre-pass below forms Lj
+// (a [64 x N] product over the segment's steps, on the matrix cores like pass 2's R update) and
+// log2 Dj; pass 2's prologue combines those of the segments to its right.
+struct SegsB {
+  int64_t cps;   // chunks per segment
+  int32_t nseg;  // segments per row
+};
+
+SegsB ssdb_seg_plan(const BwdArgs& a) {
+  const int64_t nch = (a.L + kCT - 1) / kCT;
+  const int64_t rows = a.batch * a.heads * (a.chan_per_head / kCP);
+  int64_t S = 1;
+  if (rows > 0) S = std::min<int64_t>((5 * (int64_t)cu_count() + rows - 1) / rows, nch / 8);
+  S = std::max<int64_t>(S, 1);
+  const int64_t cps = std::max<int64_t>((nch + S - 1) / S, 1);
+  return {cps, (int32_t)std::max<int64_t>((nch + cps - 1) / cps, 1)};
+}
+
+// per (row, segment): Lj as [64][NP] f32, then log2 Dj
+template <int NP>
+constexpr int64_t seg_floats() { return (int64_t)kCP * NP + 1; }
+
+// One block of 4 waves per (row, segment j >= 1); wave w forms rows p = 16 w .. of Lj.
+template <typename TIn, typename TDy, int NT>
+__global__ __launch_bounds__(kThr) void ssdb_seg_kernel(BwdArgs p, int64_t nch, SegsB sg, float* __restrict__ segw) {
+  constexpr int NP = 16 * NT;
+  constexpr bool B3 = std::is_same<TIn, bf16_t>::value;
+  __shared__ __attribute__((aligned(16))) float dyt[kCP * kST];   // dy [p][t]
+  __shared__ __attribute__((aligned(16))) float cnt[NP * kST];    // C [n][t]
+  __shared__ __attribute__((aligned(16))) float wts[kCT];         // 2^(A log2 e S_t)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nrow = p.batch * p.heads * (p.chan_per_head / kCP);
+  const int64_t rowi = blockIdx.x % nrow;
+  const int j = 1 + (int)(blockIdx.x / nrow);
+  const Blk k = block_of(p, rowi);
+  const int N = p.N;
+  const int64_t L = p.L;
+  const float A2 = p.A[k.h] * kLog2e;
+  const float bias = p.bias ? p.bias[k.h] : 0.f;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + k.b * p.dl_sb + k.h * p.dl_sh;
+  const TDy* yb = static_cast<const TDy*>(p.dy) + k.b * p.dy_sb + k.d0 * p.dy_sd;
+  const TIn* Cb = static_cast<const TIn*>(p.C) + k.b * p.C_sb + k.g * p.C_sg;
+  const int64_t cb = (int64_t)j * sg.cps, ce = std::min<int64_t>(nch, cb + sg.cps);
+  const int pp = tid >> 2, tt = 8 * (tid & 3);   // dy row and steps; C rows pp and pp + 64
+  f32x4 acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lg = 0.f;   // log2 decay from the segment's start to the chunk's (wave 0)
+  float py[8], pc0[8], pc1[8], pdl = 0.f;
+  auto fetch = [&](int64_t c) {
+    const int64_t t0 = c * kCT;
+    load_seg<8>(yb + pp * p.dy_sd, t0 + tt, L, p.vec, py);
+    if (pp < N) load_seg<8>(Cb + pp * p.C_sn, t0 + tt, L, p.vec, pc0);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pc0[e] = 0.f;
+    }
+    if (NP > 64 && pp + 64 < N) load_seg<8>(Cb + (pp + 64) * p.C_sn, t0 + tt, L, p.vec, pc1);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pc1[e] = 0.f;
+    }
+    if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
+  };
+  fetch(cb);
+  for (int64_t c = cb; c < ce; ++c) {
+    const int64_t t0 = c * kCT;
+    if (wave == 0) {
+      const bool live = lane < kCT && t0 + lane < L;
+      const float x = pdl + bias;
+      const float dt = live ? (p.softplus ? softplus_fast(x) : x) : 0.f;
+      const float sc = scan32(dt * A2);
+      if (lane < kCT) wts[lane] = __builtin_amdgcn_exp2f(lg + sc);
+      lg += lane_f(sc, kCT - 1);
+    }
+    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt) = f32x4{py[0], py[1], py[2], py[3]};
+    *reinterpret_cast<f32x4*>(dyt + pp * kST + tt + 4) = f32x4{py[4], py[5], py[6], py[7]};
+    if (pp < NP) {
+      *reinterpret_cast<f32x4*>(cnt + pp * kST + tt) = f32x4{pc0[0], pc0[1], pc0[2], pc0[3]};
+      *reinterpret_cast<f32x4*>(cnt + pp * kST + tt + 4) = f32x4{pc0[4], pc0[5], pc0[6], pc0[7]};
+    }
+    if (NP > 64 && pp + 64 < NP) {
+      *reinterpret_cast<f32x4*>(cnt + (pp + 64) * kST + tt) = f32x4{pc1[0], pc1[1], pc1[2], pc1[3]};
+      *reinterpret_cast<f32x4*>(cnt + (pp + 64) * kST + tt + 4) = f32x4{pc1[4], pc1[5], pc1[6], pc1[7]};
+    }
+    __syncthreads();
+    if (c + 1 < ce) fetch(c + 1);
+    if constexpr (B3) mm3<kCT, NT, false, true, true>(dyt + 16 * wave * kST, kST, cnt, kST, 16 * kST, lane, acc, wts);
+    else mm<kCT, NT, true>(dyt + 16 * wave * kST, kST, cnt, kST, 16 * kST, lane, acc, wts);
+    __syncthreads();
+  }
+  float* out = segw + (rowi * sg.nseg + j) * seg_floats<NP>();
+  const int q = lane >> 4, l16 = lane & 15;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[(16 * wave + 4 * q + r) * NP + 16 * t + l16] = acc[t][r];
+  if (tid == 0) out[kCP * NP] = lg;
+}
+
 // Pass 2: the chunks in reverse, 8 waves (two per SIMD, so that one wave's LDS and MFMA waits
 // are covered by the other's work).  Tiles per wave w: DX and C B^T (w < 4: rows 16 (w / 2),
 // columns 16 (w % 2)); [T x N] products dY H0, X R, dC, dB (rows 16 (w % 2), state tiles
@@ -415,7 +522,8 @@ __global__ __launch_bounds__(kThr) void ssdb_state_kernel(BwdArgs p, int64_t nch
 constexpr int kThrB = 512;
 template <typename TIn, typename TDy, int NT>
 __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch, const float* __restrict__ ws,
-                                                          const float* __restrict__ cbws) {
+                                                          const float* __restrict__ cbws, SegsB sg,
+                                                          const float* __restrict__ segw) {
   constexpr int NP = 16 * NT;
   constexpr int NB = NT >= 4 ? NT / 4 : 1;   // [T x N] state tiles per wave
   constexpr int NR = NT / 2;                 // R state tiles per wave
@@ -437,7 +545,11 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
   __shared__ float alp[4][kCT], bet[4][kCT], udp[4][kCT], rowp[2][kCT], colp[2][kCT], rh0[8];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int q = lane >> 4, l16 = lane & 15;
-  const Blk k = block_of(p, blockIdx.x);
+  // block = segment * rows + (batch, head, slab) row; the segment's chunks [cbeg, cend)
+  const int64_t nrow = p.batch * p.heads * (p.chan_per_head / kCP);
+  const int64_t rowi = blockIdx.x % nrow, sgi = blockIdx.x / nrow;
+  const int64_t cbeg = sgi * sg.cps, cend = std::min<int64_t>(nch, cbeg + sg.cps);
+  const Blk k = block_of(p, rowi);
   const int N = p.N;
   const int64_t L = p.L;
   const float Ah = p.A[k.h], A2 = Ah * kLog2e;
@@ -452,7 +564,7 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
   float* dCb = p.dC + k.b * p.dC_sb + k.g * p.dC_sg;
   float* dub = p.du + k.b * p.du_sb + k.d0 * p.du_sd;
   float* ddb = p.ddelta + k.b * p.dd_sb + k.h * p.dd_sh;
-  const float* wsb = ws + (int64_t)blockIdx.x * nch * NP * kCP;
+  const float* wsb = ws + rowi * nch * NP * kCP;
   const float* cbg = cbws + (k.b * p.groups + k.g) * nch * 1024;
   const int w2 = wave & 1, wg = wave >> 1;      // row block of 16 steps, and a group of four
   const bool dxw = wave < 4;                    // the waves forming DX and C B^T
@@ -464,7 +576,7 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
     const float* hc = wsb + c * NP * kCP;
     for (int i = wave; i < NP / 4; i += 8) dma16(hc + i * 256 + 4 * lane, hnp + i * 256);
   };
-  h0_copy(nch - 1);
+  h0_copy(cend - 1);
   // this thread's share of a chunk's loads, fetched one chunk ahead: u and dy (threads < 256: row
   // pp, 8 steps from tt), B and C (row bn, 8 steps from bt8), the raw step (wave 0)
   const int pp = (tid & 255) >> 2, tt = 8 * (tid & 3);
@@ -487,17 +599,27 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
     }
     if (wave == 0) pdl = (lane < kCT && t0 + lane < L) ? to_f32(dr[t0 + lane]) : 0.f;
   };
-  fetch(nch - 1);
+  fetch(cend - 1);
   // D of the channel this lane's dX tile covers
   const int pch = 16 * wg + l16;
   const float Dp = p.D ? p.D[p.d_per_head ? k.h : k.d0 + pch] : 0.f;
   f32x4 R[NR];   // R[p = 16 rpi + 4 q + r][n = 16 (nr0 + j) + l16]
 #pragma unroll
   for (int j = 0; j < NR; ++j) R[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the R entering the segment from the right: R(k) = D_{k+1} R(k+1) + L_{k+1}
+  for (int64_t jj = sg.nseg - 1; jj > sgi; --jj) {
+    const float* sj = segw + (rowi * sg.nseg + jj) * seg_floats<NP>();
+    const float dj = __builtin_amdgcn_exp2f(sj[kCP * NP]);
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        R[j][r] = fmaf(dj, R[j][r], sj[(16 * rpi + 4 * q + r) * NP + 16 * (nr0 + j) + l16]);
+  }
   float dDl = 0.f;
   float dAacc = 0.f, dbacc = 0.f;
 
-  for (int64_t c = nch - 1; c >= 0; --c) {
+  for (int64_t c = cend - 1; c >= cbeg; --c) {
     const int64_t t0 = c * kCT;
     // ---- staging (from the registers fetched during the previous chunk)
     if (wave == 0) {
@@ -623,7 +745,7 @@ __global__ __launch_bounds__(kThrB) void ssdb_main_kernel(BwdArgs p, int64_t nch
       if (lane == 0) rh0[wave] = rh;
     }
     __syncthreads();   // m1, m1t, lcbt, row and column sums, alp, bet, rh0 ready; hnp no longer read
-    if (c > 0) {
+    if (c > cbeg) {
       h0_copy(c - 1);   // lands while this chunk's second half runs
       fetch(c - 1);
     }
@@ -799,8 +921,15 @@ hipError_t launch_nt(const BwdArgs& a, float* ws, hipStream_t s) {
   const dim3 grid((unsigned)(a.batch * a.heads * (a.chan_per_head / kCP))), block(kThr);
   float* cbws = ws + a.batch * a.heads * (a.chan_per_head / kCP) * nch * (16 * NT) * kCP;
   hipLaunchKernelGGL((ssdb_state_kernel<TIn, NT>), dim3(kStateSplit<NT> * grid.x), block, 0, s, a, nch, ws, cbws);
-  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), grid, dim3(kThrB), 0, s, a, nch,
-                     static_cast<const float*>(ws), static_cast<const float*>(cbws));
+  // sequence segments of pass 2: the pre-pass's results follow the C B^T records
+  const SegsB sg = ssdb_seg_plan(a);
+  float* segw = cbws + a.batch * a.groups * nch * 1024;
+  if (sg.nseg > 1)
+    hipLaunchKernelGGL((ssdb_seg_kernel<TIn, TDy, NT>), dim3((unsigned)(grid.x * (sg.nseg - 1))), block, 0, s, a, nch,
+                       sg, segw);
+  hipLaunchKernelGGL((ssdb_main_kernel<TIn, TDy, NT>), dim3((unsigned)(grid.x * sg.nseg)), dim3(kThrB), 0, s, a,
+                     nch, static_cast<const float*>(ws), static_cast<const float*>(cbws), sg,
+                     static_cast<const float*>(segw));
   return hipGetLastError();
 }
 
@@ -820,8 +949,12 @@ bool ssd_bwd_path(const BwdArgs& a) {
 int64_t ssd_bwd_workspace_floats(const BwdArgs& a) {
   const int64_t np = a.N <= 32 ? 32 : a.N <= 64 ? 64 : 128;
   const int64_t nch = (a.L + kCT - 1) / kCT;
-  // chunk states, then C B^T of every (batch, group, chunk)
-  return a.batch * a.heads * (a.chan_per_head / kCP) * nch * np * kCP + a.batch * a.groups * nch * 1024;
+  // chunk states, then C B^T of every (batch, group, chunk), then (with sequence segments) the
+  // pre-pass's [64][np] + 1 floats per (row, segment)
+  const int64_t rows = a.batch * a.heads * (a.chan_per_head / kCP);
+  const SegsB sg = ssdb_seg_plan(a);
+  return rows * nch * np * kCP + a.batch * a.groups * nch * 1024 +
+         (sg.nseg > 1 ? rows * sg.nseg * (kCP * np + 1) : 0);
 }
 
 hipError_t launch_ssd_bwd(const BwdArgs& a, float* ws, hipStream_t s) {

@@ -151,6 +151,26 @@ GATED_MATRIX_CASES = {
 }
 
 
+MATRIX_SEGMENT_CASES = {
+    # few (batch, head, slab) rows and long sequences: the matrix form's reverse pass is cut into
+    # sequence segments (at least 8 chunks of 32 steps each), each started from the R that the
+    # segments to its right hand over
+    "N128 bf16 L5000, 19 segments": lambda: inputs.random_problem(790, 1, 64, 5000, 128, heads=1, scalar_decay=True,
+                                                                 gate=False),
+    "N33 f32 ragged L4001, 15 segments": lambda: inputs.random_problem(791, 1, 64, 4001, 33, heads=1,
+                                                                      scalar_decay=True, in_dtype="f32", gate=False),
+    "gated N64 bf16 two heads L3000": lambda: inputs.random_problem(792, 1, 128, 3000, 64, heads=2, scalar_decay=True,
+                                                                   gate=True),
+    "N16 f32 two batches L2600": lambda: inputs.random_problem(793, 2, 64, 2600, 16, heads=1, scalar_decay=True,
+                                                               in_dtype="f32", gate=False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MATRIX_SEGMENT_CASES))
+def test_matrix_backward_sequence_segments(case):
+    check_bwd(MATRIX_SEGMENT_CASES[case](), "matrix segments: " + case)
+
+
 @pytest.mark.parametrize("case", sorted(GATED_MATRIX_CASES))
 def test_gated_matrix_backward(case):
     check_bwd(GATED_MATRIX_CASES[case](), "gated matrix " + case)
