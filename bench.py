@@ -322,7 +322,14 @@ def backward_bench(args, p, to_dev, dev):
             rev = 4 * 2 * 2 + bcw * (2 * NB * 3 + 2 * NB * 2 + 2 * NB * 2) + 8 * (NT // 2 * 2 + 3 + NR * 2)
             fwd = SPL * 4 * (NT // SPL) * 2
             cbt = 4 * (16 * NT // 32)
-            mf = (blocks * nch * (rev + fwd) + p.batch * p.groups * nch * cbt) * 16384.0
+            # the reverse pass's sequence segments (about five blocks per CU, at least 8 chunks
+            # each): a pre-pass over every segment but the first forms its part of the adjoint,
+            # 4 waves x NT tiles x 2 (dy split, C exact) per chunk
+            S = max(1, min(-(-5 * 256 // blocks), nch // 8))
+            cps = -(-nch // S)
+            pre_chunks = nch - cps if -(-nch // cps) > 1 else 0
+            mf = (blocks * nch * (rev + fwd) + blocks * pre_chunks * 4 * NT * 2 +
+                  p.batch * p.groups * nch * cbt) * 16384.0
             peak = BF16_MFMA_PEAK_TFLOPS
         else:
             # v_mfma_f32_16x16x4_f32 (2048 flops each)

@@ -426,7 +426,10 @@ SegsB ssdb_seg_plan(const BwdArgs& a) {
   const int64_t nch = (a.L + kCT - 1) / kCT;
   const int64_t rows = a.batch * a.heads * (a.chan_per_head / kCP);
   int64_t S = 1;
-  if (rows > 0) S = std::min<int64_t>((5 * (int64_t)cu_count() + rows - 1) / rows, nch / 8);
+#ifndef SS_SSDB_SEG_ROUNDS
+#define SS_SSDB_SEG_ROUNDS 5   // pass-2 blocks per CU the segments aim for (a tuning override)
+#endif
+  if (rows > 0) S = std::min<int64_t>((SS_SSDB_SEG_ROUNDS * (int64_t)cu_count() + rows - 1) / rows, nch / 8);
   S = std::max<int64_t>(S, 1);
   const int64_t cps = std::max<int64_t>((nch + S - 1) / S, 1);
   return {cps, (int32_t)std::max<int64_t>((nch + cps - 1) / cps, 1)};
