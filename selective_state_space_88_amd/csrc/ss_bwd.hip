@@ -232,7 +232,9 @@ __global__ __launch_bounds__(64 * kBWaves) void bwd_ckpt_kernel(BwdArgs p, int P
 // and the value entering segment k from the right is R(k) = D_{k+1} R(k+1) + L_{k+1}, R(last) = 0.
 constexpr int kSegMaxN = 32;          // the segmented path serves N <= 32 (states in registers)
 constexpr int64_t kSegMinWin = 4;     // segments of at least 4 windows (2048 steps)
-constexpr int kSegG = 8;              // states whose C rows the pre-pass loads together
+// states whose C rows the pre-pass loads together (measured on the 1M-step layer's backward:
+// 4: 35.0, 8: 35.6, 16: 36.7 ms per call; 4 keeps three waves per SIMD)
+constexpr int kSegG = 4;
 
 struct BwdSegs {
   int64_t wps;   // windows per segment
