@@ -171,6 +171,14 @@ def test_matrix_backward_sequence_segments(case):
     check_bwd(MATRIX_SEGMENT_CASES[case](), "matrix segments: " + case)
 
 
+def test_sequence_segments_bf16_upstream_gradient():
+    """dy in bf16 through both segmented layouts (the pre-passes read dy in its own type)."""
+    torch = torch_dev()
+    check_bwd(inputs.random_problem(7305, 1, 8, 12000, 16, gate=True), "segments, bf16 dy", dy_dtype=torch.bfloat16)
+    check_bwd(inputs.random_problem(794, 1, 64, 4096, 64, heads=1, scalar_decay=True, gate=False),
+              "matrix segments, bf16 dy", dy_dtype=torch.bfloat16)
+
+
 @pytest.mark.parametrize("case", sorted(GATED_MATRIX_CASES))
 def test_gated_matrix_backward(case):
     check_bwd(GATED_MATRIX_CASES[case](), "gated matrix " + case)
