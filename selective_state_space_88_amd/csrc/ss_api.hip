@@ -305,13 +305,19 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
   if (scalar && A->stride[0] != 1 && A->shape[0] > 1) return SS_ERR_STRIDE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (!scalar) return ss::launch_diag(a, s) == hipSuccess ? SS_OK : SS_ERR_HIP;
-
-  // scalar decay: stream-ordered workspace for B/C (and, on the matrix path, C B^T per chunk)
-  // in the order the kernel reads them
-  const bool mfma = ss::ssd_path(a);
+  // diagonal decay: a workspace only when few long rows are cut into sequence segments; scalar
+  // decay: stream-ordered workspace for B/C (and, on the matrix path, C B^T per chunk) in the
+  // order the kernel reads them
+  const bool mfma = scalar && ss::ssd_path(a);
+  const int64_t wsb = !scalar ? ss::diag_workspace_bytes(a)
+                      : mfma  ? ss::ssd_workspace_bytes(a)
+                              : ss::scalar_workspace_floats(a) * (int64_t)sizeof(float);
+  if (!scalar && wsb == 0) return ss::launch_diag(a, s) == hipSuccess ? SS_OK : SS_ERR_HIP;
+  auto run = [&](void* ws) -> hipError_t {
+    if (!scalar) return ss::launch_diag(a, ws, s);
+    return mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
+  };
   void* ws = nullptr;
-  const int64_t wsb = mfma ? ss::ssd_workspace_bytes(a) : ss::scalar_workspace_floats(a) * (int64_t)sizeof(float);
   if (noalloc) {
     // the static scratch: every byte the kernels read they write first, so nothing is cleared
     if (wsb > (int64_t)SS_NOALLOC_SCRATCH_BYTES) return SS_ERR_SCRATCH;
@@ -319,14 +325,13 @@ int scan_common(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A, 
       (void)hipGetLastError();
       return SS_ERR_HIP;
     }
-    const hipError_t e = mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
-    return e == hipSuccess ? SS_OK : SS_ERR_HIP;
+    return run(ws) == hipSuccess ? SS_OK : SS_ERR_HIP;
   }
   if (ws_alloc(&ws, (size_t)wsb, s) != hipSuccess) {
     (void)hipGetLastError();
     return SS_ERR_HIP;
   }
-  const hipError_t e = mfma ? ss::launch_ssd(a, ws, s) : ss::launch_scalar(a, static_cast<float*>(ws), s);
+  const hipError_t e = run(ws);
   const hipError_t f = hipFreeAsync(ws, s);
   return (e == hipSuccess && f == hipSuccess) ? SS_OK : SS_ERR_HIP;
 }

@@ -1508,6 +1508,164 @@ hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+
+// ---- Sequence segments for few rows with long sequences (the window-slot path, one batch row).
+// With fewer (batch, channel) rows than four per CU the window slots leave CUs idle.  The row's
+// steps are then cut into S segments of equal length, each run by the window-slot kernel as a
+// row of its own (segment j as batch index j: every time row is contiguous, so its offset is j
+// times the segment length), started from the state the segments before it hand over.  A
+// pre-pass gives, per (channel, segment j < S - 1), the segment's end state from a zero state,
+//   E_j[n] = sum_{t in seg j} (prod_{s = t+1 .. end} a_{s,n}) dt_t u_t B_{t,n},
+// and its total step size T_j (its decay is 2^(A_n log2 e T_j)); a combine pass forms the state
+// entering each segment, H(0) = h_init (or 0), H(j + 1) = 2^(A_n log2 e T_j) H(j) + E_j.
+constexpr int kFsK = 8;                 // steps per lane of the pre-pass
+constexpr int kFsW = 64 * kFsK;         // steps per pre-pass iteration
+
+struct FwdSegs {
+  int64_t seg_len;   // steps per segment
+  int32_t nseg;      // segments (1: none)
+  int32_t sub;       // pre-pass pieces per segment (the pre-pass and the combine work on pieces)
+};
+
+bool slots_path(const ScanArgs& a);
+
+// Segments apply to the plain exponential-Euler forward (no zero-order hold, trapezoid or
+// checkpoints) of one batch row with N <= 32 on the window-slot path: S the largest power of two with S
+// rows per channel fitting one round of the slots (4 per CU), L a multiple of S windows and at
+// least kSlots windows per segment.
+FwdSegs fwd_seg_plan(const ScanArgs& a) {
+  constexpr int64_t W = 64 * kK;
+  FwdSegs f{a.L, 1, 1};
+#ifdef SS_NO_FWD_SEGS
+  return f;   // (an ablation build: no segments)
+#endif
+  if (a.batch != 1 || a.zoh || a.trap || a.ckpt || a.N > 32 || !slots_path(a) || a.channels <= 0) return f;
+  const int64_t cap = (int64_t)kWaves * cu_count() / a.channels;
+  int64_t S = 1;
+  while (2 * S <= cap && a.L % (2 * S * W) == 0 && a.L / (2 * S * W) >= kSlots) S *= 2;
+  if (S == 1) return f;
+  // pieces: enough pre-pass waves for about four per SIMD (one wave per channel and piece)
+  const int64_t seg = a.L / S, want = 16 * (int64_t)cu_count();
+  int64_t m = 1;
+  while (a.channels * (S * m - 1) < want && seg % (2 * m * kFsW) == 0) m *= 2;
+  return FwdSegs{seg, (int32_t)S, (int32_t)m};
+}
+
+// One wave per (channel d, piece j < P - 1) of the row's P equal pieces (a segment's pre-pass is
+// cut into pieces so that it has enough waves; the combine composes them): E_j[0..N) and T_j into
+// segw[(d (P - 1) + j) (N + 1) + ..].  The piece is walked from its end, kFsW steps at a time; the product of the decays
+// after step t is 2^(A_n log2 e (T_after + s_t)), T_after the step sizes of the iterations walked
+// so far (carried as the factor dp = 2^(A_n log2 e T_after)) and s_t those after t inside the
+// iteration (its total minus the prefix up to t).
+template <int NS>
+__global__ __launch_bounds__(256) void fwd_seg_kernel(ScanArgs p, int64_t plen, int npieces, float* __restrict__ segw) {
+  using TIn = bf16_t;
+  const int lane = threadIdx.x & 63;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (gw >= p.channels * (npieces - 1)) return;
+  const int64_t d = gw / (npieces - 1);
+  const int j = (int)(gw % (npieces - 1));
+  const int64_t g = d / p.chan_per_group, hd = d / p.chan_per_head;
+  const int N = p.N;
+  const TIn* ur = static_cast<const TIn*>(p.u) + d * p.u_sd;
+  const TIn* dr = static_cast<const TIn*>(p.delta) + hd * p.dl_sh;
+  const TIn* Bg = static_cast<const TIn*>(p.B) + g * p.B_sg;
+  const float bias = p.bias ? p.bias[hd] : 0.f;
+  float A2[NS], acc[NS], dp[NS];
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    A2[n] = n < N ? p.A[d * p.A_sd + n] * kLog2e : 0.f;
+    acc[n] = 0.f;
+    dp[n] = 1.f;
+  }
+  const int64_t tb = (int64_t)j * plen;
+  float stot = 0.f;
+  for (int64_t i = plen / kFsW - 1; i >= 0; --i) {
+    const int64_t t0 = tb + i * kFsW + (int64_t)lane * kFsK;   // (whole, aligned: the plan's L)
+    const u32x4 rd = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dr + t0));
+    const u32x4 ru = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ur + t0));
+    const uint32_t wd[4] = {rd.x, rd.y, rd.z, rd.w}, wu[4] = {ru.x, ru.y, ru.z, ru.w};
+    float cs[kFsK], wv[kFsK], run = 0.f;
+#pragma unroll
+    for (int k = 0; k < kFsK; ++k) {
+      const float x = ((k & 1) ? bf16_hi(wd[k / 2]) : bf16_lo(wd[k / 2])) + bias;
+      const float dt = p.softplus ? softplus_fast(x) : x;
+      run += dt;
+      cs[k] = run;
+      wv[k] = dt * ((k & 1) ? bf16_hi(wu[k / 2]) : bf16_lo(wu[k / 2]));
+    }
+    // step sizes after each step inside the iteration: its total minus the prefix up to the step
+    float inc = run;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const float wtot = readlane_f(inc, 63);
+    const float ex = inc - run;
+#pragma unroll
+    for (int k = 0; k < kFsK; ++k) cs[k] = wtot - (ex + cs[k]);
+#pragma unroll
+    for (int n0 = 0; n0 < NS; n0 += 4) {
+      if (n0 < N) {
+        u32x4 rb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rb[q] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(Bg + (int64_t)(n0 + q < N ? n0 + q : N - 1) * p.B_sn + t0));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = n0 + q;
+          if (n < N) {
+            const uint32_t wb[4] = {rb[q].x, rb[q].y, rb[q].z, rb[q].w};
+            float sacc = 0.f;
+#pragma unroll
+            for (int k = 0; k < kFsK; ++k)
+              sacc = fmaf(__builtin_amdgcn_exp2f(A2[n] * cs[k]),
+                          wv[k] * ((k & 1) ? bf16_hi(wb[k / 2]) : bf16_lo(wb[k / 2])), sacc);
+            acc[n] = fmaf(dp[n], sacc, acc[n]);
+            dp[n] *= __builtin_amdgcn_exp2f(A2[n] * wtot);
+          }
+        }
+      }
+    }
+    stot += wtot;
+  }
+  float* out = segw + (d * (npieces - 1) + j) * (N + 1);
+#pragma unroll
+  for (int n = 0; n < NS; ++n) {
+    if (n < N) {
+      float v = acc[n];
+      v += __shfl_xor(v, 32);
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 8);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 1);
+      if (lane == 0) out[n] = v;
+    }
+  }
+  if (lane == 0) out[N] = stot;
+}
+
+// The state entering each piece, [P][channels][N] into hv: one thread per (channel, state).
+__global__ __launch_bounds__(256) void fwd_seg_combine(ScanArgs p, int npieces, const float* __restrict__ segw,
+                                                       float* __restrict__ hv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int N = p.N;
+  if (i >= p.channels * N) return;
+  const int64_t d = i / N;
+  const int n = (int)(i % N);
+  const float A2 = p.A[d * p.A_sd + n] * kLog2e;
+  float h = p.h_init ? p.h_init[d * p.hi_sd + n] : 0.f;
+  hv[d * N + n] = h;
+  for (int j = 0; j + 1 < npieces; ++j) {
+    const float* e = segw + (d * (npieces - 1) + j) * (N + 1);
+    h = fmaf(__builtin_amdgcn_exp2f(A2 * e[N]), h, e[n]);
+    hv[((int64_t)(j + 1) * p.channels + d) * N + n] = h;
+  }
+}
+
 int npairs_of(const ScanArgs& a) { return (a.N + 1) / 2; }
 
 // Channels per wave: one while every row still gets its own wave in a single round of one
@@ -1585,6 +1743,52 @@ hipError_t take_spin_error(int* failed) {
   }
   *failed = v;
   return e;
+}
+
+int64_t diag_workspace_bytes(const ScanArgs& a) {
+  const FwdSegs f = fwd_seg_plan(a);
+  if (f.nseg <= 1) return 0;
+  // the pre-pass's (N + 1) floats per (channel, piece but the last), the states entering the
+  // pieces, and (with h_final) the segments' final states
+  const int64_t P = (int64_t)f.nseg * f.sub;
+  const int64_t segf = a.channels * (P - 1) * (a.N + 1);
+  const int64_t st = (int64_t)a.channels * a.N;
+  return 4 * (segf + P * st + (a.h_final ? f.nseg * st : 0));
+}
+
+hipError_t launch_diag(const ScanArgs& a, void* ws, hipStream_t s) {
+  const FwdSegs f = fwd_seg_plan(a);
+  if (f.nseg <= 1) return launch_diag(a, s);
+  if (!ws) return hipErrorInvalidValue;
+  const int P = f.nseg * f.sub;              // pre-pass pieces
+  const int64_t piece = f.seg_len / f.sub;
+  float* segw = static_cast<float*>(ws);
+  float* hv = segw + a.channels * (P - 1) * (a.N + 1);
+  float* hf = hv + (int64_t)P * a.channels * a.N;
+  const int64_t waves = a.channels * (P - 1);
+  if (a.N <= 16)
+    hipLaunchKernelGGL(fwd_seg_kernel<16>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, piece, P, segw);
+  else
+    hipLaunchKernelGGL(fwd_seg_kernel<32>, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, a, piece, P, segw);
+  hipLaunchKernelGGL(fwd_seg_combine, dim3((unsigned)((a.channels * a.N + 255) / 256)), dim3(256), 0, s, a, P, segw, hv);
+  // the segments as rows of their own: batch index = segment, each time row offset by the
+  // segment's start
+  ScanArgs v = a;
+  v.batch = f.nseg;
+  v.L = f.seg_len;
+  v.u_sb = v.dl_sb = v.B_sb = v.C_sb = v.y_sb = f.seg_len;
+  v.z_sb = a.z ? f.seg_len : 0;
+  v.h_init = hv;                                   // the state entering piece j sub
+  v.hi_sb = (int64_t)f.sub * a.channels * a.N;
+  v.hi_sd = a.N;
+  v.h_final = a.h_final ? hf : nullptr;
+  v.hf_sb = a.channels * a.N;
+  v.hf_sd = a.N;
+  const hipError_t e = a.out_bf16 ? launch_slots<bf16_t>(v, s) : launch_slots<float>(v, s);
+  if (e != hipSuccess || !a.h_final) return e;
+  // the last segment's final state is the caller's
+  return launch_state_copy(hf + (int64_t)(f.nseg - 1) * a.channels * a.N, 0, a.N, a.h_final, 0, a.hf_sd, 1,
+                           a.channels, a.N, s);
 }
 
 hipError_t launch_diag(const ScanArgs& a, hipStream_t s) {

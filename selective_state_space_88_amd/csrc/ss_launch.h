@@ -140,6 +140,11 @@ int cu_count();
 // Diagonal decay A [channels, N]: one or two (b, d) rows per wave, lanes along time; few rows
 // take several windows of each row in flight.  One kernel, no workspace.
 hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
+// The same where a few rows with long sequences are cut into sequence segments, which takes a
+// workspace: `ws` must hold diag_workspace_bytes(a) bytes (0: none, ws may be null) of device
+// memory ordered on `stream`.
+int64_t diag_workspace_bytes(const ScanArgs& a);
+hipError_t launch_diag(const ScanArgs& a, void* ws, hipStream_t stream);
 
 // Whether a bounded wait between the waves of a block has run out since the last call (then
 // the results of the calls in between are wrong); clears the record.  Synchronous.
