@@ -123,7 +123,11 @@ typedef struct {
  * library keeps on each device and never shrinks, so repeated calls reuse it without a device
  * allocation (SS_ERR_HIP, with nothing enqueued, if the allocation fails; the environment
  * variable SS_FAULT=alloc forces that failure for tests).  Diagonal-decay calls use no
- * workspace.
+ * workspace, except one batch row with at most two channels per compute unit, bf16 inputs in
+ * 16-byte aligned rows, L a multiple of 2048 and at least 6144, and N from 5 to 32 without
+ * zero-order hold or the trapezoidal rule: the sequence is then cut into segments run in
+ * parallel, and the states handed between them (O(channels * N) floats per segment) come from
+ * the same pool.
  *
  * Returns SS_OK or a negative SS_ERR_* code.
  */
@@ -166,8 +170,8 @@ int ss_scan_fwd_state(const ss_tensor* u, const ss_tensor* delta, const ss_tenso
  * handed between sequence segments, which ss_scan_fwd_state takes from its memory pool) comes
  * instead from one static device array of SS_NOALLOC_SCRATCH_BYTES (64 MiB), which each GPU
  * the library runs on holds until the process ends.  A call whose scratch would exceed it
- * returns SS_ERR_SCRATCH (nothing enqueued, y untouched); diagonal-decay calls use no scratch
- * and have no such limit.  Every call on one GPU shares that GPU's array and leaves its contents
+ * returns SS_ERR_SCRATCH (nothing enqueued, y untouched); diagonal-decay calls use scratch only
+ * for the states handed between sequence segments (a few MB at most).  Every call on one GPU shares that GPU's array and leaves its contents
  * behind (every byte a call reads, it wrote first): calls that overlap on one GPU -- on two
  * streams, or from two host threads -- race and give wrong results; order them on one stream.
  */

@@ -190,8 +190,8 @@ def scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: t
                      h_init: Optional[torch.Tensor] = None, h_final: Optional[torch.Tensor] = None,
                      zoh: bool = False, trapezoid: bool = False) -> torch.Tensor:
     """scan_fwd through ss_scan_fwd_noalloc: the caller passes y, and the library allocates
-    nothing (its scalar-decay scratch is a static 64 MiB array per device; larger calls raise
-    ScanError with code SS_ERR_SCRATCH).  Calls that overlap on one GPU race on that scratch."""
+    nothing (its scratch -- scalar decay's operands, the states handed between sequence segments --
+    is a static 64 MiB array per device; larger calls raise ScanError with code SS_ERR_SCRATCH).  Calls that overlap on one GPU race on that scratch."""
     _check_cuda(u, delta, A, B, C, D, z, delta_bias, h_init, h_final, y)
     flags = (SS_DELTA_SOFTPLUS if softplus else 0) | (SS_Z_GATE_SILU if z is not None else 0) | \
         (SS_ZOH if zoh else 0) | (SS_TRAPEZOID if trapezoid else 0)
