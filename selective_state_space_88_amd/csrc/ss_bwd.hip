@@ -901,7 +901,7 @@ ScanArgs ungated_forward(const BwdArgs& a, float* y0) {
 
 // diagonal decay (A [channels, N]) takes no workspace
 int64_t forward_ws_floats(const ScanArgs& f, bool scalar) {
-  if (!scalar) return 0;
+  if (!scalar) return (diag_workspace_bytes(f) + 3) / 4;   // (sequence segments)
   return ssd_path(f) ? (ssd_workspace_bytes(f) + 3) / 4 : scalar_workspace_floats(f);
 }
 
@@ -936,7 +936,7 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
       f.ckpt = bws;
       f.ckpt_nwin = (a.L + kBW - 1) / kBW;
     }
-    hipError_t e = !a.scalar ? launch_diag(f, s) : ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
+    hipError_t e = !a.scalar ? launch_diag(f, fws, s) : ssd_path(f) ? launch_ssd(f, fws, s) : launch_scalar(f, fws, s);
     if (e != hipSuccess) return e;
     b.ckpt_ready = fwd_ckpt ? 1 : 0;
     if (!ssd_bwd_path(b)) {

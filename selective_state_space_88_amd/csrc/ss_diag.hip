@@ -467,6 +467,7 @@ __device__ __forceinline__ void lds_write16(uint32_t addr, f32x4 v) {
 //   kTRAP  exponential-trapezoidal rule: the scan runs the state k = h + e/2, which obeys the
 //          Euler recurrence k_t = a_t k_{t-1} + e_t, and y reads C (k - e/2).
 // kCKPT: also store the backward's checkpoints (ScanArgs::ckpt); only with none of the others
+//        (the window-slot kernel: or with kSIO, a sequence segment's entering state)
 // kPERT: (window-slot kernel, plain or with kCKPT) the timing stress of perturb_wait
 constexpr int kSIO = 1, kZOH = 2, kTRAP = 4, kCKPT = 8, kPERT = 16;
 template <typename TIn, typename TOut, bool GATE, bool VEC, int ROWS, int MODE>
@@ -1342,7 +1343,7 @@ __global__ __launch_bounds__(64 * kSlotWaves) __attribute__((amdgpu_waves_per_eu
       // the backward's checkpoints: the window's start (the carried states) and 512 steps in
       float* ck0 = nullptr;
       if (CKPT && live) {
-        float* ck = p.ckpt + ((b * p.channels + d) * p.ckpt_nwin + 2 * w) * N + n0;
+        float* ck = p.ckpt + b * p.ck_sb + d * p.ck_sd + (2 * w) * N + n0;
         if (lane == 0) {
           ck[0] = carry[0];
           if (two) ck[1] = carry[1];
@@ -1453,6 +1454,13 @@ bool slots_path(const ScanArgs& a) {
 
 template <typename TOut>
 hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
+  if (a.ckpt && a.ck_sd == 0) {
+    // the dense checkpoint layout
+    ScanArgs c = a;
+    c.ck_sd = a.ckpt_nwin * a.N;
+    c.ck_sb = a.channels * c.ck_sd;
+    return launch_slots<TOut>(c, s);
+  }
   constexpr int64_t W = 64 * kK;
   const int64_t nwin = (a.L + W - 1) / W;
   const int ns = (a.N + 1) / 2;            // steps per window (two states a step)
@@ -1490,9 +1498,12 @@ hipError_t launch_slots(const ScanArgs& a, hipStream_t s) {
     default: return hipErrorInvalidValue;                                                                   \
   }
   if (mode & kCKPT) {
-    // (the backward's recompute: no gate, f32 y)
-    if (a.z || sizeof(TOut) != 4) return hipErrorInvalidValue;
-    if (mode & kPERT)
+    // (the backward's recompute: no gate, f32 y; an initial state only as a sequence segment)
+    if (a.z || sizeof(TOut) != 4 || a.h_final || a.ck_sb <= 0 || a.ck_sd <= 0) return hipErrorInvalidValue;
+    if (mode & kSIO)
+      hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kSIO | kCKPT>), grid, block, dyn, s, a, nwin, blocks_per_bg,
+                         skew, (int)steps, spin_limit, perturb);
+    else if (mode & kPERT)
       hipLaunchKernelGGL((diag_slots_kernel<TOut, false, kCKPT | kPERT>), grid, block, dyn, s, a, nwin, blocks_per_bg,
                          skew, (int)steps, spin_limit, perturb);
     else
@@ -1529,8 +1540,8 @@ struct FwdSegs {
 
 bool slots_path(const ScanArgs& a);
 
-// Segments apply to the plain exponential-Euler forward (no zero-order hold, trapezoid or
-// checkpoints) of one batch row with N <= 32 on the window-slot path: S the largest power of two with S
+// Segments apply to the plain exponential-Euler forward (no zero-order hold or trapezoid; the
+// backward's checkpointing recompute too) of one batch row with N <= 32 on the window-slot path: S the largest power of two with S
 // rows per channel fitting one round of the slots (4 per CU), L a multiple of S windows and at
 // least kSlots windows per segment.
 FwdSegs fwd_seg_plan(const ScanArgs& a) {
@@ -1539,7 +1550,8 @@ FwdSegs fwd_seg_plan(const ScanArgs& a) {
 #ifdef SS_NO_FWD_SEGS
   return f;   // (an ablation build: no segments)
 #endif
-  if (a.batch != 1 || a.zoh || a.trap || a.ckpt || a.N > 32 || !slots_path(a) || a.channels <= 0) return f;
+  if (a.batch != 1 || a.zoh || a.trap || (a.ckpt && a.h_final) || a.N > 32 || !slots_path(a) || a.channels <= 0)
+    return f;
   const int64_t cap = (int64_t)kWaves * cu_count() / a.channels;
   int64_t S = 1;
   while (2 * S <= cap && a.L % (2 * S * W) == 0 && a.L / (2 * S * W) >= kSlots) S *= 2;
@@ -1784,6 +1796,12 @@ hipError_t launch_diag(const ScanArgs& a, void* ws, hipStream_t s) {
   v.h_final = a.h_final ? hf : nullptr;
   v.hf_sb = a.channels * a.N;
   v.hf_sd = a.N;
+  if (a.ckpt) {
+    // segment s's checkpoints are the sequence's from 512-step window s seg_len / 512 on
+    v.ckpt_nwin = f.seg_len / 512;
+    v.ck_sb = v.ckpt_nwin * a.N;
+    v.ck_sd = a.ckpt_nwin * a.N;
+  }
   const hipError_t e = a.out_bf16 ? launch_slots<bf16_t>(v, s) : launch_slots<float>(v, s);
   if (e != hipSuccess || !a.h_final) return e;
   // the last segment's final state is the caller's

@@ -38,6 +38,10 @@ struct ScanArgs {
   // ceil(L / 512)), as the backward's checkpoint pass would store it
   float* ckpt;
   int64_t ckpt_nwin;
+  // the window-slot kernel's checkpoint strides of a batch row and of a channel, in floats (0:
+  // the dense layout above); a sequence segment run as a row of its own writes its checkpoints
+  // into the whole sequence's layout with them
+  int64_t ck_sb, ck_sd;
 };
 
 // Arguments of one decoding step (L = 1), already validated.  Strides in elements.

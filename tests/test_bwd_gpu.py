@@ -171,6 +171,23 @@ def test_matrix_backward_sequence_segments(case):
     check_bwd(MATRIX_SEGMENT_CASES[case](), "matrix segments: " + case)
 
 
+FORWARD_SEGMENT_CASES = {
+    # one batch row, L a multiple of two segments of 1024-step windows (at least three each): the
+    # recompute before the gate runs as 2 sequence segments (pre-pass in 16 and 8 pieces) and
+    # writes the checkpoints of both into the whole sequence's layout
+    "gated bf16 N16 L16384": lambda: inputs.random_problem(7306, 1, 8, 16384, 16, gate=True),
+    "gated bf16 N24 L12288": lambda: inputs.random_problem(7307, 1, 4, 12288, 24, gate=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(FORWARD_SEGMENT_CASES))
+def test_gated_backward_recompute_in_segments(case):
+    """A gated one-row layer: the backward's recompute of the output before the gate takes the
+    forward's sequence segments (each started from the state the combine hands it), and its
+    checkpoints feed the per-channel backward."""
+    check_bwd(FORWARD_SEGMENT_CASES[case](), "forward segments: " + case)
+
+
 def test_sequence_segments_bf16_upstream_gradient():
     """dy in bf16 through both segmented layouts (the pre-passes read dy in its own type)."""
     torch = torch_dev()
