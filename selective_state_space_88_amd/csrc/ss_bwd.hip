@@ -905,20 +905,37 @@ int64_t forward_ws_floats(const ScanArgs& f, bool scalar) {
   return ssd_path(f) ? (ssd_workspace_bytes(f) + 3) / 4 : scalar_workspace_floats(f);
 }
 
+// An ungated diagonal layer on the window-slot path (few rows): the forward stores the
+// checkpoints as it goes (on sequence segments where they apply) several times faster than the
+// checkpoint pass, which walks each row's whole sequence on one wave; its output goes to a
+// scratch row of L floats per (batch, channel)
+bool fwd_checkpoints(const BwdArgs& a) {
+  return !a.scalar && !a.z && !a.ckpt_ready && !ssd_bwd_path(a) && diag_slots_path(ungated_forward(a, nullptr));
+}
+
+// floats of the per-channel path's checkpoints and segment pre-pass
+int64_t ckpt_seg_floats(const BwdArgs& a) {
+  const BwdSegs sp = bwd_seg_plan(a);
+  const int64_t rows = a.batch * a.channels;
+  return rows * ((a.L + kBW - 1) / kBW) * a.N + (sp.nseg > 1 ? rows * sp.nseg * (a.N + 1) : 0);
+}
+
 }  // namespace
 
 int64_t bwd_workspace_floats(const BwdArgs& a) {
   if (gated_path(a)) {
     BwdArgs b = a;
     b.z = nullptr;
+    b.ckpt_ready = !a.scalar && !ssd_bwd_path(b) ? 1 : 0;   // as the launch sets it
     const int64_t ny = round64(a.batch * a.channels * a.L);
     return ny + round64(forward_ws_floats(ungated_forward(a, nullptr), a.scalar)) + bwd_workspace_floats(b);
   }
   if (ssd_bwd_path(a)) return ssd_bwd_workspace_floats(a);
-  // the checkpoints, then (with sequence segments) the pre-pass's N + 1 floats per (row, segment)
-  const BwdSegs sp = bwd_seg_plan(a);
-  const int64_t rows = a.batch * a.channels;
-  return rows * ((a.L + kBW - 1) / kBW) * a.N + (sp.nseg > 1 ? rows * sp.nseg * (a.N + 1) : 0);
+  // the checkpoints, then (with sequence segments) the pre-pass's N + 1 floats per (row, segment),
+  // then (checkpoints from the forward) its output and workspace
+  if (!fwd_checkpoints(a)) return ckpt_seg_floats(a);
+  return round64(ckpt_seg_floats(a)) + round64(a.batch * a.channels * a.L) +
+         forward_ws_floats(ungated_forward(a, nullptr), false);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
@@ -963,6 +980,17 @@ hipError_t launch_bwd(const BwdArgs& a, float* ws, hipStream_t s) {
     b.dy_sd = a.L;
     b.vec = a.vec && a.L % 4 == 0;
     return launch_bwd(b, bws, s);
+  }
+  if (fwd_checkpoints(a)) {
+    float* y0 = ws + round64(ckpt_seg_floats(a));
+    ScanArgs f = ungated_forward(a, y0);
+    f.ckpt = ws;
+    f.ckpt_nwin = (a.L + kBW - 1) / kBW;
+    const hipError_t e = launch_diag(f, y0 + round64(a.batch * a.channels * a.L), s);
+    if (e != hipSuccess) return e;
+    BwdArgs b = a;
+    b.ckpt_ready = 1;
+    return launch_bwd(b, ws, s);
   }
   if (a.in_bf16) return a.dy_bf16 ? launch_t<bf16_t, bf16_t>(a, ws, s) : launch_t<bf16_t, float>(a, ws, s);
   return a.dy_bf16 ? launch_t<float, bf16_t>(a, ws, s) : launch_t<float, float>(a, ws, s);

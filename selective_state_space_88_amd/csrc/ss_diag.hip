@@ -1757,6 +1757,8 @@ hipError_t take_spin_error(int* failed) {
   return e;
 }
 
+bool diag_slots_path(const ScanArgs& a) { return slots_path(a); }
+
 int64_t diag_workspace_bytes(const ScanArgs& a) {
   const FwdSegs f = fwd_seg_plan(a);
   if (f.nseg <= 1) return 0;

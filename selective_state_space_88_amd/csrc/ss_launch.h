@@ -148,6 +148,9 @@ hipError_t launch_diag(const ScanArgs& a, hipStream_t stream);
 // workspace: `ws` must hold diag_workspace_bytes(a) bytes (0: none, ws may be null) of device
 // memory ordered on `stream`.
 int64_t diag_workspace_bytes(const ScanArgs& a);
+// whether a diagonal-decay forward runs on the window-slot kernel (few rows, at least three
+// 1024-step windows, bf16 inputs in 16-byte aligned rows)
+bool diag_slots_path(const ScanArgs& a);
 hipError_t launch_diag(const ScanArgs& a, void* ws, hipStream_t stream);
 
 // Whether a bounded wait between the waves of a block has run out since the last call (then

@@ -188,6 +188,21 @@ def test_gated_backward_recompute_in_segments(case):
     check_bwd(FORWARD_SEGMENT_CASES[case](), "forward segments: " + case)
 
 
+UNGATED_SLOTS_CASES = {
+    # one batch row without a gate on the window-slot path: the forward (into a scratch output)
+    # stores the checkpoints instead of the checkpoint pass; on 2 sequence segments, and
+    # unsegmented with a partial last window
+    "bf16 N16 L16384, segments": lambda: inputs.random_problem(7308, 1, 8, 16384, 16, gate=False),
+    "bf16 N12 L5000 ragged": lambda: inputs.random_problem(7309, 1, 8, 5000, 12, gate=False),
+    "two batches bf16 N16 L4096": lambda: inputs.random_problem(7310, 2, 4, 4096, 16, gate=False),
+}
+
+
+@pytest.mark.parametrize("case", sorted(UNGATED_SLOTS_CASES))
+def test_ungated_backward_checkpoints_from_the_forward(case):
+    check_bwd(UNGATED_SLOTS_CASES[case](), "ungated, checkpoints from the forward: " + case)
+
+
 def test_sequence_segments_bf16_upstream_gradient():
     """dy in bf16 through both segmented layouts (the pre-passes read dy in its own type)."""
     torch = torch_dev()
