@@ -216,7 +216,11 @@ int ss_scan_step(const ss_tensor* u, const ss_tensor* delta, const ss_tensor* A,
  * (batch * channels * ceil(L / 32) * N' floats, N' = N rounded up to 32, 64 or 128) and C B^T
  * per chunk.  With a gate, either form first recomputes the output before the gate into the
  * workspace (batch * channels * L floats more); the per-channel kernel takes dz and dy s(z) from
- * it where it reads dy, the matrix form in a pass of its own.  Chain rule, with s(z) =
+ * it where it reads dy, the matrix form in a pass of its own.  Without a gate, a diagonal-decay
+ * call with few rows (at most 4 per CU) and at least three 1024-step windows also runs that
+ * forward, for the checkpoints it stores as it goes (its output, batch * channels * L floats of
+ * workspace, is unused), since it is several times faster there than a checkpoint pass that
+ * walks each row on one wave.  Chain rule, with s(z) =
  * z sigmoid(z) and
  * dy0 = dy s(z):  g_t = C_t dy0_t + exp(dt_{t+1} A) g_{t+1} (the gradient of h_t),
  * dC_t = dy0_t h_t,  dB_t = g_t dt_t u_t,  du_t = dy0_t D + sum_n g_t dt_t B_t,
